@@ -1,0 +1,215 @@
+"""CPU oracle for the forward Gaussian-splatting rasterizer.
+
+TEST INFRASTRUCTURE ONLY: imported by `tests/`, by `__graft_entry__.smoke()`
+and by the benchmark's `cpu_baseline` leg, never by the product package.
+
+Two independent pieces:
+  * `gs_oracle.c` (built to `liboracle.so` with gcc, OpenMP, -ffp-contract=off):
+    projection in binary32 following a fixed operation order, binning, and
+    per-pixel binary64 compositing over all depth-sorted Gaussians;
+  * `composite_2d` below: the dense 2D rasteriser of the lesson
+    "3D Gaussian Splatting from scratch", section "Étape 2: Rasteriser à
+    éclaboussure en 2D", in numpy binary64 (every Gaussian at every pixel,
+    alpha clamped to 0.99, ordered by depth, no early stop).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gs_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+TILE = 16
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (binary32 semantics: no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Camera(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_float * 9), ("t", ctypes.c_float * 3),
+                ("fx", ctypes.c_float), ("fy", ctypes.c_float), ("cx", ctypes.c_float),
+                ("cy", ctypes.c_float), ("znear", ctypes.c_float),
+                ("width", ctypes.c_int32), ("height", ctypes.c_int32)]
+
+
+class _Projected(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("depth", "mean2d", "cov2d", "conic", "radius", "cov3d", "rect", "tile_count", "rgb")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        lib.oracle_preprocess.argtypes = [i64, i32, P, P, P, P, P, ctypes.POINTER(_Camera),
+                                          ctypes.POINTER(_Projected)]
+        lib.oracle_preprocess.restype = None
+        lib.oracle_bin.argtypes = [i64, P, P, P, i32, i32, P, P, P, P, P]
+        lib.oracle_bin.restype = None
+        lib.oracle_total_pairs.argtypes = [i64, P]
+        lib.oracle_total_pairs.restype = i64
+        lib.oracle_composite.argtypes = [i64, P, P, P, P, P, P, P, i32, i32, P, i32, ctypes.c_double,
+                                         P, i64, P, P, P]
+        lib.oracle_composite.restype = None
+        lib.oracle_cov3d.argtypes = [P, P, P]
+        lib.oracle_cov3d.restype = None
+        lib.oracle_sh_basis.argtypes = [ctypes.c_double] * 3 + [P]
+        lib.oracle_sh_basis.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def tiles_for(camera: dict) -> tuple[int, int]:
+    return (camera["width"] + TILE - 1) // TILE, (camera["height"] + TILE - 1) // TILE
+
+
+def _camera(camera: dict) -> _Camera:
+    c = _Camera()
+    c.R[:] = [float(v) for v in np.asarray(camera["R"], np.float32).reshape(9)]
+    c.t[:] = [float(v) for v in np.asarray(camera["t"], np.float32).reshape(3)]
+    for k in ("fx", "fy", "cx", "cy", "znear"):
+        setattr(c, k, float(np.float32(camera[k])))
+    c.width, c.height = int(camera["width"]), int(camera["height"])
+    return c
+
+
+def preprocess(arrays: dict, sh_degree: int, camera: dict) -> dict:
+    """Per-Gaussian projection record (numpy planes, index g last)."""
+    lib = _load()
+    mean, quat = _f32(arrays["mean"]), _f32(arrays["quat"])
+    ls, op, sh = _f32(arrays["log_scale"]), _f32(arrays["opacity"]), _f32(arrays["sh"])
+    n = mean.shape[1]
+    out = dict(depth=np.zeros(n, np.float32), mean2d=np.zeros((2, n), np.float32),
+               cov2d=np.zeros((3, n), np.float32), conic=np.zeros((3, n), np.float32),
+               radius=np.zeros(n, np.float32), cov3d=np.zeros((6, n), np.float32),
+               rect=np.zeros((4, n), np.int32), tile_count=np.zeros(n, np.uint32),
+               rgb=np.zeros((3, n), np.float64))
+    pr = _Projected(**{k: _ptr(v).value for k, v in out.items()})
+    cam = _camera(camera)
+    lib.oracle_preprocess(n, sh_degree, _ptr(mean), _ptr(quat), _ptr(ls), _ptr(op), _ptr(sh),
+                          ctypes.byref(cam), ctypes.byref(pr))
+    out["opacity"] = op
+    out["tiles"] = tiles_for(camera)
+    return out
+
+
+def bin_pairs(proj: dict, want_unsorted: bool = True) -> dict:
+    """Duplicated (tile, depth) keys, their sorted order and per-tile ranges."""
+    lib = _load()
+    tx, ty = proj["tiles"]
+    n = proj["depth"].shape[0]
+    m = int(lib.oracle_total_pairs(n, _ptr(proj["tile_count"])))
+    ku = np.zeros(m, np.uint64) if want_unsorted else None
+    vu = np.zeros(m, np.uint32) if want_unsorted else None
+    ks, vs = np.zeros(m, np.uint64), np.zeros(m, np.uint32)
+    ranges = np.zeros((tx * ty, 2), np.uint32)
+    lib.oracle_bin(n, _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]), tx, ty,
+                   _ptr(ku), _ptr(vu), _ptr(ks), _ptr(vs), _ptr(ranges))
+    return dict(num_dups=m, keys_unsorted=ku, values_unsorted=vu, keys=ks, values=vs, ranges=ranges)
+
+
+def composite(proj: dict, camera: dict, bg=(0.0, 0.0, 0.0), pixels=None, support_all=False,
+              t_eps: float = 1e-4):
+    """Image (binary64). Returns (rgb[n_pix,3] or [H,W,3], T, blended-pair counts)."""
+    lib = _load()
+    n = proj["depth"].shape[0]
+    W, H = camera["width"], camera["height"]
+    if pixels is None:
+        npx = W * H
+        pix = None
+    else:
+        pix = np.ascontiguousarray(pixels, dtype=np.int64)
+        npx = pix.shape[0]
+    out = np.zeros((npx, 3), np.float64)
+    T = np.zeros(npx, np.float64)
+    cnt = np.zeros(npx, np.int64)
+    bgv = np.asarray(bg, np.float64)
+    rgb = np.ascontiguousarray(proj["rgb"], np.float64)
+    lib.oracle_composite(n, _ptr(proj["mean2d"]), _ptr(proj["conic"]), _ptr(_f32(proj["opacity"])),
+                         _ptr(rgb), _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]),
+                         W, H, _ptr(bgv), 1 if support_all else 0, float(t_eps), _ptr(pix), npx,
+                         _ptr(out), _ptr(T), _ptr(cnt))
+    if pixels is None:
+        return out.reshape(H, W, 3), T.reshape(H, W), cnt.reshape(H, W)
+    return out, T, cnt
+
+
+def render(arrays: dict, sh_degree: int, camera: dict, bg=(0.0, 0.0, 0.0), pixels=None):
+    proj = preprocess(arrays, sh_degree, camera)
+    return composite(proj, camera, bg=bg, pixels=pixels)
+
+
+def cov3d(quat4, log_scale3) -> np.ndarray:
+    lib = _load()
+    q, s = _f32(quat4).reshape(4), _f32(log_scale3).reshape(3)
+    out = np.zeros(6, np.float32)
+    lib.oracle_cov3d(_ptr(q), _ptr(s), _ptr(out))
+    return out
+
+
+def sh_basis(direction) -> np.ndarray:
+    lib = _load()
+    out = np.zeros(16, np.float64)
+    x, y, z = (float(v) for v in direction)
+    lib.oracle_sh_basis(x, y, z, _ptr(out))
+    return out
+
+
+def composite_2d(means, covs, colours, opacities, depths, image_size, bg=None):
+    """Dense 2D splat rasteriser in binary64.
+
+    Lesson "3D Gaussian Splatting from scratch", sections "Étape 1: Un
+    gaussien 2D" and "Étape 2: Rasteriser à éclaboussure en 2D": every
+    Gaussian is evaluated at every pixel (x = column, y = row, integer
+    positions), alpha = clamp(opacity * density, 0, 0.99), Gaussians are taken
+    in ascending depth (ties by index) and composited front to back with the
+    running transmittance; nothing stops early.  Returns (H, W, 3) and the
+    final transmittance (H, W).
+    """
+    means = np.asarray(means, np.float64)
+    covs = np.asarray(covs, np.float64)
+    colours = np.asarray(colours, np.float64)
+    opacities = np.asarray(opacities, np.float64)
+    H, W = image_size
+    yy, xx = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
+    pts = np.stack([xx, yy], axis=-1).reshape(-1, 2)
+    inv = np.linalg.inv(covs) if len(covs) else covs
+    diff = pts[None, :, :] - means[:, None, :]
+    quad = np.einsum("gpi,gij,gpj->gp", diff, inv, diff)
+    alphas = np.clip(opacities[:, None] * np.exp(-0.5 * quad), 0.0, 0.99)
+    order = np.argsort(np.asarray(depths), kind="stable")
+    T = np.ones(H * W)
+    out = np.zeros((H * W, 3))
+    for g in order:
+        a = alphas[g]
+        out += (T * a)[:, None] * colours[g][None, :]
+        T = T * (1.0 - a)
+    if bg is not None:
+        out += T[:, None] * np.asarray(bg, np.float64)[None, :]
+    return out.reshape(H, W, 3), T.reshape(H, W)
