@@ -1,0 +1,255 @@
+/*
+ * gsrast — forward tile-based 3D Gaussian-splatting rasterizer for AMD
+ * Instinct MI355X (gfx950), C ABI.
+ *
+ * The method: the lesson "3D Gaussian Splatting from scratch"
+ * (aiengineeringfromscratch.com).  A Gaussian carries a world position, a
+ * unit quaternion, per-axis log-scales, an opacity in [0,1] and
+ * spherical-harmonic colour coefficients (section "Ce qu'un Gaussien porte").
+ * Rendering projects each Gaussian with the camera extrinsics and intrinsics,
+ * assigns it to 16x16 screen tiles, depth-sorts per tile and alpha-composites
+ * front to back (flowchart under "Rastérisation, non rayée"; sections
+ * "L'étape de projection" and "La règle de composition alpha").
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers inside gs_gaussians, and the output image, are DEVICE
+ *    pointers on the context's device.  The caller owns them; the library never
+ *    frees or retains them past the call.
+ *  - Every call returns a gs_status and never aborts or throws across the ABI.
+ *    Arguments are validated on the host before any HIP call, so
+ *    GS_ERR_INVALID_ARGUMENT leaves the device untouched.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    gs_bin_and_sort and gs_render synchronise that stream once per call to
+ *    read back the number of (Gaussian, tile) pairs; all other calls are
+ *    asynchronous.
+ *  - One context per host thread / stream at a time; a context is not
+ *    thread-safe.  Views returned in gs_projected / gs_binning point into
+ *    context-owned device memory and stay valid until the next call on the
+ *    same context or gs_context_destroy.
+ */
+#ifndef GSRAST_H
+#define GSRAST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, degree or camera; nothing was enqueued */
+    GS_ERR_OUT_OF_MEMORY = 2,    /* device workspace could not grow (or would pass GS_OPT_MAX_WORKSPACE_BYTES) */
+    GS_ERR_CAPACITY = 3,         /* pair count above 2^32-1 or above GS_OPT_MAX_DUPS */
+    GS_ERR_DEVICE = 4            /* a HIP call failed; gs_last_error() has the HIP message */
+} gs_status;
+
+/* Tile edge in pixels (flowchart: "Assign to tiles (16x16 screen-space)"). */
+#define GS_TILE 16
+/* Largest alpha a single Gaussian may take (section "Étape 2": clamp to 0.99). */
+#define GS_ALPHA_MAX 0.99f
+/* A pixel stops after the blend that brings its transmittance below this. */
+#define GS_T_EPS 1e-4f
+/* Floats per projected-splat record (see gs_projected.splat). */
+#define GS_SPLAT_STRIDE 12
+
+/*
+ * Gaussian parameters, structure of arrays, fp32, device memory, index g in
+ * [0, n) fastest (section "Ce qu'un Gaussien porte" lists the fields):
+ *   mean      [3][n]  world position
+ *   quat      [4][n]  rotation quaternion (w, x, y, z); normalised in-kernel
+ *   log_scale [3][n]  per-axis log-scales, exponentiated at render time
+ *   opacity   [n]     already in [0, 1] (post-sigmoid)
+ *   sh        [K*3][n] with K = (sh_degree+1)^2; plane k*3+c is coefficient k of
+ *                     colour channel c
+ * n may be 0 (the image is then the background).  n < 2^31.
+ */
+typedef struct {
+    int64_t n;
+    int32_t sh_degree; /* 0..3 (section "Étape 6": up to 16 terms per channel) */
+    int32_t reserved;
+    const float *mean;
+    const float *quat;
+    const float *log_scale;
+    const float *opacity;
+    const float *sh;
+} gs_gaussians;
+
+/*
+ * Pinhole camera (host memory, passed by pointer).  R, t map world to camera
+ * coordinates, x right, y down, z forward: p_cam = R p_world + t, R row-major.
+ * Pixel (row i, column j) is sampled at x = j, y = i (integer positions).
+ * Requirements: width, height in [1, 32768]; fx, fy > 0; znear > 0; all
+ * finite.  Gaussians with camera-space z <= znear are culled.
+ */
+typedef struct {
+    float R[9];
+    float t[3];
+    float fx, fy, cx, cy;
+    float znear;
+    int32_t width, height;
+} gs_camera;
+
+/*
+ * Output of gs_preprocess (views into context memory, device pointers).
+ *   splat [n][GS_SPLAT_STRIDE] fp32 records:
+ *          0 u, 1 v            projected mean in pixels
+ *          2 A, 3 B, 4 C       conic = inverse 2D covariance: q = A dx^2 + 2 B dx dy + C dy^2
+ *          5 opacity
+ *          6 r, 7 g, 8 b       SH colour in the view direction
+ *          9 radius            ceil(3 sqrt(largest eigenvalue of the 2D covariance))
+ *          10, 11              unused
+ *   depth      [n] camera-space z
+ *   rect       [n][4] uint16: x0, x1, y0, y1 tile rectangle, half-open
+ *   tile_count [n] (x1-x0)*(y1-y0) for a visible Gaussian, else 0
+ * Fields other than tile_count and rect are unspecified when tile_count is 0.
+ */
+typedef struct {
+    int64_t n;
+    int32_t tiles_x, tiles_y;
+    const float *splat;
+    const float *depth;
+    const uint16_t *rect;
+    const uint32_t *tile_count;
+} gs_projected;
+
+/*
+ * Output of gs_bin_and_sort (views into context memory, device pointers).
+ * One entry per (visible Gaussian, tile of its rectangle); num_dups entries.
+ *   keys        [num_dups] (tile_id << 32) | bit pattern of the fp32 depth,
+ *               tile_id = ty * tiles_x + tx; ascending, equal keys ordered by
+ *               ascending Gaussian index.  NULL when GS_OPT_EMIT_KEYS is 0.
+ *   values      [num_dups] Gaussian index of each sorted entry
+ *   tile_ranges [tiles_x*tiles_y][2] half-open [start, end) into keys/values;
+ *               (0, 0) for a tile no Gaussian touches
+ *   keys_unsorted / values_unsorted: the pairs before sorting, listed by
+ *               Gaussian index then row-major over the rectangle; only filled in
+ *               GS_SORT_KEY64 mode with GS_OPT_EMIT_KEYS set, else NULL.
+ */
+typedef struct {
+    int64_t num_dups;
+    int32_t tiles_x, tiles_y;
+    const uint64_t *keys;
+    const uint32_t *values;
+    const uint32_t *tile_ranges;
+    const uint64_t *keys_unsorted;
+    const uint32_t *values_unsorted;
+} gs_binning;
+
+/* Sorting strategies; both give identical keys, values and ranges. */
+typedef enum {
+    /* depth-sort the Gaussians once (32-bit keys), list pairs in that order,
+       then a stable radix sort on the tile id alone (default) */
+    GS_SORT_DEPTH_FIRST = 0,
+    /* duplicate 64-bit (tile << 32 | depth) keys in Gaussian order, then a
+       stable LSD radix sort over the significant key bits */
+    GS_SORT_KEY64 = 1
+} gs_sort_mode;
+
+typedef enum {
+    GS_OPT_SORT_MODE = 0,            /* gs_sort_mode, default GS_SORT_DEPTH_FIRST */
+    GS_OPT_EMIT_KEYS = 1,            /* 1: gs_bin_and_sort materialises keys (default 1); gs_render never does */
+    GS_OPT_MAX_DUPS = 2,             /* cap on pairs per frame (default 2^32-1) -> GS_ERR_CAPACITY */
+    GS_OPT_MAX_WORKSPACE_BYTES = 3,  /* cap on context device memory (default: none) -> GS_ERR_OUT_OF_MEMORY */
+    GS_OPT_PROFILE = 4               /* 1: bracket every kernel with HIP events (see gs_profile_read) */
+} gs_option;
+
+/* Per-stage timing collected while GS_OPT_PROFILE is 1. */
+typedef enum {
+    GS_STAGE_PREPROCESS = 0,
+    GS_STAGE_DEPTH_SORT = 1,   /* depth-first mode: radix passes over the per-Gaussian depth keys */
+    GS_STAGE_SCAN = 2,         /* prefix sum of tile counts */
+    GS_STAGE_DUPLICATE = 3,
+    GS_STAGE_TILE_SORT = 4,    /* radix passes over the pair list */
+    GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission) */
+    GS_STAGE_COMPOSITE = 6,
+    GS_STAGE_READBACK = 7,     /* pair-count copy to the host + stream wait */
+    GS_STAGE_COUNT = 8
+} gs_stage;
+
+typedef struct {
+    double ms[GS_STAGE_COUNT];        /* summed kernel time per stage, milliseconds */
+    int64_t launches[GS_STAGE_COUNT]; /* kernels (or copies) timed per stage */
+} gs_profile;
+
+typedef struct gs_context gs_context;
+
+/* Creates a context on HIP device `device`.  GS_ERR_DEVICE if the device
+ * cannot be selected.  *out is set to NULL on failure. */
+gs_status gs_context_create(gs_context **out, int device);
+/* Frees all context memory.  NULL is accepted. */
+void gs_context_destroy(gs_context *ctx);
+/* Sets an option (gs_option).  GS_ERR_INVALID_ARGUMENT on an unknown option or value. */
+gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value);
+
+/*
+ * Host-only argument check used by every entry point (no HIP call).  On error
+ * writes a NUL-terminated reason into msg (if msg_len > 0).  `camera` may be
+ * NULL when only the Gaussians are checked; `gaussians` may be NULL likewise.
+ */
+gs_status gs_check_arguments(const gs_gaussians *gaussians, const gs_camera *camera, char *msg,
+                             size_t msg_len);
+
+/*
+ * Projection + SH colour + tile rectangle per Gaussian (sections "Ce qu'un
+ * Gaussien porte", "L'étape de projection", "Étape 5: De la 2D à la 3D",
+ * "Étape 6").  Sigma = R S S^T R^T; Sigma' = J W Sigma W^T J^T with J taken
+ * at the camera-space mean; radius 3 sigma along the major axis; colour from
+ * the SH expansion in the direction camera centre -> mean.
+ */
+gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
+                        gs_projected *out, hipStream_t stream);
+
+/*
+ * Tile binning of the last gs_preprocess output: prefix sum of tile counts,
+ * (tile, depth) pair listing, stable sort, and per-tile ranges (flowchart
+ * steps "Assign to tiles" and "Depth-sort per tile").  `projected` must be the
+ * view returned by the last gs_preprocess on this context.  Synchronises
+ * `stream` once.
+ */
+gs_status gs_bin_and_sort(gs_context *ctx, const gs_projected *projected, const gs_camera *camera,
+                          gs_binning *out, hipStream_t stream);
+
+/*
+ * Front-to-back alpha compositing per 16x16 tile (section "La règle de
+ * composition alpha"): alpha = min(0.99, o exp(-q/2)), C += T alpha c,
+ * T *= (1 - alpha); a pixel stops after the blend that brings T below
+ * GS_T_EPS; out = C + T bg.  bg_rgb: 3 host floats.  image_hwc: device
+ * [height][width][3] fp32, fully overwritten.
+ */
+gs_status gs_composite(gs_context *ctx, const gs_projected *projected, const gs_binning *binning,
+                       const gs_camera *camera, const float bg_rgb[3], float *image_hwc,
+                       hipStream_t stream);
+
+/*
+ * As gs_composite, and also writes per-pixel diagnostics when non-NULL:
+ * final_T [height][width] final transmittance, n_blend [height][width] number
+ * of Gaussians blended into the pixel.  If blend_total is non-NULL (a device
+ * uint64), the sum of n_blend over the image is added to it.
+ */
+gs_status gs_composite_ex(gs_context *ctx, const gs_projected *projected, const gs_binning *binning,
+                          const gs_camera *camera, const float bg_rgb[3], float *image_hwc,
+                          float *final_T, uint32_t *n_blend, unsigned long long *blend_total,
+                          hipStream_t stream);
+
+/* gs_preprocess + gs_bin_and_sort + gs_composite on one stream (keys are not
+ * materialised).  Synchronises `stream` once. */
+gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
+                    const float bg_rgb[3], float *image_hwc, hipStream_t stream);
+
+/* Reads (and resets) the accumulated per-stage times; waits for the timed work. */
+gs_status gs_profile_read(gs_context *ctx, gs_profile *out);
+
+/* Static description of a status code. */
+const char *gs_status_string(gs_status status);
+/* Message of the last failure on this context ("" if none).  NULL ctx -> "". */
+const char *gs_last_error(const gs_context *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSRAST_H */

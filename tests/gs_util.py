@@ -1,0 +1,87 @@
+"""Shared helpers for the GPU parity tests: run the HIP path and the oracle on one input."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+IMAGE_TOL = 2e-4      # max abs error per pixel channel, fp32 GPU vs fp64 oracle
+RGB_TOL = 2e-5        # SH colour: fp32 GPU vs fp64 oracle
+
+
+def note(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(arrays: dict, sh_degree: int, camera: dict, bg=(0.0, 0.0, 0.0), sort_mode: int = 0,
+            emit_keys: bool = True, aux: bool = True, rast=None):
+    """Preprocess + bin + composite through the C ABI; returns numpy copies."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    r = rast or binding.Rasterizer(sort_mode=sort_mode, emit_keys=emit_keys)
+    dev = binding.gaussians_to_device(arrays)
+    pr = r.preprocess(dev, sh_degree, camera)
+    bn = r.bin_and_sort(pr, camera)
+    H, W = camera["height"], camera["width"]
+    T = torch.empty((H, W), dtype=torch.float32, device="cuda") if aux else None
+    nb = torch.empty((H, W), dtype=torch.int32, device="cuda") if aux else None
+    tot = torch.zeros(1, dtype=torch.int64, device="cuda") if aux else None
+    img = r.composite(pr, bn, camera, bg=bg, final_T=T, n_blend=nb, blend_total=tot)
+    pt = r.projected_tensors(pr)
+    bt = r.binning_tensors(bn)
+    torch.cuda.synchronize()
+    out = dict(
+        splat=pt["splat"].cpu().numpy(),
+        depth=pt["depth"].cpu().numpy(),
+        rect=pt["rect"].cpu().numpy().view(np.uint16).astype(np.int32),
+        tile_count=pt["tile_count"].cpu().numpy().view(np.uint32),
+        num_dups=bt["num_dups"],
+        values=bt["values"].cpu().numpy().view(np.uint32),
+        ranges=bt["ranges"].cpu().numpy().view(np.uint32),
+        keys=None if bt["keys"] is None else bt["keys"].cpu().numpy().view(np.uint64),
+        keys_unsorted=None if bt["keys_unsorted"] is None else bt["keys_unsorted"].cpu().numpy().view(np.uint64),
+        values_unsorted=None if bt["values_unsorted"] is None else bt["values_unsorted"].cpu().numpy().view(np.uint32),
+        image=img.cpu().numpy(),
+    )
+    if aux:
+        out["T"] = T.cpu().numpy()
+        out["n_blend"] = nb.cpu().numpy()
+        out["blend_total"] = int(tot.item())
+    if rast is None:
+        r.close()
+    return out
+
+
+def check_preprocess(g: dict, o: dict):
+    """Integer and fp32 projection fields must match the oracle bit for bit."""
+    assert np.array_equal(g["tile_count"], o["tile_count"]), "tile_count"
+    vis = o["tile_count"] > 0
+    assert np.array_equal(g["depth"].view(np.uint32), o["depth"].view(np.uint32)), "depth bits"
+    assert np.array_equal(g["rect"].T[:, vis], o["rect"][:, vis]), "rect"
+    sp = g["splat"]
+    assert np.array_equal(sp[vis, 0].view(np.uint32), o["mean2d"][0, vis].view(np.uint32)), "u"
+    assert np.array_equal(sp[vis, 1].view(np.uint32), o["mean2d"][1, vis].view(np.uint32)), "v"
+    for k in range(3):
+        assert np.array_equal(sp[vis, 2 + k].view(np.uint32), o["conic"][k, vis].view(np.uint32)), f"conic {k}"
+    assert np.array_equal(sp[vis, 5], o["opacity"][vis]), "opacity"
+    assert np.array_equal(sp[vis, 9], o["radius"][vis]), "radius"
+    if vis.any():
+        err = np.abs(sp[vis, 6:9].astype(np.float64) - o["rgb"][:, vis].T).max()
+        assert err <= RGB_TOL, f"rgb err {err}"
+
+
+def check_binning(g: dict, ob: dict, check_keys: bool = True):
+    assert g["num_dups"] == ob["num_dups"], f"num_dups {g['num_dups']} vs {ob['num_dups']}"
+    assert np.array_equal(g["values"], ob["values"]), "sorted values"
+    assert np.array_equal(g["ranges"], ob["ranges"]), "tile ranges"
+    if check_keys:
+        assert g["keys"] is not None and np.array_equal(g["keys"], ob["keys"]), "sorted keys"
+
+
+def image_error(g_img, o_img):
+    return float(np.abs(g_img.astype(np.float64) - o_img).max()) if g_img.size else 0.0

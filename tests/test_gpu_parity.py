@@ -1,0 +1,209 @@
+"""HIP path vs CPU oracle, through the C ABI (needs an MI355X).
+
+Integers (tile counts, rectangles, depth bits, pair count, sorted keys and values,
+tile ranges) and the fp32 projection fields must be bit-identical; the image must
+be within 2e-4 per channel of the oracle's fp64 composite.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tile_differentiable_rasterizer_gs_amd import scenes
+
+from gs_util import IMAGE_TOL, check_binning, check_preprocess, gpu_run, image_error, note
+
+pytestmark = pytest.mark.gpu
+
+MODES = [0, 1]          # GS_SORT_DEPTH_FIRST, GS_SORT_KEY64
+
+
+def _full_check(arrays, deg, cam, bg=(0.0, 0.0, 0.0), mode=0, full_image=True, pixels=None):
+    g = gpu_run(arrays, deg, cam, bg=bg, sort_mode=mode)
+    o = oracle.preprocess(arrays, deg, cam)
+    check_preprocess(g, o)
+    ob = oracle.bin_pairs(o, want_unsorted=(mode == 1))
+    check_binning(g, ob)
+    if mode == 1:
+        assert np.array_equal(g["keys_unsorted"], ob["keys_unsorted"]), "unsorted keys"
+        assert np.array_equal(g["values_unsorted"], ob["values_unsorted"]), "unsorted values"
+    W = cam["width"]
+    if full_image:
+        oimg, oT, ocnt = oracle.composite(o, cam, bg=bg)
+        err = image_error(g["image"], oimg)
+        assert err <= IMAGE_TOL, f"image err {err}"
+        assert np.abs(g["T"] - oT).max() <= IMAGE_TOL
+        # blend counts agree except where the stop threshold is crossed within rounding
+        assert np.mean(g["n_blend"] != ocnt) < 1e-3
+        assert g["blend_total"] == int(g["n_blend"].astype(np.int64).sum())
+    else:
+        oimg, oT, ocnt = oracle.composite(o, cam, bg=bg, pixels=pixels)
+        gi = g["image"].reshape(-1, 3)[pixels]
+        err = image_error(gi, oimg)
+        assert err <= IMAGE_TOL, f"sampled image err {err}"
+    return g, o, err
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_c1_full_parity(mode):
+    s = scenes.make_scene("c1_10k_sh0_256")
+    note(f"c1 mode={mode}")
+    _, _, err = _full_check(s.arrays(), s.sh_degree, s.cameras[0], mode=mode)
+    note(f"c1 mode={mode} image err {err:.2e}")
+
+
+@pytest.mark.parametrize("deg", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", MODES)
+def test_random_scenes_ragged_tiles(deg, mode):
+    # image sizes not multiples of 16: ragged last tile row and column
+    w, h = 203 + 11 * deg, 141 + 7 * deg
+    s = scenes.random_scene(seed=10 + deg, n=2500, sh_degree=deg, width=w, height=h)
+    note(f"random deg={deg} mode={mode} {w}x{h}")
+    _full_check(s.arrays(), deg, s.cameras[0], bg=(0.25, 0.5, 0.75), mode=mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_large_gaussians_and_many_tiles(mode):
+    # big splats: thousands of pairs per Gaussian, long tile lists, several sort blocks
+    s = scenes.random_scene(seed=3, n=1500, sh_degree=1, width=320, height=240, log_scale_range=(-2.5, -0.5))
+    note(f"large gaussians mode={mode}")
+    g, _, _ = _full_check(s.arrays(), 1, s.cameras[0], mode=mode)
+    assert g["num_dups"] > 50_000
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_c2_full_ints_sampled_image(mode):
+    s = scenes.make_scene("c2_100k_sh3_800")
+    cam = s.cameras[0]
+    rng = np.random.default_rng(0)
+    pix = rng.choice(cam["width"] * cam["height"], 4000, replace=False)
+    note(f"c2 mode={mode}")
+    g, _, err = _full_check(s.arrays(), 3, cam, mode=mode, full_image=False, pixels=pix)
+    note(f"c2 mode={mode} pairs={g['num_dups']} sampled err {err:.2e}")
+
+
+def test_c3_headline_full_ints_sampled_image():
+    s = scenes.make_scene("c3_1m_sh3_1080p")
+    cam = s.cameras[0]
+    rng = np.random.default_rng(1)
+    pix = rng.choice(cam["width"] * cam["height"], 1500, replace=False)
+    note("c3 depth-first")
+    g, _, err = _full_check(s.arrays(), 3, cam, mode=0, full_image=False, pixels=pix)
+    note(f"c3 pairs={g['num_dups']} sampled err {err:.2e}")
+
+
+def test_modes_agree_and_runs_are_deterministic():
+    s = scenes.random_scene(seed=77, n=20000, sh_degree=3, width=400, height=300)
+    cam = s.cameras[0]
+    a = gpu_run(s.arrays(), 3, cam, sort_mode=0)
+    b = gpu_run(s.arrays(), 3, cam, sort_mode=0)
+    c = gpu_run(s.arrays(), 3, cam, sort_mode=1)
+    for k in ("keys", "values", "ranges", "image", "T", "n_blend", "tile_count", "splat"):
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("keys", "values", "ranges"):
+        assert np.array_equal(a[k], c[k]), k
+    assert np.array_equal(a["image"], c["image"])
+
+
+def test_render_equals_staged_calls():
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    s = scenes.random_scene(seed=5, n=5000, sh_degree=2, width=130, height=77)
+    cam = s.cameras[0]
+    r = binding.Rasterizer()
+    dev = binding.gaussians_to_device(s.arrays())
+    img = r.render(dev, 2, cam, bg=(0.3, 0.1, 0.0)).clone()
+    pr = r.preprocess(dev, 2, cam)
+    bn = r.bin_and_sort(pr, cam)
+    img2 = r.composite(pr, bn, cam, bg=(0.3, 0.1, 0.0))
+    torch.cuda.synchronize()
+    assert torch.equal(img, img2)
+    r.close()
+
+
+# ---------------------------------------------------------------------------
+# degenerate and edge cases
+# ---------------------------------------------------------------------------
+
+def _arrays(means, quats, ls, op, sh):
+    return dict(mean=np.ascontiguousarray(np.asarray(means, np.float32).T),
+                quat=np.ascontiguousarray(np.asarray(quats, np.float32).T),
+                log_scale=np.ascontiguousarray(np.asarray(ls, np.float32).T),
+                opacity=np.asarray(op, np.float32),
+                sh=np.ascontiguousarray(np.asarray(sh, np.float32).reshape(len(op), -1).T))
+
+
+def _cam(w, h, f=None):
+    return dict(R=np.eye(3, dtype=np.float32), t=np.zeros(3, np.float32), fx=f or float(w), fy=f or float(w),
+                cx=w / 2.0, cy=h / 2.0, znear=0.2, width=w, height=h)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_empty_scene_gives_background(mode):
+    cam = _cam(40, 24)
+    g = gpu_run(scenes.empty_arrays(0), 0, cam, bg=(0.2, 0.4, 0.6), sort_mode=mode)
+    assert g["num_dups"] == 0
+    assert np.all(g["ranges"] == 0)
+    assert np.array_equal(g["image"], np.broadcast_to(np.float32([0.2, 0.4, 0.6]), (24, 40, 3)))
+    assert np.all(g["T"] == 1.0) and np.all(g["n_blend"] == 0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_everything_culled(mode):
+    n = 50
+    rng = np.random.default_rng(2)
+    means = np.c_[rng.uniform(-1, 1, (n, 2)), rng.uniform(-3, 0.1, n)]   # behind or inside the near plane
+    arr = _arrays(means, rng.standard_normal((n, 4)), np.full((n, 3), -2.0), np.full(n, 0.9), np.ones((n, 1, 3)))
+    cam = _cam(64, 64)
+    g = gpu_run(arr, 0, cam, bg=(1.0, 0.0, 0.5), sort_mode=mode)
+    assert g["num_dups"] == 0 and np.all(g["tile_count"] == 0)
+    assert np.array_equal(g["image"], np.broadcast_to(np.float32([1.0, 0.0, 0.5]), (64, 64, 3)))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_single_pixel_image_and_single_gaussian(mode):
+    arr = _arrays([[0, 0, 3.0]], [[1, 0, 0, 0]], [[-2, -2, -2]], [0.8], [[[1.0, 2.0, -1.0]]])
+    for w, h in ((1, 1), (17, 1), (1, 33), (16, 16), (17, 17)):
+        cam = _cam(w, h, f=30.0)
+        _full_check(arr, 0, cam, bg=(0.1, 0.1, 0.1), mode=mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_screen_filling_gaussians(mode):
+    # a few Gaussians whose rectangles cover every tile, plus small ones
+    rng = np.random.default_rng(9)
+    n = 300
+    means = np.c_[rng.uniform(-0.5, 0.5, (n, 2)), rng.uniform(2, 4, n)]
+    ls = np.full((n, 3), -3.0)
+    ls[:5] = 0.5
+    arr = _arrays(means, rng.standard_normal((n, 4)), ls, rng.uniform(0.05, 1.0, n), rng.normal(0, 0.5, (n, 4, 3)))
+    cam = _cam(150, 100, f=120.0)
+    g, o, _ = _full_check(arr, 1, cam, mode=mode)
+    tiles = math.ceil(150 / 16) * math.ceil(100 / 16)
+    assert (g["tile_count"] == tiles).sum() >= 5
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_equal_depths_keep_index_order(mode):
+    n = 40
+    rng = np.random.default_rng(4)
+    means = np.c_[rng.uniform(-0.3, 0.3, (n, 2)), np.full(n, 2.5)]
+    arr = _arrays(means, rng.standard_normal((n, 4)), np.full((n, 3), -2.5), np.full(n, 0.6),
+                  rng.normal(0, 0.5, (n, 1, 3)))
+    cam = _cam(48, 48, f=40.0)
+    g, o, _ = _full_check(arr, 0, cam, mode=mode)
+    assert len(np.unique(o["depth"][o["tile_count"] > 0])) < (o["tile_count"] > 0).sum()
+
+
+def test_opacity_zero_leaves_image_unchanged():
+    s = scenes.random_scene(seed=12, n=3000, sh_degree=0, width=96, height=96)
+    cam = s.cameras[0]
+    arr = s.arrays()
+    extra = {k: np.ascontiguousarray(np.concatenate([v, v[..., :500]], axis=-1)) for k, v in arr.items()}
+    extra["opacity"][-500:] = 0.0
+    a = gpu_run(arr, 0, cam)
+    b = gpu_run(extra, 0, cam)
+    assert np.array_equal(a["image"], b["image"])

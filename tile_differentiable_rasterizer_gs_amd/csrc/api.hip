@@ -1,0 +1,592 @@
+// C ABI of the rasterizer: context, argument checks, workspace and stage ordering.
+//
+// Stage order per frame (flowchart of the lesson "3D Gaussian Splatting from
+// scratch": project -> assign to 16x16 tiles -> depth-sort per tile ->
+// alpha-composite front to back):
+//   gs_preprocess    preprocess kernel
+//   gs_bin_and_sort  depth-first mode: radix sort of per-Gaussian depth keys,
+//                    prefix sum of tile counts in depth order, pair-count
+//                    read-back, pair listing in depth order, stable radix sort on
+//                    the tile id, tile ranges (+ optional 64-bit keys)
+//                    key64 mode: prefix sum, read-back, 64-bit key listing in
+//                    Gaussian order, radix sort over tile+depth bits, ranges
+//   gs_composite     one workgroup per tile
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "gs_internal.h"
+
+using namespace gsr;
+
+namespace {
+
+struct DeviceBuffer {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct TimedSpan {
+    int stage;
+    hipEvent_t begin, end;
+};
+
+}  // namespace
+
+struct gs_context {
+    int device = 0;
+    int sort_mode = GS_SORT_DEPTH_FIRST;
+    int emit_keys = 1;
+    int profile = 0;
+    int64_t max_dups = 0xffffffffll;
+    int64_t max_workspace = -1;
+    size_t workspace = 0;
+    char err[512] = {0};
+
+    // per-Gaussian
+    DeviceBuffer splat, depth, rect, tile_count, dkey[2], dval[2], offsets, scan_scratch, dsort_scratch, total;
+    // per-pair
+    DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch;
+    // per-tile
+    DeviceBuffer ranges;
+
+    unsigned long long *host_total = nullptr;   // pinned
+
+    // last gs_preprocess
+    int64_t n = -1;
+    int32_t tiles_x = 0, tiles_y = 0;
+    int last_sort_buffer = 0;
+    const uint32_t *sorted_values = nullptr;
+
+    std::vector<TimedSpan> spans;
+    size_t spans_used = 0;
+};
+
+namespace {
+
+gs_status fail(gs_context *ctx, gs_status st, const char *fmt, ...) {
+    if (ctx) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(ctx->err, sizeof(ctx->err), fmt, ap);
+        va_end(ap);
+    }
+    return st;
+}
+
+#define GS_HIP(ctx, expr)                                                                        \
+    do {                                                                                         \
+        hipError_t e_ = (expr);                                                                  \
+        if (e_ != hipSuccess)                                                                    \
+            return fail((ctx), GS_ERR_DEVICE, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+    } while (0)
+
+#define GS_TRY(expr)                      \
+    do {                                  \
+        gs_status s_ = (expr);            \
+        if (s_ != GS_OK) return s_;       \
+    } while (0)
+
+gs_status check_launch(gs_context *ctx, const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return GS_OK;
+}
+
+// Makes the context's device current for the scope of one entry point.
+struct DeviceScope {
+    int prev = -1;
+    hipError_t status = hipSuccess;
+    explicit DeviceScope(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) status = hipSetDevice(dev);
+    }
+    ~DeviceScope() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+gs_status ensure(gs_context *ctx, DeviceBuffer &b, size_t bytes) {
+    if (bytes <= b.bytes) return GS_OK;
+    size_t want = bytes + bytes / 4;                 // grow with headroom
+    want = (want + 255) & ~(size_t)255;
+    const size_t after = ctx->workspace - b.bytes + want;
+    if (ctx->max_workspace >= 0 && after > (size_t)ctx->max_workspace) {
+        if (ctx->workspace - b.bytes + bytes > (size_t)ctx->max_workspace)
+            return fail(ctx, GS_ERR_OUT_OF_MEMORY, "workspace limit %lld bytes exceeded (need %zu more)",
+                        (long long)ctx->max_workspace, bytes - b.bytes);
+        want = bytes;
+    }
+    if (b.ptr) {
+        GS_HIP(ctx, hipFree(b.ptr));
+        ctx->workspace -= b.bytes;
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    hipError_t e = hipMalloc(&b.ptr, want);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        b.ptr = nullptr;
+        return fail(ctx, GS_ERR_OUT_OF_MEMORY, "hipMalloc(%zu) failed: %s", want, hipGetErrorString(e));
+    }
+    b.bytes = want;
+    ctx->workspace += want;
+    return GS_OK;
+}
+
+template <typename T>
+T *as(DeviceBuffer &b) {
+    return reinterpret_cast<T *>(b.ptr);
+}
+
+// Profiling: HIP events around each stage, recorded on the caller's stream.
+gs_status span_begin(gs_context *ctx, int stage, hipStream_t s) {
+    if (!ctx->profile) return GS_OK;
+    if (ctx->spans_used == ctx->spans.size()) {
+        TimedSpan t{stage, nullptr, nullptr};
+        GS_HIP(ctx, hipEventCreate(&t.begin));
+        GS_HIP(ctx, hipEventCreate(&t.end));
+        ctx->spans.push_back(t);
+    }
+    TimedSpan &t = ctx->spans[ctx->spans_used];
+    t.stage = stage;
+    GS_HIP(ctx, hipEventRecord(t.begin, s));
+    return GS_OK;
+}
+
+gs_status span_end(gs_context *ctx, hipStream_t s) {
+    if (!ctx->profile) return GS_OK;
+    GS_HIP(ctx, hipEventRecord(ctx->spans[ctx->spans_used].end, s));
+    ++ctx->spans_used;
+    return GS_OK;
+}
+
+bool finite3(const float *v, int k) {
+    for (int i = 0; i < k; ++i)
+        if (!std::isfinite(v[i])) return false;
+    return true;
+}
+
+int ceil_log2(int64_t v) {
+    int b = 0;
+    while (((int64_t)1 << b) < v) ++b;
+    return b;
+}
+
+gs_status check_projected(gs_context *ctx, const gs_projected *pr) {
+    if (!pr) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "projected is NULL");
+    if (ctx->n < 0 || pr->n != ctx->n || pr->splat != as<float>(ctx->splat) || pr->tiles_x != ctx->tiles_x ||
+        pr->tiles_y != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "projected is not the last gs_preprocess output of this context");
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gs_status_string(gs_status st) {
+    switch (st) {
+        case GS_OK: return "ok";
+        case GS_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GS_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case GS_ERR_CAPACITY: return "pair capacity exceeded";
+        case GS_ERR_DEVICE: return "HIP device error";
+    }
+    return "unknown status";
+}
+
+const char *gs_last_error(const gs_context *ctx) { return ctx ? ctx->err : ""; }
+
+gs_status gs_check_arguments(const gs_gaussians *g, const gs_camera *cam, char *msg, size_t msg_len) {
+    const char *why = nullptr;
+    char buf[160];
+    if (g) {
+        if (g->n < 0 || g->n > 0x7fffffffll) {
+            snprintf(buf, sizeof buf, "gaussian count %lld outside [0, 2^31)", (long long)g->n);
+            why = buf;
+        } else if (g->sh_degree < 0 || g->sh_degree > 3) {
+            snprintf(buf, sizeof buf, "sh_degree %d outside [0, 3]", g->sh_degree);
+            why = buf;
+        } else if (g->n > 0 && (!g->mean || !g->quat || !g->log_scale || !g->opacity || !g->sh)) {
+            why = "a Gaussian parameter pointer is NULL";
+        }
+    }
+    if (!why && cam) {
+        if (cam->width < 1 || cam->height < 1 || cam->width > 32768 || cam->height > 32768)
+            why = "image size outside [1, 32768]";
+        else if (!finite3(cam->R, 9) || !finite3(cam->t, 3) || !std::isfinite(cam->fx) ||
+                 !std::isfinite(cam->fy) || !std::isfinite(cam->cx) || !std::isfinite(cam->cy) ||
+                 !std::isfinite(cam->znear))
+            why = "camera has a non-finite value";
+        else if (!(cam->fx > 0.0f) || !(cam->fy > 0.0f))
+            why = "focal lengths must be > 0";
+        else if (!(cam->znear > 0.0f))
+            why = "znear must be > 0";
+    }
+    if (!why) {
+        if (msg && msg_len) msg[0] = 0;
+        return GS_OK;
+    }
+    if (msg && msg_len) snprintf(msg, msg_len, "%s", why);
+    return GS_ERR_INVALID_ARGUMENT;
+}
+
+gs_status gs_context_create(gs_context **out, int device) {
+    if (!out) return GS_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) {
+        (void)hipGetLastError();
+        return GS_ERR_DEVICE;
+    }
+    gs_context *ctx = new gs_context();
+    ctx->device = device;
+    DeviceScope scope(device);
+    if (scope.status != hipSuccess ||
+        hipHostMalloc((void **)&ctx->host_total, sizeof(unsigned long long), hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        delete ctx;
+        return GS_ERR_DEVICE;
+    }
+    *out = ctx;
+    return GS_OK;
+}
+
+void gs_context_destroy(gs_context *ctx) {
+    if (!ctx) return;
+    DeviceScope scope(ctx->device);
+    DeviceBuffer *all[] = {&ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1],
+                           &ctx->dval[0], &ctx->dval[1], &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch,
+                           &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
+                           &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
+                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->ranges};
+    for (DeviceBuffer *b : all)
+        if (b->ptr) (void)hipFree(b->ptr);
+    for (TimedSpan &t : ctx->spans) {
+        (void)hipEventDestroy(t.begin);
+        (void)hipEventDestroy(t.end);
+    }
+    if (ctx->host_total) (void)hipHostFree(ctx->host_total);
+    delete ctx;
+}
+
+gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    switch (option) {
+        case GS_OPT_SORT_MODE:
+            if (value != GS_SORT_DEPTH_FIRST && value != GS_SORT_KEY64)
+                return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown sort mode %lld", (long long)value);
+            ctx->sort_mode = (int)value;
+            return GS_OK;
+        case GS_OPT_EMIT_KEYS:
+            if (value != 0 && value != 1) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "emit_keys must be 0 or 1");
+            ctx->emit_keys = (int)value;
+            return GS_OK;
+        case GS_OPT_MAX_DUPS:
+            if (value < 0 || value > 0xffffffffll)
+                return fail(ctx, GS_ERR_INVALID_ARGUMENT, "max_dups outside [0, 2^32-1]");
+            ctx->max_dups = value;
+            return GS_OK;
+        case GS_OPT_MAX_WORKSPACE_BYTES:
+            ctx->max_workspace = value < 0 ? -1 : value;
+            return GS_OK;
+        case GS_OPT_PROFILE:
+            if (value != 0 && value != 1) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "profile must be 0 or 1");
+            ctx->profile = (int)value;
+            return GS_OK;
+    }
+    return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
+}
+
+gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam, gs_projected *out,
+                        hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!g || !cam || !out) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL gaussians, camera or output");
+    char why[160];
+    if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+
+    const int64_t n = g->n;
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    GS_TRY(ensure(ctx, ctx->splat, nn * GS_SPLAT_STRIDE * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->depth, nn * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->rect, nn * sizeof(uint2)));
+    GS_TRY(ensure(ctx, ctx->tile_count, nn * sizeof(uint32_t)));
+    for (int i = 0; i < 2; ++i) {
+        GS_TRY(ensure(ctx, ctx->dkey[i], nn * sizeof(uint32_t)));
+        GS_TRY(ensure(ctx, ctx->dval[i], nn * sizeof(uint32_t)));
+    }
+
+    PreprocessParams p{};
+    p.n = (int32_t)n;
+    p.sh_coeffs = (g->sh_degree + 1) * (g->sh_degree + 1);
+    p.mean = g->mean;
+    p.quat = g->quat;
+    p.log_scale = g->log_scale;
+    p.opacity = g->opacity;
+    p.sh = g->sh;
+    memcpy(p.R, cam->R, sizeof p.R);
+    memcpy(p.t, cam->t, sizeof p.t);
+    p.fx = cam->fx;
+    p.fy = cam->fy;
+    p.cx = cam->cx;
+    p.cy = cam->cy;
+    p.znear = cam->znear;
+    for (int i = 0; i < 3; ++i)   // camera centre C = -R^T t
+        p.cam_pos[i] = (float)-((double)cam->R[i] * cam->t[0] + (double)cam->R[3 + i] * cam->t[1] +
+                                (double)cam->R[6 + i] * cam->t[2]);
+    p.tiles_x = (cam->width + GS_TILE - 1) / GS_TILE;
+    p.tiles_y = (cam->height + GS_TILE - 1) / GS_TILE;
+    p.splat = as<float>(ctx->splat);
+    p.depth = as<float>(ctx->depth);
+    p.rect = as<uint2>(ctx->rect);
+    p.tile_count = as<uint32_t>(ctx->tile_count);
+    p.depth_key = as<uint32_t>(ctx->dkey[0]);
+    p.depth_index = as<uint32_t>(ctx->dval[0]);
+
+    GS_TRY(span_begin(ctx, GS_STAGE_PREPROCESS, stream));
+    launch_preprocess(p, stream);
+    GS_TRY(check_launch(ctx, "preprocess"));
+    GS_TRY(span_end(ctx, stream));
+
+    ctx->n = n;
+    ctx->tiles_x = p.tiles_x;
+    ctx->tiles_y = p.tiles_y;
+    out->n = n;
+    out->tiles_x = p.tiles_x;
+    out->tiles_y = p.tiles_y;
+    out->splat = p.splat;
+    out->depth = p.depth;
+    out->rect = reinterpret_cast<const uint16_t *>(p.rect);
+    out->tile_count = p.tile_count;
+    return GS_OK;
+}
+
+static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_keys, gs_binning *out,
+                              hipStream_t stream) {
+    const int64_t n = ctx->n;
+    const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
+    const bool depth_first = ctx->sort_mode == GS_SORT_DEPTH_FIRST;
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    GS_TRY(ensure(ctx, ctx->offsets, nn * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->scan_scratch, (size_t)scan_scratch_words((int64_t)nn) * 8));
+    GS_TRY(ensure(ctx, ctx->total, 8));
+    GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
+    unsigned long long *d_total = as<unsigned long long>(ctx->total);
+
+    const uint32_t *order = nullptr;
+    int64_t M = 0;
+    if (n > 0) {
+        if (depth_first) {
+            GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 8));
+            GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
+            const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
+                                                       as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n, 0,
+                                                       32, as<unsigned long long>(ctx->dsort_scratch), stream);
+            GS_TRY(check_launch(ctx, "depth sort"));
+            GS_TRY(span_end(ctx, stream));
+            order = as<uint32_t>(ctx->dval[buf]);
+        }
+        GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
+        launch_scan(pr->tile_count, order, as<uint32_t>(ctx->offsets), n, d_total,
+                    as<unsigned long long>(ctx->scan_scratch), stream);
+        GS_TRY(check_launch(ctx, "scan"));
+        GS_TRY(span_end(ctx, stream));
+
+        GS_TRY(span_begin(ctx, GS_STAGE_READBACK, stream));
+        GS_HIP(ctx, hipMemcpyAsync(ctx->host_total, d_total, 8, hipMemcpyDeviceToHost, stream));
+        GS_TRY(span_end(ctx, stream));
+        GS_HIP(ctx, hipStreamSynchronize(stream));
+        M = (int64_t)*ctx->host_total;
+        if (M > ctx->max_dups)
+            return fail(ctx, GS_ERR_CAPACITY, "%lld (Gaussian, tile) pairs exceed the cap of %lld", (long long)M,
+                        (long long)ctx->max_dups);
+    }
+
+    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+    launch_fill_u32(as<uint32_t>(ctx->ranges), 0u, tiles * 2, stream);
+    GS_TRY(check_launch(ctx, "fill"));
+    GS_TRY(span_end(ctx, stream));
+
+    out->num_dups = M;
+    out->tiles_x = ctx->tiles_x;
+    out->tiles_y = ctx->tiles_y;
+    out->tile_ranges = as<uint32_t>(ctx->ranges);
+    out->keys = nullptr;
+    out->values = nullptr;
+    out->keys_unsorted = nullptr;
+    out->values_unsorted = nullptr;
+    ctx->sorted_values = nullptr;
+    if (M == 0) return GS_OK;
+
+    const size_t mm = (size_t)M;
+    GS_TRY(ensure(ctx, ctx->pval[0], mm * 4));
+    GS_TRY(ensure(ctx, ctx->pval[1], mm * 4));
+    GS_TRY(ensure(ctx, ctx->psort_scratch, (size_t)sort_scratch_words(M) * 8));
+    const int tile_bits = ceil_log2(tiles);
+
+    DuplicateParams d{};
+    d.n_items = n;
+    d.num_dups = M;
+    d.offsets = as<uint32_t>(ctx->offsets);
+    d.order = order;
+    d.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    d.depth = pr->depth;
+    d.tiles_x = ctx->tiles_x;
+    d.values = as<uint32_t>(ctx->pval[0]);
+    RangesParams r{};
+    r.num_dups = M;
+    r.ranges = as<uint32_t>(ctx->ranges);
+    int buf = 0;
+    if (depth_first) {
+        GS_TRY(ensure(ctx, ctx->pkey32[0], mm * 4));
+        GS_TRY(ensure(ctx, ctx->pkey32[1], mm * 4));
+        d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
+        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
+        launch_duplicate(d, stream);
+        GS_TRY(check_launch(ctx, "duplicate"));
+        GS_TRY(span_end(ctx, stream));
+        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
+        buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
+                                         as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), M, 0, tile_bits,
+                                         as<unsigned long long>(ctx->psort_scratch), stream);
+        GS_TRY(check_launch(ctx, "tile sort"));
+        GS_TRY(span_end(ctx, stream));
+        r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
+        if (emit_keys) {
+            GS_TRY(ensure(ctx, ctx->keys_out, mm * 8));
+            r.keys_out = as<uint64_t>(ctx->keys_out);
+            r.values = as<uint32_t>(ctx->pval[buf]);
+            r.depth = pr->depth;
+            out->keys = r.keys_out;
+        }
+    } else {
+        GS_TRY(ensure(ctx, ctx->pkey64[0], mm * 8));
+        GS_TRY(ensure(ctx, ctx->pkey64[1], mm * 8));
+        d.keys64 = as<uint64_t>(ctx->pkey64[0]);
+        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
+        launch_duplicate(d, stream);
+        GS_TRY(check_launch(ctx, "duplicate"));
+        GS_TRY(span_end(ctx, stream));
+        if (emit_keys) {
+            GS_TRY(ensure(ctx, ctx->keys_unsorted, mm * 8));
+            GS_TRY(ensure(ctx, ctx->vals_unsorted, mm * 4));
+            GS_HIP(ctx, hipMemcpyAsync(ctx->keys_unsorted.ptr, d.keys64, mm * 8, hipMemcpyDeviceToDevice, stream));
+            GS_HIP(ctx, hipMemcpyAsync(ctx->vals_unsorted.ptr, d.values, mm * 4, hipMemcpyDeviceToDevice, stream));
+            out->keys_unsorted = as<uint64_t>(ctx->keys_unsorted);
+            out->values_unsorted = as<uint32_t>(ctx->vals_unsorted);
+        }
+        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
+        buf = radix_sort_pairs<uint64_t>(as<uint64_t>(ctx->pkey64[0]), as<uint32_t>(ctx->pval[0]),
+                                         as<uint64_t>(ctx->pkey64[1]), as<uint32_t>(ctx->pval[1]), M, 0,
+                                         32 + tile_bits, as<unsigned long long>(ctx->psort_scratch), stream);
+        GS_TRY(check_launch(ctx, "key sort"));
+        GS_TRY(span_end(ctx, stream));
+        r.keys64 = as<uint64_t>(ctx->pkey64[buf]);
+        out->keys = r.keys64;
+    }
+    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+    launch_ranges(r, stream);
+    GS_TRY(check_launch(ctx, "ranges"));
+    GS_TRY(span_end(ctx, stream));
+    ctx->sorted_values = as<uint32_t>(ctx->pval[buf]);
+    out->values = ctx->sorted_values;
+    return GS_OK;
+}
+
+gs_status gs_bin_and_sort(gs_context *ctx, const gs_projected *pr, const gs_camera *cam, gs_binning *out,
+                          hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!out || !cam) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL camera or output");
+    char why[160];
+    if (gs_check_arguments(nullptr, cam, why, sizeof why) != GS_OK)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    GS_TRY(check_projected(ctx, pr));
+    if ((cam->width + GS_TILE - 1) / GS_TILE != ctx->tiles_x || (cam->height + GS_TILE - 1) / GS_TILE != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "camera size differs from the one given to gs_preprocess");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    return bin_and_sort(ctx, pr, ctx->emit_keys, out, stream);
+}
+
+gs_status gs_composite_ex(gs_context *ctx, const gs_projected *pr, const gs_binning *bin, const gs_camera *cam,
+                          const float bg[3], float *image, float *final_T, uint32_t *n_blend,
+                          unsigned long long *blend_total, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!bin || !cam || !bg || !image) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL binning, camera, bg or image");
+    char why[160];
+    if (gs_check_arguments(nullptr, cam, why, sizeof why) != GS_OK)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    GS_TRY(check_projected(ctx, pr));
+    if (bin->tile_ranges != as<uint32_t>(ctx->ranges) || bin->values != ctx->sorted_values ||
+        bin->tiles_x != ctx->tiles_x || bin->tiles_y != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "binning is not the last gs_bin_and_sort output of this context");
+    if ((cam->width + GS_TILE - 1) / GS_TILE != ctx->tiles_x || (cam->height + GS_TILE - 1) / GS_TILE != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "camera size differs from the one given to gs_preprocess");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    CompositeParams c{};
+    c.width = cam->width;
+    c.height = cam->height;
+    c.tiles_x = ctx->tiles_x;
+    c.tiles_y = ctx->tiles_y;
+    c.splat = pr->splat;
+    c.values = bin->values;
+    c.ranges = bin->tile_ranges;
+    for (int i = 0; i < 3; ++i) c.bg[i] = bg[i];
+    c.image = image;
+    c.final_T = final_T;
+    c.n_blend = n_blend;
+    c.blend_total = blend_total;
+    GS_TRY(span_begin(ctx, GS_STAGE_COMPOSITE, stream));
+    launch_composite(c, stream);
+    GS_TRY(check_launch(ctx, "composite"));
+    GS_TRY(span_end(ctx, stream));
+    return GS_OK;
+}
+
+gs_status gs_composite(gs_context *ctx, const gs_projected *pr, const gs_binning *bin, const gs_camera *cam,
+                       const float bg[3], float *image, hipStream_t stream) {
+    return gs_composite_ex(ctx, pr, bin, cam, bg, image, nullptr, nullptr, nullptr, stream);
+}
+
+gs_status gs_render(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam, const float bg[3], float *image,
+                    hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!bg || !image) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL bg or image");
+    gs_projected pr;
+    GS_TRY(gs_preprocess(ctx, g, cam, &pr, stream));
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    gs_binning bin;
+    GS_TRY(bin_and_sort(ctx, &pr, 0, &bin, stream));
+    return gs_composite(ctx, &pr, &bin, cam, bg, image, stream);
+}
+
+gs_status gs_profile_read(gs_context *ctx, gs_profile *out) {
+    if (!ctx || !out) return GS_ERR_INVALID_ARGUMENT;
+    DeviceScope scope(ctx->device);
+    for (int i = 0; i < GS_STAGE_COUNT; ++i) {
+        out->ms[i] = 0.0;
+        out->launches[i] = 0;
+    }
+    for (size_t i = 0; i < ctx->spans_used; ++i) {
+        TimedSpan &t = ctx->spans[i];
+        GS_HIP(ctx, hipEventSynchronize(t.end));
+        float ms = 0.0f;
+        GS_HIP(ctx, hipEventElapsedTime(&ms, t.begin, t.end));
+        out->ms[t.stage] += ms;
+        out->launches[t.stage] += 1;
+    }
+    ctx->spans_used = 0;
+    return GS_OK;
+}
+
+}  // extern "C"

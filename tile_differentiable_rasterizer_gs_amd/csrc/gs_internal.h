@@ -1,0 +1,108 @@
+// Internal declarations of the HIP rasterizer library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gsrast.h"
+
+namespace gsr {
+
+constexpr int kTile = GS_TILE;
+constexpr int kBlock = 256;      // threads per workgroup for every kernel (4 wave64)
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// preprocess
+// ---------------------------------------------------------------------------
+struct PreprocessParams {
+    int32_t n;
+    int32_t sh_coeffs;           // K = (degree+1)^2
+    const float *mean, *quat, *log_scale, *opacity, *sh;
+    float R[9];
+    float t[3];
+    float fx, fy, cx, cy, znear;
+    float cam_pos[3];            // camera centre in world space (colour direction)
+    int32_t tiles_x, tiles_y;
+    float *splat;                // [n][GS_SPLAT_STRIDE]
+    float *depth;                // [n]
+    uint2 *rect;                 // [n] {x0 | x1 << 16, y0 | y1 << 16}
+    uint32_t *tile_count;        // [n]
+    uint32_t *depth_key;         // [n] or null: visible ? bits(depth) : 0xffffffff
+    uint32_t *depth_index;       // [n] or null: g
+};
+void launch_preprocess(const PreprocessParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// exclusive prefix sum of uint32 values (optionally gathered in[gather[i]])
+// ---------------------------------------------------------------------------
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kBlock * kScanItems;   // 4096 values per workgroup
+// number of uint64 scratch words launch_scan needs for n values
+int64_t scan_scratch_words(int64_t n);
+// out[i] = sum_{j<i} in[j]; *total = sum of all (device uint64).  n >= 1.
+void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
+                 unsigned long long *total, unsigned long long *scratch, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// stable LSD radix sort of (key, uint32 value) pairs
+// ---------------------------------------------------------------------------
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kBlock * kSortItems;   // 4096 pairs per workgroup
+constexpr int kRadixBits = 8;
+int64_t sort_scratch_words(int64_t n);           // uint64 words (histograms + scan scratch)
+// Sorts by key bits [begin_bit, end_bit).  Ping-pongs between (k0,v0) and (k1,v1);
+// returns 0 if the result is in (k0,v0), 1 if in (k1,v1).  `on_pass` timing hooks
+// are driven by the caller through the profiler, see api.hip.
+template <typename K>
+int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit,
+                     int end_bit, unsigned long long *scratch, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// pair listing, ranges
+// ---------------------------------------------------------------------------
+struct DuplicateParams {
+    int64_t n_items;             // number of (ranked) Gaussians
+    int64_t num_dups;
+    const uint32_t *offsets;     // [n_items] exclusive prefix of tile counts (in rank order)
+    const uint32_t *order;       // [n_items] rank -> Gaussian index, or null (rank = index)
+    const uint2 *rect;
+    const float *depth;
+    int32_t tiles_x;
+    uint64_t *keys64;            // key64 mode: (tile << 32) | bits(depth)
+    uint32_t *tile_keys;         // depth-first mode: tile id
+    uint32_t *values;            // Gaussian index
+};
+void launch_duplicate(const DuplicateParams &p, hipStream_t s);
+
+struct RangesParams {
+    int64_t num_dups;
+    const uint64_t *keys64;      // either keys64 (tile = key >> 32) ...
+    const uint32_t *tile_keys;   // ... or tile ids
+    uint32_t *ranges;            // [tiles][2], zeroed beforehand
+    // optional key emission (depth-first mode): keys_out[e] = tile << 32 | bits(depth[values[e]])
+    const uint32_t *values;
+    const float *depth;
+    uint64_t *keys_out;
+};
+void launch_ranges(const RangesParams &p, hipStream_t s);
+void launch_fill_u32(uint32_t *dst, uint32_t value, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// compositing
+// ---------------------------------------------------------------------------
+struct CompositeParams {
+    int32_t width, height, tiles_x, tiles_y;
+    const float *splat;
+    const uint32_t *values;
+    const uint32_t *ranges;
+    float bg[3];
+    float *image;                // [H][W][3]
+    float *final_T;              // optional [H][W]
+    uint32_t *n_blend;           // optional [H][W]
+    unsigned long long *blend_total;  // optional
+};
+void launch_composite(const CompositeParams &p, hipStream_t s);
+
+}  // namespace gsr
