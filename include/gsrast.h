@@ -152,7 +152,7 @@ typedef enum {
 typedef enum {
     GS_OPT_SORT_MODE = 0,            /* gs_sort_mode, default GS_SORT_DEPTH_FIRST */
     GS_OPT_EMIT_KEYS = 1,            /* 1: gs_bin_and_sort materialises keys (default 1); gs_render never does */
-    GS_OPT_MAX_DUPS = 2,             /* cap on pairs per frame (default 2^32-1) -> GS_ERR_CAPACITY */
+    GS_OPT_MAX_DUPS = 2,             /* cap on pairs per frame, at most and by default 2^32-1 -> GS_ERR_CAPACITY */
     GS_OPT_MAX_WORKSPACE_BYTES = 3,  /* cap on context device memory (default: none) -> GS_ERR_OUT_OF_MEMORY */
     GS_OPT_PROFILE = 4               /* 1: bracket every kernel with HIP events (see gs_profile_read) */
 } gs_option;

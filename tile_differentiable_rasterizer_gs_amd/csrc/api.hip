@@ -25,6 +25,9 @@ using namespace gsr;
 
 namespace {
 
+// pair indices are uint32 throughout
+constexpr int64_t kMaxPairs = 0xffffffffll;
+
 struct DeviceBuffer {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -42,7 +45,7 @@ struct gs_context {
     int sort_mode = GS_SORT_DEPTH_FIRST;
     int emit_keys = 1;
     int profile = 0;
-    int64_t max_dups = 0xffffffffll;
+    int64_t max_dups = kMaxPairs;
     int64_t max_workspace = -1;
     size_t workspace = 0;
     char err[512] = {0};
@@ -50,11 +53,11 @@ struct gs_context {
     // per-Gaussian
     DeviceBuffer splat, depth, rect, tile_count, dkey[2], dval[2], offsets, scan_scratch, dsort_scratch, total;
     // per-pair
-    DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch;
+    DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
     DeviceBuffer ranges;
 
-    unsigned long long *host_total = nullptr;   // pinned
+    unsigned long long *host_total = nullptr;   // pinned: pair count read back once per frame
 
     // last gs_preprocess
     int64_t n = -1;
@@ -265,7 +268,7 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->dval[0], &ctx->dval[1], &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch,
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
-                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->ranges};
+                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -289,7 +292,7 @@ gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
             ctx->emit_keys = (int)value;
             return GS_OK;
         case GS_OPT_MAX_DUPS:
-            if (value < 0 || value > 0xffffffffll)
+            if (value < 0 || value > kMaxPairs)
                 return fail(ctx, GS_ERR_INVALID_ARGUMENT, "max_dups outside [0, 2^32-1]");
             ctx->max_dups = value;
             return GS_OK;
@@ -385,11 +388,11 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     int64_t M = 0;
     if (n > 0) {
         if (depth_first) {
-            GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 8));
+            GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 4));
             GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
             const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
                                                        as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n, 0,
-                                                       32, as<unsigned long long>(ctx->dsort_scratch), stream);
+                                                       32, as<uint32_t>(ctx->dsort_scratch), stream);
             GS_TRY(check_launch(ctx, "depth sort"));
             GS_TRY(span_end(ctx, stream));
             order = as<uint32_t>(ctx->dval[buf]);
@@ -429,8 +432,9 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     const size_t mm = (size_t)M;
     GS_TRY(ensure(ctx, ctx->pval[0], mm * 4));
     GS_TRY(ensure(ctx, ctx->pval[1], mm * 4));
-    GS_TRY(ensure(ctx, ctx->psort_scratch, (size_t)sort_scratch_words(M) * 8));
     const int tile_bits = ceil_log2(tiles);
+    GS_TRY(ensure(ctx, ctx->psort_scratch, (size_t)sort_scratch_words(M) * 4));
+    GS_TRY(ensure(ctx, ctx->part, (size_t)duplicate_partition_words(M) * 4));
 
     DuplicateParams d{};
     d.n_items = n;
@@ -450,13 +454,13 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         GS_TRY(ensure(ctx, ctx->pkey32[1], mm * 4));
         d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
         GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-        launch_duplicate(d, stream);
+        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
         GS_TRY(check_launch(ctx, "duplicate"));
         GS_TRY(span_end(ctx, stream));
         GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
         buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
                                          as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), M, 0, tile_bits,
-                                         as<unsigned long long>(ctx->psort_scratch), stream);
+                                         as<uint32_t>(ctx->psort_scratch), stream);
         GS_TRY(check_launch(ctx, "tile sort"));
         GS_TRY(span_end(ctx, stream));
         r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
@@ -472,7 +476,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         GS_TRY(ensure(ctx, ctx->pkey64[1], mm * 8));
         d.keys64 = as<uint64_t>(ctx->pkey64[0]);
         GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-        launch_duplicate(d, stream);
+        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
         GS_TRY(check_launch(ctx, "duplicate"));
         GS_TRY(span_end(ctx, stream));
         if (emit_keys) {
@@ -486,7 +490,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
         buf = radix_sort_pairs<uint64_t>(as<uint64_t>(ctx->pkey64[0]), as<uint32_t>(ctx->pval[0]),
                                          as<uint64_t>(ctx->pkey64[1]), as<uint32_t>(ctx->pval[1]), M, 0,
-                                         32 + tile_bits, as<unsigned long long>(ctx->psort_scratch), stream);
+                                         32 + tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
         GS_TRY(check_launch(ctx, "key sort"));
         GS_TRY(span_end(ctx, stream));
         r.keys64 = as<uint64_t>(ctx->pkey64[buf]);

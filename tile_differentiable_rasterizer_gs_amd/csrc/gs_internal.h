@@ -48,16 +48,14 @@ void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int6
 // ---------------------------------------------------------------------------
 // stable LSD radix sort of (key, uint32 value) pairs
 // ---------------------------------------------------------------------------
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kBlock * kSortItems;   // 4096 pairs per workgroup
 constexpr int kRadixBits = 8;
-int64_t sort_scratch_words(int64_t n);           // uint64 words (histograms + scan scratch)
-// Sorts by key bits [begin_bit, end_bit).  Ping-pongs between (k0,v0) and (k1,v1);
-// returns 0 if the result is in (k0,v0), 1 if in (k1,v1).  `on_pass` timing hooks
-// are driven by the caller through the profiler, see api.hip.
+// uint32 scratch words radix_sort_pairs needs for n pairs
+int64_t sort_scratch_words(int64_t n);
+// Stable sort by key bits [begin_bit, end_bit), ping-ponging between (k0,v0) and (k1,v1);
+// returns 0 if the result is in (k0,v0), 1 if in (k1,v1).
 template <typename K>
-int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit,
-                     int end_bit, unsigned long long *scratch, hipStream_t s);
+int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit, int end_bit,
+                     uint32_t *scratch, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // pair listing, ranges
@@ -74,7 +72,9 @@ struct DuplicateParams {
     uint32_t *tile_keys;         // depth-first mode: tile id
     uint32_t *values;            // Gaussian index
 };
-void launch_duplicate(const DuplicateParams &p, hipStream_t s);
+// uint32 words of the partition table launch_duplicate needs
+int64_t duplicate_partition_words(int64_t num_dups);
+void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s);
 
 struct RangesParams {
     int64_t num_dups;

@@ -6,149 +6,203 @@
 // depths by Gaussian index.  The key of a pair is (tile_id << 32) | bits(depth);
 // for depth > 0 the IEEE bit pattern orders like the value.
 //
-// Radix sort, one pass per 8-bit digit, three kernels per pass:
-//   histogram  per-workgroup digit counts (LDS atomics), digit-major layout
-//   scan       exclusive prefix of the counts = global start of (digit, workgroup)
-//   scatter    stable rank of every pair inside its workgroup, staged in LDS so the
-//              global writes run in contiguous digit segments
-// Stable ranking inside a wave64 uses a ballot per key bit to find the lanes that
-// share a digit (the leader adds the group size to the wave's LDS counter);
-// workgroup order is wave-major, so the pass preserves input order on ties.
-// HBM traffic per pass and pair: read key+value twice (histogram + scatter),
-// write once.
+// Radix sort: 8-bit digits, least significant first, three kernels per digit on a
+// fixed grid of G workgroups, each owning one contiguous range of the input:
+//   count   per-range digit counts, counts[d][range]
+//   scan    one workgroup per digit: exclusive prefix over ranges, plus the digit total
+//   scatter each range walks its 4096-pair tiles in order; a tile ranks its keys
+//           stably in LDS (a ballot per key bit finds the lanes of a wave that
+//           share a digit) and writes them through LDS in contiguous digit runs at
+//           running per-digit offsets.
+// Ranges and tiles are processed in input order, so equal digits keep their
+// order.  No workgroup waits on another (communication only across kernel
+// boundaries): on MI355X the L2s of the eight XCDs are not coherent with each
+// other, so polling another workgroup's results costs a fabric round trip.
+// HBM traffic per pass and pair: read the key (count), read key+value and write
+// key+value (scatter).
 #include "gs_internal.h"
 
 namespace gsr {
 namespace {
+
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kBlock * kSortItems;   // 4096 pairs per tile
+constexpr int kMaxSortGroups = 1024;             // workgroups per pass (4 per CU)
 
 template <typename K>
 __device__ inline uint32_t digit_of(K key, int shift, uint32_t mask) {
     return (uint32_t)(key >> shift) & mask;
 }
 
-template <typename K>
-__global__ __launch_bounds__(kBlock) void radix_histogram_kernel(const K *keys, int64_t n, int shift, int bits,
-                                                                 uint32_t *hist, int64_t nblocks) {
-    __shared__ uint32_t counts[kBlock / kWave][1 << kRadixBits];
-    const int radix = 1 << bits;
-    const uint32_t mask = radix - 1;
-    const int wave = threadIdx.x / kWave;
-    for (int i = threadIdx.x; i < (kBlock / kWave) * (1 << kRadixBits); i += kBlock) (&counts[0][0])[i] = 0;
+__device__ inline uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Workgroup exclusive scan over threadIdx.x of one uint32 per thread.
+__device__ inline uint32_t block_exclusive_scan_u32(uint32_t x, uint32_t *s_tmp /*[4]*/) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) s_tmp[wave] = inc;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-#pragma unroll 4
-    for (int k = 0; k < kSortItems; ++k) {
-        const int64_t i = base + (int64_t)k * kBlock + threadIdx.x;
-        if (i < n) atomicAdd(&counts[wave][digit_of(keys[i], shift, mask)], 1u);
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w)
+        if (w < wave) before += s_tmp[w];
+    __syncthreads();
+    return before + inc - x;
+}
+
+// Range of the input owned by workgroup `group` (tiles of kSortTile pairs).
+__device__ inline void group_range(int64_t n, int groups, int group, int64_t *lo, int64_t *hi) {
+    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    const int64_t per = (tiles + groups - 1) / groups;
+    *lo = min<int64_t>(n, (int64_t)group * per * kSortTile);
+    *hi = min<int64_t>(n, (int64_t)(group + 1) * per * kSortTile);
+}
+
+template <typename K>
+__global__ __launch_bounds__(kBlock) void radix_count_kernel(const K *keys, int64_t n, int shift, int bits,
+                                                             uint32_t *counts /*[radix][groups]*/) {
+    constexpr int kWaves = kBlock / kWave;
+    __shared__ uint32_t s_count[kWaves][kRadix];
+    const int wave = threadIdx.x / kWave;
+    const uint32_t mask = (1u << bits) - 1;
+    for (int i = threadIdx.x; i < kWaves * kRadix; i += kBlock) (&s_count[0][0])[i] = 0;
+    __syncthreads();
+    int64_t lo, hi;
+    group_range(n, gridDim.x, blockIdx.x, &lo, &hi);
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * kBlock) {
+        K k[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) k[u] = i + u * kBlock < hi ? keys[i + u * kBlock] : K(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i + u * kBlock < hi) atomicAdd(&s_count[wave][digit_of(k[u], shift, mask)], 1u);
     }
     __syncthreads();
-    if ((int)threadIdx.x < radix) {
+    if ((int)threadIdx.x <= (int)mask) {
         uint32_t c = 0;
 #pragma unroll
-        for (int w = 0; w < kBlock / kWave; ++w) c += counts[w][threadIdx.x];
-        hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = c;
+        for (int w = 0; w < kWaves; ++w) c += s_count[w][threadIdx.x];
+        counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = c;
     }
 }
 
-__device__ inline uint32_t lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+// One workgroup per digit d: counts[d][*] -> exclusive prefix over ranges; totals[d].
+__global__ __launch_bounds__(kBlock) void radix_digit_scan_kernel(uint32_t *counts, int groups, uint32_t *totals) {
+    __shared__ uint32_t s_tmp[kBlock / kWave];
+    uint32_t *row = counts + (int64_t)blockIdx.x * groups;
+    constexpr int kPer = kMaxSortGroups / kBlock;   // groups <= kMaxSortGroups
+    uint32_t v[kPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int g = threadIdx.x * kPer + k;
+        v[k] = g < groups ? row[g] : 0u;
+        sum += v[k];
+    }
+    uint32_t run = block_exclusive_scan_u32(sum, s_tmp);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int g = threadIdx.x * kPer + k;
+        if (g < groups) row[g] = run;
+        run += v[k];
+    }
+    if (threadIdx.x == kBlock - 1) totals[blockIdx.x] = run;
 }
 
 template <typename K>
 __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in, const uint32_t *vals_in,
                                                                K *keys_out, uint32_t *vals_out, int64_t n,
-                                                               int shift, int bits, const uint32_t *offsets,
-                                                               int64_t nblocks) {
+                                                               int shift, int bits, const uint32_t *counts,
+                                                               const uint32_t *totals) {
     constexpr int kWaves = kBlock / kWave;
-    constexpr int kRadix = 1 << kRadixBits;
     __shared__ K s_keys[kSortTile];
     __shared__ uint32_t s_vals[kSortTile];
     __shared__ uint32_t s_wave_count[kWaves][kRadix];   // per-wave running counts, then wave prefixes
-    __shared__ uint32_t s_local_start[kRadix];          // start of each digit inside the workgroup
-    __shared__ uint32_t s_global_start[kRadix];         // global start of (digit, this workgroup)
-    __shared__ uint32_t s_wave_tot[kWaves];
+    __shared__ uint32_t s_local_start[kRadix];          // start of each digit inside the tile
+    __shared__ uint32_t s_next[kRadix];                 // next global position of each digit (this range)
+    __shared__ uint32_t s_tmp[kWaves];
 
     const int radix = 1 << bits;
     const uint32_t mask = radix - 1;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int i = threadIdx.x; i < kWaves * kRadix; i += kBlock) (&s_wave_count[0][0])[i] = 0;
-    if ((int)threadIdx.x < radix) s_global_start[threadIdx.x] = offsets[(int64_t)threadIdx.x * nblocks + blockIdx.x];
-    __syncthreads();
-
-    // wave w owns the contiguous segment [w*1024, (w+1)*1024) of the tile, in rounds of 64
-    const int64_t seg = (int64_t)blockIdx.x * kSortTile + (int64_t)wave * (kSortItems * kWave);
-    K key[kSortItems];
-    uint32_t val[kSortItems];
-#pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
-        const int64_t i = seg + r * kWave + lane;
-        key[r] = i < n ? keys_in[i] : (K)0;
-        val[r] = i < n ? vals_in[i] : 0u;
+    {
+        // global start of (digit, range) = exclusive prefix of digit totals + prefix over ranges
+        const uint32_t tot = (int)threadIdx.x < radix ? totals[threadIdx.x] : 0u;
+        const uint32_t base = block_exclusive_scan_u32(tot, s_tmp);
+        if ((int)threadIdx.x < radix) s_next[threadIdx.x] = base + counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x];
     }
-    uint32_t rank[kSortItems];
+    int64_t lo, hi;
+    group_range(n, gridDim.x, blockIdx.x, &lo, &hi);
+    for (int64_t tile = lo; tile < hi; tile += kSortTile) {
+        for (int i = threadIdx.x; i < kWaves * kRadix; i += kBlock) (&s_wave_count[0][0])[i] = 0;
+        __syncthreads();
+        // wave w owns the contiguous segment [w*1024, (w+1)*1024) of the tile, in rounds of 64
+        const int64_t seg = tile + (int64_t)wave * (kSortItems * kWave);
+        K key[kSortItems];
+        uint32_t val[kSortItems];
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
-        const bool valid = seg + r * kWave + lane < n;
-        const uint32_t d = digit_of(key[r], shift, mask);
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < bits; ++b) {
-            const bool bit = (d >> b) & 1u;
-            const uint64_t on = __ballot(bit);
-            peers &= bit ? on : ~on;
+        for (int r = 0; r < kSortItems; ++r) {
+            const int64_t i = seg + r * kWave + lane;
+            key[r] = i < hi ? keys_in[i] : (K)0;
+            val[r] = i < hi ? vals_in[i] : 0u;
         }
-        const uint32_t below = lanes_below(peers);
-        const uint32_t prev = valid ? s_wave_count[wave][d] : 0u;
-        rank[r] = prev + below;
-        if (valid && below == 0) s_wave_count[wave][d] = prev + (uint32_t)__popcll(peers);
-        __builtin_amdgcn_wave_barrier();
-    }
-    __syncthreads();
-
-    // per digit: exclusive prefix over waves, then over digits (workgroup-local start)
-    uint32_t digit_total = 0;
-    if ((int)threadIdx.x < kRadix) {
+        uint32_t rank[kSortItems];
+#pragma unroll
+        for (int r = 0; r < kSortItems; ++r) {
+            const bool valid = seg + r * kWave + lane < hi;
+            const uint32_t d = digit_of(key[r], shift, mask);
+            uint64_t peers = __ballot(valid);
+            for (int b = 0; b < bits; ++b) {
+                const bool bit = (d >> b) & 1u;
+                const uint64_t on = __ballot(bit);
+                peers &= bit ? on : ~on;
+            }
+            const uint32_t below = lanes_below(peers);
+            const uint32_t prev = valid ? s_wave_count[wave][d] : 0u;
+            rank[r] = prev + below;
+            if (valid && below == 0) s_wave_count[wave][d] = prev + (uint32_t)__popcll(peers);
+            __builtin_amdgcn_wave_barrier();
+        }
+        __syncthreads();
+        // thread = digit: wave prefixes and the tile's count of that digit
+        uint32_t tile_count = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const uint32_t c = s_wave_count[w][threadIdx.x];
-            s_wave_count[w][threadIdx.x] = digit_total;
-            digit_total += c;
+            s_wave_count[w][threadIdx.x] = tile_count;
+            tile_count += c;
         }
-    }
-    {
-        // workgroup exclusive scan of digit_total over threadIdx.x (= digit)
-        uint32_t inc = digit_total;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t y = __shfl_up(inc, d, kWave);
-            if (lane >= d) inc += y;
-        }
-        if (lane == kWave - 1) s_wave_tot[wave] = inc;
+        const uint32_t local_start = block_exclusive_scan_u32(tile_count, s_tmp);   // barriers inside
+        s_local_start[threadIdx.x] = local_start;
         __syncthreads();
-        uint32_t before = 0;
-        for (int w = 0; w < wave; ++w) before += s_wave_tot[w];
-        if ((int)threadIdx.x < kRadix) s_local_start[threadIdx.x] = before + inc - digit_total;
-    }
-    __syncthreads();
-
 #pragma unroll
-    for (int r = 0; r < kSortItems; ++r) {
-        if (seg + r * kWave + lane < n) {
-            const uint32_t d = digit_of(key[r], shift, mask);
-            const uint32_t pos = s_local_start[d] + s_wave_count[wave][d] + rank[r];
-            s_keys[pos] = key[r];
-            s_vals[pos] = val[r];
+        for (int r = 0; r < kSortItems; ++r) {
+            if (seg + r * kWave + lane < hi) {
+                const uint32_t d = digit_of(key[r], shift, mask);
+                const uint32_t pos = s_local_start[d] + s_wave_count[wave][d] + rank[r];
+                s_keys[pos] = key[r];
+                s_vals[pos] = val[r];
+            }
         }
-    }
-    __syncthreads();
-
-    const int64_t tile_base = (int64_t)blockIdx.x * kSortTile;
-    const int count = (int)min<int64_t>(kSortTile, n - tile_base);
-    for (int p = threadIdx.x; p < count; p += kBlock) {
-        const K k = s_keys[p];
-        const uint32_t d = digit_of(k, shift, mask);
-        const int64_t dst = (int64_t)s_global_start[d] + (p - (int64_t)s_local_start[d]);
-        keys_out[dst] = k;
-        vals_out[dst] = s_vals[p];
+        __syncthreads();
+        const int count = (int)min<int64_t>(kSortTile, hi - tile);
+        for (int q = threadIdx.x; q < count; q += kBlock) {
+            const K k = s_keys[q];
+            const uint32_t d = digit_of(k, shift, mask);
+            const int64_t dst = (int64_t)s_next[d] + (q - (int64_t)s_local_start[d]);
+            keys_out[dst] = k;
+            vals_out[dst] = s_vals[q];
+        }
+        __syncthreads();
+        s_next[threadIdx.x] += tile_count;   // every thread owns one digit slot
     }
 }
 
@@ -157,10 +211,21 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
 // offsets[i] <= e < offsets[i+1]; its tiles run row-major over the rectangle.
 // ---------------------------------------------------------------------------
 constexpr int kDupItems = 8;
-constexpr int kDupTile = kBlock * kDupItems;
+constexpr int kDupTile = kBlock * kDupItems;   // 2048 entries per workgroup
+constexpr int kDupWindow = kDupTile + 1;
 
-__device__ inline int64_t last_le(const uint32_t *offsets, int64_t lo, int64_t hi, uint32_t e) {
-    // largest i in [lo, hi] with offsets[i] <= e  (offsets non-decreasing, offsets[lo] <= e)
+// part[b] = rank whose pairs contain entry b * kDupTile.
+__global__ __launch_bounds__(kBlock) void partition_kernel(const uint32_t *offsets, int64_t n, int64_t num_dups,
+                                                           uint32_t *part) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    const int64_t start = offsets[i];
+    const int64_t end = i + 1 < n ? (int64_t)offsets[i + 1] : num_dups;
+    for (int64_t b = (start + kDupTile - 1) / kDupTile; b * kDupTile < end; ++b) part[b] = (uint32_t)i;
+    if (start < end && end == num_dups) part[(num_dups + kDupTile - 1) / kDupTile] = (uint32_t)i;
+}
+
+__device__ inline int64_t last_le_global(const uint32_t *offsets, int64_t lo, int64_t hi, uint32_t e) {
     while (lo < hi) {
         const int64_t mid = lo + (hi - lo + 1) / 2;
         if (offsets[mid] <= e) lo = mid; else hi = mid - 1;
@@ -168,42 +233,138 @@ __device__ inline int64_t last_le(const uint32_t *offsets, int64_t lo, int64_t h
     return lo;
 }
 
-__global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p) {
-    __shared__ int64_t s_window[2];
+// Workgroup b lists entries [b*2048, (b+1)*2048).  The ranks whose pairs meet that
+// span are staged in LDS; each thread then takes 8 consecutive entries: one
+// binary search for the first, then it walks the rectangles row-major.
+__global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, const uint32_t *part) {
+    __shared__ uint32_t s_off[kDupWindow];
+    __shared__ uint32_t s_g[kDupWindow];
+    __shared__ uint2 s_rect[kDupWindow];
+    __shared__ uint32_t s_depth[kDupWindow];
     const int64_t first = (int64_t)blockIdx.x * kDupTile;
-    const int64_t last = min<int64_t>(first + kDupTile, p.num_dups) - 1;
-    if (threadIdx.x == 0) s_window[0] = last_le(p.offsets, 0, p.n_items - 1, (uint32_t)first);
-    if (threadIdx.x == 1) s_window[1] = last_le(p.offsets, 0, p.n_items - 1, (uint32_t)last);
+    const int64_t lo = part[blockIdx.x];
+    const int64_t hi = part[blockIdx.x + 1];   // rank of entry (b+1)*kDupTile, or of the last entry
+    const int64_t window = hi - lo + 1;
+    const bool staged = window <= kDupWindow;
+    if (staged) {
+        for (int64_t k = threadIdx.x; k < window; k += kBlock) {
+            const int64_t i = lo + k;
+            const uint32_t g = p.order ? p.order[i] : (uint32_t)i;
+            s_off[k] = p.offsets[i];
+            s_g[k] = g;
+            s_rect[k] = p.rect[g];
+            if (p.keys64) s_depth[k] = __float_as_uint(p.depth[g]);
+        }
+    }
     __syncthreads();
-    const int64_t lo = s_window[0], hi = s_window[1];
+    const int64_t e0 = first + (int64_t)threadIdx.x * kDupItems;
+    if (e0 >= p.num_dups) return;
+    const int n_here = (int)min<int64_t>(kDupItems, p.num_dups - e0);
+
+    // rank holding e0
+    int64_t i;
+    if (staged) {
+        int a = 0, b = (int)window - 1;
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (s_off[mid] <= (uint32_t)e0) a = mid; else b = mid - 1;
+        }
+        i = a;
+    } else {
+        i = last_le_global(p.offsets, lo, hi, (uint32_t)e0) - lo;
+    }
+    auto load_rank = [&](int64_t k, uint32_t &g, uint32_t &off, uint2 &rc, uint32_t &db) {
+        if (staged) {
+            g = s_g[k];
+            off = s_off[k];
+            rc = s_rect[k];
+            db = p.keys64 ? s_depth[k] : 0u;
+        } else {
+            const int64_t r = lo + k;
+            g = p.order ? p.order[r] : (uint32_t)r;
+            off = p.offsets[r];
+            rc = p.rect[g];
+            db = p.keys64 ? __float_as_uint(p.depth[g]) : 0u;
+        }
+    };
+    uint32_t g, off, dbits;
+    uint2 rc;
+    load_rank(i, g, off, rc, dbits);
+    uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu, h = (rc.y >> 16) - y0;
+    uint32_t j = (uint32_t)e0 - off;
+    uint32_t row = j / w, col = j - row * w;
+    uint32_t tiles[kDupItems], gs[kDupItems], dbs[kDupItems];
 #pragma unroll
     for (int k = 0; k < kDupItems; ++k) {
-        const int64_t e = first + (int64_t)k * kBlock + threadIdx.x;
-        if (e > last) break;
-        const int64_t i = last_le(p.offsets, lo, hi, (uint32_t)e);
-        const uint32_t g = p.order ? p.order[i] : (uint32_t)i;
-        const uint32_t j = (uint32_t)e - p.offsets[i];
-        const uint2 rc = p.rect[g];
-        const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-        const uint32_t w = x1 - x0;
-        const uint32_t row = j / w;
-        const uint32_t tile = (y0 + row) * (uint32_t)p.tiles_x + x0 + (j - row * w);
-        if (p.keys64) p.keys64[e] = ((uint64_t)tile << 32) | __float_as_uint(p.depth[g]);
-        if (p.tile_keys) p.tile_keys[e] = tile;
-        p.values[e] = g;
+        if (k < n_here) {
+            tiles[k] = (y0 + row) * (uint32_t)p.tiles_x + x0 + col;
+            gs[k] = g;
+            dbs[k] = dbits;
+            if (++col == w) {
+                col = 0;
+                if (++row == h && k + 1 < n_here) {
+                    // next rank with pairs (ranks without pairs own no entries)
+                    do {
+                        ++i;
+                        load_rank(i, g, off, rc, dbits);
+                    } while (((rc.x >> 16) - (rc.x & 0xffffu)) * ((rc.y >> 16) - (rc.y & 0xffffu)) == 0);
+                    x0 = rc.x & 0xffffu;
+                    w = (rc.x >> 16) - x0;
+                    y0 = rc.y & 0xffffu;
+                    h = (rc.y >> 16) - y0;
+                    row = 0;
+                }
+            }
+        }
+    }
+    if (n_here == kDupItems) {
+        uint4 *vo = reinterpret_cast<uint4 *>(p.values + e0);
+        vo[0] = make_uint4(gs[0], gs[1], gs[2], gs[3]);
+        vo[1] = make_uint4(gs[4], gs[5], gs[6], gs[7]);
+        if (p.tile_keys) {
+            uint4 *to = reinterpret_cast<uint4 *>(p.tile_keys + e0);
+            to[0] = make_uint4(tiles[0], tiles[1], tiles[2], tiles[3]);
+            to[1] = make_uint4(tiles[4], tiles[5], tiles[6], tiles[7]);
+        }
+        if (p.keys64) {
+#pragma unroll
+            for (int k = 0; k < kDupItems; ++k) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
+        }
+    } else {
+        for (int k = 0; k < n_here; ++k) {
+            p.values[e0 + k] = gs[k];
+            if (p.tile_keys) p.tile_keys[e0 + k] = tiles[k];
+            if (p.keys64) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
+        }
     }
 }
 
+// ranges from sorted tiles: 4 consecutive entries per thread
+constexpr int kRangeItems = 4;
+
+template <bool kKey64>
 __global__ __launch_bounds__(kBlock) void ranges_kernel(RangesParams p) {
-    const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (e >= p.num_dups) return;
-    auto tile_at = [&](int64_t i) -> uint32_t {
-        return p.keys64 ? (uint32_t)(p.keys64[i] >> 32) : p.tile_keys[i];
-    };
-    const uint32_t t = tile_at(e);
-    if (e == 0 || tile_at(e - 1) != t) p.ranges[2 * (int64_t)t] = (uint32_t)e;
-    if (e == p.num_dups - 1 || tile_at(e + 1) != t) p.ranges[2 * (int64_t)t + 1] = (uint32_t)(e + 1);
-    if (p.keys_out) p.keys_out[e] = ((uint64_t)t << 32) | __float_as_uint(p.depth[p.values[e]]);
+    const int64_t e0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kRangeItems;
+    if (e0 >= p.num_dups) return;
+    uint32_t t[kRangeItems + 1];
+    const int cnt = (int)min<int64_t>(kRangeItems, p.num_dups - e0);
+#pragma unroll
+    for (int k = 0; k <= kRangeItems; ++k) {
+        const int64_t e = e0 + k;
+        t[k] = 0xffffffffu;
+        if (k <= cnt && e < p.num_dups)
+            t[k] = kKey64 ? (uint32_t)(p.keys64[e] >> 32) : p.tile_keys[e];
+    }
+    const uint32_t prev = e0 == 0 ? 0xffffffffu : (kKey64 ? (uint32_t)(p.keys64[e0 - 1] >> 32) : p.tile_keys[e0 - 1]);
+#pragma unroll
+    for (int k = 0; k < kRangeItems; ++k) {
+        if (k >= cnt) break;
+        const int64_t e = e0 + k;
+        const uint32_t before = k == 0 ? prev : t[k - 1];
+        if (before != t[k]) p.ranges[2 * (int64_t)t[k]] = (uint32_t)e;
+        if (t[k + 1] != t[k]) p.ranges[2 * (int64_t)t[k] + 1] = (uint32_t)(e + 1);
+        if (p.keys_out) p.keys_out[e] = ((uint64_t)t[k] << 32) | __float_as_uint(p.depth[p.values[e]]);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void fill_u32_kernel(uint32_t *dst, uint32_t value, int64_t n) {
@@ -211,53 +372,63 @@ __global__ __launch_bounds__(kBlock) void fill_u32_kernel(uint32_t *dst, uint32_
     if (i < n) dst[i] = value;
 }
 
-inline int64_t sort_blocks(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
+inline int passes_for(int begin_bit, int end_bit) { return (end_bit - begin_bit + kRadixBits - 1) / kRadixBits; }
+
+inline int sort_groups(int64_t n) {
+    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    return (int)(tiles < 1 ? 1 : (tiles > kMaxSortGroups ? kMaxSortGroups : tiles));
+}
 
 }  // namespace
 
-int64_t sort_scratch_words(int64_t n) {
-    const int64_t hist = (int64_t)(1 << kRadixBits) * sort_blocks(n);
-    return (hist + 1) / 2 + scan_scratch_words(hist) + 1;
-}
+int64_t sort_scratch_words(int64_t n) { return (int64_t)kRadix * sort_groups(n) + kRadix; }
 
 template <typename K>
 int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit, int end_bit,
-                     unsigned long long *scratch, hipStream_t s) {
+                     uint32_t *scratch, hipStream_t s) {
     if (n <= 1 || end_bit <= begin_bit) return 0;
-    const int64_t nb = sort_blocks(n);
-    uint32_t *hist = reinterpret_cast<uint32_t *>(scratch);
-    const int64_t hist_words64 = ((int64_t)(1 << kRadixBits) * nb + 1) / 2;
-    unsigned long long *scan_scratch = scratch + hist_words64 + 1;
-    unsigned long long *scan_total = scratch + hist_words64;
+    const int groups = sort_groups(n);
+    uint32_t *counts = scratch;
+    uint32_t *totals = counts + (int64_t)kRadix * groups;
     int cur = 0;
-    for (int bit = begin_bit; bit < end_bit; bit += kRadixBits) {
-        const int bits = min(kRadixBits, end_bit - bit);
+    for (int p = 0; p < passes_for(begin_bit, end_bit); ++p) {
+        const int shift = begin_bit + p * kRadixBits;
+        const int bits = min(kRadixBits, end_bit - shift);
         K *ki = cur ? k1 : k0;
         uint32_t *vi = cur ? v1 : v0;
         K *ko = cur ? k0 : k1;
         uint32_t *vo = cur ? v0 : v1;
-        radix_histogram_kernel<K><<<(unsigned)nb, kBlock, 0, s>>>(ki, n, bit, bits, hist, nb);
-        launch_scan(hist, nullptr, hist, (int64_t)(1 << bits) * nb, scan_total, scan_scratch, s);
-        radix_scatter_kernel<K><<<(unsigned)nb, kBlock, 0, s>>>(ki, vi, ko, vo, n, bit, bits, hist, nb);
+        radix_count_kernel<K><<<groups, kBlock, 0, s>>>(ki, n, shift, bits, counts);
+        radix_digit_scan_kernel<<<1 << bits, kBlock, 0, s>>>(counts, groups, totals);
+        radix_scatter_kernel<K><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, shift, bits, counts, totals);
         cur ^= 1;
     }
     return cur;
 }
 
 template int radix_sort_pairs<uint32_t>(uint32_t *, uint32_t *, uint32_t *, uint32_t *, int64_t, int, int,
-                                        unsigned long long *, hipStream_t);
+                                        uint32_t *, hipStream_t);
 template int radix_sort_pairs<uint64_t>(uint64_t *, uint32_t *, uint64_t *, uint32_t *, int64_t, int, int,
-                                        unsigned long long *, hipStream_t);
+                                        uint32_t *, hipStream_t);
 
-void launch_duplicate(const DuplicateParams &p, hipStream_t s) {
+int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTile - 1) / kDupTile + 1; }
+
+void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
     if (p.num_dups <= 0) return;
+    partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(p.offsets, p.n_items,
+                                                                                       p.num_dups, part);
     const int64_t nb = (p.num_dups + kDupTile - 1) / kDupTile;
-    duplicate_kernel<<<(unsigned)nb, kBlock, 0, s>>>(p);
+    duplicate_kernel<<<(unsigned)nb, kBlock, 0, s>>>(p, part);
 }
 
 void launch_ranges(const RangesParams &p, hipStream_t s) {
     if (p.num_dups <= 0) return;
-    ranges_kernel<<<(unsigned)((p.num_dups + kBlock - 1) / kBlock), kBlock, 0, s>>>(p);
+    const int64_t threads = (p.num_dups + kRangeItems - 1) / kRangeItems;
+    const unsigned grid = (unsigned)((threads + kBlock - 1) / kBlock);
+    if (p.keys64)
+        ranges_kernel<true><<<grid, kBlock, 0, s>>>(p);
+    else
+        ranges_kernel<false><<<grid, kBlock, 0, s>>>(p);
 }
 
 void launch_fill_u32(uint32_t *dst, uint32_t value, int64_t n, hipStream_t s) {
