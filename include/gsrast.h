@@ -54,7 +54,7 @@ typedef enum {
 /* A pixel stops after the blend that brings its transmittance below this. */
 #define GS_T_EPS 1e-4f
 /* Floats per projected-splat record (see gs_projected.splat). */
-#define GS_SPLAT_STRIDE 12
+#define GS_SPLAT_STRIDE 16
 
 /*
  * Gaussian parameters, structure of arrays, fp32, device memory, index g in
@@ -95,13 +95,15 @@ typedef struct {
 
 /*
  * Output of gs_preprocess (views into context memory, device pointers).
- *   splat [n][GS_SPLAT_STRIDE] fp32 records:
+ *   splat [n][GS_SPLAT_STRIDE] fp32 records (64 bytes):
  *          0 u, 1 v            projected mean in pixels
- *          2 A, 3 B, 4 C       conic = inverse 2D covariance: q = A dx^2 + 2 B dx dy + C dy^2
- *          5 opacity
+ *          2 opacity
+ *          3, 4, 5             -log2(e)/2 * (A, 2B, C): alpha = opacity * 2^(f3 dx^2 + f4 dx dy + f5 dy^2)
  *          6 r, 7 g, 8 b       SH colour in the view direction
  *          9 radius            ceil(3 sqrt(largest eigenvalue of the 2D covariance))
- *          10, 11              unused
+ *          10 A, 11 B, 12 C    conic = inverse 2D covariance: q = A dx^2 + 2 B dx dy + C dy^2
+ *          13 depth            camera-space z (same as depth[g])
+ *          14, 15              unused
  *   depth      [n] camera-space z
  *   rect       [n][4] uint16: x0, x1, y0, y1 tile rectangle, half-open
  *   tile_count [n] (x1-x0)*(y1-y0) for a visible Gaussian, else 0

@@ -67,8 +67,9 @@ def check_preprocess(g: dict, o: dict):
     assert np.array_equal(sp[vis, 0].view(np.uint32), o["mean2d"][0, vis].view(np.uint32)), "u"
     assert np.array_equal(sp[vis, 1].view(np.uint32), o["mean2d"][1, vis].view(np.uint32)), "v"
     for k in range(3):
-        assert np.array_equal(sp[vis, 2 + k].view(np.uint32), o["conic"][k, vis].view(np.uint32)), f"conic {k}"
-    assert np.array_equal(sp[vis, 5], o["opacity"][vis]), "opacity"
+        assert np.array_equal(sp[vis, 10 + k].view(np.uint32), o["conic"][k, vis].view(np.uint32)), f"conic {k}"
+    assert np.array_equal(sp[vis, 2], o["opacity"][vis]), "opacity"
+    assert np.array_equal(sp[vis, 13].view(np.uint32), o["depth"][vis].view(np.uint32)), "record depth"
     assert np.array_equal(sp[vis, 9], o["radius"][vis]), "radius"
     if vis.any():
         err = np.abs(sp[vis, 6:9].astype(np.float64) - o["rgb"][:, vis].T).max()

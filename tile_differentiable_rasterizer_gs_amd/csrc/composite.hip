@@ -1,92 +1,168 @@
-// Front-to-back alpha compositing, one 256-thread workgroup (four wave64) per 16x16 tile.
+// Front-to-back alpha compositing, one 128-thread workgroup (two wave64) per 16x16 tile.
 //
 // Lesson "3D Gaussian Splatting from scratch", section "La règle de composition
 // alpha": C = sum_i alpha_i T_i c_i with T_i = prod_{j<i} (1 - alpha_j) and
 // alpha_i = o_i exp(-d^T Sigma'^-1 d / 2); section "Étape 2" clamps alpha to at
 // most 0.99 and samples pixel (row i, column j) at (x = j, y = i).
 //
-// Each thread owns one pixel.  The tile's depth-sorted list is walked in batches
-// of 256 splats: every thread gathers one splat record into LDS, then all threads
-// read the batch back as wave-wide broadcasts.  A pixel stops after the blend that
-// brings T below GS_T_EPS; a wave whose 64 pixels have all stopped skips the rest
-// of the batch, and the workgroup leaves the list once a barrier count shows no
-// live pixel.  Pure VALU work (one v_exp_f32 per pair): no dense contraction, so no
-// MFMA.
+// The tile's depth-sorted list is walked in batches of 256 splats.  The workgroup
+// gathers a batch into LDS (double-buffered: the global loads of the next batch are
+// in flight while the current one is blended) and every lane reads each splat back
+// as a wave-wide LDS broadcast.  A lane owns the two pixels (x, y) and (x + 8, y),
+// which share dy, B'dy and C'dy^2 + log2(o), so a pair costs about 14 VALU ops:
+//   q = (A' dx + B' dy) dx + C' dy^2 + log2 o,  alpha = min(0.99, 2^q)
+// with (A', B', C') = -log2(e)/2 (A, 2B, C).  A pixel stops after the blend that
+// brings T below GS_T_EPS; the blend is branchless (a stopped pixel blends with T
+// masked to 0).  A wave leaves a batch once none of its 128 pixels is live (tested
+// every 8 splats) and the workgroup leaves the list when a barrier count finds no
+// live pixel.  Pure VALU work (one v_exp_f32 per pair): no dense contraction, so
+// no MFMA.
 #include "gs_internal.h"
 
 namespace gsr {
 namespace {
 
-template <bool kAux>
-__global__ __launch_bounds__(kBlock) void composite_kernel(CompositeParams p) {
-    // batch of splats in LDS; conic pre-scaled so that alpha = o * exp2(A dx^2 + B dx dy + C dy^2)
-    __shared__ float s_u[kBlock], s_v[kBlock], s_A[kBlock], s_B[kBlock], s_C[kBlock], s_o[kBlock];
-    __shared__ float s_r[kBlock], s_g[kBlock], s_b[kBlock];
+constexpr int kThreads = 128;                // 64 lanes x 2 pixels = one 16x8 half tile per wave
+constexpr int kBatch = 256;                  // splats per LDS batch
+constexpr int kLoads = kBatch / kThreads;    // records gathered per thread per batch
+constexpr int kUnroll = 8;                   // splats between wave exit tests
 
+struct Staged {
+    float4 a[kLoads];   // u, v, log2(opacity), A'
+    float4 b[kLoads];   // B', C', r, g
+    float c[kLoads];    // b
+};
+
+__device__ __forceinline__ void gather(Staged &st, const float *__restrict__ splat,
+                                       const uint32_t *__restrict__ values, uint32_t base, uint32_t end) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const uint32_t idx = base + k * kThreads + threadIdx.x;
+        if (idx < end) {
+            const float4 *rec = reinterpret_cast<const float4 *>(splat) + (size_t)values[idx] * 4;
+            const float4 r0 = rec[0], r1 = rec[1];
+            st.a[k] = make_float4(r0.x, r0.y, __log2f(r0.z), r0.w);
+            st.b[k] = r1;
+            st.c[k] = rec[2].x;
+        }
+    }
+}
+
+template <bool kAux>
+struct Pixels {
+    float x0, x1, y;
+    float T[2], r[2], g[2], b[2];
+    uint32_t blended[2];
+
+    __device__ __forceinline__ void blend(const float4 a, const float4 b4, const float c) {
+        const float dy = y - a.y;
+        const float bdy = b4.x * dy;
+        const float e = (b4.y * dy) * dy + a.z;   // C' dy^2 + log2 o
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float dx = (i ? x1 : x0) - a.x;
+            const float q = (a.w * dx + bdy) * dx + e;
+            const float alpha = fminf(GS_ALPHA_MAX, __builtin_amdgcn_exp2f(q));
+            const bool live = T[i] >= GS_T_EPS;
+            const float w = (live ? T[i] : 0.0f) * alpha;
+            r[i] += w * b4.z;
+            g[i] += w * b4.w;
+            b[i] += w * c;
+            T[i] -= w;
+            if (kAux) blended[i] += live ? 1u : 0u;
+        }
+    }
+    __device__ __forceinline__ bool live() const { return (T[0] >= GS_T_EPS) | (T[1] >= GS_T_EPS); }
+};
+
+template <bool kAux>
+__global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) {
+    __shared__ float4 s_a[2][kBatch], s_b[2][kBatch];
+    __shared__ float s_c[2][kBatch];
+    const float *__restrict__ splat = p.splat;
+    const uint32_t *__restrict__ values = p.values;
     const int tile = blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
-    const int px = tile_x * kTile + (threadIdx.x & (kTile - 1));
-    const int py = tile_y * kTile + (threadIdx.x / kTile);
-    const bool inside = px < p.width && py < p.height;
-    const float fx = (float)px, fy = (float)py;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int ix = tile_x * kTile + (lane & 7);
+    const int iy = tile_y * kTile + wave * 8 + (lane >> 3);
 
-    const uint32_t start = p.ranges[2 * tile], end = p.ranges[2 * tile + 1];
-    float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
-    uint32_t blended = 0;
-    bool done = !inside;
-    constexpr float kLog2e = 1.4426950408889634f;
-
-    for (uint32_t base = start; base < end; base += kBlock) {
-        const uint32_t idx = base + threadIdx.x;
-        if (idx < end) {
-            const uint32_t gi = p.values[idx];
-            const float4 *rec = reinterpret_cast<const float4 *>(p.splat) + (size_t)gi * 3;
-            const float4 a = rec[0], b = rec[1], c = rec[2];
-            s_u[threadIdx.x] = a.x;
-            s_v[threadIdx.x] = a.y;
-            s_A[threadIdx.x] = -0.5f * kLog2e * a.z;
-            s_B[threadIdx.x] = -kLog2e * a.w;
-            s_C[threadIdx.x] = -0.5f * kLog2e * b.x;
-            s_o[threadIdx.x] = b.y;
-            s_r[threadIdx.x] = b.z;
-            s_g[threadIdx.x] = b.w;
-            s_b[threadIdx.x] = c.x;
-        }
-        __syncthreads();
-        const int count = (int)min<uint32_t>(kBlock, end - base);
-        for (int j = 0; j < count; ++j) {
-            if (__all(done)) break;
-            const float dx = fx - s_u[j], dy = fy - s_v[j];
-            const float q = s_A[j] * dx * dx + s_B[j] * dx * dy + s_C[j] * dy * dy;
-            const float alpha = fminf(GS_ALPHA_MAX, s_o[j] * __builtin_amdgcn_exp2f(q));
-            if (!done) {
-                const float w = T * alpha;
-                cr += w * s_r[j];
-                cg += w * s_g[j];
-                cb += w * s_b[j];
-                T -= w;
-                if (kAux) ++blended;
-                done = T < GS_T_EPS;
-            }
-        }
-        if (__syncthreads_count(!done) == 0) break;
+    Pixels<kAux> px;
+    px.x0 = (float)ix;
+    px.x1 = (float)(ix + 8);
+    px.y = (float)iy;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        px.T[i] = (ix + 8 * i < p.width && iy < p.height) ? 1.0f : 0.0f;
+        px.r[i] = px.g[i] = px.b[i] = 0.0f;
+        px.blended[i] = 0u;
     }
 
-    if (inside) {
-        const size_t pix = (size_t)py * p.width + px;
-        p.image[pix * 3 + 0] = cr + T * p.bg[0];
-        p.image[pix * 3 + 1] = cg + T * p.bg[1];
-        p.image[pix * 3 + 2] = cb + T * p.bg[2];
-        if (kAux) {
-            if (p.final_T) p.final_T[pix] = T;
-            if (p.n_blend) p.n_blend[pix] = blended;
+    const uint32_t start = p.ranges[2 * tile], end = p.ranges[2 * tile + 1];
+    Staged st;
+    int buf = 0;
+    if (start < end) {
+        gather(st, splat, values, start, end);
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            s_a[0][k * kThreads + threadIdx.x] = st.a[k];
+            s_b[0][k * kThreads + threadIdx.x] = st.b[k];
+            s_c[0][k * kThreads + threadIdx.x] = st.c[k];
         }
+    }
+    __syncthreads();
+    for (uint32_t base = start; base < end; base += kBatch) {
+        const uint32_t next = base + kBatch;
+        if (next < end) gather(st, splat, values, next, end);   // in flight during the blends below
+        const int count = (int)min<uint32_t>(kBatch, end - base);
+        const float4 *sa = s_a[buf];
+        const float4 *sb = s_b[buf];
+        const float *sc = s_c[buf];
+        int j = 0;
+        bool wave_live = true;
+        for (; j + kUnroll <= count; j += kUnroll) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) px.blend(sa[j + u], sb[j + u], sc[j + u]);
+            if (!__any(px.live())) {
+                wave_live = false;
+                break;
+            }
+        }
+        if (wave_live)
+            for (; j < count; ++j) px.blend(sa[j], sb[j], sc[j]);
+        if (next < end) {
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) {
+                s_a[buf ^ 1][k * kThreads + threadIdx.x] = st.a[k];
+                s_b[buf ^ 1][k * kThreads + threadIdx.x] = st.b[k];
+                s_c[buf ^ 1][k * kThreads + threadIdx.x] = st.c[k];
+            }
+        }
+        if (__syncthreads_count(px.live()) == 0) break;
+        buf ^= 1;
+    }
+
+    uint32_t total = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int x = ix + 8 * i;
+        if (x < p.width && iy < p.height) {
+            const size_t pix = (size_t)iy * p.width + x;
+            p.image[pix * 3 + 0] = px.r[i] + px.T[i] * p.bg[0];
+            p.image[pix * 3 + 1] = px.g[i] + px.T[i] * p.bg[1];
+            p.image[pix * 3 + 2] = px.b[i] + px.T[i] * p.bg[2];
+            if (kAux) {
+                if (p.final_T) p.final_T[pix] = px.T[i];
+                if (p.n_blend) p.n_blend[pix] = px.blended[i];
+            }
+        }
+        total += px.blended[i];
     }
     if (kAux && p.blend_total) {
         __shared__ unsigned long long s_sum;
         if (threadIdx.x == 0) s_sum = 0;
         __syncthreads();
-        atomicAdd(&s_sum, (unsigned long long)blended);
+        atomicAdd(&s_sum, (unsigned long long)total);
         __syncthreads();
         if (threadIdx.x == 0 && s_sum) atomicAdd(p.blend_total, s_sum);
     }
@@ -98,9 +174,9 @@ void launch_composite(const CompositeParams &p, hipStream_t s) {
     const unsigned tiles = (unsigned)(p.tiles_x * p.tiles_y);
     if (tiles == 0) return;
     if (p.final_T || p.n_blend || p.blend_total)
-        composite_kernel<true><<<tiles, kBlock, 0, s>>>(p);
+        composite_kernel<true><<<tiles, kThreads, 0, s>>>(p);
     else
-        composite_kernel<false><<<tiles, kBlock, 0, s>>>(p);
+        composite_kernel<false><<<tiles, kThreads, 0, s>>>(p);
 }
 
 }  // namespace gsr

@@ -13,7 +13,7 @@
 // on any IEEE-754 implementation that follows the same operation order.
 //
 // Memory: structure-of-arrays planes, one coalesced fp32 load per plane per thread.
-// Reads 56 B (SH0) .. 236 B (SH3) per Gaussian, writes 64 B (+8 B for the
+// Reads 56 B (SH0) .. 236 B (SH3) per Gaussian, writes 80 B (+8 B for the
 // depth-first sort keys).  HBM-bound; no LDS, no MFMA.
 #include "gs_internal.h"
 
@@ -159,10 +159,14 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
             for (int ch = 0; ch < 3; ++ch) rgb[ch] += Y[k] * p.sh[(size_t)(k * 3 + ch) * n + g];
     }
 
-    float4 *rec = reinterpret_cast<float4 *>(p.splat) + (size_t)g * 3;
-    rec[0] = make_float4(u, v, A, B);
-    rec[1] = make_float4(C, opac, rgb[0], rgb[1]);
-    rec[2] = make_float4(rgb[2], radius, 0.0f, 0.0f);
+    // record: what compositing reads first (conic pre-scaled so alpha = o * exp2(A' dx^2 + B' dx dy + C' dy^2)),
+    // then the exact conic, radius and depth
+    constexpr float kNegHalfLog2e = -0.72134752044448170f;   // -log2(e) / 2
+    float4 *rec = reinterpret_cast<float4 *>(p.splat) + (size_t)g * 4;
+    rec[0] = make_float4(u, v, opac, kNegHalfLog2e * A);
+    rec[1] = make_float4(2.0f * kNegHalfLog2e * B, kNegHalfLog2e * C, rgb[0], rgb[1]);
+    rec[2] = make_float4(rgb[2], radius, A, B);
+    rec[3] = make_float4(C, tz, 0.0f, 0.0f);
     p.depth[g] = tz;
     p.rect[g] = make_uint2(x0 | (x1 << 16), y0 | (y1 << 16));
     p.tile_count[g] = visible ? (x1 - x0) * (y1 - y0) : 0u;
