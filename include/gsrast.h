@@ -19,8 +19,11 @@
  *    Arguments are validated on the host before any HIP call, so
  *    GS_ERR_INVALID_ARGUMENT leaves the device untouched.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
- *    gs_bin_and_sort and gs_render synchronise that stream once per call to
- *    read back the number of (Gaussian, tile) pairs; all other calls are
+ *    gs_bin_and_sort and gs_render wait, once per call, until the number of
+ *    (Gaussian, tile) pairs has been copied to the host.  The pair kernels are
+ *    enqueued before that wait on buffers sized from earlier calls, so the GPU
+ *    does not idle; when the count exceeds that capacity the buffers grow and
+ *    the pair kernels run again before the call returns.  All other calls are
  *    asynchronous.
  *  - One context per host thread / stream at a time; a context is not
  *    thread-safe.  Views returned in gs_projected / gs_binning point into
@@ -123,7 +126,8 @@ typedef struct {
  * One entry per (visible Gaussian, tile of its rectangle); num_dups entries.
  *   keys        [num_dups] (tile_id << 32) | bit pattern of the fp32 depth,
  *               tile_id = ty * tiles_x + tx; ascending, equal keys ordered by
- *               ascending Gaussian index.  NULL when GS_OPT_EMIT_KEYS is 0.
+ *               ascending Gaussian index.  NULL in GS_SORT_DEPTH_FIRST mode when
+ *               GS_OPT_EMIT_KEYS is 0.
  *   values      [num_dups] Gaussian index of each sorted entry
  *   tile_ranges [tiles_x*tiles_y][2] half-open [start, end) into keys/values;
  *               (0, 0) for a tile no Gaussian touches

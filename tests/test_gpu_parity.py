@@ -207,3 +207,66 @@ def test_opacity_zero_leaves_image_unchanged():
     a = gpu_run(arr, 0, cam)
     b = gpu_run(extra, 0, cam)
     assert np.array_equal(a["image"], b["image"])
+
+
+# ---------------------------------------------------------------------------
+# one context across scenes: pair-buffer capacity grows, then is reused
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES)
+def test_capacity_growth_and_reuse_on_one_context(mode):
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    r = binding.Rasterizer(sort_mode=mode)
+    small = scenes.random_scene(seed=61, n=400, sh_degree=1, width=96, height=80)
+    big = scenes.random_scene(seed=62, n=6000, sh_degree=1, width=200, height=150, log_scale_range=(-3.5, -1.5))
+    mid = scenes.random_scene(seed=63, n=2000, sh_degree=1, width=120, height=90)
+    note(f"capacity sequence mode={mode}")
+    for s in (small, big, small, mid, big):
+        cam = s.cameras[0]
+        g = gpu_run(s.arrays(), 1, cam, bg=(0.1, 0.0, 0.2), sort_mode=mode, rast=r)
+        o = oracle.preprocess(s.arrays(), 1, cam)
+        check_preprocess(g, o)
+        check_binning(g, oracle.bin_pairs(o, want_unsorted=False))
+        oimg, _, _ = oracle.composite(o, cam, bg=(0.1, 0.0, 0.2))
+        assert image_error(g["image"], oimg) <= IMAGE_TOL
+    r.close()
+
+
+def test_device_error_paths():
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    s = scenes.random_scene(seed=71, n=300, sh_degree=0, width=64, height=64)
+    cam = s.cameras[0]
+    dev = binding.gaussians_to_device(s.arrays())
+    r = binding.Rasterizer()
+    r.set_option(binding.GS_OPT_MAX_DUPS, 10)
+    pr = r.preprocess(dev, 0, cam)
+    with pytest.raises(binding.GsError) as e:
+        r.bin_and_sort(pr, cam)
+    assert e.value.status == binding.GS_ERR_CAPACITY
+    r.set_option(binding.GS_OPT_MAX_DUPS, (1 << 32) - 1)
+    bn = r.bin_and_sort(pr, cam)                       # recovers once the cap allows it
+    assert bn.num_dups > 10
+    with pytest.raises(binding.GsError) as e:
+        r.set_option(binding.GS_OPT_SORT_MODE, 7)
+    assert e.value.status == binding.GS_ERR_INVALID_ARGUMENT
+    stale = binding.Projected.from_buffer_copy(pr)
+    stale.n = pr.n + 1
+    with pytest.raises(binding.GsError) as e:
+        r.bin_and_sort(stale, cam)
+    assert e.value.status == binding.GS_ERR_INVALID_ARGUMENT
+    bigger = dict(cam, width=cam["width"] + 32)
+    with pytest.raises(binding.GsError) as e:
+        r.bin_and_sort(pr, bigger)
+    assert e.value.status == binding.GS_ERR_INVALID_ARGUMENT
+    r.close()
+    r2 = binding.Rasterizer()
+    r2.set_option(binding.GS_OPT_MAX_WORKSPACE_BYTES, 4096)
+    with pytest.raises(binding.GsError) as e:
+        r2.preprocess(dev, 0, cam)
+    assert e.value.status == binding.GS_ERR_OUT_OF_MEMORY
+    r2.close()
+    torch.cuda.synchronize()

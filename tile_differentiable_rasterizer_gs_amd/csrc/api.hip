@@ -51,7 +51,8 @@ struct gs_context {
     char err[512] = {0};
 
     // per-Gaussian
-    DeviceBuffer splat, depth, rect, tile_count, dkey[2], dval[2], offsets, scan_scratch, dsort_scratch, total;
+    DeviceBuffer splat, depth, rect, tile_count, dkey[2], dval[2], dcount, offsets, scan_scratch, dsort_scratch,
+        total;
     // per-pair
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
@@ -62,8 +63,10 @@ struct gs_context {
     // last gs_preprocess
     int64_t n = -1;
     int32_t tiles_x = 0, tiles_y = 0;
-    int last_sort_buffer = 0;
-    const uint32_t *sorted_values = nullptr;
+    const uint32_t *sorted_values = nullptr;   // last binning: sorted Gaussian indices
+    const uint64_t *sorted_keys = nullptr;
+    int64_t pair_capacity = 0;                 // entries the pair buffers hold
+    hipEvent_t total_ready = nullptr;          // pair count has reached host_total
 
     std::vector<TimedSpan> spans;
     size_t spans_used = 0;
@@ -265,6 +268,7 @@ void gs_context_destroy(gs_context *ctx) {
     if (!ctx) return;
     DeviceScope scope(ctx->device);
     DeviceBuffer *all[] = {&ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1],
+                           &ctx->dcount,
                            &ctx->dval[0], &ctx->dval[1], &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch,
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
@@ -276,6 +280,7 @@ void gs_context_destroy(gs_context *ctx) {
         (void)hipEventDestroy(t.end);
     }
     if (ctx->host_total) (void)hipHostFree(ctx->host_total);
+    if (ctx->total_ready) (void)hipEventDestroy(ctx->total_ready);
     delete ctx;
 }
 
@@ -372,6 +377,107 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     return GS_OK;
 }
 
+// Enqueues the pair listing, the tile sort and the ranges for at most `cap` pairs.  The
+// kernels read the actual pair count (the scan total) from device memory, so this can be
+// enqueued before the host knows it.
+static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const uint32_t *order, int emit_keys,
+                               int64_t cap, hipStream_t stream) {
+    const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
+    const bool depth_first = ctx->sort_mode == GS_SORT_DEPTH_FIRST;
+    const size_t mm = (size_t)cap;
+    const int tile_bits = ceil_log2(tiles);
+    unsigned long long *d_total = as<unsigned long long>(ctx->total);
+    GS_TRY(ensure(ctx, ctx->pval[0], mm * 4));
+    GS_TRY(ensure(ctx, ctx->pval[1], mm * 4));
+    GS_TRY(ensure(ctx, ctx->psort_scratch, (size_t)sort_scratch_words(cap) * 4));
+    GS_TRY(ensure(ctx, ctx->part, (size_t)duplicate_partition_words(cap) * 4));
+    if (depth_first) {
+        GS_TRY(ensure(ctx, ctx->pkey32[0], mm * 4));
+        GS_TRY(ensure(ctx, ctx->pkey32[1], mm * 4));
+        if (emit_keys) GS_TRY(ensure(ctx, ctx->keys_out, mm * 8));
+    } else {
+        GS_TRY(ensure(ctx, ctx->pkey64[0], mm * 8));
+        GS_TRY(ensure(ctx, ctx->pkey64[1], mm * 8));
+        if (emit_keys) {
+            GS_TRY(ensure(ctx, ctx->keys_unsorted, mm * 8));
+            GS_TRY(ensure(ctx, ctx->vals_unsorted, mm * 4));
+        }
+    }
+
+    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+    launch_fill_u32(as<uint32_t>(ctx->ranges), 0u, tiles * 2, stream);
+    GS_TRY(check_launch(ctx, "fill"));
+    GS_TRY(span_end(ctx, stream));
+    ctx->sorted_values = nullptr;
+    ctx->sorted_keys = nullptr;
+    if (ctx->n <= 0) return GS_OK;
+
+    DuplicateParams d{};
+    d.n_items = ctx->n;
+    d.num_dups = d_total;
+    d.capacity = cap;
+    d.offsets = as<uint32_t>(ctx->offsets);
+    d.order = order;
+    d.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    d.depth = pr->depth;
+    d.tiles_x = ctx->tiles_x;
+    d.values = as<uint32_t>(ctx->pval[0]);
+    RangesParams r{};
+    r.num_dups = d_total;
+    r.capacity = cap;
+    r.ranges = as<uint32_t>(ctx->ranges);
+    int buf = 0;
+    if (depth_first) {
+        d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
+        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
+        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
+        GS_TRY(check_launch(ctx, "duplicate"));
+        GS_TRY(span_end(ctx, stream));
+        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
+        buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
+                                         as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), cap, d_total, 0,
+                                         tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
+        GS_TRY(check_launch(ctx, "tile sort"));
+        GS_TRY(span_end(ctx, stream));
+        r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
+        if (emit_keys) {
+            r.keys_out = as<uint64_t>(ctx->keys_out);
+            r.values = as<uint32_t>(ctx->pval[buf]);
+            r.depth = pr->depth;
+            ctx->sorted_keys = r.keys_out;
+        }
+    } else {
+        d.keys64 = as<uint64_t>(ctx->pkey64[0]);
+        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
+        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
+        GS_TRY(check_launch(ctx, "duplicate"));
+        GS_TRY(span_end(ctx, stream));
+        if (emit_keys) {   // the listing before sorting, kept for inspection
+            GS_HIP(ctx, hipMemcpyAsync(ctx->keys_unsorted.ptr, d.keys64, mm * 8, hipMemcpyDeviceToDevice, stream));
+            GS_HIP(ctx, hipMemcpyAsync(ctx->vals_unsorted.ptr, d.values, mm * 4, hipMemcpyDeviceToDevice, stream));
+        }
+        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
+        buf = radix_sort_pairs<uint64_t>(as<uint64_t>(ctx->pkey64[0]), as<uint32_t>(ctx->pval[0]),
+                                         as<uint64_t>(ctx->pkey64[1]), as<uint32_t>(ctx->pval[1]), cap, d_total, 0,
+                                         32 + tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
+        GS_TRY(check_launch(ctx, "key sort"));
+        GS_TRY(span_end(ctx, stream));
+        r.keys64 = as<uint64_t>(ctx->pkey64[buf]);
+        ctx->sorted_keys = r.keys64;
+    }
+    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+    launch_ranges(r, stream);
+    GS_TRY(check_launch(ctx, "ranges"));
+    GS_TRY(span_end(ctx, stream));
+    ctx->sorted_values = as<uint32_t>(ctx->pval[buf]);
+    return GS_OK;
+}
+
+// Binning of the last preprocess.  The pair count M is known on the host only after
+// the prefix sum; rather than idling the GPU while the host waits for it, the pair
+// kernels are enqueued first on buffers sized from earlier frames (capacity), and
+// the host then checks M: if it exceeds the capacity (first frame, growth), the
+// buffers grow and the pair kernels are enqueued again, so results are always exact.
 static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_keys, gs_binning *out,
                               hipStream_t stream) {
     const int64_t n = ctx->n;
@@ -382,126 +488,64 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     GS_TRY(ensure(ctx, ctx->scan_scratch, (size_t)scan_scratch_words((int64_t)nn) * 8));
     GS_TRY(ensure(ctx, ctx->total, 8));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
+    if (!ctx->total_ready) GS_HIP(ctx, hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming));
     unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
     const uint32_t *order = nullptr;
     int64_t M = 0;
+    bool speculated = false;
     if (n > 0) {
+        const uint32_t *counts = pr->tile_count;   // tile counts in rank order
         if (depth_first) {
+            // the last depth pass also gathers each ranked Gaussian's tile count
+            GS_TRY(ensure(ctx, ctx->dcount, nn * sizeof(uint32_t)));
             GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 4));
             GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
             const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
-                                                       as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n, 0,
-                                                       32, as<uint32_t>(ctx->dsort_scratch), stream);
+                                                       as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n,
+                                                       nullptr, 0, 32, as<uint32_t>(ctx->dsort_scratch), stream,
+                                                       pr->tile_count, as<uint32_t>(ctx->dcount));
             GS_TRY(check_launch(ctx, "depth sort"));
             GS_TRY(span_end(ctx, stream));
             order = as<uint32_t>(ctx->dval[buf]);
+            counts = n > 1 ? as<uint32_t>(ctx->dcount) : pr->tile_count;
         }
         GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
-        launch_scan(pr->tile_count, order, as<uint32_t>(ctx->offsets), n, d_total,
+        launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
                     as<unsigned long long>(ctx->scan_scratch), stream);
         GS_TRY(check_launch(ctx, "scan"));
         GS_TRY(span_end(ctx, stream));
 
         GS_TRY(span_begin(ctx, GS_STAGE_READBACK, stream));
         GS_HIP(ctx, hipMemcpyAsync(ctx->host_total, d_total, 8, hipMemcpyDeviceToHost, stream));
+        GS_HIP(ctx, hipEventRecord(ctx->total_ready, stream));
         GS_TRY(span_end(ctx, stream));
-        GS_HIP(ctx, hipStreamSynchronize(stream));
+        if (ctx->pair_capacity > 0) {
+            GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
+            speculated = true;
+        }
+        GS_HIP(ctx, hipEventSynchronize(ctx->total_ready));
         M = (int64_t)*ctx->host_total;
         if (M > ctx->max_dups)
             return fail(ctx, GS_ERR_CAPACITY, "%lld (Gaussian, tile) pairs exceed the cap of %lld", (long long)M,
                         (long long)ctx->max_dups);
     }
-
-    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
-    launch_fill_u32(as<uint32_t>(ctx->ranges), 0u, tiles * 2, stream);
-    GS_TRY(check_launch(ctx, "fill"));
-    GS_TRY(span_end(ctx, stream));
+    if (!speculated || M > ctx->pair_capacity) {
+        if (speculated) GS_HIP(ctx, hipStreamSynchronize(stream));   // buffers are about to move
+        const int64_t want = M + M / 4;
+        ctx->pair_capacity = want > 4096 ? want : 4096;
+        GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
+    }
 
     out->num_dups = M;
     out->tiles_x = ctx->tiles_x;
     out->tiles_y = ctx->tiles_y;
     out->tile_ranges = as<uint32_t>(ctx->ranges);
-    out->keys = nullptr;
-    out->values = nullptr;
-    out->keys_unsorted = nullptr;
-    out->values_unsorted = nullptr;
-    ctx->sorted_values = nullptr;
-    if (M == 0) return GS_OK;
-
-    const size_t mm = (size_t)M;
-    GS_TRY(ensure(ctx, ctx->pval[0], mm * 4));
-    GS_TRY(ensure(ctx, ctx->pval[1], mm * 4));
-    const int tile_bits = ceil_log2(tiles);
-    GS_TRY(ensure(ctx, ctx->psort_scratch, (size_t)sort_scratch_words(M) * 4));
-    GS_TRY(ensure(ctx, ctx->part, (size_t)duplicate_partition_words(M) * 4));
-
-    DuplicateParams d{};
-    d.n_items = n;
-    d.num_dups = M;
-    d.offsets = as<uint32_t>(ctx->offsets);
-    d.order = order;
-    d.rect = reinterpret_cast<const uint2 *>(pr->rect);
-    d.depth = pr->depth;
-    d.tiles_x = ctx->tiles_x;
-    d.values = as<uint32_t>(ctx->pval[0]);
-    RangesParams r{};
-    r.num_dups = M;
-    r.ranges = as<uint32_t>(ctx->ranges);
-    int buf = 0;
-    if (depth_first) {
-        GS_TRY(ensure(ctx, ctx->pkey32[0], mm * 4));
-        GS_TRY(ensure(ctx, ctx->pkey32[1], mm * 4));
-        d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
-        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
-        GS_TRY(check_launch(ctx, "duplicate"));
-        GS_TRY(span_end(ctx, stream));
-        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
-        buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
-                                         as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), M, 0, tile_bits,
-                                         as<uint32_t>(ctx->psort_scratch), stream);
-        GS_TRY(check_launch(ctx, "tile sort"));
-        GS_TRY(span_end(ctx, stream));
-        r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
-        if (emit_keys) {
-            GS_TRY(ensure(ctx, ctx->keys_out, mm * 8));
-            r.keys_out = as<uint64_t>(ctx->keys_out);
-            r.values = as<uint32_t>(ctx->pval[buf]);
-            r.depth = pr->depth;
-            out->keys = r.keys_out;
-        }
-    } else {
-        GS_TRY(ensure(ctx, ctx->pkey64[0], mm * 8));
-        GS_TRY(ensure(ctx, ctx->pkey64[1], mm * 8));
-        d.keys64 = as<uint64_t>(ctx->pkey64[0]);
-        GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
-        GS_TRY(check_launch(ctx, "duplicate"));
-        GS_TRY(span_end(ctx, stream));
-        if (emit_keys) {
-            GS_TRY(ensure(ctx, ctx->keys_unsorted, mm * 8));
-            GS_TRY(ensure(ctx, ctx->vals_unsorted, mm * 4));
-            GS_HIP(ctx, hipMemcpyAsync(ctx->keys_unsorted.ptr, d.keys64, mm * 8, hipMemcpyDeviceToDevice, stream));
-            GS_HIP(ctx, hipMemcpyAsync(ctx->vals_unsorted.ptr, d.values, mm * 4, hipMemcpyDeviceToDevice, stream));
-            out->keys_unsorted = as<uint64_t>(ctx->keys_unsorted);
-            out->values_unsorted = as<uint32_t>(ctx->vals_unsorted);
-        }
-        GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
-        buf = radix_sort_pairs<uint64_t>(as<uint64_t>(ctx->pkey64[0]), as<uint32_t>(ctx->pval[0]),
-                                         as<uint64_t>(ctx->pkey64[1]), as<uint32_t>(ctx->pval[1]), M, 0,
-                                         32 + tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
-        GS_TRY(check_launch(ctx, "key sort"));
-        GS_TRY(span_end(ctx, stream));
-        r.keys64 = as<uint64_t>(ctx->pkey64[buf]);
-        out->keys = r.keys64;
-    }
-    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
-    launch_ranges(r, stream);
-    GS_TRY(check_launch(ctx, "ranges"));
-    GS_TRY(span_end(ctx, stream));
-    ctx->sorted_values = as<uint32_t>(ctx->pval[buf]);
     out->values = ctx->sorted_values;
+    out->keys = ctx->sorted_keys;
+    const bool unsorted = M && !depth_first && emit_keys;
+    out->keys_unsorted = unsorted ? as<uint64_t>(ctx->keys_unsorted) : nullptr;
+    out->values_unsorted = unsorted ? as<uint32_t>(ctx->vals_unsorted) : nullptr;
     return GS_OK;
 }
 

@@ -52,17 +52,25 @@ constexpr int kRadixBits = 8;
 // uint32 scratch words radix_sort_pairs needs for n pairs
 int64_t sort_scratch_words(int64_t n);
 // Stable sort by key bits [begin_bit, end_bit), ping-ponging between (k0,v0) and (k1,v1);
-// returns 0 if the result is in (k0,v0), 1 if in (k1,v1).
+// returns 0 if the result is in (k0,v0), 1 if in (k1,v1).  n bounds the element count
+// (grid and scratch are sized from it); when n_dev is given the kernels sort
+// min(n, *n_dev) elements, a count that only the device knows at launch.  If
+// gathered_out is given, the last pass also writes gathered_out[i] = gather_src[value_i]
+// for the sorted values.
 template <typename K>
-int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit, int end_bit,
-                     uint32_t *scratch, hipStream_t s);
+int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, const unsigned long long *n_dev,
+                     int begin_bit, int end_bit, uint32_t *scratch, hipStream_t s,
+                     const uint32_t *gather_src = nullptr, uint32_t *gathered_out = nullptr);
 
 // ---------------------------------------------------------------------------
 // pair listing, ranges
 // ---------------------------------------------------------------------------
+// Pair-list kernels read the pair count from device memory and handle
+// min(count, capacity) entries; grids are sized from the capacity.
 struct DuplicateParams {
     int64_t n_items;             // number of (ranked) Gaussians
-    int64_t num_dups;
+    const unsigned long long *num_dups;   // device: total pairs (exclusive-scan total)
+    int64_t capacity;            // entries the pair buffers hold
     const uint32_t *offsets;     // [n_items] exclusive prefix of tile counts (in rank order)
     const uint32_t *order;       // [n_items] rank -> Gaussian index, or null (rank = index)
     const uint2 *rect;
@@ -77,7 +85,8 @@ int64_t duplicate_partition_words(int64_t num_dups);
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s);
 
 struct RangesParams {
-    int64_t num_dups;
+    const unsigned long long *num_dups;   // device
+    int64_t capacity;
     const uint64_t *keys64;      // either keys64 (tile = key >> 32) ...
     const uint32_t *tile_keys;   // ... or tile ids
     uint32_t *ranges;            // [tiles][2], zeroed beforehand

@@ -26,9 +26,11 @@ namespace gsr {
 namespace {
 
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kBlock * kSortItems;   // 4096 pairs per tile
 constexpr int kMaxSortGroups = 1024;             // workgroups per pass (4 per CU)
+// pairs per thread and tile: 16 (4096-pair tiles) for long inputs, 4 (1024) for short
+// ones so that enough workgroups exist to fill the GPU
+constexpr int kItemsLarge = 16, kItemsSmall = 4;
+constexpr int64_t kSmallSort = 1 << 22;
 
 template <typename K>
 __device__ inline uint32_t digit_of(K key, int shift, uint32_t mask) {
@@ -58,38 +60,60 @@ __device__ inline uint32_t block_exclusive_scan_u32(uint32_t x, uint32_t *s_tmp 
     return before + inc - x;
 }
 
-// Range of the input owned by workgroup `group` (tiles of kSortTile pairs).
-__device__ inline void group_range(int64_t n, int groups, int group, int64_t *lo, int64_t *hi) {
-    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+// Range of the input owned by workgroup `group` (whole tiles of `tile` pairs).
+__device__ inline void group_range(int64_t n, int64_t tile, int groups, int group, int64_t *lo, int64_t *hi) {
+    const int64_t tiles = (n + tile - 1) / tile;
     const int64_t per = (tiles + groups - 1) / groups;
-    *lo = min<int64_t>(n, (int64_t)group * per * kSortTile);
-    *hi = min<int64_t>(n, (int64_t)(group + 1) * per * kSortTile);
+    *lo = min<int64_t>(n, (int64_t)group * per * tile);
+    *hi = min<int64_t>(n, (int64_t)(group + 1) * per * tile);
 }
 
-template <typename K>
-__global__ __launch_bounds__(kBlock) void radix_count_kernel(const K *keys, int64_t n, int shift, int bits,
+// Lanes of this wave whose digit equals d (one ballot per digit bit); only lanes with
+// `valid` take part.
+__device__ inline uint64_t match_digit(uint32_t d, int bits, bool valid) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t on = __ballot(bit);
+        peers &= bit ? on : ~on;
+    }
+    return peers;
+}
+
+// Element count of a pass: the host bound, or min(bound, *n_dev) when the count lives on the device.
+__device__ inline int64_t live_count(int64_t n_cap, const unsigned long long *n_dev) {
+    return n_dev ? min<int64_t>(n_cap, (int64_t)*n_dev) : n_cap;
+}
+
+// Digit counts of one range.  LDS atomics go to one of kCopies histograms per wave
+// (chosen by lane), which keeps lanes that share a digit from serialising on one word.
+template <typename K, int ITEMS>
+__global__ __launch_bounds__(kBlock) void radix_count_kernel(const K *keys, int64_t n_cap,
+                                                             const unsigned long long *n_dev, int shift, int bits,
                                                              uint32_t *counts /*[radix][groups]*/) {
-    constexpr int kWaves = kBlock / kWave;
-    __shared__ uint32_t s_count[kWaves][kRadix];
-    const int wave = threadIdx.x / kWave;
+    const int64_t n = live_count(n_cap, n_dev);
+    constexpr int kCopies = 4 * (kBlock / kWave);
+    constexpr int kStride = kRadix + 1;   // odd stride: copies of one digit sit in different banks
+    __shared__ uint32_t s_count[kCopies * kStride];
     const uint32_t mask = (1u << bits) - 1;
-    for (int i = threadIdx.x; i < kWaves * kRadix; i += kBlock) (&s_count[0][0])[i] = 0;
+    const int copy = (threadIdx.x / kWave) * 4 + (threadIdx.x & 3);
+    for (int i = threadIdx.x; i < kCopies * kStride; i += kBlock) s_count[i] = 0;
     __syncthreads();
     int64_t lo, hi;
-    group_range(n, gridDim.x, blockIdx.x, &lo, &hi);
+    group_range(n, (int64_t)kBlock * ITEMS, gridDim.x, blockIdx.x, &lo, &hi);
     for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * kBlock) {
         K k[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) k[u] = i + u * kBlock < hi ? keys[i + u * kBlock] : K(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (i + u * kBlock < hi) atomicAdd(&s_count[wave][digit_of(k[u], shift, mask)], 1u);
+            if (i + u * kBlock < hi) atomicAdd(&s_count[copy * kStride + digit_of(k[u], shift, mask)], 1u);
     }
     __syncthreads();
     if ((int)threadIdx.x <= (int)mask) {
         uint32_t c = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += s_count[w][threadIdx.x];
+        for (int w = 0; w < kCopies; ++w) c += s_count[w * kStride + threadIdx.x];
         counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = c;
     }
 }
@@ -117,12 +141,18 @@ __global__ __launch_bounds__(kBlock) void radix_digit_scan_kernel(uint32_t *coun
     if (threadIdx.x == kBlock - 1) totals[blockIdx.x] = run;
 }
 
-template <typename K>
+// gathered_out (optional): gathered_out[dst] = gather_src[value] for every moved pair.
+template <typename K, int ITEMS>
 __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in, const uint32_t *vals_in,
-                                                               K *keys_out, uint32_t *vals_out, int64_t n,
-                                                               int shift, int bits, const uint32_t *counts,
-                                                               const uint32_t *totals) {
+                                                               K *keys_out, uint32_t *vals_out, int64_t n_cap,
+                                                               const unsigned long long *n_dev, int shift,
+                                                               int bits, const uint32_t *counts,
+                                                               const uint32_t *totals, const uint32_t *gather_src,
+                                                               uint32_t *gathered_out) {
+    const int64_t n = live_count(n_cap, n_dev);
     constexpr int kWaves = kBlock / kWave;
+    constexpr int kSortItems = ITEMS;
+    constexpr int kSortTile = kBlock * ITEMS;
     __shared__ K s_keys[kSortTile];
     __shared__ uint32_t s_vals[kSortTile];
     __shared__ uint32_t s_wave_count[kWaves][kRadix];   // per-wave running counts, then wave prefixes
@@ -140,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
         if ((int)threadIdx.x < radix) s_next[threadIdx.x] = base + counts[(int64_t)threadIdx.x * gridDim.x + blockIdx.x];
     }
     int64_t lo, hi;
-    group_range(n, gridDim.x, blockIdx.x, &lo, &hi);
+    group_range(n, kSortTile, gridDim.x, blockIdx.x, &lo, &hi);
     for (int64_t tile = lo; tile < hi; tile += kSortTile) {
         for (int i = threadIdx.x; i < kWaves * kRadix; i += kBlock) (&s_wave_count[0][0])[i] = 0;
         __syncthreads();
@@ -159,12 +189,7 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
         for (int r = 0; r < kSortItems; ++r) {
             const bool valid = seg + r * kWave + lane < hi;
             const uint32_t d = digit_of(key[r], shift, mask);
-            uint64_t peers = __ballot(valid);
-            for (int b = 0; b < bits; ++b) {
-                const bool bit = (d >> b) & 1u;
-                const uint64_t on = __ballot(bit);
-                peers &= bit ? on : ~on;
-            }
+            const uint64_t peers = match_digit(d, bits, valid);
             const uint32_t below = lanes_below(peers);
             const uint32_t prev = valid ? s_wave_count[wave][d] : 0u;
             rank[r] = prev + below;
@@ -198,8 +223,10 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
             const K k = s_keys[q];
             const uint32_t d = digit_of(k, shift, mask);
             const int64_t dst = (int64_t)s_next[d] + (q - (int64_t)s_local_start[d]);
+            const uint32_t v = s_vals[q];
             keys_out[dst] = k;
-            vals_out[dst] = s_vals[q];
+            vals_out[dst] = v;
+            if (gathered_out) gathered_out[dst] = gather_src[v];
         }
         __syncthreads();
         s_next[threadIdx.x] += tile_count;   // every thread owns one digit slot
@@ -214,15 +241,17 @@ constexpr int kDupItems = 8;
 constexpr int kDupTile = kBlock * kDupItems;   // 2048 entries per workgroup
 constexpr int kDupWindow = kDupTile + 1;
 
-// part[b] = rank whose pairs contain entry b * kDupTile.
-__global__ __launch_bounds__(kBlock) void partition_kernel(const uint32_t *offsets, int64_t n, int64_t num_dups,
+// part[b] = rank whose pairs contain entry b * kDupTile; part[blocks] = rank of the last entry.
+__global__ __launch_bounds__(kBlock) void partition_kernel(const uint32_t *offsets, int64_t n_items,
+                                                           const unsigned long long *num_dev, int64_t cap,
                                                            uint32_t *part) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= n) return;
+    if (i >= n_items) return;
+    const int64_t num = live_count(cap, num_dev);
     const int64_t start = offsets[i];
-    const int64_t end = i + 1 < n ? (int64_t)offsets[i + 1] : num_dups;
+    const int64_t end = min<int64_t>(i + 1 < n_items ? (int64_t)offsets[i + 1] : (int64_t)*num_dev, num);
     for (int64_t b = (start + kDupTile - 1) / kDupTile; b * kDupTile < end; ++b) part[b] = (uint32_t)i;
-    if (start < end && end == num_dups) part[(num_dups + kDupTile - 1) / kDupTile] = (uint32_t)i;
+    if (start < end && end == num) part[(num + kDupTile - 1) / kDupTile] = (uint32_t)i;
 }
 
 __device__ inline int64_t last_le_global(const uint32_t *offsets, int64_t lo, int64_t hi, uint32_t e) {
@@ -241,7 +270,9 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     __shared__ uint32_t s_g[kDupWindow];
     __shared__ uint2 s_rect[kDupWindow];
     __shared__ uint32_t s_depth[kDupWindow];
+    const int64_t num_dups = live_count(p.capacity, p.num_dups);
     const int64_t first = (int64_t)blockIdx.x * kDupTile;
+    if (first >= num_dups) return;
     const int64_t lo = part[blockIdx.x];
     const int64_t hi = part[blockIdx.x + 1];   // rank of entry (b+1)*kDupTile, or of the last entry
     const int64_t window = hi - lo + 1;
@@ -258,8 +289,8 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     }
     __syncthreads();
     const int64_t e0 = first + (int64_t)threadIdx.x * kDupItems;
-    if (e0 >= p.num_dups) return;
-    const int n_here = (int)min<int64_t>(kDupItems, p.num_dups - e0);
+    if (e0 >= num_dups) return;
+    const int n_here = (int)min<int64_t>(kDupItems, num_dups - e0);
 
     // rank holding e0
     int64_t i;
@@ -344,15 +375,16 @@ constexpr int kRangeItems = 4;
 
 template <bool kKey64>
 __global__ __launch_bounds__(kBlock) void ranges_kernel(RangesParams p) {
+    const int64_t num_dups = live_count(p.capacity, p.num_dups);
     const int64_t e0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kRangeItems;
-    if (e0 >= p.num_dups) return;
+    if (e0 >= num_dups) return;
     uint32_t t[kRangeItems + 1];
-    const int cnt = (int)min<int64_t>(kRangeItems, p.num_dups - e0);
+    const int cnt = (int)min<int64_t>(kRangeItems, num_dups - e0);
 #pragma unroll
     for (int k = 0; k <= kRangeItems; ++k) {
         const int64_t e = e0 + k;
         t[k] = 0xffffffffu;
-        if (k <= cnt && e < p.num_dups)
+        if (k <= cnt && e < num_dups)
             t[k] = kKey64 ? (uint32_t)(p.keys64[e] >> 32) : p.tile_keys[e];
     }
     const uint32_t prev = e0 == 0 ? 0xffffffffu : (kKey64 ? (uint32_t)(p.keys64[e0 - 1] >> 32) : p.tile_keys[e0 - 1]);
@@ -372,11 +404,22 @@ __global__ __launch_bounds__(kBlock) void fill_u32_kernel(uint32_t *dst, uint32_
     if (i < n) dst[i] = value;
 }
 
-inline int passes_for(int begin_bit, int end_bit) { return (end_bit - begin_bit + kRadixBits - 1) / kRadixBits; }
+
+inline int64_t sort_tile(int64_t n) { return (int64_t)kBlock * (n <= kSmallSort ? kItemsSmall : kItemsLarge); }
 
 inline int sort_groups(int64_t n) {
-    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    const int64_t tiles = (n + sort_tile(n) - 1) / sort_tile(n);
     return (int)(tiles < 1 ? 1 : (tiles > kMaxSortGroups ? kMaxSortGroups : tiles));
+}
+
+template <typename K, int ITEMS>
+void launch_pass(K *ki, uint32_t *vi, K *ko, uint32_t *vo, int64_t n, const unsigned long long *n_dev, int shift,
+                 int bits, int groups, uint32_t *counts, uint32_t *totals, const uint32_t *gather_src,
+                 uint32_t *gathered_out, hipStream_t s) {
+    radix_count_kernel<K, ITEMS><<<groups, kBlock, 0, s>>>(ki, n, n_dev, shift, bits, counts);
+    radix_digit_scan_kernel<<<1 << bits, kBlock, 0, s>>>(counts, groups, totals);
+    radix_scatter_kernel<K, ITEMS><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts, totals,
+                                                             gather_src, gathered_out);
 }
 
 }  // namespace
@@ -384,46 +427,57 @@ inline int sort_groups(int64_t n) {
 int64_t sort_scratch_words(int64_t n) { return (int64_t)kRadix * sort_groups(n) + kRadix; }
 
 template <typename K>
-int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, int begin_bit, int end_bit,
-                     uint32_t *scratch, hipStream_t s) {
-    if (n <= 1 || end_bit <= begin_bit) return 0;
+int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, const unsigned long long *n_dev,
+                     int begin_bit, int end_bit, uint32_t *scratch, hipStream_t s, const uint32_t *gather_src,
+                     uint32_t *gathered_out) {
+    if ((n <= 1 && !n_dev) || n <= 0 || end_bit <= begin_bit) return 0;
     const int groups = sort_groups(n);
     uint32_t *counts = scratch;
     uint32_t *totals = counts + (int64_t)kRadix * groups;
-    int cur = 0;
-    for (int p = 0; p < passes_for(begin_bit, end_bit); ++p) {
-        const int shift = begin_bit + p * kRadixBits;
-        const int bits = min(kRadixBits, end_bit - shift);
+    // the fewest 8-bit-or-narrower passes, with the bits spread evenly (13 -> 7 + 6):
+    // narrower digits give longer contiguous write runs per tile
+    const int total_bits = end_bit - begin_bit;
+    const int passes = (total_bits + kRadixBits - 1) / kRadixBits;
+    int cur = 0, shift = begin_bit;
+    for (int p = 0; p < passes; ++p) {
+        const int bits = (total_bits - (shift - begin_bit) + (passes - p) - 1) / (passes - p);
         K *ki = cur ? k1 : k0;
         uint32_t *vi = cur ? v1 : v0;
         K *ko = cur ? k0 : k1;
         uint32_t *vo = cur ? v0 : v1;
-        radix_count_kernel<K><<<groups, kBlock, 0, s>>>(ki, n, shift, bits, counts);
-        radix_digit_scan_kernel<<<1 << bits, kBlock, 0, s>>>(counts, groups, totals);
-        radix_scatter_kernel<K><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, shift, bits, counts, totals);
+        const bool last = p == passes - 1;
+        if (n <= kSmallSort)
+            launch_pass<K, kItemsSmall>(ki, vi, ko, vo, n, n_dev, shift, bits, groups, counts, totals,
+                                        last ? gather_src : nullptr, last ? gathered_out : nullptr, s);
+        else
+            launch_pass<K, kItemsLarge>(ki, vi, ko, vo, n, n_dev, shift, bits, groups, counts, totals,
+                                        last ? gather_src : nullptr, last ? gathered_out : nullptr, s);
+        shift += bits;
         cur ^= 1;
     }
     return cur;
 }
 
-template int radix_sort_pairs<uint32_t>(uint32_t *, uint32_t *, uint32_t *, uint32_t *, int64_t, int, int,
-                                        uint32_t *, hipStream_t);
-template int radix_sort_pairs<uint64_t>(uint64_t *, uint32_t *, uint64_t *, uint32_t *, int64_t, int, int,
-                                        uint32_t *, hipStream_t);
+template int radix_sort_pairs<uint32_t>(uint32_t *, uint32_t *, uint32_t *, uint32_t *, int64_t,
+                                        const unsigned long long *, int, int, uint32_t *, hipStream_t,
+                                        const uint32_t *, uint32_t *);
+template int radix_sort_pairs<uint64_t>(uint64_t *, uint32_t *, uint64_t *, uint32_t *, int64_t,
+                                        const unsigned long long *, int, int, uint32_t *, hipStream_t,
+                                        const uint32_t *, uint32_t *);
 
 int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTile - 1) / kDupTile + 1; }
 
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
-    if (p.num_dups <= 0) return;
+    if (p.capacity <= 0 || p.n_items <= 0) return;
     partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(p.offsets, p.n_items,
-                                                                                       p.num_dups, part);
-    const int64_t nb = (p.num_dups + kDupTile - 1) / kDupTile;
+                                                                                       p.num_dups, p.capacity, part);
+    const int64_t nb = (p.capacity + kDupTile - 1) / kDupTile;
     duplicate_kernel<<<(unsigned)nb, kBlock, 0, s>>>(p, part);
 }
 
 void launch_ranges(const RangesParams &p, hipStream_t s) {
-    if (p.num_dups <= 0) return;
-    const int64_t threads = (p.num_dups + kRangeItems - 1) / kRangeItems;
+    if (p.capacity <= 0) return;
+    const int64_t threads = (p.capacity + kRangeItems - 1) / kRangeItems;
     const unsigned grid = (unsigned)((threads + kBlock - 1) / kBlock);
     if (p.keys64)
         ranges_kernel<true><<<grid, kBlock, 0, s>>>(p);
