@@ -270,3 +270,72 @@ def test_device_error_paths():
     assert e.value.status == binding.GS_ERR_OUT_OF_MEMORY
     r2.close()
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# the 5M workload (2 % large Gaussians, ~4e8 pairs) and the 3M 32-view orbit:
+# integers per Gaussian in full, pair lists on sampled tiles, image on sampled pixels
+# ---------------------------------------------------------------------------
+
+def _tile_list_oracle(o, tile, tiles_x):
+    """Gaussians whose rectangle holds `tile`, in (depth, index) order (numpy lexsort)."""
+    tx, ty = tile % tiles_x, tile // tiles_x
+    r = o["rect"]
+    hit = np.nonzero((o["tile_count"] > 0) & (r[0] <= tx) & (tx < r[1]) & (r[2] <= ty) & (ty < r[3]))[0]
+    order = np.lexsort((hit, o["depth"][hit]))
+    return hit[order].astype(np.uint32)
+
+
+def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0):
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    r = binding.Rasterizer(emit_keys=False)
+    dev = binding.gaussians_to_device(s.arrays())
+    pr = r.preprocess(dev, s.sh_degree, cam)
+    bn = r.bin_and_sort(pr, cam)
+    img = r.composite(pr, bn, cam)
+    pt = r.projected_tensors(pr)
+    ranges = binding.copy_device(bn.tile_ranges, (bn.tiles_x * bn.tiles_y, 2), torch.int32).cpu().numpy().view(np.uint32)
+    values = binding.copy_device(bn.values, (bn.num_dups,), torch.int32)
+    torch.cuda.synchronize()
+    o = oracle.preprocess(s.arrays(), s.sh_degree, cam)
+    g = dict(tile_count=pt["tile_count"].cpu().numpy().view(np.uint32), depth=pt["depth"].cpu().numpy(),
+             rect=pt["rect"].cpu().numpy().view(np.uint16).astype(np.int32), splat=pt["splat"].cpu().numpy())
+    check_preprocess(g, o)
+    assert bn.num_dups == int(o["tile_count"].astype(np.int64).sum())
+    # ranges tile the list in order and their lengths are the per-tile pair counts
+    nonempty = ranges[:, 1] > ranges[:, 0]
+    assert np.all(ranges[nonempty, 0][1:] == ranges[nonempty, 1][:-1])
+    assert ranges[nonempty, 0][0] == 0 and ranges[nonempty, 1][-1] == bn.num_dups
+    rng = np.random.default_rng(seed)
+    lens = ranges[:, 1].astype(np.int64) - ranges[:, 0]
+    tiles = np.concatenate([rng.choice(len(lens), n_tiles, replace=False), [int(np.argmax(lens))]])
+    for t in tiles:
+        lo, hi = (int(v) for v in ranges[t])
+        ref = _tile_list_oracle(o, int(t), bn.tiles_x)
+        got = values[lo:hi].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, ref), f"tile {t}"
+    pix = rng.choice(cam["width"] * cam["height"], n_pix, replace=False)
+    oimg, _, _ = oracle.composite(o, cam, pixels=pix)
+    err = image_error(img.cpu().numpy().reshape(-1, 3)[pix], oimg)
+    assert err <= IMAGE_TOL, f"sampled image err {err}"
+    r.close()
+    return bn.num_dups, err
+
+
+def test_c4_5m_large_gaussians_sampled():
+    s = scenes.make_scene("c4_5m_sh3_1080p_large")
+    note("c4 5M")
+    m, err = _large_check(s, s.cameras[0], n_tiles=16, n_pix=300)
+    note(f"c4 pairs={m} sampled err {err:.2e}")
+    assert m > 10 ** 8
+
+
+def test_c5_orbit_views_sampled():
+    s = scenes.make_scene("c5_3m_sh3_1080p_orbit32")
+    for k in (0, 11, 27):
+        note(f"c5 view {k}")
+        m, err = _large_check(s, s.cameras[k], n_tiles=12, n_pix=300, seed=k)
+        note(f"c5 view {k} pairs={m} sampled err {err:.2e}")
