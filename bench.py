@@ -5,7 +5,9 @@ pair listing, tile sort, ranges, composite) with the scene already resident in
 HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sort-mode 0|1]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--calibration-copy]
+
+A workload with several cameras (the 32-view orbit) renders its views round-robin.
 """
 from __future__ import annotations
 
@@ -47,6 +49,25 @@ def stage_bytes(n, sh_degree, m, n_visible):
                 ranges=ranges)
 
 
+def measured_traffic(workload):
+    """HBM bytes per composite launch from the committed rocprofv3 summary, or None when the
+    summary is missing or was taken on a different composite kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    src = os.path.join(ROOT, "tile_differentiable_rasterizer_gs_amd", "csrc", "composite.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("composite_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(float(kv["composite_traffic_bytes"]))
+
+
 def cpu_baseline(scene, cam, pixels_target=8192):
     """The oracle on a bounded sample: full projection + binning, composite on sampled pixels."""
     import numpy as np
@@ -79,6 +100,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--sort-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run one 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this rasterizer has no multi-GPU path; run with --gpus 1",
@@ -94,10 +117,18 @@ def main():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     name = args.workload or scenes.HEADLINE
     t = time.perf_counter()
     scene = scenes.make_scene(name)
-    cam = scene.cameras[0]
+    cams = scene.cameras          # several views: rendered round-robin, back to back on one stream
+    cam = cams[0]
     log(f"scene {name}: n={scene.n} generated in {time.perf_counter() - t:.1f}s")
     dev = binding.gaussians_to_device(scene.arrays())
     r = binding.Rasterizer(sort_mode=args.sort_mode, emit_keys=False)
@@ -105,20 +136,24 @@ def main():
     img = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
     bg = (0.0, 0.0, 0.0)
 
-    # frame statistics (outside the timed region): pairs and blended (pixel, Gaussian) pairs
-    pr = r.preprocess(dev, scene.sh_degree, cam)
-    bn = r.bin_and_sort(pr, cam)
-    tot = torch.zeros(1, dtype=torch.int64, device="cuda")
-    r.composite(pr, bn, cam, bg=bg, out=img, blend_total=tot)
-    tc = r.projected_tensors(pr)["tile_count"]
-    torch.cuda.synchronize()
-    pairs = int(bn.num_dups)
-    blends = int(tot.item())
-    n_visible = int((tc > 0).sum().item())
-    log(f"pairs={pairs} visible={n_visible} blended pairs={blends}")
+    # frame statistics (outside the timed region), averaged over the views: pairs, visible
+    # Gaussians and blended (pixel, Gaussian) pairs
+    pairs = blends = n_visible = 0
+    for c in cams:
+        pr = r.preprocess(dev, scene.sh_degree, c)
+        bn = r.bin_and_sort(pr, c)
+        tot = torch.zeros(1, dtype=torch.int64, device="cuda")
+        r.composite(pr, bn, c, bg=bg, out=img, blend_total=tot)
+        tc = r.projected_tensors(pr)["tile_count"]
+        torch.cuda.synchronize()
+        pairs += int(bn.num_dups)
+        blends += int(tot.item())
+        n_visible += int((tc > 0).sum().item())
+    pairs, blends, n_visible = (v / len(cams) for v in (pairs, blends, n_visible))
+    log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} blended pairs={blends:.0f} ({len(cams)} view(s))")
 
-    for _ in range(args.warmup):
-        r.render(dev, scene.sh_degree, cam, bg=bg, out=img)
+    for i in range(args.warmup):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     torch.cuda.synchronize()
 
     # timed region 1: plain frames
@@ -126,8 +161,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        r.render(dev, scene.sh_degree, cam, bg=bg, out=img)
+    for i in range(args.steps):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -139,8 +174,8 @@ def main():
     r.profile_read()
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
-        r.render(dev, scene.sh_degree, cam, bg=bg, out=img)
+    for i in range(args.steps):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     stop.record()
     torch.cuda.synchronize()
     prof_ms_per_step = start.elapsed_time(stop) / args.steps
@@ -164,7 +199,7 @@ def main():
     dominant = max(stage_ms, key=stage_ms.get)
     dom = dict(rooflines.get(dominant, {}))
     dom["kernel"] = dominant
-    dom["traffic"] = None
+    dom["traffic"] = measured_traffic(name) if dominant == "composite" else None
 
     out = {
         "metric": "frames/s and Gaussian-pixel blends/s, 1M Gaussians SH3 @1920x1080, 1 GPU",
@@ -181,8 +216,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": name, "n_gaussians": scene.n, "sh_degree": scene.sh_degree, "width": W,
-                   "height": H, "sort_mode": "depth_first" if args.sort_mode == 0 else "key64",
-                   "pairs": pairs, "blended_pairs": blends},
+                   "height": H, "views": len(cams), "sort_mode": "depth_first" if args.sort_mode == 0 else "key64",
+                   "pairs_per_frame": round(pairs), "blended_pairs_per_frame": round(blends)},
         "roofline": dom,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stage_rooflines": rooflines,
