@@ -101,7 +101,7 @@ def main():
     ap.add_argument("--sort-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="run one 1 GiB device copy first (reference for HBM byte counters)")
+                    help="run one 1 GiB read + 1 GiB write elementwise kernel first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this rasterizer has no multi-GPU path; run with --gpus 1",
@@ -118,10 +118,11 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     if args.calibration_copy:
+        # a plain elementwise kernel that reads 1 GiB and writes 1 GiB (larger than the caches)
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     name = args.workload or scenes.HEADLINE
