@@ -3,10 +3,15 @@
 TEST INFRASTRUCTURE ONLY: imported by `tests/`, by `__graft_entry__.smoke()`
 and by the benchmark's `cpu_baseline` leg, never by the product package.
 
-Two independent pieces:
-  * `gs_oracle.c` (built to `liboracle.so` with gcc, OpenMP, -ffp-contract=off):
-    projection in binary32 following a fixed operation order, binning, and
-    per-pixel binary64 compositing over all depth-sorted Gaussians;
+Independent pieces:
+  * `gs_oracle.c` (built with `gs_oracle_grad.c` into `liboracle.so` by gcc,
+    OpenMP, -ffp-contract=off): projection in binary32 following a fixed
+    operation order, binning, and per-pixel binary64 compositing over all
+    depth-sorted Gaussians;
+  * `gs_oracle_grad.c`: the same projection and compositing in binary64 over
+    fixed per-pixel lists, and their vector-Jacobian products written out by
+    hand (the gradients of the lesson's section "Pourquoi est-ce
+    différenciable");
   * `composite_2d` below: the dense 2D rasteriser of the lesson
     "3D Gaussian Splatting from scratch", section "Étape 2: Rasteriser à
     éclaboussure en 2D", in numpy binary64 (every Gaussian at every pixel,
@@ -22,17 +27,19 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gs_oracle.c")
+_SRC_GRAD = os.path.join(_HERE, "gs_oracle_grad.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 TILE = 16
 
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (binary32 semantics: no contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in (_SRC, _SRC_GRAD))
+    if force or stale:
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
                                "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
-                               "-o", tmp, _SRC, "-lm"])
+                               "-o", tmp, _SRC, _SRC_GRAD, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -73,6 +80,16 @@ def _load():
         lib.oracle_cov3d.restype = None
         lib.oracle_sh_basis.argtypes = [ctypes.c_double] * 3 + [P]
         lib.oracle_sh_basis.restype = None
+        lib.oracle_project64.argtypes = [i64, i32, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_project64.restype = None
+        lib.oracle_project_backward.argtypes = [i64, i32, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_project_backward.restype = None
+        lib.oracle_composite_fixed.argtypes = [i64, P, P, P, P, P, P, i64, i32, i32, P, P, ctypes.c_double,
+                                               P, P, P]
+        lib.oracle_composite_fixed.restype = None
+        lib.oracle_composite_backward.argtypes = [i64, P, P, P, P, P, P, i64, i32, i32, P, P, ctypes.c_double,
+                                                  P, P, P, P, P]
+        lib.oracle_composite_backward.restype = None
         _lib = lib
     return _lib
 
@@ -213,3 +230,111 @@ def composite_2d(means, covs, colours, opacities, depths, image_size, bg=None):
     if bg is not None:
         out += T[:, None] * np.asarray(bg, np.float64)[None, :]
     return out.reshape(H, W, 3), T.reshape(H, W)
+
+
+# ---------------------------------------------------------------------------
+# gradients (gs_oracle_grad.c)
+# ---------------------------------------------------------------------------
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def camera64(camera: dict) -> np.ndarray:
+    """R[9], t[3], fx, fy, cx, cy as binary64 copies of the binary32 camera values."""
+    vals = list(np.asarray(camera["R"], np.float32).reshape(9)) + list(np.asarray(camera["t"], np.float32).reshape(3))
+    vals += [np.float32(camera[k]) for k in ("fx", "fy", "cx", "cy")]
+    return np.array([float(v) for v in vals], np.float64)
+
+
+def project64(arrays: dict, sh_degree: int, camera: dict) -> dict:
+    """binary64 projection with no culling: mean2d, conic, rgb, cov2d, depth."""
+    lib = _load()
+    mean, quat, ls, sh = (_f64(arrays[k]) for k in ("mean", "quat", "log_scale", "sh"))
+    n = mean.shape[1]
+    K = (sh_degree + 1) ** 2
+    out = dict(mean2d=np.zeros((2, n)), conic=np.zeros((3, n)), rgb=np.zeros((3, n)), cov2d=np.zeros((3, n)),
+               depth=np.zeros(n))
+    lib.oracle_project64(n, K, _ptr(mean), _ptr(quat), _ptr(ls), _ptr(sh), _ptr(camera64(camera)),
+                         _ptr(out["mean2d"]), _ptr(out["conic"]), _ptr(out["rgb"]), _ptr(out["cov2d"]),
+                         _ptr(out["depth"]))
+    return out
+
+
+def project_backward(arrays: dict, sh_degree: int, camera: dict, g_mean2d=None, g_conic=None, g_rgb=None) -> dict:
+    """Vector-Jacobian product of project64: gradients for mean, quat, log_scale, sh."""
+    lib = _load()
+    mean, quat, ls, sh = (_f64(arrays[k]) for k in ("mean", "quat", "log_scale", "sh"))
+    n = mean.shape[1]
+    K = (sh_degree + 1) ** 2
+    out = dict(mean=np.zeros((3, n)), quat=np.zeros((4, n)), log_scale=np.zeros((3, n)), sh=np.zeros((K * 3, n)))
+    gm = None if g_mean2d is None else _f64(g_mean2d)
+    gc = None if g_conic is None else _f64(g_conic)
+    gr = None if g_rgb is None else _f64(g_rgb)
+    lib.oracle_project_backward(n, K, _ptr(mean), _ptr(quat), _ptr(ls), _ptr(sh), _ptr(camera64(camera)),
+                                _ptr(gm), _ptr(gc), _ptr(gr), _ptr(out["mean"]), _ptr(out["quat"]),
+                                _ptr(out["log_scale"]), _ptr(out["sh"]))
+    return out
+
+
+def depth_order(depth, tile_count) -> np.ndarray:
+    """Gaussians with tile_count > 0 in ascending (binary32 depth, index)."""
+    g = np.nonzero(np.asarray(tile_count) > 0)[0]
+    d = np.asarray(depth, np.float32)[g]
+    return np.ascontiguousarray(g[np.lexsort((g, d))], dtype=np.int64)
+
+
+def composite_fixed(screen: dict, rect, order, camera: dict, bg=(0.0, 0.0, 0.0), n_limit=None, t_eps=1e-4):
+    """binary64 compositing over fixed lists; returns (rgb [H,W,3], T [H,W], count [H,W])."""
+    lib = _load()
+    W, H = camera["width"], camera["height"]
+    n = np.asarray(screen["opacity"]).shape[0]
+    m2, co, op, rgb = (_f64(screen[k]) for k in ("mean2d", "conic", "opacity", "rgb"))
+    rect = np.ascontiguousarray(rect, np.int32)
+    order = np.ascontiguousarray(order, np.int64)
+    lim = None if n_limit is None else np.ascontiguousarray(n_limit, np.int64).reshape(-1)
+    out, T, cnt = np.zeros(H * W * 3), np.zeros(H * W), np.zeros(H * W, np.int64)
+    lib.oracle_composite_fixed(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(order), order.shape[0],
+                               W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps), _ptr(out), _ptr(T), _ptr(cnt))
+    return out.reshape(H, W, 3), T.reshape(H, W), cnt.reshape(H, W)
+
+
+def composite_backward(screen: dict, rect, order, camera: dict, g_image, bg=(0.0, 0.0, 0.0), n_limit=None,
+                       t_eps=1e-4) -> dict:
+    """Vector-Jacobian product of composite_fixed: gradients for mean2d, conic, opacity, rgb."""
+    lib = _load()
+    W, H = camera["width"], camera["height"]
+    n = np.asarray(screen["opacity"]).shape[0]
+    m2, co, op, rgb = (_f64(screen[k]) for k in ("mean2d", "conic", "opacity", "rgb"))
+    rect = np.ascontiguousarray(rect, np.int32)
+    order = np.ascontiguousarray(order, np.int64)
+    lim = None if n_limit is None else np.ascontiguousarray(n_limit, np.int64).reshape(-1)
+    gi = _f64(g_image).reshape(-1)
+    assert gi.shape[0] == H * W * 3
+    out = dict(mean2d=np.zeros((2, n)), conic=np.zeros((3, n)), opacity=np.zeros(n), rgb=np.zeros((3, n)))
+    lib.oracle_composite_backward(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(order),
+                                  order.shape[0], W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps), _ptr(gi),
+                                  _ptr(out["mean2d"]), _ptr(out["conic"]), _ptr(out["opacity"]), _ptr(out["rgb"]))
+    return out
+
+
+def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0, 0.0, 0.0)) -> dict:
+    """Gradient of sum(g_image * render(arrays)) for every Gaussian parameter.
+
+    The lists (tile rectangles, visibility, depth order) come from the binary32
+    projection of `preprocess`; compositing and all derivatives are binary64,
+    with the per-pixel stop at T < 1e-4 found by the binary64 forward walk.
+    Returns parameter gradients (mean, quat, log_scale, opacity, sh), the
+    screen-space ones (screen_mean2d, screen_conic, screen_rgb) and the
+    per-pixel blended counts.
+    """
+    proj = preprocess(arrays, sh_degree, camera)
+    order = depth_order(proj["depth"], proj["tile_count"])
+    scr = project64(arrays, sh_degree, camera)
+    scr["opacity"] = _f64(arrays["opacity"])
+    _, _, cnt = composite_fixed(scr, proj["rect"], order, camera, bg=bg)
+    gs = composite_backward(scr, proj["rect"], order, camera, g_image, bg=bg)
+    gp = project_backward(arrays, sh_degree, camera, gs["mean2d"], gs["conic"], gs["rgb"])
+    gp["opacity"] = gs["opacity"]
+    gp.update(screen_mean2d=gs["mean2d"], screen_conic=gs["conic"], screen_rgb=gs["rgb"], screen_opacity=gs["opacity"],
+              n_blend=cnt)
+    return gp
