@@ -173,7 +173,10 @@ typedef enum {
     GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission) */
     GS_STAGE_COMPOSITE = 6,
     GS_STAGE_READBACK = 7,     /* pair-count copy to the host + stream wait */
-    GS_STAGE_COUNT = 8
+    GS_STAGE_BACKWARD_COMPOSITE = 8,   /* gs_backward: per-tile reverse walk */
+    GS_STAGE_BACKWARD_REDUCE = 9,      /* gs_backward: per-Gaussian sums of the pair gradients */
+    GS_STAGE_BACKWARD_PROJECT = 10,    /* gs_backward: projection and colour chain rule */
+    GS_STAGE_COUNT = 11
 } gs_stage;
 
 typedef struct {
@@ -245,6 +248,46 @@ gs_status gs_composite_ex(gs_context *ctx, const gs_projected *projected, const 
  * materialised).  Synchronises `stream` once. */
 gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
                     const float bg_rgb[3], float *image_hwc, hipStream_t stream);
+
+/*
+ * Gradients of a scalar loss L with respect to the Gaussian parameters, device
+ * fp32 planes with the layout of gs_gaussians ([component][n], index g fastest).
+ * The five parameter planes are required; the screen-space planes are optional
+ * (NULL = not written).  Every plane is overwritten, not accumulated into.
+ *   mean [3][n], quat [4][n], log_scale [3][n], opacity [n], sh [K*3][n]
+ *   mean2d [2][n]   dL/d(u, v) of the projected mean
+ *   conic  [3][n]   dL/d(A, B, C), q = A dx^2 + 2 B dx dy + C dy^2
+ *   rgb    [3][n]   dL/d(r, g, b) of the SH colour
+ * A Gaussian in no tile list gets zeros.
+ */
+typedef struct {
+    float *mean;
+    float *quat;
+    float *log_scale;
+    float *opacity;
+    float *sh;
+    float *mean2d;
+    float *conic;
+    float *rgb;
+} gs_gradients;
+
+/*
+ * Backward pass of gs_preprocess + gs_bin_and_sort + gs_composite_ex (section
+ * "Pourquoi est-ce différenciable": projection, alpha compositing and the SH
+ * colour are differentiable in mean, quaternion, log-scales, opacity and SH
+ * coefficients).  `gaussians`, `projected` and `binning` must be the inputs
+ * and outputs of the last forward on this context; final_T and n_blend are the
+ * per-pixel outputs of that forward's gs_composite_ex (device [height][width]);
+ * grad_image is dL/d(image), device [height][width][3]; bg_rgb the forward's 3
+ * host floats.  Tile rectangles, per-tile order and each pixel's stopping point
+ * are held fixed (they are integer decisions).  Gradients are deterministic:
+ * per-(Gaussian, tile) partial sums are written to context memory and summed
+ * per Gaussian in a fixed order (no floating-point atomics).  Asynchronous.
+ */
+gs_status gs_backward(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
+                      const gs_projected *projected, const gs_binning *binning, const float bg_rgb[3],
+                      const float *final_T, const uint32_t *n_blend, const float *grad_image,
+                      const gs_gradients *grads, hipStream_t stream);
 
 /* Reads (and resets) the accumulated per-stage times; waits for the timed work. */
 gs_status gs_profile_read(gs_context *ctx, gs_profile *out);

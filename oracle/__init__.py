@@ -88,7 +88,7 @@ def _load():
                                                P, P, P]
         lib.oracle_composite_fixed.restype = None
         lib.oracle_composite_backward.argtypes = [i64, P, P, P, P, P, P, i64, i32, i32, P, P, ctypes.c_double,
-                                                  P, P, P, P, P]
+                                                  P, P, i64, P, P, P, P]
         lib.oracle_composite_backward.restype = None
         _lib = lib
     return _lib
@@ -299,8 +299,11 @@ def composite_fixed(screen: dict, rect, order, camera: dict, bg=(0.0, 0.0, 0.0),
 
 
 def composite_backward(screen: dict, rect, order, camera: dict, g_image, bg=(0.0, 0.0, 0.0), n_limit=None,
-                       t_eps=1e-4) -> dict:
-    """Vector-Jacobian product of composite_fixed: gradients for mean2d, conic, opacity, rgb."""
+                       t_eps=1e-4, pixels=None) -> dict:
+    """Vector-Jacobian product of composite_fixed: gradients for mean2d, conic, opacity, rgb.
+
+    pixels: optional flat indices y*W+x; only their cotangents are taken (the rest count as 0).
+    """
     lib = _load()
     W, H = camera["width"], camera["height"]
     n = np.asarray(screen["opacity"]).shape[0]
@@ -311,13 +314,15 @@ def composite_backward(screen: dict, rect, order, camera: dict, g_image, bg=(0.0
     gi = _f64(g_image).reshape(-1)
     assert gi.shape[0] == H * W * 3
     out = dict(mean2d=np.zeros((2, n)), conic=np.zeros((3, n)), opacity=np.zeros(n), rgb=np.zeros((3, n)))
+    pix = None if pixels is None else np.ascontiguousarray(pixels, np.int64)
     lib.oracle_composite_backward(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(order),
                                   order.shape[0], W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps), _ptr(gi),
+                                  _ptr(pix), 0 if pix is None else pix.shape[0],
                                   _ptr(out["mean2d"]), _ptr(out["conic"]), _ptr(out["opacity"]), _ptr(out["rgb"]))
     return out
 
 
-def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0, 0.0, 0.0)) -> dict:
+def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0, 0.0, 0.0), pixels=None) -> dict:
     """Gradient of sum(g_image * render(arrays)) for every Gaussian parameter.
 
     The lists (tile rectangles, visibility, depth order) come from the binary32
@@ -325,14 +330,17 @@ def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0
     with the per-pixel stop at T < 1e-4 found by the binary64 forward walk.
     Returns parameter gradients (mean, quat, log_scale, opacity, sh), the
     screen-space ones (screen_mean2d, screen_conic, screen_rgb) and the
-    per-pixel blended counts.
+    per-pixel blended counts (None when `pixels` restricts the cotangent to
+    the listed flat pixel indices, y*W+x).
     """
     proj = preprocess(arrays, sh_degree, camera)
     order = depth_order(proj["depth"], proj["tile_count"])
     scr = project64(arrays, sh_degree, camera)
     scr["opacity"] = _f64(arrays["opacity"])
-    _, _, cnt = composite_fixed(scr, proj["rect"], order, camera, bg=bg)
-    gs = composite_backward(scr, proj["rect"], order, camera, g_image, bg=bg)
+    cnt = None
+    if pixels is None:
+        _, _, cnt = composite_fixed(scr, proj["rect"], order, camera, bg=bg)
+    gs = composite_backward(scr, proj["rect"], order, camera, g_image, bg=bg, pixels=pixels)
     gp = project_backward(arrays, sh_degree, camera, gs["mean2d"], gs["conic"], gs["rgb"])
     gp["opacity"] = gs["opacity"]
     gp.update(screen_mean2d=gs["mean2d"], screen_conic=gs["conic"], screen_rgb=gs["rgb"], screen_opacity=gs["opacity"],

@@ -364,13 +364,14 @@ void oracle_composite_fixed(int64_t n, const double *mean2d, const double *conic
  *   dL/dA = -dx^2/2 o G dL/dalpha,  dL/dB = -dx dy o G dL/dalpha,
  *   dL/dC = -dy^2/2 o G dL/dalpha.
  * Outputs (overwritten): g_mean2d [2][n], g_conic [3][n], g_opacity [n],
- * g_rgb [3][n].
+ * g_rgb [3][n].  pixels: NULL for every pixel, else n_pix flat indices y*W+x,
+ * the only pixels whose cotangent is taken (the others count as zero).
  */
 void oracle_composite_backward(int64_t n, const double *mean2d, const double *conic, const double *opacity,
                                const double *rgb, const int32_t *rect, const int64_t *order, int64_t nv,
                                int32_t width, int32_t height, const double bg[3], const int64_t *n_limit,
-                               double t_eps, const double *g_image, double *g_mean2d, double *g_conic,
-                               double *g_opacity, double *g_rgb) {
+                               double t_eps, const double *g_image, const int64_t *pixels, int64_t n_pix,
+                               double *g_mean2d, double *g_conic, double *g_opacity, double *g_rgb) {
     memset(g_mean2d, 0, sizeof(double) * 2 * (size_t)n);
     memset(g_conic, 0, sizeof(double) * 3 * (size_t)n);
     memset(g_opacity, 0, sizeof(double) * (size_t)n);
@@ -379,47 +380,48 @@ void oracle_composite_backward(int64_t n, const double *mean2d, const double *co
     int64_t *list = (int64_t *)malloc(sizeof(int64_t) * cap);
     double *al = (double *)malloc(sizeof(double) * cap);
     double *Ts = (double *)malloc(sizeof(double) * cap);
-    for (int32_t py = 0; py < height; ++py)
-        for (int32_t px = 0; px < width; ++px) {
-            const int64_t p = (int64_t)py * width + px;
-            int64_t len = pixel_list(n, rect, order, nv, px, py, list);
-            if (n_limit && n_limit[p] < len) len = n_limit[p];
-            double T = 1.0;
-            int64_t cnt = 0;
-            for (int64_t i = 0; i < len; ++i) {
-                double G, dx, dy;
-                al[i] = pixel_alpha(n, list[i], px, py, mean2d, conic, opacity, &G, &dx, &dy);
-                Ts[i] = T;
-                T *= 1.0 - al[i];
-                ++cnt;
-                if (!n_limit && t_eps > 0.0 && T < t_eps) break;
+    if (!pixels) n_pix = (int64_t)width * height;
+    for (int64_t pi = 0; pi < n_pix; ++pi) {
+        const int64_t p = pixels ? pixels[pi] : pi;
+        const int32_t px = (int32_t)(p % width), py = (int32_t)(p / width);
+        int64_t len = pixel_list(n, rect, order, nv, px, py, list);
+        if (n_limit && n_limit[p] < len) len = n_limit[p];
+        double T = 1.0;
+        int64_t cnt = 0;
+        for (int64_t i = 0; i < len; ++i) {
+            double G, dx, dy;
+            al[i] = pixel_alpha(n, list[i], px, py, mean2d, conic, opacity, &G, &dx, &dy);
+            Ts[i] = T;
+            T *= 1.0 - al[i];
+            ++cnt;
+            if (!n_limit && t_eps > 0.0 && T < t_eps) break;
+        }
+        const double *gC = g_image + p * 3;
+        const double bg_term = T * (bg[0] * gC[0] + bg[1] * gC[1] + bg[2] * gC[2]);
+        double Bk[3] = {0.0, 0.0, 0.0};
+        for (int64_t i = cnt - 1; i >= 0; --i) {
+            const int64_t g = list[i];
+            double G, dx, dy;
+            const double alpha = pixel_alpha(n, g, px, py, mean2d, conic, opacity, &G, &dx, &dy);
+            double d_alpha = -bg_term / (1.0 - alpha);
+            for (int ch = 0; ch < 3; ++ch) {
+                const double c = rgb[(int64_t)ch * n + g];
+                g_rgb[(int64_t)ch * n + g] += alpha * Ts[i] * gC[ch];
+                d_alpha += Ts[i] * (c - Bk[ch]) * gC[ch];
+                Bk[ch] = alpha * c + (1.0 - alpha) * Bk[ch];
             }
-            const double *gC = g_image + p * 3;
-            const double bg_term = T * (bg[0] * gC[0] + bg[1] * gC[1] + bg[2] * gC[2]);
-            double Bk[3] = {0.0, 0.0, 0.0};
-            for (int64_t i = cnt - 1; i >= 0; --i) {
-                const int64_t g = list[i];
-                double G, dx, dy;
-                const double alpha = pixel_alpha(n, g, px, py, mean2d, conic, opacity, &G, &dx, &dy);
-                double d_alpha = -bg_term / (1.0 - alpha);
-                for (int ch = 0; ch < 3; ++ch) {
-                    const double c = rgb[(int64_t)ch * n + g];
-                    g_rgb[(int64_t)ch * n + g] += alpha * Ts[i] * gC[ch];
-                    d_alpha += Ts[i] * (c - Bk[ch]) * gC[ch];
-                    Bk[ch] = alpha * c + (1.0 - alpha) * Bk[ch];
-                }
-                if (opacity[g] * G < ALPHA_MAX) {
-                    g_opacity[g] += G * d_alpha;
-                    const double dq = opacity[g] * G * d_alpha;   /* dL/d(-q/2) */
-                    const double A = conic[g], B = conic[n + g], Cc = conic[2 * n + g];
-                    g_mean2d[g] += dq * (A * dx + B * dy);
-                    g_mean2d[n + g] += dq * (B * dx + Cc * dy);
-                    g_conic[g] += -0.5 * dx * dx * dq;
-                    g_conic[n + g] += -dx * dy * dq;
-                    g_conic[2 * n + g] += -0.5 * dy * dy * dq;
-                }
+            if (opacity[g] * G < ALPHA_MAX) {
+                g_opacity[g] += G * d_alpha;
+                const double dq = opacity[g] * G * d_alpha;   /* dL/d(-q/2) */
+                const double A = conic[g], B = conic[n + g], Cc = conic[2 * n + g];
+                g_mean2d[g] += dq * (A * dx + B * dy);
+                g_mean2d[n + g] += dq * (B * dx + Cc * dy);
+                g_conic[g] += -0.5 * dx * dx * dq;
+                g_conic[n + g] += -dx * dy * dq;
+                g_conic[2 * n + g] += -0.5 * dy * dy * dq;
             }
         }
+    }
     free(list);
     free(al);
     free(Ts);

@@ -51,6 +51,7 @@ int main(void) {
   P(gs_projected) O(gs_projected, tiles_x) O(gs_projected, splat) O(gs_projected, tile_count)
   P(gs_binning) O(gs_binning, keys) O(gs_binning, tile_ranges) O(gs_binning, values_unsorted)
   P(gs_profile) O(gs_profile, launches)
+  P(gs_gradients) O(gs_gradients, sh) O(gs_gradients, mean2d) O(gs_gradients, rgb)
   return 0;
 }
 """)
@@ -59,7 +60,7 @@ int main(void) {
                            "-I", "/opt/rocm/include", "-o", str(exe), str(src)])
     got = dict(line.rsplit(" ", 1) for line in subprocess.check_output([str(exe)], text=True).splitlines())
     ct = {"gs_gaussians": b.Gaussians, "gs_camera": b.Camera, "gs_projected": b.Projected,
-          "gs_binning": b.Binning, "gs_profile": b.Profile}
+          "gs_binning": b.Binning, "gs_profile": b.Profile, "gs_gradients": b.Gradients}
     for key, val in got.items():
         if "." in key:
             t, f = key.split(".")
@@ -134,6 +135,9 @@ def test_null_context_is_invalid_argument(lib):
     assert lib.gs_bin_and_sort(None, ctypes.byref(pr), ctypes.byref(cam), ctypes.byref(bn), None) == 1
     assert lib.gs_composite(None, ctypes.byref(pr), ctypes.byref(bn), ctypes.byref(cam), bg, None, None) == 1
     assert lib.gs_render(None, ctypes.byref(g), ctypes.byref(cam), bg, None, None) == 1
+    gr = b.Gradients()
+    assert lib.gs_backward(None, ctypes.byref(g), ctypes.byref(cam), ctypes.byref(pr), ctypes.byref(bn), bg,
+                           None, None, None, ctypes.byref(gr), None) == 1
     assert lib.gs_context_set_option(None, 0, 0) == 1
     assert lib.gs_profile_read(None, ctypes.byref(prof)) == 1
     assert lib.gs_context_create(None, 0) == 1

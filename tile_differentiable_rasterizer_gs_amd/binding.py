@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(_HERE, "libgsrast.so")
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_OUT_OF_MEMORY, GS_ERR_CAPACITY, GS_ERR_DEVICE = range(5)
 GS_SORT_DEPTH_FIRST, GS_SORT_KEY64 = 0, 1
 GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE = range(5)
-STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback")
+STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback",
+          "backward_composite", "backward_reduce", "backward_project")
 SPLAT_STRIDE = 16
 TILE = 16
 
 # symbols declared in include/gsrast.h
 EXPORTED = ("gs_context_create", "gs_context_destroy", "gs_context_set_option", "gs_check_arguments",
             "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
-            "gs_profile_read", "gs_status_string", "gs_last_error")
+            "gs_backward", "gs_profile_read", "gs_status_string", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -59,7 +60,14 @@ class Binning(ctypes.Structure):
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 8), ("launches", ctypes.c_int64 * 8)]
+    _fields_ = [("ms", ctypes.c_double * len(STAGES)), ("launches", ctypes.c_int64 * len(STAGES))]
+
+
+GRAD_FIELDS = ("mean", "quat", "log_scale", "opacity", "sh", "mean2d", "conic", "rgb")
+
+
+class Gradients(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in GRAD_FIELDS]
 
 
 _lib = None
@@ -89,13 +97,17 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.POINTER(ctypes.c_float), P, P, P, P, P]
     lib.gs_render.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(ctypes.c_float),
                               P, P]
+    lib.gs_backward.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(Projected),
+                                ctypes.POINTER(Binning), ctypes.POINTER(ctypes.c_float), P, P, P,
+                                ctypes.POINTER(Gradients), P]
     lib.gs_profile_read.argtypes = [P, ctypes.POINTER(Profile)]
     lib.gs_status_string.argtypes = [ctypes.c_int]
     lib.gs_status_string.restype = ctypes.c_char_p
     lib.gs_last_error.argtypes = [P]
     lib.gs_last_error.restype = ctypes.c_char_p
     for name in ("gs_context_create", "gs_context_set_option", "gs_check_arguments", "gs_preprocess",
-                 "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_profile_read"):
+                 "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_backward",
+                 "gs_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -244,6 +256,39 @@ class Rasterizer:
                                        ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)))
         return out
 
+    def backward(self, tensors: dict, sh_degree: int, camera: dict, projected: Projected, binning: Binning,
+                 final_T: torch.Tensor, n_blend: torch.Tensor, grad_image: torch.Tensor, bg=(0.0, 0.0, 0.0),
+                 screen: bool = False, out: dict | None = None, stream=None) -> dict:
+        """Gradients of sum(grad_image * image) for the last forward on this context.
+
+        final_T / n_blend: the per-pixel outputs of that forward's composite.  Returns
+        parameter gradients (mean, quat, log_scale, opacity, sh) and, with screen=True,
+        the screen-space ones (mean2d, conic, rgb).
+        """
+        g = make_gaussians(tensors, sh_degree)
+        cam = make_camera(camera)
+        H, W = cam.height, cam.width
+        self._check_image(final_T, (H, W), torch.float32)
+        self._check_image(n_blend, (H, W), torch.int32)
+        self._check_image(grad_image, (H, W, 3), torch.float32)
+        n = g.n
+        K = (sh_degree + 1) ** 2
+        shapes = dict(mean=(3, n), quat=(4, n), log_scale=(3, n), opacity=(n,), sh=(K * 3, n))
+        if screen:
+            shapes.update(mean2d=(2, n), conic=(3, n), rgb=(3, n))
+        grads = dict(out or {})
+        for k, shp in shapes.items():
+            if k not in grads:
+                grads[k] = torch.empty(shp, dtype=torch.float32, device="cuda")
+            self._check_image(grads[k], shp, torch.float32)
+        gr = Gradients(**{k: (grads[k].data_ptr() if k in grads and n else None) for k in GRAD_FIELDS})
+        bgv = (ctypes.c_float * 3)(*[float(v) for v in bg])
+        self._check(self.lib.gs_backward(self.ctx, ctypes.byref(g), ctypes.byref(cam), ctypes.byref(projected),
+                                         ctypes.byref(binning), bgv, ctypes.c_void_p(final_T.data_ptr()),
+                                         ctypes.c_void_p(n_blend.data_ptr()), ctypes.c_void_p(grad_image.data_ptr()),
+                                         ctypes.byref(gr), _stream_handle(stream)))
+        return grads
+
     def profile_read(self) -> dict:
         p = Profile()
         self._check(self.lib.gs_profile_read(self.ctx, ctypes.byref(p)))
@@ -277,3 +322,36 @@ class Rasterizer:
         p = b.values_unsorted
         out["values_unsorted"] = copy_device(p, (m,), torch.int32, stream=stream) if (p and m) else None
         return out
+
+
+class RenderFunction(torch.autograd.Function):
+    """Differentiable render through the HIP library (forward gs_preprocess + gs_bin_and_sort +
+    gs_composite_ex, backward gs_backward).  The rasterizer's context holds the forward state
+    until backward: do not render on the same Rasterizer in between."""
+
+    @staticmethod
+    def forward(ctx, mean, quat, log_scale, opacity, sh, rasterizer, sh_degree, camera, bg):
+        tensors = dict(mean=mean.detach(), quat=quat.detach(), log_scale=log_scale.detach(),
+                       opacity=opacity.detach(), sh=sh.detach())
+        pr = rasterizer.preprocess(tensors, sh_degree, camera)
+        bn = rasterizer.bin_and_sort(pr, camera)
+        H, W = int(camera["height"]), int(camera["width"])
+        final_T = torch.empty((H, W), dtype=torch.float32, device="cuda")
+        n_blend = torch.empty((H, W), dtype=torch.int32, device="cuda")
+        img = rasterizer.composite(pr, bn, camera, bg=bg, final_T=final_T, n_blend=n_blend)
+        ctx.state = (rasterizer, tensors, sh_degree, camera, pr, bn, final_T, n_blend, bg)
+        return img
+
+    @staticmethod
+    def backward(ctx, grad_image):
+        rasterizer, tensors, sh_degree, camera, pr, bn, final_T, n_blend, bg = ctx.state
+        g = rasterizer.backward(tensors, sh_degree, camera, pr, bn, final_T, n_blend,
+                                grad_image.contiguous().float(), bg=bg)
+        return g["mean"], g["quat"], g["log_scale"], g["opacity"], g["sh"], None, None, None, None
+
+
+def render_differentiable(rasterizer: "Rasterizer", params: dict, sh_degree: int, camera: dict,
+                          bg=(0.0, 0.0, 0.0)) -> torch.Tensor:
+    """Image [H, W, 3] with autograd support for the five parameter tensors in `params`."""
+    return RenderFunction.apply(params["mean"], params["quat"], params["log_scale"], params["opacity"],
+                                params["sh"], rasterizer, sh_degree, camera, tuple(float(v) for v in bg))

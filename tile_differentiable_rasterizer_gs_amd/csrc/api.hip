@@ -11,6 +11,8 @@
 //                    key64 mode: prefix sum, read-back, 64-bit key listing in
 //                    Gaussian order, radix sort over tile+depth bits, ranges
 //   gs_composite     one workgroup per tile
+//   gs_backward      per-tile reverse walk writing per-pair gradient records,
+//                    per-Gaussian sums of those records, projection chain rule
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -57,12 +59,19 @@ struct gs_context {
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
     DeviceBuffer ranges;
+    // gradients
+    DeviceBuffer pair_base, pair_grad, screen_grad, big_list, big_count;
 
     unsigned long long *host_total = nullptr;   // pinned: pair count read back once per frame
 
     // last gs_preprocess
     int64_t n = -1;
+    int32_t sh_degree = -1;
     int32_t tiles_x = 0, tiles_y = 0;
+    const float *g_mean = nullptr;             // Gaussian planes of the last gs_preprocess
+    // last binning
+    int64_t num_dups = 0;
+    const uint32_t *rank_order = nullptr;      // depth-first: rank -> Gaussian (null: rank = index)
     const uint32_t *sorted_values = nullptr;   // last binning: sorted Gaussian indices
     const uint64_t *sorted_keys = nullptr;
     int64_t pair_capacity = 0;                 // entries the pair buffers hold
@@ -272,7 +281,9 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->dval[0], &ctx->dval[1], &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch,
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
-                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges};
+                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
+                           &ctx->pair_base, &ctx->pair_grad, &ctx->screen_grad, &ctx->big_list,
+                           &ctx->big_count};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -365,6 +376,10 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     GS_TRY(span_end(ctx, stream));
 
     ctx->n = n;
+    ctx->sh_degree = g->sh_degree;
+    ctx->g_mean = g->mean;
+    ctx->num_dups = -1;
+    ctx->sorted_values = nullptr;
     ctx->tiles_x = p.tiles_x;
     ctx->tiles_y = p.tiles_y;
     out->n = n;
@@ -537,6 +552,8 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
     }
 
+    ctx->num_dups = M;
+    ctx->rank_order = order;
     out->num_dups = M;
     out->tiles_x = ctx->tiles_x;
     out->tiles_y = ctx->tiles_y;
@@ -616,6 +633,109 @@ gs_status gs_render(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam
     gs_binning bin;
     GS_TRY(bin_and_sort(ctx, &pr, 0, &bin, stream));
     return gs_composite(ctx, &pr, &bin, cam, bg, image, stream);
+}
+
+gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam, const gs_projected *pr,
+                      const gs_binning *bin, const float bg[3], const float *final_T, const uint32_t *n_blend,
+                      const float *grad_image, const gs_gradients *grads, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!g || !cam || !bin || !bg || !grads)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL gaussians, camera, binning, bg or gradients");
+    char why[160];
+    if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    GS_TRY(check_projected(ctx, pr));
+    if (g->n != ctx->n || g->sh_degree != ctx->sh_degree || g->mean != ctx->g_mean)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gaussians are not the ones of the last gs_preprocess");
+    if (ctx->num_dups < 0 || bin->tile_ranges != as<uint32_t>(ctx->ranges) || bin->values != ctx->sorted_values ||
+        bin->num_dups != ctx->num_dups || bin->tiles_x != ctx->tiles_x || bin->tiles_y != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "binning is not the last gs_bin_and_sort output of this context");
+    if ((cam->width + GS_TILE - 1) / GS_TILE != ctx->tiles_x || (cam->height + GS_TILE - 1) / GS_TILE != ctx->tiles_y)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "camera size differs from the one given to gs_preprocess");
+    if (!final_T || !n_blend || !grad_image)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL final_T, n_blend or grad_image");
+    const int64_t n = ctx->n;
+    if (n > 0 && (!grads->mean || !grads->quat || !grads->log_scale || !grads->opacity || !grads->sh))
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "a parameter gradient pointer is NULL");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    if (n == 0) return GS_OK;
+
+    const size_t nn = (size_t)n;
+    const int64_t M = ctx->num_dups;
+    GS_TRY(ensure(ctx, ctx->pair_grad, (size_t)(M > 0 ? M : 1) * kPairGrad * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->screen_grad, nn * kPairGrad * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->big_list, nn * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->big_count, sizeof(uint32_t)));
+    const uint32_t *pair_base = as<uint32_t>(ctx->offsets);   // key64 mode: offsets are in Gaussian order
+    if (ctx->rank_order) {
+        GS_TRY(ensure(ctx, ctx->pair_base, nn * sizeof(uint32_t)));
+        launch_pair_base(ctx->rank_order, as<uint32_t>(ctx->offsets), n, as<uint32_t>(ctx->pair_base), stream);
+        GS_TRY(check_launch(ctx, "pair base"));
+        pair_base = as<uint32_t>(ctx->pair_base);
+    }
+
+    CompositeBackwardParams c{};
+    c.width = cam->width;
+    c.height = cam->height;
+    c.tiles_x = ctx->tiles_x;
+    c.tiles_y = ctx->tiles_y;
+    c.splat = pr->splat;
+    c.values = bin->values;
+    c.ranges = bin->tile_ranges;
+    c.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    c.pair_base = pair_base;
+    c.final_T = final_T;
+    c.n_blend = n_blend;
+    c.grad_image = grad_image;
+    for (int i = 0; i < 3; ++i) c.bg[i] = bg[i];
+    c.pair_grad = as<float>(ctx->pair_grad);
+    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_COMPOSITE, stream));
+    if (M > 0) launch_composite_backward(c, stream);
+    GS_TRY(check_launch(ctx, "composite backward"));
+    GS_TRY(span_end(ctx, stream));
+
+    PairReduceParams r{};
+    r.n = n;
+    r.tile_count = pr->tile_count;
+    r.pair_base = pair_base;
+    r.pair_grad = as<float>(ctx->pair_grad);
+    r.screen = as<float>(ctx->screen_grad);
+    r.big_list = as<uint32_t>(ctx->big_list);
+    r.big_count = as<uint32_t>(ctx->big_count);
+    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_REDUCE, stream));
+    launch_pair_reduce(r, stream);
+    GS_TRY(check_launch(ctx, "pair reduce"));
+    GS_TRY(span_end(ctx, stream));
+
+    ProjectBackwardParams q{};
+    q.n = (int32_t)n;
+    q.sh_coeffs = (g->sh_degree + 1) * (g->sh_degree + 1);
+    q.mean = g->mean;
+    q.quat = g->quat;
+    q.log_scale = g->log_scale;
+    q.sh = g->sh;
+    memcpy(q.R, cam->R, sizeof q.R);
+    memcpy(q.t, cam->t, sizeof q.t);
+    q.fx = cam->fx;
+    q.fy = cam->fy;
+    for (int i = 0; i < 3; ++i)
+        q.cam_pos[i] = (float)-((double)cam->R[i] * cam->t[0] + (double)cam->R[3 + i] * cam->t[1] +
+                                (double)cam->R[6 + i] * cam->t[2]);
+    q.tile_count = pr->tile_count;
+    q.screen = as<float>(ctx->screen_grad);
+    q.g_mean = grads->mean;
+    q.g_quat = grads->quat;
+    q.g_log_scale = grads->log_scale;
+    q.g_opacity = grads->opacity;
+    q.g_sh = grads->sh;
+    q.g_mean2d = grads->mean2d;
+    q.g_conic = grads->conic;
+    q.g_rgb = grads->rgb;
+    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_PROJECT, stream));
+    launch_project_backward(q, stream);
+    GS_TRY(check_launch(ctx, "project backward"));
+    GS_TRY(span_end(ctx, stream));
+    return GS_OK;
 }
 
 gs_status gs_profile_read(gs_context *ctx, gs_profile *out) {

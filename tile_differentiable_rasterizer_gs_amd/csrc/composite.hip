@@ -57,11 +57,11 @@ struct Pixels {
     __device__ __forceinline__ void blend(const float4 a, const float4 b4, const float c) {
         const float dy = y - a.y;
         const float bdy = b4.x * dy;
-        const float e = (b4.y * dy) * dy + a.z;   // C' dy^2 + log2 o
+        const float e = splat_row_term(dy, b4.y, a.z);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const float dx = (i ? x1 : x0) - a.x;
-            const float q = (a.w * dx + bdy) * dx + e;
+            const float q = splat_exponent(dx, a.w, bdy, e);
             const float alpha = fminf(GS_ALPHA_MAX, __builtin_amdgcn_exp2f(q));
             const bool live = T[i] >= GS_T_EPS;
             const float w = (live ? T[i] : 0.0f) * alpha;

@@ -101,6 +101,17 @@ void launch_fill_u32(uint32_t *dst, uint32_t value, int64_t n, hipStream_t s);
 // ---------------------------------------------------------------------------
 // compositing
 // ---------------------------------------------------------------------------
+// Exponent of one splat at one pixel, in the base-2 form the splat record stores:
+// alpha = min(GS_ALPHA_MAX, 2^q) with q = (A' dx + B' dy) dx + C' dy^2 + log2(o).
+// The forward and the backward compositing kernels both build q from these two
+// helpers, so the backward recovers bit for bit the alpha the forward blended.
+__device__ __forceinline__ float splat_row_term(float dy, float Cp, float log2_o) {
+    return __builtin_fmaf(dy, Cp * dy, log2_o);   // C' dy^2 + log2 o
+}
+__device__ __forceinline__ float splat_exponent(float dx, float Ap, float bdy, float row_term) {
+    return __builtin_fmaf(dx, __builtin_fmaf(Ap, dx, bdy), row_term);
+}
+
 struct CompositeParams {
     int32_t width, height, tiles_x, tiles_y;
     const float *splat;
@@ -113,5 +124,55 @@ struct CompositeParams {
     unsigned long long *blend_total;  // optional
 };
 void launch_composite(const CompositeParams &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// gradients
+// ---------------------------------------------------------------------------
+// Per-pair gradient record: the contribution of one (Gaussian, tile) pair, summed
+// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b.
+constexpr int kPairGrad = 9;
+
+// pair_base[order[r]] = offsets[r]: first listing position of each Gaussian's pairs
+void launch_pair_base(const uint32_t *order, const uint32_t *offsets, int64_t n, uint32_t *pair_base,
+                      hipStream_t s);
+
+struct CompositeBackwardParams {
+    int32_t width, height, tiles_x, tiles_y;
+    const float *splat;
+    const uint32_t *values, *ranges;
+    const uint2 *rect;
+    const uint32_t *pair_base;   // [n] listing position of each Gaussian's first pair
+    const float *final_T;        // [H][W] from the forward
+    const uint32_t *n_blend;     // [H][W] from the forward
+    const float *grad_image;     // [H][W][3]
+    float bg[3];
+    float *pair_grad;            // [pairs][kPairGrad], indexed by listing position
+};
+void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s);
+
+struct PairReduceParams {
+    int64_t n;
+    const uint32_t *tile_count, *pair_base;
+    const float *pair_grad;
+    float *screen;               // [kPairGrad][n]
+    uint32_t *big_list;          // [n] Gaussians with long pair lists
+    uint32_t *big_count;         // device counter, zeroed by the launcher
+};
+void launch_pair_reduce(const PairReduceParams &p, hipStream_t s);
+
+struct ProjectBackwardParams {
+    int32_t n;
+    int32_t sh_coeffs;
+    const float *mean, *quat, *log_scale, *sh;
+    float R[9];
+    float t[3];
+    float fx, fy;
+    float cam_pos[3];
+    const uint32_t *tile_count;
+    const float *screen;         // [kPairGrad][n]
+    float *g_mean, *g_quat, *g_log_scale, *g_opacity, *g_sh;
+    float *g_mean2d, *g_conic, *g_rgb;   // optional copies of the screen-space gradients
+};
+void launch_project_backward(const ProjectBackwardParams &p, hipStream_t s);
 
 }  // namespace gsr
