@@ -5,9 +5,11 @@ pair listing, tile sort, ranges, composite) with the scene already resident in
 HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sort-mode 0|1]
-                  [--no-cpu-baseline] [--calibration-copy]
+                  [--no-cpu-baseline] [--no-backward] [--calibration-copy]
 
 A workload with several cameras (the 32-view orbit) renders its views round-robin.
+The JSON line also carries the backward pass (gs_backward for a fixed random
+image cotangent) timed on its own and as part of a forward + backward step.
 """
 from __future__ import annotations
 
@@ -30,6 +32,11 @@ VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 # opacity product (1); clamp (1); T*alpha (1); three colour multiply-adds (3);
 # transmittance update (1); stop test (1)
 COMPOSITE_OPS_PER_PAIR = 17
+# lane-ops per blended pair in the backward walk: alpha as in the forward (dx, dy, exponent
+# 4, exp2, clamp: 7); 1 - alpha and its reciprocal (2); T recovery (1); dL/dalpha from the
+# colour behind and the background (7); three colour-behind updates (6); colour gradient
+# weights (4); clamp test and opacity gradient (3); dL/dQ (2); u, v, A, B, C gradients (10)
+BACKWARD_OPS_PER_PAIR = 42
 
 
 def log(msg):
@@ -92,6 +99,76 @@ def cpu_baseline(scene, cam, pixels_target=8192):
                         f"({t3 - t2:.2f}s, {threads} threads) scaled to {npx} pixels"))
 
 
+def time_backward(r, dev, scene, cams, img, bg, steps, blends):
+    """Backward pass (gs_backward) for a fixed random cotangent dL/dimage, timed alone on one
+    view's forward state, and as part of forward (with per-pixel state) + backward steps."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    H, W = cams[0]["height"], cams[0]["width"]
+    deg = scene.sh_degree
+    T = torch.empty((H, W), dtype=torch.float32, device="cuda")
+    nb = torch.empty((H, W), dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    gimg = torch.randn((H, W, 3), generator=gen, device="cuda", dtype=torch.float32)
+    K = (deg + 1) ** 2
+    n = scene.n
+    grads = {k: torch.empty(shp, dtype=torch.float32, device="cuda")
+             for k, shp in dict(mean=(3, n), quat=(4, n), log_scale=(3, n), opacity=(n,), sh=(K * 3, n)).items()}
+
+    def forward(c):
+        pr = r.preprocess(dev, deg, c)
+        bn = r.bin_and_sort(pr, c)
+        r.composite(pr, bn, c, bg=bg, out=img, final_T=T, n_blend=nb)
+        return pr, bn
+
+    def backward(c, pr, bn):
+        r.backward(dev, deg, c, pr, bn, T, nb, gimg, bg=bg, out=grads)
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(3):
+        backward(cams[i % len(cams)], *forward(cams[i % len(cams)]))
+    torch.cuda.synchronize()
+    # forward + backward steps
+    start.record()
+    for i in range(steps):
+        c = cams[i % len(cams)]
+        backward(c, *forward(c))
+    stop.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / steps
+    # backward alone, repeated on the first view's forward state
+    pr, bn = forward(cams[0])
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        backward(cams[0], pr, bn)
+    stop.record()
+    torch.cuda.synchronize()
+    bwd_ms = start.elapsed_time(stop) / steps
+    # per-stage split of the backward
+    r.set_option(binding.GS_OPT_PROFILE, 1)
+    r.profile_read()
+    for _ in range(steps):
+        backward(cams[0], pr, bn)
+    prof = r.profile_read()
+    r.set_option(binding.GS_OPT_PROFILE, 0)
+    stage = {k: ms / steps for k, (ms, cnt) in prof.items() if cnt and k.startswith("backward")}
+    comp = stage.get("backward_composite", 0.0)
+    ops = blends * BACKWARD_OPS_PER_PAIR
+    gops = ops / (comp * 1e-3) / 1e9 if comp else 0.0
+    log(f"backward: {bwd_ms:.4f} ms alone, forward+backward step {step_ms:.4f} ms; stages " +
+        ", ".join(f"{k}={v:.4f}" for k, v in stage.items()))
+    return dict(ms=round(bwd_ms, 5), train_step_ms=round(step_ms, 5),
+                train_steps_per_s=round(1000.0 / step_ms, 2),
+                stage_ms={k: round(v, 5) for k, v in stage.items()},
+                composite_roofline=dict(bound="alu", achieved=round(gops / 1e3, 3),
+                                        peak=round(VALU_PEAK_GOPS / 1e3, 3), unit="Tlane-op/s",
+                                        frac=round(gops / VALU_PEAK_GOPS, 4), ops=ops),
+                cotangent="standard normal per pixel channel, seed 0")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +177,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--sort-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one 1 GiB read + 1 GiB write elementwise kernel first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -226,6 +304,8 @@ def main():
         "context": "pages: '100+ FPS at 1080p' for a trained scene on an unnamed GPU; 147 fps for 6M splats on an "
                    "RTX 3080 Ti (resolution not stated)",
     }
+    if not args.no_backward:
+        out["backward"] = time_backward(r, dev, scene, cams, img, bg, args.steps, blends)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(scene, cam)

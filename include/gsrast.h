@@ -174,8 +174,8 @@ typedef enum {
     GS_STAGE_COMPOSITE = 6,
     GS_STAGE_READBACK = 7,     /* pair-count copy to the host + stream wait */
     GS_STAGE_BACKWARD_COMPOSITE = 8,   /* gs_backward: per-tile reverse walk */
-    GS_STAGE_BACKWARD_REDUCE = 9,      /* gs_backward: per-Gaussian sums of the pair gradients */
-    GS_STAGE_BACKWARD_PROJECT = 10,    /* gs_backward: projection and colour chain rule */
+    GS_STAGE_BACKWARD_OFFSETS = 9,     /* gs_backward: pair offsets in Gaussian order (depth-first mode) */
+    GS_STAGE_BACKWARD_GAUSSIAN = 10,   /* gs_backward: per-Gaussian sums + projection and colour chain rule */
     GS_STAGE_COUNT = 11
 } gs_stage;
 

@@ -11,8 +11,9 @@
 //                    key64 mode: prefix sum, read-back, 64-bit key listing in
 //                    Gaussian order, radix sort over tile+depth bits, ranges
 //   gs_composite     one workgroup per tile
-//   gs_backward      per-tile reverse walk writing per-pair gradient records,
-//                    per-Gaussian sums of those records, projection chain rule
+//   gs_backward      (depth-first mode: prefix sum of tile counts in Gaussian order,)
+//                    per-tile reverse walk writing per-pair gradient records,
+//                    per-Gaussian sums of those records + projection chain rule
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -60,7 +61,7 @@ struct gs_context {
     // per-tile
     DeviceBuffer ranges;
     // gradients
-    DeviceBuffer pair_base, pair_grad, screen_grad, big_list, big_count;
+    DeviceBuffer pair_base, pair_grad, scan_total;
 
     unsigned long long *host_total = nullptr;   // pinned: pair count read back once per frame
 
@@ -282,8 +283,7 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
-                           &ctx->pair_base, &ctx->pair_grad, &ctx->screen_grad, &ctx->big_list,
-                           &ctx->big_count};
+                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -662,15 +662,19 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
 
     const size_t nn = (size_t)n;
     const int64_t M = ctx->num_dups;
-    GS_TRY(ensure(ctx, ctx->pair_grad, (size_t)(M > 0 ? M : 1) * kPairGrad * sizeof(float)));
-    GS_TRY(ensure(ctx, ctx->screen_grad, nn * kPairGrad * sizeof(float)));
-    GS_TRY(ensure(ctx, ctx->big_list, nn * sizeof(uint32_t)));
-    GS_TRY(ensure(ctx, ctx->big_count, sizeof(uint32_t)));
-    const uint32_t *pair_base = as<uint32_t>(ctx->offsets);   // key64 mode: offsets are in Gaussian order
+    GS_TRY(ensure(ctx, ctx->pair_grad, (size_t)(M > 0 ? M : 1) * kPairStride * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->scan_total, sizeof(unsigned long long)));
+    // Gaussian g's records start at pair_base[g] = sum of tile_count over indices below g:
+    // key64 mode listed the pairs in that order, depth-first mode needs its own prefix sum
+    const uint32_t *pair_base = as<uint32_t>(ctx->offsets);
     if (ctx->rank_order) {
         GS_TRY(ensure(ctx, ctx->pair_base, nn * sizeof(uint32_t)));
-        launch_pair_base(ctx->rank_order, as<uint32_t>(ctx->offsets), n, as<uint32_t>(ctx->pair_base), stream);
-        GS_TRY(check_launch(ctx, "pair base"));
+        GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_OFFSETS, stream));
+        launch_scan(pr->tile_count, nullptr, as<uint32_t>(ctx->pair_base), n,
+                    as<unsigned long long>(ctx->scan_total),
+                    as<unsigned long long>(ctx->scan_scratch), stream);
+        GS_TRY(check_launch(ctx, "pair offsets"));
+        GS_TRY(span_end(ctx, stream));
         pair_base = as<uint32_t>(ctx->pair_base);
     }
 
@@ -694,20 +698,7 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     GS_TRY(check_launch(ctx, "composite backward"));
     GS_TRY(span_end(ctx, stream));
 
-    PairReduceParams r{};
-    r.n = n;
-    r.tile_count = pr->tile_count;
-    r.pair_base = pair_base;
-    r.pair_grad = as<float>(ctx->pair_grad);
-    r.screen = as<float>(ctx->screen_grad);
-    r.big_list = as<uint32_t>(ctx->big_list);
-    r.big_count = as<uint32_t>(ctx->big_count);
-    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_REDUCE, stream));
-    launch_pair_reduce(r, stream);
-    GS_TRY(check_launch(ctx, "pair reduce"));
-    GS_TRY(span_end(ctx, stream));
-
-    ProjectBackwardParams q{};
+    GaussianBackwardParams q{};
     q.n = (int32_t)n;
     q.sh_coeffs = (g->sh_degree + 1) * (g->sh_degree + 1);
     q.mean = g->mean;
@@ -722,7 +713,8 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
         q.cam_pos[i] = (float)-((double)cam->R[i] * cam->t[0] + (double)cam->R[3 + i] * cam->t[1] +
                                 (double)cam->R[6 + i] * cam->t[2]);
     q.tile_count = pr->tile_count;
-    q.screen = as<float>(ctx->screen_grad);
+    q.pair_base = pair_base;
+    q.pair_grad = as<float>(ctx->pair_grad);
     q.g_mean = grads->mean;
     q.g_quat = grads->quat;
     q.g_log_scale = grads->log_scale;
@@ -731,9 +723,9 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     q.g_mean2d = grads->mean2d;
     q.g_conic = grads->conic;
     q.g_rgb = grads->rgb;
-    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_PROJECT, stream));
-    launch_project_backward(q, stream);
-    GS_TRY(check_launch(ctx, "project backward"));
+    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_GAUSSIAN, stream));
+    launch_gaussian_backward(q, stream);
+    GS_TRY(check_launch(ctx, "gaussian backward"));
     GS_TRY(span_end(ctx, stream));
     return GS_OK;
 }

@@ -8,8 +8,8 @@
 //
 // Three stages, all deterministic (no floating-point atomics):
 //
-// 1. composite_backward_kernel: one 256-thread workgroup per 16x16 tile, one pixel
-//    per thread.  The tile's list is walked back to front from the largest blended
+// 1. composite_backward_kernel: one wave64 per 16x16 tile, four pixels of a row per
+//    lane.  The tile's list is walked back to front from the largest blended
 //    count of its pixels.  A pixel recovers T_i = T_{i+1} / (1 - alpha_i) from the
 //    forward's final transmittance, recomputing alpha_i exactly as the forward did,
 //    and accumulates the colour behind entry i, B_{i-1} = alpha_i c_i + (1 - alpha_i) B_i:
@@ -20,36 +20,32 @@
 //      dL/do = G dL/dalpha,  dL/dQ = -alpha dL/dalpha / 2,
 //      dL/du = -2 (A dx + B dy) dL/dQ,  dL/dv = -2 (B dx + C dy) dL/dQ,
 //      dL/d(A, B, C) = (dx^2, 2 dx dy, dy^2) dL/dQ.
-//    The nine per-pixel values of each entry are summed over the wave (DPP row
-//    shifts, then the four row totals) and over the four waves in a fixed order, and
-//    written as one record at the pair's position in the listing (Gaussian-major),
-//    so each Gaussian's records are contiguous.  Entries past the last one any pixel
-//    of the tile blended get a zero record, so every record is written each call.
-// 2. pair_reduce_*: sum of each Gaussian's records (one thread per Gaussian for short
-//    lists, one workgroup per Gaussian for long ones) -> screen-space gradients.
-// 3. project_backward_kernel: chain rule through the projection (conic <- 2D
-//    covariance <- J W Sigma W^T J^T <- R(q) diag(exp(log s)), mean2d <- t) and the
-//    SH colour (sections "L'étape de projection", "Étape 5", "Étape 6"), in fp32.
+//    A lane sums its four pixels into three moments of d_i = alpha_i dL/dalpha_i
+//    (sum d, sum d dx, sum d dx^2) from which the conic and mean terms follow; the
+//    nine values per entry are summed over the wave by a butterfly that folds two
+//    values per level, and written as one record at the pair's position in the
+//    listing (Gaussian-major), so each Gaussian's records are contiguous.  Entries
+//    past the last one any pixel of the tile blended get a zero record, so every
+//    record is written each call.
+// 2. gaussian_backward_kernel: sum of each Gaussian's records (a 16-lane row per
+//    Gaussian, reading consecutive records), then the chain rule through the projection
+//    (conic <- 2D covariance <- J W Sigma W^T J^T <- R(q) diag(exp(log s)), mean2d <-
+//    t) and the SH colour (sections "L'étape de projection", "Étape 5", "Étape 6"),
+//    in fp32.  Records are laid out in Gaussian-index order (pair_base = exclusive
+//    prefix of tile counts over the index), so this stage reads and writes the
+//    parameter planes coalesced.
 #include "gs_internal.h"
 
 namespace gsr {
 namespace {
 
 // ---------------------------------------------------------------------------
-// listing position of each Gaussian's first pair
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void pair_base_kernel(const uint32_t *__restrict__ order,
-                                                           const uint32_t *__restrict__ offsets, int64_t n,
-                                                           uint32_t *__restrict__ pair_base) {
-    const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (r < n) pair_base[order[r]] = offsets[r];
-}
-
-// ---------------------------------------------------------------------------
 // compositing backward
 // ---------------------------------------------------------------------------
-constexpr int kBwdThreads = 256;   // one pixel per thread, 4 waves of 16x4 pixels
-constexpr int kBwdWaves = kBwdThreads / kWave;
+// One wave64 per tile; lane l owns the four pixels (4i + (l & 3), l >> 2), i = 0..3,
+// of one row, which share dy and the row terms of the exponent.
+constexpr int kBwdThreads = kWave;
+constexpr int kBwdPix = 4;         // pixels per lane
 constexpr int kBwdBatch = 64;      // entries staged per LDS batch
 
 template <int kCtrl>
@@ -71,178 +67,171 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// One butterfly level that reduces two values at once: lanes with `mask` clear keep
+// a + partner's a, the others b + partner's b.
+__device__ __forceinline__ float fold(float a, float b, int mask, bool upper) {
+    const float send = upper ? a : b;
+    return (upper ? b : a) + __shfl_xor(send, mask);
+}
+
+// Sums nine per-lane values over the wave.  On return lane l holds, in `packed`, the
+// total of value ((l >> 3) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 5) & 1), and every
+// lane holds the total of v[8] in `last`.  Fixed association order (deterministic).
+__device__ __forceinline__ void reduce9(const float v[9], int lane, float &packed, float &last) {
+    const bool u32 = lane & 32, u16 = lane & 16, u8 = lane & 8;
+    const float r0 = fold(v[0], v[1], 32, u32), r1 = fold(v[2], v[3], 32, u32);
+    const float r2 = fold(v[4], v[5], 32, u32), r3 = fold(v[6], v[7], 32, u32);
+    float e = v[8] + __shfl_xor(v[8], 32);
+    const float s0 = fold(r0, r1, 16, u16), s1 = fold(r2, r3, 16, u16);
+    e += __shfl_xor(e, 16);
+    float t = fold(s0, s1, 8, u8);
+    e += __shfl_xor(e, 8);
+#pragma unroll
+    for (int m = 4; m > 0; m >>= 1) {
+        t += __shfl_xor(t, m);
+        e += __shfl_xor(e, m);
+    }
+    packed = t;
+    last = e;
+}
+
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
-    // staged entries: u, v, A', B' | C', log2 o, 1/o, zero-opacity flag | A, B, C, r | g, b
+    // staged entries: u, v, A', B' | C', log2 o, 1/o (1 when o = 0), alpha cap |
+    // A, B, C, r | g, b, clamp threshold of 2^q below which alpha is smooth
     __shared__ float4 s_fwd[kBwdBatch], s_fwd2[kBwdBatch], s_conic[kBwdBatch];
-    __shared__ float2 s_col[kBwdBatch];
+    __shared__ float4 s_col[kBwdBatch];
     __shared__ uint32_t s_pos[kBwdBatch];
-    __shared__ float s_red[kBwdWaves][kBwdBatch][kPairGrad];
-    __shared__ uint32_t s_wave_max[kBwdWaves];
 
     const int tile = blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int ix = tile_x * kTile + (threadIdx.x & 15);
-    const int iy = tile_y * kTile + (threadIdx.x >> 4);
-    const bool inside = ix < p.width && iy < p.height;
-    const float x = (float)ix, y = (float)iy;
+    const int lane = threadIdx.x;
+    const int iy = tile_y * kTile + (lane >> 2);
+    const float y = (float)iy;
 
-    float T = 0.0f, gC0 = 0.0f, gC1 = 0.0f, gC2 = 0.0f, bg_term = 0.0f;
-    uint32_t n_mine = 0;
-    if (inside) {
-        const size_t pix = (size_t)iy * p.width + ix;
-        T = p.final_T[pix];
-        n_mine = p.n_blend[pix];
-        gC0 = p.grad_image[pix * 3 + 0];
-        gC1 = p.grad_image[pix * 3 + 1];
-        gC2 = p.grad_image[pix * 3 + 2];
-        bg_term = T * (p.bg[0] * gC0 + p.bg[1] * gC1 + p.bg[2] * gC2);
+    float x[kBwdPix], T[kBwdPix], gC[kBwdPix][3], bg_term[kBwdPix];
+    uint32_t n_mine[kBwdPix];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kBwdPix; ++i) {
+        const int ix = tile_x * kTile + 4 * i + (lane & 3);
+        x[i] = (float)ix;
+        T[i] = 0.0f;
+        gC[i][0] = gC[i][1] = gC[i][2] = 0.0f;
+        bg_term[i] = 0.0f;
+        n_mine[i] = 0;
+        if (ix < p.width && iy < p.height) {
+            const size_t pix = (size_t)iy * p.width + ix;
+            T[i] = p.final_T[pix];
+            n_mine[i] = p.n_blend[pix];
+            gC[i][0] = p.grad_image[pix * 3 + 0];
+            gC[i][1] = p.grad_image[pix * 3 + 1];
+            gC[i][2] = p.grad_image[pix * 3 + 2];
+            bg_term[i] = T[i] * (p.bg[0] * gC[i][0] + p.bg[1] * gC[i][1] + p.bg[2] * gC[i][2]);
+        }
+        m = max(m, n_mine[i]);
     }
     const uint32_t start = p.ranges[2 * tile], end = p.ranges[2 * tile + 1];
-    // entries a pixel never reached need no work: start from the tile's largest count
-    uint32_t m = n_mine;
+    // entries no pixel reached need no work: start from the tile's largest count
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if (lane == 0) s_wave_max[wave] = m;
-    __syncthreads();
-    uint32_t n_max = 0;
-#pragma unroll
-    for (int w = 0; w < kBwdWaves; ++w) n_max = max(n_max, s_wave_max[w]);
-    n_max = min(n_max, end - start);
+    const uint32_t n_max = min(m, end - start);
 
     const uint32_t ty = (uint32_t)tile_y, tx = (uint32_t)tile_x;
-    // entries no pixel of the tile reached contribute nothing: their records are zero
-    for (uint32_t e = start + n_max + threadIdx.x; e < end; e += kBwdThreads) {
+    // ... and contribute nothing: their records are zero
+    for (uint32_t e = start + n_max + lane; e < end; e += kBwdThreads) {
         const uint32_t g = p.values[e];
         const uint2 rc = p.rect[g];
         const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-        float *rec = p.pair_grad + (size_t)(p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0)) * kPairGrad;
+        float *rec = p.pair_grad + (size_t)(p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0)) * kPairStride;
 #pragma unroll
         for (int c = 0; c < kPairGrad; ++c) rec[c] = 0.0f;
     }
 
-    float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;   // colour behind the current entry
+    float B[kBwdPix][3];   // colour behind the current entry
+#pragma unroll
+    for (int i = 0; i < kBwdPix; ++i) B[i][0] = B[i][1] = B[i][2] = 0.0f;
+    // lane l writes value slot ((l >> 3) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 5) & 1)
+    const int slot = ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1);
     for (int hi = (int)n_max; hi > 0; hi -= kBwdBatch) {
         const int lo = hi > kBwdBatch ? hi - kBwdBatch : 0;
         const int cnt = hi - lo;
-        __syncthreads();   // the previous batch's staged entries and sums are consumed
-        if ((int)threadIdx.x < cnt) {
-            const uint32_t e = start + (uint32_t)(lo + threadIdx.x);
+        __syncthreads();   // the previous batch's staged entries are consumed
+        if (lane < cnt) {
+            const uint32_t e = start + (uint32_t)(lo + lane);
             const uint32_t g = p.values[e];
             const float4 *rec = reinterpret_cast<const float4 *>(p.splat) + (size_t)g * 4;
             const float4 r0 = rec[0], r1 = rec[1], r2 = rec[2], r3 = rec[3];
             const float o = r0.z;
             const bool zero_o = !(o > 0.0f);
-            s_fwd[threadIdx.x] = make_float4(r0.x, r0.y, r0.w, r1.x);
-            s_fwd2[threadIdx.x] = make_float4(r1.y, zero_o ? 0.0f : __log2f(o), zero_o ? 0.0f : 1.0f / o,
-                                              zero_o ? 1.0f : 0.0f);
-            s_conic[threadIdx.x] = make_float4(r2.z, r2.w, r3.x, r1.z);
-            s_col[threadIdx.x] = make_float2(r1.w, r2.x);
+            s_fwd[lane] = make_float4(r0.x, r0.y, r0.w, r1.x);
+            // o = 0: alpha is 0 and 2^q (with log2 o taken as 0) is G itself, never clamped
+            s_fwd2[lane] = make_float4(r1.y, zero_o ? 0.0f : __log2f(o), zero_o ? 1.0f : 1.0f / o,
+                                       zero_o ? 0.0f : GS_ALPHA_MAX);
+            s_conic[lane] = make_float4(r2.z, r2.w, r3.x, r1.z);
+            s_col[lane] = make_float4(r1.w, r2.x, zero_o ? INFINITY : GS_ALPHA_MAX, 0.0f);
             const uint2 rc = p.rect[g];
             const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-            s_pos[threadIdx.x] = p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0);
+            s_pos[lane] = p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0);
         }
         __syncthreads();
         for (int k = cnt - 1; k >= 0; --k) {
-            const float4 f = s_fwd[k], f2 = s_fwd2[k], cn = s_conic[k];
-            const float2 cl = s_col[k];
-            const bool zero_o = f2.w != 0.0f;
-            const float dx = x - f.x, dy = y - f.y;
-            const float q = splat_exponent(dx, f.z, f.w * dy, splat_row_term(dy, f2.x, f2.y));
-            const float raw = __builtin_amdgcn_exp2f(q);   // o G, or G when o == 0
-            const float alpha = zero_o ? 0.0f : fminf(GS_ALPHA_MAX, raw);
-            const bool active = (uint32_t)(lo + k) < n_mine;
-            const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
-            const float Ti = T * rinv;
-            const float c0 = cn.w, c1 = cl.x, c2 = cl.y;
-            float d_alpha = Ti * ((c0 - B0) * gC0 + (c1 - B1) * gC1 + (c2 - B2) * gC2) - bg_term * rinv;
-            const float wgt = alpha * Ti;
-            const bool smooth = zero_o || raw < GS_ALPHA_MAX;   // below the clamp
-            d_alpha = active ? d_alpha : 0.0f;
-            const float G = zero_o ? raw : raw * f2.z;
-            const float d_o = smooth ? G * d_alpha : 0.0f;
-            const float dQ = smooth ? -0.5f * alpha * d_alpha : 0.0f;
-            float v[kPairGrad];
-            v[0] = -2.0f * dQ * (cn.x * dx + cn.y * dy);   // u
-            v[1] = -2.0f * dQ * (cn.y * dx + cn.z * dy);   // v
-            v[2] = dQ * dx * dx;                            // A
-            v[3] = 2.0f * dQ * dx * dy;                     // B
-            v[4] = dQ * dy * dy;                            // C
-            v[5] = d_o;
-            const float wa = active ? wgt : 0.0f;
-            v[6] = wa * gC0;
-            v[7] = wa * gC1;
-            v[8] = wa * gC2;
-            if (active) {
-                B0 = __builtin_fmaf(alpha, c0 - B0, B0);
-                B1 = __builtin_fmaf(alpha, c1 - B1, B1);
-                B2 = __builtin_fmaf(alpha, c2 - B2, B2);
-                T = Ti;
+            const float4 f = s_fwd[k], f2 = s_fwd2[k], cn = s_conic[k], cl = s_col[k];
+            const uint32_t idx = (uint32_t)(lo + k);
+            const float c[3] = {cn.w, cl.x, cl.y};
+            const float dy = y - f.y;
+            const float bdy = f.w * dy;
+            const float row = splat_row_term(dy, f2.x, f2.y);
+            // per-lane sums over the four pixels:
+            //   d_i = dL/dalpha_i * alpha_i where alpha is below the clamp (else 0)
+            //   S0 = sum d_i, S1 = sum d_i dx_i, S2 = sum d_i dx_i^2
+            float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, So = 0.0f, Sc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < kBwdPix; ++i) {
+                const float dx = x[i] - f.x;
+                const float raw = __builtin_amdgcn_exp2f(splat_exponent(dx, f.z, bdy, row));
+                const bool active = idx < n_mine[i];
+                const float alpha = active ? fminf(f2.w, raw) : 0.0f;
+                const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
+                const float Ti = T[i] * rinv;
+                const float cb0 = c[0] - B[i][0], cb1 = c[1] - B[i][1], cb2 = c[2] - B[i][2];
+                const float dot = cb0 * gC[i][0] + cb1 * gC[i][1] + cb2 * gC[i][2];
+                const float d_alpha = active ? __builtin_fmaf(Ti, dot, -bg_term[i] * rinv) : 0.0f;
+                const float w = alpha * Ti;
+                Sc[0] = __builtin_fmaf(w, gC[i][0], Sc[0]);
+                Sc[1] = __builtin_fmaf(w, gC[i][1], Sc[1]);
+                Sc[2] = __builtin_fmaf(w, gC[i][2], Sc[2]);
+                B[i][0] = __builtin_fmaf(alpha, cb0, B[i][0]);
+                B[i][1] = __builtin_fmaf(alpha, cb1, B[i][1]);
+                B[i][2] = __builtin_fmaf(alpha, cb2, B[i][2]);
+                T[i] = active ? Ti : T[i];
+                const bool smooth = raw < cl.z;
+                So = __builtin_fmaf(smooth ? raw * f2.z : 0.0f, d_alpha, So);
+                const float d = (smooth ? alpha : 0.0f) * d_alpha;
+                S0 += d;
+                const float t = d * dx;
+                S1 += t;
+                S2 = __builtin_fmaf(t, dx, S2);
             }
-#pragma unroll
-            for (int c = 0; c < kPairGrad; ++c) {
-                const float s = wave_sum(v[c]);
-                if (lane == 0) s_red[wave][k][c] = s;
-            }
+            // dL/dQ_i = -d_i / 2 with Q = A dx^2 + 2 B dx dy + C dy^2:
+            //   dL/du = A S1 + B dy S0,  dL/dv = B S1 + C dy S0,
+            //   dL/dA = -S2 / 2,  dL/dB = -dy S1,  dL/dC = -dy^2 S0 / 2
+            const float dyS0 = dy * S0;
+            float v[9];
+            v[0] = __builtin_fmaf(cn.x, S1, cn.y * dyS0);
+            v[1] = __builtin_fmaf(cn.y, S1, cn.z * dyS0);
+            v[2] = -0.5f * S2;
+            v[3] = -dy * S1;
+            v[4] = -0.5f * dy * dyS0;
+            v[5] = So;
+            v[6] = Sc[0];
+            v[7] = Sc[1];
+            v[8] = Sc[2];
+            float packed, last;
+            reduce9(v, lane, packed, last);
+            float *rec = p.pair_grad + (size_t)s_pos[k] * kPairStride;
+            if ((lane & 7) == 0) rec[slot] = packed;
+            if (lane == 0) rec[8] = last;
         }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < cnt * kPairGrad; idx += kBwdThreads) {
-            const int k = idx / kPairGrad, c = idx - k * kPairGrad;
-            const float s = (s_red[0][k][c] + s_red[1][k][c]) + (s_red[2][k][c] + s_red[3][k][c]);
-            p.pair_grad[(size_t)s_pos[k] * kPairGrad + c] = s;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// per-Gaussian sums of the pair records
-// ---------------------------------------------------------------------------
-constexpr uint32_t kShortList = 32;   // pairs summed by one thread; longer lists get a workgroup
-
-__global__ __launch_bounds__(kBlock) void pair_reduce_short_kernel(PairReduceParams p) {
-    const int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (g >= p.n) return;
-    const uint32_t count = p.tile_count[g];
-    if (count > kShortList) {
-        p.big_list[atomicAdd(p.big_count, 1u)] = (uint32_t)g;
-        return;
-    }
-    float acc[kPairGrad];
-#pragma unroll
-    for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
-    const float *rec = p.pair_grad + (size_t)(count ? p.pair_base[g] : 0) * kPairGrad;
-    for (uint32_t i = 0; i < count; ++i)
-#pragma unroll
-        for (int c = 0; c < kPairGrad; ++c) acc[c] += rec[(size_t)i * kPairGrad + c];
-#pragma unroll
-    for (int c = 0; c < kPairGrad; ++c) p.screen[c * p.n + g] = acc[c];
-}
-
-__global__ __launch_bounds__(kBlock) void pair_reduce_long_kernel(PairReduceParams p) {
-    __shared__ float s_part[kBlock / kWave][kPairGrad];
-    const uint32_t total = *p.big_count;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    for (uint32_t b = blockIdx.x; b < total; b += gridDim.x) {
-        const uint32_t g = p.big_list[b];
-        const uint32_t count = p.tile_count[g];
-        const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairGrad;
-        float acc[kPairGrad];
-#pragma unroll
-        for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
-        for (uint32_t i = threadIdx.x; i < count; i += kBlock)
-#pragma unroll
-            for (int c = 0; c < kPairGrad; ++c) acc[c] += rec[(size_t)i * kPairGrad + c];
-#pragma unroll
-        for (int c = 0; c < kPairGrad; ++c) {
-            const float s = wave_sum(acc[c]);
-            if (lane == 0) s_part[wave][c] = s;
-        }
-        __syncthreads();
-        if (threadIdx.x < kPairGrad) {
-            const int c = threadIdx.x;
-            p.screen[c * p.n + g] = (s_part[0][c] + s_part[1][c]) + (s_part[2][c] + s_part[3][c]);
-        }
-        __syncthreads();
     }
 }
 
@@ -326,25 +315,25 @@ __device__ inline void sh_basis_values(float x, float y, float z, float Y[K]) {
     }
 }
 
+// Zero gradients for a Gaussian in no tile list (the image does not depend on it).
 template <int K>
-__global__ __launch_bounds__(kBlock) void project_backward_kernel(ProjectBackwardParams p) {
-    const int g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= p.n) return;
+__device__ inline void gaussian_zero(const GaussianBackwardParams &p, int g) {
     const int n = p.n;
-    if (p.tile_count[g] == 0) {   // in no tile list: the image does not depend on it
-        for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = 0.0f;
-        for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = 0.0f;
-        for (int i = 0; i < 3; ++i) p.g_log_scale[i * n + g] = 0.0f;
-        p.g_opacity[g] = 0.0f;
-        for (int i = 0; i < 3 * K; ++i) p.g_sh[(size_t)i * n + g] = 0.0f;
-        if (p.g_mean2d) p.g_mean2d[g] = p.g_mean2d[n + g] = 0.0f;
-        if (p.g_conic) p.g_conic[g] = p.g_conic[n + g] = p.g_conic[2 * n + g] = 0.0f;
-        if (p.g_rgb) p.g_rgb[g] = p.g_rgb[n + g] = p.g_rgb[2 * n + g] = 0.0f;
-        return;
-    }
-    float sg[kPairGrad];
-#pragma unroll
-    for (int c = 0; c < kPairGrad; ++c) sg[c] = p.screen[(size_t)c * n + g];
+    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = 0.0f;
+    for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = 0.0f;
+    for (int i = 0; i < 3; ++i) p.g_log_scale[i * n + g] = 0.0f;
+    p.g_opacity[g] = 0.0f;
+    for (int i = 0; i < 3 * K; ++i) p.g_sh[(size_t)i * n + g] = 0.0f;
+    if (p.g_mean2d) p.g_mean2d[g] = p.g_mean2d[n + g] = 0.0f;
+    if (p.g_conic) p.g_conic[g] = p.g_conic[n + g] = p.g_conic[2 * n + g] = 0.0f;
+    if (p.g_rgb) p.g_rgb[g] = p.g_rgb[n + g] = p.g_rgb[2 * n + g] = 0.0f;
+}
+
+// Chain rule from the screen-space gradients sg (u, v, A, B, C, opacity, r, g, b) of
+// Gaussian g to its parameters.
+template <int K>
+__device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad]) {
+    const int n = p.n;
     const float gu = sg[0], gv = sg[1], gA = sg[2], gB = sg[3], gC = sg[4];
     p.g_opacity[g] = sg[5];
     if (p.g_mean2d) { p.g_mean2d[g] = gu; p.g_mean2d[n + g] = gv; }
@@ -493,13 +482,71 @@ __global__ __launch_bounds__(kBlock) void project_backward_kernel(ProjectBackwar
     for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = gmu[i] + (gd[i] - d[i] * radial) * idn;
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// per-Gaussian sums of the pair records + chain rule
+// ---------------------------------------------------------------------------
+// A wave owns 64 consecutive Gaussians.  In 16 rounds, each 16-lane row sums the
+// records of one Gaussian (lane i takes records i, i + 16, ...: a row reads 16
+// consecutive records), reduces them with DPP row shifts and parks the nine sums in
+// LDS; then every lane runs the chain rule of one Gaussian, so the parameter planes
+// are read and written coalesced.
+constexpr int kGaussPerWave = kWave;
+constexpr int kRowLanes = 16;
 
-void launch_pair_base(const uint32_t *order, const uint32_t *offsets, int64_t n, uint32_t *pair_base,
-                      hipStream_t s) {
-    if (n <= 0) return;
-    pair_base_kernel<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(order, offsets, n, pair_base);
+// Sum over a 16-lane row; the row's last lane (15) holds the result.
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_shifted<0x111>(v);
+    v += dpp_shifted<0x112>(v);
+    v += dpp_shifted<0x114>(v);
+    v += dpp_shifted<0x118>(v);
+    return v;
 }
+
+template <int K>
+__global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackwardParams p) {
+    __shared__ float s_sum[kBlock / kWave][kGaussPerWave][kPairGrad + 1];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int row = lane / kRowLanes, li = lane & (kRowLanes - 1);
+    const int64_t g0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kGaussPerWave;
+    for (int round = 0; round < kGaussPerWave / 4; ++round) {
+        const int gl = 4 * round + row;
+        const int64_t g = g0 + gl;
+        const uint32_t count = g < p.n ? p.tile_count[g] : 0u;
+        float acc[kPairGrad];
+#pragma unroll
+        for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
+        if (count) {
+            const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
+            for (uint32_t i = li; i < count; i += kRowLanes) {
+                const float *r = rec + (size_t)i * kPairStride;
+                const float4 a = *reinterpret_cast<const float4 *>(r);
+                const float4 b = *reinterpret_cast<const float4 *>(r + 4);
+                const float c8 = r[8];
+                acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+                acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+                acc[8] += c8;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kPairGrad; ++c) {
+            const float v = row_sum(acc[c]);
+            if (li == kRowLanes - 1) s_sum[wave][gl][c] = v;
+        }
+    }
+    __syncthreads();
+    const int64_t g = g0 + lane;
+    if (g >= p.n) return;
+    if (p.tile_count[g] == 0) {
+        gaussian_zero<K>(p, (int)g);
+        return;
+    }
+    float sg[kPairGrad];
+#pragma unroll
+    for (int c = 0; c < kPairGrad; ++c) sg[c] = s_sum[wave][lane][c];
+    gaussian_vjp<K>(p, (int)g, sg);
+}
+
+}  // namespace
 
 void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s) {
     const unsigned tiles = (unsigned)(p.tiles_x * p.tiles_y);
@@ -507,22 +554,15 @@ void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s) 
     composite_backward_kernel<<<tiles, kBwdThreads, 0, s>>>(p);
 }
 
-void launch_pair_reduce(const PairReduceParams &p, hipStream_t s) {
+void launch_gaussian_backward(const GaussianBackwardParams &p, hipStream_t s) {
     if (p.n <= 0) return;
-    launch_fill_u32(p.big_count, 0u, 1, s);
-    pair_reduce_short_kernel<<<(unsigned)((p.n + kBlock - 1) / kBlock), kBlock, 0, s>>>(p);
-    const int64_t groups = p.n < 2048 ? p.n : 2048;
-    pair_reduce_long_kernel<<<(unsigned)groups, kBlock, 0, s>>>(p);
-}
-
-void launch_project_backward(const ProjectBackwardParams &p, hipStream_t s) {
-    if (p.n <= 0) return;
-    const dim3 grid((p.n + kBlock - 1) / kBlock);
+    constexpr int per_group = (kBlock / kWave) * kGaussPerWave;
+    const dim3 grid((p.n + per_group - 1) / per_group);
     switch (p.sh_coeffs) {
-        case 1: project_backward_kernel<1><<<grid, kBlock, 0, s>>>(p); break;
-        case 4: project_backward_kernel<4><<<grid, kBlock, 0, s>>>(p); break;
-        case 9: project_backward_kernel<9><<<grid, kBlock, 0, s>>>(p); break;
-        default: project_backward_kernel<16><<<grid, kBlock, 0, s>>>(p); break;
+        case 1: gaussian_backward_kernel<1><<<grid, kBlock, 0, s>>>(p); break;
+        case 4: gaussian_backward_kernel<4><<<grid, kBlock, 0, s>>>(p); break;
+        case 9: gaussian_backward_kernel<9><<<grid, kBlock, 0, s>>>(p); break;
+        default: gaussian_backward_kernel<16><<<grid, kBlock, 0, s>>>(p); break;
     }
 }
 

@@ -129,38 +129,27 @@ void launch_composite(const CompositeParams &p, hipStream_t s);
 // gradients
 // ---------------------------------------------------------------------------
 // Per-pair gradient record: the contribution of one (Gaussian, tile) pair, summed
-// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b.
+// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b; padded
+// to 12 floats so a record is three aligned 16-byte loads.
 constexpr int kPairGrad = 9;
-
-// pair_base[order[r]] = offsets[r]: first listing position of each Gaussian's pairs
-void launch_pair_base(const uint32_t *order, const uint32_t *offsets, int64_t n, uint32_t *pair_base,
-                      hipStream_t s);
+constexpr int kPairStride = 12;
 
 struct CompositeBackwardParams {
     int32_t width, height, tiles_x, tiles_y;
     const float *splat;
     const uint32_t *values, *ranges;
     const uint2 *rect;
-    const uint32_t *pair_base;   // [n] listing position of each Gaussian's first pair
+    const uint32_t *pair_base;   // [n] record index of each Gaussian's first pair
     const float *final_T;        // [H][W] from the forward
     const uint32_t *n_blend;     // [H][W] from the forward
     const float *grad_image;     // [H][W][3]
     float bg[3];
-    float *pair_grad;            // [pairs][kPairGrad], indexed by listing position
+    float *pair_grad;            // [pairs][kPairStride]: Gaussian g's pair k (row-major
+                                 // over its rectangle) at pair_base[g] + k
 };
 void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s);
 
-struct PairReduceParams {
-    int64_t n;
-    const uint32_t *tile_count, *pair_base;
-    const float *pair_grad;
-    float *screen;               // [kPairGrad][n]
-    uint32_t *big_list;          // [n] Gaussians with long pair lists
-    uint32_t *big_count;         // device counter, zeroed by the launcher
-};
-void launch_pair_reduce(const PairReduceParams &p, hipStream_t s);
-
-struct ProjectBackwardParams {
+struct GaussianBackwardParams {
     int32_t n;
     int32_t sh_coeffs;
     const float *mean, *quat, *log_scale, *sh;
@@ -168,11 +157,11 @@ struct ProjectBackwardParams {
     float t[3];
     float fx, fy;
     float cam_pos[3];
-    const uint32_t *tile_count;
-    const float *screen;         // [kPairGrad][n]
+    const uint32_t *tile_count, *pair_base;
+    const float *pair_grad;
     float *g_mean, *g_quat, *g_log_scale, *g_opacity, *g_sh;
-    float *g_mean2d, *g_conic, *g_rgb;   // optional copies of the screen-space gradients
+    float *g_mean2d, *g_conic, *g_rgb;   // optional screen-space gradients
 };
-void launch_project_backward(const ProjectBackwardParams &p, hipStream_t s);
+void launch_gaussian_backward(const GaussianBackwardParams &p, hipStream_t s);
 
 }  // namespace gsr
