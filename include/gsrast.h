@@ -170,11 +170,11 @@ typedef enum {
     GS_STAGE_SCAN = 2,         /* prefix sum of tile counts */
     GS_STAGE_DUPLICATE = 3,
     GS_STAGE_TILE_SORT = 4,    /* radix passes over the pair list */
-    GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission) */
+    GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission), heaviest-first tile launch order */
     GS_STAGE_COMPOSITE = 6,
     GS_STAGE_READBACK = 7,     /* pair-count copy to the host + stream wait */
     GS_STAGE_BACKWARD_COMPOSITE = 8,   /* gs_backward: per-tile reverse walk */
-    GS_STAGE_BACKWARD_OFFSETS = 9,     /* gs_backward: pair offsets in Gaussian order (depth-first mode) */
+    GS_STAGE_BACKWARD_SETUP = 9,       /* gs_backward: tile launch order; pair offsets in Gaussian order (depth-first mode) */
     GS_STAGE_BACKWARD_GAUSSIAN = 10,   /* gs_backward: per-Gaussian sums + projection and colour chain rule */
     GS_STAGE_COUNT = 11
 } gs_stage;

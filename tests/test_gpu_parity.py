@@ -186,6 +186,20 @@ def test_screen_filling_gaussians(mode):
     assert (g["tile_count"] == tiles).sum() >= 5
 
 
+def test_above_ordered_tile_limit():
+    # 4200 x 4200 has 263 x 263 = 69169 tiles, above the 65536 the heaviest-first launch
+    # order handles: compositing then runs in tile order; integers in full, sampled image
+    rng = np.random.default_rng(12)
+    n = 400
+    means = np.c_[rng.uniform(-1.0, 1.0, (n, 2)), rng.uniform(2, 4, n)]
+    arr = _arrays(means, rng.standard_normal((n, 4)), rng.uniform(-3.5, -1.5, (n, 3)), rng.uniform(0.1, 1.0, n),
+                  rng.normal(0, 0.5, (n, 1, 3)))
+    cam = _cam(4200, 4200, f=2000.0)
+    pix = rng.choice(4200 * 4200, 4096, replace=False)
+    note("above ordered tile limit")
+    _full_check(arr, 0, cam, bg=(0.2, 0.1, 0.0), full_image=False, pixels=pix)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_equal_depths_keep_index_order(mode):
     n = 40

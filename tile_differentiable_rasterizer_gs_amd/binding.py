@@ -19,7 +19,7 @@ GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_OUT_OF_MEMORY, GS_ERR_CAPACITY, GS_ERR_DE
 GS_SORT_DEPTH_FIRST, GS_SORT_KEY64 = 0, 1
 GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE = range(5)
 STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback",
-          "backward_composite", "backward_offsets", "backward_gaussian")
+          "backward_composite", "backward_setup", "backward_gaussian")
 SPLAT_STRIDE = 16
 TILE = 16
 

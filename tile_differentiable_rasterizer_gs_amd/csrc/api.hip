@@ -10,9 +10,10 @@
 //                    the tile id, tile ranges (+ optional 64-bit keys)
 //                    key64 mode: prefix sum, read-back, 64-bit key listing in
 //                    Gaussian order, radix sort over tile+depth bits, ranges
-//   gs_composite     one workgroup per tile
-//   gs_backward      (depth-first mode: prefix sum of tile counts in Gaussian order,)
-//                    per-tile reverse walk writing per-pair gradient records,
+//   gs_composite     one workgroup per tile, heaviest tiles (longest lists) first
+//   gs_backward      tile order by reverse-walk length (depth-first mode: prefix sum
+//                    of tile counts in Gaussian order), per-tile reverse walk writing
+//                    per-pair gradient records,
 //                    per-Gaussian sums of those records + projection chain rule
 #include <hip/hip_runtime.h>
 
@@ -59,7 +60,7 @@ struct gs_context {
     // per-pair
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
-    DeviceBuffer ranges;
+    DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd;
     // gradients
     DeviceBuffer pair_base, pair_grad, scan_total;
 
@@ -74,6 +75,7 @@ struct gs_context {
     int64_t num_dups = 0;
     const uint32_t *rank_order = nullptr;      // depth-first: rank -> Gaussian (null: rank = index)
     const uint32_t *sorted_values = nullptr;   // last binning: sorted Gaussian indices
+    const uint32_t *launch_order = nullptr;    // last binning: heaviest-first tile order (or null)
     const uint64_t *sorted_keys = nullptr;
     int64_t pair_capacity = 0;                 // entries the pair buffers hold
     hipEvent_t total_ready = nullptr;          // pair count has reached host_total
@@ -283,7 +285,8 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
-                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total};
+                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order,
+                           &ctx->tile_weight, &ctx->tile_order_bwd};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -425,6 +428,7 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     GS_TRY(span_end(ctx, stream));
     ctx->sorted_values = nullptr;
     ctx->sorted_keys = nullptr;
+    ctx->launch_order = nullptr;
     if (ctx->n <= 0) return GS_OK;
 
     DuplicateParams d{};
@@ -483,6 +487,12 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
     launch_ranges(r, stream);
     GS_TRY(check_launch(ctx, "ranges"));
+    TileOrderParams o{};
+    o.tiles = (int32_t)tiles;
+    o.ranges = r.ranges;
+    o.order = as<uint32_t>(ctx->tile_order);
+    ctx->launch_order = launch_tile_order(o, stream) ? o.order : nullptr;
+    GS_TRY(check_launch(ctx, "tile order"));
     GS_TRY(span_end(ctx, stream));
     ctx->sorted_values = as<uint32_t>(ctx->pval[buf]);
     return GS_OK;
@@ -503,6 +513,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     GS_TRY(ensure(ctx, ctx->scan_scratch, (size_t)scan_scratch_words((int64_t)nn) * 8));
     GS_TRY(ensure(ctx, ctx->total, 8));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->tile_order, (size_t)tiles * sizeof(uint32_t)));
     if (!ctx->total_ready) GS_HIP(ctx, hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming));
     unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
@@ -610,6 +621,7 @@ gs_status gs_composite_ex(gs_context *ctx, const gs_projected *pr, const gs_binn
     c.final_T = final_T;
     c.n_blend = n_blend;
     c.blend_total = blend_total;
+    c.tile_order = ctx->launch_order;
     GS_TRY(span_begin(ctx, GS_STAGE_COMPOSITE, stream));
     launch_composite(c, stream);
     GS_TRY(check_launch(ctx, "composite"));
@@ -666,17 +678,32 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     GS_TRY(ensure(ctx, ctx->scan_total, sizeof(unsigned long long)));
     // Gaussian g's records start at pair_base[g] = sum of tile_count over indices below g:
     // key64 mode listed the pairs in that order, depth-first mode needs its own prefix sum
+    const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
+    GS_TRY(ensure(ctx, ctx->tile_weight, (size_t)tiles * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->tile_order_bwd, (size_t)tiles * sizeof(uint32_t)));
     const uint32_t *pair_base = as<uint32_t>(ctx->offsets);
+    GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_SETUP, stream));
     if (ctx->rank_order) {
         GS_TRY(ensure(ctx, ctx->pair_base, nn * sizeof(uint32_t)));
-        GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_OFFSETS, stream));
         launch_scan(pr->tile_count, nullptr, as<uint32_t>(ctx->pair_base), n,
                     as<unsigned long long>(ctx->scan_total),
                     as<unsigned long long>(ctx->scan_scratch), stream);
         GS_TRY(check_launch(ctx, "pair offsets"));
-        GS_TRY(span_end(ctx, stream));
         pair_base = as<uint32_t>(ctx->pair_base);
     }
+    // heaviest-first launch order by each tile's reverse-walk length
+    const uint32_t *bwd_order = nullptr;
+    if (M > 0 && tiles <= kMaxOrderedTiles) {
+        launch_backward_tile_weight(n_blend, bin->tile_ranges, cam->width, cam->height, ctx->tiles_x, ctx->tiles_y,
+                                    as<uint32_t>(ctx->tile_weight), stream);
+        TileOrderParams o{};
+        o.tiles = (int32_t)tiles;
+        o.weights = as<uint32_t>(ctx->tile_weight);
+        o.order = as<uint32_t>(ctx->tile_order_bwd);
+        if (launch_tile_order(o, stream)) bwd_order = o.order;
+        GS_TRY(check_launch(ctx, "backward tile order"));
+    }
+    GS_TRY(span_end(ctx, stream));
 
     CompositeBackwardParams c{};
     c.width = cam->width;
@@ -693,6 +720,7 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     c.grad_image = grad_image;
     for (int i = 0; i < 3; ++i) c.bg[i] = bg[i];
     c.pair_grad = as<float>(ctx->pair_grad);
+    c.tile_order = bwd_order;
     GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_COMPOSITE, stream));
     if (M > 0) launch_composite_backward(c, stream);
     GS_TRY(check_launch(ctx, "composite backward"));

@@ -95,6 +95,76 @@ __device__ __forceinline__ void reduce9(const float v[9], int lane, float &packe
     last = e;
 }
 
+// Per-lane state of the reverse walk: four pixels of one row.
+struct BwdLane {
+    float y;
+    float x[kBwdPix], T[kBwdPix], gC[kBwdPix][3], bg_term[kBwdPix];
+    float B[kBwdPix][3];   // colour behind the current entry
+    uint32_t n[kBwdPix];   // entries the pixel blended in the forward
+
+    // Entry idx of the tile list (staged f, f2, cn, cl): steps the four pixels back over it
+    // and returns the lane's nine partial sums (u, v, A, B, C, opacity, r, g, b).
+    __device__ __forceinline__ void entry(const float4 f, const float4 f2, const float4 cn, const float4 cl,
+                                          uint32_t idx, float v[kPairGrad]) {
+        const float c[3] = {cn.w, cl.x, cl.y};
+        const float dy = y - f.y;
+        const float bdy = f.w * dy;
+        const float row = splat_row_term(dy, f2.x, f2.y);
+        // d_i = dL/dalpha_i * alpha_i where alpha is below the clamp (else 0);
+        // S0 = sum d_i, S1 = sum d_i dx_i, S2 = sum d_i dx_i^2
+        float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, So = 0.0f, Sc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < kBwdPix; ++i) {
+            const float dx = x[i] - f.x;
+            const float raw = __builtin_amdgcn_exp2f(splat_exponent(dx, f.z, bdy, row));
+            const bool active = idx < n[i];
+            const float alpha = active ? fminf(f2.w, raw) : 0.0f;
+            const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
+            const float Ti = T[i] * rinv;
+            const float cb0 = c[0] - B[i][0], cb1 = c[1] - B[i][1], cb2 = c[2] - B[i][2];
+            const float dot = cb0 * gC[i][0] + cb1 * gC[i][1] + cb2 * gC[i][2];
+            const float d_alpha = active ? __builtin_fmaf(Ti, dot, -bg_term[i] * rinv) : 0.0f;
+            const float w = alpha * Ti;
+            Sc[0] = __builtin_fmaf(w, gC[i][0], Sc[0]);
+            Sc[1] = __builtin_fmaf(w, gC[i][1], Sc[1]);
+            Sc[2] = __builtin_fmaf(w, gC[i][2], Sc[2]);
+            B[i][0] = __builtin_fmaf(alpha, cb0, B[i][0]);
+            B[i][1] = __builtin_fmaf(alpha, cb1, B[i][1]);
+            B[i][2] = __builtin_fmaf(alpha, cb2, B[i][2]);
+            T[i] = active ? Ti : T[i];
+            const bool smooth = raw < cl.z;
+            So = __builtin_fmaf(smooth ? raw * f2.z : 0.0f, d_alpha, So);
+            const float d = (smooth ? alpha : 0.0f) * d_alpha;
+            S0 += d;
+            const float t = d * dx;
+            S1 += t;
+            S2 = __builtin_fmaf(t, dx, S2);
+        }
+        // dL/dQ_i = -d_i / 2 with Q = A dx^2 + 2 B dx dy + C dy^2:
+        //   dL/du = A S1 + B dy S0,  dL/dv = B S1 + C dy S0,
+        //   dL/dA = -S2 / 2,  dL/dB = -dy S1,  dL/dC = -dy^2 S0 / 2
+        const float dyS0 = dy * S0;
+        v[0] = __builtin_fmaf(cn.x, S1, cn.y * dyS0);
+        v[1] = __builtin_fmaf(cn.y, S1, cn.z * dyS0);
+        v[2] = -0.5f * S2;
+        v[3] = -dy * S1;
+        v[4] = -0.5f * dy * dyS0;
+        v[5] = So;
+        v[6] = Sc[0];
+        v[7] = Sc[1];
+        v[8] = Sc[2];
+    }
+};
+
+// Wave sums of the nine partials, stored as one pair record.
+__device__ __forceinline__ void store_record(const float v[kPairGrad], int lane, float *rec) {
+    float packed, last;
+    reduce9(v, lane, packed, last);
+    // lane l holds value ((l >> 3) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 5) & 1)
+    if ((lane & 7) == 0) rec[((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1)] = packed;
+    if (lane == 0) rec[8] = last;
+}
+
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
     // staged entries: u, v, A', B' | C', log2 o, 1/o (1 when o = 0), alpha cap |
     // A, B, C, r | g, b, clamp threshold of 2^q below which alpha is smooth
@@ -102,33 +172,33 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
     __shared__ float4 s_col[kBwdBatch];
     __shared__ uint32_t s_pos[kBwdBatch];
 
-    const int tile = blockIdx.x;
+    const int tile = p.tile_order ? (int)p.tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
     const int lane = threadIdx.x;
     const int iy = tile_y * kTile + (lane >> 2);
-    const float y = (float)iy;
 
-    float x[kBwdPix], T[kBwdPix], gC[kBwdPix][3], bg_term[kBwdPix];
-    uint32_t n_mine[kBwdPix];
+    BwdLane px;
+    px.y = (float)iy;
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < kBwdPix; ++i) {
         const int ix = tile_x * kTile + 4 * i + (lane & 3);
-        x[i] = (float)ix;
-        T[i] = 0.0f;
-        gC[i][0] = gC[i][1] = gC[i][2] = 0.0f;
-        bg_term[i] = 0.0f;
-        n_mine[i] = 0;
+        px.x[i] = (float)ix;
+        px.T[i] = 0.0f;
+        px.gC[i][0] = px.gC[i][1] = px.gC[i][2] = 0.0f;
+        px.bg_term[i] = 0.0f;
+        px.B[i][0] = px.B[i][1] = px.B[i][2] = 0.0f;
+        px.n[i] = 0;
         if (ix < p.width && iy < p.height) {
             const size_t pix = (size_t)iy * p.width + ix;
-            T[i] = p.final_T[pix];
-            n_mine[i] = p.n_blend[pix];
-            gC[i][0] = p.grad_image[pix * 3 + 0];
-            gC[i][1] = p.grad_image[pix * 3 + 1];
-            gC[i][2] = p.grad_image[pix * 3 + 2];
-            bg_term[i] = T[i] * (p.bg[0] * gC[i][0] + p.bg[1] * gC[i][1] + p.bg[2] * gC[i][2]);
+            px.T[i] = p.final_T[pix];
+            px.n[i] = p.n_blend[pix];
+            px.gC[i][0] = p.grad_image[pix * 3 + 0];
+            px.gC[i][1] = p.grad_image[pix * 3 + 1];
+            px.gC[i][2] = p.grad_image[pix * 3 + 2];
+            px.bg_term[i] = px.T[i] * (p.bg[0] * px.gC[i][0] + p.bg[1] * px.gC[i][1] + p.bg[2] * px.gC[i][2]);
         }
-        m = max(m, n_mine[i]);
+        m = max(m, px.n[i]);
     }
     const uint32_t start = p.ranges[2 * tile], end = p.ranges[2 * tile + 1];
     // entries no pixel reached need no work: start from the tile's largest count
@@ -147,11 +217,6 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         for (int c = 0; c < kPairGrad; ++c) rec[c] = 0.0f;
     }
 
-    float B[kBwdPix][3];   // colour behind the current entry
-#pragma unroll
-    for (int i = 0; i < kBwdPix; ++i) B[i][0] = B[i][1] = B[i][2] = 0.0f;
-    // lane l writes value slot ((l >> 3) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 5) & 1)
-    const int slot = ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1);
     for (int hi = (int)n_max; hi > 0; hi -= kBwdBatch) {
         const int lo = hi > kBwdBatch ? hi - kBwdBatch : 0;
         const int cnt = hi - lo;
@@ -175,62 +240,9 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         }
         __syncthreads();
         for (int k = cnt - 1; k >= 0; --k) {
-            const float4 f = s_fwd[k], f2 = s_fwd2[k], cn = s_conic[k], cl = s_col[k];
-            const uint32_t idx = (uint32_t)(lo + k);
-            const float c[3] = {cn.w, cl.x, cl.y};
-            const float dy = y - f.y;
-            const float bdy = f.w * dy;
-            const float row = splat_row_term(dy, f2.x, f2.y);
-            // per-lane sums over the four pixels:
-            //   d_i = dL/dalpha_i * alpha_i where alpha is below the clamp (else 0)
-            //   S0 = sum d_i, S1 = sum d_i dx_i, S2 = sum d_i dx_i^2
-            float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, So = 0.0f, Sc[3] = {0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < kBwdPix; ++i) {
-                const float dx = x[i] - f.x;
-                const float raw = __builtin_amdgcn_exp2f(splat_exponent(dx, f.z, bdy, row));
-                const bool active = idx < n_mine[i];
-                const float alpha = active ? fminf(f2.w, raw) : 0.0f;
-                const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
-                const float Ti = T[i] * rinv;
-                const float cb0 = c[0] - B[i][0], cb1 = c[1] - B[i][1], cb2 = c[2] - B[i][2];
-                const float dot = cb0 * gC[i][0] + cb1 * gC[i][1] + cb2 * gC[i][2];
-                const float d_alpha = active ? __builtin_fmaf(Ti, dot, -bg_term[i] * rinv) : 0.0f;
-                const float w = alpha * Ti;
-                Sc[0] = __builtin_fmaf(w, gC[i][0], Sc[0]);
-                Sc[1] = __builtin_fmaf(w, gC[i][1], Sc[1]);
-                Sc[2] = __builtin_fmaf(w, gC[i][2], Sc[2]);
-                B[i][0] = __builtin_fmaf(alpha, cb0, B[i][0]);
-                B[i][1] = __builtin_fmaf(alpha, cb1, B[i][1]);
-                B[i][2] = __builtin_fmaf(alpha, cb2, B[i][2]);
-                T[i] = active ? Ti : T[i];
-                const bool smooth = raw < cl.z;
-                So = __builtin_fmaf(smooth ? raw * f2.z : 0.0f, d_alpha, So);
-                const float d = (smooth ? alpha : 0.0f) * d_alpha;
-                S0 += d;
-                const float t = d * dx;
-                S1 += t;
-                S2 = __builtin_fmaf(t, dx, S2);
-            }
-            // dL/dQ_i = -d_i / 2 with Q = A dx^2 + 2 B dx dy + C dy^2:
-            //   dL/du = A S1 + B dy S0,  dL/dv = B S1 + C dy S0,
-            //   dL/dA = -S2 / 2,  dL/dB = -dy S1,  dL/dC = -dy^2 S0 / 2
-            const float dyS0 = dy * S0;
-            float v[9];
-            v[0] = __builtin_fmaf(cn.x, S1, cn.y * dyS0);
-            v[1] = __builtin_fmaf(cn.y, S1, cn.z * dyS0);
-            v[2] = -0.5f * S2;
-            v[3] = -dy * S1;
-            v[4] = -0.5f * dy * dyS0;
-            v[5] = So;
-            v[6] = Sc[0];
-            v[7] = Sc[1];
-            v[8] = Sc[2];
-            float packed, last;
-            reduce9(v, lane, packed, last);
-            float *rec = p.pair_grad + (size_t)s_pos[k] * kPairStride;
-            if ((lane & 7) == 0) rec[slot] = packed;
-            if (lane == 0) rec[8] = last;
+            float v[kPairGrad];
+            px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), v);
+            store_record(v, lane, p.pair_grad + (size_t)s_pos[k] * kPairStride);
         }
     }
 }

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
     __shared__ float s_c[2][kBatch];
     const float *__restrict__ splat = p.splat;
     const uint32_t *__restrict__ values = p.values;
-    const int tile = blockIdx.x;
+    const int tile = p.tile_order ? (int)p.tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int ix = tile_x * kTile + (lane & 7);

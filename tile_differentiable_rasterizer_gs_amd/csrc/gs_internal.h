@@ -122,8 +122,24 @@ struct CompositeParams {
     float *final_T;              // optional [H][W]
     uint32_t *n_blend;           // optional [H][W]
     unsigned long long *blend_total;  // optional
+    const uint32_t *tile_order;  // optional launch order: workgroup b composites tile_order[b]
 };
 void launch_composite(const CompositeParams &p, hipStream_t s);
+
+// Heaviest-first tile order (bucket sort of per-tile weights: explicit `weights`, else
+// the tile list lengths from `ranges`).  Returns false, launching nothing, when there
+// are more than kMaxOrderedTiles tiles (callers then launch in tile order).
+constexpr int32_t kMaxOrderedTiles = 1 << 16;
+struct TileOrderParams {
+    int32_t tiles;
+    const uint32_t *ranges;
+    const uint32_t *weights;
+    uint32_t *order;
+};
+bool launch_tile_order(const TileOrderParams &p, hipStream_t s);
+// weights[t] = min(largest n_blend over tile t's pixels, tile t's list length)
+void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges, int32_t width, int32_t height,
+                                 int32_t tiles_x, int32_t tiles_y, uint32_t *weights, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // gradients
@@ -146,6 +162,7 @@ struct CompositeBackwardParams {
     float bg[3];
     float *pair_grad;            // [pairs][kPairStride]: Gaussian g's pair k (row-major
                                  // over its rectangle) at pair_base[g] + k
+    const uint32_t *tile_order;  // optional launch order: workgroup b walks tile_order[b]
 };
 void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s);
 
