@@ -156,13 +156,15 @@ struct BwdLane {
     }
 };
 
-// Wave sums of the nine partials, stored as one pair record.
+// Wave sums of the nine partials, stored as one whole record by the first kPairStride lanes.
 __device__ __forceinline__ void store_record(const float v[kPairGrad], int lane, float *rec) {
     float packed, last;
     reduce9(v, lane, packed, last);
-    // lane l holds value ((l >> 3) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 5) & 1)
-    if ((lane & 7) == 0) rec[((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1)] = packed;
-    if (lane == 0) rec[8] = last;
+    // value j < 8 sits in lane 32 (j & 1) + 16 ((j >> 1) & 1) + 8 ((j >> 2) & 1)
+    const int j = lane & 7;
+    const int src = 32 * (j & 1) + 16 * ((j >> 1) & 1) + 8 * ((j >> 2) & 1);
+    const float mine = __shfl(packed, src);
+    if (lane < kPairStride) rec[lane] = lane < 8 ? mine : (lane == 8 ? last : 0.0f);
 }
 
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
@@ -212,9 +214,10 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         const uint32_t g = p.values[e];
         const uint2 rc = p.rect[g];
         const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-        float *rec = p.pair_grad + (size_t)(p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0)) * kPairStride;
+        float4 *rec = reinterpret_cast<float4 *>(
+            p.pair_grad + (size_t)(p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0)) * kPairStride);
 #pragma unroll
-        for (int c = 0; c < kPairGrad; ++c) rec[c] = 0.0f;
+        for (int c = 0; c < kPairStride / 4; ++c) rec[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 
     for (int hi = (int)n_max; hi > 0; hi -= kBwdBatch) {

@@ -146,7 +146,7 @@ void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges
 // ---------------------------------------------------------------------------
 // Per-pair gradient record: the contribution of one (Gaussian, tile) pair, summed
 // over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b; padded
-// to 12 floats so a record is three aligned 16-byte loads.
+// with zeros to 48 bytes, always written whole (three aligned 16-byte pieces).
 constexpr int kPairGrad = 9;
 constexpr int kPairStride = 12;
 
