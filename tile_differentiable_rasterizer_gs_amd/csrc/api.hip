@@ -60,7 +60,7 @@ struct gs_context {
     // per-pair
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
-    DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd;
+    DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
     DeviceBuffer pair_base, pair_grad, scan_total;
 
@@ -286,7 +286,7 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
                            &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order,
-                           &ctx->tile_weight, &ctx->tile_order_bwd};
+                           &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -681,6 +681,7 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
     GS_TRY(ensure(ctx, ctx->tile_weight, (size_t)tiles * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->tile_order_bwd, (size_t)tiles * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->tile_cut, (size_t)tiles * sizeof(unsigned long long)));
     const uint32_t *pair_base = as<uint32_t>(ctx->offsets);
     GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_SETUP, stream));
     if (ctx->rank_order) {
@@ -721,6 +722,7 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     for (int i = 0; i < 3; ++i) c.bg[i] = bg[i];
     c.pair_grad = as<float>(ctx->pair_grad);
     c.tile_order = bwd_order;
+    c.cut = as<unsigned long long>(ctx->tile_cut);
     GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_COMPOSITE, stream));
     if (M > 0) launch_composite_backward(c, stream);
     GS_TRY(check_launch(ctx, "composite backward"));
@@ -742,6 +744,10 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
                                 (double)cam->R[6 + i] * cam->t[2]);
     q.tile_count = pr->tile_count;
     q.pair_base = pair_base;
+    q.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    q.depth = pr->depth;
+    q.cut = as<unsigned long long>(ctx->tile_cut);
+    q.tiles_x = ctx->tiles_x;
     q.pair_grad = as<float>(ctx->pair_grad);
     q.g_mean = grads->mean;
     q.g_quat = grads->quat;

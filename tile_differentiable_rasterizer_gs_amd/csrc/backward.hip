@@ -25,8 +25,9 @@
 //    nine values per entry are summed over the wave by a butterfly that folds two
 //    values per level, and written as one record at the pair's position in the
 //    listing (Gaussian-major), so each Gaussian's records are contiguous.  Entries
-//    past the last one any pixel of the tile blended get a zero record, so every
-//    record is written each call.
+//    past the last one any pixel of the tile blended contribute nothing and get no
+//    record: the tile publishes the (depth bits, index) key of its deepest walked
+//    entry, and the next stage reads exactly the records at or below it.
 // 2. gaussian_backward_kernel: sum of each Gaussian's records (a 16-lane row per
 //    Gaussian, reading consecutive records), then the chain rule through the projection
 //    (conic <- 2D covariance <- J W Sigma W^T J^T <- R(q) diag(exp(log s)), mean2d <-
@@ -209,15 +210,17 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
     const uint32_t n_max = min(m, end - start);
 
     const uint32_t ty = (uint32_t)tile_y, tx = (uint32_t)tile_x;
-    // ... and contribute nothing: their records are zero
-    for (uint32_t e = start + n_max + lane; e < end; e += kBwdThreads) {
-        const uint32_t g = p.values[e];
-        const uint2 rc = p.rect[g];
-        const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-        float4 *rec = reinterpret_cast<float4 *>(
-            p.pair_grad + (size_t)(p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0)) * kPairStride);
-#pragma unroll
-        for (int c = 0; c < kPairStride / 4; ++c) rec[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    // ... and contribute nothing: no record is written for them.  The list is sorted by
+    // (depth bits, index), so the key of the deepest walked entry tells the per-Gaussian
+    // stage which records exist.
+    if (lane == 0) {
+        unsigned long long cut = 0;
+        if (n_max > 0) {
+            const uint32_t g = p.values[start + n_max - 1];
+            const float4 r3 = reinterpret_cast<const float4 *>(p.splat)[(size_t)g * 4 + 3];
+            cut = ((unsigned long long)__float_as_uint(r3.y) << 32) | g;
+        }
+        p.cut[tile] = cut;
     }
 
     for (int hi = (int)n_max; hi > 0; hi -= kBwdBatch) {
@@ -502,9 +505,10 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
 // ---------------------------------------------------------------------------
 // A wave owns 64 consecutive Gaussians.  In 16 rounds, each 16-lane row sums the
 // records of one Gaussian (lane i takes records i, i + 16, ...: a row reads 16
-// consecutive records), reduces them with DPP row shifts and parks the nine sums in
-// LDS; then every lane runs the chain rule of one Gaussian, so the parameter planes
-// are read and written coalesced.
+// consecutive records, skipping those of tiles whose walk stopped before the
+// Gaussian), reduces them with DPP row shifts and parks the nine sums in LDS; then
+// every lane runs the chain rule of one Gaussian, so the parameter planes are read
+// and written coalesced.
 constexpr int kGaussPerWave = kWave;
 constexpr int kRowLanes = 16;
 
@@ -532,7 +536,13 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
         if (count) {
             const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
+            const uint2 rc = p.rect[g];
+            const uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu;
+            const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
             for (uint32_t i = li; i < count; i += kRowLanes) {
+                const uint32_t row = i / w;
+                const uint32_t tile = (y0 + row) * (uint32_t)p.tiles_x + x0 + (i - row * w);
+                if (key > p.cut[tile]) continue;   // no pixel of that tile reached this Gaussian
                 const float *r = rec + (size_t)i * kPairStride;
                 const float4 a = *reinterpret_cast<const float4 *>(r);
                 const float4 b = *reinterpret_cast<const float4 *>(r + 4);

@@ -163,6 +163,8 @@ struct CompositeBackwardParams {
     float *pair_grad;            // [pairs][kPairStride]: Gaussian g's pair k (row-major
                                  // over its rectangle) at pair_base[g] + k
     const uint32_t *tile_order;  // optional launch order: workgroup b walks tile_order[b]
+    unsigned long long *cut;     // [tiles] out: (depth bits << 32 | index) of the deepest entry
+                                 // walked, 0 if none; records exist exactly for entries <= it
 };
 void launch_composite_backward(const CompositeBackwardParams &p, hipStream_t s);
 
@@ -175,6 +177,10 @@ struct GaussianBackwardParams {
     float fx, fy;
     float cam_pos[3];
     const uint32_t *tile_count, *pair_base;
+    const uint2 *rect;           // tile rectangles (x0 | x1 << 16, y0 | y1 << 16)
+    const float *depth;          // [n] camera-space z
+    const unsigned long long *cut;   // [tiles] from the reverse walk
+    int32_t tiles_x;
     const float *pair_grad;
     float *g_mean, *g_quat, *g_log_scale, *g_opacity, *g_sh;
     float *g_mean2d, *g_conic, *g_rgb;   // optional screen-space gradients
