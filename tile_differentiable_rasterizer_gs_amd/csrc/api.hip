@@ -447,18 +447,31 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     r.ranges = as<uint32_t>(ctx->ranges);
     int buf = 0;
     if (depth_first) {
-        d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
+        // tile ids as 16-bit keys whenever they fit: 6 instead of 8 bytes per pair per pass
+        const bool narrow = tiles <= 65536;
+        if (narrow)
+            d.tile_keys16 = as<uint16_t>(ctx->pkey32[0]);
+        else
+            d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
         GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
         launch_duplicate(d, as<uint32_t>(ctx->part), stream);
         GS_TRY(check_launch(ctx, "duplicate"));
         GS_TRY(span_end(ctx, stream));
         GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
-        buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
-                                         as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), cap, d_total, 0,
-                                         tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
+        if (narrow)
+            buf = radix_sort_pairs<uint16_t>(as<uint16_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
+                                             as<uint16_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), cap, d_total,
+                                             0, tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
+        else
+            buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->pkey32[0]), as<uint32_t>(ctx->pval[0]),
+                                             as<uint32_t>(ctx->pkey32[1]), as<uint32_t>(ctx->pval[1]), cap, d_total,
+                                             0, tile_bits, as<uint32_t>(ctx->psort_scratch), stream);
         GS_TRY(check_launch(ctx, "tile sort"));
         GS_TRY(span_end(ctx, stream));
-        r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
+        if (narrow)
+            r.tile_keys16 = as<uint16_t>(ctx->pkey32[buf]);
+        else
+            r.tile_keys = as<uint32_t>(ctx->pkey32[buf]);
         if (emit_keys) {
             r.keys_out = as<uint64_t>(ctx->keys_out);
             r.values = as<uint32_t>(ctx->pval[buf]);

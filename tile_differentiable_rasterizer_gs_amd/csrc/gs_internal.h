@@ -77,7 +77,8 @@ struct DuplicateParams {
     const float *depth;
     int32_t tiles_x;
     uint64_t *keys64;            // key64 mode: (tile << 32) | bits(depth)
-    uint32_t *tile_keys;         // depth-first mode: tile id
+    uint32_t *tile_keys;         // depth-first mode: tile id ...
+    uint16_t *tile_keys16;       // ... or as 16 bits (at most 65536 tiles); entry count multiple of 8 per block
     uint32_t *values;            // Gaussian index
 };
 // uint32 words of the partition table launch_duplicate needs
@@ -88,7 +89,8 @@ struct RangesParams {
     const unsigned long long *num_dups;   // device
     int64_t capacity;
     const uint64_t *keys64;      // either keys64 (tile = key >> 32) ...
-    const uint32_t *tile_keys;   // ... or tile ids
+    const uint32_t *tile_keys;   // ... or tile ids ...
+    const uint16_t *tile_keys16; // ... or 16-bit tile ids
     uint32_t *ranges;            // [tiles][2], zeroed beforehand
     // optional key emission (depth-first mode): keys_out[e] = tile << 32 | bits(depth[values[e]])
     const uint32_t *values;

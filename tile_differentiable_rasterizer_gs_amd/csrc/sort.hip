@@ -357,6 +357,10 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             to[0] = make_uint4(tiles[0], tiles[1], tiles[2], tiles[3]);
             to[1] = make_uint4(tiles[4], tiles[5], tiles[6], tiles[7]);
         }
+        if (p.tile_keys16)   // eight 16-bit tile ids = one 16-byte store
+            *reinterpret_cast<uint4 *>(p.tile_keys16 + e0) =
+                make_uint4(tiles[0] | (tiles[1] << 16), tiles[2] | (tiles[3] << 16), tiles[4] | (tiles[5] << 16),
+                           tiles[6] | (tiles[7] << 16));
         if (p.keys64) {
 #pragma unroll
             for (int k = 0; k < kDupItems; ++k) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
@@ -365,6 +369,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
         for (int k = 0; k < n_here; ++k) {
             p.values[e0 + k] = gs[k];
             if (p.tile_keys) p.tile_keys[e0 + k] = tiles[k];
+            if (p.tile_keys16) p.tile_keys16[e0 + k] = (uint16_t)tiles[k];
             if (p.keys64) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
         }
     }
@@ -373,7 +378,16 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
 // ranges from sorted tiles: 4 consecutive entries per thread
 constexpr int kRangeItems = 4;
 
-template <bool kKey64>
+enum RangeKeys { kTileKeys32 = 0, kKeys64 = 1, kTileKeys16 = 2 };
+
+template <int kKind>
+__device__ __forceinline__ uint32_t tile_of_entry(const RangesParams &p, int64_t e) {
+    if constexpr (kKind == kKeys64) return (uint32_t)(p.keys64[e] >> 32);
+    else if constexpr (kKind == kTileKeys16) return p.tile_keys16[e];
+    else return p.tile_keys[e];
+}
+
+template <int kKind>
 __global__ __launch_bounds__(kBlock) void ranges_kernel(RangesParams p) {
     const int64_t num_dups = live_count(p.capacity, p.num_dups);
     const int64_t e0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kRangeItems;
@@ -384,10 +398,9 @@ __global__ __launch_bounds__(kBlock) void ranges_kernel(RangesParams p) {
     for (int k = 0; k <= kRangeItems; ++k) {
         const int64_t e = e0 + k;
         t[k] = 0xffffffffu;
-        if (k <= cnt && e < num_dups)
-            t[k] = kKey64 ? (uint32_t)(p.keys64[e] >> 32) : p.tile_keys[e];
+        if (k <= cnt && e < num_dups) t[k] = tile_of_entry<kKind>(p, e);
     }
-    const uint32_t prev = e0 == 0 ? 0xffffffffu : (kKey64 ? (uint32_t)(p.keys64[e0 - 1] >> 32) : p.tile_keys[e0 - 1]);
+    const uint32_t prev = e0 == 0 ? 0xffffffffu : tile_of_entry<kKind>(p, e0 - 1);
 #pragma unroll
     for (int k = 0; k < kRangeItems; ++k) {
         if (k >= cnt) break;
@@ -464,6 +477,9 @@ template int radix_sort_pairs<uint32_t>(uint32_t *, uint32_t *, uint32_t *, uint
 template int radix_sort_pairs<uint64_t>(uint64_t *, uint32_t *, uint64_t *, uint32_t *, int64_t,
                                         const unsigned long long *, int, int, uint32_t *, hipStream_t,
                                         const uint32_t *, uint32_t *);
+template int radix_sort_pairs<uint16_t>(uint16_t *, uint32_t *, uint16_t *, uint32_t *, int64_t,
+                                        const unsigned long long *, int, int, uint32_t *, hipStream_t,
+                                        const uint32_t *, uint32_t *);
 
 int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTile - 1) / kDupTile + 1; }
 
@@ -480,9 +496,11 @@ void launch_ranges(const RangesParams &p, hipStream_t s) {
     const int64_t threads = (p.capacity + kRangeItems - 1) / kRangeItems;
     const unsigned grid = (unsigned)((threads + kBlock - 1) / kBlock);
     if (p.keys64)
-        ranges_kernel<true><<<grid, kBlock, 0, s>>>(p);
+        ranges_kernel<kKeys64><<<grid, kBlock, 0, s>>>(p);
+    else if (p.tile_keys16)
+        ranges_kernel<kTileKeys16><<<grid, kBlock, 0, s>>>(p);
     else
-        ranges_kernel<false><<<grid, kBlock, 0, s>>>(p);
+        ranges_kernel<kTileKeys32><<<grid, kBlock, 0, s>>>(p);
 }
 
 void launch_fill_u32(uint32_t *dst, uint32_t value, int64_t n, hipStream_t s) {
