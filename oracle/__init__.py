@@ -232,6 +232,57 @@ def composite_2d(means, covs, colours, opacities, depths, image_size, bg=None):
     return out.reshape(H, W, 3), T.reshape(H, W)
 
 
+def composite_2d_backward(means, covs, colours, opacities, depths, image_size, g_image, bg=None) -> dict:
+    """Vector-Jacobian product of composite_2d in binary64, written out by hand.
+
+    For each pixel the forward walk gives T_i before entry i; walking back with the
+    colour behind B_i (B_{i-1} = a_i c_i + (1 - a_i) B_i):
+        dL/dc_i = a_i T_i dL/dC,   dL/da_i = T_i (c_i - B_i) . dL/dC - T_final (bg . dL/dC) / (1 - a_i)
+    a = clamp(o G, 0, 0.99) passes the derivative where 0 <= o G <= 0.99 (the clamp's
+    own convention at its ends); G = exp(-q/2), q = d^T P d with d = pixel - mean and
+    P = cov^-1, so dL/dq = -a dL/da / 2, dL/dmean = -2 P d dL/dq, and with
+    M = sum_pixels dL/dq d d^T the covariance gets dL/dcov = -P M P.
+    Returns means (G,2), covs (G,2,2), colours (G,3), opacities (G,).
+    """
+    means = np.asarray(means, np.float64)
+    covs = np.asarray(covs, np.float64)
+    colours = np.asarray(colours, np.float64)
+    opacities = np.asarray(opacities, np.float64)
+    H, W = image_size
+    G = means.shape[0]
+    gC = np.asarray(g_image, np.float64).reshape(H * W, 3)
+    yy, xx = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
+    pts = np.stack([xx, yy], axis=-1).reshape(-1, 2)
+    P = np.linalg.inv(covs) if G else covs
+    diff = pts[None, :, :] - means[:, None, :]
+    quad = np.einsum("gpi,gij,gpj->gp", diff, P, diff)
+    dens = np.exp(-0.5 * quad)
+    raw = opacities[:, None] * dens
+    alphas = np.clip(raw, 0.0, 0.99)
+    smooth = (raw >= 0.0) & (raw <= 0.99)
+    order = np.argsort(np.asarray(depths), kind="stable")
+    Ts = np.zeros((G, H * W))
+    T = np.ones(H * W)
+    for g in order:
+        Ts[g] = T
+        T = T * (1.0 - alphas[g])
+    bg_term = np.zeros(H * W) if bg is None else T * (gC @ np.asarray(bg, np.float64))
+    out = dict(means=np.zeros((G, 2)), covs=np.zeros((G, 2, 2)), colours=np.zeros((G, 3)), opacities=np.zeros(G))
+    B = np.zeros((H * W, 3))
+    for g in order[::-1]:
+        a = alphas[g]
+        out["colours"][g] = ((a * Ts[g])[:, None] * gC).sum(axis=0)
+        d_a = Ts[g] * ((colours[g][None, :] - B) * gC).sum(axis=1) - bg_term / (1.0 - a)
+        B = a[:, None] * colours[g][None, :] + (1.0 - a)[:, None] * B
+        d_a = np.where(smooth[g], d_a, 0.0)
+        out["opacities"][g] = (dens[g] * d_a).sum()
+        d_q = -0.5 * raw[g] * d_a
+        out["means"][g] = (-2.0 * d_q[:, None] * (diff[g] @ P[g].T)).sum(axis=0)
+        M = np.einsum("p,pi,pj->ij", d_q, diff[g], diff[g])
+        out["covs"][g] = -P[g] @ M @ P[g]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # gradients (gs_oracle_grad.c)
 # ---------------------------------------------------------------------------

@@ -213,3 +213,60 @@ def test_sh_gradient_is_the_basis():
         for k in range(16):
             for c in range(3):
                 assert math.isclose(g["sh"][k * 3 + c, i], Y[k] * cr[c, i], rel_tol=1e-12, abs_tol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# the lesson's dense 2D rasteriser ("Étape 2") and its hand-written derivative
+# ---------------------------------------------------------------------------
+def _splats2d(seed, n, H, W, opaque=False):
+    rng = np.random.default_rng(seed)
+    means = rng.uniform([0, 0], [W, H], size=(n, 2))
+    ang = rng.uniform(0, np.pi, n)
+    s = np.exp(rng.uniform(0.3, 1.6, (n, 2)))
+    R = np.stack([np.stack([np.cos(ang), -np.sin(ang)], -1), np.stack([np.sin(ang), np.cos(ang)], -1)], -2)
+    covs = R @ (s[:, :, None] ** 2 * np.eye(2)) @ np.swapaxes(R, 1, 2)
+    colours = rng.uniform(0, 1, (n, 3))
+    opac = rng.uniform(0.6, 1.0, n) if opaque else rng.uniform(0.05, 0.9, n)
+    depths = rng.uniform(0, 1, n)
+    return means, covs, colours, opac, depths
+
+
+@pytest.mark.parametrize("bg", [None, (0.3, -0.2, 0.6)])
+def test_composite_2d_backward_matches_finite_differences(bg):
+    H, W = 13, 17
+    means, covs, colours, opac, depths = _splats2d(5, 9, H, W, opaque=True)
+    gimg = np.random.default_rng(6).normal(size=(H, W, 3))
+    args = dict(means=means, covs=covs, colours=colours, opacities=opac)
+
+    def loss():
+        img, _ = oracle.composite_2d(args["means"], args["covs"], args["colours"], args["opacities"], depths, (H, W),
+                                     bg=bg)
+        return float((gimg * img).sum())
+
+    g = oracle.composite_2d_backward(means, covs, colours, opac, depths, (H, W), gimg, bg=bg)
+    _, T = oracle.composite_2d(means, covs, colours, opac, depths, (H, W))
+    assert T.min() < 0.05, "case must exercise strong occlusion"
+    for k in ("means", "covs", "colours", "opacities"):
+        _close(g[k], _fd(loss, args[k], 1e-6), 1e-6, k)
+
+
+def test_composite_2d_backward_one_splat_closed_form_and_clamp():
+    # one splat, one pixel: C = a c with a = o exp(-q/2)
+    mean = np.array([[0.3, -0.4]])
+    cov = np.array([[[2.0, 0.5], [0.5, 1.0]]])
+    c = np.array([[0.2, 0.7, 0.4]])
+    gimg = np.array([1.0, -1.0, 2.0]).reshape(1, 1, 3)
+    P = np.linalg.inv(cov[0])
+    d = -mean[0]
+    q = d @ P @ d
+    G = math.exp(-0.5 * q)
+    g = oracle.composite_2d_backward(mean, cov, c, np.array([0.5]), np.array([0.0]), (1, 1), gimg)
+    dC_da = float(c[0] @ gimg.reshape(3))
+    assert math.isclose(g["opacities"][0], G * dC_da, rel_tol=1e-13)
+    assert np.allclose(g["colours"][0], 0.5 * G * gimg.reshape(3), rtol=1e-13)
+    # dq/dmean = -2 P d; dL/dmean = -a/2 dC/da dq/dmean = a dC/da P d
+    assert np.allclose(g["means"][0], 0.5 * G * dC_da * (P @ d), rtol=1e-12)
+    # above the clamp (o = 1 at the centre): no derivative for opacity or geometry
+    g = oracle.composite_2d_backward(np.zeros((1, 2)), cov, c, np.array([1.0]), np.array([0.0]), (1, 1), gimg)
+    assert g["opacities"][0] == 0.0 and np.all(g["means"] == 0.0) and np.all(g["covs"] == 0.0)
+    assert np.allclose(g["colours"][0], 0.99 * gimg.reshape(3), rtol=1e-14)
