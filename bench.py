@@ -9,7 +9,8 @@ HBM.  Prints one JSON line.
 
 A workload with several cameras (the 32-view orbit) renders its views round-robin.
 The JSON line also carries the backward pass (gs_backward for a fixed random
-image cotangent) timed on its own and as part of a forward + backward step.
+image cotangent) timed on its own and as part of a forward + backward step, and
+the lesson's 2D splat-fitting workload (64 splats, 64x64, 200 Adam steps).
 """
 from __future__ import annotations
 
@@ -169,6 +170,42 @@ def time_backward(r, dev, scene, cams, img, bg, steps, blends):
                 cotangent="standard normal per pixel channel, seed 0")
 
 
+def time_splat2d_fit():
+    """The lesson's 2D splat-fitting workload (64 splats, 64x64 target, Adam 0.05, 200 steps) on the
+    HIP 2D rasteriser: whole-fit wall time and the rasteriser's forward + backward kernel time."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding, splat2d
+
+    r = binding.Rasterizer(emit_keys=False)
+    splat2d.fit(r, steps=10)                     # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = splat2d.fit(r, steps=200, record_every=200)
+    torch.cuda.synchronize()
+    fit_s = time.perf_counter() - t0
+    # the rasteriser alone on the fitted splats, forward + backward
+    p = res["params"]
+    args = [t.detach().contiguous() for t in splat2d.splat_arrays(p)]
+    g = torch.ones((64, 64, 3), dtype=torch.float32, device="cuda")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        r.splat2d_forward(*args, 64, 64)
+        r.splat2d_backward(*args, 64, 64, g)
+    start.record()
+    for _ in range(100):
+        r.splat2d_forward(*args, 64, 64)
+        r.splat2d_backward(*args, 64, 64, g)
+    stop.record()
+    torch.cuda.synchronize()
+    r.close()
+    losses = dict(res["losses"])
+    return dict(steps=200, fit_ms_per_step=round(fit_s * 1e3 / 200, 4), fit_steps_per_s=round(200 / fit_s, 1),
+                rasteriser_fwd_bwd_ms=round(start.elapsed_time(stop) / 100, 5),
+                mse_first=round(losses[0], 6), mse_final=round(res["final_loss"], 6),
+                note="step = forward + backward through gs_splat2d_* plus torch activations, loss and Adam")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +343,9 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = time_backward(r, dev, scene, cams, img, bg, args.steps, blends)
+        log("2D splat fit ...")
+        out["splat2d_fit"] = time_splat2d_fit()
+        log(f"2D splat fit: {out['splat2d_fit']}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(scene, cam)

@@ -289,6 +289,35 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *gaussians, const gs_c
                       const float *final_T, const uint32_t *n_blend, const float *grad_image,
                       const gs_gradients *grads, hipStream_t stream);
 
+/*
+ * The lesson's dense 2D splat rasteriser (sections "Étape 1: Un gaussien 2D",
+ * "Étape 2: Rasteriser à éclaboussure en 2D"): every splat at every pixel
+ * (x = column, y = row), alpha = clamp(o exp(-d^T cov^-1 d / 2), 0, 0.99),
+ * splats in ascending (depth, index) order, front-to-back compositing with no
+ * early stop, out = C + T bg (bg_rgb: 3 host floats, NULL = black).  All
+ * arrays are device fp32, row-major: means [n][2] (x, y in pixels),
+ * covs [n][2][2], colours [n][3], opacities [n], depths [n] (order only),
+ * image [height][width][3].  n in [0, 2^31); the ranking is quadratic in n,
+ * sized for the lesson's hundreds to thousands of splats.  Context memory:
+ * 4 bytes per (splat, pixel) for the transmittance the backward reads.
+ */
+gs_status gs_splat2d_forward(gs_context *ctx, int64_t n, const float *means, const float *covs,
+                             const float *colours, const float *opacities, const float *depths, int32_t height,
+                             int32_t width, const float bg_rgb[3], float *image, hipStream_t stream);
+
+/*
+ * Gradient of sum(grad_image * image) for the last gs_splat2d_forward on this
+ * context, called with the same arguments (section "Étape 4" trains the splats
+ * by gradient descent): grad_means [n][2], grad_covs [n][2][2] (full-matrix
+ * gradient, as for a general inverse), grad_colours [n][3], grad_opacities [n],
+ * all overwritten.  The depth order is held fixed.  Deterministic (fixed
+ * summation order, no floating-point atomics).  Asynchronous.
+ */
+gs_status gs_splat2d_backward(gs_context *ctx, int64_t n, const float *means, const float *covs,
+                              const float *colours, const float *opacities, const float *depths, int32_t height,
+                              int32_t width, const float bg_rgb[3], const float *grad_image, float *grad_means,
+                              float *grad_covs, float *grad_colours, float *grad_opacities, hipStream_t stream);
+
 /* Reads (and resets) the accumulated per-stage times; waits for the timed work. */
 gs_status gs_profile_read(gs_context *ctx, gs_profile *out);
 

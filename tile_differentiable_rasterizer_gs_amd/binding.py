@@ -26,7 +26,8 @@ TILE = 16
 # symbols declared in include/gsrast.h
 EXPORTED = ("gs_context_create", "gs_context_destroy", "gs_context_set_option", "gs_check_arguments",
             "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
-            "gs_backward", "gs_profile_read", "gs_status_string", "gs_last_error")
+            "gs_backward", "gs_splat2d_forward", "gs_splat2d_backward", "gs_profile_read", "gs_status_string",
+            "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -100,6 +101,9 @@ def load_library(path: str = LIB_PATH):
     lib.gs_backward.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(Projected),
                                 ctypes.POINTER(Binning), ctypes.POINTER(ctypes.c_float), P, P, P,
                                 ctypes.POINTER(Gradients), P]
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.gs_splat2d_forward.argtypes = [P, i64, P, P, P, P, P, i32, i32, FP, P, P]
+    lib.gs_splat2d_backward.argtypes = [P, i64, P, P, P, P, P, i32, i32, FP, P, P, P, P, P, P]
     lib.gs_profile_read.argtypes = [P, ctypes.POINTER(Profile)]
     lib.gs_status_string.argtypes = [ctypes.c_int]
     lib.gs_status_string.restype = ctypes.c_char_p
@@ -107,7 +111,7 @@ def load_library(path: str = LIB_PATH):
     lib.gs_last_error.restype = ctypes.c_char_p
     for name in ("gs_context_create", "gs_context_set_option", "gs_check_arguments", "gs_preprocess",
                  "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_backward",
-                 "gs_profile_read"):
+                 "gs_splat2d_forward", "gs_splat2d_backward", "gs_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -289,6 +293,45 @@ class Rasterizer:
                                          ctypes.byref(gr), _stream_handle(stream)))
         return grads
 
+    # ---- the lesson's dense 2D splat rasteriser ----
+    @staticmethod
+    def _splat2d_tensors(means, covs, colours, opacities, depths):
+        n = int(opacities.shape[0])
+        want = dict(means=(n, 2), covs=(n, 2, 2), colours=(n, 3), opacities=(n,), depths=(n,))
+        ts = dict(means=means, covs=covs, colours=colours, opacities=opacities, depths=depths)
+        for k, shape in want.items():
+            t = ts[k]
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or \
+                    not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{k} must be a contiguous CUDA float32 tensor of shape {shape}")
+        return n, [ctypes.c_void_p(ts[k].data_ptr()) if n else None for k in want]
+
+    def splat2d_forward(self, means, covs, colours, opacities, depths, height: int, width: int, bg=None,
+                        out=None, stream=None) -> torch.Tensor:
+        n, ptrs = self._splat2d_tensors(means, covs, colours, opacities, depths)
+        if out is None:
+            out = torch.empty((height, width, 3), dtype=torch.float32, device="cuda")
+        self._check_image(out, (height, width, 3), torch.float32)
+        bgv = None if bg is None else (ctypes.c_float * 3)(*[float(v) for v in bg])
+        self._check(self.lib.gs_splat2d_forward(self.ctx, n, *ptrs, int(height), int(width), bgv,
+                                                ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)))
+        return out
+
+    def splat2d_backward(self, means, covs, colours, opacities, depths, height: int, width: int, grad_image,
+                         bg=None, stream=None) -> dict:
+        n, ptrs = self._splat2d_tensors(means, covs, colours, opacities, depths)
+        self._check_image(grad_image, (height, width, 3), torch.float32)
+        g = dict(means=torch.empty((n, 2), dtype=torch.float32, device="cuda"),
+                 covs=torch.empty((n, 2, 2), dtype=torch.float32, device="cuda"),
+                 colours=torch.empty((n, 3), dtype=torch.float32, device="cuda"),
+                 opacities=torch.empty((n,), dtype=torch.float32, device="cuda"))
+        bgv = None if bg is None else (ctypes.c_float * 3)(*[float(v) for v in bg])
+        gp = [ctypes.c_void_p(g[k].data_ptr()) if n else None for k in ("means", "covs", "colours", "opacities")]
+        self._check(self.lib.gs_splat2d_backward(self.ctx, n, *ptrs, int(height), int(width), bgv,
+                                                 ctypes.c_void_p(grad_image.data_ptr()), *gp,
+                                                 _stream_handle(stream)))
+        return g
+
     def profile_read(self) -> dict:
         p = Profile()
         self._check(self.lib.gs_profile_read(self.ctx, ctypes.byref(p)))
@@ -355,3 +398,28 @@ def render_differentiable(rasterizer: "Rasterizer", params: dict, sh_degree: int
     """Image [H, W, 3] with autograd support for the five parameter tensors in `params`."""
     return RenderFunction.apply(params["mean"], params["quat"], params["log_scale"], params["opacity"],
                                 params["sh"], rasterizer, sh_degree, camera, tuple(float(v) for v in bg))
+
+
+class Splat2DFunction(torch.autograd.Function):
+    """The lesson's dense 2D rasteriser through the HIP library, with autograd (depths only order
+    the splats and get no gradient).  Forward state lives in the rasterizer's context until
+    backward: do not run another 2D forward on the same Rasterizer in between."""
+
+    @staticmethod
+    def forward(ctx, means, covs, colours, opacities, depths, rasterizer, height, width, bg):
+        args = [t.detach().contiguous().float() for t in (means, covs, colours, opacities, depths)]
+        img = rasterizer.splat2d_forward(*args, height, width, bg=bg)
+        ctx.state = (rasterizer, args, height, width, bg)
+        return img
+
+    @staticmethod
+    def backward(ctx, grad_image):
+        rasterizer, args, height, width, bg = ctx.state
+        g = rasterizer.splat2d_backward(*args, height, width, grad_image.contiguous().float(), bg=bg)
+        return g["means"], g["covs"], g["colours"], g["opacities"], None, None, None, None, None
+
+
+def rasterise_2d(rasterizer: "Rasterizer", means, covs, colours, opacities, depths, image_size, bg=None):
+    """Image [H, W, 3] of 2D splats (the lesson's rasteriser signature), differentiable."""
+    H, W = image_size
+    return Splat2DFunction.apply(means, covs, colours, opacities, depths, rasterizer, int(H), int(W), bg)

@@ -63,6 +63,11 @@ struct gs_context {
     DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
     DeviceBuffer pair_base, pair_grad, scan_total;
+    // 2D splat rasteriser
+    DeviceBuffer s2_order, s2_rec, s2_trans, s2_partial;
+    int64_t s2_n = -1;
+    int32_t s2_height = 0, s2_width = 0;
+    const float *s2_means = nullptr, *s2_depths = nullptr;
 
     unsigned long long *host_total = nullptr;   // pinned: pair count read back once per frame
 
@@ -286,7 +291,8 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
                            &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order,
-                           &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut};
+                           &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->s2_order,
+                           &ctx->s2_rec, &ctx->s2_trans, &ctx->s2_partial};
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -774,6 +780,86 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     launch_gaussian_backward(q, stream);
     GS_TRY(check_launch(ctx, "gaussian backward"));
     GS_TRY(span_end(ctx, stream));
+    return GS_OK;
+}
+
+static gs_status splat2d_check(gs_context *ctx, int64_t n, const float *means, const float *covs,
+                               const float *colours, const float *opacities, const float *depths, int32_t height,
+                               int32_t width) {
+    if (n < 0 || n > 0x7fffffffll) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "splat count outside [0, 2^31)");
+    if (height < 1 || width < 1 || height > 32768 || width > 32768)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "image size outside [1, 32768]");
+    if (n > 0 && (!means || !covs || !colours || !opacities || !depths))
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "a splat array pointer is NULL");
+    return GS_OK;
+}
+
+gs_status gs_splat2d_forward(gs_context *ctx, int64_t n, const float *means, const float *covs,
+                             const float *colours, const float *opacities, const float *depths, int32_t height,
+                             int32_t width, const float bg[3], float *image, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    GS_TRY(splat2d_check(ctx, n, means, covs, colours, opacities, depths, height, width));
+    if (!image) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL image");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    GS_TRY(ensure(ctx, ctx->s2_order, nn * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->s2_rec, nn * 12 * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->s2_trans, nn * (size_t)height * (size_t)width * sizeof(float)));
+    Splat2DParams p{};
+    p.n = (int32_t)n;
+    p.height = height;
+    p.width = width;
+    p.means = means;
+    p.covs = covs;
+    p.colours = colours;
+    p.opacities = opacities;
+    p.depths = depths;
+    for (int i = 0; i < 3; ++i) p.bg[i] = bg ? bg[i] : 0.0f;
+    p.image = image;
+    launch_splat2d_forward(p, as<uint32_t>(ctx->s2_order), as<float>(ctx->s2_rec), as<float>(ctx->s2_trans), stream);
+    GS_TRY(check_launch(ctx, "splat2d forward"));
+    ctx->s2_n = n;
+    ctx->s2_height = height;
+    ctx->s2_width = width;
+    ctx->s2_means = means;
+    ctx->s2_depths = depths;
+    return GS_OK;
+}
+
+gs_status gs_splat2d_backward(gs_context *ctx, int64_t n, const float *means, const float *covs,
+                              const float *colours, const float *opacities, const float *depths, int32_t height,
+                              int32_t width, const float bg[3], const float *grad_image, float *grad_means,
+                              float *grad_covs, float *grad_colours, float *grad_opacities, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    GS_TRY(splat2d_check(ctx, n, means, covs, colours, opacities, depths, height, width));
+    if (n != ctx->s2_n || height != ctx->s2_height || width != ctx->s2_width || means != ctx->s2_means ||
+        depths != ctx->s2_depths)
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "arguments differ from the last gs_splat2d_forward on this context");
+    if (!grad_image || (n > 0 && (!grad_means || !grad_covs || !grad_colours || !grad_opacities)))
+        return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL gradient pointer");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    if (n == 0) return GS_OK;
+    const size_t tiles = (size_t)((width + GS_TILE - 1) / GS_TILE) * (size_t)((height + GS_TILE - 1) / GS_TILE);
+    GS_TRY(ensure(ctx, ctx->s2_partial, (size_t)n * tiles * kPairGrad * sizeof(float)));
+    Splat2DParams p{};
+    p.n = (int32_t)n;
+    p.height = height;
+    p.width = width;
+    p.means = means;
+    p.covs = covs;
+    p.colours = colours;
+    p.opacities = opacities;
+    p.depths = depths;
+    for (int i = 0; i < 3; ++i) p.bg[i] = bg ? bg[i] : 0.0f;
+    p.grad_image = grad_image;
+    p.g_means = grad_means;
+    p.g_covs = grad_covs;
+    p.g_colours = grad_colours;
+    p.g_opacities = grad_opacities;
+    launch_splat2d_backward(p, as<float>(ctx->s2_rec), as<float>(ctx->s2_trans), as<float>(ctx->s2_partial), stream);
+    GS_TRY(check_launch(ctx, "splat2d backward"));
     return GS_OK;
 }
 

@@ -189,4 +189,21 @@ struct GaussianBackwardParams {
 };
 void launch_gaussian_backward(const GaussianBackwardParams &p, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// the lesson's dense 2D splat rasteriser
+// ---------------------------------------------------------------------------
+struct Splat2DParams {
+    int32_t n, height, width;
+    const float *means, *covs, *colours, *opacities, *depths;   // [n][2], [n][2][2], [n][3], [n], [n]
+    float bg[3];
+    float *image;                // forward output [H][W][3]
+    const float *grad_image;     // backward input [H][W][3]
+    float *g_means, *g_covs, *g_colours, *g_opacities;
+};
+// order [n], rec [n][12], trans [n][H][W] (T before each splat in depth order)
+void launch_splat2d_forward(const Splat2DParams &p, uint32_t *order, float *rec, float *trans, hipStream_t s);
+// partial [n][tiles][9]
+void launch_splat2d_backward(const Splat2DParams &p, const float *rec, const float *trans, float *partial,
+                             hipStream_t s);
+
 }  // namespace gsr
