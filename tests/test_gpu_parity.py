@@ -353,3 +353,31 @@ def test_c5_orbit_views_sampled():
         note(f"c5 view {k}")
         m, err = _large_check(s, s.cameras[k], n_tiles=12, n_pix=300, seed=k)
         note(f"c5 view {k} pairs={m} sampled err {err:.2e}")
+
+
+def test_views_in_flight_on_separate_contexts_match_sequential():
+    # several contexts, each on its own stream, rendering views back to back (the multi-view
+    # pipelining the benchmark uses) give the same bits as one context rendering them in turn
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    sc = scenes.random_scene(31, 20000, 3, 320, 240)
+    cams = [scenes.look_at_camera(scenes.orbit_position(4.0, 0.4 * k, 0.2), (0, 0, 0), 320.0, 320, 240)
+            for k in range(6)]
+    dev = binding.gaussians_to_device(sc.arrays())
+    ref_r = binding.Rasterizer(emit_keys=False)
+    ref = [ref_r.render(dev, 3, c).clone() for c in cams]
+    torch.cuda.synchronize()
+    ref_r.close()
+    lanes = [(binding.Rasterizer(emit_keys=False), torch.cuda.Stream()) for _ in range(3)]
+    outs = [torch.empty((240, 320, 3), device="cuda") for _ in cams]
+    for rep in range(2):
+        for i, c in enumerate(cams):
+            r, s = lanes[i % 3]
+            r.render(dev, 3, c, out=outs[i], stream=s)
+        torch.cuda.synchronize()
+        for i in range(len(cams)):
+            assert torch.equal(outs[i], ref[i]), (rep, i)
+    for r, _ in lanes:
+        r.close()
