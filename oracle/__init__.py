@@ -53,7 +53,10 @@ class _Camera(ctypes.Structure):
 
 class _Projected(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in
-                ("depth", "mean2d", "cov2d", "conic", "radius", "cov3d", "rect", "tile_count", "rgb")]
+                ("depth", "mean2d", "cov2d", "conic", "radius", "cov3d", "rect", "tile_count", "rgb", "ellipse")]
+
+
+TILE_SQUARE, TILE_ELLIPSE = 0, 1   # tile membership rules (the library's GS_OPT_TILE_TEST)
 
 
 _lib = None
@@ -69,8 +72,19 @@ def _load():
         lib.oracle_preprocess.argtypes = [i64, i32, P, P, P, P, P, ctypes.POINTER(_Camera),
                                           ctypes.POINTER(_Projected)]
         lib.oracle_preprocess.restype = None
+        lib.oracle_preprocess_ex.argtypes = [i64, i32, P, P, P, P, P, ctypes.POINTER(_Camera), i32,
+                                             ctypes.POINTER(_Projected)]
+        lib.oracle_preprocess_ex.restype = None
         lib.oracle_bin.argtypes = [i64, P, P, P, i32, i32, P, P, P, P, P]
         lib.oracle_bin.restype = None
+        lib.oracle_bin_ex.argtypes = [i64, P, P, P, i32, i32, P, P, i32, P, P, P, P, P]
+        lib.oracle_bin_ex.restype = None
+        lib.oracle_composite_ex.argtypes = [i64, P, P, P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_double,
+                                            P, i64, P, P, P]
+        lib.oracle_composite_ex.restype = None
+        lib.oracle_row_span.argtypes = [ctypes.c_float, ctypes.c_float, P, i32, i32, i32,
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.oracle_row_span.restype = None
         lib.oracle_total_pairs.argtypes = [i64, P]
         lib.oracle_total_pairs.restype = i64
         lib.oracle_composite.argtypes = [i64, P, P, P, P, P, P, P, i32, i32, P, i32, ctypes.c_double,
@@ -84,11 +98,11 @@ def _load():
         lib.oracle_project64.restype = None
         lib.oracle_project_backward.argtypes = [i64, i32, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_project_backward.restype = None
-        lib.oracle_composite_fixed.argtypes = [i64, P, P, P, P, P, P, i64, i32, i32, P, P, ctypes.c_double,
-                                               P, P, P]
+        lib.oracle_composite_fixed.argtypes = [i64, P, P, P, P, P, P, P, i32, P, i64, i32, i32, P, P,
+                                               ctypes.c_double, P, P, P]
         lib.oracle_composite_fixed.restype = None
-        lib.oracle_composite_backward.argtypes = [i64, P, P, P, P, P, P, i64, i32, i32, P, P, ctypes.c_double,
-                                                  P, P, i64, P, P, P, P]
+        lib.oracle_composite_backward.argtypes = [i64, P, P, P, P, P, P, P, i32, P, i64, i32, i32, P, P,
+                                                  ctypes.c_double, P, P, i64, P, P, P, P]
         lib.oracle_composite_backward.restype = None
         _lib = lib
     return _lib
@@ -116,8 +130,9 @@ def _camera(camera: dict) -> _Camera:
     return c
 
 
-def preprocess(arrays: dict, sh_degree: int, camera: dict) -> dict:
-    """Per-Gaussian projection record (numpy planes, index g last)."""
+def preprocess(arrays: dict, sh_degree: int, camera: dict, tile_test: int = TILE_SQUARE) -> dict:
+    """Per-Gaussian projection record (numpy planes, index g last).  tile_test selects the tile
+    membership rule (the pages' square, or its part that meets the exact 3-sigma ellipse)."""
     lib = _load()
     mean, quat = _f32(arrays["mean"]), _f32(arrays["quat"])
     ls, op, sh = _f32(arrays["log_scale"]), _f32(arrays["opacity"]), _f32(arrays["sh"])
@@ -126,14 +141,25 @@ def preprocess(arrays: dict, sh_degree: int, camera: dict) -> dict:
                cov2d=np.zeros((3, n), np.float32), conic=np.zeros((3, n), np.float32),
                radius=np.zeros(n, np.float32), cov3d=np.zeros((6, n), np.float32),
                rect=np.zeros((4, n), np.int32), tile_count=np.zeros(n, np.uint32),
-               rgb=np.zeros((3, n), np.float64))
+               rgb=np.zeros((3, n), np.float64), ellipse=np.zeros((5, n), np.float32))
     pr = _Projected(**{k: _ptr(v).value for k, v in out.items()})
     cam = _camera(camera)
-    lib.oracle_preprocess(n, sh_degree, _ptr(mean), _ptr(quat), _ptr(ls), _ptr(op), _ptr(sh),
-                          ctypes.byref(cam), ctypes.byref(pr))
+    lib.oracle_preprocess_ex(n, sh_degree, _ptr(mean), _ptr(quat), _ptr(ls), _ptr(op), _ptr(sh),
+                             ctypes.byref(cam), int(tile_test), ctypes.byref(pr))
     out["opacity"] = op
     out["tiles"] = tiles_for(camera)
+    out["tile_test"] = int(tile_test)
     return out
+
+
+def row_span(u: float, v: float, ellipse5, x0: int, x1: int, ty: int) -> tuple[int, int]:
+    """Kept tiles [a, b) of tile row ty under the exact-footprint rule (binary32)."""
+    lib = _load()
+    E = _f32(ellipse5).reshape(5)
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    lib.oracle_row_span(float(np.float32(u)), float(np.float32(v)), _ptr(E), int(x0), int(x1), int(ty),
+                        ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
 
 
 def bin_pairs(proj: dict, want_unsorted: bool = True) -> dict:
@@ -146,8 +172,9 @@ def bin_pairs(proj: dict, want_unsorted: bool = True) -> dict:
     vu = np.zeros(m, np.uint32) if want_unsorted else None
     ks, vs = np.zeros(m, np.uint64), np.zeros(m, np.uint32)
     ranges = np.zeros((tx * ty, 2), np.uint32)
-    lib.oracle_bin(n, _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]), tx, ty,
-                   _ptr(ku), _ptr(vu), _ptr(ks), _ptr(vs), _ptr(ranges))
+    lib.oracle_bin_ex(n, _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]), tx, ty,
+                      _ptr(proj["mean2d"]), _ptr(proj["ellipse"]), int(proj.get("tile_test", TILE_SQUARE)),
+                      _ptr(ku), _ptr(vu), _ptr(ks), _ptr(vs), _ptr(ranges))
     return dict(num_dups=m, keys_unsorted=ku, values_unsorted=vu, keys=ks, values=vs, ranges=ranges)
 
 
@@ -168,10 +195,11 @@ def composite(proj: dict, camera: dict, bg=(0.0, 0.0, 0.0), pixels=None, support
     cnt = np.zeros(npx, np.int64)
     bgv = np.asarray(bg, np.float64)
     rgb = np.ascontiguousarray(proj["rgb"], np.float64)
-    lib.oracle_composite(n, _ptr(proj["mean2d"]), _ptr(proj["conic"]), _ptr(_f32(proj["opacity"])),
-                         _ptr(rgb), _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]),
-                         W, H, _ptr(bgv), 1 if support_all else 0, float(t_eps), _ptr(pix), npx,
-                         _ptr(out), _ptr(T), _ptr(cnt))
+    lib.oracle_composite_ex(n, _ptr(proj["mean2d"]), _ptr(proj["conic"]), _ptr(_f32(proj["opacity"])),
+                            _ptr(rgb), _ptr(proj["depth"]), _ptr(proj["rect"]), _ptr(proj["tile_count"]),
+                            _ptr(proj["ellipse"]), int(proj.get("tile_test", TILE_SQUARE)),
+                            W, H, _ptr(bgv), 1 if support_all else 0, float(t_eps), _ptr(pix), npx,
+                            _ptr(out), _ptr(T), _ptr(cnt))
     if pixels is None:
         return out.reshape(H, W, 3), T.reshape(H, W), cnt.reshape(H, W)
     return out, T, cnt
@@ -334,9 +362,19 @@ def depth_order(depth, tile_count) -> np.ndarray:
     return np.ascontiguousarray(g[np.lexsort((g, d))], dtype=np.int64)
 
 
-def composite_fixed(screen: dict, rect, order, camera: dict, bg=(0.0, 0.0, 0.0), n_limit=None, t_eps=1e-4):
-    """binary64 compositing over fixed lists; returns (rgb [H,W,3], T [H,W], count [H,W])."""
+def _list_rule(proj32):
+    """(mean2d32, ellipse, tile_test) of a binary32 projection, or the plain rectangle rule."""
+    if proj32 is None or proj32.get("tile_test", TILE_SQUARE) == TILE_SQUARE:
+        return None, None, TILE_SQUARE
+    return _f32(proj32["mean2d"]), _f32(proj32["ellipse"]), int(proj32["tile_test"])
+
+
+def composite_fixed(screen: dict, rect, order, camera: dict, bg=(0.0, 0.0, 0.0), n_limit=None, t_eps=1e-4,
+                    proj32=None):
+    """binary64 compositing over fixed lists; returns (rgb [H,W,3], T [H,W], count [H,W]).
+    proj32 (a `preprocess` result) supplies the tile membership rule when it is not the rectangle."""
     lib = _load()
+    m32, ell, tt = _list_rule(proj32)
     W, H = camera["width"], camera["height"]
     n = np.asarray(screen["opacity"]).shape[0]
     m2, co, op, rgb = (_f64(screen[k]) for k in ("mean2d", "conic", "opacity", "rgb"))
@@ -344,18 +382,20 @@ def composite_fixed(screen: dict, rect, order, camera: dict, bg=(0.0, 0.0, 0.0),
     order = np.ascontiguousarray(order, np.int64)
     lim = None if n_limit is None else np.ascontiguousarray(n_limit, np.int64).reshape(-1)
     out, T, cnt = np.zeros(H * W * 3), np.zeros(H * W), np.zeros(H * W, np.int64)
-    lib.oracle_composite_fixed(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(order), order.shape[0],
-                               W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps), _ptr(out), _ptr(T), _ptr(cnt))
+    lib.oracle_composite_fixed(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(m32), _ptr(ell), tt,
+                               _ptr(order), order.shape[0], W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps),
+                               _ptr(out), _ptr(T), _ptr(cnt))
     return out.reshape(H, W, 3), T.reshape(H, W), cnt.reshape(H, W)
 
 
 def composite_backward(screen: dict, rect, order, camera: dict, g_image, bg=(0.0, 0.0, 0.0), n_limit=None,
-                       t_eps=1e-4, pixels=None) -> dict:
+                       t_eps=1e-4, pixels=None, proj32=None) -> dict:
     """Vector-Jacobian product of composite_fixed: gradients for mean2d, conic, opacity, rgb.
 
     pixels: optional flat indices y*W+x; only their cotangents are taken (the rest count as 0).
     """
     lib = _load()
+    m32, ell, tt = _list_rule(proj32)
     W, H = camera["width"], camera["height"]
     n = np.asarray(screen["opacity"]).shape[0]
     m2, co, op, rgb = (_f64(screen[k]) for k in ("mean2d", "conic", "opacity", "rgb"))
@@ -366,14 +406,16 @@ def composite_backward(screen: dict, rect, order, camera: dict, g_image, bg=(0.0
     assert gi.shape[0] == H * W * 3
     out = dict(mean2d=np.zeros((2, n)), conic=np.zeros((3, n)), opacity=np.zeros(n), rgb=np.zeros((3, n)))
     pix = None if pixels is None else np.ascontiguousarray(pixels, np.int64)
-    lib.oracle_composite_backward(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(order),
-                                  order.shape[0], W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps), _ptr(gi),
+    lib.oracle_composite_backward(n, _ptr(m2), _ptr(co), _ptr(op), _ptr(rgb), _ptr(rect), _ptr(m32), _ptr(ell),
+                                  tt, _ptr(order), order.shape[0], W, H, _ptr(_f64(bg)), _ptr(lim), float(t_eps),
+                                  _ptr(gi),
                                   _ptr(pix), 0 if pix is None else pix.shape[0],
                                   _ptr(out["mean2d"]), _ptr(out["conic"]), _ptr(out["opacity"]), _ptr(out["rgb"]))
     return out
 
 
-def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0, 0.0, 0.0), pixels=None) -> dict:
+def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0, 0.0, 0.0), pixels=None,
+                    tile_test: int = TILE_SQUARE) -> dict:
     """Gradient of sum(g_image * render(arrays)) for every Gaussian parameter.
 
     The lists (tile rectangles, visibility, depth order) come from the binary32
@@ -384,14 +426,14 @@ def render_backward(arrays: dict, sh_degree: int, camera: dict, g_image, bg=(0.0
     per-pixel blended counts (None when `pixels` restricts the cotangent to
     the listed flat pixel indices, y*W+x).
     """
-    proj = preprocess(arrays, sh_degree, camera)
+    proj = preprocess(arrays, sh_degree, camera, tile_test=tile_test)
     order = depth_order(proj["depth"], proj["tile_count"])
     scr = project64(arrays, sh_degree, camera)
     scr["opacity"] = _f64(arrays["opacity"])
     cnt = None
     if pixels is None:
-        _, _, cnt = composite_fixed(scr, proj["rect"], order, camera, bg=bg)
-    gs = composite_backward(scr, proj["rect"], order, camera, g_image, bg=bg, pixels=pixels)
+        _, _, cnt = composite_fixed(scr, proj["rect"], order, camera, bg=bg, proj32=proj)
+    gs = composite_backward(scr, proj["rect"], order, camera, g_image, bg=bg, pixels=pixels, proj32=proj)
     gp = project_backward(arrays, sh_degree, camera, gs["mean2d"], gs["conic"], gs["rgb"])
     gp["opacity"] = gs["opacity"]
     gp.update(screen_mean2d=gs["mean2d"], screen_conic=gs["conic"], screen_rgb=gs["rgb"], screen_opacity=gs["opacity"],

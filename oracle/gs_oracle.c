@@ -34,6 +34,10 @@ typedef struct {
     int32_t width, height;
 } oracle_camera;
 
+/* Tile membership rules (option GS_OPT_TILE_TEST of the library). */
+#define TILE_TEST_SQUARE 0   /* every tile of [u-r, u+r] x [v-r, v+r] (the pages' rule)              */
+#define TILE_TEST_ELLIPSE 1  /* those of them whose pixel-centre box meets the 3-sigma ellipse q <= 9 */
+
 /* Outputs are planes of length n (index g). */
 typedef struct {
     float *depth;              /* camera-space z                                 */
@@ -45,6 +49,7 @@ typedef struct {
     int32_t *rect;             /* [4][n]  x0, x1, y0, y1 in tiles, [x0,x1)x[y0,y1) */
     uint32_t *tile_count;      /* [n]                                             */
     double *rgb;               /* [3][n]  SH colour in binary64                   */
+    float *ellipse;            /* [5][n]  ymax, dyr, b/c, det/c, c (see oracle_row_span); may be NULL */
 } oracle_projected;
 
 /* Clamp that sends NaN to the lower bound (so the int conversion is defined). */
@@ -138,9 +143,76 @@ void oracle_cov3d(const float q_in[4], const float ls[3], float out6[6]) {
  * Tile assignment (flowchart "Assign to tiles (16x16 screen-space)") takes
  * every 16x16 tile met by the square [u-r, u+r] x [v-r, v+r].
  */
+/*
+ * Exact 3-sigma footprint per tile row (tile test ELLIPSE; an integer rule that
+ * the library's GS_TILE_ELLIPSE option states the same way).  With the 2D
+ * covariance [[a, b], [b, c]], the ellipse q <= 9 cut at height dy is centred at
+ * (b/c) dy with half-width sqrt((det/c) (9 - dy^2/c)), |dy| <= 3 sqrt(c); its right
+ * end is largest at dy = 3b/sqrt(a) and its left end smallest at -3b/sqrt(a).  For
+ * tile row ty (pixel-centre rows 16 ty .. 16 ty + 15) those heights are clamped to
+ * the row's band, giving the x-extent [u + xl, u + xr]; the kept tiles are the tx of
+ * the rectangle [x0, x1) whose pixel-centre columns 16 tx .. 16 tx + 15 meet it.
+ * binary32 in this order, no contraction; E = (ymax, dyr, bc, kc, c).  Writes the
+ * half-open span [*a, *b) (empty: *a == *b).
+ */
+void oracle_row_span(float u, float v, const float E[5], int32_t x0, int32_t x1, int32_t ty, int32_t *pa,
+                     int32_t *pb) {
+    const float ymax = E[0], dyr = E[1], bc = E[2], kc = E[3], c = E[4];
+    *pa = *pb = x0;
+    const float p = (float)(16 * ty) - v;
+    const float q = (float)(16 * ty + 15) - v;
+    const float lo = fmaxf(p, -ymax), hi = fminf(q, ymax);
+    if (!(lo <= hi)) return;
+    const float dr = fminf(fmaxf(dyr, lo), hi);
+    const float dl = fminf(fmaxf(-dyr, lo), hi);
+    const float tr = fmaxf(9.0f - (dr * dr) / c, 0.0f);
+    const float tl = fmaxf(9.0f - (dl * dl) / c, 0.0f);
+    const float xr = bc * dr + sqrtf(kc * tr);
+    const float xl = bc * dl - sqrtf(kc * tl);
+    float fa = ceilf(((u + xl) - 15.0f) * 0.0625f);
+    float fb = floorf((u + xr) * 0.0625f) + 1.0f;
+    fa = fmaxf(fa, (float)x0);
+    fb = fminf(fb, (float)x1);
+    if (!(fa < fb)) return;
+    *pa = (int32_t)fa;
+    *pb = (int32_t)fb;
+}
+
+/* Ellipse parameters of oracle_row_span from the 2D covariance (binary32, this order). */
+static void ellipse_params(float a, float b, float c, float det, float E[5]) {
+    E[0] = 3.0f * sqrtf(c);
+    E[1] = (3.0f * b) / sqrtf(a);
+    E[2] = b / c;
+    E[3] = det / c;
+    E[4] = c;
+}
+
+/* Whether tile (tx, ty) of Gaussian g's rectangle is one of its pairs. */
+int32_t oracle_tile_kept(int64_t n, int64_t g, const float *mean2d, const float *ellipse, const int32_t *rect,
+                         int32_t tile_test, int32_t tx, int32_t ty) {
+    if (tx < rect[g] || tx >= rect[n + g] || ty < rect[2 * n + g] || ty >= rect[3 * n + g]) return 0;
+    if (tile_test != TILE_TEST_ELLIPSE) return 1;
+    float E[5];
+    for (int k = 0; k < 5; ++k) E[k] = ellipse[k * n + g];
+    if (!(E[4] > 0.0f) || !(E[0] > 0.0f)) return 1;   /* degenerate covariance: the whole rectangle */
+    int32_t a, b;
+    oracle_row_span(mean2d[g], mean2d[n + g], E, rect[g], rect[n + g], ty, &a, &b);
+    return tx >= a && tx < b;
+}
+
+void oracle_preprocess_ex(int64_t n, int32_t sh_degree, const float *mean, const float *quat,
+                          const float *log_scale, const float *opacity, const float *sh,
+                          const oracle_camera *cam, int32_t tile_test, oracle_projected *out);
+
 void oracle_preprocess(int64_t n, int32_t sh_degree, const float *mean, const float *quat,
                        const float *log_scale, const float *opacity, const float *sh,
                        const oracle_camera *cam, oracle_projected *out) {
+    oracle_preprocess_ex(n, sh_degree, mean, quat, log_scale, opacity, sh, cam, TILE_TEST_SQUARE, out);
+}
+
+void oracle_preprocess_ex(int64_t n, int32_t sh_degree, const float *mean, const float *quat,
+                          const float *log_scale, const float *opacity, const float *sh,
+                          const oracle_camera *cam, int32_t tile_test, oracle_projected *out) {
     (void)opacity;
     const int32_t tiles_x = (cam->width + TILE - 1) / TILE;
     const int32_t tiles_y = (cam->height + TILE - 1) / TILE;
@@ -222,7 +294,21 @@ void oracle_preprocess(int64_t n, int32_t sh_degree, const float *mean, const fl
         out->rect[n + g] = x1;
         out->rect[2 * n + g] = y0;
         out->rect[3 * n + g] = y1;
-        out->tile_count[g] = (uint32_t)((x1 - x0) * (y1 - y0));
+        float E[5];
+        ellipse_params(a, b, c, det, E);
+        if (out->ellipse)
+            for (int k = 0; k < 5; ++k) out->ellipse[k * n + g] = E[k];
+        if (tile_test == TILE_TEST_ELLIPSE && E[4] > 0.0f && E[0] > 0.0f) {
+            uint32_t count = 0;
+            for (int32_t ty = y0; ty < y1; ++ty) {
+                int32_t sa, sb;
+                oracle_row_span(u, v, E, x0, x1, ty, &sa, &sb);
+                count += (uint32_t)(sb - sa);
+            }
+            out->tile_count[g] = count;
+        } else {
+            out->tile_count[g] = (uint32_t)((x1 - x0) * (y1 - y0));
+        }
     }
 }
 
@@ -262,9 +348,24 @@ int64_t oracle_total_pairs(int64_t n, const uint32_t *tile_count) {
  * depth (section "Étape 5").  Equal depths keep ascending Gaussian index.
  * Any output pointer may be NULL.
  */
+void oracle_bin_ex(int64_t n, const float *depth, const int32_t *rect, const uint32_t *tile_count,
+                   int32_t tiles_x, int32_t tiles_y, const float *mean2d, const float *ellipse, int32_t tile_test,
+                   uint64_t *keys_unsorted, uint32_t *vals_unsorted, uint64_t *keys_sorted, uint32_t *vals_sorted,
+                   uint32_t *ranges);
+
 void oracle_bin(int64_t n, const float *depth, const int32_t *rect, const uint32_t *tile_count,
                 int32_t tiles_x, int32_t tiles_y, uint64_t *keys_unsorted, uint32_t *vals_unsorted,
                 uint64_t *keys_sorted, uint32_t *vals_sorted, uint32_t *ranges) {
+    oracle_bin_ex(n, depth, rect, tile_count, tiles_x, tiles_y, NULL, NULL, TILE_TEST_SQUARE, keys_unsorted,
+                  vals_unsorted, keys_sorted, vals_sorted, ranges);
+}
+
+/* As oracle_bin; with tile_test ELLIPSE only the kept tiles of each rectangle are
+ * listed (still row-major), which needs mean2d and ellipse. */
+void oracle_bin_ex(int64_t n, const float *depth, const int32_t *rect, const uint32_t *tile_count,
+                   int32_t tiles_x, int32_t tiles_y, const float *mean2d, const float *ellipse, int32_t tile_test,
+                   uint64_t *keys_unsorted, uint32_t *vals_unsorted, uint64_t *keys_sorted, uint32_t *vals_sorted,
+                   uint32_t *ranges) {
     int64_t m = oracle_total_pairs(n, tile_count);
     kv_pair *pairs = (kv_pair *)malloc(sizeof(kv_pair) * (size_t)(m > 0 ? m : 1));
     int64_t e = 0;
@@ -273,6 +374,9 @@ void oracle_bin(int64_t n, const float *depth, const int32_t *rect, const uint32
         int32_t x0 = rect[g], x1 = rect[n + g], y0 = rect[2 * n + g], y1 = rect[3 * n + g];
         for (int32_t ty = y0; ty < y1; ++ty)
             for (int32_t tx = x0; tx < x1; ++tx) {
+                if (tile_test == TILE_TEST_ELLIPSE &&
+                    !oracle_tile_kept(n, g, mean2d, ellipse, rect, tile_test, tx, ty))
+                    continue;
                 uint64_t tile = (uint64_t)(ty * tiles_x + tx);
                 pairs[e].key = (tile << 32) | float_bits(depth[g]);
                 pairs[e].val = (uint32_t)g;
@@ -330,11 +434,28 @@ static int cmp_depth(const void *pa, const void *pb) {
  * out_rgb[n_pix*3], out_T[n_pix], out_count[n_pix] (blended pairs); out_T and
  * out_count may be NULL.
  */
+void oracle_composite_ex(int64_t n, const float *mean2d, const float *conic, const float *opacity,
+                         const double *rgb, const float *depth, const int32_t *rect,
+                         const uint32_t *tile_count, const float *ellipse, int32_t tile_test, int32_t width,
+                         int32_t height, const double bg[3], int32_t support_all, double t_eps,
+                         const int64_t *pixels, int64_t n_pix, double *out_rgb, double *out_T, int64_t *out_count);
+
 void oracle_composite(int64_t n, const float *mean2d, const float *conic, const float *opacity,
                       const double *rgb, const float *depth, const int32_t *rect,
                       const uint32_t *tile_count, int32_t width, int32_t height, const double bg[3],
                       int32_t support_all, double t_eps, const int64_t *pixels, int64_t n_pix,
                       double *out_rgb, double *out_T, int64_t *out_count) {
+    oracle_composite_ex(n, mean2d, conic, opacity, rgb, depth, rect, tile_count, NULL, TILE_TEST_SQUARE, width,
+                        height, bg, support_all, t_eps, pixels, n_pix, out_rgb, out_T, out_count);
+}
+
+/* As oracle_composite; with tile_test ELLIPSE a Gaussian reaches a pixel only when the
+ * pixel's tile is one of its kept tiles (oracle_tile_kept). */
+void oracle_composite_ex(int64_t n, const float *mean2d, const float *conic, const float *opacity,
+                         const double *rgb, const float *depth, const int32_t *rect,
+                         const uint32_t *tile_count, const float *ellipse, int32_t tile_test, int32_t width,
+                         int32_t height, const double bg[3], int32_t support_all, double t_eps,
+                         const int64_t *pixels, int64_t n_pix, double *out_rgb, double *out_T, int64_t *out_count) {
     depth_order *order = (depth_order *)malloc(sizeof(depth_order) * (size_t)(n > 0 ? n : 1));
     int64_t nv = 0;
     for (int64_t g = 0; g < n; ++g)
@@ -357,6 +478,9 @@ void oracle_composite(int64_t n, const float *mean2d, const float *conic, const 
             int64_t g = order[k].g;
             if (!support_all) {
                 if (tx < rect[g] || tx >= rect[n + g] || ty < rect[2 * n + g] || ty >= rect[3 * n + g])
+                    continue;
+                if (tile_test == TILE_TEST_ELLIPSE &&
+                    !oracle_tile_kept(n, g, mean2d, ellipse, rect, tile_test, tx, ty))
                     continue;
             }
             double dx = (double)px - (double)mean2d[g];

@@ -16,9 +16,10 @@
  *   oracle_project_backward   its vector-Jacobian product;
  *   oracle_composite_fixed    front-to-back compositing (section "La règle de
  *                             composition alpha") over FIXED per-pixel lists:
- *                             the Gaussians whose tile rectangle holds the
- *                             pixel's tile, in a given depth order, cut after
- *                             a given count per pixel (or at T < t_eps);
+ *                             the Gaussians one of whose tiles (the rectangle,
+ *                             or its exact-footprint part) is the pixel's, in a
+ *                             given depth order, cut after a given count per
+ *                             pixel (or at T < t_eps);
  *   oracle_composite_backward its vector-Jacobian product.
  *
  * With the lists held fixed the image is a smooth function of the screen
@@ -290,14 +291,24 @@ void oracle_project_backward(int64_t n, int32_t K, const double *mean, const dou
     }
 }
 
-/* The list of pixel (px, py): Gaussians of order[] whose rectangle holds its tile. */
-static int64_t pixel_list(int64_t n, const int32_t *rect, const int64_t *order, int64_t nv, int32_t px, int32_t py,
-                          int64_t *list) {
+int32_t oracle_tile_kept(int64_t n, int64_t g, const float *mean2d, const float *ellipse, const int32_t *rect,
+                         int32_t tile_test, int32_t tx, int32_t ty);
+
+/* Tile membership of the lists: the rectangle, and with tile_test 1 the exact 3-sigma
+ * footprint of gs_oracle.c (binary32 mean2d32 and ellipse from its projection). */
+typedef struct {
+    const float *mean2d32, *ellipse;
+    int32_t tile_test;
+} list_rule;
+
+/* The list of pixel (px, py): Gaussians of order[] one of whose tiles is the pixel's. */
+static int64_t pixel_list(int64_t n, const int32_t *rect, const list_rule *rule, const int64_t *order, int64_t nv,
+                          int32_t px, int32_t py, int64_t *list) {
     const int32_t tx = px / TILE, ty = py / TILE;
     int64_t len = 0;
     for (int64_t k = 0; k < nv; ++k) {
         const int64_t g = order[k];
-        if (tx >= rect[g] && tx < rect[n + g] && ty >= rect[2 * n + g] && ty < rect[3 * n + g]) list[len++] = g;
+        if (oracle_tile_kept(n, g, rule->mean2d32, rule->ellipse, rect, rule->tile_test, tx, ty)) list[len++] = g;
     }
     return len;
 }
@@ -323,14 +334,16 @@ static double pixel_alpha(int64_t n, int64_t g, double px, double py, const doub
  * entries); out_T and out_count may be NULL.
  */
 void oracle_composite_fixed(int64_t n, const double *mean2d, const double *conic, const double *opacity,
-                            const double *rgb, const int32_t *rect, const int64_t *order, int64_t nv,
+                            const double *rgb, const int32_t *rect, const float *mean2d32, const float *ellipse,
+                            int32_t tile_test, const int64_t *order, int64_t nv,
                             int32_t width, int32_t height, const double bg[3], const int64_t *n_limit, double t_eps,
                             double *out_rgb, double *out_T, int64_t *out_count) {
+    const list_rule rule = {mean2d32, ellipse, tile_test};
     int64_t *list = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nv > 0 ? nv : 1));
     for (int32_t py = 0; py < height; ++py)
         for (int32_t px = 0; px < width; ++px) {
             const int64_t p = (int64_t)py * width + px;
-            int64_t len = pixel_list(n, rect, order, nv, px, py, list);
+            int64_t len = pixel_list(n, rect, &rule, order, nv, px, py, list);
             if (n_limit && n_limit[p] < len) len = n_limit[p];
             double T = 1.0, C[3] = {0.0, 0.0, 0.0};
             int64_t cnt = 0;
@@ -368,7 +381,8 @@ void oracle_composite_fixed(int64_t n, const double *mean2d, const double *conic
  * the only pixels whose cotangent is taken (the others count as zero).
  */
 void oracle_composite_backward(int64_t n, const double *mean2d, const double *conic, const double *opacity,
-                               const double *rgb, const int32_t *rect, const int64_t *order, int64_t nv,
+                               const double *rgb, const int32_t *rect, const float *mean2d32, const float *ellipse,
+                               int32_t tile_test, const int64_t *order, int64_t nv,
                                int32_t width, int32_t height, const double bg[3], const int64_t *n_limit,
                                double t_eps, const double *g_image, const int64_t *pixels, int64_t n_pix,
                                double *g_mean2d, double *g_conic, double *g_opacity, double *g_rgb) {
@@ -380,11 +394,12 @@ void oracle_composite_backward(int64_t n, const double *mean2d, const double *co
     int64_t *list = (int64_t *)malloc(sizeof(int64_t) * cap);
     double *al = (double *)malloc(sizeof(double) * cap);
     double *Ts = (double *)malloc(sizeof(double) * cap);
+    const list_rule rule = {mean2d32, ellipse, tile_test};
     if (!pixels) n_pix = (int64_t)width * height;
     for (int64_t pi = 0; pi < n_pix; ++pi) {
         const int64_t p = pixels ? pixels[pi] : pi;
         const int32_t px = (int32_t)(p % width), py = (int32_t)(p / width);
-        int64_t len = pixel_list(n, rect, order, nv, px, py, list);
+        int64_t len = pixel_list(n, rect, &rule, order, nv, px, py, list);
         if (n_limit && n_limit[p] < len) len = n_limit[p];
         double T = 1.0;
         int64_t cnt = 0;

@@ -114,10 +114,14 @@ def test_composite_backward_matches_finite_differences():
         assert np.array_equal(g[k], g2[k]), k
 
 
-def test_render_backward_end_to_end_matches_finite_differences():
+@pytest.mark.parametrize("tile_test", [0, 1])
+def test_render_backward_end_to_end_matches_finite_differences(tile_test):
     sc, cam, a, p32, order, scr = _screen_case(seed=33)
+    if tile_test:
+        p32 = oracle.preprocess(a, 2, cam, tile_test=tile_test)
+        order = oracle.depth_order(p32["depth"], p32["tile_count"])
     bg = (0.1, 0.2, 0.3)
-    _, _, cnt = oracle.composite_fixed(scr, p32["rect"], order, cam, bg=bg)
+    _, _, cnt = oracle.composite_fixed(scr, p32["rect"], order, cam, bg=bg, proj32=p32)
     rng = np.random.default_rng(4)
     gimg = rng.normal(size=(cam["height"], cam["width"], 3))
     a64 = _as64(a)
@@ -125,10 +129,10 @@ def test_render_backward_end_to_end_matches_finite_differences():
     def loss():
         s = oracle.project64(a64, 2, cam)
         s["opacity"] = a64["opacity"]
-        img, _, _ = oracle.composite_fixed(s, p32["rect"], order, cam, bg=bg, n_limit=cnt)
+        img, _, _ = oracle.composite_fixed(s, p32["rect"], order, cam, bg=bg, n_limit=cnt, proj32=p32)
         return float((gimg * img).sum())
 
-    g = oracle.render_backward(a, 2, cam, gimg, bg=bg)
+    g = oracle.render_backward(a, 2, cam, gimg, bg=bg, tile_test=tile_test)
     vis = order
     for k, h in (("mean", 1e-6), ("quat", 1e-6), ("log_scale", 1e-6), ("opacity", 1e-6), ("sh", 1e-5)):
         fd = _fd(loss, a64[k], h)
