@@ -155,12 +155,28 @@ typedef enum {
     GS_SORT_KEY64 = 1
 } gs_sort_mode;
 
+/* Which tiles a Gaussian is listed in. */
+typedef enum {
+    /* every tile of the square [u-r, u+r] x [v-r, v+r], r the 3-sigma radius along the major
+       axis (flowchart "Assign to tiles (16x16 screen-space)"; the default) */
+    GS_TILE_SQUARE = 0,
+    /* those tiles of the square whose pixel-centre box [16tx, 16tx+15] x [16ty, 16ty+15]
+       meets the 3-sigma ellipse d^T cov2d^-1 d <= 9 (fewer pairs; drops contributions
+       below o exp(-9/2) per pixel).  Per tile row the kept tiles are one span: the
+       ellipse cut at height dy is centred at (b/c) dy with half-width
+       sqrt((det/c)(9 - dy^2/c)); its ends peak at dy = +-3b/sqrt(a) clamped to the
+       row's band.  Evaluated in binary32 in a fixed order, so counts and keys are exact. */
+    GS_TILE_ELLIPSE = 1
+} gs_tile_test;
+
 typedef enum {
     GS_OPT_SORT_MODE = 0,            /* gs_sort_mode, default GS_SORT_DEPTH_FIRST */
     GS_OPT_EMIT_KEYS = 1,            /* 1: gs_bin_and_sort materialises keys (default 1); gs_render never does */
     GS_OPT_MAX_DUPS = 2,             /* cap on pairs per frame, at most and by default 2^32-1 -> GS_ERR_CAPACITY */
     GS_OPT_MAX_WORKSPACE_BYTES = 3,  /* cap on context device memory (default: none) -> GS_ERR_OUT_OF_MEMORY */
-    GS_OPT_PROFILE = 4               /* 1: bracket every kernel with HIP events (see gs_profile_read) */
+    GS_OPT_PROFILE = 4,              /* 1: bracket every kernel with HIP events (see gs_profile_read) */
+    GS_OPT_TILE_TEST = 5             /* gs_tile_test, default GS_TILE_SQUARE; read by gs_preprocess, and the
+                                        binning, compositing and backward of that projection follow it */
 } gs_option;
 
 /* Per-stage timing collected while GS_OPT_PROFILE is 1. */

@@ -17,13 +17,13 @@ def note(msg: str):
 
 
 def gpu_run(arrays: dict, sh_degree: int, camera: dict, bg=(0.0, 0.0, 0.0), sort_mode: int = 0,
-            emit_keys: bool = True, aux: bool = True, rast=None):
+            emit_keys: bool = True, aux: bool = True, rast=None, tile_test: int = 0):
     """Preprocess + bin + composite through the C ABI; returns numpy copies."""
     import torch
 
     from tile_differentiable_rasterizer_gs_amd import binding
 
-    r = rast or binding.Rasterizer(sort_mode=sort_mode, emit_keys=emit_keys)
+    r = rast or binding.Rasterizer(sort_mode=sort_mode, emit_keys=emit_keys, tile_test=tile_test)
     dev = binding.gaussians_to_device(arrays)
     pr = r.preprocess(dev, sh_degree, camera)
     bn = r.bin_and_sort(pr, camera)

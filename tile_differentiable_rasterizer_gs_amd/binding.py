@@ -17,7 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libgsrast.so")
 
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_OUT_OF_MEMORY, GS_ERR_CAPACITY, GS_ERR_DEVICE = range(5)
 GS_SORT_DEPTH_FIRST, GS_SORT_KEY64 = 0, 1
-GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE = range(5)
+GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE, GS_OPT_TILE_TEST = \
+    range(6)
+GS_TILE_SQUARE, GS_TILE_ELLIPSE = 0, 1
 STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback",
           "backward_composite", "backward_setup", "backward_gaussian")
 SPLAT_STRIDE = 16
@@ -182,7 +184,8 @@ def make_gaussians(tensors: dict, sh_degree: int) -> Gaussians:
 class Rasterizer:
     """One library context on the current HIP device."""
 
-    def __init__(self, device: int | None = None, sort_mode: int = GS_SORT_DEPTH_FIRST, emit_keys: bool = True):
+    def __init__(self, device: int | None = None, sort_mode: int = GS_SORT_DEPTH_FIRST, emit_keys: bool = True,
+                 tile_test: int = GS_TILE_SQUARE):
         self.lib = load_library()
         self.device = torch.cuda.current_device() if device is None else device
         ctx = ctypes.c_void_p()
@@ -192,6 +195,7 @@ class Rasterizer:
         self.ctx = ctx
         self.set_option(GS_OPT_SORT_MODE, sort_mode)
         self.set_option(GS_OPT_EMIT_KEYS, 1 if emit_keys else 0)
+        self.set_option(GS_OPT_TILE_TEST, tile_test)
         self._keep = []
 
     def close(self):

@@ -49,6 +49,8 @@ struct gs_context {
     int sort_mode = GS_SORT_DEPTH_FIRST;
     int emit_keys = 1;
     int profile = 0;
+    int tile_test = GS_TILE_SQUARE;            // option
+    int tile_test_used = GS_TILE_SQUARE;       // the rule of the last gs_preprocess
     int64_t max_dups = kMaxPairs;
     int64_t max_workspace = -1;
     size_t workspace = 0;
@@ -56,7 +58,7 @@ struct gs_context {
 
     // per-Gaussian
     DeviceBuffer splat, depth, rect, tile_count, dkey[2], dval[2], dcount, offsets, scan_scratch, dsort_scratch,
-        total;
+        total, ellipse;
     // per-pair
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // per-tile
@@ -290,7 +292,7 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
-                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order,
+                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order, &ctx->ellipse,
                            &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->s2_order,
                            &ctx->s2_rec, &ctx->s2_trans, &ctx->s2_partial};
     for (DeviceBuffer *b : all)
@@ -327,6 +329,11 @@ gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
         case GS_OPT_PROFILE:
             if (value != 0 && value != 1) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "profile must be 0 or 1");
             ctx->profile = (int)value;
+            return GS_OK;
+        case GS_OPT_TILE_TEST:
+            if (value != GS_TILE_SQUARE && value != GS_TILE_ELLIPSE)
+                return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown tile test %lld", (long long)value);
+            ctx->tile_test = (int)value;
             return GS_OK;
     }
     return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
@@ -378,6 +385,10 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     p.tile_count = as<uint32_t>(ctx->tile_count);
     p.depth_key = as<uint32_t>(ctx->dkey[0]);
     p.depth_index = as<uint32_t>(ctx->dval[0]);
+    if (ctx->tile_test == GS_TILE_ELLIPSE) {
+        GS_TRY(ensure(ctx, ctx->ellipse, nn * sizeof(EllipseRec)));
+        p.ellipse = as<EllipseRec>(ctx->ellipse);
+    }
 
     GS_TRY(span_begin(ctx, GS_STAGE_PREPROCESS, stream));
     launch_preprocess(p, stream);
@@ -385,6 +396,7 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     GS_TRY(span_end(ctx, stream));
 
     ctx->n = n;
+    ctx->tile_test_used = ctx->tile_test;
     ctx->sh_degree = g->sh_degree;
     ctx->g_mean = g->mean;
     ctx->num_dups = -1;
@@ -447,6 +459,10 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     d.depth = pr->depth;
     d.tiles_x = ctx->tiles_x;
     d.values = as<uint32_t>(ctx->pval[0]);
+    if (ctx->tile_test_used == GS_TILE_ELLIPSE) {
+        d.ellipse = as<EllipseRec>(ctx->ellipse);
+        d.tile_count = pr->tile_count;
+    }
     RangesParams r{};
     r.num_dups = d_total;
     r.capacity = cap;
@@ -742,6 +758,8 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     c.pair_grad = as<float>(ctx->pair_grad);
     c.tile_order = bwd_order;
     c.cut = as<unsigned long long>(ctx->tile_cut);
+    const EllipseRec *ell = ctx->tile_test_used == GS_TILE_ELLIPSE ? as<EllipseRec>(ctx->ellipse) : nullptr;
+    c.ellipse = ell;
     GS_TRY(span_begin(ctx, GS_STAGE_BACKWARD_COMPOSITE, stream));
     if (M > 0) launch_composite_backward(c, stream);
     GS_TRY(check_launch(ctx, "composite backward"));
@@ -766,6 +784,7 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     q.rect = reinterpret_cast<const uint2 *>(pr->rect);
     q.depth = pr->depth;
     q.cut = as<unsigned long long>(ctx->tile_cut);
+    q.ellipse = ell;
     q.tiles_x = ctx->tiles_x;
     q.pair_grad = as<float>(ctx->pair_grad);
     q.g_mean = grads->mean;

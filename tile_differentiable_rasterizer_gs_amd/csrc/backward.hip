@@ -193,7 +193,8 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
             s_col[lane] = make_float4(r1.w, r2.x, zero_o ? INFINITY : GS_ALPHA_MAX, 0.0f);
             const uint2 rc = p.rect[g];
             const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
-            s_pos[lane] = p.pair_base[g] + (ty - y0) * (x1 - x0) + (tx - x0);
+            s_pos[lane] = p.pair_base[g] + (p.ellipse ? kept_index(p.ellipse[g], x0, x1, y0, tx, ty)
+                                                      : (ty - y0) * (x1 - x0) + (tx - x0));
         }
         __syncthreads();
         for (int k = cnt - 1; k >= 0; --k) {
@@ -476,7 +477,29 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         float acc[kPairGrad];
 #pragma unroll
         for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
-        if (count) {
+        if (count && p.ellipse) {
+            // exact footprint: records follow the row spans; the row's lanes take its tiles
+            const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
+            const uint2 rc = p.rect[g];
+            const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y1 = rc.y >> 16;
+            const EllipseRec E = p.ellipse[g];
+            const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
+            uint32_t k0 = 0, sa, sb;
+            for (uint32_t ty = rc.y & 0xffffu; ty < y1; ++ty) {
+                row_span(E, x0, x1, ty, sa, sb);
+                for (uint32_t tx = sa + li; tx < sb; tx += kRowLanes) {
+                    if (key > p.cut[ty * (uint32_t)p.tiles_x + tx]) continue;
+                    const float *r = rec + (size_t)(k0 + tx - sa) * kPairStride;
+                    const float4 a = *reinterpret_cast<const float4 *>(r);
+                    const float4 b = *reinterpret_cast<const float4 *>(r + 4);
+                    const float c8 = r[8];
+                    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+                    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+                    acc[8] += c8;
+                }
+                k0 += sb - sa;
+            }
+        } else if (count) {
             const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
             const uint2 rc = p.rect[g];
             const uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu;

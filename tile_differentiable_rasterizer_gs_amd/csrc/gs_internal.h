@@ -14,6 +14,71 @@ constexpr int kBlock = 256;      // threads per workgroup for every kernel (4 wa
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
+// exact-footprint tile rule (GS_TILE_ELLIPSE)
+// ---------------------------------------------------------------------------
+// Per Gaussian: e = (ymax, dyr, b/c, det/c), f = (c, u, v, valid) with [[a, b], [b, c]] the
+// 2D covariance, ymax = 3 sqrt(c), dyr = 3b / sqrt(a); valid = 0 when a or c is not
+// positive (then the whole square is kept).
+struct EllipseRec {
+    float4 e;
+    float4 f;
+};
+
+__device__ __forceinline__ EllipseRec make_ellipse(float a, float b, float c, float det, float u, float v) {
+#pragma clang fp contract(off)
+    EllipseRec E;
+    E.e = make_float4(3.0f * sqrtf(c), (3.0f * b) / sqrtf(a), b / c, det / c);
+    E.f = make_float4(c, u, v, (c > 0.0f && E.e.x > 0.0f) ? 1.0f : 0.0f);
+    return E;
+}
+
+// Kept tiles [*pa, *pb) of tile row ty of the square [x0, x1): those whose pixel-centre
+// columns 16 tx .. 16 tx + 15 meet the x-extent of the 3-sigma ellipse over the row's
+// pixel-centre band 16 ty .. 16 ty + 15.  The ellipse cut at height dy is centred at
+// (b/c) dy with half-width sqrt((det/c)(9 - dy^2/c)); its right end peaks at dy = dyr,
+// its left end at -dyr, each clamped to the band.  binary32 in this order, no
+// contraction: the tile counts and keys are a function of the inputs alone.
+__device__ __forceinline__ void row_span(const EllipseRec &E, uint32_t x0, uint32_t x1, uint32_t ty, uint32_t &pa,
+                                         uint32_t &pb) {
+#pragma clang fp contract(off)
+    pa = pb = x0;
+    if (E.f.w == 0.0f) {
+        pb = x1;
+        return;
+    }
+    const float ymax = E.e.x, dyr = E.e.y, bc = E.e.z, kc = E.e.w, c = E.f.x, u = E.f.y, v = E.f.z;
+    const float p = (float)(16 * ty) - v;
+    const float q = (float)(16 * ty + 15) - v;
+    const float lo = fmaxf(p, -ymax), hi = fminf(q, ymax);
+    if (!(lo <= hi)) return;
+    const float dr = fminf(fmaxf(dyr, lo), hi);
+    const float dl = fminf(fmaxf(-dyr, lo), hi);
+    const float tr = fmaxf(9.0f - (dr * dr) / c, 0.0f);
+    const float tl = fmaxf(9.0f - (dl * dl) / c, 0.0f);
+    const float xr = bc * dr + sqrtf(kc * tr);
+    const float xl = bc * dl - sqrtf(kc * tl);
+    float fa = ceilf(((u + xl) - 15.0f) * 0.0625f);
+    float fb = floorf((u + xr) * 0.0625f) + 1.0f;
+    fa = fmaxf(fa, (float)x0);
+    fb = fminf(fb, (float)x1);
+    if (!(fa < fb)) return;
+    pa = (uint32_t)fa;
+    pb = (uint32_t)fb;
+}
+
+// Index of tile (tx, ty) among a Gaussian's kept tiles (row-major over the square).
+__device__ __forceinline__ uint32_t kept_index(const EllipseRec &E, uint32_t x0, uint32_t x1, uint32_t y0,
+                                               uint32_t tx, uint32_t ty) {
+    uint32_t k = 0, a, b;
+    for (uint32_t r = y0; r < ty; ++r) {
+        row_span(E, x0, x1, r, a, b);
+        k += b - a;
+    }
+    row_span(E, x0, x1, ty, a, b);
+    return k + (tx - a);
+}
+
+// ---------------------------------------------------------------------------
 // preprocess
 // ---------------------------------------------------------------------------
 struct PreprocessParams {
@@ -31,6 +96,7 @@ struct PreprocessParams {
     uint32_t *tile_count;        // [n]
     uint32_t *depth_key;         // [n] or null: visible ? bits(depth) : 0xffffffff
     uint32_t *depth_index;       // [n] or null: g
+    EllipseRec *ellipse;         // [n] or null: exact-footprint rule (tile counts from the row spans)
 };
 void launch_preprocess(const PreprocessParams &p, hipStream_t s);
 
@@ -80,6 +146,8 @@ struct DuplicateParams {
     uint32_t *tile_keys;         // depth-first mode: tile id ...
     uint16_t *tile_keys16;       // ... or as 16 bits (at most 65536 tiles); entry count multiple of 8 per block
     uint32_t *values;            // Gaussian index
+    const EllipseRec *ellipse;   // null, or the exact-footprint rule: only the row spans are listed
+    const uint32_t *tile_count;  // [n] (needed with ellipse)
 };
 // uint32 words of the partition table launch_duplicate needs
 int64_t duplicate_partition_words(int64_t num_dups);
@@ -165,6 +233,7 @@ struct CompositeBackwardParams {
     float *pair_grad;            // [pairs][kPairStride]: Gaussian g's pair k (row-major
                                  // over its rectangle) at pair_base[g] + k
     const uint32_t *tile_order;  // optional launch order: workgroup b walks tile_order[b]
+    const EllipseRec *ellipse;   // null, or the exact-footprint rule (pair index from the row spans)
     unsigned long long *cut;     // [tiles] out: (depth bits << 32 | index) of the deepest entry
                                  // walked, 0 if none; records exist exactly for entries <= it
 };
@@ -182,6 +251,7 @@ struct GaussianBackwardParams {
     const uint2 *rect;           // tile rectangles (x0 | x1 << 16, y0 | y1 << 16)
     const float *depth;          // [n] camera-space z
     const unsigned long long *cut;   // [tiles] from the reverse walk
+    const EllipseRec *ellipse;   // null, or the exact-footprint rule
     int32_t tiles_x;
     const float *pair_grad;
     float *g_mean, *g_quat, *g_log_scale, *g_opacity, *g_sh;

@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
 
     float tx, ty, tz, u, v, A, B, C, radius;
     uint32_t x0 = 0, x1 = 0, y0 = 0, y1 = 0;
+    uint32_t kept = 0;   // tile count under the exact-footprint rule
     bool visible;
     {
 #pragma clang fp contract(off)
@@ -144,6 +145,19 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
             visible = (x1 > x0) && (y1 > y0);
         }
         if (!visible) x0 = x1 = y0 = y1 = 0;
+        if (p.ellipse) {
+            const EllipseRec E = make_ellipse(a, b, c, det, u, v);
+            p.ellipse[g] = E;
+            if (visible) {   // exact footprint: the sum of the row spans
+                uint32_t count = 0, sa, sb;
+                for (uint32_t row = y0; row < y1; ++row) {
+                    row_span(E, x0, x1, row, sa, sb);
+                    count += sb - sa;
+                }
+                kept = count;
+                visible = count > 0;
+            }
+        }
     }
 
     // view-dependent colour: SH expansion in the direction camera centre -> mean
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     rec[3] = make_float4(C, tz, 0.0f, 0.0f);
     p.depth[g] = tz;
     p.rect[g] = make_uint2(x0 | (x1 << 16), y0 | (y1 << 16));
-    p.tile_count[g] = visible ? (x1 - x0) * (y1 - y0) : 0u;
+    p.tile_count[g] = !visible ? 0u : (p.ellipse ? kept : (x1 - x0) * (y1 - y0));
     if (p.depth_key) {
         p.depth_key[g] = visible ? __float_as_uint(tz) : 0xffffffffu;
         p.depth_index[g] = (uint32_t)g;

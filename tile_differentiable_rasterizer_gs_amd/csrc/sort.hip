@@ -321,10 +321,45 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     uint32_t g, off, dbits;
     uint2 rc;
     load_rank(i, g, off, rc, dbits);
+    uint32_t tiles[kDupItems], gs[kDupItems], dbs[kDupItems];
+    if (p.ellipse) {
+        // exact footprint: the kept tiles of each row form one span; walk the spans
+        EllipseRec E = p.ellipse[g];
+        uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y1 = rc.y >> 16;
+        uint32_t ty = rc.y & 0xffffu, sa, sb;
+        uint32_t j = (uint32_t)e0 - off;
+        row_span(E, x0, x1, ty, sa, sb);
+        while (j >= sb - sa) {
+            j -= sb - sa;
+            row_span(E, x0, x1, ++ty, sa, sb);
+        }
+        uint32_t tx = sa + j;
+        for (int k = 0; k < n_here; ++k) {
+            tiles[k] = ty * (uint32_t)p.tiles_x + tx;
+            gs[k] = g;
+            dbs[k] = dbits;
+            if (++tx == sb && k + 1 < n_here) {
+                do {   // next row with a span, else the next rank with pairs
+                    if (++ty == y1) {
+                        do {
+                            ++i;
+                            load_rank(i, g, off, rc, dbits);
+                        } while (p.tile_count[g] == 0);
+                        E = p.ellipse[g];
+                        x0 = rc.x & 0xffffu;
+                        x1 = rc.x >> 16;
+                        y1 = rc.y >> 16;
+                        ty = rc.y & 0xffffu;
+                    }
+                    row_span(E, x0, x1, ty, sa, sb);
+                } while (sa == sb);
+                tx = sa;
+            }
+        }
+    } else {
     uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu, h = (rc.y >> 16) - y0;
     uint32_t j = (uint32_t)e0 - off;
     uint32_t row = j / w, col = j - row * w;
-    uint32_t tiles[kDupItems], gs[kDupItems], dbs[kDupItems];
 #pragma unroll
     for (int k = 0; k < kDupItems; ++k) {
         if (k < n_here) {
@@ -347,6 +382,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
                 }
             }
         }
+    }
     }
     if (n_here == kDupItems) {
         uint4 *vo = reinterpret_cast<uint4 *>(p.values + e0);
