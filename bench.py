@@ -10,7 +10,8 @@ HBM.  Prints one JSON line.
 A workload with several cameras (the 32-view orbit) renders its views round-robin.
 The JSON line also carries the backward pass (gs_backward for a fixed random
 image cotangent) timed on its own and as part of a forward + backward step, and
-the lesson's 2D splat-fitting workload (64 splats, 64x64, 200 Adam steps).
+the lesson's 2D splat-fitting workload (64 splats, 64x64, 200 Adam steps), and the
+same frames under the exact-footprint tile rule (GS_TILE_ELLIPSE).
 """
 from __future__ import annotations
 
@@ -170,6 +171,45 @@ def time_backward(r, dev, scene, cams, img, bg, steps, blends):
                 cotangent="standard normal per pixel channel, seed 0")
 
 
+def time_ellipse_rule(dev, scene, cams, bg, steps, sort_mode):
+    """The same frames under the exact-footprint tile rule (GS_TILE_ELLIPSE): fewer pairs, an
+    image that drops contributions below o exp(-9/2) per pixel.  Forward frame time, stage
+    split, pairs, and the backward."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    r = binding.Rasterizer(sort_mode=sort_mode, emit_keys=False, tile_test=binding.GS_TILE_ELLIPSE)
+    H, W = cams[0]["height"], cams[0]["width"]
+    img = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
+    pr = r.preprocess(dev, scene.sh_degree, cams[0])
+    bn = r.bin_and_sort(pr, cams[0])
+    pairs = int(bn.num_dups)
+    for i in range(10):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    r.set_option(binding.GS_OPT_PROFILE, 1)
+    r.profile_read()
+    for i in range(steps):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+    prof = r.profile_read()
+    r.set_option(binding.GS_OPT_PROFILE, 0)
+    stage = {k: round(v / steps, 5) for k, (v, c) in prof.items() if c}
+    bwd = time_backward(r, dev, scene, cams[:1], img, bg, max(10, steps // 4), 0)
+    r.close()
+    log(f"ellipse rule: {ms:.4f} ms/frame, {pairs} pairs; stages {stage}; backward {bwd['ms']} ms")
+    return dict(ms_per_step=round(ms, 5), frames_per_s=round(1000.0 / ms, 2), pairs_per_frame=pairs,
+                stage_ms=stage, backward_ms=bwd["ms"], train_step_ms=bwd["train_step_ms"],
+                note="GS_TILE_ELLIPSE: tiles of the square whose pixel-centre box meets the 3-sigma ellipse")
+
+
 def time_splat2d_fit():
     """The lesson's 2D splat-fitting workload (64 splats, 64x64 target, Adam 0.05, 200 steps) on the
     HIP 2D rasteriser: whole-fit wall time and the rasteriser's forward + backward kernel time."""
@@ -215,6 +255,7 @@ def main():
     ap.add_argument("--sort-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-ellipse", action="store_true", help="skip the exact-footprint tile rule timing")
     ap.add_argument("--streams", type=int, default=0,
                     help="views in flight (contexts on their own streams); default 3 for multi-view workloads, else 1")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -362,6 +403,8 @@ def main():
         "context": "pages: '100+ FPS at 1080p' for a trained scene on an unnamed GPU; 147 fps for 6M splats on an "
                    "RTX 3080 Ti (resolution not stated)",
     }
+    if not args.no_ellipse:
+        out["tile_test_ellipse"] = time_ellipse_rule(dev, scene, cams, bg, args.steps, args.sort_mode)
     if not args.no_backward:
         out["backward"] = time_backward(r, dev, scene, cams, img, bg, args.steps, blends)
         log("2D splat fit ...")
