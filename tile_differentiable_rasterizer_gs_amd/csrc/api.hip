@@ -71,7 +71,8 @@ struct gs_context {
     int32_t s2_height = 0, s2_width = 0;
     const float *s2_means = nullptr, *s2_depths = nullptr;
 
-    unsigned long long *host_total = nullptr;   // pinned: pair count read back once per frame
+    unsigned long long *host_total = nullptr;   // pinned, host-coherent: the pair count of each frame
+    unsigned long long *host_total_dev = nullptr;   // its device address (the scan stores the count there)
 
     // last gs_preprocess
     int64_t n = -1;
@@ -274,7 +275,9 @@ gs_status gs_context_create(gs_context **out, int device) {
     ctx->device = device;
     DeviceScope scope(device);
     if (scope.status != hipSuccess ||
-        hipHostMalloc((void **)&ctx->host_total, sizeof(unsigned long long), hipHostMallocDefault) != hipSuccess) {
+        hipHostMalloc((void **)&ctx->host_total, sizeof(unsigned long long),
+                      hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess ||
+        hipHostGetDevicePointer((void **)&ctx->host_total_dev, ctx->host_total, 0) != hipSuccess) {
         (void)hipGetLastError();
         delete ctx;
         return GS_ERR_DEVICE;
@@ -549,7 +552,10 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     GS_TRY(ensure(ctx, ctx->total, 8));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->tile_order, (size_t)tiles * sizeof(uint32_t)));
-    if (!ctx->total_ready) GS_HIP(ctx, hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming));
+    // the pair count reaches the host by the scan's own system-scope store, so this event only
+    // has to say that the scan ran: no system-scope fence (a cache writeback of ~9 us per frame)
+    if (!ctx->total_ready)
+        GS_HIP(ctx, hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming | hipEventDisableSystemFence));
     unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
     const uint32_t *order = nullptr;
@@ -571,14 +577,17 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             order = as<uint32_t>(ctx->dval[buf]);
             counts = n > 1 ? as<uint32_t>(ctx->dcount) : pr->tile_count;
         }
+        // the scan's last kernel stores the pair count straight into host-coherent memory (no copy
+        // on the stream); a sentinel shows a count that never arrived
+        constexpr unsigned long long kNoCount = ~0ull;
+        *ctx->host_total = kNoCount;
         GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
         launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
-                    as<unsigned long long>(ctx->scan_scratch), stream);
+                    as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
         GS_TRY(check_launch(ctx, "scan"));
         GS_TRY(span_end(ctx, stream));
 
         GS_TRY(span_begin(ctx, GS_STAGE_READBACK, stream));
-        GS_HIP(ctx, hipMemcpyAsync(ctx->host_total, d_total, 8, hipMemcpyDeviceToHost, stream));
         GS_HIP(ctx, hipEventRecord(ctx->total_ready, stream));
         GS_TRY(span_end(ctx, stream));
         if (ctx->pair_capacity > 0) {
@@ -586,7 +595,15 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             speculated = true;
         }
         GS_HIP(ctx, hipEventSynchronize(ctx->total_ready));
-        M = (int64_t)*ctx->host_total;
+        unsigned long long published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
+        for (int spin = 0; published == kNoCount && spin < (1 << 20); ++spin)
+            published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
+        if (published == kNoCount) {   // not seen yet: wait for the whole stream, then it must be there
+            GS_HIP(ctx, hipStreamSynchronize(stream));
+            published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
+            if (published == kNoCount) return fail(ctx, GS_ERR_DEVICE, "the pair count did not reach the host");
+        }
+        M = (int64_t)published;
         if (M > ctx->max_dups)
             return fail(ctx, GS_ERR_CAPACITY, "%lld (Gaussian, tile) pairs exceed the cap of %lld", (long long)M,
                         (long long)ctx->max_dups);

@@ -108,8 +108,10 @@ constexpr int kScanTile = kBlock * kScanItems;   // 4096 values per workgroup
 // number of uint64 scratch words launch_scan needs for n values
 int64_t scan_scratch_words(int64_t n);
 // out[i] = sum_{j<i} in[j]; *total = sum of all (device uint64).  n >= 1.
+// host_total (optional): device address of host-coherent memory that also receives the sum.
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
-                 unsigned long long *total, unsigned long long *scratch, hipStream_t s);
+                 unsigned long long *total, unsigned long long *scratch, hipStream_t s,
+                 unsigned long long *host_total = nullptr);
 
 // ---------------------------------------------------------------------------
 // stable LSD radix sort of (key, uint32 value) pairs

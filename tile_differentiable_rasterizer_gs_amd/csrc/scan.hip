@@ -72,11 +72,13 @@ __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const TIn *in, cons
 }
 
 // out[i] = prefix[block] + exclusive scan within the block.  When `total` is
-// non-null (single-block case) the block total is written there.
+// non-null (single-block case) the block total is written there, and also to
+// `host_total` (host-coherent memory, a system-scope store) when that is non-null.
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, const uint32_t *gather,
                                                                 int64_t n, const unsigned long long *prefix,
-                                                                TOut *out, unsigned long long *total) {
+                                                                TOut *out, unsigned long long *total,
+                                                                unsigned long long *host_total) {
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
     unsigned long long v[kScanItems];
     load_items(in, gather, n, base, v);
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
         if (i < n) out[i] = (TOut)run;
         run += v[k];
     }
-    if (total && threadIdx.x == 0) *total = block_total;
+    if (total && threadIdx.x == 0) {
+        *total = block_total;
+        if (host_total) __hip_atomic_store(host_total, block_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 }
 
 inline int64_t blocks_for(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
@@ -100,17 +105,19 @@ inline int64_t blocks_for(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
 // Scans `in` (n values) into `out`; partials for the next level live in scratch.
 template <typename TIn, typename TOut>
 void scan_level(const TIn *in, const uint32_t *gather, TOut *out, int64_t n, unsigned long long *total,
-                unsigned long long *scratch, hipStream_t s) {
+                unsigned long long *host_total, unsigned long long *scratch, hipStream_t s) {
     const int64_t nb = blocks_for(n);
     if (nb == 1) {
-        scan_downsweep_kernel<TIn, TOut><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, out, total);
+        scan_downsweep_kernel<TIn, TOut><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, out, total, host_total);
         return;
     }
     unsigned long long *partials = scratch;
     scan_reduce_kernel<TIn><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials);
     // exclusive scan of the partials, in place (reads before writes within each block)
-    scan_level<unsigned long long, unsigned long long>(partials, nullptr, partials, nb, total, scratch + nb, s);
-    scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, out, nullptr);
+    scan_level<unsigned long long, unsigned long long>(partials, nullptr, partials, nb, total, host_total,
+                                                       scratch + nb, s);
+    scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, out, nullptr,
+                                                                     nullptr);
 }
 
 }  // namespace
@@ -122,8 +129,9 @@ int64_t scan_scratch_words(int64_t n) {
 }
 
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
-                 unsigned long long *total, unsigned long long *scratch, hipStream_t s) {
-    scan_level<uint32_t, uint32_t>(in, gather, out, n, total, scratch, s);
+                 unsigned long long *total, unsigned long long *scratch, hipStream_t s,
+                 unsigned long long *host_total) {
+    scan_level<uint32_t, uint32_t>(in, gather, out, n, total, host_total, scratch, s);
 }
 
 }  // namespace gsr
