@@ -334,6 +334,17 @@ gs_status gs_splat2d_backward(gs_context *ctx, int64_t n, const float *means, co
                               int32_t width, const float bg_rgb[3], const float *grad_image, float *grad_means,
                               float *grad_covs, float *grad_colours, float *grad_opacities, hipStream_t stream);
 
+/*
+ * The scale activation of gs_preprocess (lesson, sections "Ce qu'un Gaussien
+ * porte" and "Étape 5": S = diag(exp(log_scale))), elementwise:
+ * scale[i] = binary32 rounding of the binary64 exp of log_scale[i].  Device
+ * arrays of n >= 0 floats (may not overlap).  Tile counts and keys depend on
+ * these bits, so the call exists to check the device's exp against a host's
+ * for every input of a range.  Asynchronous.
+ */
+gs_status gs_scale_activation(gs_context *ctx, const float *log_scale, float *scale, int64_t n,
+                              hipStream_t stream);
+
 /* Reads (and resets) the accumulated per-stage times; waits for the timed work. */
 gs_status gs_profile_read(gs_context *ctx, gs_profile *out);
 

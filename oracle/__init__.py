@@ -91,6 +91,7 @@ def _load():
                                          P, i64, P, P, P]
         lib.oracle_composite.restype = None
         lib.oracle_cov3d.argtypes = [P, P, P]
+        lib.oracle_scale_activation.argtypes = [i64, P, P]
         lib.oracle_cov3d.restype = None
         lib.oracle_sh_basis.argtypes = [ctypes.c_double] * 3 + [P]
         lib.oracle_sh_basis.restype = None
@@ -215,6 +216,15 @@ def cov3d(quat4, log_scale3) -> np.ndarray:
     q, s = _f32(quat4).reshape(4), _f32(log_scale3).reshape(3)
     out = np.zeros(6, np.float32)
     lib.oracle_cov3d(_ptr(q), _ptr(s), _ptr(out))
+    return out
+
+
+def scale_activation(log_scale) -> np.ndarray:
+    """(float)exp((double)log_scale) elementwise, the host's libm exp (binary32 array in, out)."""
+    lib = _load()
+    ls = np.ascontiguousarray(log_scale, dtype=np.float32).ravel()
+    out = np.empty_like(ls)
+    lib.oracle_scale_activation(ls.size, _ptr(ls), _ptr(out))
     return out
 
 

@@ -102,6 +102,18 @@ static void sh_basis(double x, double y, double z, double Y[16]) {
 void oracle_sh_basis(double x, double y, double z, double *out16) { sh_basis(x, y, z, out16); }
 
 /*
+ * Scale activation (lesson, "Ce qu'un Gaussien porte": log-scales exponentiated
+ * at render time): the binary64 exp of the binary32 log-scale, rounded to
+ * binary32.  oracle_scale_activation applies it to an array (OpenMP).
+ */
+static float scale_activation(float log_scale) { return (float)exp((double)log_scale); }
+
+void oracle_scale_activation(int64_t n, const float *log_scale, float *scale) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) scale[i] = scale_activation(log_scale[i]);
+}
+
+/*
  * 3D covariance Sigma = R S S^T R^T with R from the normalised quaternion
  * (w, x, y, z) and S = diag(exp(log_scale)).  Lesson, sections "Ce qu'un
  * Gaussien porte" and "Étape 5: De la 2D à la 3D".  binary32, no contraction.
@@ -122,7 +134,7 @@ void oracle_cov3d(const float q_in[4], const float ls[3], float out6[6]) {
     r[2][1] = 2.0f * (y * z + w * x);
     r[2][2] = 1.0f - 2.0f * (x * x + y * y);
     float s[3];
-    for (int i = 0; i < 3; ++i) s[i] = (float)exp((double)ls[i]);
+    for (int i = 0; i < 3; ++i) s[i] = scale_activation(ls[i]);
     float m[3][3];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j) m[i][j] = r[i][j] * s[j];

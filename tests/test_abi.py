@@ -140,6 +140,10 @@ def test_null_context_is_invalid_argument(lib):
                            None, None, None, ctypes.byref(gr), None) == 1
     assert lib.gs_context_set_option(None, 0, 0) == 1
     assert lib.gs_profile_read(None, ctypes.byref(prof)) == 1
+    assert lib.gs_splat2d_forward(None, 0, None, None, None, None, None, 4, 4, bg, None, None) == 1
+    assert lib.gs_splat2d_backward(None, 0, None, None, None, None, None, 4, 4, bg, None, None, None, None,
+                                   None, None) == 1
+    assert lib.gs_scale_activation(None, None, None, 0, None) == 1
     assert lib.gs_context_create(None, 0) == 1
     lib.gs_context_destroy(None)
     assert lib.gs_last_error(None) == b""

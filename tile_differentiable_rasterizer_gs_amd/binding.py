@@ -28,8 +28,8 @@ TILE = 16
 # symbols declared in include/gsrast.h
 EXPORTED = ("gs_context_create", "gs_context_destroy", "gs_context_set_option", "gs_check_arguments",
             "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
-            "gs_backward", "gs_splat2d_forward", "gs_splat2d_backward", "gs_profile_read", "gs_status_string",
-            "gs_last_error")
+            "gs_backward", "gs_splat2d_forward", "gs_splat2d_backward", "gs_scale_activation", "gs_profile_read",
+            "gs_status_string", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -106,6 +106,7 @@ def load_library(path: str = LIB_PATH):
     FP = ctypes.POINTER(ctypes.c_float)
     lib.gs_splat2d_forward.argtypes = [P, i64, P, P, P, P, P, i32, i32, FP, P, P]
     lib.gs_splat2d_backward.argtypes = [P, i64, P, P, P, P, P, i32, i32, FP, P, P, P, P, P, P]
+    lib.gs_scale_activation.argtypes = [P, P, P, i64, P]
     lib.gs_profile_read.argtypes = [P, ctypes.POINTER(Profile)]
     lib.gs_status_string.argtypes = [ctypes.c_int]
     lib.gs_status_string.restype = ctypes.c_char_p
@@ -309,6 +310,19 @@ class Rasterizer:
                     not t.is_contiguous() or tuple(t.shape) != shape:
                 raise ValueError(f"{k} must be a contiguous CUDA float32 tensor of shape {shape}")
         return n, [ctypes.c_void_p(ts[k].data_ptr()) if n else None for k in want]
+
+    def scale_activation(self, log_scale, out=None, stream=None) -> torch.Tensor:
+        """gs_scale_activation: (float)exp((double)x) elementwise on a contiguous fp32 device tensor."""
+        if log_scale.dtype != torch.float32 or not log_scale.is_cuda or not log_scale.is_contiguous():
+            raise ValueError("log_scale must be a contiguous float32 device tensor")
+        if out is None:
+            out = torch.empty_like(log_scale)
+        if out.shape != log_scale.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor shaped like log_scale")
+        self._check(self.lib.gs_scale_activation(self.ctx, ctypes.c_void_p(log_scale.data_ptr()),
+                                                 ctypes.c_void_p(out.data_ptr()), log_scale.numel(),
+                                                 _stream_handle(stream)))
+        return out
 
     def splat2d_forward(self, means, covs, colours, opacities, depths, height: int, width: int, bg=None,
                         out=None, stream=None) -> torch.Tensor:

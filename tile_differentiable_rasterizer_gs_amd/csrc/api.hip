@@ -830,6 +830,18 @@ static gs_status splat2d_check(gs_context *ctx, int64_t n, const float *means, c
     return GS_OK;
 }
 
+gs_status gs_scale_activation(gs_context *ctx, const float *log_scale, float *scale, int64_t n,
+                              hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (n < 0) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "negative n");
+    if (n > 0 && (!log_scale || !scale)) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL array");
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    launch_scale_activation(log_scale, scale, n, stream);
+    GS_TRY(check_launch(ctx, "scale activation"));
+    return GS_OK;
+}
+
 gs_status gs_splat2d_forward(gs_context *ctx, int64_t n, const float *means, const float *covs,
                              const float *colours, const float *opacities, const float *depths, int32_t height,
                              int32_t width, const float bg[3], float *image, hipStream_t stream) {

@@ -81,6 +81,11 @@ __device__ __forceinline__ uint32_t kept_index(const EllipseRec &E, uint32_t x0,
 // ---------------------------------------------------------------------------
 // preprocess
 // ---------------------------------------------------------------------------
+// Scale activation: the binary64 exp of the log-scale, rounded to binary32 (the same
+// value on any implementation whose binary64 exp rounds to the same binary32).
+__device__ __forceinline__ float scale_activation(float log_scale) { return (float)exp((double)log_scale); }
+void launch_scale_activation(const float *log_scale, float *scale, int64_t n, hipStream_t s);
+
 struct PreprocessParams {
     int32_t n;
     int32_t sh_coeffs;           // K = (degree+1)^2

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
         r[2][0] = 2.0f * (x * z - w * y);
         r[2][1] = 2.0f * (y * z + w * x);
         r[2][2] = 1.0f - 2.0f * (x * x + y * y);
-        const float s[3] = {(float)exp((double)l0), (float)exp((double)l1), (float)exp((double)l2)};
+        const float s[3] = {scale_activation(l0), scale_activation(l1), scale_activation(l2)};
         // M = R diag(s); Sigma = M M^T
         float m[3][3];
 #pragma unroll
@@ -190,7 +190,19 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     }
 }
 
+__global__ __launch_bounds__(kBlock) void scale_activation_kernel(const float *__restrict__ in,
+                                                                   float *__restrict__ out, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) out[i] = scale_activation(in[i]);
+}
+
 }  // namespace
+
+void launch_scale_activation(const float *log_scale, float *scale, int64_t n, hipStream_t s) {
+    if (n <= 0) return;
+    const int64_t blocks = (n + kBlock - 1) / kBlock;
+    scale_activation_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), kBlock, 0, s>>>(log_scale, scale, n);
+}
 
 void launch_preprocess(const PreprocessParams &p, hipStream_t s) {
     if (p.n <= 0) return;
