@@ -171,6 +171,42 @@ def time_backward(r, dev, scene, cams, img, bg, steps, blends):
                 cotangent="standard normal per pixel channel, seed 0")
 
 
+def copy_bandwidth(reps: int = 20) -> float:
+    """Device-to-device copy of 1 GiB (read 1 GiB + write 1 GiB), best of `reps`: GB/s moved."""
+    import torch
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(reps):
+        start.record()
+        dst.copy_(src)
+        stop.record()
+        stop.synchronize()
+        best = min(best, start.elapsed_time(stop))
+    nbytes = 2 * src.numel() * 4
+    del src, dst
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def frame_distribution(r, dev, scene, cams, bg, img, steps):
+    """Per-frame times from a HIP event pair around each frame: median, p10, p90 (ms)."""
+    import numpy as np
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(median=round(float(np.median(t)), 5), p10=round(float(np.percentile(t, 10)), 5),
+                p90=round(float(np.percentile(t, 90)), 5))
+
+
 def time_ellipse_rule(dev, scene, cams, bg, steps, sort_mode):
     """The same frames under the exact-footprint tile rule (GS_TILE_ELLIPSE): fewer pairs, an
     image that drops contributions below o exp(-9/2) per pixel.  Forward frame time, stage
@@ -361,13 +397,19 @@ def main():
     stage_ms = {k: (ms / args.steps) for k, (ms, cnt) in prof.items() if cnt}
     log("stages (ms/frame): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
 
+    # per-frame distribution (one event pair per frame) and the device's copy bandwidth
+    dist = frame_distribution(r, dev, scene, cams, bg, img, args.steps)
+    copy_gbs = copy_bandwidth()
+    log(f"frame ms median {dist['median']} p10 {dist['p10']} p90 {dist['p90']}; 1 GiB copy {copy_gbs:.0f} GB/s")
+
     nbytes = stage_bytes(scene.n, scene.sh_degree, pairs, n_visible)
     rooflines = {}
     for st, b in nbytes.items():
         if st in stage_ms and stage_ms[st] > 0:
             gbs = b / (stage_ms[st] * 1e-3) / 1e9
             rooflines[st] = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                                 frac=round(gbs / HBM_PEAK_GBS, 4), bytes=b)
+                                 frac=round(gbs / HBM_PEAK_GBS, 4), frac_of_copy=round(gbs / copy_gbs, 4),
+                                 bytes=b)
     comp_ms = stage_ms.get("composite", 0.0)
     comp_gops = blends * COMPOSITE_OPS_PER_PAIR / (comp_ms * 1e-3) / 1e9 if comp_ms else 0.0
     rooflines["composite"] = dict(bound="alu", achieved=round(comp_gops / 1e3, 3), peak=round(VALU_PEAK_GOPS / 1e3, 3),
@@ -400,6 +442,8 @@ def main():
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stage_rooflines": rooflines,
         "profiled_ms_per_step": round(prof_ms_per_step, 5),
+        "frame_ms_distribution": dist,
+        "copy_gbs": round(copy_gbs, 1),
         "context": "pages: '100+ FPS at 1080p' for a trained scene on an unnamed GPU; 147 fps for 6M splats on an "
                    "RTX 3080 Ti (resolution not stated)",
     }
