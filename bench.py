@@ -77,8 +77,9 @@ def measured_traffic(workload):
     return int(float(kv["composite_traffic_bytes"]))
 
 
-def cpu_baseline(scene, cam, pixels_target=8192):
-    """The oracle on a bounded sample: full projection + binning, composite on sampled pixels."""
+def cpu_baseline(scene, cam, pixels_target=262144):
+    """The oracle on a bounded sample (about 10 s of host work at 1080p on 16 threads): full
+    projection + binning, composite on 262144 sampled pixels (12.6 % of the frame)."""
     import numpy as np
 
     import oracle
