@@ -443,14 +443,16 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
         }
     }
 
-    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
-    launch_fill_u32(as<uint32_t>(ctx->ranges), 0u, tiles * 2, stream);
-    GS_TRY(check_launch(ctx, "fill"));
-    GS_TRY(span_end(ctx, stream));
     ctx->sorted_values = nullptr;
     ctx->sorted_keys = nullptr;
     ctx->launch_order = nullptr;
-    if (ctx->n <= 0) return GS_OK;
+    if (ctx->n <= 0) {   // no pairs: every tile range is empty (otherwise the partition kernel clears them)
+        GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+        launch_fill_u32(as<uint32_t>(ctx->ranges), 0u, tiles * 2, stream);
+        GS_TRY(check_launch(ctx, "fill"));
+        GS_TRY(span_end(ctx, stream));
+        return GS_OK;
+    }
 
     DuplicateParams d{};
     d.n_items = ctx->n;
@@ -462,6 +464,8 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     d.depth = pr->depth;
     d.tiles_x = ctx->tiles_x;
     d.values = as<uint32_t>(ctx->pval[0]);
+    d.clear = as<uint32_t>(ctx->ranges);
+    d.clear_words = tiles * 2;
     if (ctx->tile_test_used == GS_TILE_ELLIPSE) {
         d.ellipse = as<EllipseRec>(ctx->ellipse);
         d.tile_count = pr->tile_count;

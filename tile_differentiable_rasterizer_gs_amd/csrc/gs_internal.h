@@ -155,6 +155,8 @@ struct DuplicateParams {
     uint32_t *values;            // Gaussian index
     const EllipseRec *ellipse;   // null, or the exact-footprint rule: only the row spans are listed
     const uint32_t *tile_count;  // [n] (needed with ellipse)
+    uint32_t *clear;             // zeroed by the partition kernel ([clear_words]; the tile ranges)
+    int64_t clear_words;
 };
 // uint32 words of the partition table launch_duplicate needs
 int64_t duplicate_partition_words(int64_t num_dups);

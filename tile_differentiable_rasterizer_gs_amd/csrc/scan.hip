@@ -71,14 +71,25 @@ __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const TIn *in, cons
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
 }
 
-// out[i] = prefix[block] + exclusive scan within the block.  When `total` is
-// non-null (single-block case) the block total is written there, and also to
+// out[i] = the block's offset + exclusive scan within the block.  The offset is
+// prefix[block] (scanned block totals), or, with block_sums, the sum of the block
+// totals before this block, added up here (few blocks: it saves a kernel).  When
+// `total` is non-null the last block writes the grand total there, and also to
 // `host_total` (host-coherent memory, a system-scope store) when that is non-null.
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, const uint32_t *gather,
                                                                 int64_t n, const unsigned long long *prefix,
-                                                                TOut *out, unsigned long long *total,
+                                                                const unsigned long long *block_sums, TOut *out,
+                                                                unsigned long long *total,
                                                                 unsigned long long *host_total) {
+    unsigned long long offset = 0;
+    if (prefix) {
+        offset = prefix[blockIdx.x];
+    } else if (block_sums) {
+        unsigned long long before = 0;
+        for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kBlock) before += block_sums[j];
+        block_exclusive_scan(before, &offset);
+    }
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
     unsigned long long v[kScanItems];
     load_items(in, gather, n, base, v);
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) s += v[k];
     unsigned long long block_total;
-    unsigned long long run = block_exclusive_scan(s, &block_total) + (prefix ? prefix[blockIdx.x] : 0ull);
+    unsigned long long run = block_exclusive_scan(s, &block_total) + offset;
     const int64_t first = base + (int64_t)threadIdx.x * kScanItems;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
@@ -94,13 +105,17 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
         if (i < n) out[i] = (TOut)run;
         run += v[k];
     }
-    if (total && threadIdx.x == 0) {
-        *total = block_total;
-        if (host_total) __hip_atomic_store(host_total, block_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (total && threadIdx.x == 0 && blockIdx.x == gridDim.x - 1) {
+        const unsigned long long all = offset + block_total;
+        *total = all;
+        if (host_total) __hip_atomic_store(host_total, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
 inline int64_t blocks_for(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
+
+// Up to this many blocks (4 M values) the downsweep sums the partials itself.
+constexpr int64_t kDirectBlocks = 1024;
 
 // Scans `in` (n values) into `out`; partials for the next level live in scratch.
 template <typename TIn, typename TOut>
@@ -108,16 +123,22 @@ void scan_level(const TIn *in, const uint32_t *gather, TOut *out, int64_t n, uns
                 unsigned long long *host_total, unsigned long long *scratch, hipStream_t s) {
     const int64_t nb = blocks_for(n);
     if (nb == 1) {
-        scan_downsweep_kernel<TIn, TOut><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, out, total, host_total);
+        scan_downsweep_kernel<TIn, TOut><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, nullptr, out, total,
+                                                              host_total);
         return;
     }
     unsigned long long *partials = scratch;
     scan_reduce_kernel<TIn><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials);
+    if (nb <= kDirectBlocks) {   // each block adds up the partials before it
+        scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, nullptr, partials, out,
+                                                                         total, host_total);
+        return;
+    }
     // exclusive scan of the partials, in place (reads before writes within each block)
     scan_level<unsigned long long, unsigned long long>(partials, nullptr, partials, nb, total, host_total,
                                                        scratch + nb, s);
-    scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, out, nullptr,
-                                                                     nullptr);
+    scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, nullptr, out,
+                                                                     nullptr, nullptr);
 }
 
 }  // namespace

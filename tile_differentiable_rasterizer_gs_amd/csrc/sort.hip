@@ -242,10 +242,12 @@ constexpr int kDupTile = kBlock * kDupItems;   // 2048 entries per workgroup
 constexpr int kDupWindow = kDupTile + 1;
 
 // part[b] = rank whose pairs contain entry b * kDupTile; part[blocks] = rank of the last entry.
+// Also zeroes clear[0, clear_words) (the tile ranges, so that tiles without pairs read as empty).
 __global__ __launch_bounds__(kBlock) void partition_kernel(const uint32_t *offsets, int64_t n_items,
                                                            const unsigned long long *num_dev, int64_t cap,
-                                                           uint32_t *part) {
+                                                           uint32_t *part, uint32_t *clear, int64_t clear_words) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    for (int64_t w = i; w < clear_words; w += (int64_t)gridDim.x * kBlock) clear[w] = 0u;
     if (i >= n_items) return;
     const int64_t num = live_count(cap, num_dev);
     const int64_t start = offsets[i];
@@ -521,8 +523,8 @@ int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTil
 
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
     if (p.capacity <= 0 || p.n_items <= 0) return;
-    partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(p.offsets, p.n_items,
-                                                                                       p.num_dups, p.capacity, part);
+    partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(
+        p.offsets, p.n_items, p.num_dups, p.capacity, part, p.clear, p.clear_words);
     const int64_t nb = (p.capacity + kDupTile - 1) / kDupTile;
     duplicate_kernel<<<(unsigned)nb, kBlock, 0, s>>>(p, part);
 }
