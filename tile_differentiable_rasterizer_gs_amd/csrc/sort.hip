@@ -265,13 +265,16 @@ __device__ inline int64_t last_le_global(const uint32_t *offsets, int64_t lo, in
 }
 
 // Workgroup b lists entries [b*2048, (b+1)*2048).  The ranks whose pairs meet that
-// span are staged in LDS; each thread then takes 8 consecutive entries: one
-// binary search for the first, then it walks the rectangles row-major.
+// span are staged in LDS, and each rank marks the threads whose first entry it holds;
+// each thread then takes 8 consecutive entries and walks the rectangles row-major.
+// kDepth: the 64-bit keys carry the depth bits (staged only then).
+template <bool kDepth>
 __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, const uint32_t *part) {
     __shared__ uint32_t s_off[kDupWindow];
     __shared__ uint32_t s_g[kDupWindow];
     __shared__ uint2 s_rect[kDupWindow];
-    __shared__ uint32_t s_depth[kDupWindow];
+    __shared__ uint32_t s_depth[kDepth ? kDupWindow : 1];
+    __shared__ uint16_t s_rank[kBlock];   // rank (in the window) holding each thread's first entry
     const int64_t num_dups = live_count(p.capacity, p.num_dups);
     const int64_t first = (int64_t)blockIdx.x * kDupTile;
     if (first >= num_dups) return;
@@ -286,7 +289,16 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             s_off[k] = p.offsets[i];
             s_g[k] = g;
             s_rect[k] = p.rect[g];
-            if (p.keys64) s_depth[k] = __float_as_uint(p.depth[g]);
+            if (kDepth) s_depth[k] = __float_as_uint(p.depth[g]);
+        }
+        __syncthreads();
+        // rank k holds entries [s_off[k], s_off[k+1]); thread t starts at first + 8t
+        for (int64_t k = threadIdx.x; k < window; k += kBlock) {
+            const int64_t a = (int64_t)s_off[k] - first;
+            const int64_t b = k + 1 < window ? (int64_t)s_off[k + 1] - first : (int64_t)kDupTile;
+            const int64_t t0 = a <= 0 ? 0 : (a + kDupItems - 1) / kDupItems;
+            const int64_t t1 = min<int64_t>(kBlock, b <= 0 ? 0 : (b + kDupItems - 1) / kDupItems);
+            for (int64_t t = t0; t < t1; ++t) s_rank[t] = (uint16_t)k;
         }
     }
     __syncthreads();
@@ -297,12 +309,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     // rank holding e0
     int64_t i;
     if (staged) {
-        int a = 0, b = (int)window - 1;
-        while (a < b) {
-            const int mid = (a + b + 1) >> 1;
-            if (s_off[mid] <= (uint32_t)e0) a = mid; else b = mid - 1;
-        }
-        i = a;
+        i = s_rank[threadIdx.x];
     } else {
         i = last_le_global(p.offsets, lo, hi, (uint32_t)e0) - lo;
     }
@@ -311,13 +318,13 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             g = s_g[k];
             off = s_off[k];
             rc = s_rect[k];
-            db = p.keys64 ? s_depth[k] : 0u;
+            db = kDepth ? s_depth[k] : 0u;
         } else {
             const int64_t r = lo + k;
             g = p.order ? p.order[r] : (uint32_t)r;
             off = p.offsets[r];
             rc = p.rect[g];
-            db = p.keys64 ? __float_as_uint(p.depth[g]) : 0u;
+            db = kDepth ? __float_as_uint(p.depth[g]) : 0u;
         }
     };
     uint32_t g, off, dbits;
@@ -526,7 +533,10 @@ void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
     partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(
         p.offsets, p.n_items, p.num_dups, p.capacity, part, p.clear, p.clear_words);
     const int64_t nb = (p.capacity + kDupTile - 1) / kDupTile;
-    duplicate_kernel<<<(unsigned)nb, kBlock, 0, s>>>(p, part);
+    if (p.keys64)
+        duplicate_kernel<true><<<(unsigned)nb, kBlock, 0, s>>>(p, part);
+    else
+        duplicate_kernel<false><<<(unsigned)nb, kBlock, 0, s>>>(p, part);
 }
 
 void launch_ranges(const RangesParams &p, hipStream_t s) {
