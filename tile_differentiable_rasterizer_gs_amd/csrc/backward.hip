@@ -470,10 +470,24 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int row = lane / kRowLanes, li = lane & (kRowLanes - 1);
     const int64_t g0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kGaussPerWave;
+    // the 64 Gaussians' counts, record bases, rectangles and depth bits, one per lane (loaded
+    // once, coalesced); each round's rows fetch theirs by shuffle
+    const int64_t gm = g0 + lane;
+    const uint32_t m_count = gm < p.n ? p.tile_count[gm] : 0u;
+    uint32_t m_base = 0, m_rx = 0, m_ry = 0, m_depth = 0;
+    if (m_count && !p.ellipse) {
+        m_base = p.pair_base[gm];
+        const uint2 rc = p.rect[gm];
+        m_rx = rc.x;
+        m_ry = rc.y;
+        m_depth = __float_as_uint(p.depth[gm]);
+    }
     for (int round = 0; round < kGaussPerWave / 4; ++round) {
         const int gl = 4 * round + row;
         const int64_t g = g0 + gl;
-        const uint32_t count = g < p.n ? p.tile_count[g] : 0u;
+        const uint32_t count = (uint32_t)__shfl((int)m_count, gl);
+        const uint32_t base = (uint32_t)__shfl((int)m_base, gl), rx = (uint32_t)__shfl((int)m_rx, gl);
+        const uint32_t ry = (uint32_t)__shfl((int)m_ry, gl), dbits = (uint32_t)__shfl((int)m_depth, gl);
         float acc[kPairGrad];
 #pragma unroll
         for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
@@ -500,10 +514,9 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
                 k0 += sb - sa;
             }
         } else if (count) {
-            const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
-            const uint2 rc = p.rect[g];
-            const uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu;
-            const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
+            const float *rec = p.pair_grad + (size_t)base * kPairStride;
+            const uint32_t x0 = rx & 0xffffu, w = (rx >> 16) - x0, y0 = ry & 0xffffu;
+            const unsigned long long key = ((unsigned long long)dbits << 32) | (uint64_t)g;
             for (uint32_t i = li; i < count; i += kRowLanes) {
                 const uint32_t row = i / w;
                 const uint32_t tile = (y0 + row) * (uint32_t)p.tiles_x + x0 + (i - row * w);
