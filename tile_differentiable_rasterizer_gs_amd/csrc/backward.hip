@@ -78,7 +78,9 @@ struct BwdLane {
             const float Ti = T[i] * rinv;
             const float cb0 = c[0] - B[i][0], cb1 = c[1] - B[i][1], cb2 = c[2] - B[i][2];
             const float dot = cb0 * gC[i][0] + cb1 * gC[i][1] + cb2 * gC[i][2];
-            const float d_alpha = active ? __builtin_fmaf(Ti, dot, -bg_term[i] * rinv) : 0.0f;
+            // (an inactive pixel has alpha = 0, so 1/(1 - alpha) = 1 exactly and Ti = T; its
+            // dL/dalpha is finite and reaches the sums only through `smooth`, which is false)
+            const float d_alpha = __builtin_fmaf(Ti, dot, -bg_term[i] * rinv);
             const float w = alpha * Ti;
             Sc[0] = __builtin_fmaf(w, gC[i][0], Sc[0]);
             Sc[1] = __builtin_fmaf(w, gC[i][1], Sc[1]);
@@ -86,8 +88,8 @@ struct BwdLane {
             B[i][0] = __builtin_fmaf(alpha, cb0, B[i][0]);
             B[i][1] = __builtin_fmaf(alpha, cb1, B[i][1]);
             B[i][2] = __builtin_fmaf(alpha, cb2, B[i][2]);
-            T[i] = active ? Ti : T[i];
-            const bool smooth = raw < cl.z;
+            T[i] = Ti;
+            const bool smooth = active && raw < cl.z;
             So = __builtin_fmaf(smooth ? raw * f2.z : 0.0f, d_alpha, So);
             const float d = (smooth ? alpha : 0.0f) * d_alpha;
             S0 += d;

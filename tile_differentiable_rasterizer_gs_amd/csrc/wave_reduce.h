@@ -24,6 +24,12 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp_moved(float v) {
+    // a lane permutation inside each 16-lane row (every source lane valid)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
+}
+
 // One butterfly level that reduces two values at once: lanes with `mask` clear keep
 // a + partner's a, the others b + partner's b.
 __device__ __forceinline__ float fold(float a, float b, int mask, bool upper) {
@@ -43,11 +49,14 @@ __device__ __forceinline__ void reduce9(const float v[9], int lane, float &packe
     e += __shfl_xor(e, 16);
     float t = fold(s0, s1, 8, u8);
     e += __shfl_xor(e, 8);
-#pragma unroll
-    for (int m = 4; m > 0; m >>= 1) {
-        t += __shfl_xor(t, m);
-        e += __shfl_xor(e, m);
-    }
+    // the last three levels stay inside groups of 8 lanes: row moves instead of permutes
+    // (lane ^ 1, lane ^ 2, then lane i with 7 - i); every lane of a group ends with the same sum
+    t += dpp_moved<0xB1>(t);
+    e += dpp_moved<0xB1>(e);
+    t += dpp_moved<0x4E>(t);
+    e += dpp_moved<0x4E>(e);
+    t += dpp_moved<0x141>(t);
+    e += dpp_moved<0x141>(e);
     packed = t;
     last = e;
 }
