@@ -20,6 +20,8 @@
 // other, so polling another workgroup's results costs a fabric round trip.
 // HBM traffic per pass and pair: read the key (count), read key+value and write
 // key+value (scatter).
+#include <type_traits>
+
 #include "gs_internal.h"
 
 namespace gsr {
@@ -153,11 +155,16 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
     constexpr int kWaves = kBlock / kWave;
     constexpr int kSortItems = ITEMS;
     constexpr int kSortTile = kBlock * ITEMS;
-    __shared__ K s_keys[kSortTile];
-    __shared__ uint32_t s_vals[kSortTile];
+    // keys narrower than 64 bits travel with their value as one 8-byte LDS entry
+    constexpr bool kPacked = sizeof(K) <= 4;
+    using Entry = typename std::conditional<kPacked, uint2, uint32_t>::type;
+    __shared__ Entry s_pack[kPacked ? kSortTile : 1];
+    __shared__ K s_keys[kPacked ? 1 : kSortTile];
+    __shared__ uint32_t s_vals[kPacked ? 1 : kSortTile];
     __shared__ uint32_t s_wave_count[kWaves][kRadix];   // per-wave running counts, then wave prefixes
     __shared__ uint32_t s_local_start[kRadix];          // start of each digit inside the tile
     __shared__ uint32_t s_next[kRadix];                 // next global position of each digit (this range)
+    __shared__ uint32_t s_dst[kRadix];                  // s_next - s_local_start (>= 0), for the tile's writes
     __shared__ uint32_t s_tmp[kWaves];
 
     const int radix = 1 << bits;
@@ -207,23 +214,35 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
         }
         const uint32_t local_start = block_exclusive_scan_u32(tile_count, s_tmp);   // barriers inside
         s_local_start[threadIdx.x] = local_start;
+        s_dst[threadIdx.x] = s_next[threadIdx.x] - local_start;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < kSortItems; ++r) {
             if (seg + r * kWave + lane < hi) {
                 const uint32_t d = digit_of(key[r], shift, mask);
                 const uint32_t pos = s_local_start[d] + s_wave_count[wave][d] + rank[r];
-                s_keys[pos] = key[r];
-                s_vals[pos] = val[r];
+                if constexpr (kPacked) {
+                    s_pack[pos] = make_uint2((uint32_t)key[r], val[r]);
+                } else {
+                    s_keys[pos] = key[r];
+                    s_vals[pos] = val[r];
+                }
             }
         }
         __syncthreads();
         const int count = (int)min<int64_t>(kSortTile, hi - tile);
         for (int q = threadIdx.x; q < count; q += kBlock) {
-            const K k = s_keys[q];
-            const uint32_t d = digit_of(k, shift, mask);
-            const int64_t dst = (int64_t)s_next[d] + (q - (int64_t)s_local_start[d]);
-            const uint32_t v = s_vals[q];
+            K k;
+            uint32_t v;
+            if constexpr (kPacked) {
+                const uint2 e = s_pack[q];
+                k = (K)e.x;
+                v = e.y;
+            } else {
+                k = s_keys[q];
+                v = s_vals[q];
+            }
+            const int64_t dst = (int64_t)s_dst[digit_of(k, shift, mask)] + q;
             keys_out[dst] = k;
             vals_out[dst] = v;
             if (gathered_out) gathered_out[dst] = gather_src[v];
