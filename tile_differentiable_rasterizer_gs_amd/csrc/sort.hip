@@ -71,15 +71,22 @@ __device__ inline void group_range(int64_t n, int64_t tile, int groups, int grou
 }
 
 // Lanes of this wave whose digit equals d (one ballot per digit bit); only lanes with
-// `valid` take part.
+// `valid` take part.  kBits > 0: the digit width is a compile-time constant (unrolled).
+template <int kBits>
 __device__ inline uint64_t match_digit(uint32_t d, int bits, bool valid) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t on = __ballot(bit);
-        peers &= bit ? on : ~on;
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const int nb = kBits > 0 ? kBits : bits;
+#pragma unroll
+    for (int b = 0; b < (kBits > 0 ? kBits : 8); ++b) {
+        if (kBits == 0 && b >= nb) break;
+        const uint32_t neg = 0u - ((d >> b) & 1u);   // all ones where this lane's bit is set
+        const uint64_t on = __ballot(neg != 0u);
+        // keep the lanes whose bit equals this lane's: ~(on ^ neg), one 32-bit half at a time
+        lo &= ~((uint32_t)on ^ neg);
+        hi &= ~((uint32_t)(on >> 32) ^ neg);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Element count of a pass: the host bound, or min(bound, *n_dev) when the count lives on the device.
@@ -144,7 +151,8 @@ __global__ __launch_bounds__(kBlock) void radix_digit_scan_kernel(uint32_t *coun
 }
 
 // gathered_out (optional): gathered_out[dst] = gather_src[value] for every moved pair.
-template <typename K, int ITEMS>
+// kBits > 0: the pass's digit width as a compile-time constant (else `bits`).
+template <typename K, int ITEMS, int kBits>
 __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in, const uint32_t *vals_in,
                                                                K *keys_out, uint32_t *vals_out, int64_t n_cap,
                                                                const unsigned long long *n_dev, int shift,
@@ -186,17 +194,17 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
         K key[kSortItems];
         uint32_t val[kSortItems];
 #pragma unroll
-        for (int r = 0; r < kSortItems; ++r) {
-            const int64_t i = seg + r * kWave + lane;
-            key[r] = i < hi ? keys_in[i] : (K)0;
-            val[r] = i < hi ? vals_in[i] : 0u;
+        for (int r = 0; r < kSortItems; ++r) {   // past the range: a repeat of the last pair, not ranked
+            const int64_t i = min<int64_t>(seg + r * kWave + lane, hi - 1);
+            key[r] = keys_in[i];
+            val[r] = vals_in[i];
         }
         uint32_t rank[kSortItems];
 #pragma unroll
         for (int r = 0; r < kSortItems; ++r) {
             const bool valid = seg + r * kWave + lane < hi;
             const uint32_t d = digit_of(key[r], shift, mask);
-            const uint64_t peers = match_digit(d, bits, valid);
+            const uint64_t peers = match_digit<kBits>(d, bits, valid);
             const uint32_t below = lanes_below(peers);
             const uint32_t prev = valid ? s_wave_count[wave][d] : 0u;
             rank[r] = prev + below;
@@ -495,8 +503,24 @@ void launch_pass(K *ki, uint32_t *vi, K *ko, uint32_t *vo, int64_t n, const unsi
                  uint32_t *gathered_out, hipStream_t s) {
     radix_count_kernel<K, ITEMS><<<groups, kBlock, 0, s>>>(ki, n, n_dev, shift, bits, counts);
     radix_digit_scan_kernel<<<1 << bits, kBlock, 0, s>>>(counts, groups, totals);
-    radix_scatter_kernel<K, ITEMS><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts, totals,
-                                                             gather_src, gathered_out);
+    switch (bits) {   // the digit widths the passes use (8-bit digits, 13 tile bits -> 7 + 6)
+        case 8:
+            radix_scatter_kernel<K, ITEMS, 8><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts,
+                                                                        totals, gather_src, gathered_out);
+            break;
+        case 7:
+            radix_scatter_kernel<K, ITEMS, 7><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts,
+                                                                        totals, gather_src, gathered_out);
+            break;
+        case 6:
+            radix_scatter_kernel<K, ITEMS, 6><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts,
+                                                                        totals, gather_src, gathered_out);
+            break;
+        default:
+            radix_scatter_kernel<K, ITEMS, 0><<<groups, kBlock, 0, s>>>(ki, vi, ko, vo, n, n_dev, shift, bits, counts,
+                                                                        totals, gather_src, gathered_out);
+            break;
+    }
 }
 
 }  // namespace
