@@ -170,9 +170,8 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
     __shared__ K s_keys[kPacked ? 1 : kSortTile];
     __shared__ uint32_t s_vals[kPacked ? 1 : kSortTile];
     __shared__ uint32_t s_wave_count[kWaves][kRadix];   // per-wave running counts, then wave prefixes
-    __shared__ uint32_t s_local_start[kRadix];          // start of each digit inside the tile
     __shared__ uint32_t s_next[kRadix];                 // next global position of each digit (this range)
-    __shared__ uint32_t s_dst[kRadix];                  // s_next - s_local_start (>= 0), for the tile's writes
+    __shared__ uint32_t s_dst[kRadix];                  // s_next - the digit's start in the tile (>= 0)
     __shared__ uint32_t s_tmp[kWaves];
 
     const int radix = 1 << bits;
@@ -208,27 +207,29 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
             const uint32_t below = lanes_below(peers);
             const uint32_t prev = valid ? s_wave_count[wave][d] : 0u;
             rank[r] = prev + below;
-            if (valid && below == 0) s_wave_count[wave][d] = prev + (uint32_t)__popcll(peers);
+            // every lane of a digit group writes the same new count
+            if (valid) s_wave_count[wave][d] = prev + (uint32_t)__popcll(peers);
             __builtin_amdgcn_wave_barrier();
         }
         __syncthreads();
-        // thread = digit: wave prefixes and the tile's count of that digit
-        uint32_t tile_count = 0;
+        // thread = digit: the tile's count of that digit, then each wave's first slot for it
+        // (the digit's start in the tile plus the counts of the waves before)
+        uint32_t tile_count = 0, before[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const uint32_t c = s_wave_count[w][threadIdx.x];
-            s_wave_count[w][threadIdx.x] = tile_count;
-            tile_count += c;
+            before[w] = tile_count;
+            tile_count += s_wave_count[w][threadIdx.x];
         }
         const uint32_t local_start = block_exclusive_scan_u32(tile_count, s_tmp);   // barriers inside
-        s_local_start[threadIdx.x] = local_start;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s_wave_count[w][threadIdx.x] = local_start + before[w];
         s_dst[threadIdx.x] = s_next[threadIdx.x] - local_start;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < kSortItems; ++r) {
             if (seg + r * kWave + lane < hi) {
                 const uint32_t d = digit_of(key[r], shift, mask);
-                const uint32_t pos = s_local_start[d] + s_wave_count[wave][d] + rank[r];
+                const uint32_t pos = s_wave_count[wave][d] + rank[r];
                 if constexpr (kPacked) {
                     s_pack[pos] = make_uint2((uint32_t)key[r], val[r]);
                 } else {
