@@ -110,14 +110,20 @@ __global__ __launch_bounds__(kBlock) void radix_count_kernel(const K *keys, int6
     __syncthreads();
     int64_t lo, hi;
     group_range(n, (int64_t)kBlock * ITEMS, gridDim.x, blockIdx.x, &lo, &hi);
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * kBlock) {
-        K k[4];
+    // 16-byte loads of kV keys (lo is a multiple of the sort tile, so they are aligned), then the tail
+    constexpr int kV = 16 / (int)sizeof(K);
+    const int64_t nvec = (hi - lo) / kV;
+    const uint4 *kvec = reinterpret_cast<const uint4 *>(keys + lo);
+#pragma unroll 2
+    for (int64_t j = threadIdx.x; j < nvec; j += kBlock) {
+        const uint4 w = kvec[j];
+        K k[kV];
+        __builtin_memcpy(k, &w, sizeof w);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) k[u] = i + u * kBlock < hi ? keys[i + u * kBlock] : K(0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * kBlock < hi) atomicAdd(&s_count[copy * kStride + digit_of(k[u], shift, mask)], 1u);
+        for (int u = 0; u < kV; ++u) atomicAdd(&s_count[copy * kStride + digit_of(k[u], shift, mask)], 1u);
     }
+    for (int64_t i = lo + nvec * kV + threadIdx.x; i < hi; i += kBlock)
+        atomicAdd(&s_count[copy * kStride + digit_of(keys[i], shift, mask)], 1u);
     __syncthreads();
     if ((int)threadIdx.x <= (int)mask) {
         uint32_t c = 0;
