@@ -292,6 +292,7 @@ def main():
     ap.add_argument("--sort-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-splat2d", action="store_true", help="skip the 2D splat-fitting timing")
     ap.add_argument("--no-ellipse", action="store_true", help="skip the exact-footprint tile rule timing")
     ap.add_argument("--streams", type=int, default=0,
                     help="views in flight (contexts on their own streams); default 3 for multi-view workloads, else 1")
@@ -452,6 +453,7 @@ def main():
         out["tile_test_ellipse"] = time_ellipse_rule(dev, scene, cams, bg, args.steps, args.sort_mode)
     if not args.no_backward:
         out["backward"] = time_backward(r, dev, scene, cams, img, bg, args.steps, blends)
+    if not args.no_splat2d:
         log("2D splat fit ...")
         out["splat2d_fit"] = time_splat2d_fit()
         log(f"2D splat fit: {out['splat2d_fit']}")
