@@ -1,5 +1,5 @@
 /*
- * gsrast — forward tile-based 3D Gaussian-splatting rasterizer for AMD
+ * gsrast — tile-based differentiable 3D Gaussian-splatting rasterizer for AMD
  * Instinct MI355X (gfx950), C ABI.
  *
  * The method: the lesson "3D Gaussian Splatting from scratch"
@@ -19,12 +19,13 @@
  *    Arguments are validated on the host before any HIP call, so
  *    GS_ERR_INVALID_ARGUMENT leaves the device untouched.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
- *    gs_bin_and_sort and gs_render wait, once per call, until the number of
- *    (Gaussian, tile) pairs has been copied to the host.  The pair kernels are
- *    enqueued before that wait on buffers sized from earlier calls, so the GPU
- *    does not idle; when the count exceeds that capacity the buffers grow and
- *    the pair kernels run again before the call returns.  All other calls are
- *    asynchronous.
+ *    gs_bin_and_sort and gs_render wait, once per call, for the number of
+ *    (Gaussian, tile) pairs: the prefix-sum kernel stores it into host memory
+ *    and the call waits for that kernel (not for the whole stream).  The pair
+ *    kernels are enqueued before that wait on buffers sized from earlier calls,
+ *    so the GPU does not idle; when the count exceeds that capacity the buffers
+ *    grow and the pair kernels run again before the call returns.  All other
+ *    calls are asynchronous.
  *  - One context per host thread / stream at a time; a context is not
  *    thread-safe.  Views returned in gs_projected / gs_binning point into
  *    context-owned device memory and stay valid until the next call on the
@@ -232,8 +233,8 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *gaussians, const gs
  * Tile binning of the last gs_preprocess output: prefix sum of tile counts,
  * (tile, depth) pair listing, stable sort, and per-tile ranges (flowchart
  * steps "Assign to tiles" and "Depth-sort per tile").  `projected` must be the
- * view returned by the last gs_preprocess on this context.  Synchronises
- * `stream` once.
+ * view returned by the last gs_preprocess on this context.  Waits once for
+ * the pair count (see the conventions above).
  */
 gs_status gs_bin_and_sort(gs_context *ctx, const gs_projected *projected, const gs_camera *camera,
                           gs_binning *out, hipStream_t stream);
@@ -261,7 +262,7 @@ gs_status gs_composite_ex(gs_context *ctx, const gs_projected *projected, const 
                           hipStream_t stream);
 
 /* gs_preprocess + gs_bin_and_sort + gs_composite on one stream (keys are not
- * materialised).  Synchronises `stream` once. */
+ * materialised).  Waits once for the pair count (see the conventions above). */
 gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
                     const float bg_rgb[3], float *image_hwc, hipStream_t stream);
 
