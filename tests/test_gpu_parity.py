@@ -300,12 +300,12 @@ def _tile_list_oracle(o, tile, tiles_x):
     return hit[order].astype(np.uint32)
 
 
-def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0):
+def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0):
     import torch
 
     from tile_differentiable_rasterizer_gs_amd import binding
 
-    r = binding.Rasterizer(emit_keys=False)
+    r = binding.Rasterizer(sort_mode=mode, emit_keys=False)
     dev = binding.gaussians_to_device(s.arrays())
     pr = r.preprocess(dev, s.sh_degree, cam)
     bn = r.bin_and_sort(pr, cam)
@@ -345,6 +345,17 @@ def test_c4_5m_large_gaussians_sampled():
     m, err = _large_check(s, s.cameras[0], n_tiles=16, n_pix=300)
     note(f"c4 pairs={m} sampled err {err:.2e}")
     assert m > 10 ** 8
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_long_pair_lists_sampled(mode):
+    # 30 000 large Gaussians, ~7.5e7 pairs: enough for the listing's long workgroups (16 entries
+    # per thread), in both sort modes
+    s = scenes.random_scene(seed=93, n=30000, sh_degree=0, width=1280, height=720, log_scale_range=(-1.2, -0.4))
+    note(f"long pair lists mode={mode}")
+    m, err = _large_check(s, s.cameras[0], n_tiles=16, n_pix=300, seed=3, mode=mode)
+    note(f"long pair lists mode={mode} pairs={m} sampled err {err:.2e}")
+    assert m > 7 * 10 ** 7
 
 
 def test_c5_orbit_views_sampled():

@@ -271,23 +271,27 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
 // pair listing: entry e of the list belongs to the ranked Gaussian i with
 // offsets[i] <= e < offsets[i+1]; its tiles run row-major over the rectangle.
 // ---------------------------------------------------------------------------
-constexpr int kDupItems = 8;
-constexpr int kDupTile = kBlock * kDupItems;   // 2048 entries per workgroup
-constexpr int kDupWindow = kDupTile + 1;
+// Entries per thread: 8 (2048 per workgroup), or 16 for long lists, where each workgroup's
+// fixed cost (locating and staging its ranks) is then spread over twice the entries.
+constexpr int kDupItems = 8, kDupItemsLong = 16;   // multiples of 8 (16-byte stores of 16-bit keys)
+constexpr int64_t kLongListing = 1 << 26;           // pair capacity from which the long blocks are used
+constexpr int kDupTileMin = kBlock * kDupItems;
+constexpr int kDupWindow = kDupTileMin + 1;         // ranks a workgroup stages in LDS
 
-// part[b] = rank whose pairs contain entry b * kDupTile; part[blocks] = rank of the last entry.
+// part[b] = rank whose pairs contain entry b * tile; part[blocks] = rank of the last entry.
 // Also zeroes clear[0, clear_words) (the tile ranges, so that tiles without pairs read as empty).
 __global__ __launch_bounds__(kBlock) void partition_kernel(const uint32_t *offsets, int64_t n_items,
                                                            const unsigned long long *num_dev, int64_t cap,
-                                                           uint32_t *part, uint32_t *clear, int64_t clear_words) {
+                                                           int64_t tile, uint32_t *part, uint32_t *clear,
+                                                           int64_t clear_words) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     for (int64_t w = i; w < clear_words; w += (int64_t)gridDim.x * kBlock) clear[w] = 0u;
     if (i >= n_items) return;
     const int64_t num = live_count(cap, num_dev);
     const int64_t start = offsets[i];
     const int64_t end = min<int64_t>(i + 1 < n_items ? (int64_t)offsets[i + 1] : (int64_t)*num_dev, num);
-    for (int64_t b = (start + kDupTile - 1) / kDupTile; b * kDupTile < end; ++b) part[b] = (uint32_t)i;
-    if (start < end && end == num) part[(num + kDupTile - 1) / kDupTile] = (uint32_t)i;
+    for (int64_t b = (start + tile - 1) / tile; b * tile < end; ++b) part[b] = (uint32_t)i;
+    if (start < end && end == num) part[(num + tile - 1) / tile] = (uint32_t)i;
 }
 
 __device__ inline int64_t last_le_global(const uint32_t *offsets, int64_t lo, int64_t hi, uint32_t e) {
@@ -298,22 +302,25 @@ __device__ inline int64_t last_le_global(const uint32_t *offsets, int64_t lo, in
     return lo;
 }
 
-// Workgroup b lists entries [b*2048, (b+1)*2048).  The ranks whose pairs meet that
-// span are staged in LDS, and each rank marks the threads whose first entry it holds;
-// each thread then takes 8 consecutive entries and walks the rectangles row-major.
+// Workgroup b lists entries [b*kTile, (b+1)*kTile).  The ranks whose pairs meet that
+// span are staged in LDS (up to kDupWindow of them; else they are searched in global
+// memory), and each rank marks the threads whose first entry it holds; each thread then
+// takes kItems consecutive entries and walks the rectangles row-major.
 // kDepth: the 64-bit keys carry the depth bits (staged only then).
-template <bool kDepth>
+template <bool kDepth, int kItems>
 __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, const uint32_t *part) {
+    static_assert(kItems % 8 == 0, "listing stores whole 16-byte vectors");
+    constexpr int kTile = kBlock * kItems;
     __shared__ uint32_t s_off[kDupWindow];
     __shared__ uint32_t s_g[kDupWindow];
     __shared__ uint2 s_rect[kDupWindow];
     __shared__ uint32_t s_depth[kDepth ? kDupWindow : 1];
     __shared__ uint16_t s_rank[kBlock];   // rank (in the window) holding each thread's first entry
     const int64_t num_dups = live_count(p.capacity, p.num_dups);
-    const int64_t first = (int64_t)blockIdx.x * kDupTile;
+    const int64_t first = (int64_t)blockIdx.x * kTile;
     if (first >= num_dups) return;
     const int64_t lo = part[blockIdx.x];
-    const int64_t hi = part[blockIdx.x + 1];   // rank of entry (b+1)*kDupTile, or of the last entry
+    const int64_t hi = part[blockIdx.x + 1];   // rank of entry (b+1)*kTile, or of the last entry
     const int64_t window = hi - lo + 1;
     const bool staged = window <= kDupWindow;
     if (staged) {
@@ -326,19 +333,19 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             if (kDepth) s_depth[k] = __float_as_uint(p.depth[g]);
         }
         __syncthreads();
-        // rank k holds entries [s_off[k], s_off[k+1]); thread t starts at first + 8t
+        // rank k holds entries [s_off[k], s_off[k+1]); thread t starts at first + kItems*t
         for (int64_t k = threadIdx.x; k < window; k += kBlock) {
             const int64_t a = (int64_t)s_off[k] - first;
-            const int64_t b = k + 1 < window ? (int64_t)s_off[k + 1] - first : (int64_t)kDupTile;
-            const int64_t t0 = a <= 0 ? 0 : (a + kDupItems - 1) / kDupItems;
-            const int64_t t1 = min<int64_t>(kBlock, b <= 0 ? 0 : (b + kDupItems - 1) / kDupItems);
+            const int64_t b = k + 1 < window ? (int64_t)s_off[k + 1] - first : (int64_t)kTile;
+            const int64_t t0 = a <= 0 ? 0 : (a + kItems - 1) / kItems;
+            const int64_t t1 = min<int64_t>(kBlock, b <= 0 ? 0 : (b + kItems - 1) / kItems);
             for (int64_t t = t0; t < t1; ++t) s_rank[t] = (uint16_t)k;
         }
     }
     __syncthreads();
-    const int64_t e0 = first + (int64_t)threadIdx.x * kDupItems;
+    const int64_t e0 = first + (int64_t)threadIdx.x * kItems;
     if (e0 >= num_dups) return;
-    const int n_here = (int)min<int64_t>(kDupItems, num_dups - e0);
+    const int n_here = (int)min<int64_t>(kItems, num_dups - e0);
 
     // rank holding e0
     int64_t i;
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     uint32_t g, off, dbits;
     uint2 rc;
     load_rank(i, g, off, rc, dbits);
-    uint32_t tiles[kDupItems], gs[kDupItems], dbs[kDupItems];
+    uint32_t tiles[kItems], gs[kItems], dbs[kItems];
     if (p.ellipse) {
         // exact footprint: the kept tiles of each row form one span; walk the spans
         EllipseRec E = p.ellipse[g];
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     uint32_t j = (uint32_t)e0 - off;
     uint32_t row = j / w, col = j - row * w;
 #pragma unroll
-    for (int k = 0; k < kDupItems; ++k) {
+    for (int k = 0; k < kItems; ++k) {
         if (k < n_here) {
             tiles[k] = (y0 + row) * (uint32_t)p.tiles_x + x0 + col;
             gs[k] = g;
@@ -427,22 +434,28 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
         }
     }
     }
-    if (n_here == kDupItems) {
+    if (n_here == kItems) {
         uint4 *vo = reinterpret_cast<uint4 *>(p.values + e0);
-        vo[0] = make_uint4(gs[0], gs[1], gs[2], gs[3]);
-        vo[1] = make_uint4(gs[4], gs[5], gs[6], gs[7]);
+#pragma unroll
+        for (int q = 0; q < kItems / 4; ++q)
+            vo[q] = make_uint4(gs[4 * q], gs[4 * q + 1], gs[4 * q + 2], gs[4 * q + 3]);
         if (p.tile_keys) {
             uint4 *to = reinterpret_cast<uint4 *>(p.tile_keys + e0);
-            to[0] = make_uint4(tiles[0], tiles[1], tiles[2], tiles[3]);
-            to[1] = make_uint4(tiles[4], tiles[5], tiles[6], tiles[7]);
+#pragma unroll
+            for (int q = 0; q < kItems / 4; ++q)
+                to[q] = make_uint4(tiles[4 * q], tiles[4 * q + 1], tiles[4 * q + 2], tiles[4 * q + 3]);
         }
-        if (p.tile_keys16)   // eight 16-bit tile ids = one 16-byte store
-            *reinterpret_cast<uint4 *>(p.tile_keys16 + e0) =
-                make_uint4(tiles[0] | (tiles[1] << 16), tiles[2] | (tiles[3] << 16), tiles[4] | (tiles[5] << 16),
-                           tiles[6] | (tiles[7] << 16));
+        if (p.tile_keys16) {   // eight 16-bit tile ids = one 16-byte store
+            uint4 *to = reinterpret_cast<uint4 *>(p.tile_keys16 + e0);
+#pragma unroll
+            for (int q = 0; q < kItems / 8; ++q) {
+                const uint32_t *t = tiles + 8 * q;
+                to[q] = make_uint4(t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16));
+            }
+        }
         if (p.keys64) {
 #pragma unroll
-            for (int k = 0; k < kDupItems; ++k) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
+            for (int k = 0; k < kItems; ++k) p.keys64[e0 + k] = ((uint64_t)tiles[k] << 32) | dbs[k];
         }
     } else {
         for (int k = 0; k < n_here; ++k) {
@@ -576,17 +589,26 @@ template int radix_sort_pairs<uint16_t>(uint16_t *, uint32_t *, uint16_t *, uint
                                         const unsigned long long *, int, int, uint32_t *, hipStream_t,
                                         const uint32_t *, uint32_t *);
 
-int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTile - 1) / kDupTile + 1; }
+int64_t duplicate_partition_words(int64_t num_dups) { return (num_dups + kDupTileMin - 1) / kDupTileMin + 1; }
 
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
     if (p.capacity <= 0 || p.n_items <= 0) return;
+    const bool long_list = p.capacity >= kLongListing;
+    const int64_t tile = (int64_t)kBlock * (long_list ? kDupItemsLong : kDupItems);
     partition_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(
-        p.offsets, p.n_items, p.num_dups, p.capacity, part, p.clear, p.clear_words);
-    const int64_t nb = (p.capacity + kDupTile - 1) / kDupTile;
-    if (p.keys64)
-        duplicate_kernel<true><<<(unsigned)nb, kBlock, 0, s>>>(p, part);
-    else
-        duplicate_kernel<false><<<(unsigned)nb, kBlock, 0, s>>>(p, part);
+        p.offsets, p.n_items, p.num_dups, p.capacity, tile, part, p.clear, p.clear_words);
+    const unsigned nb = (unsigned)((p.capacity + tile - 1) / tile);
+    if (p.keys64) {
+        if (long_list)
+            duplicate_kernel<true, kDupItemsLong><<<nb, kBlock, 0, s>>>(p, part);
+        else
+            duplicate_kernel<true, kDupItems><<<nb, kBlock, 0, s>>>(p, part);
+    } else {
+        if (long_list)
+            duplicate_kernel<false, kDupItemsLong><<<nb, kBlock, 0, s>>>(p, part);
+        else
+            duplicate_kernel<false, kDupItems><<<nb, kBlock, 0, s>>>(p, part);
+    }
 }
 
 void launch_ranges(const RangesParams &p, hipStream_t s) {
