@@ -4,63 +4,84 @@
 // near the centre of a view carry several times the mean.  Launched in tile order,
 // the heavy tiles start late and the frame ends with a few of them running on an
 // otherwise idle chip.  Launching them first (longest-processing-time-first) evens
-// the finish.  The order is a bucket sort by weight, coarsened to 256 buckets
-// between 0 and the largest weight; order within a bucket is arbitrary, which only
-// changes when a tile runs, never what it computes.
+// the finish.  The order is a counting sort by weight on a logarithmic scale, 2048
+// buckets of 1/64 octave (the leading bit of the weight and the six below it), so no
+// pass for the largest weight is needed; order within a bucket is arbitrary, which
+// only changes when a tile runs, never what it computes.
 #include "gs_internal.h"
 
 namespace gsr {
 namespace {
 
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderBuckets = 256;
+constexpr int kOrderSubBits = 6;                              // bits below the leading one
+constexpr int kOrderBuckets = 32 << kOrderSubBits;            // 2048
+constexpr int kOrderPer = kOrderBuckets / kOrderThreads;      // buckets per thread in the scan
+constexpr int kOrderKept = 8;   // tiles per thread whose bucket stays in registers (8192 tiles)
 
 __device__ __forceinline__ uint32_t tile_weight(const TileOrderParams &p, int t) {
     return p.weights ? p.weights[t] : p.ranges[2 * t + 1] - p.ranges[2 * t];
 }
 
+// Bucket of a weight, heaviest first: 2047 - (64 * floor(log2 w) + the six bits after
+// the leading one); weight 0 goes last.
+__device__ __forceinline__ uint32_t order_bucket(uint32_t w) {
+    if (w == 0) return kOrderBuckets - 1;
+    const uint32_t lead = 31u - (uint32_t)__clz(w);
+    const uint32_t frac = ((w << (31u - lead)) >> (31 - kOrderSubBits)) & ((1u << kOrderSubBits) - 1u);
+    return (uint32_t)(kOrderBuckets - 1) - ((lead << kOrderSubBits) + frac);
+}
+
 __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(TileOrderParams p) {
-    __shared__ uint32_t s_max;
     __shared__ uint32_t s_count[kOrderBuckets];
-    __shared__ uint32_t s_wave[kOrderBuckets / kWave];
+    __shared__ uint32_t s_wave[kOrderThreads / kWave];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    if (threadIdx.x == 0) s_max = 0;
     for (int b = threadIdx.x; b < kOrderBuckets; b += kOrderThreads) s_count[b] = 0;
     __syncthreads();
-    uint32_t m = 0;
-    for (int t = threadIdx.x; t < p.tiles; t += kOrderThreads) m = max(m, tile_weight(p, t));
+    // each thread keeps the buckets of its first kOrderKept tiles (and recomputes the rest)
+    uint32_t kept[kOrderKept];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if (lane == 0) atomicMax(&s_max, m);
-    __syncthreads();
-    const uint64_t wmax = (uint64_t)s_max + 1;
-    // bucket 0 holds the heaviest tiles
-    auto bucket = [&](uint32_t w) {
-        return (uint32_t)(kOrderBuckets - 1) - (uint32_t)(((uint64_t)w * kOrderBuckets) / wmax);
-    };
-    for (int t = threadIdx.x; t < p.tiles; t += kOrderThreads) atomicAdd(&s_count[bucket(tile_weight(p, t))], 1u);
-    __syncthreads();
-    // exclusive prefix over the 256 buckets: a scan per wave, then the wave totals
-    uint32_t c = 0, incl = 0;
-    if (threadIdx.x < kOrderBuckets) {
-        c = s_count[threadIdx.x];
-        incl = c;
+    for (int j = 0; j < kOrderKept; ++j) {
+        const int t = threadIdx.x + j * kOrderThreads;
+        kept[j] = t < p.tiles ? order_bucket(tile_weight(p, t)) : 0u;
+    }
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t up = (uint32_t)__shfl_up((int)incl, off);
-            if (lane >= off) incl += up;
-        }
-        if (lane == kWave - 1) s_wave[wave] = incl;
+    for (int j = 0; j < kOrderKept; ++j)
+        if (threadIdx.x + j * kOrderThreads < p.tiles) atomicAdd(&s_count[kept[j]], 1u);
+    for (int t = threadIdx.x + kOrderKept * kOrderThreads; t < p.tiles; t += kOrderThreads)
+        atomicAdd(&s_count[order_bucket(tile_weight(p, t))], 1u);
+    __syncthreads();
+    // exclusive prefix over the buckets: kOrderPer consecutive buckets per thread, a scan per
+    // wave, then the wave totals
+    uint32_t c[kOrderPer], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kOrderPer; ++k) {
+        c[k] = s_count[threadIdx.x * kOrderPer + k];
+        sum += c[k];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t up = (uint32_t)__shfl_up((int)incl, off);
+        if (lane >= off) incl += up;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - sum;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+#pragma unroll
+    for (int k = 0; k < kOrderPer; ++k) {
+        s_count[threadIdx.x * kOrderPer + k] = base;
+        base += c[k];
     }
     __syncthreads();
-    if (threadIdx.x < kOrderBuckets) {
-        uint32_t base = 0;
-        for (int w = 0; w < wave; ++w) base += s_wave[w];
-        s_count[threadIdx.x] = base + incl - c;
+#pragma unroll
+    for (int j = 0; j < kOrderKept; ++j) {
+        const int t = threadIdx.x + j * kOrderThreads;
+        if (t < p.tiles) p.order[atomicAdd(&s_count[kept[j]], 1u)] = (uint32_t)t;
     }
-    __syncthreads();
-    for (int t = threadIdx.x; t < p.tiles; t += kOrderThreads)
-        p.order[atomicAdd(&s_count[bucket(tile_weight(p, t))], 1u)] = (uint32_t)t;
+    for (int t = threadIdx.x + kOrderKept * kOrderThreads; t < p.tiles; t += kOrderThreads)
+        p.order[atomicAdd(&s_count[order_bucket(tile_weight(p, t))], 1u)] = (uint32_t)t;
 }
 
 // Backward work of a tile: the entries up to the deepest one any of its pixels blended.
