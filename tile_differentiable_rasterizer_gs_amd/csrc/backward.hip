@@ -113,12 +113,12 @@ struct BwdLane {
     }
 };
 
-// Wave sums of the nine partials, stored as one whole record by the first kPairStride lanes.
+// Wave sums of the nine partials, stored as one record by lanes 0-8.
 __device__ __forceinline__ void store_record(const float v[kPairGrad], int lane, float *rec) {
     float packed, last;
     reduce9(v, lane, packed, last);
     const float mine = gather9(packed, last, lane);
-    if (lane < kPairStride) rec[lane] = lane < kPairGrad ? mine : 0.0f;
+    if (lane < kPairGrad) rec[lane] = mine;
 }
 
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
@@ -506,12 +506,8 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
                 for (uint32_t tx = sa + li; tx < sb; tx += kRowLanes) {
                     if (key > p.cut[ty * (uint32_t)p.tiles_x + tx]) continue;
                     const float *r = rec + (size_t)(k0 + tx - sa) * kPairStride;
-                    const float4 a = *reinterpret_cast<const float4 *>(r);
-                    const float4 b = *reinterpret_cast<const float4 *>(r + 4);
-                    const float c8 = r[8];
-                    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-                    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-                    acc[8] += c8;
+#pragma unroll
+                    for (int c = 0; c < kPairGrad; ++c) acc[c] += r[c];
                 }
                 k0 += sb - sa;
             }
@@ -524,12 +520,8 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
                 const uint32_t tile = (y0 + row) * (uint32_t)p.tiles_x + x0 + (i - row * w);
                 if (key > p.cut[tile]) continue;   // no pixel of that tile reached this Gaussian
                 const float *r = rec + (size_t)i * kPairStride;
-                const float4 a = *reinterpret_cast<const float4 *>(r);
-                const float4 b = *reinterpret_cast<const float4 *>(r + 4);
-                const float c8 = r[8];
-                acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-                acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-                acc[8] += c8;
+#pragma unroll
+                for (int c = 0; c < kPairGrad; ++c) acc[c] += r[c];
             }
         }
 #pragma unroll

@@ -224,10 +224,9 @@ void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges
 // gradients
 // ---------------------------------------------------------------------------
 // Per-pair gradient record: the contribution of one (Gaussian, tile) pair, summed
-// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b; padded
-// with zeros to 48 bytes, always written whole (three aligned 16-byte pieces).
+// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b; 36 bytes.
 constexpr int kPairGrad = 9;
-constexpr int kPairStride = 12;
+constexpr int kPairStride = kPairGrad;
 
 struct CompositeBackwardParams {
     int32_t width, height, tiles_x, tiles_y;
