@@ -5,11 +5,12 @@
 // alpha-composite front to back):
 //   gs_preprocess    preprocess kernel
 //   gs_bin_and_sort  depth-first mode: radix sort of per-Gaussian depth keys,
-//                    prefix sum of tile counts in depth order, pair-count
-//                    read-back, pair listing in depth order, stable radix sort on
-//                    the tile id, tile ranges (+ optional 64-bit keys)
-//                    key64 mode: prefix sum, read-back, 64-bit key listing in
-//                    Gaussian order, radix sort over tile+depth bits, ranges
+//                    prefix sum of tile counts in depth order (its last kernel
+//                    stores the pair count into host memory), pair listing in depth
+//                    order, stable radix sort on the tile id, tile ranges (+ optional
+//                    64-bit keys)
+//                    key64 mode: prefix sum, 64-bit key listing in Gaussian order,
+//                    radix sort over tile+depth bits, ranges
 //   gs_composite     one workgroup per tile, heaviest tiles (longest lists) first
 //   gs_backward      tile order by reverse-walk length (depth-first mode: prefix sum
 //                    of tile counts in Gaussian order), per-tile reverse walk writing
@@ -86,7 +87,7 @@ struct gs_context {
     const uint32_t *launch_order = nullptr;    // last binning: heaviest-first tile order (or null)
     const uint64_t *sorted_keys = nullptr;
     int64_t pair_capacity = 0;                 // entries the pair buffers hold
-    hipEvent_t total_ready = nullptr;          // pair count has reached host_total
+    hipEvent_t total_ready = nullptr;          // the prefix sum ran (its last kernel stores host_total)
 
     std::vector<TimedSpan> spans;
     size_t spans_used = 0;
