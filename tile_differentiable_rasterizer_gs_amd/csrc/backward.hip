@@ -176,6 +176,11 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         p.cut[tile] = cut;
     }
 
+    // The wave sum of an entry's partials is a chain of cross-lane steps; it is done one
+    // entry late, so that it overlaps the pixel work of the next entry.
+    float held[kPairGrad];
+    uint32_t held_pos = 0;
+    bool holding = false;
     for (int hi = (int)n_max; hi > 0; hi -= kBwdBatch) {
         const int lo = hi > kBwdBatch ? hi - kBwdBatch : 0;
         const int cnt = hi - lo;
@@ -199,12 +204,23 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
                                                       : (ty - y0) * (x1 - x0) + (tx - x0));
         }
         __syncthreads();
-        for (int k = cnt - 1; k >= 0; --k) {
+        int k = cnt - 1;
+        if (!holding) {   // the tile's first entry
+            px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), held);
+            held_pos = s_pos[k];
+            holding = true;
+            --k;
+        }
+        for (; k >= 0; --k) {
             float v[kPairGrad];
             px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), v);
-            store_record(v, lane, p.pair_grad + (size_t)s_pos[k] * kPairStride);
+            store_record(held, lane, p.pair_grad + (size_t)held_pos * kPairStride);
+#pragma unroll
+            for (int c = 0; c < kPairGrad; ++c) held[c] = v[c];
+            held_pos = s_pos[k];
         }
     }
+    if (holding) store_record(held, lane, p.pair_grad + (size_t)held_pos * kPairStride);
 }
 
 // ---------------------------------------------------------------------------
