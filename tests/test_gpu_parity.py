@@ -201,6 +201,18 @@ def test_above_ordered_tile_limit():
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_tiny_footprints_many_ranks_per_listing_block(mode):
+    # 20 000 Gaussians of about one tile each: a 2048-entry listing block meets up to ~1650
+    # ranks, more than a workgroup stages (1025), so those blocks search their ranks in
+    # global memory
+    s = scenes.random_scene(seed=94, n=20000, sh_degree=1, width=320, height=240, log_scale_range=(-7.0, -6.0))
+    o = oracle.preprocess(s.arrays(), 1, s.cameras[0])
+    assert o["tile_count"].sum() < 1.3 * (o["tile_count"] > 0).sum()
+    note(f"tiny footprints mode={mode}")
+    _full_check(s.arrays(), 1, s.cameras[0], bg=(0.1, 0.2, 0.3), mode=mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_equal_depths_keep_index_order(mode):
     n = 40
     rng = np.random.default_rng(4)

@@ -276,7 +276,10 @@ __global__ __launch_bounds__(kBlock) void radix_scatter_kernel(const K *keys_in,
 constexpr int kDupItems = 8, kDupItemsLong = 16;   // multiples of 8 (16-byte stores of 16-bit keys)
 constexpr int64_t kLongListing = 1 << 26;           // pair capacity from which the long blocks are used
 constexpr int kDupTileMin = kBlock * kDupItems;
-constexpr int kDupWindow = kDupTileMin + 1;         // ranks a workgroup stages in LDS
+// ranks a workgroup stages in LDS (more, i.e. fewer than two pairs per rank on average,
+// are searched in global memory); half the 2049 a 2048-entry block can meet, for a
+// smaller LDS footprint: at 1 M Gaussians no block meets more than ~450
+constexpr int kDupWindow = 1025;
 
 // part[b] = rank whose pairs contain entry b * tile; part[blocks] = rank of the last entry.
 // Also zeroes clear[0, clear_words) (the tile ranges, so that tiles without pairs read as empty).
