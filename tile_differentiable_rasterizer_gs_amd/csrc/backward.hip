@@ -500,79 +500,58 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         m_ry = rc.y;
         m_depth = __float_as_uint(p.depth[gm]);
     }
-    // exact footprint: a Gaussian's records follow its row spans; the row's lanes take its tiles
-    auto ellipse_sum = [&](int gl, uint32_t count, float *acc) {
-        if (!count) return;
+    for (int round = 0; round < kGaussPerWave / 4; ++round) {
+        const int gl = 4 * round + row;
         const int64_t g = g0 + gl;
-        const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
-        const uint2 rc = p.rect[g];
-        const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y1 = rc.y >> 16;
-        const EllipseRec E = p.ellipse[g];
-        const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
-        uint32_t k0 = 0, sa, sb;
-        for (uint32_t ty = rc.y & 0xffffu; ty < y1; ++ty) {
-            row_span(E, x0, x1, ty, sa, sb);
-            for (uint32_t tx = sa + li; tx < sb; tx += kRowLanes) {
-                if (key > p.cut[ty * (uint32_t)p.tiles_x + tx]) continue;
-                const float *r = rec + (size_t)(k0 + tx - sa) * kPairStride;
+        const uint32_t count = (uint32_t)__shfl((int)m_count, gl);
+        const uint32_t base = (uint32_t)__shfl((int)m_base, gl), rx = (uint32_t)__shfl((int)m_rx, gl);
+        const uint32_t ry = (uint32_t)__shfl((int)m_ry, gl), dbits = (uint32_t)__shfl((int)m_depth, gl);
+        float acc[kPairGrad];
 #pragma unroll
-                for (int c = 0; c < kPairGrad; ++c) acc[c] += r[c];
+        for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
+        if (count && p.ellipse) {
+            // exact footprint: records follow the row spans; the row's lanes take its tiles
+            const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
+            const uint2 rc = p.rect[g];
+            const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y1 = rc.y >> 16;
+            const EllipseRec E = p.ellipse[g];
+            const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
+            uint32_t k0 = 0, sa, sb;
+            for (uint32_t ty = rc.y & 0xffffu; ty < y1; ++ty) {
+                row_span(E, x0, x1, ty, sa, sb);
+                for (uint32_t tx = sa + li; tx < sb; tx += kRowLanes) {
+                    if (key > p.cut[ty * (uint32_t)p.tiles_x + tx]) continue;
+                    const float *r = rec + (size_t)(k0 + tx - sa) * kPairStride;
+#pragma unroll
+                    for (int c = 0; c < kPairGrad; ++c) acc[c] += r[c];
+                }
+                k0 += sb - sa;
             }
-            k0 += sb - sa;
-        }
-    };
-    // Two rounds at a time: the rows' record reads for two Gaussians are in flight together.
-    for (int round = 0; round < kGaussPerWave / 4; round += 2) {
-        const int glA = 4 * round + row, glB = glA + 4;
-        const uint32_t countA = (uint32_t)__shfl((int)m_count, glA), countB = (uint32_t)__shfl((int)m_count, glB);
-        float accA[kPairGrad], accB[kPairGrad];
-#pragma unroll
-        for (int c = 0; c < kPairGrad; ++c) accA[c] = accB[c] = 0.0f;
-        if (p.ellipse) {
-            ellipse_sum(glA, countA, accA);
-            ellipse_sum(glB, countB, accB);
-        } else {
-            const uint32_t baseA = (uint32_t)__shfl((int)m_base, glA), baseB = (uint32_t)__shfl((int)m_base, glB);
-            const uint32_t rxA = (uint32_t)__shfl((int)m_rx, glA), rxB = (uint32_t)__shfl((int)m_rx, glB);
-            const uint32_t ryA = (uint32_t)__shfl((int)m_ry, glA), ryB = (uint32_t)__shfl((int)m_ry, glB);
-            const uint32_t dA = (uint32_t)__shfl((int)m_depth, glA), dB = (uint32_t)__shfl((int)m_depth, glB);
-            const float *recA = p.pair_grad + (size_t)baseA * kPairStride;
-            const float *recB = p.pair_grad + (size_t)baseB * kPairStride;
-            const uint32_t x0A = rxA & 0xffffu, wA = (rxA >> 16) - x0A, y0A = ryA & 0xffffu;
-            const uint32_t x0B = rxB & 0xffffu, wB = (rxB >> 16) - x0B, y0B = ryB & 0xffffu;
-            const unsigned long long keyA = ((unsigned long long)dA << 32) | (uint64_t)(g0 + glA);
-            const unsigned long long keyB = ((unsigned long long)dB << 32) | (uint64_t)(g0 + glB);
-            const uint32_t cmax = max(countA, countB);
-            for (uint32_t i = li; i < cmax; i += kRowLanes) {
-                // skip the records of tiles whose walk stopped before the Gaussian
-                if (i < countA) {
-                    const uint32_t r = i / wA;
-                    const uint32_t tile = (y0A + r) * (uint32_t)p.tiles_x + x0A + (i - r * wA);
-                    if (keyA <= p.cut[tile]) {
-                        const float *q = recA + (size_t)i * kPairStride;
-#pragma unroll
-                        for (int c = 0; c < kPairGrad; ++c) accA[c] += q[c];
-                    }
+        } else if (count) {
+            const float *rec = p.pair_grad + (size_t)base * kPairStride;
+            const uint32_t x0 = rx & 0xffffu, w = (rx >> 16) - x0, y0 = ry & 0xffffu;
+            const unsigned long long key = ((unsigned long long)dbits << 32) | (uint64_t)g;
+            // record i's tile is (row, col) = divmod(i, w), stepped by divmod(16, w) per record
+            uint32_t r = li / w, col = li - r * w;
+            const uint32_t q16 = kRowLanes / w, s16 = kRowLanes - q16 * w;
+            for (uint32_t i = li; i < count; i += kRowLanes) {
+                const uint32_t tile = (y0 + r) * (uint32_t)p.tiles_x + x0 + col;
+                r += q16;
+                col += s16;
+                if (col >= w) {
+                    col -= w;
+                    ++r;
                 }
-                if (i < countB) {
-                    const uint32_t r = i / wB;
-                    const uint32_t tile = (y0B + r) * (uint32_t)p.tiles_x + x0B + (i - r * wB);
-                    if (keyB <= p.cut[tile]) {
-                        const float *q = recB + (size_t)i * kPairStride;
+                if (key > p.cut[tile]) continue;   // no pixel of that tile reached this Gaussian
+                const float *q = rec + (size_t)i * kPairStride;
 #pragma unroll
-                        for (int c = 0; c < kPairGrad; ++c) accB[c] += q[c];
-                    }
-                }
+                for (int c = 0; c < kPairGrad; ++c) acc[c] += q[c];
             }
         }
 #pragma unroll
         for (int c = 0; c < kPairGrad; ++c) {
-            const float va = row_sum(accA[c]);
-            const float vb = row_sum(accB[c]);
-            if (li == kRowLanes - 1) {
-                s_sum[wave][glA][c] = va;
-                s_sum[wave][glB][c] = vb;
-            }
+            const float v = row_sum(acc[c]);
+            if (li == kRowLanes - 1) s_sum[wave][gl][c] = v;
         }
     }
     __syncthreads();
