@@ -3,17 +3,20 @@
 // Flowchart of the lesson "3D Gaussian Splatting from scratch", steps "Assign to
 // tiles (16x16 screen-space)" and "Depth-sort per tile": every (Gaussian, tile)
 // pair is listed and the list is ordered by (tile, camera-space depth), equal
-// depths by Gaussian index.  The key of a pair is (tile_id << 32) | bits(depth);
-// for depth > 0 the IEEE bit pattern orders like the value.
+// depths by Gaussian index.  In the 64-bit mode the key of a pair is
+// (tile_id << 32) | bits(depth); for depth > 0 the IEEE bit pattern orders like the
+// value.  In the default mode the Gaussians are sorted by depth first, the pairs are
+// listed in that order, and a stable sort on the tile id alone finishes the order.
 //
-// Radix sort: 8-bit digits, least significant first, three kernels per digit on a
-// fixed grid of G workgroups, each owning one contiguous range of the input:
+// Radix sort: digits of at most 8 bits, least significant first (32-bit depth keys in
+// 4 x 8, 13 tile bits in 7 + 6), three kernels per digit on a fixed grid of G
+// workgroups, each owning one contiguous range of the input:
 //   count   per-range digit counts, counts[d][range]
 //   scan    one workgroup per digit: exclusive prefix over ranges, plus the digit total
-//   scatter each range walks its 4096-pair tiles in order; a tile ranks its keys
-//           stably in LDS (a ballot per key bit finds the lanes of a wave that
-//           share a digit) and writes them through LDS in contiguous digit runs at
-//           running per-digit offsets.
+//   scatter each range walks its tiles of 4096 pairs (1024 for inputs up to 4 M) in
+//           order; a tile ranks its keys stably in LDS (a ballot per key bit finds the
+//           lanes of a wave that share a digit) and writes them through LDS in
+//           contiguous digit runs at running per-digit offsets.
 // Ranges and tiles are processed in input order, so equal digits keep their
 // order.  No workgroup waits on another (communication only across kernel
 // boundaries): on MI355X the L2s of the eight XCDs are not coherent with each
