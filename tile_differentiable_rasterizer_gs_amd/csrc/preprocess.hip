@@ -185,6 +185,8 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     p.rect[g] = make_uint2(x0 | (x1 << 16), y0 | (y1 << 16));
     p.tile_count[g] = !visible ? 0u : (p.ellipse ? kept : (x1 - x0) * (y1 - y0));
     if (p.depth_key) {
+        // Gaussians without pairs sort last: interleaved with the others they would dilute the
+        // pair listing's rank windows (a 2048-entry block would meet thousands of empty ranks)
         p.depth_key[g] = visible ? __float_as_uint(tz) : 0xffffffffu;
         p.depth_index[g] = (uint32_t)g;
     }
