@@ -212,6 +212,26 @@ def test_tiny_footprints_many_ranks_per_listing_block(mode):
     _full_check(s.arrays(), 1, s.cameras[0], bg=(0.1, 0.2, 0.3), mode=mode)
 
 
+@pytest.mark.parametrize("runs", [(2000, 500), (40, 40)])
+@pytest.mark.parametrize("mode", MODES)
+def test_runs_of_culled_gaussians_between_listed_ones(mode, runs):
+    # index runs of Gaussians behind the camera between runs of visible ones: in index order (the
+    # 64-bit-key mode) the listing meets runs of ranks without pairs and must step over them; with
+    # runs of 2000 and 500 a listing block meets ~2500 ranks (more than it stages), with runs of
+    # 40 and 40 ~900 (staged)
+    culled, shown = runs
+    cam = scenes.look_at_camera(scenes.orbit_position(4.0, 0.3, 0.2), (0, 0, 0), 300.0, 320, 240)
+    s = scenes.random_scene(seed=96, n=40000, sh_degree=1, width=320, height=240, log_scale_range=(-4.0, -3.0))
+    arr = s.arrays()
+    behind = (np.arange(40000) % (culled + shown)) < culled
+    c = np.asarray(scenes.orbit_position(4.0, 0.3, 0.2))
+    arr["mean"] = np.ascontiguousarray(np.where(behind[None, :], (3.0 * c)[:, None], arr["mean"]).astype(np.float32))
+    o = oracle.preprocess(arr, 1, cam)
+    assert (o["tile_count"][behind] == 0).all() and (o["tile_count"][~behind] > 0).sum() > 7000
+    note(f"culled runs {runs} mode={mode}")
+    _full_check(arr, 1, cam, bg=(0.2, 0.1, 0.0), mode=mode)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_equal_depths_keep_index_order(mode):
     n = 40

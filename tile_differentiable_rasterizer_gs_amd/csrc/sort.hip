@@ -374,6 +374,21 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             db = kDepth ? __float_as_uint(p.depth[g]) : 0u;
         }
     };
+    // The rank after rank i that holds entry e_next: the last one whose offset is <= e_next
+    // (ranks without pairs share the offset of the next rank with pairs).  Usually i + 1;
+    // past a run of ranks without pairs, a bisection over the window.
+    const int64_t last = hi - lo;
+    auto rank_offset = [&](int64_t k) -> uint32_t { return staged ? s_off[k] : p.offsets[lo + k]; };
+    auto next_rank = [&](int64_t i, uint32_t e_next) -> int64_t {
+        ++i;
+        if (i >= last || rank_offset(i + 1) > e_next) return i;
+        int64_t a = i + 1, b = last;
+        while (a < b) {
+            const int64_t mid = a + (b - a + 1) / 2;
+            if (rank_offset(mid) <= e_next) a = mid; else b = mid - 1;
+        }
+        return a;
+    };
     uint32_t g, off, dbits;
     uint2 rc;
     load_rank(i, g, off, rc, dbits);
@@ -397,10 +412,8 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             if (++tx == sb && k + 1 < n_here) {
                 do {   // next row with a span, else the next rank with pairs
                     if (++ty == y1) {
-                        do {
-                            ++i;
-                            load_rank(i, g, off, rc, dbits);
-                        } while (p.tile_count[g] == 0);
+                        i = next_rank(i, (uint32_t)e0 + k + 1);
+                        load_rank(i, g, off, rc, dbits);
                         E = p.ellipse[g];
                         x0 = rc.x & 0xffffu;
                         x1 = rc.x >> 16;
@@ -425,11 +438,13 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             if (++col == w) {
                 col = 0;
                 if (++row == h && k + 1 < n_here) {
-                    // next rank with pairs (ranks without pairs own no entries)
-                    do {
-                        ++i;
+                    // next rank with pairs (ranks without pairs own no entries): usually the
+                    // next one, its rectangle loaded anyway
+                    load_rank(++i, g, off, rc, dbits);
+                    if (((rc.x >> 16) - (rc.x & 0xffffu)) * ((rc.y >> 16) - (rc.y & 0xffffu)) == 0) {
+                        i = next_rank(i - 1, (uint32_t)e0 + k + 1);
                         load_rank(i, g, off, rc, dbits);
-                    } while (((rc.x >> 16) - (rc.x & 0xffffu)) * ((rc.y >> 16) - (rc.y & 0xffffu)) == 0);
+                    }
                     x0 = rc.x & 0xffffu;
                     w = (rc.x >> 16) - x0;
                     y0 = rc.y & 0xffffu;
