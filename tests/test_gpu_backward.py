@@ -103,7 +103,7 @@ def test_backward_c1(mode):
 
 
 def test_backward_long_pair_lists():
-    # large Gaussians: many cover more than 32 tiles (the workgroup-per-Gaussian sum)
+    # large Gaussians: many cover more than 32 tiles (several passes of a 16-lane row)
     sc = scenes.random_scene(7, 300, 3, 240, 176, log_scale_range=(-1.6, -0.9))
     cam = sc.cameras[0]
     tc = oracle.preprocess(sc.arrays(), 3, cam)["tile_count"]
@@ -113,6 +113,21 @@ def test_backward_long_pair_lists():
     g = gpu_grads(sc.arrays(), 3, cam, gimg, bg=(0.5, 0.5, 0.5))
     o = oracle.render_backward(sc.arrays(), 3, cam, gimg, bg=(0.5, 0.5, 0.5))
     check_grads(g, o, "long lists")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_backward_lists_longer_than_a_row_takes(mode):
+    # hundreds of Gaussians with more than 512 records: their lists are summed by a whole
+    # workgroup before the per-Gaussian pass, the others by 16-lane rows
+    sc = scenes.random_scene(23, 400, 3, 640, 480, log_scale_range=(-1.2, -0.4))
+    cam = sc.cameras[0]
+    tc = oracle.preprocess(sc.arrays(), 3, cam)["tile_count"]
+    assert (tc > 512).sum() > 100 and ((tc > 0) & (tc <= 512)).sum() > 20
+    gimg = _cotangent(cam, 4)
+    note(f"backward lists over 512 mode={mode}")
+    g = gpu_grads(sc.arrays(), 3, cam, gimg, bg=(0.2, 0.3, 0.4), mode=mode)
+    o = oracle.render_backward(sc.arrays(), 3, cam, gimg, bg=(0.2, 0.3, 0.4))
+    check_grads(g, o, f"lists over 512 mode={mode}")
 
 
 def test_backward_opacity_zero_and_clamped():

@@ -29,7 +29,8 @@
 //    record: the tile publishes the (depth bits, index) key of its deepest walked
 //    entry, and the next stage reads exactly the records at or below it.
 // 2. gaussian_backward_kernel: sum of each Gaussian's records (a 16-lane row per
-//    Gaussian, reading consecutive records), then the chain rule through the projection
+//    Gaussian, reading consecutive records; the whole workgroup for a list longer than
+//    512 records), then the chain rule through the projection
 //    (conic <- 2D covariance <- J W Sigma W^T J^T <- R(q) diag(exp(log s)), mean2d <-
 //    t) and the SH colour (sections "L'étape de projection", "Étape 5", "Étape 6"),
 //    in fp32.  Records are laid out in Gaussian-index order (pair_base = exclusive
@@ -481,10 +482,63 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
 // and written coalesced.
 constexpr int kGaussPerWave = kWave;
 constexpr int kRowLanes = 16;
+// Lists longer than this (square rule) are left to the whole workgroup once the rows are
+// done: a 16-lane row would otherwise walk a list of thousands of records (the large
+// Gaussians of a scene) alone while the rest of the workgroup waits for it.
+constexpr uint32_t kLongRecords = 512;
+
+// Sum of the long list of Gaussian g (count records, square rule) by all threads of the
+// workgroup: thread t adds records t, t + 256, ... that pass the cut test, then a
+// fixed-order reduction over the waves, whose nine sums threads 0..8 store to out[0..8].
+// Every thread of the workgroup must call it (two barriers).
+__device__ __forceinline__ void long_list_sum(const GaussianBackwardParams &p, int64_t g,
+                                              float (*s_part)[kPairGrad], float *out) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const uint32_t count = p.tile_count[g];
+    const float *rec = p.pair_grad + (size_t)p.pair_base[g] * kPairStride;
+    const uint2 rc = p.rect[g];
+    const uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu;
+    const unsigned long long key = ((unsigned long long)__float_as_uint(p.depth[g]) << 32) | (uint64_t)g;
+    float acc[kPairGrad];
+#pragma unroll
+    for (int c = 0; c < kPairGrad; ++c) acc[c] = 0.0f;
+    // record i's tile is (row, col) = divmod(i, w), stepped by divmod(256, w)
+    uint32_t r = threadIdx.x / w, col = threadIdx.x - r * w;
+    const uint32_t qs = kBlock / w, ss = kBlock - qs * w;
+    for (uint32_t i = threadIdx.x; i < count; i += kBlock) {
+        const uint32_t tile = (y0 + r) * (uint32_t)p.tiles_x + x0 + col;
+        r += qs;
+        col += ss;
+        if (col >= w) {
+            col -= w;
+            ++r;
+        }
+        if (key > p.cut[tile]) continue;   // no pixel of that tile reached this Gaussian
+        const float *q = rec + (size_t)i * kPairStride;
+#pragma unroll
+        for (int c = 0; c < kPairGrad; ++c) acc[c] += q[c];
+    }
+#pragma unroll
+    for (int c = 0; c < kPairGrad; ++c) {
+        const float v = wave_sum(acc[c]);
+        if (lane == 0) s_part[wave][c] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kPairGrad) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < kBlock / kWave; ++w2) t += s_part[w2][threadIdx.x];
+        out[threadIdx.x] = t;
+    }
+    __syncthreads();
+}
 
 template <int K>
 __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackwardParams p) {
     __shared__ float s_sum[kBlock / kWave][kGaussPerWave][kPairGrad + 1];
+    __shared__ uint8_t s_long[kBlock / kWave][kGaussPerWave];   // per wave: lanes with a long list
+    __shared__ int s_long_n[kBlock / kWave];
+    __shared__ float s_part[kBlock / kWave][kPairGrad];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int row = lane / kRowLanes, li = lane & (kRowLanes - 1);
     const int64_t g0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kGaussPerWave;
@@ -492,6 +546,11 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
     // once, coalesced); each round's rows fetch theirs by shuffle
     const int64_t gm = g0 + lane;
     const uint32_t m_count = gm < p.n ? p.tile_count[gm] : 0u;
+    const bool m_long = !p.ellipse && m_count > kLongRecords;
+    const uint64_t longs = __ballot(m_long);
+    if (m_long) s_long[wave][__builtin_amdgcn_mbcnt_hi((uint32_t)(longs >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)longs, 0u))] = (uint8_t)lane;
+    if (lane == 0) s_long_n[wave] = __popcll(longs);
     uint32_t m_base = 0, m_rx = 0, m_ry = 0, m_depth = 0;
     if (m_count && !p.ellipse) {
         m_base = p.pair_base[gm];
@@ -527,6 +586,8 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
                 }
                 k0 += sb - sa;
             }
+        } else if (count > kLongRecords) {
+            // summed by the whole workgroup below
         } else if (count) {
             const float *rec = p.pair_grad + (size_t)base * kPairStride;
             const uint32_t x0 = rx & 0xffffu, w = (rx >> 16) - x0, y0 = ry & 0xffffu;
@@ -555,6 +616,13 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         }
     }
     __syncthreads();
+    // the long lists of the workgroup's 256 Gaussians, one after another (the counts are in
+    // LDS, so the branch and the loop are uniform over the workgroup)
+    for (int w = 0; w < kBlock / kWave; ++w)
+        for (int q = 0; q < s_long_n[w]; ++q) {
+            const int l = s_long[w][q];
+            long_list_sum(p, ((int64_t)blockIdx.x * (kBlock / kWave) + w) * kGaussPerWave + l, s_part, s_sum[w][l]);
+        }
     const int64_t g = g0 + lane;
     if (g >= p.n) return;
     if (p.tile_count[g] == 0) {
