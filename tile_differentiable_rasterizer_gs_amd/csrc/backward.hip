@@ -474,7 +474,7 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
 // ---------------------------------------------------------------------------
 // per-Gaussian sums of the pair records + chain rule
 // ---------------------------------------------------------------------------
-// A wave owns 64 consecutive Gaussians.  In 16 rounds, each 16-lane row sums the
+// A wave owns 64 consecutive Gaussians.  In up to 16 rounds, each 16-lane row sums the
 // records of one Gaussian (lane i takes records i, i + 16, ...: a row reads 16
 // consecutive records, skipping those of tiles whose walk stopped before the
 // Gaussian), reduces them with DPP row shifts and parks the nine sums in LDS; then
@@ -559,8 +559,22 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         m_ry = rc.y;
         m_depth = __float_as_uint(p.depth[gm]);
     }
+    // The rows take the wave's Gaussians in descending order of their list lengths (a bitonic
+    // sort of (count, lane) over the wave; a long list counts as empty, the workgroup sums it),
+    // so the four rows of a round walk lists of similar length; after the last Gaussian with a
+    // list, the remaining rounds have nothing to do.
+    uint32_t order = ((m_long ? 0u : min(m_count, 0xffffffu)) << 6) | (uint32_t)lane;
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)order, j);
+            const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+            order = keep_max ? max(order, other) : min(order, other);
+        }
     for (int round = 0; round < kGaussPerWave / 4; ++round) {
-        const int gl = 4 * round + row;
+        if ((__builtin_amdgcn_readlane((int)order, 4 * round) >> 6) == 0) break;
+        const int gl = (int)((uint32_t)__shfl((int)order, 4 * round + row) & (kWave - 1));
         const int64_t g = g0 + gl;
         const uint32_t count = (uint32_t)__shfl((int)m_count, gl);
         const uint32_t base = (uint32_t)__shfl((int)m_base, gl), rx = (uint32_t)__shfl((int)m_rx, gl);
