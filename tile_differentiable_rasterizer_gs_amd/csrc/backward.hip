@@ -304,25 +304,14 @@ __device__ inline void sh_basis_values(float x, float y, float z, float Y[K]) {
     }
 }
 
-// Zero gradients for a Gaussian in no tile list (the image does not depend on it).
-template <int K>
-__device__ inline void gaussian_zero(const GaussianBackwardParams &p, int g) {
-    const int n = p.n;
-    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = 0.0f;
-    for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = 0.0f;
-    for (int i = 0; i < 3; ++i) p.g_log_scale[i * n + g] = 0.0f;
-    p.g_opacity[g] = 0.0f;
-    for (int i = 0; i < 3 * K; ++i) p.g_sh[(size_t)i * n + g] = 0.0f;
-    if (p.g_mean2d) p.g_mean2d[g] = p.g_mean2d[n + g] = 0.0f;
-    if (p.g_conic) p.g_conic[g] = p.g_conic[n + g] = p.g_conic[2 * n + g] = 0.0f;
-    if (p.g_rgb) p.g_rgb[g] = p.g_rgb[n + g] = p.g_rgb[2 * n + g] = 0.0f;
-}
-
 // Chain rule from the screen-space gradients sg (u, v, A, B, C, opacity, r, g, b) of
-// Gaussian g to its parameters.
+// Gaussian g to its parameters.  A Gaussian in no tile list (live false, sg zero) gets zero
+// gradients through the same stores, so that a wave writes each parameter plane with one
+// store instruction: two partial-wave stores to the same lines cost extra HBM writes.
 template <int K>
-__device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad]) {
+__device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad], bool live) {
     const int n = p.n;
+    auto out = [live](float v) { return live ? v : 0.0f; };   // culled Gaussians may give inf or NaN
     const float gu = sg[0], gv = sg[1], gA = sg[2], gB = sg[3], gC = sg[4];
     p.g_opacity[g] = sg[5];
     if (p.g_mean2d) { p.g_mean2d[g] = gu; p.g_mean2d[n + g] = gv; }
@@ -431,7 +420,7 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
             gs[j] += gM * R[i][j];
         }
 #pragma unroll
-    for (int j = 0; j < 3; ++j) p.g_log_scale[j * n + g] = gs[j] * s[j];
+    for (int j = 0; j < 3; ++j) p.g_log_scale[j * n + g] = out(gs[j] * s[j]);
 
     // ---- R of the unit quaternion, then the normalisation ----
     float gq[4];
@@ -445,7 +434,7 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     const float qh[4] = {qw, qx, qy, qz};
     const float dot = qh[0] * gq[0] + qh[1] * gq[1] + qh[2] * gq[2] + qh[3] * gq[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = (gq[i] - qh[i] * dot) / qn;
+    for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = out((gq[i] - qh[i] * dot) / qn);
 
     // ---- colour: rgb = sum_k Y_k(d) sh_k with d = (mean - C) / |mean - C| ----
     float dir[3] = {mu[0] - p.cam_pos[0], mu[1] - p.cam_pos[1], mu[2] - p.cam_pos[2]};
@@ -459,7 +448,7 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
             const size_t plane = (size_t)(k * 3 + ch) * n + g;
-            p.g_sh[plane] = Y[k] * sg[6 + ch];
+            p.g_sh[plane] = out(Y[k] * sg[6 + ch]);
             acc += p.sh[plane] * sg[6 + ch];
         }
         wk[k] = acc;
@@ -468,7 +457,7 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     sh_basis_vjp<K>(d[0], d[1], d[2], wk, gd);
     const float radial = gd[0] * d[0] + gd[1] * d[1] + gd[2] * d[2];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = gmu[i] + (gd[i] - d[i] * radial) * idn;
+    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = out(gmu[i] + (gd[i] - d[i] * radial) * idn);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,14 +628,11 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
         }
     const int64_t g = g0 + lane;
     if (g >= p.n) return;
-    if (p.tile_count[g] == 0) {
-        gaussian_zero<K>(p, (int)g);
-        return;
-    }
+    const bool live = m_count != 0;   // else in no tile list: zero gradients
     float sg[kPairGrad];
 #pragma unroll
-    for (int c = 0; c < kPairGrad; ++c) sg[c] = s_sum[wave][lane][c];
-    gaussian_vjp<K>(p, (int)g, sg);
+    for (int c = 0; c < kPairGrad; ++c) sg[c] = live ? s_sum[wave][lane][c] : 0.0f;
+    gaussian_vjp<K>(p, (int)g, sg, live);
 }
 
 }  // namespace
