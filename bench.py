@@ -35,10 +35,11 @@ VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 # transmittance update (1); stop test (1)
 COMPOSITE_OPS_PER_PAIR = 17
 # lane-ops per blended pair in the backward walk: alpha as in the forward (dx, dy, exponent
-# 4, exp2, clamp: 7); 1 - alpha and its reciprocal (2); T recovery (1); dL/dalpha from the
-# colour behind and the background (7); three colour-behind updates (6); colour gradient
-# weights (4); clamp test and opacity gradient (3); dL/dQ (2); u, v, A, B, C gradients (10)
-BACKWARD_OPS_PER_PAIR = 42
+# 4, exp2, clamp: 7); 1 - alpha and its reciprocal (2); T recovery (1); dL/dalpha from
+# c . dL/dC, the carried (colour behind) . dL/dC and the background (7); the update of that
+# carried product (1); colour gradient weights (4); clamp test and opacity gradient (3);
+# dL/dQ (2); u, v, A, B, C gradients (10)
+BACKWARD_OPS_PER_PAIR = 37
 
 
 def log(msg):

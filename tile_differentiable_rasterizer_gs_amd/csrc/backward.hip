@@ -12,7 +12,8 @@
 //    lane.  The tile's list is walked back to front from the largest blended
 //    count of its pixels.  A pixel recovers T_i = T_{i+1} / (1 - alpha_i) from the
 //    forward's final transmittance, recomputing alpha_i exactly as the forward did,
-//    and accumulates the colour behind entry i, B_{i-1} = alpha_i c_i + (1 - alpha_i) B_i:
+//    and accumulates the colour behind entry i, B_{i-1} = alpha_i c_i + (1 - alpha_i) B_i
+//    (only its product with dL/dC is needed, and carried):
 //      dL/dc_i     = alpha_i T_i dL/dC
 //      dL/dalpha_i = T_i (c_i - B_i) . dL/dC - T_final (bg . dL/dC) / (1 - alpha_i)
 //    and, where alpha_i = o G is below the 0.99 clamp, with G = exp(-Q/2),
@@ -55,7 +56,7 @@ constexpr int kBwdBatch = 64;      // entries staged per LDS batch
 struct BwdLane {
     float y;
     float x[kBwdPix], T[kBwdPix], gC[kBwdPix][3], bg_term[kBwdPix];
-    float B[kBwdPix][3];   // colour behind the current entry
+    float BgC[kBwdPix];    // B . dL/dC, B the colour behind the current entry
     uint32_t n[kBwdPix];   // entries the pixel blended in the forward
 
     // Entry idx of the tile list (staged f, f2, cn, cl): steps the four pixels back over it
@@ -77,8 +78,9 @@ struct BwdLane {
             const float alpha = active ? fminf(f2.w, raw) : 0.0f;
             const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
             const float Ti = T[i] * rinv;
-            const float cb0 = c[0] - B[i][0], cb1 = c[1] - B[i][1], cb2 = c[2] - B[i][2];
-            const float dot = cb0 * gC[i][0] + cb1 * gC[i][1] + cb2 * gC[i][2];
+            // (c - B) . dL/dC, with B . dL/dC carried as one number: B_{i-1} = B_i + alpha (c - B_i)
+            // gives B_{i-1} . dL/dC = B_i . dL/dC + alpha (c - B_i) . dL/dC
+            const float dot = (c[0] * gC[i][0] + c[1] * gC[i][1] + c[2] * gC[i][2]) - BgC[i];
             // (an inactive pixel has alpha = 0, so 1/(1 - alpha) = 1 exactly and Ti = T; its
             // dL/dalpha is finite and reaches the sums only through `smooth`, which is false)
             const float d_alpha = __builtin_fmaf(Ti, dot, -bg_term[i] * rinv);
@@ -86,9 +88,7 @@ struct BwdLane {
             Sc[0] = __builtin_fmaf(w, gC[i][0], Sc[0]);
             Sc[1] = __builtin_fmaf(w, gC[i][1], Sc[1]);
             Sc[2] = __builtin_fmaf(w, gC[i][2], Sc[2]);
-            B[i][0] = __builtin_fmaf(alpha, cb0, B[i][0]);
-            B[i][1] = __builtin_fmaf(alpha, cb1, B[i][1]);
-            B[i][2] = __builtin_fmaf(alpha, cb2, B[i][2]);
+            BgC[i] = __builtin_fmaf(alpha, dot, BgC[i]);
             T[i] = Ti;
             const bool smooth = active && raw < cl.z;
             So = __builtin_fmaf(smooth ? raw * f2.z : 0.0f, d_alpha, So);
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         px.T[i] = 0.0f;
         px.gC[i][0] = px.gC[i][1] = px.gC[i][2] = 0.0f;
         px.bg_term[i] = 0.0f;
-        px.B[i][0] = px.B[i][1] = px.B[i][2] = 0.0f;
+        px.BgC[i] = 0.0f;
         px.n[i] = 0;
         if (ix < p.width && iy < p.height) {
             const size_t pix = (size_t)iy * p.width + ix;
