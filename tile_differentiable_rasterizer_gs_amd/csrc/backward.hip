@@ -114,12 +114,41 @@ struct BwdLane {
     }
 };
 
-// Wave sums of the nine partials, stored as one record by lanes 0-8.
-__device__ __forceinline__ void store_record(const float v[kPairGrad], int lane, float *rec) {
-    float packed, last;
-    reduce9(v, lane, packed, last);
-    const float mine = gather9(packed, last, lane);
-    if (lane < kPairGrad) rec[lane] = mine;
+// Wave sums of the nine partials, stored as one record.  The walk is bound by VALU issue,
+// so the sums go through LDS rather than a butterfly: lane l writes its nine values to
+// s_red[c][l]; then lane l adds the eight values of component l / 8 held by lanes
+// 8 (l % 8) .. 8 (l % 8) + 7 (two 16-byte reads, a fixed add tree), and the same block of
+// component 8; three row moves (lane ^ 1, lane ^ 2, lane i with 7 - i) finish each sum over
+// its eight blocks.  About ten VALU instructions fewer per entry; the shuffling moves to the
+// LDS pipe.  One wave per workgroup: its LDS accesses complete in order.
+__device__ __forceinline__ float sum8(const float4 a, const float4 b) {
+    return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+}
+
+__device__ __forceinline__ void store_record(const float v[kPairGrad], int lane, float *s_red /*[9][64]*/,
+                                             float *rec) {
+    // compiler-only ordering: the previous record's reads before these writes, the writes
+    // before the reads of other lanes' values (the wave's LDS accesses run in program order)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < kPairGrad; ++c) s_red[c * kWave + lane] = v[c];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const float4 *blk = reinterpret_cast<const float4 *>(s_red) + 2 * (lane & 7);
+    const float4 *mine = blk + (lane >> 3) * (kWave / 4);
+    const float4 *last = blk + 8 * (kWave / 4);
+    float t = sum8(mine[0], mine[1]);
+    float q = sum8(last[0], last[1]);
+    t += dpp_moved<0xB1>(t);
+    q += dpp_moved<0xB1>(q);
+    t += dpp_moved<0x4E>(t);
+    q += dpp_moved<0x4E>(q);
+    t += dpp_moved<0x141>(t);
+    q += dpp_moved<0x141>(q);
+    // component j < 8 from lane 8 j, component 8 from lane 1
+    const bool first = (lane & 7) == 0;
+    if (first || lane == 1) rec[first ? lane >> 3 : 8] = first ? t : q;
 }
 
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
@@ -128,6 +157,7 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
     __shared__ float4 s_fwd[kBwdBatch], s_fwd2[kBwdBatch], s_conic[kBwdBatch];
     __shared__ float4 s_col[kBwdBatch];
     __shared__ uint32_t s_pos[kBwdBatch];
+    __shared__ __align__(16) float s_red[kPairGrad * kWave];   // store_record's transpose
 
     const int tile = p.tile_order ? (int)p.tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
@@ -215,13 +245,13 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         for (; k >= 0; --k) {
             float v[kPairGrad];
             px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), v);
-            store_record(held, lane, p.pair_grad + (size_t)held_pos * kPairStride);
+            store_record(held, lane, s_red, p.pair_grad + (size_t)held_pos * kPairStride);
 #pragma unroll
             for (int c = 0; c < kPairGrad; ++c) held[c] = v[c];
             held_pos = s_pos[k];
         }
     }
-    if (holding) store_record(held, lane, p.pair_grad + (size_t)held_pos * kPairStride);
+    if (holding) store_record(held, lane, s_red, p.pair_grad + (size_t)held_pos * kPairStride);
 }
 
 // ---------------------------------------------------------------------------
