@@ -48,6 +48,13 @@ __device__ __forceinline__ void gather(Staged &st, const float *__restrict__ spl
     }
 }
 
+// Value of lane 8 (l / 8) + u for lane l (within each group of 8 lanes), by ds_swizzle in
+// its bit mode: source lane = (l & 0x18) | u inside each half-wave of 32.
+template <int u>
+__device__ __forceinline__ float group8_get(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (u << 5)));
+}
+
 template <bool kAux>
 struct Pixels {
     float x0, x1, y;
@@ -56,8 +63,11 @@ struct Pixels {
 
     __device__ __forceinline__ void blend(const float4 a, const float4 b4, const float c) {
         const float dy = y - a.y;
-        const float bdy = b4.x * dy;
-        const float e = splat_row_term(dy, b4.y, a.z);
+        blend_row(a, b4, c, b4.x * dy, splat_row_term(dy, b4.y, a.z));
+    }
+    // the same, given the splat's row terms B' dy and C' dy^2 + log2 o for this lane's row
+    __device__ __forceinline__ void blend_row(const float4 a, const float4 b4, const float c, const float bdy,
+                                              const float e) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const float dx = (i ? x1 : x0) - a.x;
@@ -121,8 +131,24 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
         int j = 0;
         bool wave_live = true;
         for (; j + kUnroll <= count; j += kUnroll) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) px.blend(sa[j + u], sb[j + u], sc[j + u]);
+            // The row terms of the next 8 splats, computed once per (splat, row): lane l takes
+            // splat j + l % 8 at its own row (lanes 8r .. 8r + 7 share row r), then each lane
+            // fetches splat u's terms from lane 8 (l / 8) + u of its group with a swizzle,
+            // which runs on the LDS pipe; the blend itself is bound by VALU issue.
+            const float4 ra = sa[j + (lane & 7)], rb = sb[j + (lane & 7)];
+            const float rdy = px.y - ra.y;
+            const float r_bdy = rb.x * rdy, r_e = splat_row_term(rdy, rb.y, ra.z);
+            static_assert(kUnroll == 8, "one splat per lane of an 8-lane group");
+#define GS_BLEND_ROW(u) px.blend_row(sa[j + u], sb[j + u], sc[j + u], group8_get<u>(r_bdy), group8_get<u>(r_e))
+            GS_BLEND_ROW(0);
+            GS_BLEND_ROW(1);
+            GS_BLEND_ROW(2);
+            GS_BLEND_ROW(3);
+            GS_BLEND_ROW(4);
+            GS_BLEND_ROW(5);
+            GS_BLEND_ROW(6);
+            GS_BLEND_ROW(7);
+#undef GS_BLEND_ROW
             if (!__any(px.live())) {
                 wave_live = false;
                 break;
