@@ -30,11 +30,12 @@ HBM_PEAK_GBS = 8000.0
 # VALU issue peak: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz, one lane-op per lane per clock
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 # lane-ops per blended (pixel, Gaussian) pair in the composite inner loop, counting a
-# multiply-add as one: dx (1); exponent (A' dx + B' dy) dx + (C' dy^2 + log2 o) as two
-# multiply-adds on the row terms (2); exp2 (1); clamp (1); stop test and masked T (2);
-# T*alpha (1); three colour multiply-adds (3); transmittance update (1); plus the row terms
-# dy, B' dy, C' dy^2 + log2 o (4), computed once per (splat, pixel row of 16): 0.25
-COMPOSITE_OPS_PER_PAIR = 12.25
+# multiply-add as one: dx (1); exponent (A' dx + B' dy) dx + (C' dy^2 + log2(o / 0.99)) as
+# two multiply-adds on the row terms (2); exp2 with its clamp to 1 (1); stop test and
+# masked T (2); T*alpha (1); three colour multiply-adds (3); transmittance update (1);
+# plus the row terms dy, B' dy, C' dy^2 + log2(o / 0.99) (4), computed once per (splat,
+# pixel row of 16): 0.25
+COMPOSITE_OPS_PER_PAIR = 11.25
 # lane-ops per blended pair in the backward walk: alpha as in the forward (dx, dy, exponent
 # 4, exp2, clamp: 7); 1 - alpha and its reciprocal (2); T recovery (1); dL/dalpha from
 # c . dL/dC, the carried (colour behind) . dL/dC and the background (7); the update of that

@@ -73,9 +73,10 @@ struct BwdLane {
 #pragma unroll
         for (int i = 0; i < kBwdPix; ++i) {
             const float dx = x[i] - f.x;
-            const float raw = __builtin_amdgcn_exp2f(splat_exponent(dx, f.z, bdy, row));
+            // raw = min(1, 2^q) = alpha / 0.99 (G itself when o = 0), as the forward computed it
+            const float raw = splat_alpha_scaled(splat_exponent(dx, f.z, bdy, row));
             const bool active = idx < n[i];
-            const float alpha = active ? fminf(f2.w, raw) : 0.0f;
+            const float alpha = active ? f2.w * raw : 0.0f;
             const float rinv = __builtin_amdgcn_rcpf(1.0f - alpha);
             const float Ti = T[i] * rinv;
             // (c - B) . dL/dC, with B . dL/dC carried as one number: B_{i-1} = B_i + alpha (c - B_i)
@@ -152,8 +153,8 @@ __device__ __forceinline__ void store_record(const float v[kPairGrad], int lane,
 }
 
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
-    // staged entries: u, v, A', B' | C', log2 o, 1/o (1 when o = 0), alpha cap |
-    // A, B, C, r | g, b, clamp threshold of 2^q below which alpha is smooth
+    // staged entries: u, v, A', B' | C', log2(o / 0.99), 0.99 / o (1 when o = 0), alpha cap |
+    // A, B, C, r | g, b, value of min(1, 2^q) below which alpha is smooth (1, or inf when o = 0)
     __shared__ float4 s_fwd[kBwdBatch], s_fwd2[kBwdBatch], s_conic[kBwdBatch];
     __shared__ float4 s_col[kBwdBatch];
     __shared__ uint32_t s_pos[kBwdBatch];
@@ -224,11 +225,13 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
             const float o = r0.z;
             const bool zero_o = !(o > 0.0f);
             s_fwd[lane] = make_float4(r0.x, r0.y, r0.w, r1.x);
-            // o = 0: alpha is 0 and 2^q (with log2 o taken as 0) is G itself, never clamped
-            s_fwd2[lane] = make_float4(r1.y, zero_o ? 0.0f : __log2f(o), zero_o ? 1.0f : 1.0f / o,
-                                       zero_o ? 0.0f : GS_ALPHA_MAX);
+            // the exponent carries log2(o / 0.99) as in the forward, so min(1, 2^q) = alpha / 0.99
+            // and G = min(1, 2^q) 0.99 / o below the clamp; o = 0: alpha is 0 and 2^q (with
+            // the log term taken as 0) is G itself, never clamped
+            s_fwd2[lane] = make_float4(r1.y, zero_o ? 0.0f : splat_log2_scaled_opacity(o),
+                                       zero_o ? 1.0f : GS_ALPHA_MAX / o, zero_o ? 0.0f : GS_ALPHA_MAX);
             s_conic[lane] = make_float4(r2.z, r2.w, r3.x, r1.z);
-            s_col[lane] = make_float4(r1.w, r2.x, zero_o ? INFINITY : GS_ALPHA_MAX, 0.0f);
+            s_col[lane] = make_float4(r1.w, r2.x, zero_o ? INFINITY : 1.0f, 0.0f);
             const uint2 rc = p.rect[g];
             const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
             s_pos[lane] = p.pair_base[g] + (p.ellipse ? kept_index(p.ellipse[g], x0, x1, y0, tx, ty)

@@ -8,10 +8,12 @@
 // The tile's depth-sorted list is walked in batches of 256 splats.  The workgroup
 // gathers a batch into LDS (double-buffered: the global loads of the next batch are
 // in flight while the current one is blended) and every lane reads each splat back
-// as a wave-wide LDS broadcast.  A lane owns the two pixels (x, y) and (x + 8, y),
-// which share dy, B'dy and C'dy^2 + log2(o), so a pair costs about 14 VALU ops:
-//   q = (A' dx + B' dy) dx + C' dy^2 + log2 o,  alpha = min(0.99, 2^q)
-// with (A', B', C') = -log2(e)/2 (A, 2B, C).  A pixel stops after the blend that
+// as a wave-wide LDS broadcast.  A lane owns the two pixels (x, y) and (x + 8, y);
+// the row terms B'dy and C'dy^2 + log2(o / 0.99) are computed once per (splat, row) and
+// shared through a swizzle, so a pair costs 11 VALU ops:
+//   q = (A' dx + B' dy) dx + C' dy^2 + log2(o / 0.99),  alpha = 0.99 min(1, 2^q)
+// with (A', B', C') = -log2(e)/2 (A, 2B, C); the min is the exp's output clamp and the
+// factor 0.99 rides on the staged colours and the T update.  A pixel stops after the blend that
 // brings T below GS_T_EPS; the blend is branchless (a stopped pixel blends with T
 // masked to 0).  A wave leaves a batch once none of its 128 pixels is live (tested
 // every 8 splats) and the workgroup leaves the list when a barrier count finds no
@@ -41,9 +43,11 @@ __device__ __forceinline__ void gather(Staged &st, const float *__restrict__ spl
         if (idx < end) {
             const float4 *rec = reinterpret_cast<const float4 *>(splat) + (size_t)values[idx] * 4;
             const float4 r0 = rec[0], r1 = rec[1];
-            st.a[k] = make_float4(r0.x, r0.y, __log2f(r0.z), r0.w);
-            st.b[k] = r1;
-            st.c[k] = rec[2].x;
+            // alpha = GS_ALPHA_MAX min(1, 2^q): the exponent carries log2(o / GS_ALPHA_MAX) and
+            // the colours carry the factor GS_ALPHA_MAX, which leaves the clamp to the exp
+            st.a[k] = make_float4(r0.x, r0.y, splat_log2_scaled_opacity(r0.z), r0.w);
+            st.b[k] = make_float4(r1.x, r1.y, GS_ALPHA_MAX * r1.z, GS_ALPHA_MAX * r1.w);
+            st.c[k] = GS_ALPHA_MAX * rec[2].x;
         }
     }
 }
@@ -71,14 +75,14 @@ struct Pixels {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const float dx = (i ? x1 : x0) - a.x;
-            const float q = splat_exponent(dx, a.w, bdy, e);
-            const float alpha = fminf(GS_ALPHA_MAX, __builtin_amdgcn_exp2f(q));
+            // alpha / GS_ALPHA_MAX; the colours are staged times GS_ALPHA_MAX
+            const float as = splat_alpha_scaled(splat_exponent(dx, a.w, bdy, e));
             const bool live = T[i] >= GS_T_EPS;
-            const float w = (live ? T[i] : 0.0f) * alpha;
+            const float w = (live ? T[i] : 0.0f) * as;   // T alpha / GS_ALPHA_MAX
             r[i] += w * b4.z;
             g[i] += w * b4.w;
             b[i] += w * c;
-            T[i] -= w;
+            T[i] = __builtin_fmaf(-GS_ALPHA_MAX, w, T[i]);
             if (kAux) blended[i] += live ? 1u : 0u;
         }
     }

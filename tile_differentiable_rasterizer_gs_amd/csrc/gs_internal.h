@@ -181,14 +181,24 @@ void launch_fill_u32(uint32_t *dst, uint32_t value, int64_t n, hipStream_t s);
 // compositing
 // ---------------------------------------------------------------------------
 // Exponent of one splat at one pixel, in the base-2 form the splat record stores:
-// alpha = min(GS_ALPHA_MAX, 2^q) with q = (A' dx + B' dy) dx + C' dy^2 + log2(o).
-// The forward and the backward compositing kernels both build q from these two
-// helpers, so the backward recovers bit for bit the alpha the forward blended.
+// q = (A' dx + B' dy) dx + C' dy^2 + log2(o / GS_ALPHA_MAX), and
+// alpha = min(GS_ALPHA_MAX, o G) = GS_ALPHA_MAX * min(1, 2^q), the min being the
+// exp instruction's free output clamp (splat_alpha_scaled).  The forward and the
+// backward compositing kernels both build q and the clamp from these helpers, so the
+// backward recovers bit for bit the alpha the forward blended.
 __device__ __forceinline__ float splat_row_term(float dy, float Cp, float log2_o) {
     return __builtin_fmaf(dy, Cp * dy, log2_o);   // C' dy^2 + log2 o
 }
 __device__ __forceinline__ float splat_exponent(float dx, float Ap, float bdy, float row_term) {
     return __builtin_fmaf(dx, __builtin_fmaf(Ap, dx, bdy), row_term);
+}
+// alpha / GS_ALPHA_MAX = min(1, 2^q) (v_exp_f32 with its clamp bit)
+__device__ __forceinline__ float splat_alpha_scaled(float q) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(q), 0.0f, 1.0f);
+}
+// log2(o / GS_ALPHA_MAX) for o > 0, the row term's constant
+__device__ __forceinline__ float splat_log2_scaled_opacity(float o) {
+    return __log2f(o) + 0.0144995696951150766f;   // -log2(0.99)
 }
 
 struct CompositeParams {
