@@ -186,6 +186,20 @@ def test_screen_filling_gaussians(mode):
     assert (g["tile_count"] == tiles).sum() >= 5
 
 
+def test_opaque_gaussians_hit_the_alpha_cap():
+    # a third of the Gaussians fully opaque (alpha reaches the 0.99 cap near their centres,
+    # lesson section "Etape 2"), a third at 0.995, the rest random: image, final T and blend
+    # counts against the oracle's min(0.99, o G)
+    sc = scenes.random_scene(31, 1500, 1, 160, 120, log_scale_range=(-3.0, -1.8))
+    a = sc.arrays()
+    idx = np.arange(sc.n)
+    a["opacity"] = np.where(idx % 3 == 0, 1.0, np.where(idx % 3 == 1, 0.995, a["opacity"])).astype(np.float32)
+    note("opaque Gaussians at the alpha cap")
+    g, o, err = _full_check(a, 1, sc.cameras[0], bg=(0.3, 0.2, 0.1))
+    assert (g["n_blend"] > 0).mean() > 0.5
+    note(f"  image err {err:.2e}")
+
+
 def test_above_ordered_tile_limit():
     # 4200 x 4200 has 263 x 263 = 69169 tiles, above the 65536 the heaviest-first launch
     # order handles: compositing then runs in tile order; integers in full, sampled image
