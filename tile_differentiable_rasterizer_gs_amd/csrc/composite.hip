@@ -29,10 +29,12 @@ constexpr int kBatch = 256;                  // splats per LDS batch
 constexpr int kLoads = kBatch / kThreads;    // records gathered per thread per batch
 constexpr int kUnroll = 8;                   // splats between wave exit tests
 
+// A staged splat: what the per-pixel blend reads (a, c) apart from what only the per-row
+// terms need (b), so that the blend reads two LDS words per splat.
 struct Staged {
-    float4 a[kLoads];   // u, v, log2(opacity), A'
-    float4 b[kLoads];   // B', C', r, g
-    float c[kLoads];    // b
+    float4 a[kLoads];   // u, A', 0.99 r, 0.99 g
+    float4 b[kLoads];   // v, log2(o / 0.99), B', C'
+    float c[kLoads];    // 0.99 b
 };
 
 __device__ __forceinline__ void gather(Staged &st, const float *__restrict__ splat,
@@ -45,8 +47,8 @@ __device__ __forceinline__ void gather(Staged &st, const float *__restrict__ spl
             const float4 r0 = rec[0], r1 = rec[1];
             // alpha = GS_ALPHA_MAX min(1, 2^q): the exponent carries log2(o / GS_ALPHA_MAX) and
             // the colours carry the factor GS_ALPHA_MAX, which leaves the clamp to the exp
-            st.a[k] = make_float4(r0.x, r0.y, splat_log2_scaled_opacity(r0.z), r0.w);
-            st.b[k] = make_float4(r1.x, r1.y, GS_ALPHA_MAX * r1.z, GS_ALPHA_MAX * r1.w);
+            st.a[k] = make_float4(r0.x, r0.w, GS_ALPHA_MAX * r1.z, GS_ALPHA_MAX * r1.w);
+            st.b[k] = make_float4(r0.y, splat_log2_scaled_opacity(r0.z), r1.x, r1.y);
             st.c[k] = GS_ALPHA_MAX * rec[2].x;
         }
     }
@@ -66,21 +68,20 @@ struct Pixels {
     uint32_t blended[2];
 
     __device__ __forceinline__ void blend(const float4 a, const float4 b4, const float c) {
-        const float dy = y - a.y;
-        blend_row(a, b4, c, b4.x * dy, splat_row_term(dy, b4.y, a.z));
+        const float dy = y - b4.x;
+        blend_row(a, c, b4.z * dy, splat_row_term(dy, b4.w, b4.y));
     }
-    // the same, given the splat's row terms B' dy and C' dy^2 + log2 o for this lane's row
-    __device__ __forceinline__ void blend_row(const float4 a, const float4 b4, const float c, const float bdy,
-                                              const float e) {
+    // the same, given the splat's row terms B' dy and C' dy^2 + log2(o / 0.99) for this lane's row
+    __device__ __forceinline__ void blend_row(const float4 a, const float c, const float bdy, const float e) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const float dx = (i ? x1 : x0) - a.x;
             // alpha / GS_ALPHA_MAX; the colours are staged times GS_ALPHA_MAX
-            const float as = splat_alpha_scaled(splat_exponent(dx, a.w, bdy, e));
+            const float as = splat_alpha_scaled(splat_exponent(dx, a.y, bdy, e));
             const bool live = T[i] >= GS_T_EPS;
             const float w = (live ? T[i] : 0.0f) * as;   // T alpha / GS_ALPHA_MAX
-            r[i] += w * b4.z;
-            g[i] += w * b4.w;
+            r[i] += w * a.z;
+            g[i] += w * a.w;
             b[i] += w * c;
             T[i] = __builtin_fmaf(-GS_ALPHA_MAX, w, T[i]);
             if (kAux) blended[i] += live ? 1u : 0u;
@@ -139,11 +140,11 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
             // splat j + l % 8 at its own row (lanes 8r .. 8r + 7 share row r), then each lane
             // fetches splat u's terms from lane 8 (l / 8) + u of its group with a swizzle,
             // which runs on the LDS pipe; the blend itself is bound by VALU issue.
-            const float4 ra = sa[j + (lane & 7)], rb = sb[j + (lane & 7)];
-            const float rdy = px.y - ra.y;
-            const float r_bdy = rb.x * rdy, r_e = splat_row_term(rdy, rb.y, ra.z);
+            const float4 rb = sb[j + (lane & 7)];
+            const float rdy = px.y - rb.x;
+            const float r_bdy = rb.z * rdy, r_e = splat_row_term(rdy, rb.w, rb.y);
             static_assert(kUnroll == 8, "one splat per lane of an 8-lane group");
-#define GS_BLEND_ROW(u) px.blend_row(sa[j + u], sb[j + u], sc[j + u], group8_get<u>(r_bdy), group8_get<u>(r_e))
+#define GS_BLEND_ROW(u) px.blend_row(sa[j + u], sc[j + u], group8_get<u>(r_bdy), group8_get<u>(r_e))
             GS_BLEND_ROW(0);
             GS_BLEND_ROW(1);
             GS_BLEND_ROW(2);
