@@ -40,8 +40,9 @@ COMPOSITE_OPS_PER_PAIR = 11.25
 # 4, exp2, clamp: 7); 1 - alpha and its reciprocal (2); T recovery (1); dL/dalpha from
 # c . dL/dC, the carried (colour behind) . dL/dC and the background (7); the update of that
 # carried product (1); colour gradient weights (4); clamp test and opacity gradient (3);
-# dL/dQ (2); u, v, A, B, C gradients (10)
-BACKWARD_OPS_PER_PAIR = 37
+# dL/dQ (2); the moments dy S0, dy S1, dy^2 S0 that the u, v, A, B, C gradients are linear in (3;
+# the conic is applied per Gaussian, after the sum over its records)
+BACKWARD_OPS_PER_PAIR = 30
 
 
 def log(msg):

@@ -102,12 +102,15 @@ struct BwdLane {
         // dL/dQ_i = -d_i / 2 with Q = A dx^2 + 2 B dx dy + C dy^2:
         //   dL/du = A S1 + B dy S0,  dL/dv = B S1 + C dy S0,
         //   dL/dA = -S2 / 2,  dL/dB = -dy S1,  dL/dC = -dy^2 S0 / 2
+        // all linear in five moments with the Gaussian's own conic: the record carries the
+        // moments (S1, dy S0, S2, dy S1, dy^2 S0) and the per-Gaussian stage applies the conic
+        // once to their sum over the Gaussian's records
         const float dyS0 = dy * S0;
-        v[0] = __builtin_fmaf(cn.x, S1, cn.y * dyS0);
-        v[1] = __builtin_fmaf(cn.y, S1, cn.z * dyS0);
-        v[2] = -0.5f * S2;
-        v[3] = -dy * S1;
-        v[4] = -0.5f * dy * dyS0;
+        v[0] = S1;
+        v[1] = dyS0;
+        v[2] = S2;
+        v[3] = dy * S1;
+        v[4] = dy * dyS0;
         v[5] = So;
         v[6] = Sc[0];
         v[7] = Sc[1];
@@ -345,9 +348,10 @@ template <int K>
 __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad], bool live) {
     const int n = p.n;
     auto out = [live](float v) { return live ? v : 0.0f; };   // culled Gaussians may give inf or NaN
-    const float gu = sg[0], gv = sg[1], gA = sg[2], gB = sg[3], gC = sg[4];
+    // conic gradients from the summed moments (S2, dy S1, dy^2 S0); the mean gradients (from
+    // S1 and dy S0) need the conic, below
+    const float gA = -0.5f * sg[2], gB = -sg[3], gC = -0.5f * sg[4];
     p.g_opacity[g] = sg[5];
-    if (p.g_mean2d) { p.g_mean2d[g] = gu; p.g_mean2d[n + g] = gv; }
     if (p.g_conic) { p.g_conic[g] = gA; p.g_conic[n + g] = gB; p.g_conic[2 * n + g] = gC; }
     if (p.g_rgb) { p.g_rgb[g] = sg[6]; p.g_rgb[n + g] = sg[7]; p.g_rgb[2 * n + g] = sg[8]; }
 
@@ -403,6 +407,10 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     const float c = T1[0] * ST1[0] + T1[1] * ST1[1] + T1[2] * ST1[2];
     const float idet = 1.0f / (a * c - b * b);
     const float idet2 = idet * idet;
+    // dL/du = A S1 + B dy S0, dL/dv = B S1 + C dy S0 with the conic (A, B, C) = (c, -b, a) / det
+    const float cA = c * idet, cB = -b * idet, cC = a * idet;
+    const float gu = out(__builtin_fmaf(cA, sg[0], cB * sg[1])), gv = out(__builtin_fmaf(cB, sg[0], cC * sg[1]));
+    if (p.g_mean2d) { p.g_mean2d[g] = gu; p.g_mean2d[n + g] = gv; }
 
     // ---- conic (A, B, C) = (c, -b, a) / det  ->  2D covariance ----
     const float ga = (-c * c * gA + b * c * gB - b * b * gC) * idet2;
