@@ -22,9 +22,10 @@
 //      dL/du = -2 (A dx + B dy) dL/dQ,  dL/dv = -2 (B dx + C dy) dL/dQ,
 //      dL/d(A, B, C) = (dx^2, 2 dx dy, dy^2) dL/dQ.
 //    A lane sums its four pixels into three moments of d_i = alpha_i dL/dalpha_i
-//    (sum d, sum d dx, sum d dx^2) from which the conic and mean terms follow; the
-//    nine values per entry are summed over the wave by a butterfly that folds two
-//    values per level, and written as one record at the pair's position in the
+//    (sum d, sum d dx, sum d dx^2), from which the conic and mean terms follow linearly
+//    with the Gaussian's conic; five moments (times powers of dy) and the opacity and
+//    colour sums, nine values per entry, are summed over the wave through LDS and
+//    written as one record at the pair's position in the
 //    listing (Gaussian-major), so each Gaussian's records are contiguous.  Entries
 //    past the last one any pixel of the tile blended contribute nothing and get no
 //    record: the tile publishes the (depth bits, index) key of its deepest walked
@@ -60,7 +61,7 @@ struct BwdLane {
     uint32_t n[kBwdPix];   // entries the pixel blended in the forward
 
     // Entry idx of the tile list (staged f, f2, cn, cl): steps the four pixels back over it
-    // and returns the lane's nine partial sums (u, v, A, B, C, opacity, r, g, b).
+    // and returns the lane's nine partial sums (S1, dy S0, S2, dy S1, dy^2 S0, opacity, r, g, b).
     __device__ __forceinline__ void entry(const float4 f, const float4 f2, const float4 cn, const float4 cl,
                                           uint32_t idx, float v[kPairGrad]) {
         const float c[3] = {cn.w, cl.x, cl.y};
@@ -340,7 +341,7 @@ __device__ inline void sh_basis_values(float x, float y, float z, float Y[K]) {
     }
 }
 
-// Chain rule from the screen-space gradients sg (u, v, A, B, C, opacity, r, g, b) of
+// Chain rule from the summed record sg (S1, dy S0, S2, dy S1, dy^2 S0, opacity, r, g, b) of
 // Gaussian g to its parameters.  A Gaussian in no tile list (live false, sg zero) gets zero
 // gradients through the same stores, so that a wave writes each parameter plane with one
 // store instruction: two partial-wave stores to the same lines cost extra HBM writes.

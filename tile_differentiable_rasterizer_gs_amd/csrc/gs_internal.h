@@ -233,8 +233,10 @@ void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges
 // ---------------------------------------------------------------------------
 // gradients
 // ---------------------------------------------------------------------------
-// Per-pair gradient record: the contribution of one (Gaussian, tile) pair, summed
-// over the tile's pixels, to dL/d of: u, v, A, B, C (conic), opacity, r, g, b; 36 bytes.
+// Per-pair gradient record: one (Gaussian, tile) pair's sums over the tile's pixels of
+// the moments S1, dy S0, S2, dy S1, dy^2 S0 (d = alpha dL/dalpha; S0, S1, S2 = sums of d,
+// d dx, d dx^2), which dL/d(u, v, A, B, C) are linear in with the Gaussian's conic, and of
+// dL/d(opacity, r, g, b); 36 bytes.
 constexpr int kPairGrad = 9;
 constexpr int kPairStride = kPairGrad;
 
