@@ -62,9 +62,9 @@ struct BwdLane {
 
     // Entry idx of the tile list (staged f, f2, cn, cl): steps the four pixels back over it
     // and returns the lane's nine partial sums (S1, dy S0, S2, dy S1, dy^2 S0, opacity, r, g, b).
-    __device__ __forceinline__ void entry(const float4 f, const float4 f2, const float4 cn, const float4 cl,
+    __device__ __forceinline__ void entry(const float4 f, const float4 f2, const float4 cl,
                                           uint32_t idx, float v[kPairGrad]) {
-        const float c[3] = {cn.w, cl.x, cl.y};
+        const float c[3] = {cl.w, cl.x, cl.y};
         const float dy = y - f.y;
         const float bdy = f.w * dy;
         const float row = splat_row_term(dy, f2.x, f2.y);
@@ -158,8 +158,8 @@ __device__ __forceinline__ void store_record(const float v[kPairGrad], int lane,
 
 __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(CompositeBackwardParams p) {
     // staged entries: u, v, A', B' | C', log2(o / 0.99), 0.99 / o (1 when o = 0), alpha cap |
-    // A, B, C, r | g, b, value of min(1, 2^q) below which alpha is smooth (1, or inf when o = 0)
-    __shared__ float4 s_fwd[kBwdBatch], s_fwd2[kBwdBatch], s_conic[kBwdBatch];
+    // g, b, value of min(1, 2^q) below which alpha is smooth (1, or inf when o = 0), r
+    __shared__ float4 s_fwd[kBwdBatch], s_fwd2[kBwdBatch];
     __shared__ float4 s_col[kBwdBatch];
     __shared__ uint32_t s_pos[kBwdBatch];
     __shared__ __align__(16) float s_red[kPairGrad * kWave];   // store_record's transpose
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
             const uint32_t e = start + (uint32_t)(lo + lane);
             const uint32_t g = p.values[e];
             const float4 *rec = reinterpret_cast<const float4 *>(p.splat) + (size_t)g * 4;
-            const float4 r0 = rec[0], r1 = rec[1], r2 = rec[2], r3 = rec[3];
+            const float4 r0 = rec[0], r1 = rec[1];
+            const float b = reinterpret_cast<const float *>(rec)[8];
             const float o = r0.z;
             const bool zero_o = !(o > 0.0f);
             s_fwd[lane] = make_float4(r0.x, r0.y, r0.w, r1.x);
@@ -234,8 +235,7 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
             // the log term taken as 0) is G itself, never clamped
             s_fwd2[lane] = make_float4(r1.y, zero_o ? 0.0f : splat_log2_scaled_opacity(o),
                                        zero_o ? 1.0f : GS_ALPHA_MAX / o, zero_o ? 0.0f : GS_ALPHA_MAX);
-            s_conic[lane] = make_float4(r2.z, r2.w, r3.x, r1.z);
-            s_col[lane] = make_float4(r1.w, r2.x, zero_o ? INFINITY : 1.0f, 0.0f);
+            s_col[lane] = make_float4(r1.w, b, zero_o ? INFINITY : 1.0f, r1.z);
             const uint2 rc = p.rect[g];
             const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu;
             s_pos[lane] = p.pair_base[g] + (p.ellipse ? kept_index(p.ellipse[g], x0, x1, y0, tx, ty)
@@ -244,14 +244,14 @@ __global__ __launch_bounds__(kBwdThreads) void composite_backward_kernel(Composi
         __syncthreads();
         int k = cnt - 1;
         if (!holding) {   // the tile's first entry
-            px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), held);
+            px.entry(s_fwd[k], s_fwd2[k], s_col[k], (uint32_t)(lo + k), held);
             held_pos = s_pos[k];
             holding = true;
             --k;
         }
         for (; k >= 0; --k) {
             float v[kPairGrad];
-            px.entry(s_fwd[k], s_fwd2[k], s_conic[k], s_col[k], (uint32_t)(lo + k), v);
+            px.entry(s_fwd[k], s_fwd2[k], s_col[k], (uint32_t)(lo + k), v);
             store_record(held, lane, s_red, p.pair_grad + (size_t)held_pos * kPairStride);
 #pragma unroll
             for (int c = 0; c < kPairGrad; ++c) held[c] = v[c];
