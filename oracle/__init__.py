@@ -236,38 +236,54 @@ def sh_basis(direction) -> np.ndarray:
     return out
 
 
+def _splat2d_terms(means, covs, colours, opacities, depths, H, W):
+    """Per-splat quantities of the dense 2D rasteriser over an H x W grid, splats ranked by
+    (depth, index): rank, mean, colour, opacity, offsets dx [n,1,W] and dy [n,H,1] of the
+    pixel positions (x = column, y = row) from the mean, the closed-form inverse P [n,2,2] of
+    the 2x2 covariance, the density exp(-q/2) and the unclamped o * density [n, H*W]."""
+    means = np.asarray(means, np.float64).reshape(-1, 2)
+    covs = np.asarray(covs, np.float64).reshape(-1, 2, 2)
+    colours = np.asarray(colours, np.float64).reshape(-1, 3)
+    opacities = np.asarray(opacities, np.float64).reshape(-1)
+    n = len(opacities)
+    rank = np.lexsort((np.arange(n), np.asarray(depths, np.float64).reshape(-1)))
+    m, S = means[rank], covs[rank]
+    det = S[:, 0, 0] * S[:, 1, 1] - S[:, 0, 1] * S[:, 1, 0]
+    P = np.empty_like(S)
+    P[:, 0, 0], P[:, 0, 1] = S[:, 1, 1] / det, -S[:, 0, 1] / det
+    P[:, 1, 0], P[:, 1, 1] = -S[:, 1, 0] / det, S[:, 0, 0] / det
+    dx = np.arange(W, dtype=np.float64)[None, None, :] - m[:, 0, None, None]
+    dy = np.arange(H, dtype=np.float64)[None, :, None] - m[:, 1, None, None]
+    p = lambda i, j: P[:, i, j, None, None]
+    q = p(0, 0) * dx * dx + (p(0, 1) + p(1, 0)) * dx * dy + p(1, 1) * dy * dy
+    dens = np.exp(-0.5 * q).reshape(n, H * W)
+    raw = opacities[rank][:, None] * dens
+    return dict(rank=rank, col=colours[rank], dx=dx, dy=dy, P=P, dens=dens, raw=raw)
+
+
 def composite_2d(means, covs, colours, opacities, depths, image_size, bg=None):
     """Dense 2D splat rasteriser in binary64.
 
-    Lesson "3D Gaussian Splatting from scratch", sections "Étape 1: Un
-    gaussien 2D" and "Étape 2: Rasteriser à éclaboussure en 2D": every
-    Gaussian is evaluated at every pixel (x = column, y = row, integer
-    positions), alpha = clamp(opacity * density, 0, 0.99), Gaussians are taken
-    in ascending depth (ties by index) and composited front to back with the
-    running transmittance; nothing stops early.  Returns (H, W, 3) and the
-    final transmittance (H, W).
+    The lesson "3D Gaussian Splatting from scratch", sections "Étape 1: Un
+    gaussien 2D" (density of one splat at a pixel) and "Étape 2: Rasteriser à
+    éclaboussure en 2D" (every splat at every pixel, opacity times density
+    clamped to [0, 0.99], ascending depth, front-to-back blend, no early stop;
+    pixel (i, j) sits at x = j, y = i).  Written here as the closed form of the
+    blend: with the splats of pixel p ranked k = 0, 1, ... by (depth, index),
+        C(p) = sum_k c_k a_k(p) prod_{j<k} (1 - a_j(p)),   T(p) = prod_k (1 - a_k(p)),
+    a_k(p) = min(0.99, max(0, o_k exp(-q_k(p) / 2))), q_k(p) = d^T cov_k^-1 d with
+    d = p - mean_k and the 2x2 inverse in closed form.  Returns (H, W, 3) and T (H, W).
     """
-    means = np.asarray(means, np.float64)
-    covs = np.asarray(covs, np.float64)
-    colours = np.asarray(colours, np.float64)
-    opacities = np.asarray(opacities, np.float64)
     H, W = image_size
-    yy, xx = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
-    pts = np.stack([xx, yy], axis=-1).reshape(-1, 2)
-    inv = np.linalg.inv(covs) if len(covs) else covs
-    diff = pts[None, :, :] - means[:, None, :]
-    quad = np.einsum("gpi,gij,gpj->gp", diff, inv, diff)
-    alphas = np.clip(opacities[:, None] * np.exp(-0.5 * quad), 0.0, 0.99)
-    order = np.argsort(np.asarray(depths), kind="stable")
-    T = np.ones(H * W)
-    out = np.zeros((H * W, 3))
-    for g in order:
-        a = alphas[g]
-        out += (T * a)[:, None] * colours[g][None, :]
-        T = T * (1.0 - a)
+    s = _splat2d_terms(means, covs, colours, opacities, depths, H, W)
+    a = np.clip(s["raw"], 0.0, 0.99)
+    after = np.cumprod(1.0 - a, axis=0)              # transmittance behind each ranked splat
+    before = np.vstack([np.ones((1, H * W)), after[:-1]]) if len(a) else after
+    rgb = (a * before).T @ s["col"]                  # [H*W, 3]
+    T = after[-1] if len(a) else np.ones(H * W)
     if bg is not None:
-        out += T[:, None] * np.asarray(bg, np.float64)[None, :]
-    return out.reshape(H, W, 3), T.reshape(H, W)
+        rgb = rgb + T[:, None] * np.asarray(bg, np.float64)[None, :]
+    return rgb.reshape(H, W, 3), T.reshape(H, W)
 
 
 def composite_2d_backward(means, covs, colours, opacities, depths, image_size, g_image, bg=None) -> dict:
@@ -278,46 +294,44 @@ def composite_2d_backward(means, covs, colours, opacities, depths, image_size, g
         dL/dc_i = a_i T_i dL/dC,   dL/da_i = T_i (c_i - B_i) . dL/dC - T_final (bg . dL/dC) / (1 - a_i)
     a = clamp(o G, 0, 0.99) passes the derivative where 0 <= o G <= 0.99 (the clamp's
     own convention at its ends); G = exp(-q/2), q = d^T P d with d = pixel - mean and
-    P = cov^-1, so dL/dq = -a dL/da / 2, dL/dmean = -2 P d dL/dq, and with
-    M = sum_pixels dL/dq d d^T the covariance gets dL/dcov = -P M P.
+    P = cov^-1, so dL/dq = -o G dL/da / 2, dL/dmean = -(P + P^T) d dL/dq summed over
+    pixels, and with M = sum_pixels dL/dq d d^T the covariance gets dL/dcov = -P^T M P^T.
     Returns means (G,2), covs (G,2,2), colours (G,3), opacities (G,).
     """
-    means = np.asarray(means, np.float64)
-    covs = np.asarray(covs, np.float64)
-    colours = np.asarray(colours, np.float64)
-    opacities = np.asarray(opacities, np.float64)
     H, W = image_size
-    G = means.shape[0]
+    s = _splat2d_terms(means, covs, colours, opacities, depths, H, W)
+    rank, col, P, dens, raw = s["rank"], s["col"], s["P"], s["dens"], s["raw"]
+    n = len(rank)
     gC = np.asarray(g_image, np.float64).reshape(H * W, 3)
-    yy, xx = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
-    pts = np.stack([xx, yy], axis=-1).reshape(-1, 2)
-    P = np.linalg.inv(covs) if G else covs
-    diff = pts[None, :, :] - means[:, None, :]
-    quad = np.einsum("gpi,gij,gpj->gp", diff, P, diff)
-    dens = np.exp(-0.5 * quad)
-    raw = opacities[:, None] * dens
-    alphas = np.clip(raw, 0.0, 0.99)
+    dx = np.broadcast_to(s["dx"], (n, H, W)).reshape(n, H * W)
+    dy = np.broadcast_to(s["dy"], (n, H, W)).reshape(n, H * W)
+    a = np.clip(raw, 0.0, 0.99)
     smooth = (raw >= 0.0) & (raw <= 0.99)
-    order = np.argsort(np.asarray(depths), kind="stable")
-    Ts = np.zeros((G, H * W))
     T = np.ones(H * W)
-    for g in order:
-        Ts[g] = T
-        T = T * (1.0 - alphas[g])
+    Ts = np.empty((n, H * W))
+    for k in range(n):
+        Ts[k] = T
+        T = T * (1.0 - a[k])
     bg_term = np.zeros(H * W) if bg is None else T * (gC @ np.asarray(bg, np.float64))
-    out = dict(means=np.zeros((G, 2)), covs=np.zeros((G, 2, 2)), colours=np.zeros((G, 3)), opacities=np.zeros(G))
+    ranked = dict(means=np.zeros((n, 2)), covs=np.zeros((n, 2, 2)), colours=np.zeros((n, 3)), opacities=np.zeros(n))
     B = np.zeros((H * W, 3))
-    for g in order[::-1]:
-        a = alphas[g]
-        out["colours"][g] = ((a * Ts[g])[:, None] * gC).sum(axis=0)
-        d_a = Ts[g] * ((colours[g][None, :] - B) * gC).sum(axis=1) - bg_term / (1.0 - a)
-        B = a[:, None] * colours[g][None, :] + (1.0 - a)[:, None] * B
-        d_a = np.where(smooth[g], d_a, 0.0)
-        out["opacities"][g] = (dens[g] * d_a).sum()
-        d_q = -0.5 * raw[g] * d_a
-        out["means"][g] = (-2.0 * d_q[:, None] * (diff[g] @ P[g].T)).sum(axis=0)
-        M = np.einsum("p,pi,pj->ij", d_q, diff[g], diff[g])
-        out["covs"][g] = -P[g] @ M @ P[g]
+    for k in range(n - 1, -1, -1):
+        ranked["colours"][k] = (a[k] * Ts[k]) @ gC
+        d_a = Ts[k] * ((col[k][None, :] - B) * gC).sum(axis=1) - bg_term / (1.0 - a[k])
+        B = a[k][:, None] * col[k][None, :] + (1.0 - a[k])[:, None] * B
+        d_a = np.where(smooth[k], d_a, 0.0)
+        ranked["opacities"][k] = dens[k] @ d_a
+        d_q = -0.5 * raw[k] * d_a
+        Ps = P[k] + P[k].T
+        ranked["means"][k, 0] = -(d_q * (Ps[0, 0] * dx[k] + Ps[0, 1] * dy[k])).sum()
+        ranked["means"][k, 1] = -(d_q * (Ps[1, 0] * dx[k] + Ps[1, 1] * dy[k])).sum()
+        M = np.array([[d_q @ (dx[k] * dx[k]), d_q @ (dx[k] * dy[k])],
+                      [d_q @ (dy[k] * dx[k]), d_q @ (dy[k] * dy[k])]])
+        ranked["covs"][k] = -P[k].T @ M @ P[k].T
+    out = {}
+    for key, v in ranked.items():
+        out[key] = np.zeros_like(v)
+        out[key][rank] = v
     return out
 
 

@@ -293,6 +293,82 @@ def test_tile_rect_brute_force():
     _ = rng
 
 
+def _anisotropic_sample(n=2400, seed=12):
+    """Rotated Gaussians with per-axis log-scales far apart (ratios up to e^4 per axis), seen by
+    an off-axis camera, so that the projected covariances have b != 0 and a != c."""
+    rng = np.random.default_rng(seed)
+    means = rng.uniform(-1.2, 1.2, (n, 3))
+    q = rng.standard_normal((n, 4))
+    ls = np.c_[rng.uniform(-5.0, -1.5, n), rng.uniform(-5.0, -1.5, n), rng.uniform(-5.0, -1.5, n)]
+    arr = _scene_arrays(means, q, ls, np.full(n, 0.5), np.ones((n, 1, 3)))
+    cam = scenes.look_at_camera((1.1, -0.8, -4.5), (0.1, 0.2, 0.0), 560.0, 640, 480)
+    p = oracle.preprocess(arr, 0, cam)
+    vis = np.nonzero(p["tile_count"] > 0)[0]
+    return p, cam, vis
+
+
+def _cov2d64(p, g):
+    a, b, c = (float(x) for x in p["cov2d"][:, g])
+    return np.array([[a, b], [b, c]])
+
+
+def test_anisotropic_radius_is_three_sigma_of_largest_eigenvalue():
+    """The lesson's "L'étape de projection": the 2D footprint is an ellipse whose axes are the
+    eigenvectors of Sigma'; the 3-sigma screen radius is ceil(3 sqrt(lambda_max)).  Reference:
+    numpy's symmetric eigensolver in binary64 on the (separately pinned) 2D covariance; values
+    of 3 sqrt(lambda_max) within 1e-4 (relative 1e-5) of an integer are skipped, since binary32
+    rounding may decide them either way."""
+    p, _, vis = _anisotropic_sample()
+    checked = 0
+    wrong = dict(lam_min=0, no_b2=0, two_sigma=0)
+    aniso = 0
+    for g in vis:
+        S = _cov2d64(p, g)
+        lo, hi = np.linalg.eigvalsh(S)
+        x = 3.0 * math.sqrt(hi)
+        if abs(x - round(x)) < 1e-4 + 1e-5 * x:
+            continue
+        ref = math.ceil(x)
+        assert p["radius"][g] == ref, (g, p["radius"][g], ref, S)
+        checked += 1
+        aniso += hi > 4.0 * lo and abs(S[0, 1]) > 0.1 * math.sqrt(S[0, 0] * S[1, 1])
+        # plausible slips in the radius line that this reference tells apart
+        a, b, c = S[0, 0], S[0, 1], S[1, 1]
+        wrong["lam_min"] += math.ceil(3.0 * math.sqrt(lo)) != ref
+        wrong["no_b2"] += math.ceil(3.0 * math.sqrt(0.5 * (a + c) + abs(0.5 * (a - c)))) != ref
+        wrong["two_sigma"] += math.ceil(2.0 * math.sqrt(hi)) != ref
+    assert checked >= 1000, checked
+    assert aniso >= 300, aniso
+    for k, v in wrong.items():
+        assert v >= 0.3 * checked, (k, v, checked)
+
+
+def test_tiles_outside_the_square_miss_the_ellipse():
+    """Containment: every tile of the grid just outside a Gaussian's tile rectangle has a
+    pixel-centre box on which the quadratic form d^T Sigma'^-1 d stays above 9 (binary64
+    minimum over the box), i.e. the square loses no part of the 3-sigma ellipse; and the
+    rectangle holds the tile of the projected mean when that lies on the image."""
+    from test_oracle_ellipse import _qmin_box
+
+    p, cam, vis = _anisotropic_sample(n=1200, seed=13)
+    tx, ty = oracle.tiles_for(cam)
+    ring_tiles = 0
+    for g in vis:
+        u, v = (float(x) for x in p["mean2d"][:, g])
+        a, b, c = (float(x) for x in p["cov2d"][:, g])
+        x0, x1, y0, y1 = (int(x) for x in p["rect"][:, g])
+        for yy in range(max(y0 - 1, 0), min(y1 + 1, ty)):
+            for xx in range(max(x0 - 1, 0), min(x1 + 1, tx)):
+                if x0 <= xx < x1 and y0 <= yy < y1:
+                    continue
+                q = _qmin_box(u, v, a, b, c, 16 * xx, 16 * xx + 15, 16 * yy, 16 * yy + 15)
+                assert q > 9.0, (g, xx, yy, q)
+                ring_tiles += 1
+        if 0 <= u < cam["width"] and 0 <= v < cam["height"]:
+            assert x0 <= int(u // 16) < x1 and y0 <= int(v // 16) < y1
+    assert ring_tiles > 5000, ring_tiles
+
+
 # --------------------------------------------------------------------------
 # Binning
 # --------------------------------------------------------------------------
@@ -386,6 +462,24 @@ def test_splat2d_worked_case_numpy_oracle():
     img, _ = oracle.composite_2d(means, covs, cols, [0.5, 0.5], [two["front"]["depth"], two["back"]["depth"]],
                                  (H, W))
     np.testing.assert_allclose(img[c["y"], c["x"]], two["swapped_depths_centre_rgb"], atol=1e-12)
+
+
+def test_splat2d_opacity_limits():
+    """The lesson's "Étape 2" clamps opacity x density to [0, 0.99]: an opaque splat at its own
+    (integer) mean leaves 1 % of the light through, an opacity-0 splat changes nothing, and a
+    splat with opacity 1 in front of another shows 0.99 of its colour plus 0.01 of the back."""
+    H, W = 12, 10
+    mean = np.array([[5.0, 7.0]])
+    cov = np.array([[[1.5, 0.4], [0.4, 0.9]]])
+    img, T = oracle.composite_2d(mean, cov, [[1.0, 0.5, 0.25]], [1.0], [0.3], (H, W))
+    np.testing.assert_allclose(img[7, 5], [0.99, 0.495, 0.2475], rtol=0, atol=1e-15)
+    assert abs(T[7, 5] - 0.01) < 1e-15
+    img0, T0 = oracle.composite_2d(mean, cov, [[1.0, 0.5, 0.25]], [0.0], [0.3], (H, W), bg=(0.2, 0.3, 0.4))
+    assert np.all(T0 == 1.0) and np.all(img0 == np.array([0.2, 0.3, 0.4]))
+    means = np.array([[5.0, 7.0], [5.0, 7.0]])
+    covs = np.concatenate([cov, cov])
+    img2, _ = oracle.composite_2d(means, covs, [[0.0, 0.0, 1.0], [1.0, 0.0, 0.0]], [0.5, 1.0], [0.9, 0.1], (H, W))
+    np.testing.assert_allclose(img2[7, 5], [0.99, 0.0, 0.01 * 0.5], rtol=0, atol=1e-15)
 
 
 def test_splat2d_worked_case_through_3d_oracle():
