@@ -166,7 +166,11 @@ typedef enum {
        below o exp(-9/2) per pixel).  Per tile row the kept tiles are one span: the
        ellipse cut at height dy is centred at (b/c) dy with half-width
        sqrt((det/c)(9 - dy^2/c)); its ends peak at dy = +-3b/sqrt(a) clamped to the
-       row's band.  Evaluated in binary32 in a fixed order, so counts and keys are exact. */
+       row's band.  Evaluated in binary32 in a fixed order, so counts and keys are exact.
+       The pair listing checks on the device that each Gaussian's spans add up to its tile
+       count and stays inside its rectangle either way; a mismatch (never seen) raises a
+       flag that the next gs_bin_and_sort / gs_render on the context returns as
+       GS_ERR_DEVICE. */
     GS_TILE_ELLIPSE = 1
 } gs_tile_test;
 

@@ -86,3 +86,44 @@ def check_binning(g: dict, ob: dict, check_keys: bool = True):
 
 def image_error(g_img, o_img):
     return float(np.abs(g_img.astype(np.float64) - o_img).max()) if g_img.size else 0.0
+
+
+def tile_pixels(cam: dict, tiles) -> np.ndarray:
+    """Flat indices y*W+x of every image pixel of the given 16x16 tiles (partial tiles clipped)."""
+    W, H = cam["width"], cam["height"]
+    tx_n = (W + 15) // 16
+    out = []
+    for t in tiles:
+        tx, ty = int(t) % tx_n, int(t) // tx_n
+        ys = np.arange(16 * ty, min(16 * ty + 16, H))
+        xs = np.arange(16 * tx, min(16 * tx + 16, W))
+        out.append((ys[:, None] * W + xs[None, :]).ravel())
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def bottom_tile_row_pixels(cam: dict) -> np.ndarray:
+    """Every pixel of the last tile row (partial when the height is not a multiple of 16)."""
+    W, H = cam["width"], cam["height"]
+    y0 = 16 * ((H - 1) // 16)
+    return np.arange(y0 * W, H * W, dtype=np.int64)
+
+
+def per_tile_counts(o: dict) -> np.ndarray:
+    """Pairs per tile under the square rule, counted independently of the binning: every
+    visible Gaussian adds one to each tile of its rectangle (2D difference array)."""
+    tx, ty = o["tiles"]
+    vis = o["tile_count"] > 0
+    x0, x1, y0, y1 = (o["rect"][i][vis].astype(np.int64) for i in range(4))
+    D = np.zeros((ty + 1, tx + 1), np.int64)
+    np.add.at(D, (y0, x0), 1)
+    np.add.at(D, (y0, x1), -1)
+    np.add.at(D, (y1, x0), -1)
+    np.add.at(D, (y1, x1), 1)
+    return D.cumsum(0).cumsum(1)[:ty, :tx].reshape(-1)
+
+
+def ranges_from_counts(per_tile: np.ndarray) -> np.ndarray:
+    """[tiles][2] half-open ranges of a list sorted by tile: (0, 0) for empty tiles."""
+    end = np.cumsum(per_tile)
+    start = end - per_tile
+    return np.where(per_tile[:, None] > 0, np.stack([start, end], 1), 0).astype(np.int64)

@@ -240,3 +240,27 @@ def test_backward_headline_scene_sampled_pixels():
     note(f"headline: {int(touched.sum())} Gaussians reach the sampled pixels")
     assert touched.sum() > 100
     check_grads(g, o, "headline sampled")
+
+
+@pytest.mark.parametrize("tile_test", [0, 1])
+def test_backward_elongated_footprints(tile_test):
+    # thin, strongly anisotropic Gaussians (one axis up to e^5 longer than the others): the
+    # 2D covariance's determinant cancels most, so the conic the per-Gaussian stage applies to
+    # the summed moments must still give the forward's gradients, under both tile rules
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    rng = np.random.default_rng(15)
+    n = 600
+    sc = scenes.random_scene(16, n, 1, 180, 130)
+    a = sc.arrays()
+    a["log_scale"] = np.ascontiguousarray(np.c_[rng.uniform(-3.0, -0.8, n), rng.uniform(-6.0, -4.0, n),
+                                                rng.uniform(-6.0, -4.0, n)].T.astype(np.float32))
+    cam = sc.cameras[0]
+    gimg = _cotangent(cam, 11)
+    bg = (0.1, 0.3, -0.2)
+    note(f"backward elongated tile_test={tile_test}")
+    r = binding.Rasterizer(emit_keys=False, tile_test=tile_test)
+    g = gpu_grads(a, 1, cam, gimg, bg=bg, rast=r)
+    r.close()
+    o = oracle.render_backward(a, 1, cam, gimg, bg=bg, tile_test=tile_test)
+    check_grads(g, o, f"elongated tile_test={tile_test}")

@@ -12,7 +12,8 @@ import pytest
 import oracle
 from tile_differentiable_rasterizer_gs_amd import scenes
 
-from gs_util import IMAGE_TOL, check_binning, check_preprocess, gpu_run, image_error, note
+from gs_util import (IMAGE_TOL, bottom_tile_row_pixels, check_binning, check_preprocess, gpu_run, image_error,
+                     note, per_tile_counts, ranges_from_counts, tile_pixels)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,12 +84,20 @@ def test_c2_full_ints_sampled_image(mode):
     note(f"c2 mode={mode} pairs={g['num_dups']} sampled err {err:.2e}")
 
 
+def _heavy_tiles(o, k=4):
+    return np.argsort(per_tile_counts(o), kind="stable")[::-1][:k]
+
+
 def test_c3_headline_full_ints_sampled_image():
+    # integers in full; image on random pixels, every pixel of the four longest tile lists
+    # and every pixel of the half-height bottom tile row
     s = scenes.make_scene("c3_1m_sh3_1080p")
     cam = s.cameras[0]
     rng = np.random.default_rng(1)
-    pix = rng.choice(cam["width"] * cam["height"], 1500, replace=False)
-    note("c3 depth-first")
+    o = oracle.preprocess(s.arrays(), 3, cam)
+    pix = np.unique(np.concatenate([rng.choice(cam["width"] * cam["height"], 1500, replace=False),
+                                    tile_pixels(cam, _heavy_tiles(o)), bottom_tile_row_pixels(cam)]))
+    note(f"c3 depth-first ({pix.size} pixels)")
     g, _, err = _full_check(s.arrays(), 3, cam, mode=0, full_image=False, pixels=pix)
     note(f"c3 pairs={g['num_dups']} sampled err {err:.2e}")
 
@@ -346,7 +355,7 @@ def _tile_list_oracle(o, tile, tiles_x):
     return hit[order].astype(np.uint32)
 
 
-def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0):
+def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0, heavy=4, bottom_row=False):
     import torch
 
     from tile_differentiable_rasterizer_gs_amd import binding
@@ -365,10 +374,10 @@ def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0):
              rect=pt["rect"].cpu().numpy().view(np.uint16).astype(np.int32), splat=pt["splat"].cpu().numpy())
     check_preprocess(g, o)
     assert bn.num_dups == int(o["tile_count"].astype(np.int64).sum())
-    # ranges tile the list in order and their lengths are the per-tile pair counts
-    nonempty = ranges[:, 1] > ranges[:, 0]
-    assert np.all(ranges[nonempty, 0][1:] == ranges[nonempty, 1][:-1])
-    assert ranges[nonempty, 0][0] == 0 and ranges[nonempty, 1][-1] == bn.num_dups
+    # every tile's range: the list is sorted by tile, so the ranges follow from per-tile pair
+    # counts, taken here from the oracle's rectangles alone (not from its binning)
+    per_tile = per_tile_counts(o)
+    assert np.array_equal(ranges.astype(np.int64), ranges_from_counts(per_tile)), "tile ranges"
     rng = np.random.default_rng(seed)
     lens = ranges[:, 1].astype(np.int64) - ranges[:, 0]
     tiles = np.concatenate([rng.choice(len(lens), n_tiles, replace=False), [int(np.argmax(lens))]])
@@ -377,7 +386,12 @@ def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0):
         ref = _tile_list_oracle(o, int(t), bn.tiles_x)
         got = values[lo:hi].cpu().numpy().view(np.uint32)
         assert np.array_equal(got, ref), f"tile {t}"
-    pix = rng.choice(cam["width"] * cam["height"], n_pix, replace=False)
+    pix = [rng.choice(cam["width"] * cam["height"], n_pix, replace=False)]
+    if heavy:
+        pix.append(tile_pixels(cam, np.argsort(per_tile, kind="stable")[::-1][:heavy]))
+    if bottom_row:
+        pix.append(bottom_tile_row_pixels(cam))
+    pix = np.unique(np.concatenate(pix))
     oimg, _, _ = oracle.composite(o, cam, pixels=pix)
     err = image_error(img.cpu().numpy().reshape(-1, 3)[pix], oimg)
     assert err <= IMAGE_TOL, f"sampled image err {err}"
@@ -388,7 +402,7 @@ def _large_check(s, cam, n_tiles=24, n_pix=600, seed=0, mode=0):
 def test_c4_5m_large_gaussians_sampled():
     s = scenes.make_scene("c4_5m_sh3_1080p_large")
     note("c4 5M")
-    m, err = _large_check(s, s.cameras[0], n_tiles=16, n_pix=300)
+    m, err = _large_check(s, s.cameras[0], n_tiles=16, n_pix=300, bottom_row=True)
     note(f"c4 pairs={m} sampled err {err:.2e}")
     assert m > 10 ** 8
 
@@ -438,3 +452,35 @@ def test_views_in_flight_on_separate_contexts_match_sequential():
             assert torch.equal(outs[i], ref[i]), (rep, i)
     for r, _ in lanes:
         r.close()
+
+
+def test_c5_views_in_flight_match_oracle():
+    # the 3M-Gaussian orbit rendered as the benchmark's pipelined mode does: three contexts, one
+    # stream each, views issued round-robin and left in flight together; every frame's image
+    # against the oracle on random pixels and all pixels of its four longest tile lists
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    s = scenes.make_scene("c5_3m_sh3_1080p_orbit32")
+    views = [0, 5, 11, 16, 27, 31]
+    dev = binding.gaussians_to_device(s.arrays())
+    lanes = [(binding.Rasterizer(emit_keys=False), torch.cuda.Stream()) for _ in range(3)]
+    H, W = s.cameras[0]["height"], s.cameras[0]["width"]
+    outs = [torch.empty((H, W, 3), device="cuda") for _ in views]
+    note("c5 views in flight")
+    for i, k in enumerate(views):
+        r, st = lanes[i % 3]
+        r.render(dev, 3, s.cameras[k], out=outs[i], stream=st)
+    torch.cuda.synchronize()
+    for r, _ in lanes:
+        r.close()
+    rng = np.random.default_rng(40)
+    for i, k in enumerate(views):
+        cam = s.cameras[k]
+        o = oracle.preprocess(s.arrays(), 3, cam)
+        pix = np.unique(np.concatenate([rng.choice(W * H, 300, replace=False), tile_pixels(cam, _heavy_tiles(o))]))
+        oimg, _, _ = oracle.composite(o, cam, pixels=pix)
+        err = image_error(outs[i].cpu().numpy().reshape(-1, 3)[pix], oimg)
+        note(f"c5 view {k} in flight: sampled err {err:.2e}")
+        assert err <= IMAGE_TOL, (k, err)

@@ -607,3 +607,22 @@ def test_early_stop_error_bound():
     assert np.all(cnt_e <= cnt_x)
     stopped = cnt_e < cnt_x
     assert stopped.any() and np.all(T_e[stopped] < 1e-4)
+
+
+def test_ranges_equal_per_tile_rectangle_counts():
+    """The binning's tile ranges follow from per-tile counts built from the rectangles alone
+    (a 2D difference array), at scales beyond the brute-force pair enumeration above."""
+    from gs_util import per_tile_counts, ranges_from_counts, tile_pixels, bottom_tile_row_pixels
+
+    for seed, (w, h) in enumerate([(203, 141), (320, 240), (97, 33)]):
+        s = scenes.random_scene(200 + seed, 3000, 0, w, h, log_scale_range=(-4.0, -1.0))
+        cam = s.cameras[0]
+        p = oracle.preprocess(s.arrays(), 0, cam)
+        b = oracle.bin_pairs(p, want_unsorted=False)
+        assert np.array_equal(b["ranges"].astype(np.int64), ranges_from_counts(per_tile_counts(p)))
+        tx, _ = oracle.tiles_for(cam)
+        last = ((h - 1) // 16) * tx + tx - 1          # the bottom-right (partial) tile
+        px = tile_pixels(cam, [0, last])
+        assert px.size == 256 + (16 if w % 16 == 0 else w % 16) * (16 if h % 16 == 0 else h % 16)
+        assert np.all(px < w * h) and np.unique(px).size == px.size
+        assert bottom_tile_row_pixels(cam).size == w * (h - 16 * ((h - 1) // 16))

@@ -72,7 +72,8 @@ struct gs_context {
     int32_t s2_height = 0, s2_width = 0;
     const float *s2_means = nullptr, *s2_depths = nullptr;
 
-    unsigned long long *host_total = nullptr;   // pinned, host-coherent: the pair count of each frame
+    unsigned long long *host_total = nullptr;   // pinned, host-coherent: [0] the pair count of each frame,
+                                                // [1] fault bits raised by the exact-footprint listing
     unsigned long long *host_total_dev = nullptr;   // its device address (the scan stores the count there)
 
     // last gs_preprocess
@@ -276,13 +277,14 @@ gs_status gs_context_create(gs_context **out, int device) {
     ctx->device = device;
     DeviceScope scope(device);
     if (scope.status != hipSuccess ||
-        hipHostMalloc((void **)&ctx->host_total, sizeof(unsigned long long),
+        hipHostMalloc((void **)&ctx->host_total, 2 * sizeof(unsigned long long),
                       hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess ||
         hipHostGetDevicePointer((void **)&ctx->host_total_dev, ctx->host_total, 0) != hipSuccess) {
         (void)hipGetLastError();
         delete ctx;
         return GS_ERR_DEVICE;
     }
+    ctx->host_total[1] = 0;
     *out = ctx;
     return GS_OK;
 }
@@ -470,6 +472,7 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     if (ctx->tile_test_used == GS_TILE_ELLIPSE) {
         d.ellipse = as<EllipseRec>(ctx->ellipse);
         d.tile_count = pr->tile_count;
+        d.fault = ctx->host_total_dev + 1;
     }
     RangesParams r{};
     r.num_dups = d_total;
@@ -609,6 +612,12 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             if (published == kNoCount) return fail(ctx, GS_ERR_DEVICE, "the pair count did not reach the host");
         }
         M = (int64_t)published;
+        // listings enqueued before this frame's count arrived have run (same stream)
+        if (__atomic_load_n(ctx->host_total + 1, __ATOMIC_ACQUIRE) != 0) {
+            __atomic_store_n(ctx->host_total + 1, 0ull, __ATOMIC_RELEASE);
+            return fail(ctx, GS_ERR_DEVICE, "the exact-footprint pair listing of an earlier frame met a Gaussian "
+                                            "whose row spans disagree with its tile count");
+        }
         if (M > ctx->max_dups)
             return fail(ctx, GS_ERR_CAPACITY, "%lld (Gaussian, tile) pairs exceed the cap of %lld", (long long)M,
                         (long long)ctx->max_dups);

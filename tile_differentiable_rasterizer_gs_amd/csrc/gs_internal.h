@@ -154,6 +154,8 @@ struct DuplicateParams {
     uint16_t *tile_keys16;       // ... or as 16 bits (at most 65536 tiles); entry count multiple of 8 per block
     uint32_t *values;            // Gaussian index
     const EllipseRec *ellipse;   // null, or the exact-footprint rule: only the row spans are listed
+    unsigned long long *fault;   // with ellipse: host-coherent word, bit 0 set (system scope) when a
+                                 // Gaussian's row spans do not add up to its tile count
     const uint32_t *tile_count;  // [n] (needed with ellipse)
     uint32_t *clear;             // zeroed by the partition kernel ([clear_words]; the tile ranges)
     int64_t clear_words;

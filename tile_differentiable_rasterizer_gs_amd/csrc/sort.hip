@@ -394,13 +394,24 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
     load_rank(i, g, off, rc, dbits);
     uint32_t tiles[kItems], gs[kItems], dbs[kItems];
     if (p.ellipse) {
-        // exact footprint: the kept tiles of each row form one span; walk the spans
+        // exact footprint: the kept tiles of each row form one span; walk the spans.  The
+        // spans of a rank add up to its tile count (the preprocess summed the same spans),
+        // so no walk leaves its rectangle or the staged ranks; should one ever try, the
+        // thread repeats its last pair, raises the fault bit and stops walking.
         EllipseRec E = p.ellipse[g];
         uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y1 = rc.y >> 16;
         uint32_t ty = rc.y & 0xffffu, sa, sb;
         uint32_t j = (uint32_t)e0 - off;
+        bool broken = false;
         row_span(E, x0, x1, ty, sa, sb);
         while (j >= sb - sa) {
+            if (ty + 1 >= y1) {
+                broken = true;
+                j = 0;
+                sa = x0;
+                sb = x0 + 1;
+                break;
+            }
             j -= sb - sa;
             row_span(E, x0, x1, ++ty, sa, sb);
         }
@@ -409,9 +420,13 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             tiles[k] = ty * (uint32_t)p.tiles_x + tx;
             gs[k] = g;
             dbs[k] = dbits;
-            if (++tx == sb && k + 1 < n_here) {
+            if (++tx == sb && k + 1 < n_here && !broken) {
                 do {   // next row with a span, else the next rank with pairs
                     if (++ty == y1) {
+                        if (i >= last) {
+                            broken = true;
+                            break;
+                        }
                         i = next_rank(i, (uint32_t)e0 + k + 1);
                         load_rank(i, g, off, rc, dbits);
                         E = p.ellipse[g];
@@ -424,7 +439,12 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
                 } while (sa == sb);
                 tx = sa;
             }
+            if (broken) {   // repeat the last pair
+                ty = tiles[k] / (uint32_t)p.tiles_x;
+                tx = tiles[k] - ty * (uint32_t)p.tiles_x;
+            }
         }
+        if (broken) __hip_atomic_fetch_or(p.fault, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
     uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu, h = (rc.y >> 16) - y0;
     uint32_t j = (uint32_t)e0 - off;
