@@ -65,7 +65,7 @@ struct gs_context {
     // per-tile
     DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
-    DeviceBuffer pair_base, pair_grad, scan_total;
+    DeviceBuffer pair_base, pair_grad, scan_total, fix_list, fix_count;
     // 2D splat rasteriser
     DeviceBuffer s2_order, s2_rec, s2_trans, s2_partial;
     int64_t s2_n = -1;
@@ -298,7 +298,8 @@ void gs_context_destroy(gs_context *ctx) {
                            &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
                            &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
                            &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
-                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->tile_order, &ctx->ellipse,
+                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count,
+                           &ctx->tile_order, &ctx->ellipse,
                            &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->s2_order,
                            &ctx->s2_rec, &ctx->s2_trans, &ctx->s2_partial};
     for (DeviceBuffer *b : all)
@@ -742,6 +743,8 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     const int64_t M = ctx->num_dups;
     GS_TRY(ensure(ctx, ctx->pair_grad, (size_t)(M > 0 ? M : 1) * kPairStride * sizeof(float)));
     GS_TRY(ensure(ctx, ctx->scan_total, sizeof(unsigned long long)));
+    GS_TRY(ensure(ctx, ctx->fix_list, nn * kFixStride * sizeof(float)));
+    GS_TRY(ensure(ctx, ctx->fix_count, (nn + 63) / 64 * sizeof(uint32_t)));
     // Gaussian g's records start at pair_base[g] = sum of tile_count over indices below g:
     // key64 mode listed the pairs in that order, depth-first mode needs its own prefix sum
     const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
@@ -818,6 +821,8 @@ gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *c
     q.ellipse = ell;
     q.tiles_x = ctx->tiles_x;
     q.pair_grad = as<float>(ctx->pair_grad);
+    q.fix_list = as<float>(ctx->fix_list);
+    q.fix_count = as<uint32_t>(ctx->fix_count);
     q.g_mean = grads->mean;
     q.g_quat = grads->quat;
     q.g_log_scale = grads->log_scale;

@@ -341,42 +341,53 @@ __device__ inline void sh_basis_values(float x, float y, float z, float Y[K]) {
     }
 }
 
-// Chain rule from the summed record sg (S1, dy S0, S2, dy S1, dy^2 S0, opacity, r, g, b) of
-// Gaussian g to its parameters.  A Gaussian in no tile list (live false, sg zero) gets zero
-// gradients through the same stores, so that a wave writes each parameter plane with one
-// store instruction: two partial-wave stores to the same lines cost extra HBM writes.
-template <int K>
-__device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad], bool live) {
-    const int n = p.n;
-    auto out = [live](float v) { return live ? v : 0.0f; };   // culled Gaussians may give inf or NaN
-    // conic gradients from the summed moments (S2, dy S1, dy^2 S0); the mean gradients (from
-    // S1 and dy S0) need the conic, below
-    const float gA = -0.5f * sg[2], gB = -sg[3], gC = -0.5f * sg[4];
-    p.g_opacity[g] = sg[5];
-    if (p.g_conic) { p.g_conic[g] = gA; p.g_conic[n + g] = gB; p.g_conic[2 * n + g] = gC; }
-    if (p.g_rgb) { p.g_rgb[g] = sg[6]; p.g_rgb[n + g] = sg[7]; p.g_rgb[2 * n + g] = sg[8]; }
+// Activated scale in the chain's precision: binary32 expf, or the binary64 exp.
+__device__ __forceinline__ float chain_scale(float ls, float) { return expf(ls); }
+__device__ __forceinline__ double chain_scale(float ls, double) { return exp((double)ls); }
 
-    const float *W = p.R;
+// Chain rule of one Gaussian, from its summed record (S1, dy S0, S2, dy S1, dy^2 S0,
+// opacity, r, g, b) to its parameters.  A Gaussian in no tile list (live false, sums zero)
+// gets zero gradients through the same stores, so that a wave writes each parameter plane
+// with one store instruction: two partial-wave stores to the same lines cost extra HBM
+// writes.
+//
+// Geometric part: the moments m (S1, dy S0, S2, dy S1, dy^2 S0) through the conic, the 2D
+// covariance, Sigma and J to the scales, rotation and mean; writes dL/d(u, v) (optional
+// plane), dL/dlog_scale and dL/dquat, returns the mean's share in gmu and a c / det.
+// Real is the precision of the chain.  For a thin footprint the derivative of the conic
+// (an inverse) and of Sigma' = T Sigma T^T cancel in proportion to the 2D covariance's
+// condition: in binary32 that rounding alone outgrew a thin axis' log-scale gradient once
+// a c / det passed ~100, so the binary32 pass queues such Gaussians for a binary64 one.
+template <typename Real>
+__device__ inline float geometric_vjp(const GaussianBackwardParams &p, int g, const float m[5], bool live,
+                                      float gmu[3]) {
+    const int n = p.n;
+    auto out = [live](Real v) { return live ? (float)v : 0.0f; };   // culled Gaussians may give inf or NaN
+    const float gA = -0.5f * m[2], gB = -m[3], gC = -0.5f * m[4];   // dL/d(A, B, C) of the conic
     const float mu[3] = {p.mean[g], p.mean[n + g], p.mean[2 * n + g]};
-    const float q4[4] = {p.quat[g], p.quat[n + g], p.quat[2 * n + g], p.quat[3 * n + g]};
+    Real W[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) W[i] = (Real)p.R[i];
+    const Real q4[4] = {p.quat[g], p.quat[n + g], p.quat[2 * n + g], p.quat[3 * n + g]};
+    const Real one = 1, two = 2, half = 0.5;
 
     // ---- forward quantities ----
-    const float qn = sqrtf(q4[0] * q4[0] + q4[1] * q4[1] + q4[2] * q4[2] + q4[3] * q4[3]);
-    const float qw = q4[0] / qn, qx = q4[1] / qn, qy = q4[2] / qn, qz = q4[3] / qn;
-    float R[3][3];
-    R[0][0] = 1.0f - 2.0f * (qy * qy + qz * qz);
-    R[0][1] = 2.0f * (qx * qy - qw * qz);
-    R[0][2] = 2.0f * (qx * qz + qw * qy);
-    R[1][0] = 2.0f * (qx * qy + qw * qz);
-    R[1][1] = 1.0f - 2.0f * (qx * qx + qz * qz);
-    R[1][2] = 2.0f * (qy * qz - qw * qx);
-    R[2][0] = 2.0f * (qx * qz - qw * qy);
-    R[2][1] = 2.0f * (qy * qz + qw * qx);
-    R[2][2] = 1.0f - 2.0f * (qx * qx + qy * qy);
-    float s[3];
+    const Real qn = sqrt(q4[0] * q4[0] + q4[1] * q4[1] + q4[2] * q4[2] + q4[3] * q4[3]);
+    const Real qw = q4[0] / qn, qx = q4[1] / qn, qy = q4[2] / qn, qz = q4[3] / qn;
+    Real R[3][3];
+    R[0][0] = one - two * (qy * qy + qz * qz);
+    R[0][1] = two * (qx * qy - qw * qz);
+    R[0][2] = two * (qx * qz + qw * qy);
+    R[1][0] = two * (qx * qy + qw * qz);
+    R[1][1] = one - two * (qx * qx + qz * qz);
+    R[1][2] = two * (qy * qz - qw * qx);
+    R[2][0] = two * (qx * qz - qw * qy);
+    R[2][1] = two * (qy * qz + qw * qx);
+    R[2][2] = one - two * (qx * qx + qy * qy);
+    Real s[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) s[j] = expf(p.log_scale[j * n + g]);
-    float M[3][3], S[3][3];
+    for (int j = 0; j < 3; ++j) s[j] = chain_scale(p.log_scale[j * n + g], Real(0));
+    Real M[3][3], S[3][3];
 #pragma unroll
     for (int i = 0; i < 3; ++i)
 #pragma unroll
@@ -385,55 +396,59 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int j = 0; j < 3; ++j) S[i][j] = M[i][0] * M[j][0] + M[i][1] * M[j][1] + M[i][2] * M[j][2];
-    float t[3];
+    Real t[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) t[i] = W[3 * i] * mu[0] + W[3 * i + 1] * mu[1] + W[3 * i + 2] * mu[2] + p.t[i];
-    const float iz = 1.0f / t[2];
-    const float j00 = p.fx * iz, j02 = -p.fx * t[0] * iz * iz;
-    const float j11 = p.fy * iz, j12 = -p.fy * t[1] * iz * iz;
-    float T0[3], T1[3];
+    for (int i = 0; i < 3; ++i)
+        t[i] = W[3 * i] * (Real)mu[0] + W[3 * i + 1] * (Real)mu[1] + W[3 * i + 2] * (Real)mu[2] + (Real)p.t[i];
+    const Real fx = p.fx, fy = p.fy;
+    const Real iz = one / t[2];
+    const Real j00 = fx * iz, j02 = -fx * t[0] * iz * iz;
+    const Real j11 = fy * iz, j12 = -fy * t[1] * iz * iz;
+    Real T0[3], T1[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         T0[k] = j00 * W[k] + j02 * W[6 + k];
         T1[k] = j11 * W[3 + k] + j12 * W[6 + k];
     }
-    float ST0[3], ST1[3];   // Sigma T0, Sigma T1
+    Real ST0[3], ST1[3];   // Sigma T0, Sigma T1
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         ST0[i] = S[i][0] * T0[0] + S[i][1] * T0[1] + S[i][2] * T0[2];
         ST1[i] = S[i][0] * T1[0] + S[i][1] * T1[1] + S[i][2] * T1[2];
     }
-    const float a = T0[0] * ST0[0] + T0[1] * ST0[1] + T0[2] * ST0[2];
-    const float b = T1[0] * ST0[0] + T1[1] * ST0[1] + T1[2] * ST0[2];
-    const float c = T1[0] * ST1[0] + T1[1] * ST1[1] + T1[2] * ST1[2];
-    const float idet = 1.0f / (a * c - b * b);
-    const float idet2 = idet * idet;
+    const Real a = T0[0] * ST0[0] + T0[1] * ST0[1] + T0[2] * ST0[2];
+    const Real b = T1[0] * ST0[0] + T1[1] * ST0[1] + T1[2] * ST0[2];
+    const Real c = T1[0] * ST1[0] + T1[1] * ST1[1] + T1[2] * ST1[2];
+    const Real det = a * c - b * b;
+    const Real idet = one / det;
+    const Real idet2 = idet * idet;
     // dL/du = A S1 + B dy S0, dL/dv = B S1 + C dy S0 with the conic (A, B, C) = (c, -b, a) / det
-    const float cA = c * idet, cB = -b * idet, cC = a * idet;
-    const float gu = out(__builtin_fmaf(cA, sg[0], cB * sg[1])), gv = out(__builtin_fmaf(cB, sg[0], cC * sg[1]));
-    if (p.g_mean2d) { p.g_mean2d[g] = gu; p.g_mean2d[n + g] = gv; }
+    const Real cA = c * idet, cB = -b * idet, cC = a * idet;
+    const Real gu = cA * (Real)m[0] + cB * (Real)m[1], gv = cB * (Real)m[0] + cC * (Real)m[1];
+    if (p.g_mean2d) { p.g_mean2d[g] = out(gu); p.g_mean2d[n + g] = out(gv); }
 
     // ---- conic (A, B, C) = (c, -b, a) / det  ->  2D covariance ----
-    const float ga = (-c * c * gA + b * c * gB - b * b * gC) * idet2;
-    const float gb = (2.0f * b * c * gA - (a * c + b * b) * gB + 2.0f * a * b * gC) * idet2;
-    const float gc = (-b * b * gA + a * b * gB - a * a * gC) * idet2;
+    const Real dA = gA, dB = gB, dC = gC;
+    const Real ga = (-c * c * dA + b * c * dB - b * b * dC) * idet2;
+    const Real gb = (two * b * c * dA - (a * c + b * b) * dB + two * a * b * dC) * idet2;
+    const Real gc = (-b * b * dA + a * b * dB - a * a * dC) * idet2;
 
     // ---- (a, b, c) = (T0.S.T0, T0.S.T1, T1.S.T1) -> T0, T1 and Sigma ----
-    float gT0[3], gT1[3];
+    Real gT0[3], gT1[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-        gT0[i] = 2.0f * ga * ST0[i] + gb * ST1[i];
-        gT1[i] = gb * ST0[i] + 2.0f * gc * ST1[i];
+        gT0[i] = two * ga * ST0[i] + gb * ST1[i];
+        gT1[i] = gb * ST0[i] + two * gc * ST1[i];
     }
-    float gS[3][3];   // symmetric
+    Real gS[3][3];   // symmetric
 #pragma unroll
     for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int j = 0; j < 3; ++j)
-            gS[i][j] = ga * T0[i] * T0[j] + 0.5f * gb * (T0[i] * T1[j] + T1[i] * T0[j]) + gc * T1[i] * T1[j];
+            gS[i][j] = ga * T0[i] * T0[j] + half * gb * (T0[i] * T1[j] + T1[i] * T0[j]) + gc * T1[i] * T1[j];
 
     // ---- T rows = J W  ->  J entries  ->  camera-space mean ----
-    float gj00 = 0.0f, gj02 = 0.0f, gj11 = 0.0f, gj12 = 0.0f;
+    Real gj00 = 0, gj02 = 0, gj11 = 0, gj12 = 0;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         gj00 += gT0[k] * W[k];
@@ -441,23 +456,22 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
         gj11 += gT1[k] * W[3 + k];
         gj12 += gT1[k] * W[6 + k];
     }
-    const float iz2 = iz * iz, iz3 = iz2 * iz;
-    float gt[3];
-    gt[0] = -p.fx * iz2 * gj02 + p.fx * iz * gu;
-    gt[1] = -p.fy * iz2 * gj12 + p.fy * iz * gv;
-    gt[2] = -p.fx * iz2 * gj00 + 2.0f * p.fx * t[0] * iz3 * gj02 - p.fy * iz2 * gj11 +
-            2.0f * p.fy * t[1] * iz3 * gj12 - p.fx * t[0] * iz2 * gu - p.fy * t[1] * iz2 * gv;
-    float gmu[3];
+    const Real iz2 = iz * iz, iz3 = iz2 * iz;
+    Real gt[3];
+    gt[0] = -fx * iz2 * gj02 + fx * iz * gu;
+    gt[1] = -fy * iz2 * gj12 + fy * iz * gv;
+    gt[2] = -fx * iz2 * gj00 + two * fx * t[0] * iz3 * gj02 - fy * iz2 * gj11 + two * fy * t[1] * iz3 * gj12 -
+            fx * t[0] * iz2 * gu - fy * t[1] * iz2 * gv;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) gmu[i] = W[i] * gt[0] + W[3 + i] * gt[1] + W[6 + i] * gt[2];
+    for (int i = 0; i < 3; ++i) gmu[i] = (float)(W[i] * gt[0] + W[3 + i] * gt[1] + W[6 + i] * gt[2]);
 
     // ---- Sigma = M M^T, M = R diag(s) ----
-    float gR[3][3], gs[3] = {0.0f, 0.0f, 0.0f};
+    Real gR[3][3], gs[3] = {0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 3; ++i)
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-            const float gM = 2.0f * (gS[i][0] * M[0][j] + gS[i][1] * M[1][j] + gS[i][2] * M[2][j]);
+            const Real gM = two * (gS[i][0] * M[0][j] + gS[i][1] * M[1][j] + gS[i][2] * M[2][j]);
             gR[i][j] = gM * s[j];
             gs[j] += gM * R[i][j];
         }
@@ -465,20 +479,30 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     for (int j = 0; j < 3; ++j) p.g_log_scale[j * n + g] = out(gs[j] * s[j]);
 
     // ---- R of the unit quaternion, then the normalisation ----
-    float gq[4];
-    gq[0] = 2.0f * (qz * (gR[1][0] - gR[0][1]) + qy * (gR[0][2] - gR[2][0]) + qx * (gR[2][1] - gR[1][2]));
-    gq[1] = 2.0f * (qy * (gR[0][1] + gR[1][0]) + qz * (gR[0][2] + gR[2][0]) + qw * (gR[2][1] - gR[1][2]) -
-                    2.0f * qx * (gR[1][1] + gR[2][2]));
-    gq[2] = 2.0f * (qx * (gR[0][1] + gR[1][0]) + qz * (gR[1][2] + gR[2][1]) + qw * (gR[0][2] - gR[2][0]) -
-                    2.0f * qy * (gR[0][0] + gR[2][2]));
-    gq[3] = 2.0f * (qx * (gR[0][2] + gR[2][0]) + qy * (gR[1][2] + gR[2][1]) + qw * (gR[1][0] - gR[0][1]) -
-                    2.0f * qz * (gR[0][0] + gR[1][1]));
-    const float qh[4] = {qw, qx, qy, qz};
-    const float dot = qh[0] * gq[0] + qh[1] * gq[1] + qh[2] * gq[2] + qh[3] * gq[3];
+    Real gq[4];
+    gq[0] = two * (qz * (gR[1][0] - gR[0][1]) + qy * (gR[0][2] - gR[2][0]) + qx * (gR[2][1] - gR[1][2]));
+    gq[1] = two * (qy * (gR[0][1] + gR[1][0]) + qz * (gR[0][2] + gR[2][0]) + qw * (gR[2][1] - gR[1][2]) -
+                   two * qx * (gR[1][1] + gR[2][2]));
+    gq[2] = two * (qx * (gR[0][1] + gR[1][0]) + qz * (gR[1][2] + gR[2][1]) + qw * (gR[0][2] - gR[2][0]) -
+                   two * qy * (gR[0][0] + gR[2][2]));
+    gq[3] = two * (qx * (gR[0][2] + gR[2][0]) + qy * (gR[1][2] + gR[2][1]) + qw * (gR[1][0] - gR[0][1]) -
+                   two * qz * (gR[0][0] + gR[1][1]));
+    const Real qh[4] = {qw, qx, qy, qz};
+    const Real dot = qh[0] * gq[0] + qh[1] * gq[1] + qh[2] * gq[2] + qh[3] * gq[3];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p.g_quat[i * n + g] = out((gq[i] - qh[i] * dot) / qn);
 
-    // ---- colour: rgb = sum_k Y_k(d) sh_k with d = (mean - C) / |mean - C| ----
+    return (float)((a * c) / det);
+}
+
+// Colour part: dL/dsh from dL/drgb, and the mean's share through the view direction (gmu).
+template <int K>
+__device__ inline void colour_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad], bool live,
+                                  float gmu[3]) {
+    const int n = p.n;
+    auto out = [live](float v) { return live ? v : 0.0f; };
+    const float mu[3] = {p.mean[g], p.mean[n + g], p.mean[2 * n + g]};
+    // ---- rgb = sum_k Y_k(d) sh_k with d = (mean - C) / |mean - C| ----
     float dir[3] = {mu[0] - p.cam_pos[0], mu[1] - p.cam_pos[1], mu[2] - p.cam_pos[2]};
     const float idn = 1.0f / sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
     const float d[3] = {dir[0] * idn, dir[1] * idn, dir[2] * idn};
@@ -499,7 +523,24 @@ __device__ inline void gaussian_vjp(const GaussianBackwardParams &p, int g, cons
     sh_basis_vjp<K>(d[0], d[1], d[2], wk, gd);
     const float radial = gd[0] * d[0] + gd[1] * d[1] + gd[2] * d[2];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = out(gmu[i] + (gd[i] - d[i] * radial) * idn);
+    for (int i = 0; i < 3; ++i) gmu[i] = (gd[i] - d[i] * radial) * idn;
+}
+
+// Every gradient plane of Gaussian g.  Returns a c / det of its 2D covariance and the colour
+// part of dL/dmean (col), which the binary64 geometric pass needs when it redoes the rest.
+template <int K>
+__device__ inline float gaussian_vjp(const GaussianBackwardParams &p, int g, const float sg[kPairGrad], bool live,
+                                     float col[3]) {
+    const int n = p.n;
+    p.g_opacity[g] = sg[5];
+    if (p.g_conic) { p.g_conic[g] = -0.5f * sg[2]; p.g_conic[n + g] = -sg[3]; p.g_conic[2 * n + g] = -0.5f * sg[4]; }
+    if (p.g_rgb) { p.g_rgb[g] = sg[6]; p.g_rgb[n + g] = sg[7]; p.g_rgb[2 * n + g] = sg[8]; }
+    float geo[3];
+    const float kappa = geometric_vjp<float>(p, g, sg, live, geo);
+    colour_vjp<K>(p, g, sg, live, col);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) p.g_mean[i * n + g] = live ? geo[i] + col[i] : 0.0f;
+    return kappa;
 }
 
 // ---------------------------------------------------------------------------
@@ -674,7 +715,64 @@ __global__ __launch_bounds__(kBlock) void gaussian_backward_kernel(GaussianBackw
     float sg[kPairGrad];
 #pragma unroll
     for (int c = 0; c < kPairGrad; ++c) sg[c] = live ? s_sum[wave][lane][c] : 0.0f;
-    gaussian_vjp<K>(p, (int)g, sg, live);
+    float col[3];
+    const float kappa = gaussian_vjp<K>(p, (int)g, sg, live, col);
+    // ill-conditioned 2D covariances go to the binary64 pass: each wave compacts its queued
+    // Gaussians into its own 64-entry segment and stores their number (no atomics)
+    const bool queue = live && !(kappa <= kChainKappa);
+    const uint64_t queued = __ballot(queue);
+    const int64_t seg = g0 / kWave;
+    if (queue) {
+        const uint32_t slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(queued >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)queued, 0u));
+        float *e = p.fix_list + (size_t)(seg * kWave + slot) * kFixStride;
+        e[0] = __uint_as_float((uint32_t)g);
+#pragma unroll
+        for (int c = 0; c < 5; ++c) e[1 + c] = sg[c];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) e[6 + i] = col[i];
+    }
+    if (lane == 0) p.fix_count[seg] = (uint32_t)__popcll(queued);   // lane 0 holds g0 < n
+}
+
+// The geometric chain again, in binary64, for the Gaussians the binary32 pass queued: it
+// overwrites their mean, log-scale, quaternion and (u, v) gradients.  A wave takes
+// kFixSegs consecutive segments (lane l < kFixSegs reads segment l's count), scans the
+// counts, and its lanes take the queued entries of those segments one after another: at a
+// few percent of Gaussians queued that is about one pass per wave with most lanes busy,
+// over enough waves to hide the memory latency of the scattered parameter reads.  An entry
+// holds the index, the five moments and the colour part of the mean gradient.
+constexpr int kFixSegs = 8;
+__global__ __launch_bounds__(kBlock) void gaussian_backward_fp64_kernel(GaussianBackwardParams p) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int n = p.n;
+    const int64_t segs = ((int64_t)n + kWave - 1) / kWave;
+    const int64_t seg0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kFixSegs;
+    // inclusive prefix of the kFixSegs counts, the same in every lane
+    uint32_t incl[kFixSegs];
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < kFixSegs; ++j) {
+        run += seg0 + j < segs ? p.fix_count[seg0 + j] : 0u;
+        incl[j] = run;
+    }
+    for (uint32_t k = lane; k < run; k += kWave) {
+        // the segment holding queued entry k: the first j with incl[j] > k
+        uint32_t j = 0, before = 0;
+#pragma unroll
+        for (int i = 0; i + 1 < kFixSegs; ++i)
+            if (k >= incl[i]) {
+                j = i + 1;
+                before = incl[i];
+            }
+        const float *e = p.fix_list + (size_t)((seg0 + j) * kWave + (k - before)) * kFixStride;
+        const int g = (int)__float_as_uint(e[0]);
+        const float m[5] = {e[1], e[2], e[3], e[4], e[5]};
+        float geo[3];
+        (void)geometric_vjp<double>(p, g, m, true, geo);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) p.g_mean[c * n + g] = geo[c] + e[6 + c];
+    }
 }
 
 }  // namespace
@@ -695,6 +793,9 @@ void launch_gaussian_backward(const GaussianBackwardParams &p, hipStream_t s) {
         case 9: gaussian_backward_kernel<9><<<grid, kBlock, 0, s>>>(p); break;
         default: gaussian_backward_kernel<16><<<grid, kBlock, 0, s>>>(p); break;
     }
+    const int64_t segs = ((int64_t)p.n + kWave - 1) / kWave;       // 64-Gaussian queue segments
+    const int64_t per_fix_group = (int64_t)(kBlock / kWave) * kFixSegs;   // segments per workgroup
+    gaussian_backward_fp64_kernel<<<(unsigned)((segs + per_fix_group - 1) / per_fix_group), kBlock, 0, s>>>(p);
 }
 
 }  // namespace gsr

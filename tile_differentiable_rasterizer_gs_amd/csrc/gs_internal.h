@@ -241,6 +241,8 @@ void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges
 // dL/d(opacity, r, g, b); 36 bytes.
 constexpr int kPairGrad = 9;
 constexpr int kPairStride = kPairGrad;
+constexpr int kFixStride = 9;               // queue entry: Gaussian index, five moments, colour part of dL/dmean
+constexpr float kChainKappa = 8.0f;         // a c / det above which the chain runs in binary64
 
 struct CompositeBackwardParams {
     int32_t width, height, tiles_x, tiles_y;
@@ -276,6 +278,12 @@ struct GaussianBackwardParams {
     const EllipseRec *ellipse;   // null, or the exact-footprint rule
     int32_t tiles_x;
     const float *pair_grad;
+    // Gaussians whose 2D covariance has a c / det above kChainKappa, queued by the binary32
+    // chain rule for the binary64 geometric pass: wave w (Gaussians 64w .. 64w + 63) puts its
+    // queued ones in fix_list[64w ..] ([n][kFixStride]: index, the five moments, the colour
+    // part of dL/dmean) and their number in fix_count[w] ([ceil(n / 64)])
+    float *fix_list;
+    uint32_t *fix_count;
     float *g_mean, *g_quat, *g_log_scale, *g_opacity, *g_sh;
     float *g_mean2d, *g_conic, *g_rgb;   // optional screen-space gradients
 };
