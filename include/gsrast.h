@@ -59,6 +59,8 @@ typedef enum {
 #define GS_T_EPS 1e-4f
 /* Floats per projected-splat record (see gs_projected.splat). */
 #define GS_SPLAT_STRIDE 16
+/* Bytes of the static device array gs_render_noalloc takes its buffers from (per device). */
+#define GS_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * Gaussian parameters, structure of arrays, fp32, device memory, index g in
@@ -269,6 +271,26 @@ gs_status gs_composite_ex(gs_context *ctx, const gs_projected *projected, const 
  * materialised).  Waits once for the pair count (see the conventions above). */
 gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
                     const float bg_rgb[3], float *image_hwc, hipStream_t stream);
+
+/*
+ * gs_render for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, stages, kernels
+ * and result (bit for bit) as gs_render, but no intermediate buffer comes from the context's
+ * workspace: every one is carved from one static device array of GS_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that each device the library runs on holds until the process ends, and the call
+ * makes no allocation (no hipMalloc, hipFree or event creation; profiling is off for it).
+ * The context must exist (created beforehand: it holds the host-visible pair-count word).
+ * Limits: the Gaussians and tiles may take at most half the array (104 bytes per Gaussian +
+ * 12 per tile, about 320 k Gaussians at 1080p), the frame as a whole with its pairs
+ * (12 bytes each, counted on the device) the full array; beyond either the call returns
+ * GS_ERR_CAPACITY (the pair case after waiting for the count, with nothing composited).
+ * Every call on one device shares that device's array and leaves its contents behind:
+ * calls that overlap on one device (other streams, threads or contexts) race, and the
+ * caller must order them.  Afterwards the context holds no projection or binning (the
+ * staged entry points need a new gs_preprocess); its own workspace is untouched.
+ */
+gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *gaussians, const gs_camera *camera,
+                            const float bg_rgb[3], float *image_hwc, hipStream_t stream);
 
 /*
  * Gradients of a scalar loss L with respect to the Gaussian parameters, device

@@ -27,7 +27,7 @@ TILE = 16
 
 # symbols declared in include/gsrast.h
 EXPORTED = ("gs_context_create", "gs_context_destroy", "gs_context_set_option", "gs_check_arguments",
-            "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
+            "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_render_noalloc",
             "gs_backward", "gs_splat2d_forward", "gs_splat2d_backward", "gs_scale_activation", "gs_profile_read",
             "gs_status_string", "gs_last_error")
 
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_composite_ex.argtypes = [P, ctypes.POINTER(Projected), ctypes.POINTER(Binning), ctypes.POINTER(Camera),
                                     ctypes.POINTER(ctypes.c_float), P, P, P, P, P]
     lib.gs_render.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(ctypes.c_float),
+                              P, P]
+    lib.gs_render_noalloc.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(ctypes.c_float),
                               P, P]
     lib.gs_backward.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(Projected),
                                 ctypes.POINTER(Binning), ctypes.POINTER(ctypes.c_float), P, P, P,
@@ -263,6 +265,19 @@ class Rasterizer:
         bgv = (ctypes.c_float * 3)(*[float(v) for v in bg])
         self._check(self.lib.gs_render(self.ctx, ctypes.byref(g), ctypes.byref(cam), bgv,
                                        ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)))
+        return out
+
+    def render_noalloc(self, tensors: dict, sh_degree: int, camera: dict, bg=(0.0, 0.0, 0.0), out=None,
+                       stream=None) -> torch.Tensor:
+        """gs_render_noalloc: as render, with every intermediate buffer in the library's static scratch."""
+        g = make_gaussians(tensors, sh_degree)
+        cam = make_camera(camera)
+        if out is None:
+            out = torch.empty((cam.height, cam.width, 3), dtype=torch.float32, device="cuda")
+        self._check_image(out, (cam.height, cam.width, 3), torch.float32)
+        bgv = (ctypes.c_float * 3)(*[float(v) for v in bg])
+        self._check(self.lib.gs_render_noalloc(self.ctx, ctypes.byref(g), ctypes.byref(cam), bgv,
+                                               ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)))
         return out
 
     def backward(self, tensors: dict, sh_degree: int, camera: dict, projected: Projected, binning: Binning,

@@ -22,6 +22,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "gs_internal.h"
@@ -42,6 +43,39 @@ struct TimedSpan {
     int stage;
     hipEvent_t begin, end;
 };
+
+// Device memory of gs_render_noalloc: every intermediate buffer of a frame is carved from
+// this array.  In host code `scratch` is only a stand-in for the symbol; the device address
+// of each device's copy comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kNoAllocBytes = GS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+unsigned char *g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_status[kMaxDevices] = {};
+bool g_scratch_done[kMaxDevices] = {};
+
+// Looks up (once per device, with that device current) the device address of `scratch`.
+unsigned char *scratch_address(int device, hipError_t *status) {
+    if (device < 0 || device >= kMaxDevices) {
+        *status = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_done[device]) {
+        void *ptr = nullptr;
+        g_scratch_status[device] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (g_scratch_status[device] != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[device] = static_cast<unsigned char *>(ptr);
+        g_scratch_done[device] = true;
+    }
+    *status = g_scratch_status[device];
+    return g_scratch_ptr[device];
+}
 
 }  // namespace
 
@@ -92,6 +126,11 @@ struct gs_context {
 
     std::vector<TimedSpan> spans;
     size_t spans_used = 0;
+
+    // gs_render_noalloc: while set, ensure() carves buffers from this arena (the device's
+    // `scratch`) instead of allocating
+    unsigned char *arena = nullptr;
+    size_t arena_size = 0, arena_used = 0;
 };
 
 namespace {
@@ -141,6 +180,17 @@ struct DeviceScope {
 
 gs_status ensure(gs_context *ctx, DeviceBuffer &b, size_t bytes) {
     if (bytes <= b.bytes) return GS_OK;
+    if (ctx->arena) {   // gs_render_noalloc: carve, never allocate
+        const size_t off = (ctx->arena_used + 255) & ~(size_t)255;
+        if (off > ctx->arena_size || bytes > ctx->arena_size - off)
+            return fail(ctx, GS_ERR_CAPACITY,
+                        "gs_render_noalloc: the frame needs more than the %zu-byte scratch (%zu in use, %zu more)",
+                        ctx->arena_size, off, bytes);
+        b.ptr = ctx->arena + off;
+        b.bytes = bytes;
+        ctx->arena_used = off + bytes;
+        return GS_OK;
+    }
     size_t want = bytes + bytes / 4;                 // grow with headroom
     want = (want + 255) & ~(size_t)255;
     const size_t after = ctx->workspace - b.bytes + want;
@@ -204,6 +254,20 @@ int ceil_log2(int64_t v) {
     int b = 0;
     while (((int64_t)1 << b) < v) ++b;
     return b;
+}
+
+// Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
+constexpr int kContextBuffers = 39;
+void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
+    DeviceBuffer *all[kContextBuffers] = {
+        &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
+        &ctx->dval[1], &ctx->dcount, &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch, &ctx->total,
+        &ctx->ellipse, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1], &ctx->pval[0],
+        &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted, &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part,
+        &ctx->ranges, &ctx->tile_order, &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->pair_base,
+        &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
+        &ctx->s2_trans, &ctx->s2_partial};
+    for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
 
 gs_status check_projected(gs_context *ctx, const gs_projected *pr) {
@@ -285,6 +349,17 @@ gs_status gs_context_create(gs_context **out, int device) {
         return GS_ERR_DEVICE;
     }
     ctx->host_total[1] = 0;
+    // the pair-count event: no timing, no system-scope fence (the count reaches the host by
+    // the scan's own system-scope store, so the event only has to say that the scan ran)
+    if (hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming | hipEventDisableSystemFence) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipHostFree(ctx->host_total);
+        delete ctx;
+        return GS_ERR_DEVICE;
+    }
+    hipError_t scratch_status;
+    (void)scratch_address(device, &scratch_status);   // once per device; gs_render_noalloc reports failure
     *out = ctx;
     return GS_OK;
 }
@@ -292,16 +367,8 @@ gs_status gs_context_create(gs_context **out, int device) {
 void gs_context_destroy(gs_context *ctx) {
     if (!ctx) return;
     DeviceScope scope(ctx->device);
-    DeviceBuffer *all[] = {&ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1],
-                           &ctx->dcount,
-                           &ctx->dval[0], &ctx->dval[1], &ctx->offsets, &ctx->scan_scratch, &ctx->dsort_scratch,
-                           &ctx->total, &ctx->pkey32[0], &ctx->pkey32[1], &ctx->pkey64[0], &ctx->pkey64[1],
-                           &ctx->pval[0], &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted,
-                           &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part, &ctx->ranges,
-                           &ctx->pair_base, &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count,
-                           &ctx->tile_order, &ctx->ellipse,
-                           &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->s2_order,
-                           &ctx->s2_rec, &ctx->s2_trans, &ctx->s2_partial};
+    DeviceBuffer *all[kContextBuffers];
+    context_buffers(ctx, all);
     for (DeviceBuffer *b : all)
         if (b->ptr) (void)hipFree(b->ptr);
     for (TimedSpan &t : ctx->spans) {
@@ -561,10 +628,6 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     GS_TRY(ensure(ctx, ctx->total, 8));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->tile_order, (size_t)tiles * sizeof(uint32_t)));
-    // the pair count reaches the host by the scan's own system-scope store, so this event only
-    // has to say that the scan ran: no system-scope fence (a cache writeback of ~9 us per frame)
-    if (!ctx->total_ready)
-        GS_HIP(ctx, hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming | hipEventDisableSystemFence));
     unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
     const uint32_t *order = nullptr;
@@ -625,8 +688,12 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     }
     if (!speculated || M > ctx->pair_capacity) {
         if (speculated) GS_HIP(ctx, hipStreamSynchronize(stream));   // buffers are about to move
-        const int64_t want = M + M / 4;
-        ctx->pair_capacity = want > 4096 ? want : 4096;
+        if (ctx->arena) {   // the fixed scratch: exactly the frame's pairs, no headroom
+            ctx->pair_capacity = M > 1 ? M : 1;
+        } else {
+            const int64_t want = M + M / 4;
+            ctx->pair_capacity = want > 4096 ? want : 4096;
+        }
         GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
     }
 
@@ -712,6 +779,64 @@ gs_status gs_render(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam
     gs_binning bin;
     GS_TRY(bin_and_sort(ctx, &pr, 0, &bin, stream));
     return gs_composite(ctx, &pr, &bin, cam, bg, image, stream);
+}
+
+gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam, const float bg[3],
+                            float *image, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (!g || !cam || !bg || !image) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "NULL gaussians, camera, bg or image");
+    char why[160];
+    if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_render_noalloc is already running on this context");
+    // what the Gaussians and the tiles need before any pair (per Gaussian: record 64, depth 4,
+    // rect 8, count 4, two key/index pairs 16, gathered count 4, offsets 4; per tile: range 8,
+    // launch order 4), checked before anything is enqueued; the pairs are checked once counted
+    const int64_t tiles = (int64_t)((cam->width + GS_TILE - 1) / GS_TILE) * ((cam->height + GS_TILE - 1) / GS_TILE);
+    const int64_t fixed = g->n * 104 + tiles * 12;
+    if (fixed > (int64_t)(kNoAllocBytes / 2))
+        return fail(ctx, GS_ERR_CAPACITY,
+                    "gs_render_noalloc: %lld Gaussians and %lld tiles need %lld bytes, more than half of the "
+                    "%zu-byte scratch", (long long)g->n, (long long)tiles, (long long)fixed, kNoAllocBytes);
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    hipError_t sst;
+    unsigned char *base = scratch_address(ctx->device, &sst);
+    if (!base) return fail(ctx, GS_ERR_DEVICE, "address of the scratch array: %s", hipGetErrorString(sst));
+
+    // swap the context's own workspace out: every ensure() of this frame carves from the scratch
+    DeviceBuffer *bufs[kContextBuffers];
+    context_buffers(ctx, bufs);
+    DeviceBuffer saved[kContextBuffers];
+    for (int i = 0; i < kContextBuffers; ++i) {
+        saved[i] = *bufs[i];
+        *bufs[i] = DeviceBuffer{};
+    }
+    const int64_t saved_capacity = ctx->pair_capacity;
+    const int saved_profile = ctx->profile;
+    ctx->pair_capacity = 0;   // size the pair buffers from the frame's own count
+    ctx->profile = 0;         // timing events would be allocated
+    ctx->arena = base;
+    ctx->arena_size = kNoAllocBytes;
+    ctx->arena_used = 0;
+
+    gs_projected pr;
+    gs_binning bin;
+    gs_status st = gs_preprocess(ctx, g, cam, &pr, stream);
+    if (st == GS_OK) st = bin_and_sort(ctx, &pr, 0, &bin, stream);
+    if (st == GS_OK) st = gs_composite(ctx, &pr, &bin, cam, bg, image, stream);
+
+    for (int i = 0; i < kContextBuffers; ++i) *bufs[i] = saved[i];
+    ctx->arena = nullptr;
+    ctx->arena_size = ctx->arena_used = 0;
+    ctx->pair_capacity = saved_capacity;
+    ctx->profile = saved_profile;
+    // the frame's projection and binning lived in the scratch: none is left on the context
+    ctx->n = -1;
+    ctx->num_dups = -1;
+    ctx->rank_order = ctx->sorted_values = ctx->launch_order = nullptr;
+    ctx->sorted_keys = nullptr;
+    ctx->g_mean = nullptr;
+    return st;
 }
 
 gs_status gs_backward(gs_context *ctx, const gs_gaussians *g, const gs_camera *cam, const gs_projected *pr,
