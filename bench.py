@@ -11,7 +11,10 @@ A workload with several cameras (the 32-view orbit) renders its views round-robi
 The JSON line also carries the backward pass (gs_backward for a fixed random
 image cotangent) timed on its own and as part of a forward + backward step, and
 the lesson's 2D splat-fitting workload (64 splats, 64x64, 200 Adam steps), and the
-same frames under the exact-footprint tile rule (GS_TILE_ELLIPSE).
+same frames under the exact-footprint tile rule (GS_TILE_ELLIPSE), and (field
+`workloads`) the other four scenes: 10 k SH0 256x256, 100 k SH3 800x800, 5 M SH3
+1080p with 2 % large Gaussians, and the 3 M SH3 1080p 32-view orbit (one stream and
+three views in flight), each with its stage split and stage rooflines.
 """
 from __future__ import annotations
 
@@ -27,6 +30,10 @@ if ROOT not in sys.path:
 
 # MI355X published peaks
 HBM_PEAK_GBS = 8000.0
+# LDS read path: 256 bytes per clock per CU (gfx950 doubles the previous generation's 128),
+# x 256 CUs x 2.4 GHz, in GB/s
+LDS_PEAK_GBS = 256 * 256 * 2.4
+EXTRA_WORKLOADS = ("c1_10k_sh0_256", "c2_100k_sh3_800", "c4_5m_sh3_1080p_large", "c5_3m_sh3_1080p_orbit32")
 # VALU issue peak: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz, one lane-op per lane per clock
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 # lane-ops per blended (pixel, Gaussian) pair in the composite inner loop, counting a
@@ -62,12 +69,11 @@ def stage_bytes(n, sh_degree, m, n_visible):
                 ranges=ranges)
 
 
-def measured_traffic(workload):
-    """HBM bytes per composite launch from the committed rocprofv3 summary, or None when the
-    summary is missing or was taken on a different composite kernel source."""
+def _profile_summary(path):
+    """key: value lines of a committed rocprofv3 summary, or None when it is missing or was
+    taken on another composite kernel source."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     src = os.path.join(ROOT, "tile_differentiable_rasterizer_gs_amd", "csrc", "composite.hip")
     if not os.path.exists(path):
         return None
@@ -78,12 +84,52 @@ def measured_traffic(workload):
             kv[k.strip()] = v.strip()
     if kv.get("composite_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
-    return int(float(kv["composite_traffic_bytes"]))
+    return kv
 
 
-def cpu_baseline(scene, cam, pixels_target=262144):
-    """The oracle on a bounded sample (about 10 s of host work at 1080p on 16 threads): full
-    projection + binning, composite on 262144 sampled pixels (12.6 % of the frame)."""
+def measured_traffic(workload):
+    """HBM bytes per composite launch from the committed rocprofv3 summary (None if stale)."""
+    kv = _profile_summary(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"))
+    return None if kv is None else int(float(kv["composite_traffic_bytes"]))
+
+
+def composite_lds(workload, comp_ms):
+    """LDS roofline of the composite: bytes its LDS instructions deliver per launch (rocprofv3
+    SQ_INSTS_LDS_LOAD_BANDWIDTH + SQ_INSTS_LDS_STORE_BANDWIDTH, 64-byte units, from the
+    committed summary) over the launch time measured here, against LDS_PEAK_GBS; and the LDS
+    pipe's busy fraction (SQ_LDS_IDX_ACTIVE over the kernel's cycles x CUs).  None if stale."""
+    kv = _profile_summary(os.path.join(ROOT, "profiles", f"lds_{workload}.txt"))
+    if kv is None or not comp_ms:
+        return None
+    nbytes = float(kv["composite_lds_bytes"])
+    gbs = nbytes / (comp_ms * 1e-3) / 1e9
+    return dict(bound="lds", achieved=round(gbs, 1), peak=round(LDS_PEAK_GBS, 1), unit="GB/s",
+                frac=round(gbs / LDS_PEAK_GBS, 4), bytes=nbytes,
+                pipe_busy_frac=round(float(kv["composite_lds_busy_frac"]), 4),
+                source="profiles/lds_%s.txt" % workload)
+
+
+def _host_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n):
+    """Thread count of the oracle's OpenMP regions started from this thread (libgomp)."""
+    import ctypes
+
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def oracle_frame(scene, cam, pixels_target, binning=True, seed=0):
+    """The oracle on one frame: projection and binning (single thread) in full, the per-pixel
+    composite (OpenMP) on `pixels_target` sampled pixels scaled to the whole image (or every
+    pixel when the image has fewer).  Returns seconds per frame and what was sampled."""
     import numpy as np
 
     import oracle
@@ -91,19 +137,59 @@ def cpu_baseline(scene, cam, pixels_target=262144):
     t0 = time.perf_counter()
     p = oracle.preprocess(scene.arrays(), scene.sh_degree, cam)
     t1 = time.perf_counter()
-    oracle.bin_pairs(p, want_unsorted=False)
+    if binning:
+        oracle.bin_pairs(p, want_unsorted=False)
     t2 = time.perf_counter()
-    rng = np.random.default_rng(0)
     npx = cam["width"] * cam["height"]
-    pix = rng.choice(npx, min(pixels_target, npx), replace=False)
+    pix = None
+    if pixels_target < npx:
+        pix = np.random.default_rng(seed).choice(npx, pixels_target, replace=False)
     oracle.composite(p, cam, pixels=pix)
     t3 = time.perf_counter()
-    frame_s = (t1 - t0) + (t2 - t1) + (t3 - t2) * npx / len(pix)
+    done = npx if pix is None else len(pix)
+    frame_s = (t1 - t0) + (t2 - t1) + (t3 - t2) * npx / done
+    what = (f"projection {t1 - t0:.2f}s" + (f", binning {t2 - t1:.2f}s" if binning else ", binning not run") +
+            f" (1 thread), composite of {done} of {npx} pixels {t3 - t2:.2f}s")
+    return frame_s, what
+
+
+def cpu_baseline(scene, cam, pixels_target=262144):
+    """The oracle on a bounded sample of the timed workload (about 10 s of host work at 1080p
+    on 16 threads): full projection + binning, composite on 262144 sampled pixels (12.6 % of
+    the frame)."""
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return dict(value=1.0 / frame_s, unit="frames/s", cores=threads, kind="oracle",
-                sample=(f"full projection ({t1 - t0:.2f}s, 1 thread) and binning ({t2 - t1:.2f}s, 1 thread) of "
-                        f"the {scene.n}-Gaussian scene, composite of {len(pix)} random pixels "
-                        f"({t3 - t2:.2f}s, {threads} threads) scaled to {npx} pixels"))
+    _omp_threads(threads)
+    frame_s, what = oracle_frame(scene, cam, pixels_target)
+    return dict(value=1.0 / frame_s, unit="frames/s", cores=threads, kind="oracle", host_cpu=_host_model(),
+                sample=f"{scene.n}-Gaussian scene: {what}, {threads} threads, scaled to the full image")
+
+
+def cpu_baseline_workloads(scenes_by_name):
+    """One oracle frame of every other workload (sampled where the full frame would take minutes)
+    and the 10 k frame on one thread.  The 5 M scene's binning (4e8 pairs through a host qsort)
+    is not run; its per-pixel composite needs no binning."""
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    plan = {"c1_10k_sh0_256": (1 << 20, True), "c2_100k_sh3_800": (65536, True),
+            "c4_5m_sh3_1080p_large": (4096, False), "c5_3m_sh3_1080p_orbit32": (16384, True)}
+    out = {}
+    for name, (px, binning) in plan.items():
+        sc = scenes_by_name.get(name)
+        if sc is None:
+            continue
+        _omp_threads(threads)
+        frame_s, what = oracle_frame(sc, sc.cameras[0], px, binning=binning)
+        out[name] = dict(value=round(1.0 / frame_s, 5), unit="frames/s", cores=threads,
+                         sample=what + ("; view 0 of 32" if len(sc.cameras) > 1 else ""))
+        log(f"oracle {name}: {frame_s:.2f} s/frame ({what})")
+    sc = scenes_by_name.get("c1_10k_sh0_256")
+    if sc is not None:
+        _omp_threads(1)
+        frame_s, what = oracle_frame(sc, sc.cameras[0], 1 << 20)
+        out["c1_10k_sh0_256_single_thread"] = dict(value=round(1.0 / frame_s, 5), unit="frames/s", cores=1,
+                                                   sample=what)
+        log(f"oracle c1 on 1 thread: {frame_s:.2f} s/frame")
+        _omp_threads(threads)
+    return out
 
 
 def time_backward(r, dev, scene, cams, img, bg, steps, blends):
@@ -287,6 +373,134 @@ def time_splat2d_fit():
                 note="step = forward + backward through gs_splat2d_* plus torch activations, loss and Adam")
 
 
+def frame_stats(r, dev, scene, cams, img, bg):
+    """Pairs, blended (pixel, Gaussian) pairs and visible Gaussians per frame, averaged over the
+    views (outside any timed region)."""
+    import torch
+
+    pairs = blends = n_visible = 0
+    for c in cams:
+        pr = r.preprocess(dev, scene.sh_degree, c)
+        bn = r.bin_and_sort(pr, c)
+        tot = torch.zeros(1, dtype=torch.int64, device="cuda")
+        r.composite(pr, bn, c, bg=bg, out=img, blend_total=tot)
+        tc = r.projected_tensors(pr)["tile_count"]
+        torch.cuda.synchronize()
+        pairs += int(bn.num_dups)
+        blends += int(tot.item())
+        n_visible += int((tc > 0).sum().item())
+    return tuple(v / len(cams) for v in (pairs, blends, n_visible))
+
+
+def timed_frames(r, dev, scene, cams, img, bg, steps, S, sort_mode):
+    """`steps` frames back to back on one stream, or with S > 1 view i on context i mod S with
+    its own stream, so that one view's compositing overlaps the next view's front end.
+    Returns (ms per frame from HIP events, wall seconds)."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    lanes = [(r, torch.cuda.current_stream(), img)]
+    for _ in range(S - 1):
+        lanes.append((binding.Rasterizer(sort_mode=sort_mode, emit_keys=False), torch.cuda.Stream(),
+                      torch.empty_like(img)))
+    for i in range(S):   # warm every context (workspace sized before timing)
+        lr, ls, li = lanes[i]
+        for c in cams[:2]:
+            lr.render(dev, scene.sh_degree, c, bg=bg, out=li, stream=ls)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for ls in (l[1] for l in lanes[1:]):
+        ls.wait_event(start)
+    for i in range(steps):
+        lr, ls, li = lanes[i % S]
+        lr.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=li, stream=ls)
+    main = torch.cuda.current_stream()
+    for ls in (l[1] for l in lanes[1:]):
+        main.wait_stream(ls)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for extra in lanes[1:]:
+        extra[0].close()
+    return start.elapsed_time(stop) / steps, wall
+
+
+def stage_split(r, dev, scene, cams, img, bg, steps):
+    """The same frames with HIP events around every stage (GS_OPT_PROFILE, on the render
+    stream): (ms per stage per frame, ms per frame with the events)."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r.set_option(binding.GS_OPT_PROFILE, 1)
+    r.profile_read()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+    stop.record()
+    torch.cuda.synchronize()
+    prof_ms = start.elapsed_time(stop) / steps
+    prof = r.profile_read()
+    r.set_option(binding.GS_OPT_PROFILE, 0)
+    return {k: (ms / steps) for k, (ms, cnt) in prof.items() if cnt}, prof_ms
+
+
+def stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs):
+    nbytes = stage_bytes(scene.n, scene.sh_degree, pairs, n_visible)
+    out = {}
+    for st, b in nbytes.items():
+        if st in stage_ms and stage_ms[st] > 0:
+            gbs = b / (stage_ms[st] * 1e-3) / 1e9
+            out[st] = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                           frac=round(gbs / HBM_PEAK_GBS, 4), frac_of_copy=round(gbs / copy_gbs, 4), bytes=b)
+    comp_ms = stage_ms.get("composite", 0.0)
+    comp_gops = blends * COMPOSITE_OPS_PER_PAIR / (comp_ms * 1e-3) / 1e9 if comp_ms else 0.0
+    out["composite"] = dict(bound="alu", achieved=round(comp_gops / 1e3, 3), peak=round(VALU_PEAK_GOPS / 1e3, 3),
+                            unit="Tlane-op/s", frac=round(comp_gops / VALU_PEAK_GOPS, 4),
+                            ops=blends * COMPOSITE_OPS_PER_PAIR)
+    return out
+
+
+def measure_workload(name, scene, steps, warmup, sort_mode, copy_gbs, bg=(0.0, 0.0, 0.0)):
+    """Frame time (one stream; multi-view scenes also three views in flight), stage split and
+    stage rooflines of one workload, on a context of its own."""
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    cams = scene.cameras
+    dev = binding.gaussians_to_device(scene.arrays())
+    r = binding.Rasterizer(sort_mode=sort_mode, emit_keys=False)
+    img = torch.empty((cams[0]["height"], cams[0]["width"], 3), dtype=torch.float32, device="cuda")
+    pairs, blends, n_visible = frame_stats(r, dev, scene, cams, img, bg)
+    for i in range(warmup):
+        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
+    ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 1, sort_mode)
+    res = dict(n_gaussians=scene.n, sh_degree=scene.sh_degree, width=cams[0]["width"], height=cams[0]["height"],
+               views=len(cams), steps=steps, ms_per_frame=round(ms, 5), frames_per_s=round(1000.0 / ms, 2),
+               blends_per_s=round(blends * 1000.0 / ms, 1), pairs_per_frame=round(pairs),
+               blended_pairs_per_frame=round(blends), visible_per_frame=round(n_visible))
+    if len(cams) > 1:
+        p_ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 3, sort_mode)
+        res["pipelined"] = {"views_in_flight": 3, "ms_per_frame": round(p_ms, 5),
+                            "frames_per_s": round(1000.0 / p_ms, 2)}
+    stage_ms, _ = stage_split(r, dev, scene, cams, img, bg, steps)
+    res["stage_ms"] = {k: round(v, 5) for k, v in stage_ms.items()}
+    res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs)
+    r.close()
+    del dev, img
+    torch.cuda.empty_cache()
+    log(f"{name}: {ms:.4f} ms/frame" + (f", {res['pipelined']['ms_per_frame']:.4f} with 3 in flight"
+                                         if "pipelined" in res else "") +
+        f"; pairs {pairs:.0f}; stages " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +512,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-splat2d", action="store_true", help="skip the 2D splat-fitting timing")
     ap.add_argument("--no-ellipse", action="store_true", help="skip the exact-footprint tile rule timing")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other four workloads")
     ap.add_argument("--streams", type=int, default=0,
                     help="views in flight (contexts on their own streams) for the timed frames; default 1 "
                          "(multi-view workloads also report three in flight as `pipelined`)")
@@ -309,7 +524,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from tile_differentiable_rasterizer_gs_amd import binding, scenes
@@ -338,82 +552,24 @@ def main():
     img = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
     bg = (0.0, 0.0, 0.0)
 
-    # frame statistics (outside the timed region), averaged over the views: pairs, visible
-    # Gaussians and blended (pixel, Gaussian) pairs
-    pairs = blends = n_visible = 0
-    for c in cams:
-        pr = r.preprocess(dev, scene.sh_degree, c)
-        bn = r.bin_and_sort(pr, c)
-        tot = torch.zeros(1, dtype=torch.int64, device="cuda")
-        r.composite(pr, bn, c, bg=bg, out=img, blend_total=tot)
-        tc = r.projected_tensors(pr)["tile_count"]
-        torch.cuda.synchronize()
-        pairs += int(bn.num_dups)
-        blends += int(tot.item())
-        n_visible += int((tc > 0).sum().item())
-    pairs, blends, n_visible = (v / len(cams) for v in (pairs, blends, n_visible))
+    pairs, blends, n_visible = frame_stats(r, dev, scene, cams, img, bg)
     log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} blended pairs={blends:.0f} ({len(cams)} view(s))")
-
     for i in range(args.warmup):
         r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     torch.cuda.synchronize()
 
-    # timed region 1: plain frames, back to back on one stream (or, with --streams S, view i on
-    # context i mod S with its own stream, so one view's compositing overlaps the next view's
-    # front end).
-    def timed_frames(S):
-        lanes = [(r, torch.cuda.current_stream(), img)]
-        for _ in range(S - 1):
-            lanes.append((binding.Rasterizer(sort_mode=args.sort_mode, emit_keys=False), torch.cuda.Stream(),
-                          torch.empty_like(img)))
-        for i in range(S):   # warm every context (workspace sized before timing)
-            lr, ls, li = lanes[i]
-            for c in cams[:2]:
-                lr.render(dev, scene.sh_degree, c, bg=bg, out=li, stream=ls)
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for ls in (l[1] for l in lanes[1:]):
-            ls.wait_event(start)
-        for i in range(args.steps):
-            lr, ls, li = lanes[i % S]
-            lr.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=li, stream=ls)
-        main = torch.cuda.current_stream()
-        for ls in (l[1] for l in lanes[1:]):
-            main.wait_stream(ls)
-        stop.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        for extra in lanes[1:]:
-            extra[0].close()
-        return start.elapsed_time(stop) / args.steps, wall
-
+    # timed region: plain frames (`value`)
     S = max(1, args.streams)
-    ms_per_step, wall = timed_frames(S)
+    ms_per_step, wall = timed_frames(r, dev, scene, cams, img, bg, args.steps, S, args.sort_mode)
     log(f"timed: {ms_per_step:.4f} ms/frame (wall {wall / args.steps * 1e3:.4f} ms, {S} view(s) in flight)")
     pipelined = None
     if len(cams) > 1 and args.streams == 0:
-        # multi-view workloads: the same frames with three views in flight, reported beside the
-        # one-stream rate (which is `value`)
-        p_ms, p_wall = timed_frames(3)
+        p_ms, p_wall = timed_frames(r, dev, scene, cams, img, bg, args.steps, 3, args.sort_mode)
         pipelined = {"views_in_flight": 3, "ms_per_frame": round(p_ms, 5), "frames_per_s": round(1000.0 / p_ms, 2)}
         log(f"three views in flight: {p_ms:.4f} ms/frame (wall {p_wall / args.steps * 1e3:.4f} ms)")
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # timed region 2: same frames with HIP events around every stage (on the render stream)
-    r.set_option(binding.GS_OPT_PROFILE, 1)
-    r.profile_read()
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
-    stop.record()
-    torch.cuda.synchronize()
-    prof_ms_per_step = start.elapsed_time(stop) / args.steps
-    prof = r.profile_read()
-    r.set_option(binding.GS_OPT_PROFILE, 0)
-    stage_ms = {k: (ms / args.steps) for k, (ms, cnt) in prof.items() if cnt}
+    # same frames with HIP events around every stage (on the render stream)
+    stage_ms, prof_ms_per_step = stage_split(r, dev, scene, cams, img, bg, args.steps)
     log("stages (ms/frame): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
 
     # per-frame distribution (one event pair per frame) and the device's copy bandwidth
@@ -421,19 +577,10 @@ def main():
     copy_gbs = copy_bandwidth()
     log(f"frame ms median {dist['median']} p10 {dist['p10']} p90 {dist['p90']}; 1 GiB copy {copy_gbs:.0f} GB/s")
 
-    nbytes = stage_bytes(scene.n, scene.sh_degree, pairs, n_visible)
-    rooflines = {}
-    for st, b in nbytes.items():
-        if st in stage_ms and stage_ms[st] > 0:
-            gbs = b / (stage_ms[st] * 1e-3) / 1e9
-            rooflines[st] = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                                 frac=round(gbs / HBM_PEAK_GBS, 4), frac_of_copy=round(gbs / copy_gbs, 4),
-                                 bytes=b)
-    comp_ms = stage_ms.get("composite", 0.0)
-    comp_gops = blends * COMPOSITE_OPS_PER_PAIR / (comp_ms * 1e-3) / 1e9 if comp_ms else 0.0
-    rooflines["composite"] = dict(bound="alu", achieved=round(comp_gops / 1e3, 3), peak=round(VALU_PEAK_GOPS / 1e3, 3),
-                                  unit="Tlane-op/s", frac=round(comp_gops / VALU_PEAK_GOPS, 4),
-                                  ops=blends * COMPOSITE_OPS_PER_PAIR)
+    rooflines = stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs)
+    lds = composite_lds(name, stage_ms.get("composite", 0.0))
+    if lds:
+        rooflines["composite_lds"] = lds
     dominant = max(stage_ms, key=stage_ms.get)
     dom = dict(rooflines.get(dominant, {}))
     dom["kernel"] = dominant
@@ -476,10 +623,27 @@ def main():
         log("2D splat fit ...")
         out["splat2d_fit"] = time_splat2d_fit()
         log(f"2D splat fit: {out['splat2d_fit']}")
+    r.close()
+    del dev, img
+    torch.cuda.empty_cache()
+    others = {}
+    if not args.no_workloads:
+        out["workloads"] = {}
+        for wname in EXTRA_WORKLOADS:
+            if wname == name:
+                continue
+            t = time.perf_counter()
+            others[wname] = scenes.make_scene(wname)
+            log(f"scene {wname}: n={others[wname].n} generated in {time.perf_counter() - t:.1f}s")
+            many = len(others[wname].cameras) > 1 or others[wname].n >= 5_000_000
+            steps = 64 if len(others[wname].cameras) > 1 else (20 if many else args.steps)
+            warmup = 8 if many else args.warmup
+            out["workloads"][wname] = measure_workload(wname, others[wname], steps, warmup, args.sort_mode, copy_gbs)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(scene, cam)
-    r.close()
+        if others:
+            out["cpu_baseline"]["workloads"] = cpu_baseline_workloads(others)
     print(json.dumps(out), flush=True)
 
 
