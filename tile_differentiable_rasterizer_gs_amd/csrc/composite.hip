@@ -15,10 +15,12 @@
 // with (A', B', C') = -log2(e)/2 (A, 2B, C); the min is the exp's output clamp and the
 // factor 0.99 rides on the staged colours and the T update.  A pixel stops after the blend that
 // brings T below GS_T_EPS; the blend is branchless (a stopped pixel blends with T
-// masked to 0).  A wave leaves a batch once none of its 128 pixels is live (tested
-// every 8 splats) and the workgroup leaves the list when a barrier count finds no
-// live pixel.  Pure VALU work (one v_exp_f32 per pair): no dense contraction, so
-// no MFMA.
+// masked to 0).  Every 8 splats a wave counts its live pixels: with none left it
+// stops blending for the rest of the list; with 64 or fewer it packs them one per
+// lane (cross-lane permutes, no LDS) and blends the rest of the list one pixel per
+// lane, since a lane of two stopped pixels would otherwise spend its issue slots on
+// nothing.  The workgroup leaves the list when a barrier count finds no live pixel.
+// Pure VALU work (one v_exp_f32 per pair): no dense contraction, so no MFMA.
 #include "gs_internal.h"
 
 namespace gsr {
@@ -61,6 +63,25 @@ __device__ __forceinline__ float group8_get(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (u << 5)));
 }
 
+// Position of the k-th (from 0) set bit of m, for k < popcount(m).
+__device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t k) {
+    uint32_t pos = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const uint32_t c = (uint32_t)__popcll(m & ((1ull << w) - 1));
+        if (k >= c) {
+            k -= c;
+            m >>= w;
+            pos += w;
+        }
+    }
+    return pos;
+}
+
+__device__ __forceinline__ float lane_pull(int src, float v) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
 template <bool kAux>
 struct Pixels {
     float x0, x1, y;
@@ -87,8 +108,38 @@ struct Pixels {
             if (kAux) blended[i] += live ? 1u : 0u;
         }
     }
+    // One pixel per lane (slot 0) after the wave has packed its live pixels: the row terms
+    // are this lane's own, computed by the same operations as the shared ones.
+    __device__ __forceinline__ void blend_one(const float4 a, const float4 b4, const float c) {
+        const float dy = y - b4.x;
+        const float bdy = b4.z * dy, e = splat_row_term(dy, b4.w, b4.y);
+        const float as = splat_alpha_scaled(splat_exponent(x0 - a.x, a.y, bdy, e));
+        const bool live = T[0] >= GS_T_EPS;
+        const float w = (live ? T[0] : 0.0f) * as;
+        r[0] += w * a.z;
+        g[0] += w * a.w;
+        b[0] += w * c;
+        T[0] = __builtin_fmaf(-GS_ALPHA_MAX, w, T[0]);
+        if (kAux) blended[0] += live ? 1u : 0u;
+    }
     __device__ __forceinline__ bool live() const { return (T[0] >= GS_T_EPS) | (T[1] >= GS_T_EPS); }
 };
+
+// Output of one pixel: C + T bg, and the per-pixel state the backward reads.
+template <bool kAux>
+__device__ __forceinline__ void write_pixel(const CompositeParams &p, int x, int y, float r, float g, float b,
+                                            float T, uint32_t blended) {
+    if (x < p.width && y < p.height) {
+        const size_t pix = (size_t)y * p.width + x;
+        p.image[pix * 3 + 0] = r + T * p.bg[0];
+        p.image[pix * 3 + 1] = g + T * p.bg[1];
+        p.image[pix * 3 + 2] = b + T * p.bg[2];
+        if (kAux) {
+            if (p.final_T) p.final_T[pix] = T;
+            if (p.n_blend) p.n_blend[pix] = blended;
+        }
+    }
+}
 
 template <bool kAux>
 __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) {
@@ -126,6 +177,12 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
         }
     }
     __syncthreads();
+    // Wave-uniform state: 'single' once the wave has packed its live pixels one per lane
+    // (slot 0 holds the pixel at (sx, sy), 'held' says the lane got one), 'done' once none
+    // is left.  Pixels that were no longer live when the wave packed are written then.
+    bool single = false, done = false, held = false;
+    int sx = 0, sy = 0;
+    uint32_t total = 0;
     for (uint32_t base = start; base < end; base += kBatch) {
         const uint32_t next = base + kBatch;
         if (next < end) gather(st, splat, values, next, end);   // in flight during the blends below
@@ -134,33 +191,86 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
         const float4 *sb = s_b[buf];
         const float *sc = s_c[buf];
         int j = 0;
-        bool wave_live = true;
-        for (; j + kUnroll <= count; j += kUnroll) {
-            // The row terms of the next 8 splats, computed once per (splat, row): lane l takes
-            // splat j + l % 8 at its own row (lanes 8r .. 8r + 7 share row r), then each lane
-            // fetches splat u's terms from lane 8 (l / 8) + u of its group with a swizzle,
-            // which runs on the LDS pipe; the blend itself is bound by VALU issue.
-            const float4 rb = sb[j + (lane & 7)];
-            const float rdy = px.y - rb.x;
-            const float r_bdy = rb.z * rdy, r_e = splat_row_term(rdy, rb.w, rb.y);
-            static_assert(kUnroll == 8, "one splat per lane of an 8-lane group");
+        if (!done && !single) {
+            for (; j + kUnroll <= count;) {
+                // The row terms of the next 8 splats, computed once per (splat, row): lane l takes
+                // splat j + l % 8 at its own row (lanes 8r .. 8r + 7 share row r), then each lane
+                // fetches splat u's terms from lane 8 (l / 8) + u of its group with a swizzle,
+                // which runs on the LDS pipe; the blend itself is bound by VALU issue.
+                const float4 rb = sb[j + (lane & 7)];
+                const float rdy = px.y - rb.x;
+                const float r_bdy = rb.z * rdy, r_e = splat_row_term(rdy, rb.w, rb.y);
+                static_assert(kUnroll == 8, "one splat per lane of an 8-lane group");
 #define GS_BLEND_ROW(u) px.blend_row(sa[j + u], sc[j + u], group8_get<u>(r_bdy), group8_get<u>(r_e))
-            GS_BLEND_ROW(0);
-            GS_BLEND_ROW(1);
-            GS_BLEND_ROW(2);
-            GS_BLEND_ROW(3);
-            GS_BLEND_ROW(4);
-            GS_BLEND_ROW(5);
-            GS_BLEND_ROW(6);
-            GS_BLEND_ROW(7);
+                GS_BLEND_ROW(0);
+                GS_BLEND_ROW(1);
+                GS_BLEND_ROW(2);
+                GS_BLEND_ROW(3);
+                GS_BLEND_ROW(4);
+                GS_BLEND_ROW(5);
+                GS_BLEND_ROW(6);
+                GS_BLEND_ROW(7);
 #undef GS_BLEND_ROW
-            if (!__any(px.live())) {
-                wave_live = false;
-                break;
+                j += kUnroll;
+                const uint64_t m0 = __ballot(px.T[0] >= GS_T_EPS), m1 = __ballot(px.T[1] >= GS_T_EPS);
+                if ((m0 | m1) == 0) {
+                    done = true;
+                    break;
+                }
+                const uint32_t n0 = (uint32_t)__popcll(m0), n = n0 + (uint32_t)__popcll(m1);
+                if (n <= (uint32_t)kWave) {
+                    // Pack: lane k takes the wave's k-th live pixel, slot 0 ones (in lane order)
+                    // before slot 1 ones.  First write this lane's pixels that are not live.
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        if (!(px.T[i] >= GS_T_EPS)) {
+                            write_pixel<kAux>(p, ix + 8 * i, iy, px.r[i], px.g[i], px.b[i], px.T[i], px.blended[i]);
+                            total += px.blended[i];
+                        }
+                    const uint32_t k = (uint32_t)lane;
+                    const bool second = k >= n0;
+                    held = k < n;
+                    const int src = held ? (int)(second ? nth_set_bit(m1, k - n0) : nth_set_bit(m0, k)) : lane;
+                    float v[2][4];
+                    uint32_t nb[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        v[i][0] = lane_pull(src, px.T[i]);
+                        v[i][1] = lane_pull(src, px.r[i]);
+                        v[i][2] = lane_pull(src, px.g[i]);
+                        v[i][3] = lane_pull(src, px.b[i]);
+                        nb[i] = kAux ? (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)px.blended[i]) : 0u;
+                    }
+                    const int i = second ? 1 : 0;
+                    sx = tile_x * kTile + (src & 7) + 8 * i;
+                    sy = tile_y * kTile + wave * 8 + (src >> 3);
+                    px.T[0] = held ? (second ? v[1][0] : v[0][0]) : 0.0f;
+                    px.r[0] = second ? v[1][1] : v[0][1];
+                    px.g[0] = second ? v[1][2] : v[0][2];
+                    px.b[0] = second ? v[1][3] : v[0][3];
+                    px.blended[0] = second ? nb[1] : nb[0];
+                    px.T[1] = 0.0f;
+                    px.x0 = (float)sx;
+                    px.y = (float)sy;
+                    single = true;
+                    break;
+                }
             }
+            if (!done && !single)
+                for (; j < count; ++j) px.blend(sa[j], sb[j], sc[j]);
         }
-        if (wave_live)
-            for (; j < count; ++j) px.blend(sa[j], sb[j], sc[j]);
+        if (!done && single) {
+            for (; j + kUnroll <= count; j += kUnroll) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) px.blend_one(sa[j + u], sb[j + u], sc[j + u]);
+                if (!__any(px.T[0] >= GS_T_EPS)) {
+                    done = true;
+                    break;
+                }
+            }
+            if (!done)
+                for (; j < count; ++j) px.blend_one(sa[j], sb[j], sc[j]);
+        }
         if (next < end) {
 #pragma unroll
             for (int k = 0; k < kLoads; ++k) {
@@ -173,21 +283,15 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
         buf ^= 1;
     }
 
-    uint32_t total = 0;
+    if (!single) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int x = ix + 8 * i;
-        if (x < p.width && iy < p.height) {
-            const size_t pix = (size_t)iy * p.width + x;
-            p.image[pix * 3 + 0] = px.r[i] + px.T[i] * p.bg[0];
-            p.image[pix * 3 + 1] = px.g[i] + px.T[i] * p.bg[1];
-            p.image[pix * 3 + 2] = px.b[i] + px.T[i] * p.bg[2];
-            if (kAux) {
-                if (p.final_T) p.final_T[pix] = px.T[i];
-                if (p.n_blend) p.n_blend[pix] = px.blended[i];
-            }
+        for (int i = 0; i < 2; ++i) {
+            write_pixel<kAux>(p, ix + 8 * i, iy, px.r[i], px.g[i], px.b[i], px.T[i], px.blended[i]);
+            total += px.blended[i];
         }
-        total += px.blended[i];
+    } else if (held) {
+        write_pixel<kAux>(p, sx, sy, px.r[0], px.g[0], px.b[0], px.T[0], px.blended[0]);
+        total += px.blended[0];
     }
     if (kAux && p.blend_total) {
         __shared__ unsigned long long s_sum;
