@@ -392,6 +392,21 @@ def frame_stats(r, dev, scene, cams, img, bg):
     return tuple(v / len(cams) for v in (pairs, blends, n_visible))
 
 
+def settle_clock(r, dev, scene, cams, img, bg, seconds=0.3):
+    """Untimed frames for about `seconds`, so that the shader clock has left its idle state
+    before the warm-up and timed frames (a 20-frame timed region lasts ~12 ms).  Returns the
+    number of frames rendered."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for i in range(10):
+            r.render(dev, scene.sh_degree, cams[(n + i) % len(cams)], bg=bg, out=img)
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def timed_frames(r, dev, scene, cams, img, bg, steps, S, sort_mode):
     """`steps` frames back to back on one stream, or with S > 1 view i on context i mod S with
     its own stream, so that one view's compositing overlaps the next view's front end.
@@ -554,6 +569,7 @@ def main():
 
     pairs, blends, n_visible = frame_stats(r, dev, scene, cams, img, bg)
     log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} blended pairs={blends:.0f} ({len(cams)} view(s))")
+    settle = settle_clock(r, dev, scene, cams, img, bg)
     for i in range(args.warmup):
         r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     torch.cuda.synchronize()
@@ -594,6 +610,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_frames": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
