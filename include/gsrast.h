@@ -150,8 +150,8 @@ typedef struct {
 
 /* Sorting strategies; both give identical keys, values and ranges. */
 typedef enum {
-    /* depth-sort the Gaussians once (32-bit keys), list pairs in that order,
-       then a stable radix sort on the tile id alone (default) */
+    /* depth-sort the Gaussians once (32-bit keys), then build the per-tile lists in that
+       order (GS_OPT_BINNING says how; the default) */
     GS_SORT_DEPTH_FIRST = 0,
     /* duplicate 64-bit (tile << 32 | depth) keys in Gaussian order, then a
        stable LSD radix sort over the significant key bits */
@@ -176,14 +176,28 @@ typedef enum {
     GS_TILE_ELLIPSE = 1
 } gs_tile_test;
 
+/* How GS_SORT_DEPTH_FIRST turns the depth-ordered Gaussians into per-tile lists; both give
+   identical values and ranges (and keys, when emitted). */
+typedef enum {
+    /* group the tiles 8 x 8 into super-tiles, sort the Gaussians stably by super-tile (one
+       8-bit radix pass over about two entries per Gaussian), then expand each super-tile's
+       list into its 64 tiles, ranking a Gaussian within a tile by ballots in list order
+       (the default; used when the image has at most 256 super-tiles and 65536 tiles, and
+       more than one Gaussian, else GS_BINNING_RADIX) */
+    GS_BINNING_SUPER_TILE = 0,
+    /* list every (Gaussian, tile) pair, then a stable radix sort on the tile id */
+    GS_BINNING_RADIX = 1
+} gs_binning_mode;
+
 typedef enum {
     GS_OPT_SORT_MODE = 0,            /* gs_sort_mode, default GS_SORT_DEPTH_FIRST */
     GS_OPT_EMIT_KEYS = 1,            /* 1: gs_bin_and_sort materialises keys (default 1); gs_render never does */
     GS_OPT_MAX_DUPS = 2,             /* cap on pairs per frame, at most and by default 2^32-1 -> GS_ERR_CAPACITY */
     GS_OPT_MAX_WORKSPACE_BYTES = 3,  /* cap on context device memory (default: none) -> GS_ERR_OUT_OF_MEMORY */
     GS_OPT_PROFILE = 4,              /* 1: bracket every kernel with HIP events (see gs_profile_read) */
-    GS_OPT_TILE_TEST = 5             /* gs_tile_test, default GS_TILE_SQUARE; read by gs_preprocess, and the
+    GS_OPT_TILE_TEST = 5,            /* gs_tile_test, default GS_TILE_SQUARE; read by gs_preprocess, and the
                                         binning, compositing and backward of that projection follow it */
+    GS_OPT_BINNING = 6               /* gs_binning_mode, default GS_BINNING_SUPER_TILE (depth-first mode) */
 } gs_option;
 
 /* Per-stage timing collected while GS_OPT_PROFILE is 1. */
@@ -195,7 +209,7 @@ typedef enum {
     GS_STAGE_TILE_SORT = 4,    /* radix passes over the pair list */
     GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission), heaviest-first tile launch order */
     GS_STAGE_COMPOSITE = 6,
-    GS_STAGE_READBACK = 7,     /* pair-count copy to the host + stream wait */
+    GS_STAGE_READBACK = 7,     /* not recorded: the pair count reaches the host with no stream operation */
     GS_STAGE_BACKWARD_COMPOSITE = 8,   /* gs_backward: per-tile reverse walk */
     GS_STAGE_BACKWARD_SETUP = 9,       /* gs_backward: tile launch order; pair offsets in Gaussian order (depth-first mode) */
     GS_STAGE_BACKWARD_GAUSSIAN = 10,   /* gs_backward: per-Gaussian sums + projection and colour chain rule */
@@ -280,9 +294,9 @@ gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_cam
  * (64 MiB) that each device the library runs on holds until the process ends, and the call
  * makes no allocation (no hipMalloc, hipFree or event creation; profiling is off for it).
  * The context must exist (created beforehand: it holds the host-visible pair-count word).
- * Limits: the Gaussians and tiles may take at most half the array (104 bytes per Gaussian +
- * 12 per tile, about 320 k Gaussians at 1080p), the frame as a whole with its pairs
- * (12 bytes each, counted on the device) the full array; beyond either the call returns
+ * Limits: the Gaussians and tiles may take at most half the array (108 bytes per Gaussian +
+ * 12 per tile, about 310 k Gaussians at 1080p), the frame as a whole with its pairs
+ * (4 to 12 bytes each, counted on the device) the full array; beyond either the call returns
  * GS_ERR_CAPACITY (the pair case after waiting for the count, with nothing composited).
  * Every call on one device shares that device's array and leaves its contents behind:
  * calls that overlap on one device (other streams, threads or contexts) race, and the

@@ -18,6 +18,7 @@
 //                    per-Gaussian sums of those records + projection chain rule
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -86,6 +87,7 @@ struct gs_context {
     int profile = 0;
     int tile_test = GS_TILE_SQUARE;            // option
     int tile_test_used = GS_TILE_SQUARE;       // the rule of the last gs_preprocess
+    int binning = GS_BINNING_SUPER_TILE;       // option (depth-first mode)
     int64_t max_dups = kMaxPairs;
     int64_t max_workspace = -1;
     size_t workspace = 0;
@@ -96,6 +98,10 @@ struct gs_context {
         total, ellipse;
     // per-pair
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
+    // super-tile binning: the super list (ping-pong), its sort scratch and partition table,
+    // per-(segment, tile) counts, per-tile totals
+    DeviceBuffer skey[2], sval[2], ssort_scratch, spart, seg_tiles, tile_total, pcount;
+    bool packed_counts = false;                // the last gs_preprocess wrote pcount
     // per-tile
     DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
@@ -122,7 +128,7 @@ struct gs_context {
     const uint32_t *launch_order = nullptr;    // last binning: heaviest-first tile order (or null)
     const uint64_t *sorted_keys = nullptr;
     int64_t pair_capacity = 0;                 // entries the pair buffers hold
-    hipEvent_t total_ready = nullptr;          // the prefix sum ran (its last kernel stores host_total)
+    int64_t super_capacity = 0;                // entries the super-list buffers hold
 
     std::vector<TimedSpan> spans;
     size_t spans_used = 0;
@@ -257,7 +263,7 @@ int ceil_log2(int64_t v) {
 }
 
 // Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
-constexpr int kContextBuffers = 39;
+constexpr int kContextBuffers = 48;
 void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
     DeviceBuffer *all[kContextBuffers] = {
         &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
@@ -266,7 +272,8 @@ void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
         &ctx->pval[1], &ctx->keys_out, &ctx->keys_unsorted, &ctx->vals_unsorted, &ctx->psort_scratch, &ctx->part,
         &ctx->ranges, &ctx->tile_order, &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->pair_base,
         &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
-        &ctx->s2_trans, &ctx->s2_partial};
+        &ctx->s2_trans, &ctx->s2_partial, &ctx->skey[0], &ctx->skey[1], &ctx->sval[0], &ctx->sval[1],
+        &ctx->ssort_scratch, &ctx->spart, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount};
     for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
 
@@ -349,15 +356,6 @@ gs_status gs_context_create(gs_context **out, int device) {
         return GS_ERR_DEVICE;
     }
     ctx->host_total[1] = 0;
-    // the pair-count event: no timing, no system-scope fence (the count reaches the host by
-    // the scan's own system-scope store, so the event only has to say that the scan ran)
-    if (hipEventCreateWithFlags(&ctx->total_ready, hipEventDisableTiming | hipEventDisableSystemFence) !=
-        hipSuccess) {
-        (void)hipGetLastError();
-        (void)hipHostFree(ctx->host_total);
-        delete ctx;
-        return GS_ERR_DEVICE;
-    }
     hipError_t scratch_status;
     (void)scratch_address(device, &scratch_status);   // once per device; gs_render_noalloc reports failure
     *out = ctx;
@@ -376,7 +374,6 @@ void gs_context_destroy(gs_context *ctx) {
         (void)hipEventDestroy(t.end);
     }
     if (ctx->host_total) (void)hipHostFree(ctx->host_total);
-    if (ctx->total_ready) (void)hipEventDestroy(ctx->total_ready);
     delete ctx;
 }
 
@@ -408,6 +405,11 @@ gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
             if (value != GS_TILE_SQUARE && value != GS_TILE_ELLIPSE)
                 return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown tile test %lld", (long long)value);
             ctx->tile_test = (int)value;
+            return GS_OK;
+        case GS_OPT_BINNING:
+            if (value != GS_BINNING_SUPER_TILE && value != GS_BINNING_RADIX)
+                return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown binning %lld", (long long)value);
+            ctx->binning = (int)value;
             return GS_OK;
     }
     return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
@@ -463,6 +465,15 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
         GS_TRY(ensure(ctx, ctx->ellipse, nn * sizeof(EllipseRec)));
         p.ellipse = as<EllipseRec>(ctx->ellipse);
     }
+    // super-tile binning gathers each ranked Gaussian's tile and super-tile counts in one word
+    const int64_t super_tiles = (int64_t)((p.tiles_x + kSuperSide - 1) / kSuperSide) *
+                                ((p.tiles_y + kSuperSide - 1) / kSuperSide);
+    const bool pack = ctx->sort_mode == GS_SORT_DEPTH_FIRST && ctx->binning == GS_BINNING_SUPER_TILE &&
+                      (int64_t)p.tiles_x * p.tiles_y <= kMaxSuperBinningTiles && super_tiles <= kMaxSuper;
+    if (pack) {
+        GS_TRY(ensure(ctx, ctx->pcount, nn * sizeof(uint32_t)));
+        p.packed_count = as<uint32_t>(ctx->pcount);
+    }
 
     GS_TRY(span_begin(ctx, GS_STAGE_PREPROCESS, stream));
     launch_preprocess(p, stream);
@@ -470,6 +481,7 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     GS_TRY(span_end(ctx, stream));
 
     ctx->n = n;
+    ctx->packed_counts = pack;
     ctx->tile_test_used = ctx->tile_test;
     ctx->sh_degree = g->sh_degree;
     ctx->g_mean = g->mean;
@@ -612,6 +624,92 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     return GS_OK;
 }
 
+// Depth-first binning through super-tiles (GS_BINNING_SUPER_TILE) for at most `cap` pairs and
+// `scap` super-list entries: the super list, its sort by super-tile, the expansion into
+// per-tile lists and the launch order.  The kernels read both counts from device memory
+// (total[1] pairs, total[2] super-list entries), so this too can be enqueued before the host
+// knows them.
+static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, const uint32_t *order, int emit_keys,
+                                     int64_t cap, int64_t scap, hipStream_t stream) {
+    const int64_t tiles = (int64_t)ctx->tiles_x * ctx->tiles_y;
+    const int32_t super_x = (ctx->tiles_x + kSuperSide - 1) / kSuperSide;
+    const int32_t super_y = (ctx->tiles_y + kSuperSide - 1) / kSuperSide;
+    const size_t mm = (size_t)cap, ss = (size_t)scap;
+    const int64_t segs = super_segment_capacity(scap);
+    unsigned long long *d_total = as<unsigned long long>(ctx->total);
+    GS_TRY(ensure(ctx, ctx->pval[0], mm * 4));
+    if (emit_keys) GS_TRY(ensure(ctx, ctx->keys_out, mm * 8));
+    GS_TRY(ensure(ctx, ctx->skey[0], ss * 4));
+    GS_TRY(ensure(ctx, ctx->skey[1], ss * 4));
+    GS_TRY(ensure(ctx, ctx->sval[0], ss * 4));
+    GS_TRY(ensure(ctx, ctx->sval[1], ss * 4));
+    GS_TRY(ensure(ctx, ctx->ssort_scratch, (size_t)sort_scratch_words(scap) * 4));
+    GS_TRY(ensure(ctx, ctx->spart, (size_t)duplicate_partition_words(scap) * 4));
+    GS_TRY(ensure(ctx, ctx->seg_tiles, (size_t)segs * kWave * 4));
+    GS_TRY(ensure(ctx, ctx->tile_total, (size_t)tiles * 4));
+    ctx->sorted_values = nullptr;
+    ctx->sorted_keys = nullptr;
+    ctx->launch_order = nullptr;
+
+    DuplicateParams d{};
+    d.n_items = ctx->n;
+    d.num_dups = d_total + 2;
+    d.capacity = scap;
+    d.offsets = as<uint32_t>(ctx->offsets);
+    d.order = order;
+    d.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    d.super = 1;
+    d.tiles_x = super_x;
+    d.tile_keys = as<uint32_t>(ctx->skey[0]);
+    d.values = as<uint32_t>(ctx->sval[0]);
+    GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
+    launch_duplicate(d, as<uint32_t>(ctx->spart), stream);
+    GS_TRY(check_launch(ctx, "super-tile listing"));
+    GS_TRY(span_end(ctx, stream));
+
+    GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));
+    // by the super-tile id, the key's low 8 bits (the local rectangle above them travels along)
+    const int sbuf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->skey[0]), as<uint32_t>(ctx->sval[0]),
+                                                as<uint32_t>(ctx->skey[1]), as<uint32_t>(ctx->sval[1]), scap,
+                                                d_total + 2, 0, kRadixBits, as<uint32_t>(ctx->ssort_scratch), stream);
+    GS_TRY(check_launch(ctx, "super-tile sort"));
+    SuperBinParams b{};
+    b.tiles_x = ctx->tiles_x;
+    b.tiles_y = ctx->tiles_y;
+    b.super_x = super_x;
+    b.super_y = super_y;
+    b.super_totals = as<uint32_t>(ctx->ssort_scratch) + sort_totals_offset(scap);
+    b.keys = as<uint32_t>(ctx->skey[sbuf]);
+    b.gauss = as<uint32_t>(ctx->sval[sbuf]);
+    b.ellipse = ctx->tile_test_used == GS_TILE_ELLIPSE ? as<EllipseRec>(ctx->ellipse) : nullptr;
+    b.seg_tiles = as<uint32_t>(ctx->seg_tiles);
+    b.seg_capacity = segs;
+    b.tile_total = as<uint32_t>(ctx->tile_total);
+    b.ranges = as<uint32_t>(ctx->ranges);
+    b.num_dups = d_total + 1;
+    b.capacity = cap;
+    b.values = as<uint32_t>(ctx->pval[0]);
+    if (emit_keys) {
+        b.depth = pr->depth;
+        b.keys_out = as<uint64_t>(ctx->keys_out);
+    }
+    launch_super_binning(b, stream);
+    GS_TRY(check_launch(ctx, "super-tile expansion"));
+    GS_TRY(span_end(ctx, stream));
+
+    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
+    TileOrderParams o{};
+    o.tiles = (int32_t)tiles;
+    o.ranges = b.ranges;
+    o.order = as<uint32_t>(ctx->tile_order);
+    ctx->launch_order = launch_tile_order(o, stream) ? o.order : nullptr;
+    GS_TRY(check_launch(ctx, "tile order"));
+    GS_TRY(span_end(ctx, stream));
+    ctx->sorted_values = b.values;
+    ctx->sorted_keys = b.keys_out;
+    return GS_OK;
+}
+
 // Binning of the last preprocess.  The pair count M is known on the host only after
 // the prefix sum; rather than idling the GPU while the host waits for it, the pair
 // kernels are enqueued first on buffers sized from earlier frames (capacity), and
@@ -625,13 +723,18 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     const size_t nn = (size_t)(n > 0 ? n : 1);
     GS_TRY(ensure(ctx, ctx->offsets, nn * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->scan_scratch, (size_t)scan_scratch_words((int64_t)nn) * 8));
-    GS_TRY(ensure(ctx, ctx->total, 8));
+    GS_TRY(ensure(ctx, ctx->total, 3 * sizeof(unsigned long long)));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->tile_order, (size_t)tiles * sizeof(uint32_t)));
     unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
+    // super-tile binning where it applies (depth-first mode; counts packed for the scan)
+    const int64_t super_tiles = (int64_t)((ctx->tiles_x + kSuperSide - 1) / kSuperSide) *
+                                ((ctx->tiles_y + kSuperSide - 1) / kSuperSide);
+    const bool super_bin = depth_first && ctx->binning == GS_BINNING_SUPER_TILE && ctx->packed_counts && n >= 2 &&
+                           tiles <= kMaxSuperBinningTiles && super_tiles <= kMaxSuper;
     const uint32_t *order = nullptr;
-    int64_t M = 0;
+    int64_t M = 0, S = 0;
     bool speculated = false;
     if (n > 0) {
         const uint32_t *counts = pr->tile_count;   // tile counts in rank order
@@ -643,7 +746,8 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
                                                        as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n,
                                                        nullptr, 0, 32, as<uint32_t>(ctx->dsort_scratch), stream,
-                                                       pr->tile_count, as<uint32_t>(ctx->dcount));
+                                                       super_bin ? as<uint32_t>(ctx->pcount) : pr->tile_count,
+                                                       as<uint32_t>(ctx->dcount));
             GS_TRY(check_launch(ctx, "depth sort"));
             GS_TRY(span_end(ctx, stream));
             order = as<uint32_t>(ctx->dval[buf]);
@@ -654,28 +758,43 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         constexpr unsigned long long kNoCount = ~0ull;
         *ctx->host_total = kNoCount;
         GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
-        launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
-                    as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
+        if (super_bin)   // the super-list offsets; the count word holds both totals
+            launch_scan_pairs(counts, as<uint32_t>(ctx->offsets), n, d_total,
+                              as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
+        else
+            launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
+                        as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
         GS_TRY(check_launch(ctx, "scan"));
         GS_TRY(span_end(ctx, stream));
 
-        GS_TRY(span_begin(ctx, GS_STAGE_READBACK, stream));
-        GS_HIP(ctx, hipEventRecord(ctx->total_ready, stream));
-        GS_TRY(span_end(ctx, stream));
-        if (ctx->pair_capacity > 0) {
-            GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
+        if (ctx->pair_capacity > 0 && (!super_bin || ctx->super_capacity > 0)) {
+            if (super_bin)
+                GS_TRY(enqueue_super_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, ctx->super_capacity,
+                                           stream));
+            else
+                GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
             speculated = true;
         }
-        GS_HIP(ctx, hipEventSynchronize(ctx->total_ready));
+        // The host polls the count itself: no event in the stream (an event record cost the
+        // GPU ~5 us per frame at 10 k Gaussians).  After 200 ms without it, wait for the stream.
         unsigned long long published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
-        for (int spin = 0; published == kNoCount && spin < (1 << 20); ++spin)
-            published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
+        if (published == kNoCount) {
+            const auto t0 = std::chrono::steady_clock::now();
+            while ((published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE)) == kNoCount &&
+                   std::chrono::steady_clock::now() - t0 < std::chrono::milliseconds(200))
+                __builtin_ia32_pause();
+        }
         if (published == kNoCount) {   // not seen yet: wait for the whole stream, then it must be there
             GS_HIP(ctx, hipStreamSynchronize(stream));
             published = __atomic_load_n(ctx->host_total, __ATOMIC_ACQUIRE);
             if (published == kNoCount) return fail(ctx, GS_ERR_DEVICE, "the pair count did not reach the host");
         }
-        M = (int64_t)published;
+        if (super_bin) {
+            M = (int64_t)(published & ((1ull << kPairShift) - 1));
+            S = (int64_t)(published >> kPairShift);
+        } else {
+            M = (int64_t)published;
+        }
         // listings enqueued before this frame's count arrived have run (same stream)
         if (__atomic_load_n(ctx->host_total + 1, __ATOMIC_ACQUIRE) != 0) {
             __atomic_store_n(ctx->host_total + 1, 0ull, __ATOMIC_RELEASE);
@@ -686,15 +805,20 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             return fail(ctx, GS_ERR_CAPACITY, "%lld (Gaussian, tile) pairs exceed the cap of %lld", (long long)M,
                         (long long)ctx->max_dups);
     }
-    if (!speculated || M > ctx->pair_capacity) {
+    if (!speculated || M > ctx->pair_capacity || (super_bin && S > ctx->super_capacity)) {
         if (speculated) GS_HIP(ctx, hipStreamSynchronize(stream));   // buffers are about to move
         if (ctx->arena) {   // the fixed scratch: exactly the frame's pairs, no headroom
             ctx->pair_capacity = M > 1 ? M : 1;
+            ctx->super_capacity = S > 1 ? S : 1;
         } else {
-            const int64_t want = M + M / 4;
+            const int64_t want = M + M / 4, swant = S + S / 4;
             ctx->pair_capacity = want > 4096 ? want : 4096;
+            ctx->super_capacity = swant > 4096 ? swant : 4096;
         }
-        GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
+        if (super_bin)
+            GS_TRY(enqueue_super_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, ctx->super_capacity, stream));
+        else
+            GS_TRY(enqueue_pairs(ctx, pr, order, emit_keys, ctx->pair_capacity, stream));
     }
 
     ctx->num_dups = M;
@@ -789,10 +913,11 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
     if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
     if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_render_noalloc is already running on this context");
     // what the Gaussians and the tiles need before any pair (per Gaussian: record 64, depth 4,
-    // rect 8, count 4, two key/index pairs 16, gathered count 4, offsets 4; per tile: range 8,
-    // launch order 4), checked before anything is enqueued; the pairs are checked once counted
+    // rect 8, count 4, packed count 4, two key/index pairs 16, gathered count 4, offsets 4; per
+    // tile: range 8, launch order 4), checked before anything is enqueued; the pairs are checked
+    // once counted
     const int64_t tiles = (int64_t)((cam->width + GS_TILE - 1) / GS_TILE) * ((cam->height + GS_TILE - 1) / GS_TILE);
-    const int64_t fixed = g->n * 104 + tiles * 12;
+    const int64_t fixed = g->n * 108 + tiles * 12;
     if (fixed > (int64_t)(kNoAllocBytes / 2))
         return fail(ctx, GS_ERR_CAPACITY,
                     "gs_render_noalloc: %lld Gaussians and %lld tiles need %lld bytes, more than half of the "
@@ -811,9 +936,9 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
         saved[i] = *bufs[i];
         *bufs[i] = DeviceBuffer{};
     }
-    const int64_t saved_capacity = ctx->pair_capacity;
+    const int64_t saved_capacity = ctx->pair_capacity, saved_super = ctx->super_capacity;
     const int saved_profile = ctx->profile;
-    ctx->pair_capacity = 0;   // size the pair buffers from the frame's own count
+    ctx->pair_capacity = ctx->super_capacity = 0;   // size the pair buffers from the frame's own counts
     ctx->profile = 0;         // timing events would be allocated
     ctx->arena = base;
     ctx->arena_size = kNoAllocBytes;
@@ -829,6 +954,7 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
     ctx->arena = nullptr;
     ctx->arena_size = ctx->arena_used = 0;
     ctx->pair_capacity = saved_capacity;
+    ctx->super_capacity = saved_super;
     ctx->profile = saved_profile;
     // the frame's projection and binning lived in the scratch: none is left on the context
     ctx->n = -1;

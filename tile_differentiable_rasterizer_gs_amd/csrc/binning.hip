@@ -1,0 +1,340 @@
+// Per-tile lists through super-tiles: the depth-ranked Gaussians expanded into their tiles
+// without sorting the (Gaussian, tile) pairs.
+//
+// Lesson "3D Gaussian Splatting from scratch", flowchart steps "Assign to tiles (16x16
+// screen-space)" and "Depth-sort per tile": each tile gets the Gaussians whose footprint
+// meets it, nearest first (ties by index).  The Gaussians arrive in that order (depth ranks).
+// Tiles are grouped 8 x 8 into super-tiles; every Gaussian is listed once per super-tile of
+// its rectangle, with its part of the rectangle inside that super-tile in the key, and that
+// short list (about two entries per Gaussian at 1080p) is sorted stably by super-tile in one
+// 8-bit radix pass (sort.hip), so each super-tile's list keeps the depth order.  Here each super-tile's list is cut into segments of kSegment entries, one
+// wave each, taken 64 entries (one per lane) at a time.  An entry's tiles inside its
+// super-tile form a 64-bit mask (bit 8 r + c: tile column c, row r of the super-tile), one
+// row span per tile row: the rectangle's columns, or the exact-footprint rule's span.
+//   super_count_kernel   pairs per (segment, tile), from span corners in an LDS difference grid
+//   super_column_kernel  per super-tile: each segment's offset within each tile, tile totals
+//   tile_ranges_kernel   exclusive scan of the tile totals: [start, end) per tile
+//   super_place_kernel   per tile of the super-tile, a ballot ranks the chunk's entries that
+//                        meet it, and they write at the tile's next position plus their rank
+// The lists equal those of a stable sort of the pairs by tile, and each pair is written once,
+// 4 bytes (plus 8 when the 64-bit keys are asked for).
+#include "gs_internal.h"
+
+namespace gsr {
+namespace {
+
+constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup ...
+constexpr int kRangePer = kMaxSuperBinningTiles / kRangeThreads;   // ... of 64 tiles per thread
+constexpr int kColumnWaves = 16;      // super_column_kernel: waves per super-tile ...
+constexpr int kColumnBatch = 8;       // ... and segment counts each lane loads per round trip
+
+// Segment geometry from the super-tile totals, built by the first wave of each workgroup:
+// super-tile s owns segments [first[s], first[s + 1]) and entries [start[s], start[s + 1]) of
+// the sorted super list.
+struct SegmentTable {
+    uint32_t first[kMaxSuper + 1];
+    uint32_t start[kMaxSuper + 1];
+};
+
+__device__ void build_segment_table(const SuperBinParams &p, SegmentTable &t) {
+    constexpr int kPer = kMaxSuper / kWave;
+    const int lane = threadIdx.x;
+    const int supers = p.super_x * p.super_y;
+    if (lane < kWave) {   // the first wave builds it
+        uint32_t n[kPer], segs[kPer], sum_n = 0, sum_s = 0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int s = lane * kPer + k;
+            n[k] = s < supers ? p.super_totals[s] : 0u;
+            segs[k] = (n[k] + kSegment - 1) / kSegment;
+            sum_n += n[k];
+            sum_s += segs[k];
+        }
+        uint32_t inc_n = sum_n, inc_s = sum_s;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t a = (uint32_t)__shfl_up((int)inc_n, d), b = (uint32_t)__shfl_up((int)inc_s, d);
+            if (lane >= d) {
+                inc_n += a;
+                inc_s += b;
+            }
+        }
+        uint32_t run_n = inc_n - sum_n, run_s = inc_s - sum_s;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            t.start[lane * kPer + k] = run_n;
+            t.first[lane * kPer + k] = run_s;
+            run_n += n[k];
+            run_s += segs[k];
+        }
+        if (lane == kWave - 1) {
+            t.start[kMaxSuper] = run_n;
+            t.first[kMaxSuper] = run_s;
+        }
+    }
+    __syncthreads();
+}
+
+// Super-tile of segment seg (< first[kMaxSuper]): the last s with first[s] <= seg; super-tiles
+// without entries own no segment and share the next one's first.
+__device__ inline int segment_super(const SegmentTable &t, uint32_t seg) {
+    int lo = 0, hi = kMaxSuper - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.first[mid] <= seg) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+struct SegmentRange {
+    int sx, sy;
+    uint32_t a, b;   // entries [a, b) of the sorted super list
+};
+
+__device__ inline SegmentRange segment_range(const SuperBinParams &p, const SegmentTable &t, uint32_t seg) {
+    const int s = segment_super(t, seg);
+    SegmentRange r;
+    r.sx = s % p.super_x;
+    r.sy = s / p.super_x;
+    r.a = t.start[s] + (seg - t.first[s]) * (uint32_t)kSegment;
+    r.b = min(t.start[s + 1], r.a + (uint32_t)kSegment);
+    return r;
+}
+
+// An entry's part of its rectangle inside the super-tile, from its key: columns [a, b),
+// rows [r0, r1), relative to the super-tile's first tile.
+struct LocalRect {
+    uint32_t a, b, r0, r1;
+};
+__device__ inline LocalRect local_rect(uint32_t key) {
+    return LocalRect{(key >> 8) & 15u, (key >> 12) & 15u, (key >> 16) & 15u, (key >> 20) & 15u};
+}
+
+// The exact-footprint rule's kept columns [sa, sb) of local row `row` (relative, like lr):
+// the row span within the entry's columns of the super-tile, which equals the span within
+// the whole rectangle clamped to the super-tile.
+__device__ inline void local_span(const EllipseRec &E, const LocalRect &lr, uint32_t cx, uint32_t cy, uint32_t row,
+                                  uint32_t &sa, uint32_t &sb) {
+    row_span(E, cx + lr.a, cx + lr.b, cy + row, sa, sb);
+    sa -= cx;
+    sb -= cx;
+}
+
+// An entry's tiles inside super-tile (sx, sy) as a 64-bit mask (bit 8 r + c for tile column
+// c, row r of the super-tile): the square rule's rectangle, or each row's span.
+__device__ inline uint64_t entry_mask(const SuperBinParams &p, uint32_t key, uint32_t g, int sx, int sy) {
+    const LocalRect lr = local_rect(key);
+    uint64_t mask = 0;
+    if (p.ellipse) {
+        const EllipseRec E = p.ellipse[g];
+        const uint32_t cx = (uint32_t)sx * kSuperSide, cy = (uint32_t)sy * kSuperSide;
+        for (uint32_t row = lr.r0; row < lr.r1; ++row) {
+            uint32_t sa, sb;
+            local_span(E, lr, cx, cy, row, sa, sb);
+            if (sa < sb) mask |= ((1ull << (sb - sa)) - 1ull) << (kSuperSide * row + sa);
+        }
+    } else if (lr.a < lr.b && lr.r0 < lr.r1) {
+        // the row's bits repeated on rows r0 .. r1 - 1 (one byte per row: no carries)
+        const uint64_t rows = (0x0101010101010101ull >> (kSuperSide * (kSuperSide - (lr.r1 - lr.r0)))) << (kSuperSide * lr.r0);
+        mask = (((1ull << (lr.b - lr.a)) - 1ull) << lr.a) * rows;
+    }
+    return mask;
+}
+
+static_assert(kSegment == kWave, "one entry per lane");
+
+// Pairs per (segment, tile of its super-tile): each entry adds +1 / -1 at the corners of its
+// part (the rectangle, or each row span of the exact-footprint rule) in a 9 x 9 difference
+// grid, whose 2D prefix is then the count of each tile.  The square rule reads the keys only.
+__global__ __launch_bounds__(kWave) void super_count_kernel(SuperBinParams p) {
+    __shared__ SegmentTable t;
+    __shared__ uint32_t s_diff[kSuperSide + 1][kSuperSide + 1];
+    build_segment_table(p, t);
+    const uint32_t seg = blockIdx.x;
+    if (seg >= t.first[kMaxSuper]) return;
+    const SegmentRange r = segment_range(p, t, seg);
+    const uint32_t lane = threadIdx.x;
+    for (uint32_t i = lane; i < (kSuperSide + 1) * (kSuperSide + 1); i += kWave) (&s_diff[0][0])[i] = 0u;
+    const uint32_t e = r.a + lane;
+    const uint32_t key = p.keys[e < r.b ? e : r.a];
+    __syncthreads();
+    auto corners = [&](uint32_t r0, uint32_t r1, uint32_t a, uint32_t b) {   // rows [r0, r1), columns [a, b)
+        atomicAdd(&s_diff[r0][a], 1u);
+        atomicAdd(&s_diff[r0][b], 0xffffffffu);
+        atomicAdd(&s_diff[r1][a], 0xffffffffu);
+        atomicAdd(&s_diff[r1][b], 1u);
+    };
+    if (e < r.b) {
+        const LocalRect lr = local_rect(key);
+        if (p.ellipse) {
+            const EllipseRec E = p.ellipse[p.gauss[e]];
+            const uint32_t cx = (uint32_t)r.sx * kSuperSide, cy = (uint32_t)r.sy * kSuperSide;
+            for (uint32_t row = lr.r0; row < lr.r1; ++row) {
+                uint32_t sa, sb;
+                local_span(E, lr, cx, cy, row, sa, sb);
+                if (sa < sb) corners(row, row + 1, sa, sb);
+            }
+        } else if (lr.a < lr.b && lr.r0 < lr.r1) {
+            corners(lr.r0, lr.r1, lr.a, lr.b);
+        }
+    }
+    __syncthreads();
+    if (lane <= kSuperSide)
+        for (int c = 1; c <= kSuperSide; ++c) s_diff[lane][c] += s_diff[lane][c - 1];
+    __syncthreads();
+    if (lane <= kSuperSide)
+        for (int row = 1; row <= kSuperSide; ++row) s_diff[row][lane] += s_diff[row - 1][lane];
+    __syncthreads();
+    p.seg_tiles[(size_t)seg * kWave + lane] = s_diff[lane / kSuperSide][lane % kSuperSide];
+}
+
+// One workgroup per super-tile; lane k of each wave owns tile k.  The super-tile's segments are
+// split into kColumnWaves contiguous blocks, one per wave: each wave sums its block's counts,
+// the waves' sums are scanned through LDS, and each wave then replaces every count of its
+// block by the pairs of the tile in the segments before it.  The total is the tile's.
+__global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(SuperBinParams p) {
+    __shared__ SegmentTable t;
+    __shared__ uint32_t s_sum[kColumnWaves][kWave];
+    build_segment_table(p, t);
+    const int s = blockIdx.x;
+    if (s >= p.super_x * p.super_y) return;
+    const uint32_t lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const uint32_t j0 = t.first[s], j1 = t.first[s + 1];
+    const uint32_t per = (j1 - j0 + kColumnWaves - 1) / kColumnWaves;
+    const uint32_t lo = min(j1, j0 + wave * per), hi = min(j1, lo + per);
+    uint32_t sum = 0;
+    for (uint32_t j = lo; j < hi; j += kColumnBatch) {
+        uint32_t c[kColumnBatch];
+#pragma unroll
+        for (int q = 0; q < kColumnBatch; ++q) c[q] = j + q < hi ? p.seg_tiles[(size_t)(j + q) * kWave + lane] : 0u;
+#pragma unroll
+        for (int q = 0; q < kColumnBatch; ++q) sum += c[q];
+    }
+    s_sum[wave][lane] = sum;
+    __syncthreads();
+    uint32_t off = 0, total = 0;
+    for (uint32_t w = 0; w < (uint32_t)kColumnWaves; ++w) {
+        const uint32_t v = s_sum[w][lane];
+        off += w < wave ? v : 0u;
+        total += v;
+    }
+    for (uint32_t j = lo; j < hi; j += kColumnBatch) {
+        uint32_t c[kColumnBatch];
+#pragma unroll
+        for (int q = 0; q < kColumnBatch; ++q) c[q] = j + q < hi ? p.seg_tiles[(size_t)(j + q) * kWave + lane] : 0u;
+#pragma unroll
+        for (int q = 0; q < kColumnBatch; ++q) {
+            if (j + q < hi) p.seg_tiles[(size_t)(j + q) * kWave + lane] = off;
+            off += c[q];
+        }
+    }
+    const int tx = (s % p.super_x) * kSuperSide + (int)lane % kSuperSide;
+    const int ty = (s / p.super_x) * kSuperSide + (int)lane / kSuperSide;
+    if (wave == 0 && tx < p.tiles_x && ty < p.tiles_y) p.tile_total[ty * p.tiles_x + tx] = total;
+}
+
+// [start, end) of every tile: an exclusive scan of the tile totals in tile order (one
+// workgroup, each thread kRangePer consecutive tiles); (0, 0) for a tile without pairs.
+__global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinParams p) {
+    __shared__ uint32_t s_wave[kRangeThreads / kWave];
+    const int tiles = p.tiles_x * p.tiles_y;
+    const int lo = (int)threadIdx.x * kRangePer;
+    uint32_t c[kRangePer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kRangePer; ++i) {
+        c[i] = lo + i < tiles ? p.tile_total[lo + i] : 0u;
+        sum += c[i];
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t inc = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int w = 0; w < wave; ++w) run += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < kRangePer; ++i) {
+        if (lo + i < tiles) {
+            reinterpret_cast<uint2 *>(p.ranges)[lo + i] = c[i] ? make_uint2(run, run + c[i]) : make_uint2(0u, 0u);
+            run += c[i];
+        }
+    }
+}
+
+// The segment's entries, one per lane, in list order.  For each tile k of the super-tile (a
+// uniform loop): the ballot of the lanes whose entry meets tile k gives each such lane its
+// rank among them, and they write their Gaussians at the tile's position for this segment
+// (its start plus the segment's offset, held by lane k and read with readlane) plus the rank:
+// one store instruction writes a contiguous run.  When the frame has more pairs than the
+// value buffer holds (a launch on buffers sized for an earlier frame, which the host then
+// repeats) nothing is written.  kKeys: also the 64-bit keys.  kNarrow: positions below 2^30,
+// so a store's address is the buffer plus a 32-bit byte offset.
+template <bool kKeys, bool kNarrow>
+__global__ __launch_bounds__(kWave) void super_place_kernel(SuperBinParams p) {
+    __shared__ SegmentTable t;
+    if ((int64_t)*p.num_dups > p.capacity) return;
+    build_segment_table(p, t);
+    const uint32_t seg = blockIdx.x;
+    if (seg >= t.first[kMaxSuper]) return;
+    const SegmentRange r = segment_range(p, t, seg);
+    const uint32_t lane = threadIdx.x;
+    const uint32_t e = r.a + lane;
+    const bool valid = e < r.b;
+    const uint32_t key = p.keys[valid ? e : r.a];   // a lane past the segment meets no tile
+    const uint32_t g = p.gauss[valid ? e : r.a];
+    const uint32_t tx = (uint32_t)r.sx * kSuperSide + lane % kSuperSide;
+    const uint32_t ty = (uint32_t)r.sy * kSuperSide + lane / kSuperSide;
+    const bool have_tile = tx < (uint32_t)p.tiles_x && ty < (uint32_t)p.tiles_y;
+    const uint32_t at = have_tile ? p.ranges[2 * (ty * p.tiles_x + tx)] + p.seg_tiles[(size_t)seg * kWave + lane] : 0u;
+    const uint64_t mask = valid ? entry_mask(p, key, g, r.sx, r.sy) : 0ull;
+    const uint32_t mlo = (uint32_t)mask, mhi = (uint32_t)(mask >> 32);
+    const uint32_t dbits = kKeys ? __float_as_uint(p.depth[g]) : 0u;
+    const uint32_t tile0 = (uint32_t)r.sy * kSuperSide * p.tiles_x + (uint32_t)r.sx * kSuperSide;
+    // Every load has landed here.  Said explicitly: otherwise the compiler counts the Gaussian's
+    // load (skipped on some paths) as pending at each store below, and since the counter also
+    // counts stores, each store would wait for all the earlier ones.
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int k = 0; k < kWave; ++k) {
+        const uint32_t meets = __builtin_amdgcn_ubfe(k < 32 ? mlo : mhi, (uint32_t)(k & 31), 1u);
+        const uint64_t bk = __ballot(meets != 0u);
+        if (bk == 0) continue;
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)at, k);
+        if (meets != 0u) {
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u));
+            if (kNarrow) {
+                *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(p.values) + ((rank << 2) + (base << 2))) = g;
+            } else {
+                p.values[(size_t)base + rank] = g;
+            }
+            if (kKeys) {
+                const uint32_t tile = tile0 + (uint32_t)(k / kSuperSide) * p.tiles_x + (uint32_t)(k % kSuperSide);
+                p.keys_out[(size_t)base + rank] = ((uint64_t)tile << 32) | dbits;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+int64_t super_segment_capacity(int64_t entries) { return entries / kSegment + kMaxSuper + 1; }
+
+void launch_super_binning(const SuperBinParams &p, hipStream_t s) {
+    const unsigned segs = (unsigned)p.seg_capacity;
+    super_count_kernel<<<segs, kWave, 0, s>>>(p);
+    super_column_kernel<<<kMaxSuper, kColumnWaves * kWave, 0, s>>>(p);
+    tile_ranges_kernel<<<1, kRangeThreads, 0, s>>>(p);
+    const bool narrow = p.capacity <= ((int64_t)1 << 30);
+    if (p.keys_out)
+        super_place_kernel<true, false><<<segs, kWave, 0, s>>>(p);
+    else if (narrow)
+        super_place_kernel<false, true><<<segs, kWave, 0, s>>>(p);
+    else
+        super_place_kernel<false, false><<<segs, kWave, 0, s>>>(p);
+}
+
+}  // namespace gsr

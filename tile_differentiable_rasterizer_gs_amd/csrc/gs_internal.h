@@ -102,6 +102,7 @@ struct PreprocessParams {
     uint32_t *depth_key;         // [n] or null: visible ? bits(depth) : 0xffffffff
     uint32_t *depth_index;       // [n] or null: g
     EllipseRec *ellipse;         // [n] or null: exact-footprint rule (tile counts from the row spans)
+    uint32_t *packed_count;      // [n] or null: pack_counts(tile count, rect), for super-tile binning
 };
 void launch_preprocess(const PreprocessParams &p, hipStream_t s);
 
@@ -117,6 +118,11 @@ int64_t scan_scratch_words(int64_t n);
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
                  unsigned long long *total, unsigned long long *scratch, hipStream_t s,
                  unsigned long long *host_total = nullptr);
+// The same over packed counts (tile count | super count << kPackShift): out[i] = the super
+// counts before i; total[0] = tiles | super-tiles << kPairShift (also to host_total),
+// total[1] = the tile total, total[2] = the super-tile total.
+void launch_scan_pairs(const uint32_t *packed, uint32_t *out, int64_t n, unsigned long long *total,
+                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total);
 
 // ---------------------------------------------------------------------------
 // stable LSD radix sort of (key, uint32 value) pairs
@@ -134,6 +140,65 @@ template <typename K>
 int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, const unsigned long long *n_dev,
                      int begin_bit, int end_bit, uint32_t *scratch, hipStream_t s,
                      const uint32_t *gather_src = nullptr, uint32_t *gathered_out = nullptr);
+// Offset (in uint32 words) into the scratch of radix_sort_pairs(n) of the per-digit totals
+// of the last pass: totals[d] = elements whose last-pass digit is d.
+int64_t sort_totals_offset(int64_t n);
+
+// ---------------------------------------------------------------------------
+// super-tile binning (depth-first mode, GS_BINNING_SUPER_TILE)
+// ---------------------------------------------------------------------------
+// Tiles are grouped 8 x 8 into super-tiles.  Each depth-ranked Gaussian is listed once per
+// super-tile of its rectangle, that list is sorted stably by super-tile (one 8-bit radix
+// pass), and each super-tile's list, cut into segments, is expanded into its 64 tiles.
+constexpr int kSuperShift = 3;                     // 8 x 8 tiles per super-tile
+constexpr int kSuperSide = 1 << kSuperShift;
+constexpr int kMaxSuper = 1 << kRadixBits;         // super-tiles one 8-bit pass orders
+constexpr int kMaxSuperBinningTiles = 1 << 16;     // tile counts fit the packed count below
+constexpr int kSegment = 64;                       // super-list entries per segment (one wave, one per lane)
+constexpr int kPackShift = 17;                     // packed count: tile count | super count << 17
+constexpr int kPairShift = 36;                     // scan of packed counts: tiles | super-tiles << 36
+
+// Super-list key: the super-tile id (bits 0-7, what the list is sorted by) and the part of the
+// Gaussian's tile rectangle inside that super-tile, relative to its first tile: columns
+// [a, b) and rows [r0, r1), each bound in 4 bits.
+__host__ __device__ inline uint32_t super_key(uint32_t sid, uint32_t a, uint32_t b, uint32_t r0, uint32_t r1) {
+    return sid | (a << 8) | (b << 12) | (r0 << 16) | (r1 << 20);
+}
+
+// The super-tile rectangle of a tile rectangle {x0 | x1 << 16, y0 | y1 << 16} (empty stays empty).
+__host__ __device__ inline uint2 super_rect(uint2 rc) {
+    const uint32_t x0 = rc.x & 0xffffu, x1 = rc.x >> 16, y0 = rc.y & 0xffffu, y1 = rc.y >> 16;
+    if (x1 <= x0 || y1 <= y0) return make_uint2(0u, 0u);
+    return make_uint2((x0 >> kSuperShift) | ((((x1 - 1) >> kSuperShift) + 1) << 16),
+                      (y0 >> kSuperShift) | ((((y1 - 1) >> kSuperShift) + 1) << 16));
+}
+// A Gaussian's tile count and number of super-tiles in one word (tile count <= 65536).
+__host__ __device__ inline uint32_t pack_counts(uint32_t tile_count, uint2 rc) {
+    if (tile_count == 0) return 0u;
+    const uint2 sr = super_rect(rc);
+    return tile_count | (((sr.x >> 16) - (sr.x & 0xffffu)) * ((sr.y >> 16) - (sr.y & 0xffffu)) << kPackShift);
+}
+
+struct SuperBinParams {
+    int32_t tiles_x, tiles_y, super_x, super_y;
+    const uint32_t *super_totals;  // [kMaxSuper] entries of each super-tile in the sorted super list
+    const uint32_t *keys;          // sorted super list: super_key of each entry
+    const uint32_t *gauss;         // sorted super list: the Gaussian of each entry
+    const EllipseRec *ellipse;     // null, or the exact-footprint rule (a row span per tile row)
+    uint32_t *seg_tiles;           // [segment capacity][64] pairs per (segment, tile), then offsets
+    int64_t seg_capacity;          // segments the grids cover
+    uint32_t *tile_total;          // [tiles] pairs per tile
+    uint32_t *ranges;              // [tiles][2]
+    const unsigned long long *num_dups;   // device: the frame's pair count
+    int64_t capacity;              // entries `values` holds; with more pairs nothing is written
+    uint32_t *values;              // out: Gaussian index per entry, by tile then depth
+    const float *depth;            // key emission (optional): keys_out[e] = tile << 32 | bits(depth[g])
+    uint64_t *keys_out;
+};
+// Segments the grids need for a super list of `entries` entries.
+int64_t super_segment_capacity(int64_t entries);
+// Per-tile counts, ranges, then the values (and keys).
+void launch_super_binning(const SuperBinParams &p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // pair listing, ranges
@@ -154,6 +219,8 @@ struct DuplicateParams {
     uint16_t *tile_keys16;       // ... or as 16 bits (at most 65536 tiles); entry count multiple of 8 per block
     uint32_t *values;            // Gaussian index
     const EllipseRec *ellipse;   // null, or the exact-footprint rule: only the row spans are listed
+    int32_t super;               // 1: list each Gaussian once per super-tile of its rectangle, the key
+                                 // super_key(...) into tile_keys; tiles_x is then the super-tile width
     unsigned long long *fault;   // with ellipse: host-coherent word, bit 0 set (system scope) when a
                                  // Gaussian's row spans do not add up to its tile count
     const uint32_t *tile_count;  // [n] (needed with ellipse)

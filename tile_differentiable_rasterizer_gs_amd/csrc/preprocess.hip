@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     rec[3] = make_float4(C, tz, 0.0f, 0.0f);
     p.depth[g] = tz;
     p.rect[g] = make_uint2(x0 | (x1 << 16), y0 | (y1 << 16));
-    p.tile_count[g] = !visible ? 0u : (p.ellipse ? kept : (x1 - x0) * (y1 - y0));
+    const uint32_t tile_count = !visible ? 0u : (p.ellipse ? kept : (x1 - x0) * (y1 - y0));
+    p.tile_count[g] = tile_count;
+    if (p.packed_count) p.packed_count[g] = pack_counts(tile_count, make_uint2(x0 | (x1 << 16), y0 | (y1 << 16)));
     if (p.depth_key) {
         // Gaussians without pairs sort last: interleaved with the others they would dilute the
         // pair listing's rank windows (a 2048-entry block would meet thousands of empty ranks)

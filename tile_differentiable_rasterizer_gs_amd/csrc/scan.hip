@@ -46,7 +46,10 @@ __device__ inline T block_exclusive_scan(T x, T *total) {
     return before + inc - x;
 }
 
-template <typename TIn>
+// kPair: the inputs are packed counts (tile count | super count << kPackShift), summed as
+// two fields of one uint64 (tiles | super-tiles << kPairShift; neither field overflows: the
+// tile total is below 2^32 by the callers' cap, the super total below 2^28).
+template <typename TIn, bool kPair>
 __device__ inline void load_items(const TIn *in, const uint32_t *gather, int64_t n, int64_t base,
                                   unsigned long long v[kScanItems]) {
     const int64_t first = base + (int64_t)threadIdx.x * kScanItems;
@@ -55,14 +58,16 @@ __device__ inline void load_items(const TIn *in, const uint32_t *gather, int64_t
         const int64_t i = first + k;
         v[k] = 0;
         if (i < n) v[k] = gather ? (unsigned long long)in[gather[i]] : (unsigned long long)in[i];
+        if (kPair)
+            v[k] = (v[k] & ((1ull << kPackShift) - 1)) | ((v[k] >> kPackShift) << kPairShift);
     }
 }
 
-template <typename TIn>
+template <typename TIn, bool kPair>
 __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const TIn *in, const uint32_t *gather,
                                                              int64_t n, unsigned long long *partials) {
     unsigned long long v[kScanItems];
-    load_items(in, gather, n, (int64_t)blockIdx.x * kScanTile, v);
+    load_items<TIn, kPair>(in, gather, n, (int64_t)blockIdx.x * kScanTile, v);
     unsigned long long s = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) s += v[k];
@@ -76,7 +81,9 @@ __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const TIn *in, cons
 // totals before this block, added up here (few blocks: it saves a kernel).  When
 // `total` is non-null the last block writes the grand total there, and also to
 // `host_total` (host-coherent memory, a system-scope store) when that is non-null.
-template <typename TIn, typename TOut>
+// kPair: packed inputs (load_items); out[i] is the super-tile part of the prefix.
+// kDecode: the total is packed; total[1] and total[2] also get its two fields.
+template <typename TIn, typename TOut, bool kPair, bool kDecode>
 __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, const uint32_t *gather,
                                                                 int64_t n, const unsigned long long *prefix,
                                                                 const unsigned long long *block_sums, TOut *out,
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
     }
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
     unsigned long long v[kScanItems];
-    load_items(in, gather, n, base, v);
+    load_items<TIn, kPair>(in, gather, n, base, v);
     unsigned long long s = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) s += v[k];
@@ -102,12 +109,16 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const int64_t i = first + k;
-        if (i < n) out[i] = (TOut)run;
+        if (i < n) out[i] = kPair ? (TOut)(run >> kPairShift) : (TOut)run;
         run += v[k];
     }
     if (total && threadIdx.x == 0 && blockIdx.x == gridDim.x - 1) {
         const unsigned long long all = offset + block_total;
         *total = all;
+        if (kDecode) {
+            total[1] = all & ((1ull << kPairShift) - 1);
+            total[2] = all >> kPairShift;
+        }
         if (host_total) __hip_atomic_store(host_total, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
@@ -118,27 +129,28 @@ inline int64_t blocks_for(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
 constexpr int64_t kDirectBlocks = 1024;
 
 // Scans `in` (n values) into `out`; partials for the next level live in scratch.
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool kPair, bool kDecode>
 void scan_level(const TIn *in, const uint32_t *gather, TOut *out, int64_t n, unsigned long long *total,
                 unsigned long long *host_total, unsigned long long *scratch, hipStream_t s) {
     const int64_t nb = blocks_for(n);
     if (nb == 1) {
-        scan_downsweep_kernel<TIn, TOut><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, nullptr, out, total,
-                                                              host_total);
+        scan_downsweep_kernel<TIn, TOut, kPair, kDecode><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, nullptr, out,
+                                                                              total, host_total);
         return;
     }
     unsigned long long *partials = scratch;
-    scan_reduce_kernel<TIn><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials);
+    scan_reduce_kernel<TIn, kPair><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials);
     if (nb <= kDirectBlocks) {   // each block adds up the partials before it
-        scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, nullptr, partials, out,
-                                                                         total, host_total);
+        scan_downsweep_kernel<TIn, TOut, kPair, kDecode><<<(unsigned)nb, kBlock, 0, s>>>(
+            in, gather, n, nullptr, partials, out, total, host_total);
         return;
     }
-    // exclusive scan of the partials, in place (reads before writes within each block)
-    scan_level<unsigned long long, unsigned long long>(partials, nullptr, partials, nb, total, host_total,
-                                                       scratch + nb, s);
-    scan_downsweep_kernel<TIn, TOut><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, nullptr, out,
-                                                                     nullptr, nullptr);
+    // exclusive scan of the partials (already in the packed form), in place (reads before
+    // writes within each block); that level writes the total
+    scan_level<unsigned long long, unsigned long long, false, kDecode>(partials, nullptr, partials, nb, total,
+                                                                      host_total, scratch + nb, s);
+    scan_downsweep_kernel<TIn, TOut, kPair, false><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, nullptr,
+                                                                                  out, nullptr, nullptr);
 }
 
 }  // namespace
@@ -152,7 +164,12 @@ int64_t scan_scratch_words(int64_t n) {
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
                  unsigned long long *total, unsigned long long *scratch, hipStream_t s,
                  unsigned long long *host_total) {
-    scan_level<uint32_t, uint32_t>(in, gather, out, n, total, host_total, scratch, s);
+    scan_level<uint32_t, uint32_t, false, false>(in, gather, out, n, total, host_total, scratch, s);
+}
+
+void launch_scan_pairs(const uint32_t *packed, uint32_t *out, int64_t n, unsigned long long *total,
+                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total) {
+    scan_level<uint32_t, uint32_t, true, true>(packed, nullptr, out, n, total, host_total, scratch, s);
 }
 
 }  // namespace gsr
