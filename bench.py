@@ -56,15 +56,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_bytes(n, sh_degree, m, n_visible):
-    """Algorithmic HBM bytes per frame for each stage (depth-first mode)."""
+def stage_bytes(n, sh_degree, m, n_visible, supers, tiles):
+    """Algorithmic HBM bytes per frame for each stage (depth-first mode).  m pairs; supers > 0:
+    the per-tile lists came from super-tile binning over `supers` super-list entries, else from
+    the radix sort of the pairs on the tile id."""
     K = (sh_degree + 1) ** 2
     pre = n * ((3 + 4 + 3 + 1 + 3 * K) * 4 + 12 * 4 + 4 + 8 + 4 + 8)
-    depth_sort = 4 * n * 16            # 4 passes x (read key+value, write key+value)
+    depth_sort = 4 * n * 16 + n * 8    # 4 passes x (read key+value, write key+value); the last gathers the counts
     scan = n * (4 + 4 + 4)             # gathered count + order read, offset write
-    dup = n_visible * (4 + 4 + 8) + m * 8
-    tile_sort = 2 * m * 16
-    ranges = m * 4 + 0                  # tile ids read; range table is tiny
+    if supers:
+        # listing: offset, rank and rectangle per visible Gaussian, one (key, Gaussian) per entry
+        dup = n_visible * (4 + 4 + 8) + supers * 8
+        # one 8-bit pass over the super list (count reads the key; scatter reads and writes key and
+        # value), the count and place kernels read it again, each tile entry written once (4 B),
+        # the per-segment tile counts written, read and rewritten by the column scan, read by place
+        segs = supers // 64 + 257
+        tile_sort = supers * (4 + 16) + supers * (4 + 8) + m * 4 + segs * 64 * 4 * 4 + tiles * 12
+        ranges = tiles * 12              # the heaviest-first launch order from the ranges
+    else:
+        kb = 2 if tiles <= 1 << 16 else 4   # tile-id key bytes
+        passes = max(1, (max(tiles - 1, 1).bit_length() + 7) // 8)
+        dup = n_visible * (4 + 4 + 8) + m * (kb + 4)
+        tile_sort = passes * m * (kb + 2 * (kb + 4))   # count reads the key; scatter reads and writes both
+        ranges = m * kb + tiles * 12
     return dict(preprocess=pre, depth_sort=depth_sort, scan=scan, duplicate=dup, tile_sort=tile_sort,
                 ranges=ranges)
 
@@ -374,11 +388,11 @@ def time_splat2d_fit():
 
 
 def frame_stats(r, dev, scene, cams, img, bg):
-    """Pairs, blended (pixel, Gaussian) pairs and visible Gaussians per frame, averaged over the
-    views (outside any timed region)."""
+    """Pairs, blended (pixel, Gaussian) pairs, visible Gaussians and super-tile list entries (0
+    when the radix binning ran) per frame, averaged over the views (outside any timed region)."""
     import torch
 
-    pairs = blends = n_visible = 0
+    pairs = blends = n_visible = supers = 0
     for c in cams:
         pr = r.preprocess(dev, scene.sh_degree, c)
         bn = r.bin_and_sort(pr, c)
@@ -387,9 +401,10 @@ def frame_stats(r, dev, scene, cams, img, bg):
         tc = r.projected_tensors(pr)["tile_count"]
         torch.cuda.synchronize()
         pairs += int(bn.num_dups)
+        supers += int(bn.super_entries)
         blends += int(tot.item())
         n_visible += int((tc > 0).sum().item())
-    return tuple(v / len(cams) for v in (pairs, blends, n_visible))
+    return tuple(v / len(cams) for v in (pairs, blends, n_visible, supers))
 
 
 def settle_clock(r, dev, scene, cams, img, bg, seconds=0.3):
@@ -465,8 +480,10 @@ def stage_split(r, dev, scene, cams, img, bg, steps):
     return {k: (ms / steps) for k, (ms, cnt) in prof.items() if cnt}, prof_ms
 
 
-def stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs):
-    nbytes = stage_bytes(scene.n, scene.sh_degree, pairs, n_visible)
+def stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs):
+    cam = scene.cameras[0]
+    tiles = ((cam["width"] + 15) // 16) * ((cam["height"] + 15) // 16)
+    nbytes = stage_bytes(scene.n, scene.sh_degree, round(pairs), round(n_visible), round(supers), tiles)
     out = {}
     for st, b in nbytes.items():
         if st in stage_ms and stage_ms[st] > 0:
@@ -492,21 +509,22 @@ def measure_workload(name, scene, steps, warmup, sort_mode, copy_gbs, bg=(0.0, 0
     dev = binding.gaussians_to_device(scene.arrays())
     r = binding.Rasterizer(sort_mode=sort_mode, emit_keys=False)
     img = torch.empty((cams[0]["height"], cams[0]["width"], 3), dtype=torch.float32, device="cuda")
-    pairs, blends, n_visible = frame_stats(r, dev, scene, cams, img, bg)
+    pairs, blends, n_visible, supers = frame_stats(r, dev, scene, cams, img, bg)
     for i in range(warmup):
         r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 1, sort_mode)
     res = dict(n_gaussians=scene.n, sh_degree=scene.sh_degree, width=cams[0]["width"], height=cams[0]["height"],
                views=len(cams), steps=steps, ms_per_frame=round(ms, 5), frames_per_s=round(1000.0 / ms, 2),
                blends_per_s=round(blends * 1000.0 / ms, 1), pairs_per_frame=round(pairs),
-               blended_pairs_per_frame=round(blends), visible_per_frame=round(n_visible))
+               blended_pairs_per_frame=round(blends), visible_per_frame=round(n_visible),
+               super_entries_per_frame=round(supers))
     if len(cams) > 1:
         p_ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 3, sort_mode)
         res["pipelined"] = {"views_in_flight": 3, "ms_per_frame": round(p_ms, 5),
                             "frames_per_s": round(1000.0 / p_ms, 2)}
     stage_ms, _ = stage_split(r, dev, scene, cams, img, bg, steps)
     res["stage_ms"] = {k: round(v, 5) for k, v in stage_ms.items()}
-    res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs)
+    res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs)
     r.close()
     del dev, img
     torch.cuda.empty_cache()
@@ -567,8 +585,9 @@ def main():
     img = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
     bg = (0.0, 0.0, 0.0)
 
-    pairs, blends, n_visible = frame_stats(r, dev, scene, cams, img, bg)
-    log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} blended pairs={blends:.0f} ({len(cams)} view(s))")
+    pairs, blends, n_visible, supers = frame_stats(r, dev, scene, cams, img, bg)
+    log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} super-list entries={supers:.0f} "
+        f"blended pairs={blends:.0f} ({len(cams)} view(s))")
     settle = settle_clock(r, dev, scene, cams, img, bg)
     for i in range(args.warmup):
         r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
@@ -593,7 +612,7 @@ def main():
     copy_gbs = copy_bandwidth()
     log(f"frame ms median {dist['median']} p10 {dist['p10']} p90 {dist['p90']}; 1 GiB copy {copy_gbs:.0f} GB/s")
 
-    rooflines = stage_rooflines(scene, pairs, n_visible, blends, stage_ms, copy_gbs)
+    rooflines = stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs)
     lds = composite_lds(name, stage_ms.get("composite", 0.0))
     if lds:
         rooflines["composite_lds"] = lds

@@ -137,6 +137,9 @@ typedef struct {
  *   keys_unsorted / values_unsorted: the pairs before sorting, listed by
  *               Gaussian index then row-major over the rectangle; only filled in
  *               GS_SORT_KEY64 mode with GS_OPT_EMIT_KEYS set, else NULL.
+ *   super_entries  entries of the super-tile list (one per visible Gaussian and 8 x 8-tile
+ *               super-tile its rectangle meets) when the lists were built by super-tile
+ *               binning, else 0 (informational: the traffic of the binning stage)
  */
 typedef struct {
     int64_t num_dups;
@@ -146,6 +149,7 @@ typedef struct {
     const uint32_t *tile_ranges;
     const uint64_t *keys_unsorted;
     const uint32_t *values_unsorted;
+    int64_t super_entries;
 } gs_binning;
 
 /* Sorting strategies; both give identical keys, values and ranges. */
@@ -176,17 +180,20 @@ typedef enum {
     GS_TILE_ELLIPSE = 1
 } gs_tile_test;
 
-/* How GS_SORT_DEPTH_FIRST turns the depth-ordered Gaussians into per-tile lists; both give
+/* How GS_SORT_DEPTH_FIRST turns the depth-ordered Gaussians into per-tile lists; all give
    identical values and ranges (and keys, when emitted). */
 typedef enum {
+    /* GS_BINNING_SUPER_TILE for scenes of at least 65536 Gaussians, else GS_BINNING_RADIX
+       (below that the super-tile path's extra kernels cost more than they save; the default) */
+    GS_BINNING_AUTO = 0,
     /* group the tiles 8 x 8 into super-tiles, sort the Gaussians stably by super-tile (one
        8-bit radix pass over about two entries per Gaussian), then expand each super-tile's
        list into its 64 tiles, ranking a Gaussian within a tile by ballots in list order
-       (the default; used when the image has at most 256 super-tiles and 65536 tiles, and
-       more than one Gaussian, else GS_BINNING_RADIX) */
-    GS_BINNING_SUPER_TILE = 0,
+       (used when the image has at most 256 super-tiles and 65536 tiles, and more than one
+       Gaussian, else GS_BINNING_RADIX) */
+    GS_BINNING_SUPER_TILE = 1,
     /* list every (Gaussian, tile) pair, then a stable radix sort on the tile id */
-    GS_BINNING_RADIX = 1
+    GS_BINNING_RADIX = 2
 } gs_binning_mode;
 
 typedef enum {
@@ -197,7 +204,7 @@ typedef enum {
     GS_OPT_PROFILE = 4,              /* 1: bracket every kernel with HIP events (see gs_profile_read) */
     GS_OPT_TILE_TEST = 5,            /* gs_tile_test, default GS_TILE_SQUARE; read by gs_preprocess, and the
                                         binning, compositing and backward of that projection follow it */
-    GS_OPT_BINNING = 6               /* gs_binning_mode, default GS_BINNING_SUPER_TILE (depth-first mode) */
+    GS_OPT_BINNING = 6               /* gs_binning_mode, default GS_BINNING_AUTO (depth-first mode) */
 } gs_option;
 
 /* Per-stage timing collected while GS_OPT_PROFILE is 1. */

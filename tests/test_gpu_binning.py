@@ -1,5 +1,5 @@
-"""Super-tile binning (GS_BINNING_SUPER_TILE, the default) against the two-pass radix tile sort
-(GS_BINNING_RADIX) and the oracle (needs an MI355X).
+"""Super-tile binning (GS_BINNING_SUPER_TILE) against the two-pass radix tile sort (GS_BINNING_RADIX)
+and the oracle (needs an MI355X); GS_BINNING_AUTO picks one of them by scene size.
 
 Both build the per-tile lists of the lesson's flowchart ("Assign to tiles (16x16
 screen-space)", then "Depth-sort per tile"): every tile's Gaussians in (depth, index)

@@ -20,7 +20,7 @@ GS_SORT_DEPTH_FIRST, GS_SORT_KEY64 = 0, 1
 (GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE, GS_OPT_TILE_TEST,
  GS_OPT_BINNING) = range(7)
 GS_TILE_SQUARE, GS_TILE_ELLIPSE = 0, 1
-GS_BINNING_SUPER_TILE, GS_BINNING_RADIX = 0, 1
+GS_BINNING_AUTO, GS_BINNING_SUPER_TILE, GS_BINNING_RADIX = 0, 1, 2
 STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback",
           "backward_composite", "backward_setup", "backward_gaussian")
 SPLAT_STRIDE = 16
@@ -60,7 +60,8 @@ class Projected(ctypes.Structure):
 class Binning(ctypes.Structure):
     _fields_ = [("num_dups", ctypes.c_int64), ("tiles_x", ctypes.c_int32), ("tiles_y", ctypes.c_int32),
                 ("keys", ctypes.c_void_p), ("values", ctypes.c_void_p), ("tile_ranges", ctypes.c_void_p),
-                ("keys_unsorted", ctypes.c_void_p), ("values_unsorted", ctypes.c_void_p)]
+                ("keys_unsorted", ctypes.c_void_p), ("values_unsorted", ctypes.c_void_p),
+                ("super_entries", ctypes.c_int64)]
 
 
 class Profile(ctypes.Structure):
@@ -189,7 +190,7 @@ class Rasterizer:
     """One library context on the current HIP device."""
 
     def __init__(self, device: int | None = None, sort_mode: int = GS_SORT_DEPTH_FIRST, emit_keys: bool = True,
-                 tile_test: int = GS_TILE_SQUARE, binning: int = GS_BINNING_SUPER_TILE):
+                 tile_test: int = GS_TILE_SQUARE, binning: int = GS_BINNING_AUTO):
         self.lib = load_library()
         self.device = torch.cuda.current_device() if device is None else device
         ctx = ctypes.c_void_p()

@@ -87,7 +87,7 @@ struct gs_context {
     int profile = 0;
     int tile_test = GS_TILE_SQUARE;            // option
     int tile_test_used = GS_TILE_SQUARE;       // the rule of the last gs_preprocess
-    int binning = GS_BINNING_SUPER_TILE;       // option (depth-first mode)
+    int binning = GS_BINNING_AUTO;             // option (depth-first mode)
     int64_t max_dups = kMaxPairs;
     int64_t max_workspace = -1;
     size_t workspace = 0;
@@ -407,7 +407,7 @@ gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
             ctx->tile_test = (int)value;
             return GS_OK;
         case GS_OPT_BINNING:
-            if (value != GS_BINNING_SUPER_TILE && value != GS_BINNING_RADIX)
+            if (value != GS_BINNING_AUTO && value != GS_BINNING_SUPER_TILE && value != GS_BINNING_RADIX)
                 return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown binning %lld", (long long)value);
             ctx->binning = (int)value;
             return GS_OK;
@@ -468,7 +468,8 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     // super-tile binning gathers each ranked Gaussian's tile and super-tile counts in one word
     const int64_t super_tiles = (int64_t)((p.tiles_x + kSuperSide - 1) / kSuperSide) *
                                 ((p.tiles_y + kSuperSide - 1) / kSuperSide);
-    const bool pack = ctx->sort_mode == GS_SORT_DEPTH_FIRST && ctx->binning == GS_BINNING_SUPER_TILE &&
+    const bool want = ctx->binning == GS_BINNING_SUPER_TILE || (ctx->binning == GS_BINNING_AUTO && n >= kAutoSuperMin);
+    const bool pack = ctx->sort_mode == GS_SORT_DEPTH_FIRST && want &&
                       (int64_t)p.tiles_x * p.tiles_y <= kMaxSuperBinningTiles && super_tiles <= kMaxSuper;
     if (pack) {
         GS_TRY(ensure(ctx, ctx->pcount, nn * sizeof(uint32_t)));
@@ -731,8 +732,8 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     // super-tile binning where it applies (depth-first mode; counts packed for the scan)
     const int64_t super_tiles = (int64_t)((ctx->tiles_x + kSuperSide - 1) / kSuperSide) *
                                 ((ctx->tiles_y + kSuperSide - 1) / kSuperSide);
-    const bool super_bin = depth_first && ctx->binning == GS_BINNING_SUPER_TILE && ctx->packed_counts && n >= 2 &&
-                           tiles <= kMaxSuperBinningTiles && super_tiles <= kMaxSuper;
+    const bool super_bin = depth_first && ctx->packed_counts && n >= 2 && tiles <= kMaxSuperBinningTiles &&
+                           super_tiles <= kMaxSuper;   // the preprocess packed the counts for it
     const uint32_t *order = nullptr;
     int64_t M = 0, S = 0;
     bool speculated = false;
@@ -832,6 +833,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     const bool unsorted = M && !depth_first && emit_keys;
     out->keys_unsorted = unsorted ? as<uint64_t>(ctx->keys_unsorted) : nullptr;
     out->values_unsorted = unsorted ? as<uint32_t>(ctx->vals_unsorted) : nullptr;
+    out->super_entries = super_bin ? S : 0;
     return GS_OK;
 }
 

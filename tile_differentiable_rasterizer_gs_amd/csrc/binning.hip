@@ -23,8 +23,9 @@
 namespace gsr {
 namespace {
 
-constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup ...
-constexpr int kRangePer = kMaxSuperBinningTiles / kRangeThreads;   // ... of 64 tiles per thread
+constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup, each thread up to 64 tiles,
+constexpr int kRangeBatch = 8;        // loaded 8 per round trip
+constexpr int kXcds = 8;              // XCDs of the chip (workgroups are dealt to them round-robin)
 constexpr int kColumnWaves = 16;      // super_column_kernel: waves per super-tile ...
 constexpr int kColumnBatch = 8;       // ... and segment counts each lane loads per round trip
 
@@ -234,16 +235,19 @@ __global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(Supe
 }
 
 // [start, end) of every tile: an exclusive scan of the tile totals in tile order (one
-// workgroup, each thread kRangePer consecutive tiles); (0, 0) for a tile without pairs.
+// workgroup, each thread a run of consecutive tiles); (0, 0) for a tile without pairs.
 __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinParams p) {
     __shared__ uint32_t s_wave[kRangeThreads / kWave];
     const int tiles = p.tiles_x * p.tiles_y;
-    const int lo = (int)threadIdx.x * kRangePer;
-    uint32_t c[kRangePer], sum = 0;
+    const int per = (tiles + kRangeThreads - 1) / kRangeThreads;   // at most 64
+    const int lo = min(tiles, (int)threadIdx.x * per), hi = min(tiles, lo + per);
+    uint32_t sum = 0;
+    for (int i0 = lo; i0 < hi; i0 += kRangeBatch) {
+        uint32_t c[kRangeBatch];
 #pragma unroll
-    for (int i = 0; i < kRangePer; ++i) {
-        c[i] = lo + i < tiles ? p.tile_total[lo + i] : 0u;
-        sum += c[i];
+        for (int q = 0; q < kRangeBatch; ++q) c[q] = i0 + q < hi ? p.tile_total[i0 + q] : 0u;
+#pragma unroll
+        for (int q = 0; q < kRangeBatch; ++q) sum += c[q];
     }
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t inc = sum;
@@ -256,11 +260,15 @@ __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinPara
     __syncthreads();
     uint32_t run = inc - sum;
     for (int w = 0; w < wave; ++w) run += s_wave[w];
+    for (int i0 = lo; i0 < hi; i0 += kRangeBatch) {
+        uint32_t c[kRangeBatch];
 #pragma unroll
-    for (int i = 0; i < kRangePer; ++i) {
-        if (lo + i < tiles) {
-            reinterpret_cast<uint2 *>(p.ranges)[lo + i] = c[i] ? make_uint2(run, run + c[i]) : make_uint2(0u, 0u);
-            run += c[i];
+        for (int q = 0; q < kRangeBatch; ++q) c[q] = i0 + q < hi ? p.tile_total[i0 + q] : 0u;
+#pragma unroll
+        for (int q = 0; q < kRangeBatch; ++q) {
+            if (i0 + q < hi)
+                reinterpret_cast<uint2 *>(p.ranges)[i0 + q] = c[q] ? make_uint2(run, run + c[q]) : make_uint2(0u, 0u);
+            run += c[q];
         }
     }
 }
@@ -278,7 +286,11 @@ __global__ __launch_bounds__(kWave) void super_place_kernel(SuperBinParams p) {
     __shared__ SegmentTable t;
     if ((int64_t)*p.num_dups > p.capacity) return;
     build_segment_table(p, t);
-    const uint32_t seg = blockIdx.x;
+    // Workgroups go round-robin to the eight XCDs, each with its own L2: XCD x takes the x-th
+    // contiguous block of segments, so the short runs that consecutive segments write into
+    // one tile's list meet in one L2 and leave it as whole lines.
+    const uint32_t per_xcd = gridDim.x / kXcds;   // the grid is a multiple of kXcds
+    const uint32_t seg = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (seg >= t.first[kMaxSuper]) return;
     const SegmentRange r = segment_range(p, t, seg);
     const uint32_t lane = threadIdx.x;
@@ -326,15 +338,16 @@ int64_t super_segment_capacity(int64_t entries) { return entries / kSegment + kM
 void launch_super_binning(const SuperBinParams &p, hipStream_t s) {
     const unsigned segs = (unsigned)p.seg_capacity;
     super_count_kernel<<<segs, kWave, 0, s>>>(p);
-    super_column_kernel<<<kMaxSuper, kColumnWaves * kWave, 0, s>>>(p);
+    super_column_kernel<<<(unsigned)(p.super_x * p.super_y), kColumnWaves * kWave, 0, s>>>(p);
     tile_ranges_kernel<<<1, kRangeThreads, 0, s>>>(p);
     const bool narrow = p.capacity <= ((int64_t)1 << 30);
+    const unsigned segs8 = (segs + kXcds - 1) / kXcds * kXcds;   // every segment below it has a workgroup
     if (p.keys_out)
-        super_place_kernel<true, false><<<segs, kWave, 0, s>>>(p);
+        super_place_kernel<true, false><<<segs8, kWave, 0, s>>>(p);
     else if (narrow)
-        super_place_kernel<false, true><<<segs, kWave, 0, s>>>(p);
+        super_place_kernel<false, true><<<segs8, kWave, 0, s>>>(p);
     else
-        super_place_kernel<false, false><<<segs, kWave, 0, s>>>(p);
+        super_place_kernel<false, false><<<segs8, kWave, 0, s>>>(p);
 }
 
 }  // namespace gsr

@@ -154,6 +154,7 @@ constexpr int kSuperShift = 3;                     // 8 x 8 tiles per super-tile
 constexpr int kSuperSide = 1 << kSuperShift;
 constexpr int kMaxSuper = 1 << kRadixBits;         // super-tiles one 8-bit pass orders
 constexpr int kMaxSuperBinningTiles = 1 << 16;     // tile counts fit the packed count below
+constexpr int64_t kAutoSuperMin = 1 << 16;         // GS_BINNING_AUTO: super-tile binning from this many Gaussians
 constexpr int kSegment = 64;                       // super-list entries per segment (one wave, one per lane)
 constexpr int kPackShift = 17;                     // packed count: tile count | super count << 17
 constexpr int kPairShift = 36;                     // scan of packed counts: tiles | super-tiles << 36
@@ -288,6 +289,18 @@ void launch_composite(const CompositeParams &p, hipStream_t s);
 // the tile list lengths from `ranges`).  Returns false, launching nothing, when there
 // are more than kMaxOrderedTiles tiles (callers then launch in tile order).
 constexpr int32_t kMaxOrderedTiles = 1 << 16;
+// The order is a counting sort by weight on a logarithmic scale: 2048 buckets of 1/64
+// octave (the leading bit of the weight and the six below it), heaviest first.
+constexpr int kOrderSubBits = 6;                              // bits below the leading one
+constexpr int kOrderBuckets = 32 << kOrderSubBits;            // 2048
+// Bucket of a weight: 2047 - (64 floor(log2 w) + the six bits after the leading one); weight 0
+// goes last.
+__device__ __forceinline__ uint32_t order_bucket(uint32_t w) {
+    if (w == 0) return kOrderBuckets - 1;
+    const uint32_t lead = 31u - (uint32_t)__clz(w);
+    const uint32_t frac = ((w << (31u - lead)) >> (31 - kOrderSubBits)) & ((1u << kOrderSubBits) - 1u);
+    return (uint32_t)(kOrderBuckets - 1) - ((lead << kOrderSubBits) + frac);
+}
 struct TileOrderParams {
     int32_t tiles;
     const uint32_t *ranges;

@@ -14,22 +14,11 @@ namespace gsr {
 namespace {
 
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderSubBits = 6;                              // bits below the leading one
-constexpr int kOrderBuckets = 32 << kOrderSubBits;            // 2048
 constexpr int kOrderPer = kOrderBuckets / kOrderThreads;      // buckets per thread in the scan
 constexpr int kOrderKept = 8;   // tiles per thread whose bucket stays in registers (8192 tiles)
 
 __device__ __forceinline__ uint32_t tile_weight(const TileOrderParams &p, int t) {
     return p.weights ? p.weights[t] : p.ranges[2 * t + 1] - p.ranges[2 * t];
-}
-
-// Bucket of a weight, heaviest first: 2047 - (64 * floor(log2 w) + the six bits after
-// the leading one); weight 0 goes last.
-__device__ __forceinline__ uint32_t order_bucket(uint32_t w) {
-    if (w == 0) return kOrderBuckets - 1;
-    const uint32_t lead = 31u - (uint32_t)__clz(w);
-    const uint32_t frac = ((w << (31u - lead)) >> (31 - kOrderSubBits)) & ((1u << kOrderSubBits) - 1u);
-    return (uint32_t)(kOrderBuckets - 1) - ((lead << kOrderSubBits) + frac);
 }
 
 __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(TileOrderParams p) {
