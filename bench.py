@@ -56,13 +56,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_bytes(n, sh_degree, m, n_visible, supers, tiles):
+def stage_bytes(n, sh_degree, m, n_visible, supers, tiles, buckets):
     """Algorithmic HBM bytes per frame for each stage (depth-first mode).  m pairs; supers > 0:
     the per-tile lists came from super-tile binning over `supers` super-list entries, else from
-    the radix sort of the pairs on the tile id."""
+    the radix sort of the pairs on the tile id; buckets > 0: the depth order came from that many
+    depth buckets, else from the radix sort of the depth bits."""
     K = (sh_degree + 1) ** 2
     pre = n * ((3 + 4 + 3 + 1 + 3 * K) * 4 + 12 * 4 + 4 + 8 + 4 + 8)
-    depth_sort = 4 * n * 16 + n * 8    # 4 passes x (read key+value, write key+value); the last gathers the counts
+    if buckets:
+        # count and scatter read the key (4 + 4), the scatter writes an 8-byte entry, the bucket
+        # sort reads it and writes rank -> Gaussian and the gathered count (8 + 8), gathering 4
+        depth_sort = n * (4 + 4 + 8 + 8 + 8 + 4)
+    else:
+        depth_sort = 4 * n * 16 + n * 8    # 4 passes x (read key+value, write key+value); the last gathers
     scan = n * (4 + 4 + 4)             # gathered count + order read, offset write
     if supers:
         # listing: offset, rank and rectangle per visible Gaussian, one (key, Gaussian) per entry
@@ -388,11 +394,12 @@ def time_splat2d_fit():
 
 
 def frame_stats(r, dev, scene, cams, img, bg):
-    """Pairs, blended (pixel, Gaussian) pairs, visible Gaussians and super-tile list entries (0
-    when the radix binning ran) per frame, averaged over the views (outside any timed region)."""
+    """Pairs, blended (pixel, Gaussian) pairs, visible Gaussians, super-tile list entries (0
+    when the radix binning ran) and depth buckets (0 when the radix sort ordered the depths) per
+    frame, averaged over the views (outside any timed region)."""
     import torch
 
-    pairs = blends = n_visible = supers = 0
+    pairs = blends = n_visible = supers = buckets = 0
     for c in cams:
         pr = r.preprocess(dev, scene.sh_degree, c)
         bn = r.bin_and_sort(pr, c)
@@ -402,9 +409,10 @@ def frame_stats(r, dev, scene, cams, img, bg):
         torch.cuda.synchronize()
         pairs += int(bn.num_dups)
         supers += int(bn.super_entries)
+        buckets += int(bn.depth_buckets)
         blends += int(tot.item())
         n_visible += int((tc > 0).sum().item())
-    return tuple(v / len(cams) for v in (pairs, blends, n_visible, supers))
+    return tuple(v / len(cams) for v in (pairs, blends, n_visible, supers, buckets))
 
 
 def settle_clock(r, dev, scene, cams, img, bg, seconds=0.3):
@@ -480,10 +488,11 @@ def stage_split(r, dev, scene, cams, img, bg, steps):
     return {k: (ms / steps) for k, (ms, cnt) in prof.items() if cnt}, prof_ms
 
 
-def stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs):
+def stage_rooflines(scene, pairs, n_visible, supers, buckets, blends, stage_ms, copy_gbs):
     cam = scene.cameras[0]
     tiles = ((cam["width"] + 15) // 16) * ((cam["height"] + 15) // 16)
-    nbytes = stage_bytes(scene.n, scene.sh_degree, round(pairs), round(n_visible), round(supers), tiles)
+    nbytes = stage_bytes(scene.n, scene.sh_degree, round(pairs), round(n_visible), round(supers), tiles,
+                         round(buckets))
     out = {}
     for st, b in nbytes.items():
         if st in stage_ms and stage_ms[st] > 0:
@@ -509,7 +518,7 @@ def measure_workload(name, scene, steps, warmup, sort_mode, copy_gbs, bg=(0.0, 0
     dev = binding.gaussians_to_device(scene.arrays())
     r = binding.Rasterizer(sort_mode=sort_mode, emit_keys=False)
     img = torch.empty((cams[0]["height"], cams[0]["width"], 3), dtype=torch.float32, device="cuda")
-    pairs, blends, n_visible, supers = frame_stats(r, dev, scene, cams, img, bg)
+    pairs, blends, n_visible, supers, buckets = frame_stats(r, dev, scene, cams, img, bg)
     for i in range(warmup):
         r.render(dev, scene.sh_degree, cams[i % len(cams)], bg=bg, out=img)
     ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 1, sort_mode)
@@ -517,14 +526,14 @@ def measure_workload(name, scene, steps, warmup, sort_mode, copy_gbs, bg=(0.0, 0
                views=len(cams), steps=steps, ms_per_frame=round(ms, 5), frames_per_s=round(1000.0 / ms, 2),
                blends_per_s=round(blends * 1000.0 / ms, 1), pairs_per_frame=round(pairs),
                blended_pairs_per_frame=round(blends), visible_per_frame=round(n_visible),
-               super_entries_per_frame=round(supers))
+               super_entries_per_frame=round(supers), depth_buckets=round(buckets))
     if len(cams) > 1:
         p_ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 3, sort_mode)
         res["pipelined"] = {"views_in_flight": 3, "ms_per_frame": round(p_ms, 5),
                             "frames_per_s": round(1000.0 / p_ms, 2)}
     stage_ms, _ = stage_split(r, dev, scene, cams, img, bg, steps)
     res["stage_ms"] = {k: round(v, 5) for k, v in stage_ms.items()}
-    res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs)
+    res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, supers, buckets, blends, stage_ms, copy_gbs)
     r.close()
     del dev, img
     torch.cuda.empty_cache()
@@ -585,8 +594,9 @@ def main():
     img = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
     bg = (0.0, 0.0, 0.0)
 
-    pairs, blends, n_visible, supers = frame_stats(r, dev, scene, cams, img, bg)
+    pairs, blends, n_visible, supers, buckets = frame_stats(r, dev, scene, cams, img, bg)
     log(f"per frame: pairs={pairs:.0f} visible={n_visible:.0f} super-list entries={supers:.0f} "
+        f"depth buckets={buckets:.0f} "
         f"blended pairs={blends:.0f} ({len(cams)} view(s))")
     settle = settle_clock(r, dev, scene, cams, img, bg)
     for i in range(args.warmup):
@@ -612,7 +622,7 @@ def main():
     copy_gbs = copy_bandwidth()
     log(f"frame ms median {dist['median']} p10 {dist['p10']} p90 {dist['p90']}; 1 GiB copy {copy_gbs:.0f} GB/s")
 
-    rooflines = stage_rooflines(scene, pairs, n_visible, supers, blends, stage_ms, copy_gbs)
+    rooflines = stage_rooflines(scene, pairs, n_visible, supers, buckets, blends, stage_ms, copy_gbs)
     lds = composite_lds(name, stage_ms.get("composite", 0.0))
     if lds:
         rooflines["composite_lds"] = lds

@@ -140,6 +140,9 @@ typedef struct {
  *   super_entries  entries of the super-tile list (one per visible Gaussian and 8 x 8-tile
  *               super-tile its rectangle meets) when the lists were built by super-tile
  *               binning, else 0 (informational: the traffic of the binning stage)
+ *   depth_buckets  number of depth buckets when GS_DEPTH_ORDER_BUCKETS ordered the
+ *               Gaussians of this frame, 0 when the radix sort did (GS_DEPTH_ORDER_RADIX,
+ *               a fallback from too large a bucket, GS_SORT_KEY64, or fewer than 2 Gaussians)
  */
 typedef struct {
     int64_t num_dups;
@@ -150,6 +153,7 @@ typedef struct {
     const uint64_t *keys_unsorted;
     const uint32_t *values_unsorted;
     int64_t super_entries;
+    int64_t depth_buckets;
 } gs_binning;
 
 /* Sorting strategies; both give identical keys, values and ranges. */
@@ -196,6 +200,19 @@ typedef enum {
     GS_BINNING_RADIX = 2
 } gs_binning_mode;
 
+/* How GS_SORT_DEPTH_FIRST orders the Gaussians by (depth, index); both give the same order
+   (flowchart step "Depth-sort per tile"). */
+typedef enum {
+    /* B buckets linear in depth between the smallest and largest depth of the Gaussians with
+       tiles (B = 256 .. 8192 with the scene), one distribution pass, then each bucket sorted
+       by (depth bits, index) in LDS.  If a bucket holds more than 4096 Gaussians (depths
+       crowded into a sliver of the range) the frame falls back to GS_DEPTH_ORDER_RADIX.
+       The default. */
+    GS_DEPTH_ORDER_BUCKETS = 0,
+    /* stable LSD radix sort of the 32 depth bits, four 8-bit passes */
+    GS_DEPTH_ORDER_RADIX = 1
+} gs_depth_order;
+
 typedef enum {
     GS_OPT_SORT_MODE = 0,            /* gs_sort_mode, default GS_SORT_DEPTH_FIRST */
     GS_OPT_EMIT_KEYS = 1,            /* 1: gs_bin_and_sort materialises keys (default 1); gs_render never does */
@@ -204,7 +221,9 @@ typedef enum {
     GS_OPT_PROFILE = 4,              /* 1: bracket every kernel with HIP events (see gs_profile_read) */
     GS_OPT_TILE_TEST = 5,            /* gs_tile_test, default GS_TILE_SQUARE; read by gs_preprocess, and the
                                         binning, compositing and backward of that projection follow it */
-    GS_OPT_BINNING = 6               /* gs_binning_mode, default GS_BINNING_AUTO (depth-first mode) */
+    GS_OPT_BINNING = 6,              /* gs_binning_mode, default GS_BINNING_AUTO (depth-first mode) */
+    GS_OPT_DEPTH_ORDER = 7           /* gs_depth_order, default GS_DEPTH_ORDER_BUCKETS (depth-first mode); read
+                                        by gs_preprocess and the binning of that projection */
 } gs_option;
 
 /* Per-stage timing collected while GS_OPT_PROFILE is 1. */
@@ -301,8 +320,9 @@ gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_cam
  * (64 MiB) that each device the library runs on holds until the process ends, and the call
  * makes no allocation (no hipMalloc, hipFree or event creation; profiling is off for it).
  * The context must exist (created beforehand: it holds the host-visible pair-count word).
- * Limits: the Gaussians and tiles may take at most half the array (108 bytes per Gaussian +
- * 12 per tile, about 310 k Gaussians at 1080p), the frame as a whole with its pairs
+ * Limits: the Gaussians and tiles may take at most half the array (116 bytes per Gaussian,
+ * up to 8 MiB of depth-bucket counts, 12 bytes per tile: about 280 k Gaussians at 1080p),
+ * the frame as a whole with its pairs
  * (4 to 12 bytes each, counted on the device) the full array; beyond either the call returns
  * GS_ERR_CAPACITY (the pair case after waiting for the count, with nothing composited).
  * Every call on one device shares that device's array and leaves its contents behind:

@@ -41,6 +41,7 @@ def gpu_run(arrays: dict, sh_degree: int, camera: dict, bg=(0.0, 0.0, 0.0), sort
         rect=pt["rect"].cpu().numpy().view(np.uint16).astype(np.int32),
         tile_count=pt["tile_count"].cpu().numpy().view(np.uint32),
         num_dups=bt["num_dups"],
+        depth_buckets=int(bn.depth_buckets),
         values=bt["values"].cpu().numpy().view(np.uint32),
         ranges=bt["ranges"].cpu().numpy().view(np.uint32),
         keys=None if bt["keys"] is None else bt["keys"].cpu().numpy().view(np.uint64),

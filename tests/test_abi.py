@@ -50,7 +50,7 @@ int main(void) {
   P(gs_camera) O(gs_camera, t) O(gs_camera, fx) O(gs_camera, znear) O(gs_camera, width) O(gs_camera, height)
   P(gs_projected) O(gs_projected, tiles_x) O(gs_projected, splat) O(gs_projected, tile_count)
   P(gs_binning) O(gs_binning, keys) O(gs_binning, tile_ranges) O(gs_binning, values_unsorted)
-  O(gs_binning, super_entries)
+  O(gs_binning, super_entries) O(gs_binning, depth_buckets)
   P(gs_profile) O(gs_profile, launches)
   P(gs_gradients) O(gs_gradients, sh) O(gs_gradients, mean2d) O(gs_gradients, rgb)
   return 0;

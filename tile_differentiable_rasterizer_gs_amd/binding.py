@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libgsrast.so")
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_OUT_OF_MEMORY, GS_ERR_CAPACITY, GS_ERR_DEVICE = range(5)
 GS_SORT_DEPTH_FIRST, GS_SORT_KEY64 = 0, 1
 (GS_OPT_SORT_MODE, GS_OPT_EMIT_KEYS, GS_OPT_MAX_DUPS, GS_OPT_MAX_WORKSPACE_BYTES, GS_OPT_PROFILE, GS_OPT_TILE_TEST,
- GS_OPT_BINNING) = range(7)
+ GS_OPT_BINNING, GS_OPT_DEPTH_ORDER) = range(8)
 GS_TILE_SQUARE, GS_TILE_ELLIPSE = 0, 1
 GS_BINNING_AUTO, GS_BINNING_SUPER_TILE, GS_BINNING_RADIX = 0, 1, 2
+GS_DEPTH_ORDER_BUCKETS, GS_DEPTH_ORDER_RADIX = 0, 1
 STAGES = ("preprocess", "depth_sort", "scan", "duplicate", "tile_sort", "ranges", "composite", "readback",
           "backward_composite", "backward_setup", "backward_gaussian")
 SPLAT_STRIDE = 16
@@ -61,7 +62,7 @@ class Binning(ctypes.Structure):
     _fields_ = [("num_dups", ctypes.c_int64), ("tiles_x", ctypes.c_int32), ("tiles_y", ctypes.c_int32),
                 ("keys", ctypes.c_void_p), ("values", ctypes.c_void_p), ("tile_ranges", ctypes.c_void_p),
                 ("keys_unsorted", ctypes.c_void_p), ("values_unsorted", ctypes.c_void_p),
-                ("super_entries", ctypes.c_int64)]
+                ("super_entries", ctypes.c_int64), ("depth_buckets", ctypes.c_int64)]
 
 
 class Profile(ctypes.Structure):
@@ -190,7 +191,8 @@ class Rasterizer:
     """One library context on the current HIP device."""
 
     def __init__(self, device: int | None = None, sort_mode: int = GS_SORT_DEPTH_FIRST, emit_keys: bool = True,
-                 tile_test: int = GS_TILE_SQUARE, binning: int = GS_BINNING_AUTO):
+                 tile_test: int = GS_TILE_SQUARE, binning: int = GS_BINNING_AUTO,
+                 depth_order: int = GS_DEPTH_ORDER_BUCKETS):
         self.lib = load_library()
         self.device = torch.cuda.current_device() if device is None else device
         ctx = ctypes.c_void_p()
@@ -202,6 +204,7 @@ class Rasterizer:
         self.set_option(GS_OPT_EMIT_KEYS, 1 if emit_keys else 0)
         self.set_option(GS_OPT_TILE_TEST, tile_test)
         self.set_option(GS_OPT_BINNING, binning)
+        self.set_option(GS_OPT_DEPTH_ORDER, depth_order)
         self._keep = []
 
     def close(self):

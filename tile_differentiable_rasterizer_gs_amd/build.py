@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgsrast.so")
-SOURCES = ["api.hip", "preprocess.hip", "scan.hip", "sort.hip", "binning.hip", "composite.hip", "backward.hip", "schedule.hip",
+SOURCES = ["api.hip", "preprocess.hip", "scan.hip", "depth_sort.hip", "sort.hip", "binning.hip", "composite.hip", "backward.hip", "schedule.hip",
            "splat2d.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

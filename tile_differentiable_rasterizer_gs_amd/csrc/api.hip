@@ -88,6 +88,7 @@ struct gs_context {
     int tile_test = GS_TILE_SQUARE;            // option
     int tile_test_used = GS_TILE_SQUARE;       // the rule of the last gs_preprocess
     int binning = GS_BINNING_AUTO;             // option (depth-first mode)
+    int depth_order = GS_DEPTH_ORDER_BUCKETS;  // option (depth-first mode)
     int64_t max_dups = kMaxPairs;
     int64_t max_workspace = -1;
     size_t workspace = 0;
@@ -102,6 +103,9 @@ struct gs_context {
     // per-(segment, tile) counts, per-tile totals
     DeviceBuffer skey[2], sval[2], ssort_scratch, spart, seg_tiles, tile_total, pcount;
     bool packed_counts = false;                // the last gs_preprocess wrote pcount
+    // bucketed depth order: the bound slots, the bucketed entries and the count tables
+    DeviceBuffer drange, dentries, dbscratch;
+    bool depth_range = false;                  // the last gs_preprocess reduced its depths into drange
     // per-tile
     DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
@@ -113,7 +117,8 @@ struct gs_context {
     const float *s2_means = nullptr, *s2_depths = nullptr;
 
     unsigned long long *host_total = nullptr;   // pinned, host-coherent: [0] the pair count of each frame,
-                                                // [1] fault bits raised by the exact-footprint listing
+                                                // [1] fault bits raised by the exact-footprint listing,
+                                                // [2] 1 when the bucketed depth order met a bucket too large
     unsigned long long *host_total_dev = nullptr;   // its device address (the scan stores the count there)
 
     // last gs_preprocess
@@ -263,7 +268,7 @@ int ceil_log2(int64_t v) {
 }
 
 // Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
-constexpr int kContextBuffers = 48;
+constexpr int kContextBuffers = 51;
 void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
     DeviceBuffer *all[kContextBuffers] = {
         &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
@@ -273,7 +278,8 @@ void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
         &ctx->ranges, &ctx->tile_order, &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->pair_base,
         &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
         &ctx->s2_trans, &ctx->s2_partial, &ctx->skey[0], &ctx->skey[1], &ctx->sval[0], &ctx->sval[1],
-        &ctx->ssort_scratch, &ctx->spart, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount};
+        &ctx->ssort_scratch, &ctx->spart, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount, &ctx->drange,
+        &ctx->dentries, &ctx->dbscratch};
     for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
 
@@ -348,14 +354,14 @@ gs_status gs_context_create(gs_context **out, int device) {
     ctx->device = device;
     DeviceScope scope(device);
     if (scope.status != hipSuccess ||
-        hipHostMalloc((void **)&ctx->host_total, 2 * sizeof(unsigned long long),
+        hipHostMalloc((void **)&ctx->host_total, 3 * sizeof(unsigned long long),
                       hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess ||
         hipHostGetDevicePointer((void **)&ctx->host_total_dev, ctx->host_total, 0) != hipSuccess) {
         (void)hipGetLastError();
         delete ctx;
         return GS_ERR_DEVICE;
     }
-    ctx->host_total[1] = 0;
+    ctx->host_total[1] = ctx->host_total[2] = 0;
     hipError_t scratch_status;
     (void)scratch_address(device, &scratch_status);   // once per device; gs_render_noalloc reports failure
     *out = ctx;
@@ -411,6 +417,11 @@ gs_status gs_context_set_option(gs_context *ctx, int option, int64_t value) {
                 return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown binning %lld", (long long)value);
             ctx->binning = (int)value;
             return GS_OK;
+        case GS_OPT_DEPTH_ORDER:
+            if (value != GS_DEPTH_ORDER_BUCKETS && value != GS_DEPTH_ORDER_RADIX)
+                return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown depth order %lld", (long long)value);
+            ctx->depth_order = (int)value;
+            return GS_OK;
     }
     return fail(ctx, GS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
 }
@@ -430,10 +441,8 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
     GS_TRY(ensure(ctx, ctx->depth, nn * sizeof(float)));
     GS_TRY(ensure(ctx, ctx->rect, nn * sizeof(uint2)));
     GS_TRY(ensure(ctx, ctx->tile_count, nn * sizeof(uint32_t)));
-    for (int i = 0; i < 2; ++i) {
-        GS_TRY(ensure(ctx, ctx->dkey[i], nn * sizeof(uint32_t)));
-        GS_TRY(ensure(ctx, ctx->dval[i], nn * sizeof(uint32_t)));
-    }
+    GS_TRY(ensure(ctx, ctx->dkey[0], nn * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->dval[0], nn * sizeof(uint32_t)));
 
     PreprocessParams p{};
     p.n = (int32_t)n;
@@ -475,6 +484,18 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
         GS_TRY(ensure(ctx, ctx->pcount, nn * sizeof(uint32_t)));
         p.packed_count = as<uint32_t>(ctx->pcount);
     }
+    // the bucketed depth order takes its bounds from the depths of this projection; the slots
+    // start empty (freshly carved or allocated), afterwards the order's last kernel empties them
+    const bool depth_range = ctx->sort_mode == GS_SORT_DEPTH_FIRST && ctx->depth_order == GS_DEPTH_ORDER_BUCKETS;
+    if (depth_range) {
+        const void *before = ctx->drange.ptr;
+        GS_TRY(ensure(ctx, ctx->drange, 2 * kDepthSlots * sizeof(uint32_t)));
+        if (ctx->drange.ptr != before) {
+            launch_depth_range_fill(as<uint32_t>(ctx->drange), stream);
+            GS_TRY(check_launch(ctx, "depth bound slots"));
+        }
+        p.depth_range = as<uint32_t>(ctx->drange);
+    }
 
     GS_TRY(span_begin(ctx, GS_STAGE_PREPROCESS, stream));
     launch_preprocess(p, stream);
@@ -483,6 +504,7 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
 
     ctx->n = n;
     ctx->packed_counts = pack;
+    ctx->depth_range = depth_range;
     ctx->tile_test_used = ctx->tile_test;
     ctx->sh_degree = g->sh_degree;
     ctx->g_mean = g->mean;
@@ -625,6 +647,62 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     return GS_OK;
 }
 
+// Rank -> Gaussian by (depth, index) into *order, and ctx->dcount = gather[rank -> Gaussian]
+// (n > 1; otherwise the identity).  buckets: the bucketed order, whose overflow flag (device
+// memory) comes back in *flag; else the four-pass radix sort of the depth bits.
+static gs_status order_by_depth(gs_context *ctx, int64_t n, const uint32_t *gather, bool buckets,
+                                const uint32_t **order, const unsigned long long **flag, hipStream_t stream) {
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    GS_TRY(ensure(ctx, ctx->dcount, nn * sizeof(uint32_t)));
+    GS_TRY(ensure(ctx, ctx->dval[1], nn * sizeof(uint32_t)));
+    GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
+    if (buckets) {
+        GS_TRY(ensure(ctx, ctx->dentries, nn * sizeof(uint64_t)));
+        GS_TRY(ensure(ctx, ctx->dbscratch, (size_t)depth_bucket_scratch_words(n) * sizeof(uint32_t)));
+        DepthBucketParams b{};
+        depth_bucket_layout(as<uint32_t>(ctx->dbscratch), n, b);
+        b.keys = as<uint32_t>(ctx->dkey[0]);
+        b.range = as<uint32_t>(ctx->drange);
+        b.entries = as<uint64_t>(ctx->dentries);
+        b.gather_src = gather;
+        b.order = as<uint32_t>(ctx->dval[1]);
+        b.gathered = as<uint32_t>(ctx->dcount);
+        launch_depth_bucket_sort(b, stream);
+        GS_TRY(check_launch(ctx, "depth buckets"));
+        *order = b.order;
+        if (flag) *flag = b.flag;
+    } else {
+        // the last radix pass also gathers each ranked Gaussian's count
+        GS_TRY(ensure(ctx, ctx->dkey[1], nn * sizeof(uint32_t)));
+        GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 4));
+        const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
+                                                   as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n,
+                                                   nullptr, 0, 32, as<uint32_t>(ctx->dsort_scratch), stream, gather,
+                                                   as<uint32_t>(ctx->dcount));
+        GS_TRY(check_launch(ctx, "depth sort"));
+        *order = as<uint32_t>(ctx->dval[buf]);
+        if (flag) *flag = nullptr;
+    }
+    return span_end(ctx, stream);
+}
+
+// Exclusive prefix of the per-rank counts into ctx->offsets (the super-list offsets when
+// super_bin, the count word then holding both totals); the total also goes to host_total
+// (device address of host-coherent memory, with host_total[2] = *flag first) when given.
+static gs_status enqueue_scan(gs_context *ctx, const uint32_t *counts, int64_t n, bool super_bin,
+                              unsigned long long *host_total, const unsigned long long *flag, hipStream_t stream) {
+    unsigned long long *d_total = as<unsigned long long>(ctx->total);
+    GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
+    if (super_bin)
+        launch_scan_pairs(counts, as<uint32_t>(ctx->offsets), n, d_total, as<unsigned long long>(ctx->scan_scratch),
+                          stream, host_total, flag);
+    else
+        launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
+                    as<unsigned long long>(ctx->scan_scratch), stream, host_total, flag);
+    GS_TRY(check_launch(ctx, "scan"));
+    return span_end(ctx, stream);
+}
+
 // Depth-first binning through super-tiles (GS_BINNING_SUPER_TILE) for at most `cap` pairs and
 // `scap` super-list entries: the super list, its sort by super-tile, the expansion into
 // per-tile lists and the launch order.  The kernels read both counts from device memory
@@ -736,37 +814,25 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
                            super_tiles <= kMaxSuper;   // the preprocess packed the counts for it
     const uint32_t *order = nullptr;
     int64_t M = 0, S = 0;
+    int64_t depth_buckets = 0;   // buckets of the depth order that stood, 0: the radix sort
     bool speculated = false;
     if (n > 0) {
         const uint32_t *counts = pr->tile_count;   // tile counts in rank order
+        // by buckets of depth when the preprocess left the depth bounds (a bucket too large
+        // raises a flag that travels with the pair count; then the radix sort redoes it)
+        const bool buckets = depth_first && ctx->depth_range && n >= 2;
+        const uint32_t *gather = super_bin ? as<uint32_t>(ctx->pcount) : pr->tile_count;
+        const unsigned long long *bucket_flag = nullptr;
         if (depth_first) {
-            // the last depth pass also gathers each ranked Gaussian's tile count
-            GS_TRY(ensure(ctx, ctx->dcount, nn * sizeof(uint32_t)));
-            GS_TRY(ensure(ctx, ctx->dsort_scratch, (size_t)sort_scratch_words(n) * 4));
-            GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
-            const int buf = radix_sort_pairs<uint32_t>(as<uint32_t>(ctx->dkey[0]), as<uint32_t>(ctx->dval[0]),
-                                                       as<uint32_t>(ctx->dkey[1]), as<uint32_t>(ctx->dval[1]), n,
-                                                       nullptr, 0, 32, as<uint32_t>(ctx->dsort_scratch), stream,
-                                                       super_bin ? as<uint32_t>(ctx->pcount) : pr->tile_count,
-                                                       as<uint32_t>(ctx->dcount));
-            GS_TRY(check_launch(ctx, "depth sort"));
-            GS_TRY(span_end(ctx, stream));
-            order = as<uint32_t>(ctx->dval[buf]);
+            GS_TRY(order_by_depth(ctx, n, gather, buckets, &order, &bucket_flag, stream));
             counts = n > 1 ? as<uint32_t>(ctx->dcount) : pr->tile_count;
+            if (buckets) depth_buckets = (int64_t)1 << depth_bucket_bits(n);
         }
         // the scan's last kernel stores the pair count straight into host-coherent memory (no copy
         // on the stream); a sentinel shows a count that never arrived
         constexpr unsigned long long kNoCount = ~0ull;
         *ctx->host_total = kNoCount;
-        GS_TRY(span_begin(ctx, GS_STAGE_SCAN, stream));
-        if (super_bin)   // the super-list offsets; the count word holds both totals
-            launch_scan_pairs(counts, as<uint32_t>(ctx->offsets), n, d_total,
-                              as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
-        else
-            launch_scan(counts, nullptr, as<uint32_t>(ctx->offsets), n, d_total,
-                        as<unsigned long long>(ctx->scan_scratch), stream, ctx->host_total_dev);
-        GS_TRY(check_launch(ctx, "scan"));
-        GS_TRY(span_end(ctx, stream));
+        GS_TRY(enqueue_scan(ctx, counts, n, super_bin, ctx->host_total_dev, bucket_flag, stream));
 
         if (ctx->pair_capacity > 0 && (!super_bin || ctx->super_capacity > 0)) {
             if (super_bin)
@@ -795,6 +861,15 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             S = (int64_t)(published >> kPairShift);
         } else {
             M = (int64_t)published;
+        }
+        if (bucket_flag && __atomic_load_n(ctx->host_total + 2, __ATOMIC_ACQUIRE) != 0) {
+            // a bucket too large to sort in LDS: order this frame by the radix sort, recount the
+            // offsets in that order (the totals do not change) and list the pairs afresh
+            GS_HIP(ctx, hipStreamSynchronize(stream));
+            GS_TRY(order_by_depth(ctx, n, gather, false, &order, nullptr, stream));
+            GS_TRY(enqueue_scan(ctx, counts, n, super_bin, nullptr, nullptr, stream));
+            speculated = false;
+            depth_buckets = 0;
         }
         // listings enqueued before this frame's count arrived have run (same stream)
         if (__atomic_load_n(ctx->host_total + 1, __ATOMIC_ACQUIRE) != 0) {
@@ -834,6 +909,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     out->keys_unsorted = unsorted ? as<uint64_t>(ctx->keys_unsorted) : nullptr;
     out->values_unsorted = unsorted ? as<uint32_t>(ctx->vals_unsorted) : nullptr;
     out->super_entries = super_bin ? S : 0;
+    out->depth_buckets = depth_buckets;
     return GS_OK;
 }
 
@@ -915,11 +991,11 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
     if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
     if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_render_noalloc is already running on this context");
     // what the Gaussians and the tiles need before any pair (per Gaussian: record 64, depth 4,
-    // rect 8, count 4, packed count 4, two key/index pairs 16, gathered count 4, offsets 4; per
-    // tile: range 8, launch order 4), checked before anything is enqueued; the pairs are checked
-    // once counted
+    // rect 8, count 4, packed count 4, two key/index pairs 16, bucket entry 8, gathered count 4,
+    // offsets 4; the bucket count tables; per tile: range 8, launch order 4), checked before
+    // anything is enqueued; the pairs are checked once counted
     const int64_t tiles = (int64_t)((cam->width + GS_TILE - 1) / GS_TILE) * ((cam->height + GS_TILE - 1) / GS_TILE);
-    const int64_t fixed = g->n * 108 + tiles * 12;
+    const int64_t fixed = g->n * 116 + depth_bucket_scratch_words(g->n) * 4 + tiles * 12;
     if (fixed > (int64_t)(kNoAllocBytes / 2))
         return fail(ctx, GS_ERR_CAPACITY,
                     "gs_render_noalloc: %lld Gaussians and %lld tiles need %lld bytes, more than half of the "

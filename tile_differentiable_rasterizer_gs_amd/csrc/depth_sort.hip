@@ -1,0 +1,442 @@
+// Depth order of the Gaussians by buckets of depth (depth-first mode).
+//
+// Flowchart of the lesson "3D Gaussian Splatting from scratch", step "Depth-sort per
+// tile": compositing needs every tile's Gaussians front to back.  The depth-first path
+// orders all Gaussians once by (camera-space depth, index); the per-tile lists built in
+// that order inherit it.  Here that order comes from one distribution pass and one sort in
+// LDS per bucket, instead of four 8-bit radix passes of three kernels each:
+//   bounds   the preprocess leaves the smallest and largest depth bits of the Gaussians
+//            with pairs in kDepthSlots (min, max) slots, one atomic pair per wave
+//   count    G groups, each a contiguous range of Gaussians, count how many fall into
+//            each of B buckets: floor((z - zmin) * B / (zmax - zmin)), clamped to
+//            [0, B - 1].  binary32 subtraction and product round monotonically, so the
+//            bucket never decreases with the depth whatever the bounds (they only set the
+//            balance).  Gaussians without pairs form bucket B.
+//   column   per bucket: exclusive prefix of the group counts, and the bucket total
+//   scatter  each group puts its Gaussians at running per-bucket cursors in LDS: an entry
+//            (bits(depth) << 32 | index) into the bucket's range, a Gaussian without
+//            pairs straight into the output tail (their relative order is immaterial:
+//            they have no pairs, and their gathered count is 0)
+//   rank     one workgroup per bucket of at most kRankCap entries: an entry's place is the
+//            number of smaller entries, counted against the whole bucket in LDS (every lane
+//            reads the same word: a broadcast); it writes rank -> Gaussian and the
+//            gathered per-Gaussian count.  Larger buckets go to a list for
+//   sub-bin  per listed bucket (up to kBucketCap entries): a counting sort in LDS into
+//            kSubBins finer depth bins (the fractional part of the same bucket coordinate,
+//            monotone too), then each entry ranked within its sub-bin
+// Entries compare as 64-bit integers, i.e. by depth then index: the order the stable
+// radix sort of the depth bits gives.  A bucket of more than kBucketCap entries (depths
+// crowded into a sliver of the range) is written unsorted and raises a flag; the host
+// reads it with the pair count and orders the frame with the radix sort instead.
+#include <cfloat>
+
+#include "gs_internal.h"
+
+namespace gsr {
+namespace {
+
+constexpr int kGroupThreads = 1024;  // count and scatter workgroups
+constexpr int kGroupBatch = 4;       // 16-byte key loads per thread in flight
+constexpr int kXcds = 8;             // workgroups go round-robin to the eight XCDs
+constexpr int kRankThreads = kBlock; // rank workgroups
+constexpr int kRankCap = 2 * kRankThreads;   // largest bucket the rank kernel sorts
+constexpr int kSubBins = kBlock;     // sub-bins of a larger bucket
+constexpr int kSubbinGroups = 4096;  // workgroups that share the list of larger buckets
+
+struct Bounds {
+    float zlo, scale;   // scale 0: every Gaussian with pairs in bucket 0
+    int buckets;
+};
+
+__device__ inline uint32_t bucket_of(uint32_t key, const Bounds &b) {
+#pragma clang fp contract(off)
+    if (key == kNoPairsKey) return (uint32_t)b.buckets;
+    if (b.scale == 0.0f) return 0u;
+    const float t = (__uint_as_float(key) - b.zlo) * b.scale;
+    if (!(t > 0.0f)) return 0u;
+    return t < (float)b.buckets ? (uint32_t)t : (uint32_t)b.buckets - 1u;
+}
+
+// The frame's depth bounds from the slots (whole workgroup; a barrier inside).
+__device__ inline Bounds load_bounds(const uint32_t *range, int buckets, uint32_t *s_lo, uint32_t *s_hi) {
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    if (t < kDepthSlots) {
+        lo = range[t];
+        hi = range[kDepthSlots + t];
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+    }
+    if (lane == 0 && w < kDepthSlots / kWave) {
+        s_lo[w] = lo;
+        s_hi[w] = hi;
+    }
+    __syncthreads();
+    lo = s_lo[0];
+    hi = s_hi[0];
+#pragma unroll
+    for (int i = 1; i < kDepthSlots / kWave; ++i) {
+        lo = min(lo, s_lo[i]);
+        hi = max(hi, s_hi[i]);
+    }
+    Bounds b;
+    b.buckets = buckets;
+    b.zlo = 0.0f;
+    b.scale = 0.0f;
+    if (lo < hi) {   // two distinct finite positive depths
+        b.zlo = __uint_as_float(lo);
+        const float span = __uint_as_float(hi) - b.zlo;
+        const float sc = (float)buckets / span;
+        if (span > 0.0f && sc <= FLT_MAX) b.scale = sc;
+    }
+    return b;
+}
+
+// Exclusive prefix over the workgroup of one value per thread (kThreads threads); *total
+// gets the sum.  Barriers inside.
+template <int kThreads>
+__device__ inline uint32_t block_scan(uint32_t x, uint32_t *s_tmp /*[kThreads / kWave]*/, uint32_t *total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) s_tmp[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        const uint32_t v = s_tmp[w];
+        if (w < wave) before += v;
+        all += v;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+// Group of this workgroup (XCD x takes the x-th contiguous block of groups, so that the runs
+// consecutive groups write into one bucket meet in one L2) and its range of Gaussians
+// (a multiple of 4 long, for 16-byte loads).  Returns false for a padding workgroup.
+__device__ inline bool group_range(const DepthBucketParams &p, int *grp, int64_t *lo, int64_t *hi) {
+    const int per_xcd = gridDim.x / kXcds;   // the grid is a multiple of kXcds
+    *grp = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (*grp >= p.groups) return false;
+    const int64_t chunk = ((p.n + p.groups - 1) / p.groups + 3) & ~(int64_t)3;
+    *lo = min<int64_t>(p.n, (int64_t)*grp * chunk);
+    *hi = min<int64_t>(p.n, *lo + chunk);
+    return true;
+}
+
+// Visits every Gaussian of [lo, hi) once: f(index, key), kGroupBatch 16-byte loads per thread
+// issued together.
+template <typename F>
+__device__ inline void for_each_key(const uint32_t *keys, int64_t lo, int64_t hi, F f) {
+    const int64_t vlo = lo / 4, vhi = hi / 4;   // lo is a multiple of 4
+    const uint4 *kv = reinterpret_cast<const uint4 *>(keys);
+    for (int64_t j0 = vlo + threadIdx.x; j0 < vhi; j0 += (int64_t)kGroupThreads * kGroupBatch) {
+        uint4 k[kGroupBatch];
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int64_t j = j0 + (int64_t)u * kGroupThreads;
+            k[u] = kv[j < vhi ? j : j0];
+        }
+#pragma unroll
+        for (int u = 0; u < kGroupBatch; ++u) {
+            const int64_t j = j0 + (int64_t)u * kGroupThreads;
+            if (j < vhi) {
+                f(4 * j, k[u].x);
+                f(4 * j + 1, k[u].y);
+                f(4 * j + 2, k[u].z);
+                f(4 * j + 3, k[u].w);
+            }
+        }
+    }
+    for (int64_t i = max(lo, 4 * vhi) + threadIdx.x; i < hi; i += kGroupThreads) f(i, keys[i]);
+}
+
+// counts[b * G + group] = Gaussians of the group in bucket b (b = 0 .. B).  Group 0 also
+// clears the overflow flag and the list of larger buckets.
+__global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucketParams p) {
+    extern __shared__ uint32_t s_hist[];   // [B + 1]
+    __shared__ uint32_t s_lo[kDepthSlots / kWave], s_hi[kDepthSlots / kWave];
+    int grp;
+    int64_t lo, hi;
+    if (!group_range(p, &grp, &lo, &hi)) return;   // whole workgroup
+    const int nb = (1 << p.bucket_bits) + 1;
+    for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_hist[i] = 0u;
+    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
+    if (grp == 0 && threadIdx.x == 0) {
+        *p.flag = 0ull;
+        *p.big_count = 0u;
+    }
+    for_each_key(p.keys, lo, hi, [&](int64_t, uint32_t key) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
+    __syncthreads();
+    for (int b = threadIdx.x; b < nb; b += kGroupThreads) p.counts[(int64_t)b * p.groups + grp] = s_hist[b];
+}
+
+// One workgroup per bucket b (0 .. B): counts[b][*] -> exclusive prefix over groups; totals[b].
+__global__ __launch_bounds__(kBlock) void bucket_column_kernel(DepthBucketParams p) {
+    __shared__ uint32_t s_tmp[kBlock / kWave];
+    uint32_t *row = p.counts + (int64_t)blockIdx.x * p.groups;
+    const uint32_t v = (int)threadIdx.x < p.groups ? row[threadIdx.x] : 0u;   // groups <= kBlock
+    uint32_t total;
+    const uint32_t before = block_scan<kBlock>(v, s_tmp, &total);
+    if ((int)threadIdx.x < p.groups) row[threadIdx.x] = before;
+    if (threadIdx.x == 0) p.totals[blockIdx.x] = total;
+}
+
+// Each group places its Gaussians: bucket starts (exclusive prefix of the totals; group 0
+// also stores them for the sort kernels) plus the group's prefix give the cursors.
+__global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBucketParams p) {
+    extern __shared__ uint32_t s_cur[];   // [B + 1]
+    __shared__ uint32_t s_lo[kDepthSlots / kWave], s_hi[kDepthSlots / kWave];
+    __shared__ uint32_t s_tmp[kGroupThreads / kWave];
+    int grp;
+    int64_t lo, hi;
+    if (!group_range(p, &grp, &lo, &hi)) return;   // whole workgroup
+    const int nb = (1 << p.bucket_bits) + 1;
+    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);
+    // thread t: buckets [b0, b1)
+    const int per = (nb + kGroupThreads - 1) / kGroupThreads;
+    const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+    uint32_t sum = 0;
+    for (int b = b0; b < b1; ++b) sum += p.totals[b];
+    uint32_t all;
+    uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);
+    for (int b = b0; b < b1; ++b) {
+        s_cur[b] = run + p.counts[(int64_t)b * p.groups + grp];
+        if (grp == 0) p.starts[b] = run;
+        run += p.totals[b];
+    }
+    if (grp == 0 && threadIdx.x == 0) {
+        p.starts[nb] = all;
+        p.bounds[0] = bd.zlo;   // for the sub-bins of larger buckets
+        p.bounds[1] = bd.scale;
+    }
+    __syncthreads();
+    for_each_key(p.keys, lo, hi, [&](int64_t i, uint32_t key) {
+        const uint32_t b = bucket_of(key, bd);
+        const uint32_t pos = atomicAdd(&s_cur[b], 1u);
+        if ((int)b < nb - 1) {
+            p.entries[pos] = ((uint64_t)key << 32) | (uint32_t)i;
+        } else {
+            p.order[pos] = (uint32_t)i;
+            p.gathered[pos] = 0u;
+        }
+    });
+}
+
+// Writes a sorted entry: rank -> Gaussian and the Gaussian's count (read beforehand with
+// count_of, so that a thread's reads are in flight together and overlap the sorting).
+__device__ inline uint32_t count_of(const DepthBucketParams &p, uint64_t entry) {
+    return p.gather_src[(uint32_t)entry];
+}
+__device__ inline void emit(const DepthBucketParams &p, uint32_t at, uint64_t entry, uint32_t count) {
+    p.order[at] = (uint32_t)entry;
+    p.gathered[at] = count;
+}
+
+// Rank sort of one bucket of `size` <= kE * kRankThreads entries: thread t holds entries t,
+// t + kRankThreads, ..; each counts the bucket's smaller entries, two per 16-byte broadcast read.
+template <int kE>
+__device__ inline void rank_bucket(const DepthBucketParams &p, uint64_t *s_ent, uint32_t start, uint32_t size) {
+    uint64_t v[kE];
+    uint32_t rank[kE], cnt[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+        const uint32_t i = threadIdx.x + e * kRankThreads;
+        v[e] = i < size ? p.entries[start + i] : ~0ull;
+        rank[e] = 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+        const uint32_t i = threadIdx.x + e * kRankThreads;
+        cnt[e] = i < size ? count_of(p, v[e]) : 0u;
+        if (i < size) s_ent[i] = v[e];
+    }
+    // pad to a multiple of 8 entries with ~0 (never smaller than an entry)
+    if (threadIdx.x < 8 && size + threadIdx.x < (uint32_t)kRankCap + 8) s_ent[size + threadIdx.x] = ~0ull;
+    __syncthreads();
+    const ulonglong2 *pairs = reinterpret_cast<const ulonglong2 *>(s_ent);
+    for (uint32_t q = 0; q < (size + 7) / 8; ++q) {   // 4 independent 16-byte broadcast reads per step
+        ulonglong2 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = pairs[4 * q + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < kE; ++e) rank[e] += (uint32_t)(w[u].x < v[e]) + (uint32_t)(w[u].y < v[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+        const uint32_t i = threadIdx.x + e * kRankThreads;
+        if (i < size) emit(p, start + rank[e], v[e], cnt[e]);
+    }
+}
+
+// One workgroup per bucket of Gaussians with pairs: buckets of at most kRankCap entries are
+// ranked here, larger ones listed for the sub-bin kernel, and one of more than kBucketCap
+// entries is written unsorted with the flag raised.  Workgroup 0 also empties the bound
+// slots for the next preprocess (no later kernel reads them).
+__global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketParams p) {
+    __shared__ __align__(16) uint64_t s_ent[kRankCap + 8];
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < kDepthSlots; i += kRankThreads) {
+            p.range[i] = 0xffffffffu;
+            p.range[kDepthSlots + i] = 0u;
+        }
+    }
+    const uint32_t start = p.starts[blockIdx.x];
+    const uint32_t size = p.starts[blockIdx.x + 1] - start;
+    if (size == 0) return;
+    if (size > (uint32_t)kBucketCap) {   // not sorted here: the host redoes the frame's order
+        for (uint32_t i = threadIdx.x; i < size; i += kRankThreads) {
+            const uint64_t v = p.entries[start + i];
+            emit(p, start + i, v, count_of(p, v));
+        }
+        if (threadIdx.x == 0) *p.flag = 1ull;
+        return;
+    }
+    if (size > (uint32_t)kRankCap) {
+        if (threadIdx.x == 0) p.big_list[atomicAdd(p.big_count, 1u)] = blockIdx.x;
+        return;
+    }
+    if (size <= (uint32_t)kRankThreads)
+        rank_bucket<1>(p, s_ent, start, size);
+    else
+        rank_bucket<2>(p, s_ent, start, size);
+}
+
+// Sub-bin of an entry of bucket b: the fractional part of the bucket coordinate
+// t = (z - zmin) * scale (the same operations as bucket_of, so the same t) in kSubBins
+// steps, clamped.  Monotone in the depth, like the bucket.
+__device__ inline uint32_t sub_bin(uint64_t entry, uint32_t b, float zlo, float scale) {
+#pragma clang fp contract(off)
+    const float t = (__uint_as_float((uint32_t)(entry >> 32)) - zlo) * scale;
+    const float f = (t - (float)b) * (float)kSubBins;
+    if (!(f > 0.0f)) return 0u;
+    return f < (float)kSubBins ? (uint32_t)f : (uint32_t)kSubBins - 1u;
+}
+
+// The listed buckets (kRankCap < size <= kBucketCap), shared round-robin by the workgroups:
+// a counting sort into kSubBins sub-bins in LDS, then each entry ranked among the entries of
+// its own sub-bin.
+__global__ __launch_bounds__(kBlock) void bucket_subbin_kernel(DepthBucketParams p) {
+    constexpr int kE = kBucketCap / kBlock;
+    __shared__ uint64_t s_ent[kBucketCap];
+    __shared__ uint32_t s_cnt[kSubBins], s_base[kSubBins], s_tmp[kBlock / kWave];
+    const uint32_t count = *p.big_count;
+    const float zlo = p.bounds[0], scale = p.bounds[1];
+    for (uint32_t li = blockIdx.x; li < count; li += gridDim.x) {
+        const uint32_t b = p.big_list[li];
+        const uint32_t start = p.starts[b];
+        const uint32_t size = p.starts[b + 1] - start;
+        uint64_t v[kE];
+        uint32_t sub[kE], off[kE], cnt[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t i = threadIdx.x + e * kBlock;
+            v[e] = i < size ? p.entries[start + i] : 0ull;
+        }
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t i = threadIdx.x + e * kBlock;
+            cnt[e] = i < size ? count_of(p, v[e]) : 0u;
+            sub[e] = sub_bin(v[e], b, zlo, scale);
+        }
+        for (int i = threadIdx.x; i < kSubBins; i += kBlock) s_cnt[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            if (threadIdx.x + e * kBlock < size) off[e] = atomicAdd(&s_cnt[sub[e]], 1u);
+        __syncthreads();
+        uint32_t total;
+        const uint32_t c = s_cnt[threadIdx.x];   // kSubBins == kBlock
+        s_base[threadIdx.x] = block_scan<kBlock>(c, s_tmp, &total);   // barriers inside
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            if (threadIdx.x + e * kBlock < size) s_ent[s_base[sub[e]] + off[e]] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            if (threadIdx.x + e * kBlock < size) {
+                const uint32_t lo = s_base[sub[e]], hi = lo + s_cnt[sub[e]];
+                uint32_t r = 0;
+                for (uint32_t q = lo; q < hi; ++q) r += (uint32_t)(s_ent[q] < v[e]);
+                emit(p, start + lo + r, v[e], cnt[e]);
+            }
+        }
+        __syncthreads();   // the next bucket reuses the LDS
+    }
+}
+
+__global__ void fill_range_kernel(uint32_t *range) {
+    for (int i = threadIdx.x; i < kDepthSlots; i += blockDim.x) {
+        range[i] = 0xffffffffu;
+        range[kDepthSlots + i] = 0u;
+    }
+}
+
+}  // namespace
+
+static_assert(kBucketCap % kBlock == 0 && kSubBins == kBlock, "sub-bin kernel shapes");
+static_assert(kRankCap == 2 * kRankThreads && kRankCap % 8 == 0, "rank kernel shapes");
+
+int depth_bucket_bits(int64_t n) {
+    int bits = kMinBucketBits;
+    while (bits < kMaxBucketBits && ((int64_t)1 << bits) * kBucketTarget < n) ++bits;
+    return bits;
+}
+
+int depth_bucket_groups(int64_t n) {
+    const int64_t buckets = ((int64_t)1 << depth_bucket_bits(n)) + 1;
+    int64_t g = (n + kGroupKeys - 1) / kGroupKeys;
+    const int64_t cap = kMaxCountWords / buckets;
+    g = g < cap ? g : cap;
+    g = g < kBlock ? g : kBlock;
+    return (int)(g < 1 ? 1 : g);
+}
+
+int64_t depth_bucket_scratch_words(int64_t n) {
+    const int64_t B = (int64_t)1 << depth_bucket_bits(n), nb = B + 1;
+    // flag (u64), larger-bucket count (+ pad), bounds (2 floats), counts, totals, starts,
+    // larger-bucket list
+    return 2 + 2 + 2 + nb * depth_bucket_groups(n) + nb + (nb + 1) + B;
+}
+
+void depth_bucket_layout(uint32_t *scratch, int64_t n, DepthBucketParams &p) {
+    p.n = n;
+    p.bucket_bits = depth_bucket_bits(n);
+    p.groups = depth_bucket_groups(n);
+    const int64_t B = (int64_t)1 << p.bucket_bits, nb = B + 1;
+    p.flag = reinterpret_cast<unsigned long long *>(scratch);   // scratch is 8-byte aligned
+    p.big_count = scratch + 2;
+    p.bounds = reinterpret_cast<float *>(scratch + 4);
+    p.counts = scratch + 6;
+    p.totals = p.counts + nb * p.groups;
+    p.starts = p.totals + nb;
+    p.big_list = p.starts + nb + 1;
+}
+
+void launch_depth_range_fill(uint32_t *range, hipStream_t s) { fill_range_kernel<<<1, kBlock, 0, s>>>(range); }
+
+void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
+    if (p.n <= 0) return;
+    const int buckets = 1 << p.bucket_bits;
+    const unsigned grid = (unsigned)((p.groups + kXcds - 1) / kXcds * kXcds);
+    const size_t lds = (size_t)(buckets + 1) * sizeof(uint32_t);
+    bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
+    bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
+    bucket_scatter_kernel<<<grid, kGroupThreads, lds, s>>>(p);
+    bucket_rank_kernel<<<buckets, kRankThreads, 0, s>>>(p);
+    bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBlock, 0, s>>>(p);
+}
+
+}  // namespace gsr

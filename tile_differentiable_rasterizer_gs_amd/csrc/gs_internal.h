@@ -86,6 +86,12 @@ __device__ __forceinline__ uint32_t kept_index(const EllipseRec &E, uint32_t x0,
 __device__ __forceinline__ float scale_activation(float log_scale) { return (float)exp((double)log_scale); }
 void launch_scale_activation(const float *log_scale, float *scale, int64_t n, hipStream_t s);
 
+// Depth key of a Gaussian without pairs (sorts after every depth).
+constexpr uint32_t kNoPairsKey = 0xffffffffu;
+// Slots of the visible depth range the preprocess leaves for the bucketed depth order:
+// range[s] = min, range[kDepthSlots + s] = max of the depth bits reduced into slot s.
+constexpr int kDepthSlots = 256;
+
 struct PreprocessParams {
     int32_t n;
     int32_t sh_coeffs;           // K = (degree+1)^2
@@ -99,8 +105,9 @@ struct PreprocessParams {
     float *depth;                // [n]
     uint2 *rect;                 // [n] {x0 | x1 << 16, y0 | y1 << 16}
     uint32_t *tile_count;        // [n]
-    uint32_t *depth_key;         // [n] or null: visible ? bits(depth) : 0xffffffff
+    uint32_t *depth_key;         // [n] or null: visible ? bits(depth) : kNoPairsKey
     uint32_t *depth_index;       // [n] or null: g
+    uint32_t *depth_range;       // [2][kDepthSlots] or null: atomic min / max of the visible depth bits
     EllipseRec *ellipse;         // [n] or null: exact-footprint rule (tile counts from the row spans)
     uint32_t *packed_count;      // [n] or null: pack_counts(tile count, rect), for super-tile binning
 };
@@ -114,15 +121,18 @@ constexpr int kScanTile = kBlock * kScanItems;   // 4096 values per workgroup
 // number of uint64 scratch words launch_scan needs for n values
 int64_t scan_scratch_words(int64_t n);
 // out[i] = sum_{j<i} in[j]; *total = sum of all (device uint64).  n >= 1.
-// host_total (optional): device address of host-coherent memory that also receives the sum.
+// host_total (optional): device address of host-coherent memory that also receives the sum;
+// with `flag` (device memory) host_total[2] first receives *flag, and the sum is stored
+// with release order after it.
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
                  unsigned long long *total, unsigned long long *scratch, hipStream_t s,
-                 unsigned long long *host_total = nullptr);
+                 unsigned long long *host_total = nullptr, const unsigned long long *flag = nullptr);
 // The same over packed counts (tile count | super count << kPackShift): out[i] = the super
 // counts before i; total[0] = tiles | super-tiles << kPairShift (also to host_total),
 // total[1] = the tile total, total[2] = the super-tile total.
 void launch_scan_pairs(const uint32_t *packed, uint32_t *out, int64_t n, unsigned long long *total,
-                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total);
+                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total,
+                       const unsigned long long *flag = nullptr);
 
 // ---------------------------------------------------------------------------
 // stable LSD radix sort of (key, uint32 value) pairs
@@ -143,6 +153,43 @@ int radix_sort_pairs(K *k0, uint32_t *v0, K *k1, uint32_t *v1, int64_t n, const 
 // Offset (in uint32 words) into the scratch of radix_sort_pairs(n) of the per-digit totals
 // of the last pass: totals[d] = elements whose last-pass digit is d.
 int64_t sort_totals_offset(int64_t n);
+
+// ---------------------------------------------------------------------------
+// depth order by buckets of depth (depth-first mode, GS_DEPTH_ORDER_BUCKETS)
+// ---------------------------------------------------------------------------
+constexpr int kBucketCap = 4096;          // largest bucket one workgroup sorts in LDS
+constexpr int kMinBucketBits = 8, kMaxBucketBits = 13;
+constexpr int64_t kBucketTarget = 256;    // Gaussians per bucket the bucket count aims at
+constexpr int64_t kGroupKeys = 4096;      // Gaussians per counting group (at least)
+constexpr int64_t kMaxCountWords = 1 << 21;   // bound on the (bucket, group) count table
+
+struct DepthBucketParams {
+    const uint32_t *keys;          // [n] bits(depth), kNoPairsKey for a Gaussian without pairs
+    int64_t n;
+    int32_t bucket_bits;           // B = 1 << bucket_bits buckets; bucket B: no pairs
+    int32_t groups;                // G contiguous ranges of Gaussians
+    uint32_t *range;               // [2][kDepthSlots] bound slots (reset by the last kernel)
+    unsigned long long *flag;      // device: 1 when a bucket was too large to sort
+    uint32_t *big_count;           // device: buckets listed for the sub-bin kernel
+    uint32_t *big_list;            // [B] their ids
+    float *bounds;                 // [2] the frame's (zmin, B / (zmax - zmin)) for the sub-bins
+    uint32_t *counts;              // [(B + 1) * G]
+    uint32_t *totals;              // [B + 1]
+    uint32_t *starts;              // [B + 2]
+    uint64_t *entries;             // [n] bits(depth) << 32 | index, grouped by bucket
+    const uint32_t *gather_src;    // [n] per-Gaussian value to gather in rank order
+    uint32_t *order;               // out [n]: rank -> Gaussian
+    uint32_t *gathered;            // out [n]: gather_src[order[r]]
+};
+int depth_bucket_bits(int64_t n);
+int depth_bucket_groups(int64_t n);
+// uint32 words of scratch for n Gaussians, and the carving of p.flag, big_count, bounds,
+// counts, totals, starts and big_list out of it (also sets p.n, p.bucket_bits, p.groups)
+int64_t depth_bucket_scratch_words(int64_t n);
+void depth_bucket_layout(uint32_t *scratch, int64_t n, DepthBucketParams &p);
+void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s);
+// sets the bound slots to the empty range (min = all ones, max = 0)
+void launch_depth_range_fill(uint32_t *range, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // super-tile binning (depth-first mode, GS_BINNING_SUPER_TILE)

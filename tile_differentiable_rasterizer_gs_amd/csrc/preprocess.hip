@@ -189,8 +189,36 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     if (p.depth_key) {
         // Gaussians without pairs sort last: interleaved with the others they would dilute the
         // pair listing's rank windows (a 2048-entry block would meet thousands of empty ranks)
-        p.depth_key[g] = visible ? __float_as_uint(tz) : 0xffffffffu;
+        p.depth_key[g] = visible ? __float_as_uint(tz) : kNoPairsKey;
         p.depth_index[g] = (uint32_t)g;
+    }
+    if (p.depth_range) {
+        // the wave's smallest and largest depth bits among Gaussians with pairs (positive
+        // floats order like their bit patterns) into one of kDepthSlots slots
+        uint32_t lo = visible ? __float_as_uint(tz) : 0xffffffffu, hi = visible ? __float_as_uint(tz) : 0u;
+        const uint64_t live = __ballot(1);   // lanes past n have left
+        if (live == ~0ull) {
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) {
+                lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+                hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+            }
+        } else {
+            uint32_t wl = 0xffffffffu, wh = 0u;
+            for (uint64_t m = live; m; m &= m - 1) {
+                const int l = __builtin_ctzll(m);
+                wl = min(wl, (uint32_t)__builtin_amdgcn_readlane((int)lo, l));
+                wh = max(wh, (uint32_t)__builtin_amdgcn_readlane((int)hi, l));
+            }
+            lo = wl;
+            hi = wh;
+        }
+        const uint32_t lane = __builtin_amdgcn_mbcnt_hi((uint32_t)(live >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)live, 0u));
+        if (lane == 0 && lo <= hi) {
+            const uint32_t slot = (blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave) & (kDepthSlots - 1);
+            atomicMin(&p.depth_range[slot], lo);
+            atomicMax(&p.depth_range[kDepthSlots + slot], hi);
+        }
     }
 }
 

@@ -80,7 +80,9 @@ __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const TIn *in, cons
 // prefix[block] (scanned block totals), or, with block_sums, the sum of the block
 // totals before this block, added up here (few blocks: it saves a kernel).  When
 // `total` is non-null the last block writes the grand total there, and also to
-// `host_total` (host-coherent memory, a system-scope store) when that is non-null.
+// `host_total` (host-coherent memory, a system-scope store) when that is non-null; with
+// `flag`, host_total[2] = *flag is stored first and the total after it with release order,
+// so a host that sees the total also sees the flag.
 // kPair: packed inputs (load_items); out[i] is the super-tile part of the prefix.
 // kDecode: the total is packed; total[1] and total[2] also get its two fields.
 template <typename TIn, typename TOut, bool kPair, bool kDecode>
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
                                                                 int64_t n, const unsigned long long *prefix,
                                                                 const unsigned long long *block_sums, TOut *out,
                                                                 unsigned long long *total,
-                                                                unsigned long long *host_total) {
+                                                                unsigned long long *host_total,
+                                                                const unsigned long long *flag) {
     unsigned long long offset = 0;
     if (prefix) {
         offset = prefix[blockIdx.x];
@@ -119,7 +122,12 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
             total[1] = all & ((1ull << kPairShift) - 1);
             total[2] = all >> kPairShift;
         }
-        if (host_total) __hip_atomic_store(host_total, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (host_total && flag) {
+            __hip_atomic_store(host_total + 2, *flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(host_total, all, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        } else if (host_total) {
+            __hip_atomic_store(host_total, all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 }
 
@@ -131,26 +139,27 @@ constexpr int64_t kDirectBlocks = 1024;
 // Scans `in` (n values) into `out`; partials for the next level live in scratch.
 template <typename TIn, typename TOut, bool kPair, bool kDecode>
 void scan_level(const TIn *in, const uint32_t *gather, TOut *out, int64_t n, unsigned long long *total,
-                unsigned long long *host_total, unsigned long long *scratch, hipStream_t s) {
+                unsigned long long *host_total, const unsigned long long *flag, unsigned long long *scratch,
+                hipStream_t s) {
     const int64_t nb = blocks_for(n);
     if (nb == 1) {
         scan_downsweep_kernel<TIn, TOut, kPair, kDecode><<<1, kBlock, 0, s>>>(in, gather, n, nullptr, nullptr, out,
-                                                                              total, host_total);
+                                                                              total, host_total, flag);
         return;
     }
     unsigned long long *partials = scratch;
     scan_reduce_kernel<TIn, kPair><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials);
     if (nb <= kDirectBlocks) {   // each block adds up the partials before it
         scan_downsweep_kernel<TIn, TOut, kPair, kDecode><<<(unsigned)nb, kBlock, 0, s>>>(
-            in, gather, n, nullptr, partials, out, total, host_total);
+            in, gather, n, nullptr, partials, out, total, host_total, flag);
         return;
     }
     // exclusive scan of the partials (already in the packed form), in place (reads before
     // writes within each block); that level writes the total
     scan_level<unsigned long long, unsigned long long, false, kDecode>(partials, nullptr, partials, nb, total,
-                                                                      host_total, scratch + nb, s);
+                                                                      host_total, flag, scratch + nb, s);
     scan_downsweep_kernel<TIn, TOut, kPair, false><<<(unsigned)nb, kBlock, 0, s>>>(in, gather, n, partials, nullptr,
-                                                                                  out, nullptr, nullptr);
+                                                                                  out, nullptr, nullptr, nullptr);
 }
 
 }  // namespace
@@ -163,13 +172,14 @@ int64_t scan_scratch_words(int64_t n) {
 
 void launch_scan(const uint32_t *in, const uint32_t *gather, uint32_t *out, int64_t n,
                  unsigned long long *total, unsigned long long *scratch, hipStream_t s,
-                 unsigned long long *host_total) {
-    scan_level<uint32_t, uint32_t, false, false>(in, gather, out, n, total, host_total, scratch, s);
+                 unsigned long long *host_total, const unsigned long long *flag) {
+    scan_level<uint32_t, uint32_t, false, false>(in, gather, out, n, total, host_total, flag, scratch, s);
 }
 
 void launch_scan_pairs(const uint32_t *packed, uint32_t *out, int64_t n, unsigned long long *total,
-                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total) {
-    scan_level<uint32_t, uint32_t, true, true>(packed, nullptr, out, n, total, host_total, scratch, s);
+                       unsigned long long *scratch, hipStream_t s, unsigned long long *host_total,
+                       const unsigned long long *flag) {
+    scan_level<uint32_t, uint32_t, true, true>(packed, nullptr, out, n, total, host_total, flag, scratch, s);
 }
 
 }  // namespace gsr
