@@ -5,7 +5,7 @@
 // alpha_i = o_i exp(-d^T Sigma'^-1 d / 2); section "Étape 2" clamps alpha to at
 // most 0.99 and samples pixel (row i, column j) at (x = j, y = i).
 //
-// The tile's depth-sorted list is walked in batches of 256 splats.  The workgroup
+// The tile's depth-sorted list is walked in batches of 128 splats.  The workgroup
 // gathers a batch into LDS (double-buffered: the global loads of the next batch are
 // in flight while the current one is blended) and every lane reads each splat back
 // as a wave-wide LDS broadcast.  A lane owns the two pixels (x, y) and (x + 8, y);
@@ -27,7 +27,7 @@ namespace gsr {
 namespace {
 
 constexpr int kThreads = 128;                // 64 lanes x 2 pixels = one 16x8 half tile per wave
-constexpr int kBatch = 256;                  // splats per LDS batch
+constexpr int kBatch = 128;                  // splats per LDS batch (9.5 KB of LDS per workgroup: 6 waves per SIMD)
 constexpr int kLoads = kBatch / kThreads;    // records gathered per thread per batch
 constexpr int kUnroll = 8;                   // splats between wave exit tests
 
