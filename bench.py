@@ -533,6 +533,13 @@ def measure_workload(name, scene, steps, warmup, sort_mode, copy_gbs, bg=(0.0, 0
                             "frames_per_s": round(1000.0 / p_ms, 2)}
     stage_ms, _ = stage_split(r, dev, scene, cams, img, bg, steps)
     res["stage_ms"] = {k: round(v, 5) for k, v in stage_ms.items()}
+    if len(cams) > 1:   # several views of one scene: the 3D covariances computed once (row f3)
+        r.cache_covariance(dev, scene.sh_degree)
+        c_ms, _ = timed_frames(r, dev, scene, cams, img, bg, steps, 1, sort_mode)
+        c_stage, _ = stage_split(r, dev, scene, cams, img, bg, steps)
+        r.cache_covariance(None)
+        res["covariance_cache"] = {"ms_per_frame": round(c_ms, 5), "preprocess_ms": round(c_stage["preprocess"], 5),
+                                   "note": "gs_cache_covariance once, then every view reads Sigma"}
     res["stage_rooflines"] = stage_rooflines(scene, pairs, n_visible, supers, buckets, blends, stage_ms, copy_gbs)
     r.close()
     del dev, img

@@ -276,6 +276,21 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *gaussians, const gs
                         gs_projected *out, hipStream_t stream);
 
 /*
+ * Caches the view-independent part of the projection: the 3D covariance
+ * Sigma = R S S^T R^T of every Gaussian (section "Ce qu'un Gaussien porte"), six
+ * floats per Gaussian in context memory.  While the cache is held, gs_preprocess
+ * (and gs_render) on the same context reads it instead of quat and log_scale
+ * whenever its gaussians have the same n, quat and log_scale pointers: several
+ * views of one scene then compute Sigma once.  The result is bit-identical to the
+ * uncached preprocess.  The library cannot see writes to caller memory: after
+ * changing quat or log_scale in place, call again (or drop the cache).
+ * `gaussians` NULL drops the cache.  gs_render_noalloc never uses it.
+ * Asynchronous on `stream`; errors as gs_preprocess (invalid arguments are
+ * checked with gs_check_arguments).
+ */
+gs_status gs_cache_covariance(gs_context *ctx, const gs_gaussians *gaussians, hipStream_t stream);
+
+/*
  * Tile binning of the last gs_preprocess output: prefix sum of tile counts,
  * (tile, depth) pair listing, stable sort, and per-tile ranges (flowchart
  * steps "Assign to tiles" and "Depth-sort per tile").  `projected` must be the

@@ -29,7 +29,8 @@ TILE = 16
 
 # symbols declared in include/gsrast.h
 EXPORTED = ("gs_context_create", "gs_context_destroy", "gs_context_set_option", "gs_check_arguments",
-            "gs_preprocess", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_render_noalloc",
+            "gs_preprocess", "gs_cache_covariance", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
+            "gs_render_noalloc",
             "gs_backward", "gs_splat2d_forward", "gs_splat2d_backward", "gs_scale_activation", "gs_profile_read",
             "gs_status_string", "gs_last_error")
 
@@ -96,6 +97,7 @@ def load_library(path: str = LIB_PATH):
     lib.gs_check_arguments.argtypes = [ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.c_char_p,
                                        ctypes.c_size_t]
     lib.gs_preprocess.argtypes = [P, ctypes.POINTER(Gaussians), ctypes.POINTER(Camera), ctypes.POINTER(Projected), P]
+    lib.gs_cache_covariance.argtypes = [P, ctypes.POINTER(Gaussians), P]
     lib.gs_bin_and_sort.argtypes = [P, ctypes.POINTER(Projected), ctypes.POINTER(Camera), ctypes.POINTER(Binning), P]
     lib.gs_composite.argtypes = [P, ctypes.POINTER(Projected), ctypes.POINTER(Binning), ctypes.POINTER(Camera),
                                  ctypes.POINTER(ctypes.c_float), P, P]
@@ -118,7 +120,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_last_error.argtypes = [P]
     lib.gs_last_error.restype = ctypes.c_char_p
     for name in ("gs_context_create", "gs_context_set_option", "gs_check_arguments", "gs_preprocess",
-                 "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render", "gs_backward",
+                 "gs_cache_covariance", "gs_bin_and_sort", "gs_composite", "gs_composite_ex", "gs_render",
+                 "gs_backward",
                  "gs_splat2d_forward", "gs_splat2d_backward", "gs_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -233,6 +236,15 @@ class Rasterizer:
         self._check(self.lib.gs_preprocess(self.ctx, ctypes.byref(g), ctypes.byref(cam), ctypes.byref(out),
                                            _stream_handle(stream)))
         return out
+
+    def cache_covariance(self, tensors: dict | None, sh_degree: int = 0, stream=None):
+        """gs_cache_covariance: Sigma of these Gaussians computed once and reused by later
+        preprocess / render calls with the same quat and log_scale tensors (None drops it)."""
+        if tensors is None:
+            self._check(self.lib.gs_cache_covariance(self.ctx, None, _stream_handle(stream)))
+            return
+        g = make_gaussians(tensors, sh_degree)
+        self._check(self.lib.gs_cache_covariance(self.ctx, ctypes.byref(g), _stream_handle(stream)))
 
     def bin_and_sort(self, projected: Projected, camera: dict, stream=None) -> Binning:
         cam = make_camera(camera)

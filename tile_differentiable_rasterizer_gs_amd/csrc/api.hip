@@ -106,6 +106,10 @@ struct gs_context {
     // bucketed depth order: the bound slots, the bucketed entries and the count tables
     DeviceBuffer drange, dentries, dbscratch;
     bool depth_range = false;                  // the last gs_preprocess reduced its depths into drange
+    // gs_cache_covariance: Sigma [6][cov_n] of the Gaussians with these quat / log_scale planes
+    DeviceBuffer cov;
+    const float *cov_quat = nullptr, *cov_log_scale = nullptr;
+    int64_t cov_n = -1;
     // per-tile
     DeviceBuffer ranges, tile_order, tile_weight, tile_order_bwd, tile_cut;
     // gradients
@@ -268,7 +272,7 @@ int ceil_log2(int64_t v) {
 }
 
 // Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
-constexpr int kContextBuffers = 51;
+constexpr int kContextBuffers = 52;
 void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
     DeviceBuffer *all[kContextBuffers] = {
         &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
@@ -279,7 +283,7 @@ void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
         &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
         &ctx->s2_trans, &ctx->s2_partial, &ctx->skey[0], &ctx->skey[1], &ctx->sval[0], &ctx->sval[1],
         &ctx->ssort_scratch, &ctx->spart, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount, &ctx->drange,
-        &ctx->dentries, &ctx->dbscratch};
+        &ctx->dentries, &ctx->dbscratch, &ctx->cov};
     for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
 
@@ -484,6 +488,9 @@ gs_status gs_preprocess(gs_context *ctx, const gs_gaussians *g, const gs_camera 
         GS_TRY(ensure(ctx, ctx->pcount, nn * sizeof(uint32_t)));
         p.packed_count = as<uint32_t>(ctx->pcount);
     }
+    // the cached covariances, when they are these Gaussians' (never inside gs_render_noalloc)
+    if (!ctx->arena && n > 0 && ctx->cov_n == n && ctx->cov_quat == g->quat && ctx->cov_log_scale == g->log_scale)
+        p.cov = as<float>(ctx->cov);
     // the bucketed depth order takes its bounds from the depths of this projection; the slots
     // start empty (freshly carved or allocated), afterwards the order's last kernel empties them
     const bool depth_range = ctx->sort_mode == GS_SORT_DEPTH_FIRST && ctx->depth_order == GS_DEPTH_ORDER_BUCKETS;
@@ -910,6 +917,27 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     out->values_unsorted = unsorted ? as<uint32_t>(ctx->vals_unsorted) : nullptr;
     out->super_entries = super_bin ? S : 0;
     out->depth_buckets = depth_buckets;
+    return GS_OK;
+}
+
+gs_status gs_cache_covariance(gs_context *ctx, const gs_gaussians *g, hipStream_t stream) {
+    if (!ctx) return GS_ERR_INVALID_ARGUMENT;
+    if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_cache_covariance inside gs_render_noalloc");
+    ctx->cov_n = -1;   // dropped unless rebuilt below
+    ctx->cov_quat = ctx->cov_log_scale = nullptr;
+    if (!g) return GS_OK;
+    char why[160];
+    if (gs_check_arguments(g, nullptr, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
+    DeviceScope scope(ctx->device);
+    if (scope.status != hipSuccess) return fail(ctx, GS_ERR_DEVICE, "hipSetDevice failed");
+    if (g->n > 0) {
+        GS_TRY(ensure(ctx, ctx->cov, (size_t)g->n * 6 * sizeof(float)));
+        launch_covariance(g->quat, g->log_scale, (int32_t)g->n, as<float>(ctx->cov), stream);
+        GS_TRY(check_launch(ctx, "covariance cache"));
+    }
+    ctx->cov_n = g->n;
+    ctx->cov_quat = g->quat;
+    ctx->cov_log_scale = g->log_scale;
     return GS_OK;
 }
 

@@ -110,8 +110,12 @@ struct PreprocessParams {
     uint32_t *depth_range;       // [2][kDepthSlots] or null: atomic min / max of the visible depth bits
     EllipseRec *ellipse;         // [n] or null: exact-footprint rule (tile counts from the row spans)
     uint32_t *packed_count;      // [n] or null: pack_counts(tile count, rect), for super-tile binning
+    const float *cov;            // [6][n] or null: cached 3D covariances (then quat and log_scale are not read)
 };
 void launch_preprocess(const PreprocessParams &p, hipStream_t s);
+// cov[k][g], k = 0..5: upper triangle (xx, xy, xz, yy, yz, zz) of Gaussian g's 3D covariance,
+// bit-identical to what the preprocess computes from quat and log_scale
+void launch_covariance(const float *quat, const float *log_scale, int32_t n, float *cov, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // exclusive prefix sum of uint32 values (optionally gathered in[gather[i]])

@@ -57,14 +57,47 @@ __device__ inline void sh_basis(float x, float y, float z, float Y[K]) {
     }
 }
 
+// 3D covariance of Gaussian g (lesson, "Ce qu'un Gaussien porte": Sigma = R S S^T R^T with R
+// from the normalised quaternion and S = diag(exp(log_scale))), upper triangle
+// (xx, xy, xz, yy, yz, zz).  binary32 in this order, no contraction: the same bits wherever it is
+// evaluated (the preprocess, or the covariance cache it may read instead).
+__device__ __forceinline__ void covariance3d(const float *quat, const float *log_scale, int n, int g, float cov[6]) {
+#pragma clang fp contract(off)
+    const float qw = quat[g], qx = quat[n + g], qy = quat[2 * n + g], qz = quat[3 * n + g];
+    const float l0 = log_scale[g], l1 = log_scale[n + g], l2 = log_scale[2 * n + g];
+    // rotation from the normalised quaternion (w, x, y, z), Hamilton convention
+    const float nq = sqrtf(((qw * qw + qx * qx) + qy * qy) + qz * qz);
+    const float w = qw / nq, x = qx / nq, y = qy / nq, z = qz / nq;
+    float r[3][3];
+    r[0][0] = 1.0f - 2.0f * (y * y + z * z);
+    r[0][1] = 2.0f * (x * y - w * z);
+    r[0][2] = 2.0f * (x * z + w * y);
+    r[1][0] = 2.0f * (x * y + w * z);
+    r[1][1] = 1.0f - 2.0f * (x * x + z * z);
+    r[1][2] = 2.0f * (y * z - w * x);
+    r[2][0] = 2.0f * (x * z - w * y);
+    r[2][1] = 2.0f * (y * z + w * x);
+    r[2][2] = 1.0f - 2.0f * (x * x + y * y);
+    const float s[3] = {scale_activation(l0), scale_activation(l1), scale_activation(l2)};
+    // M = R diag(s); Sigma = M M^T
+    float m[3][3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) m[i][j] = r[i][j] * s[j];
+    int k = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = i; j < 3; ++j) cov[k++] = (m[i][0] * m[j][0] + m[i][1] * m[j][1]) + m[i][2] * m[j][2];
+}
+
 template <int K>
 __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) {
     const int g = blockIdx.x * kBlock + threadIdx.x;
     if (g >= p.n) return;
     const int n = p.n;
     const float mx = p.mean[g], my = p.mean[n + g], mz = p.mean[2 * n + g];
-    const float qw = p.quat[g], qx = p.quat[n + g], qy = p.quat[2 * n + g], qz = p.quat[3 * n + g];
-    const float l0 = p.log_scale[g], l1 = p.log_scale[n + g], l2 = p.log_scale[2 * n + g];
     const float opac = p.opacity[g];
 
     float tx, ty, tz, u, v, A, B, C, radius;
@@ -78,34 +111,14 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
         ty = ((W[3] * mx + W[4] * my) + W[5] * mz) + p.t[1];
         tz = ((W[6] * mx + W[7] * my) + W[8] * mz) + p.t[2];
 
-        // rotation from the normalised quaternion (w, x, y, z), Hamilton convention
-        const float nq = sqrtf(((qw * qw + qx * qx) + qy * qy) + qz * qz);
-        const float w = qw / nq, x = qx / nq, y = qy / nq, z = qz / nq;
-        float r[3][3];
-        r[0][0] = 1.0f - 2.0f * (y * y + z * z);
-        r[0][1] = 2.0f * (x * y - w * z);
-        r[0][2] = 2.0f * (x * z + w * y);
-        r[1][0] = 2.0f * (x * y + w * z);
-        r[1][1] = 1.0f - 2.0f * (x * x + z * z);
-        r[1][2] = 2.0f * (y * z - w * x);
-        r[2][0] = 2.0f * (x * z - w * y);
-        r[2][1] = 2.0f * (y * z + w * x);
-        r[2][2] = 1.0f - 2.0f * (x * x + y * y);
-        const float s[3] = {scale_activation(l0), scale_activation(l1), scale_activation(l2)};
-        // M = R diag(s); Sigma = M M^T
-        float m[3][3];
+        float cv[6];
+        if (p.cov) {   // cached by gs_cache_covariance for these parameters
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-#pragma unroll
-            for (int j = 0; j < 3; ++j) m[i][j] = r[i][j] * s[j];
-        float S[3][3];
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-#pragma unroll
-            for (int j = i; j < 3; ++j) {
-                S[i][j] = (m[i][0] * m[j][0] + m[i][1] * m[j][1]) + m[i][2] * m[j][2];
-                S[j][i] = S[i][j];
-            }
+            for (int k = 0; k < 6; ++k) cv[k] = p.cov[(size_t)k * n + g];
+        } else {
+            covariance3d(p.quat, p.log_scale, n, g, cv);
+        }
+        const float S[3][3] = {{cv[0], cv[1], cv[2]}, {cv[1], cv[3], cv[4]}, {cv[2], cv[4], cv[5]}};
         // Jacobian of (fx x/z + cx, fy y/z + cy) at the camera-space mean, times W
         const float j00 = p.fx / tz;
         const float j02 = -(p.fx * tx) / (tz * tz);
@@ -222,6 +235,18 @@ __global__ __launch_bounds__(kBlock) void preprocess_kernel(PreprocessParams p) 
     }
 }
 
+// cov[k][g] = the k-th upper-triangle element of Gaussian g's 3D covariance.
+__global__ __launch_bounds__(kBlock) void covariance_kernel(const float *__restrict__ quat,
+                                                             const float *__restrict__ log_scale, int n,
+                                                             float *__restrict__ cov) {
+    const int g = blockIdx.x * kBlock + threadIdx.x;
+    if (g >= n) return;
+    float cv[6];
+    covariance3d(quat, log_scale, n, g, cv);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) cov[(size_t)k * n + g] = cv[k];
+}
+
 __global__ __launch_bounds__(kBlock) void scale_activation_kernel(const float *__restrict__ in,
                                                                    float *__restrict__ out, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
@@ -234,6 +259,11 @@ void launch_scale_activation(const float *log_scale, float *scale, int64_t n, hi
     if (n <= 0) return;
     const int64_t blocks = (n + kBlock - 1) / kBlock;
     scale_activation_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), kBlock, 0, s>>>(log_scale, scale, n);
+}
+
+void launch_covariance(const float *quat, const float *log_scale, int32_t n, float *cov, hipStream_t s) {
+    if (n <= 0) return;
+    covariance_kernel<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(quat, log_scale, n, cov);
 }
 
 void launch_preprocess(const PreprocessParams &p, hipStream_t s) {
