@@ -23,8 +23,7 @@
 namespace gsr {
 namespace {
 
-constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup, each thread up to 64 tiles,
-constexpr int kRangeBatch = 8;        // loaded 8 per round trip
+constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup, each thread up to 64 tiles
 constexpr int kXcds = 8;              // XCDs of the chip (workgroups are dealt to them round-robin)
 constexpr int kColumnWaves = 16;      // super_column_kernel: waves per super-tile ...
 constexpr int kColumnBatch = 8;       // ... and segment counts each lane loads per round trip
@@ -235,19 +234,20 @@ __global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(Supe
 }
 
 // [start, end) of every tile: an exclusive scan of the tile totals in tile order (one
-// workgroup, each thread a run of consecutive tiles); (0, 0) for a tile without pairs.
+// workgroup, each thread a run of consecutive tiles, held in registers between the sum and the
+// writes); (0, 0) for a tile without pairs.
 __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinParams p) {
+    constexpr int kMaxPer = kMaxSuperBinningTiles / kRangeThreads;
     __shared__ uint32_t s_wave[kRangeThreads / kWave];
     const int tiles = p.tiles_x * p.tiles_y;
-    const int per = (tiles + kRangeThreads - 1) / kRangeThreads;   // at most 64
+    const int per = (tiles + kRangeThreads - 1) / kRangeThreads;   // at most kMaxPer
     const int lo = min(tiles, (int)threadIdx.x * per), hi = min(tiles, lo + per);
+    uint32_t c[kMaxPer];
     uint32_t sum = 0;
-    for (int i0 = lo; i0 < hi; i0 += kRangeBatch) {
-        uint32_t c[kRangeBatch];
 #pragma unroll
-        for (int q = 0; q < kRangeBatch; ++q) c[q] = i0 + q < hi ? p.tile_total[i0 + q] : 0u;
-#pragma unroll
-        for (int q = 0; q < kRangeBatch; ++q) sum += c[q];
+    for (int q = 0; q < kMaxPer; ++q) {
+        c[q] = lo + q < hi ? p.tile_total[lo + q] : 0u;
+        sum += c[q];
     }
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t inc = sum;
@@ -260,16 +260,11 @@ __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinPara
     __syncthreads();
     uint32_t run = inc - sum;
     for (int w = 0; w < wave; ++w) run += s_wave[w];
-    for (int i0 = lo; i0 < hi; i0 += kRangeBatch) {
-        uint32_t c[kRangeBatch];
 #pragma unroll
-        for (int q = 0; q < kRangeBatch; ++q) c[q] = i0 + q < hi ? p.tile_total[i0 + q] : 0u;
-#pragma unroll
-        for (int q = 0; q < kRangeBatch; ++q) {
-            if (i0 + q < hi)
-                reinterpret_cast<uint2 *>(p.ranges)[i0 + q] = c[q] ? make_uint2(run, run + c[q]) : make_uint2(0u, 0u);
-            run += c[q];
-        }
+    for (int q = 0; q < kMaxPer; ++q) {
+        if (lo + q < hi)
+            reinterpret_cast<uint2 *>(p.ranges)[lo + q] = c[q] ? make_uint2(run, run + c[q]) : make_uint2(0u, 0u);
+        run += c[q];
     }
 }
 

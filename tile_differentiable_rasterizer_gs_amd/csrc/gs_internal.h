@@ -120,8 +120,8 @@ void launch_covariance(const float *quat, const float *log_scale, int32_t n, flo
 // ---------------------------------------------------------------------------
 // exclusive prefix sum of uint32 values (optionally gathered in[gather[i]])
 // ---------------------------------------------------------------------------
-constexpr int kScanItems = 16;
-constexpr int kScanTile = kBlock * kScanItems;   // 4096 values per workgroup
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kBlock * kScanItems;   // 2048 values per workgroup
 // number of uint64 scratch words launch_scan needs for n values
 int64_t scan_scratch_words(int64_t n);
 // out[i] = sum_{j<i} in[j]; *total = sum of all (device uint64).  n >= 1.

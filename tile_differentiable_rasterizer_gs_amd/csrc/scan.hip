@@ -2,7 +2,7 @@
 //
 // Used for the per-Gaussian tile counts (the offsets where each Gaussian's pairs
 // start, and their total) and for the radix-sort digit histograms.  Each
-// workgroup owns 4096 consecutive values (16 per thread, blocked), so a level
+// workgroup owns 2048 consecutive values (8 per thread, blocked), so a level
 // reads its input once to reduce and once to scan: 8 B of HBM traffic per value
 // plus the 4 B write.  Partial sums are uint64 so totals above 2^32 are reported
 // exactly (the caller rejects them).
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
 
 inline int64_t blocks_for(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
 
-// Up to this many blocks (4 M values) the downsweep sums the partials itself.
+// Up to this many blocks (2 M values) the downsweep sums the partials itself.
 constexpr int64_t kDirectBlocks = 1024;
 
 // Scans `in` (n values) into `out`; partials for the next level live in scratch.
