@@ -257,7 +257,7 @@ __device__ inline void rank_bucket(const DepthBucketParams &p, uint64_t *s_ent, 
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
         const uint32_t i = threadIdx.x + e * kRankThreads;
-        cnt[e] = i < size ? count_of(p, v[e]) : 0u;
+        cnt[e] = count_of(p, i < size ? v[e] : 0ull);   // a padding lane reads Gaussian 0's, unused
         if (i < size) s_ent[i] = v[e];
     }
     // pad to a multiple of 8 entries with ~0 (never smaller than an entry)
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void bucket_subbin_kernel(DepthBucketParams
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
             const uint32_t i = threadIdx.x + e * kBlock;
-            cnt[e] = i < size ? count_of(p, v[e]) : 0u;
+            cnt[e] = count_of(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's count, unused
             sub[e] = sub_bin(v[e], b, zlo, scale);
         }
         for (int i = threadIdx.x; i < kSubBins; i += kBlock) s_cnt[i] = 0u;
