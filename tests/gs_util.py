@@ -128,3 +128,20 @@ def ranges_from_counts(per_tile: np.ndarray) -> np.ndarray:
     end = np.cumsum(per_tile)
     start = end - per_tile
     return np.where(per_tile[:, None] > 0, np.stack([start, end], 1), 0).astype(np.int64)
+
+
+def plane_scene(seed: int, n: int, depths, w: int = 320, h: int = 240, sh_degree: int = 0):
+    """Means spread over x, y in front of a camera at the origin looking down +z (R = I, t = 0,
+    so each camera-space depth is exactly the mean's z), z drawn from `depths`: a scene whose
+    depths crowd into a few values, as a flat wall facing the camera gives."""
+    rng = np.random.default_rng(seed)
+    z = rng.choice(np.asarray(depths, np.float32), n)
+    mean = np.stack([rng.uniform(-2.0, 2.0, n) * z / 5.0, rng.uniform(-1.5, 1.5, n) * z / 5.0, z]).astype(np.float32)
+    k = 3 * (sh_degree + 1) ** 2
+    arrays = dict(mean=np.ascontiguousarray(mean), quat=rng.normal(size=(4, n)).astype(np.float32),
+                  log_scale=rng.uniform(-4.5, -3.0, (3, n)).astype(np.float32),
+                  opacity=rng.uniform(-1.0, 2.0, n).astype(np.float32),
+                  sh=rng.normal(0.0, 0.3, (k, n)).astype(np.float32))
+    cam = dict(R=[1.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 1.0], t=[0.0, 0.0, 0.0], fx=250.0, fy=250.0,
+               cx=w / 2.0, cy=h / 2.0, znear=0.2, width=w, height=h)
+    return arrays, cam

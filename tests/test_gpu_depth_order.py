@@ -15,7 +15,7 @@ import pytest
 import oracle
 from tile_differentiable_rasterizer_gs_amd import binding, scenes
 
-from gs_util import check_binning, gpu_run, note
+from gs_util import check_binning, gpu_run, note, plane_scene
 
 pytestmark = pytest.mark.gpu
 
@@ -80,29 +80,13 @@ def test_bucket_order_with_super_tile_binning():
     _check(s.arrays(), 1, s.cameras[0], "super-tile binning", binning=binding.GS_BINNING_SUPER_TILE)
 
 
-def _plane_scene(seed, n, depths, w=320, h=240):
-    """Means spread over x, y in front of a camera at the origin looking down +z (R = I,
-    t = 0, so each camera-space depth is exactly the mean's z), z drawn from `depths`."""
-    rng = np.random.default_rng(seed)
-    z = rng.choice(np.asarray(depths, np.float32), n)
-    mean = np.stack([rng.uniform(-2.0, 2.0, n) * z / 5.0, rng.uniform(-1.5, 1.5, n) * z / 5.0, z]).astype(np.float32)
-    quat = rng.normal(size=(4, n)).astype(np.float32)
-    arrays = dict(mean=np.ascontiguousarray(mean), quat=quat,
-                  log_scale=rng.uniform(-4.5, -3.0, (3, n)).astype(np.float32),
-                  opacity=rng.uniform(-1.0, 2.0, n).astype(np.float32),
-                  sh=rng.normal(0.0, 0.3, (3, n)).astype(np.float32))
-    cam = dict(R=[1.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 1.0], t=[0.0, 0.0, 0.0], fx=250.0, fy=250.0,
-               cx=w / 2.0, cy=h / 2.0, znear=0.2, width=w, height=h)
-    return arrays, cam
-
-
 @pytest.mark.parametrize("depths,n,fallback", [
     ((5.0,), 6000, True),               # one depth: one bucket of 6000, the radix sort takes over
     ((3.0, 4.0, 5.0), 15000, True),     # three buckets of ~5000
     ((3.0, 4.0, 5.0), 9000, False),     # ~3000 equal depths per bucket: the widest network
 ])
 def test_bucket_order_crowded_depths(depths, n, fallback):
-    arrays, cam = _plane_scene(320 + n, n, depths)
+    arrays, cam = plane_scene(320 + n, n, depths)
     _check(arrays, 0, cam, f"depths {depths} n={n}", fallback=fallback)
 
 
@@ -137,7 +121,7 @@ def test_bucket_order_sequence_on_one_context():
     for seed, n in ((340, 3000), (341, 40000), (342, 700)):
         s = scenes.random_scene(seed, n, 0, 301, 197, log_scale_range=(-4.0, -2.0))
         frames.append((s.arrays(), s.cameras[0]))
-    frames.insert(2, _plane_scene(343, 7000, (5.0,)))   # one bucket of 7000: the fallback
+    frames.insert(2, plane_scene(343, 7000, (5.0,)))   # one bucket of 7000: the fallback
     for arrays, cam in frames:
         g = gpu_run(arrays, 0, cam, rast=r)
         check_binning(g, oracle.bin_pairs(oracle.preprocess(arrays, 0, cam)))

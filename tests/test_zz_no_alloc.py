@@ -10,7 +10,7 @@ import pytest
 import oracle
 from tile_differentiable_rasterizer_gs_amd import scenes
 
-from gs_util import IMAGE_TOL, image_error, note
+from gs_util import IMAGE_TOL, image_error, note, plane_scene
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,25 @@ def test_noalloc_render_matches_render_twice_then_smaller():
     bn = r.bin_and_sort(pr, small.cameras[0])
     img = r.composite(pr, bn, small.cameras[0], bg=(0.4, 0.0, 0.2))
     assert torch.equal(img, got)
+    r.close()
+
+
+def test_noalloc_crowded_depths_fall_back_inside_the_scratch():
+    # every depth equal: the bucketed depth order overflows and the frame is redone with the
+    # radix sort, whose buffers then come from the scratch too; twice, then a normal frame
+    import torch
+
+    from tile_differentiable_rasterizer_gs_amd import binding
+
+    r = binding.Rasterizer()
+    for seed, n, depths in ((210, 7000, (5.0,)), (211, 5000, (3.0,)), (212, 4000, (2.0, 3.0, 4.0, 6.0))):
+        arrays, cam = plane_scene(seed, n, depths)
+        note(f"noalloc crowded: n={n} depths={depths}")
+        dev = binding.gaussians_to_device(arrays)
+        ref = r.render(dev, 0, cam, bg=(0.3, 0.3, 0.1)).clone()
+        got = r.render_noalloc(dev, 0, cam, bg=(0.3, 0.3, 0.1))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), depths
     r.close()
 
 
