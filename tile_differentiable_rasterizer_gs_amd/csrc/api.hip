@@ -101,7 +101,7 @@ struct gs_context {
     DeviceBuffer pkey32[2], pkey64[2], pval[2], keys_out, keys_unsorted, vals_unsorted, psort_scratch, part;
     // super-tile binning: the super list (ping-pong), its sort scratch and partition table,
     // per-(segment, tile) counts, per-tile totals
-    DeviceBuffer skey[2], sval[2], ssort_scratch, spart, seg_tiles, tile_total, pcount;
+    DeviceBuffer skey[2], sval[2], ssort_scratch, seg_tiles, tile_total, pcount;
     bool packed_counts = false;                // the last gs_preprocess wrote pcount
     // bucketed depth order: the bound slots, the bucketed entries and the count tables
     DeviceBuffer drange, dentries, dbscratch;
@@ -272,7 +272,7 @@ int ceil_log2(int64_t v) {
 }
 
 // Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
-constexpr int kContextBuffers = 52;
+constexpr int kContextBuffers = 51;
 void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
     DeviceBuffer *all[kContextBuffers] = {
         &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
@@ -282,7 +282,7 @@ void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
         &ctx->ranges, &ctx->tile_order, &ctx->tile_weight, &ctx->tile_order_bwd, &ctx->tile_cut, &ctx->pair_base,
         &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
         &ctx->s2_trans, &ctx->s2_partial, &ctx->skey[0], &ctx->skey[1], &ctx->sval[0], &ctx->sval[1],
-        &ctx->ssort_scratch, &ctx->spart, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount, &ctx->drange,
+        &ctx->ssort_scratch, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount, &ctx->drange,
         &ctx->dentries, &ctx->dbscratch, &ctx->cov};
     for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
@@ -730,7 +730,6 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
     GS_TRY(ensure(ctx, ctx->sval[0], ss * 4));
     GS_TRY(ensure(ctx, ctx->sval[1], ss * 4));
     GS_TRY(ensure(ctx, ctx->ssort_scratch, (size_t)sort_scratch_words(scap) * 4));
-    GS_TRY(ensure(ctx, ctx->spart, (size_t)duplicate_partition_words(scap) * 4));
     GS_TRY(ensure(ctx, ctx->seg_tiles, (size_t)segs * kWave * 4));
     GS_TRY(ensure(ctx, ctx->tile_total, (size_t)tiles * 4));
     ctx->sorted_values = nullptr;
@@ -744,12 +743,11 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
     d.offsets = as<uint32_t>(ctx->offsets);
     d.order = order;
     d.rect = reinterpret_cast<const uint2 *>(pr->rect);
-    d.super = 1;
     d.tiles_x = super_x;
     d.tile_keys = as<uint32_t>(ctx->skey[0]);
     d.values = as<uint32_t>(ctx->sval[0]);
     GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-    launch_duplicate(d, as<uint32_t>(ctx->spart), stream);
+    launch_super_list(d, stream);
     GS_TRY(check_launch(ctx, "super-tile listing"));
     GS_TRY(span_end(ctx, stream));
 

@@ -233,6 +233,58 @@ __global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(Supe
     if (wave == 0 && tx < p.tiles_x && ty < p.tiles_y) p.tile_total[ty * p.tiles_x + tx] = total;
 }
 
+// The super list in rank order: a thread per ranked Gaussian writes its entries, one per
+// super-tile of its tile rectangle (row-major over the super-tiles), at its offset from the
+// prefix sum; how many is the distance to the next rank's offset (a Gaussian without pairs
+// owns none, whatever its rectangle).  With about two entries per Gaussian a thread per rank
+// is balanced enough and needs no partition table or staged rank window; a rank of more than
+// kSuperListSolo entries (a large footprint) is written by its whole wave instead, one entry
+// per lane.  Entries past the buffer's capacity are not written (a launch on buffers sized
+// for an earlier frame, which the host then repeats).
+constexpr uint32_t kSuperListSolo = 16;
+
+__device__ inline void super_entry(const DuplicateParams &p, int64_t k, uint32_t j, uint32_t g, uint2 rc) {
+    const uint32_t tx0 = rc.x & 0xffffu, tx1 = rc.x >> 16, ty0 = rc.y & 0xffffu, ty1 = rc.y >> 16;
+    const uint32_t sx0 = tx0 >> kSuperShift, sw = ((tx1 - 1) >> kSuperShift) + 1 - sx0, sy0 = ty0 >> kSuperShift;
+    const uint32_t row = j / sw, sx = sx0 + (j - row * sw), sy = sy0 + row;
+    const uint32_t cx = sx << kSuperShift, cy = sy << kSuperShift;
+    p.tile_keys[k] = super_key(sy * (uint32_t)p.tiles_x + sx, max(tx0, cx) - cx, min(tx1, cx + kSuperSide) - cx,
+                               max(ty0, cy) - cy, min(ty1, cy + kSuperSide) - cy);
+    p.values[k] = g;
+}
+
+__global__ __launch_bounds__(kBlock) void super_list_kernel(DuplicateParams p) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    int64_t k0 = 0, stop = 0;
+    uint32_t g = 0;
+    uint2 rc = make_uint2(0u, 0u);
+    if (i < p.n_items) {
+        const int64_t total = (int64_t)*p.num_dups;
+        stop = min<int64_t>(p.capacity, i + 1 < p.n_items ? (int64_t)p.offsets[i + 1] : total);
+        k0 = p.offsets[i];
+        if (k0 < stop) {
+            g = p.order ? p.order[i] : (uint32_t)i;
+            rc = p.rect[g];
+        }
+    }
+    const bool solo = stop - k0 > (int64_t)kSuperListSolo;
+    if (!solo)
+        for (int64_t k = k0; k < stop; ++k) super_entry(p, k, (uint32_t)(k - k0), g, rc);
+    // the wave writes each large rank's entries together
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    for (uint64_t m = __ballot(solo); m; m &= m - 1) {
+        const int l = __builtin_ctzll(m);
+        const int64_t a = ((int64_t)__builtin_amdgcn_readlane((int)(k0 >> 32), l) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)k0, l);
+        const int64_t b = ((int64_t)__builtin_amdgcn_readlane((int)(stop >> 32), l) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)stop, l);
+        const uint32_t gl = (uint32_t)__builtin_amdgcn_readlane((int)g, l);
+        const uint2 rl = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)rc.x, l),
+                                    (uint32_t)__builtin_amdgcn_readlane((int)rc.y, l));
+        for (int64_t k = a + lane; k < b; k += kWave) super_entry(p, k, (uint32_t)(k - a), gl, rl);
+    }
+}
+
 // [start, end) of every tile: an exclusive scan of the tile totals in tile order (one
 // workgroup, each thread a run of consecutive tiles, held in registers between the sum and the
 // writes); (0, 0) for a tile without pairs.
@@ -329,6 +381,11 @@ __global__ __launch_bounds__(kWave) void super_place_kernel(SuperBinParams p) {
 }  // namespace
 
 int64_t super_segment_capacity(int64_t entries) { return entries / kSegment + kMaxSuper + 1; }
+
+void launch_super_list(const DuplicateParams &p, hipStream_t s) {
+    if (p.n_items <= 0 || p.capacity <= 0) return;
+    super_list_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(p);
+}
 
 void launch_super_binning(const SuperBinParams &p, hipStream_t s) {
     const unsigned segs = (unsigned)p.seg_capacity;

@@ -271,8 +271,6 @@ struct DuplicateParams {
     uint16_t *tile_keys16;       // ... or as 16 bits (at most 65536 tiles); entry count multiple of 8 per block
     uint32_t *values;            // Gaussian index
     const EllipseRec *ellipse;   // null, or the exact-footprint rule: only the row spans are listed
-    int32_t super;               // 1: list each Gaussian once per super-tile of its rectangle, the key
-                                 // super_key(...) into tile_keys; tiles_x is then the super-tile width
     unsigned long long *fault;   // with ellipse: host-coherent word, bit 0 set (system scope) when a
                                  // Gaussian's row spans do not add up to its tile count
     const uint32_t *tile_count;  // [n] (needed with ellipse)
@@ -282,6 +280,10 @@ struct DuplicateParams {
 // uint32 words of the partition table launch_duplicate needs
 int64_t duplicate_partition_words(int64_t num_dups);
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s);
+// The super list in rank order, a thread per ranked Gaussian: num_dups is the device's
+// super-list total, offsets its prefix in rank order, tiles_x the super-tile width, and the
+// super_key of each entry goes to tile_keys.
+void launch_super_list(const DuplicateParams &p, hipStream_t s);
 
 struct RangesParams {
     const unsigned long long *num_dups;   // device

@@ -445,41 +445,6 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             }
         }
         if (broken) __hip_atomic_fetch_or(p.fault, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    } else if (p.super) {
-        // one entry per super-tile of the rank's rectangle, row-major over the super-tiles; the
-        // next rank with entries by the offsets (ranks without pairs own none)
-        uint32_t tx0 = rc.x & 0xffffu, tx1 = rc.x >> 16, ty0 = rc.y & 0xffffu, ty1 = rc.y >> 16;
-        uint32_t sx0 = tx0 >> kSuperShift, sw = ((tx1 - 1) >> kSuperShift) + 1 - sx0;
-        uint32_t sy0 = ty0 >> kSuperShift, sh = ((ty1 - 1) >> kSuperShift) + 1 - sy0;
-        uint32_t j = (uint32_t)e0 - off;
-        uint32_t row = j / sw, col = j - row * sw;
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) {
-            if (k < n_here) {
-                const uint32_t sx = sx0 + col, sy = sy0 + row;
-                const uint32_t cx = sx << kSuperShift, cy = sy << kSuperShift;
-                tiles[k] = super_key(sy * (uint32_t)p.tiles_x + sx, max(tx0, cx) - cx, min(tx1, cx + kSuperSide) - cx,
-                                     max(ty0, cy) - cy, min(ty1, cy + kSuperSide) - cy);
-                gs[k] = g;
-                dbs[k] = dbits;
-                if (++col == sw) {
-                    col = 0;
-                    if (++row == sh && k + 1 < n_here) {
-                        i = next_rank(i, (uint32_t)e0 + k + 1);
-                        load_rank(i, g, off, rc, dbits);
-                        tx0 = rc.x & 0xffffu;
-                        tx1 = rc.x >> 16;
-                        ty0 = rc.y & 0xffffu;
-                        ty1 = rc.y >> 16;
-                        sx0 = tx0 >> kSuperShift;
-                        sw = ((tx1 - 1) >> kSuperShift) + 1 - sx0;
-                        sy0 = ty0 >> kSuperShift;
-                        sh = ((ty1 - 1) >> kSuperShift) + 1 - sy0;
-                        row = 0;
-                    }
-                }
-            }
-        }
     } else {
     uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu, h = (rc.y >> 16) - y0;
     uint32_t j = (uint32_t)e0 - off;
