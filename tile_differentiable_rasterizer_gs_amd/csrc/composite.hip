@@ -26,20 +26,32 @@
 namespace gsr {
 namespace {
 
-constexpr int kThreads = 128;                // 64 lanes x 2 pixels = one 16x8 half tile per wave
-constexpr int kBatch = 128;                  // splats per LDS batch (9.5 KB of LDS per workgroup: 6 waves per SIMD)
-constexpr int kLoads = kBatch / kThreads;    // records gathered per thread per batch
+// Workgroup shape by pixels per lane: two (two waves of 16 x 8 pixels: the row terms shared by a
+// lane's pixels; the default) or one (four waves of 16 x 4: twice the waves on a tile, for images
+// of few tiles, where the frame waits on its heaviest tiles' serial blend chains).
+template <int kPix>
+struct Shape {
+    static constexpr int kThreads = kTile * kTile / kPix;   // 128 or 256
+    static constexpr int kBatch = 128 * (3 - kPix);         // splats per LDS batch (9.5 KB of LDS per
+                                                            // two-pixel workgroup: 6 waves per SIMD)
+    static constexpr int kLoads = kBatch / kThreads;        // records gathered per thread per batch
+    static constexpr int kRowsPerWave = kWave * kPix / kTile;
+};
+constexpr int kFewTiles = 1024;              // images with fewer tiles take one pixel per lane
 constexpr int kUnroll = 8;                   // splats between wave exit tests
+static_assert(Shape<1>::kLoads == 1 && Shape<2>::kLoads == 1, "one record per thread per batch");
 
 // A staged splat: what the per-pixel blend reads (a, c) apart from what only the per-row
 // terms need (b), so that the blend reads two LDS words per splat.
+template <int kLoads>
 struct Staged {
     float4 a[kLoads];   // u, A', 0.99 r, 0.99 g
     float4 b[kLoads];   // v, log2(o / 0.99), B', C'
     float c[kLoads];    // 0.99 b
 };
 
-__device__ __forceinline__ void gather(Staged &st, const float *__restrict__ splat,
+template <int kThreads, int kLoads>
+__device__ __forceinline__ void gather(Staged<kLoads> &st, const float *__restrict__ splat,
                                        const uint32_t *__restrict__ values, uint32_t base, uint32_t end) {
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
@@ -82,11 +94,11 @@ __device__ __forceinline__ float lane_pull(int src, float v) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-template <bool kAux>
+template <bool kAux, int kPix>
 struct Pixels {
-    float x0, x1, y;
-    float T[2], r[2], g[2], b[2];
-    uint32_t blended[2];
+    float x0, x1, y;   // x1: the second pixel's column (kPix == 2)
+    float T[kPix], r[kPix], g[kPix], b[kPix];
+    uint32_t blended[kPix];
 
     __device__ __forceinline__ void blend(const float4 a, const float4 b4, const float c) {
         const float dy = y - b4.x;
@@ -95,7 +107,7 @@ struct Pixels {
     // the same, given the splat's row terms B' dy and C' dy^2 + log2(o / 0.99) for this lane's row
     __device__ __forceinline__ void blend_row(const float4 a, const float c, const float bdy, const float e) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kPix; ++i) {
             const float dx = (i ? x1 : x0) - a.x;
             // alpha / GS_ALPHA_MAX; the colours are staged times GS_ALPHA_MAX
             const float as = splat_alpha_scaled(splat_exponent(dx, a.y, bdy, e));
@@ -122,7 +134,12 @@ struct Pixels {
         T[0] = __builtin_fmaf(-GS_ALPHA_MAX, w, T[0]);
         if (kAux) blended[0] += live ? 1u : 0u;
     }
-    __device__ __forceinline__ bool live() const { return (T[0] >= GS_T_EPS) | (T[1] >= GS_T_EPS); }
+    __device__ __forceinline__ bool live() const {
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < kPix; ++i) any |= T[i] >= GS_T_EPS;
+        return any;
+    }
 };
 
 // Output of one pixel: C + T bg, and the per-pixel state the backward reads.
@@ -141,8 +158,10 @@ __device__ __forceinline__ void write_pixel(const CompositeParams &p, int x, int
     }
 }
 
-template <bool kAux>
-__global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) {
+template <bool kAux, int kPix>
+__global__ __launch_bounds__(Shape<kPix>::kThreads) void composite_kernel(CompositeParams p) {
+    constexpr int kThreads = Shape<kPix>::kThreads, kBatch = Shape<kPix>::kBatch, kLoads = Shape<kPix>::kLoads;
+    constexpr int kPerRow = kTile / kPix;   // lanes of a pixel row (16 or 8): groups of 8 share its row terms
     __shared__ float4 s_a[2][kBatch], s_b[2][kBatch];
     __shared__ float s_c[2][kBatch];
     const float *__restrict__ splat = p.splat;
@@ -150,25 +169,25 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
     const int tile = p.tile_order ? (int)p.tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tile_x = tile % p.tiles_x, tile_y = tile / p.tiles_x;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int ix = tile_x * kTile + (lane & 7);
-    const int iy = tile_y * kTile + wave * 8 + (lane >> 3);
+    const int ix = tile_x * kTile + (lane % kPerRow);
+    const int iy = tile_y * kTile + wave * Shape<kPix>::kRowsPerWave + lane / kPerRow;
 
-    Pixels<kAux> px;
+    Pixels<kAux, kPix> px;
     px.x0 = (float)ix;
     px.x1 = (float)(ix + 8);
     px.y = (float)iy;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kPix; ++i) {
         px.T[i] = (ix + 8 * i < p.width && iy < p.height) ? 1.0f : 0.0f;
         px.r[i] = px.g[i] = px.b[i] = 0.0f;
         px.blended[i] = 0u;
     }
 
     const uint32_t start = p.ranges[2 * tile], end = p.ranges[2 * tile + 1];
-    Staged st;
+    Staged<kLoads> st;
     int buf = 0;
     if (start < end) {
-        gather(st, splat, values, start, end);
+        gather<kThreads, kLoads>(st, splat, values, start, end);
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
             s_a[0][k * kThreads + threadIdx.x] = st.a[k];
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
     uint32_t total = 0;
     for (uint32_t base = start; base < end; base += kBatch) {
         const uint32_t next = base + kBatch;
-        if (next < end) gather(st, splat, values, next, end);   // in flight during the blends below
+        if (next < end) gather<kThreads, kLoads>(st, splat, values, next, end);   // in flight during the blends below
         const int count = (int)min<uint32_t>(kBatch, end - base);
         const float4 *sa = s_a[buf];
         const float4 *sb = s_b[buf];
@@ -212,48 +231,55 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
                 GS_BLEND_ROW(7);
 #undef GS_BLEND_ROW
                 j += kUnroll;
-                const uint64_t m0 = __ballot(px.T[0] >= GS_T_EPS), m1 = __ballot(px.T[1] >= GS_T_EPS);
-                if ((m0 | m1) == 0) {
-                    done = true;
-                    break;
-                }
-                const uint32_t n0 = (uint32_t)__popcll(m0), n = n0 + (uint32_t)__popcll(m1);
-                if (n <= (uint32_t)kWave) {
-                    // Pack: lane k takes the wave's k-th live pixel, slot 0 ones (in lane order)
-                    // before slot 1 ones.  First write this lane's pixels that are not live.
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (!(px.T[i] >= GS_T_EPS)) {
-                            write_pixel<kAux>(p, ix + 8 * i, iy, px.r[i], px.g[i], px.b[i], px.T[i], px.blended[i]);
-                            total += px.blended[i];
-                        }
-                    const uint32_t k = (uint32_t)lane;
-                    const bool second = k >= n0;
-                    held = k < n;
-                    const int src = held ? (int)(second ? nth_set_bit(m1, k - n0) : nth_set_bit(m0, k)) : lane;
-                    float v[2][4];
-                    uint32_t nb[2];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        v[i][0] = lane_pull(src, px.T[i]);
-                        v[i][1] = lane_pull(src, px.r[i]);
-                        v[i][2] = lane_pull(src, px.g[i]);
-                        v[i][3] = lane_pull(src, px.b[i]);
-                        nb[i] = kAux ? (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)px.blended[i]) : 0u;
+                if constexpr (kPix == 1) {
+                    if (!__any(px.T[0] >= GS_T_EPS)) {
+                        done = true;
+                        break;
                     }
-                    const int i = second ? 1 : 0;
-                    sx = tile_x * kTile + (src & 7) + 8 * i;
-                    sy = tile_y * kTile + wave * 8 + (src >> 3);
-                    px.T[0] = held ? (second ? v[1][0] : v[0][0]) : 0.0f;
-                    px.r[0] = second ? v[1][1] : v[0][1];
-                    px.g[0] = second ? v[1][2] : v[0][2];
-                    px.b[0] = second ? v[1][3] : v[0][3];
-                    px.blended[0] = second ? nb[1] : nb[0];
-                    px.T[1] = 0.0f;
-                    px.x0 = (float)sx;
-                    px.y = (float)sy;
-                    single = true;
-                    break;
+                } else {
+                    const uint64_t m0 = __ballot(px.T[0] >= GS_T_EPS), m1 = __ballot(px.T[kPix - 1] >= GS_T_EPS);
+                    if ((m0 | m1) == 0) {
+                        done = true;
+                        break;
+                    }
+                    const uint32_t n0 = (uint32_t)__popcll(m0), n = n0 + (uint32_t)__popcll(m1);
+                    if (n <= (uint32_t)kWave) {
+                        // Pack: lane k takes the wave's k-th live pixel, slot 0 ones (in lane order)
+                        // before slot 1 ones.  First write this lane's pixels that are not live.
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+                            if (!(px.T[i] >= GS_T_EPS)) {
+                                write_pixel<kAux>(p, ix + 8 * i, iy, px.r[i], px.g[i], px.b[i], px.T[i], px.blended[i]);
+                                total += px.blended[i];
+                            }
+                        const uint32_t k = (uint32_t)lane;
+                        const bool second = k >= n0;
+                        held = k < n;
+                        const int src = held ? (int)(second ? nth_set_bit(m1, k - n0) : nth_set_bit(m0, k)) : lane;
+                        float v[2][4];
+                        uint32_t nb[2];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            v[i][0] = lane_pull(src, px.T[i]);
+                            v[i][1] = lane_pull(src, px.r[i]);
+                            v[i][2] = lane_pull(src, px.g[i]);
+                            v[i][3] = lane_pull(src, px.b[i]);
+                            nb[i] = kAux ? (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)px.blended[i]) : 0u;
+                        }
+                        const int i = second ? 1 : 0;
+                        sx = tile_x * kTile + (src & 7) + 8 * i;
+                        sy = tile_y * kTile + wave * 8 + (src >> 3);
+                        px.T[0] = held ? (second ? v[1][0] : v[0][0]) : 0.0f;
+                        px.r[0] = second ? v[1][1] : v[0][1];
+                        px.g[0] = second ? v[1][2] : v[0][2];
+                        px.b[0] = second ? v[1][3] : v[0][3];
+                        px.blended[0] = second ? nb[1] : nb[0];
+                        px.T[1] = 0.0f;
+                        px.x0 = (float)sx;
+                        px.y = (float)sy;
+                        single = true;
+                        break;
+                    }
                 }
             }
             if (!done && !single)
@@ -285,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
 
     if (!single) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kPix; ++i) {
             write_pixel<kAux>(p, ix + 8 * i, iy, px.r[i], px.g[i], px.b[i], px.T[i], px.blended[i]);
             total += px.blended[i];
         }
@@ -303,15 +329,23 @@ __global__ __launch_bounds__(kThreads) void composite_kernel(CompositeParams p) 
     }
 }
 
+template <int kPix>
+void launch_shape(const CompositeParams &p, unsigned tiles, hipStream_t s) {
+    if (p.final_T || p.n_blend || p.blend_total)
+        composite_kernel<true, kPix><<<tiles, Shape<kPix>::kThreads, 0, s>>>(p);
+    else
+        composite_kernel<false, kPix><<<tiles, Shape<kPix>::kThreads, 0, s>>>(p);
+}
+
 }  // namespace
 
 void launch_composite(const CompositeParams &p, hipStream_t s) {
     const unsigned tiles = (unsigned)(p.tiles_x * p.tiles_y);
     if (tiles == 0) return;
-    if (p.final_T || p.n_blend || p.blend_total)
-        composite_kernel<true><<<tiles, kThreads, 0, s>>>(p);
+    if (tiles < (unsigned)kFewTiles)
+        launch_shape<1>(p, tiles, s);
     else
-        composite_kernel<false><<<tiles, kThreads, 0, s>>>(p);
+        launch_shape<2>(p, tiles, s);
 }
 
 }  // namespace gsr
