@@ -37,7 +37,7 @@ struct Shape {
     static constexpr int kLoads = kBatch / kThreads;        // records gathered per thread per batch
     static constexpr int kRowsPerWave = kWave * kPix / kTile;
 };
-constexpr int kFewTiles = 1024;              // images with fewer tiles take one pixel per lane
+constexpr int kFewTiles = 4096;              // images with fewer tiles take one pixel per lane
 constexpr int kUnroll = 8;                   // splats between wave exit tests
 static_assert(Shape<1>::kLoads == 1 && Shape<2>::kLoads == 1, "one record per thread per batch");
 
