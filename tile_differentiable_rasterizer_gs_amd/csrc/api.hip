@@ -34,6 +34,9 @@ namespace {
 
 // pair indices are uint32 throughout
 constexpr int64_t kMaxPairs = 0xffffffffll;
+// pair capacity per Gaussian up to which the depth-first square-rule listing takes a thread per
+// rank (5 pairs per Gaussian at 10 k: 15.6 -> 7.1 us; 16 at 1 M: 38 -> 67 us, so not there)
+constexpr int64_t kPairListPerRank = 8;
 
 struct DeviceBuffer {
     void *ptr = nullptr;
@@ -597,7 +600,12 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
         else
             d.tile_keys = as<uint32_t>(ctx->pkey32[0]);
         GS_TRY(span_begin(ctx, GS_STAGE_DUPLICATE, stream));
-        launch_duplicate(d, as<uint32_t>(ctx->part), stream);
+        // a thread per rank for short lists per Gaussian; the windowed listing balances long ones
+        // (and walks the row spans of the exact-footprint rule); both list the same pairs
+        if (!d.ellipse && cap <= kPairListPerRank * ctx->n)
+            launch_pair_list(d, stream);
+        else
+            launch_duplicate(d, as<uint32_t>(ctx->part), stream);
         GS_TRY(check_launch(ctx, "duplicate"));
         GS_TRY(span_end(ctx, stream));
         GS_TRY(span_begin(ctx, GS_STAGE_TILE_SORT, stream));

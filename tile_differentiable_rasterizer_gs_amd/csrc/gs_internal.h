@@ -280,6 +280,9 @@ struct DuplicateParams {
 // uint32 words of the partition table launch_duplicate needs
 int64_t duplicate_partition_words(int64_t num_dups);
 void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s);
+// Depth-first listing under the square rule (tile_keys16 or tile_keys, values; no ellipse, no
+// 64-bit keys), a thread per ranked Gaussian; also zeroes clear[0, clear_words).
+void launch_pair_list(const DuplicateParams &p, hipStream_t s);
 // The super list in rank order, a thread per ranked Gaussian: num_dups is the device's
 // super-list total, offsets its prefix in rank order, tiles_x the super-tile width, and the
 // super_key of each entry goes to tile_keys.

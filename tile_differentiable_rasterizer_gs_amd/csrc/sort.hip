@@ -520,6 +520,59 @@ __device__ __forceinline__ uint32_t tile_of_entry(const RangesParams &p, int64_t
     else return p.tile_keys[e];
 }
 
+// Depth-first listing under the square rule, a thread per ranked Gaussian: its pairs, row-major
+// over its tile rectangle, at its offset from the prefix sum (as many as the distance to the
+// next rank's offset); a rank of more than kPairListSolo pairs is written by its whole wave,
+// one pair per lane.  Needs no partition table or staged rank window.  Pairs past the buffer's
+// capacity are not written (a launch on buffers sized for an earlier frame, which the host
+// then repeats).  Also zeroes clear[0, clear_words) (the tile ranges, so that tiles without
+// pairs read as empty).
+constexpr uint32_t kPairListSolo = 16;
+
+template <bool kKey16>
+__device__ inline void pair_entry(const DuplicateParams &p, int64_t k, uint32_t j, uint32_t g, uint2 rc) {
+    const uint32_t x0 = rc.x & 0xffffu, w = (rc.x >> 16) - x0, y0 = rc.y & 0xffffu;
+    const uint32_t row = j / w, tile = (y0 + row) * (uint32_t)p.tiles_x + x0 + (j - row * w);
+    if constexpr (kKey16)
+        p.tile_keys16[k] = (uint16_t)tile;
+    else
+        p.tile_keys[k] = tile;
+    p.values[k] = g;
+}
+
+template <bool kKey16>
+__global__ __launch_bounds__(kBlock) void pair_list_kernel(DuplicateParams p) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    for (int64_t w = i; w < p.clear_words; w += (int64_t)gridDim.x * kBlock) p.clear[w] = 0u;
+    int64_t k0 = 0, stop = 0;
+    uint32_t g = 0;
+    uint2 rc = make_uint2(0u, 0u);
+    if (i < p.n_items) {
+        stop = min<int64_t>(p.capacity, i + 1 < p.n_items ? (int64_t)p.offsets[i + 1] : (int64_t)*p.num_dups);
+        k0 = p.offsets[i];
+        if (k0 < stop) {
+            g = p.order ? p.order[i] : (uint32_t)i;
+            rc = p.rect[g];
+        }
+    }
+    const bool solo = stop - k0 > (int64_t)kPairListSolo;
+    if (!solo)
+        for (int64_t k = k0; k < stop; ++k) pair_entry<kKey16>(p, k, (uint32_t)(k - k0), g, rc);
+    // the wave writes each large rank's pairs together
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    for (uint64_t m = __ballot(solo); m; m &= m - 1) {
+        const int l = __builtin_ctzll(m);
+        const int64_t a = ((int64_t)__builtin_amdgcn_readlane((int)(k0 >> 32), l) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)k0, l);
+        const int64_t b = ((int64_t)__builtin_amdgcn_readlane((int)(stop >> 32), l) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)stop, l);
+        const uint32_t gl = (uint32_t)__builtin_amdgcn_readlane((int)g, l);
+        const uint2 rl = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)rc.x, l),
+                                    (uint32_t)__builtin_amdgcn_readlane((int)rc.y, l));
+        for (int64_t k = a + lane; k < b; k += kWave) pair_entry<kKey16>(p, k, (uint32_t)(k - a), gl, rl);
+    }
+}
+
 template <int kKind>
 __global__ __launch_bounds__(kBlock) void ranges_kernel(RangesParams p) {
     const int64_t num_dups = live_count(p.capacity, p.num_dups);
@@ -651,6 +704,15 @@ void launch_duplicate(const DuplicateParams &p, uint32_t *part, hipStream_t s) {
         else
             duplicate_kernel<false, kDupItems><<<nb, kBlock, 0, s>>>(p, part);
     }
+}
+
+void launch_pair_list(const DuplicateParams &p, hipStream_t s) {
+    if (p.capacity <= 0 || p.n_items <= 0) return;
+    const unsigned grid = (unsigned)((p.n_items + kBlock - 1) / kBlock);
+    if (p.tile_keys16)
+        pair_list_kernel<true><<<grid, kBlock, 0, s>>>(p);
+    else
+        pair_list_kernel<false><<<grid, kBlock, 0, s>>>(p);
 }
 
 void launch_ranges(const RangesParams &p, hipStream_t s) {
