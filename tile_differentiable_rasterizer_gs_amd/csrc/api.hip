@@ -818,7 +818,6 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     GS_TRY(ensure(ctx, ctx->total, 3 * sizeof(unsigned long long)));
     GS_TRY(ensure(ctx, ctx->ranges, (size_t)tiles * 2 * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->tile_order, (size_t)tiles * sizeof(uint32_t)));
-    unsigned long long *d_total = as<unsigned long long>(ctx->total);
 
     // super-tile binning where it applies (depth-first mode; counts packed for the scan)
     const int64_t super_tiles = (int64_t)((ctx->tiles_x + kSuperSide - 1) / kSuperSide) *

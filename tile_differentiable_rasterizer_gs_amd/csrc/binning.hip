@@ -7,8 +7,10 @@
 // Tiles are grouped 8 x 8 into super-tiles; every Gaussian is listed once per super-tile of
 // its rectangle, with its part of the rectangle inside that super-tile in the key, and that
 // short list (about two entries per Gaussian at 1080p) is sorted stably by super-tile in one
-// 8-bit radix pass (sort.hip), so each super-tile's list keeps the depth order.  Here each super-tile's list is cut into segments of kSegment entries, one
-// wave each, taken 64 entries (one per lane) at a time.  An entry's tiles inside its
+// 8-bit radix pass (sort.hip), so each super-tile's list keeps the depth order.  Here each
+// super-tile's list is cut into segments of kSegment entries, one wave each (one per lane);
+// a workgroup's waves take consecutive segments and share the segment table that its first
+// wave builds in LDS.  An entry's tiles inside its
 // super-tile form a 64-bit mask (bit 8 r + c: tile column c, row r of the super-tile), one
 // row span per tile row: the rectangle's columns, or the exact-footprint rule's span.
 //   super_count_kernel   pairs per (segment, tile), from span corners in an LDS difference grid
@@ -27,6 +29,12 @@ constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup, each
 constexpr int kXcds = 8;              // XCDs of the chip (workgroups are dealt to them round-robin)
 constexpr int kColumnWaves = 16;      // super_column_kernel: waves per super-tile ...
 constexpr int kColumnBatch = 8;       // ... and segment counts each lane loads per round trip
+// Segments (one a wave) per workgroup, which share the workgroup's segment table: the count
+// kernel takes 4; the place kernel 4, or 16 from kPlaceWideSegs segments on (a larger grid
+// hides the table's build better in bigger workgroups).
+constexpr int kCountWaves = 4;
+constexpr int kPlaceWaves = 4, kPlaceWideWaves = 16;
+constexpr uint32_t kPlaceWideSegs = 1u << 16;
 
 // Segment geometry from the super-tile totals, built by the first wave of each workgroup:
 // super-tile s owns segments [first[s], first[s + 1]) and entries [start[s], start[s + 1]) of
@@ -146,17 +154,18 @@ static_assert(kSegment == kWave, "one entry per lane");
 // Pairs per (segment, tile of its super-tile): each entry adds +1 / -1 at the corners of its
 // part (the rectangle, or each row span of the exact-footprint rule) in a 9 x 9 difference
 // grid, whose 2D prefix is then the count of each tile.  The square rule reads the keys only.
-__global__ __launch_bounds__(kWave) void super_count_kernel(SuperBinParams p) {
+__global__ __launch_bounds__(kCountWaves * kWave) void super_count_kernel(SuperBinParams p) {
     __shared__ SegmentTable t;
-    __shared__ uint32_t s_diff[kSuperSide + 1][kSuperSide + 1];
+    __shared__ uint32_t s_all[kCountWaves][kSuperSide + 1][kSuperSide + 1];
     build_segment_table(p, t);
-    const uint32_t seg = blockIdx.x;
-    if (seg >= t.first[kMaxSuper]) return;
-    const SegmentRange r = segment_range(p, t, seg);
-    const uint32_t lane = threadIdx.x;
+    const uint32_t lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const uint32_t seg = blockIdx.x * kCountWaves + wave;
+    const bool live = seg < t.first[kMaxSuper];   // the workgroup's barriers need every wave
+    uint32_t(&s_diff)[kSuperSide + 1][kSuperSide + 1] = s_all[wave];
+    const SegmentRange r = segment_range(p, t, live ? seg : 0u);
     for (uint32_t i = lane; i < (kSuperSide + 1) * (kSuperSide + 1); i += kWave) (&s_diff[0][0])[i] = 0u;
     const uint32_t e = r.a + lane;
-    const uint32_t key = p.keys[e < r.b ? e : r.a];
+    const uint32_t key = live ? p.keys[e < r.b ? e : r.a] : 0u;
     __syncthreads();
     auto corners = [&](uint32_t r0, uint32_t r1, uint32_t a, uint32_t b) {   // rows [r0, r1), columns [a, b)
         atomicAdd(&s_diff[r0][a], 1u);
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kWave) void super_count_kernel(SuperBinParams p) {
         atomicAdd(&s_diff[r1][a], 0xffffffffu);
         atomicAdd(&s_diff[r1][b], 1u);
     };
-    if (e < r.b) {
+    if (live && e < r.b) {
         const LocalRect lr = local_rect(key);
         if (p.ellipse) {
             const EllipseRec E = p.ellipse[p.gauss[e]];
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(kWave) void super_count_kernel(SuperBinParams p) {
     if (lane <= kSuperSide)
         for (int row = 1; row <= kSuperSide; ++row) s_diff[row][lane] += s_diff[row - 1][lane];
     __syncthreads();
-    p.seg_tiles[(size_t)seg * kWave + lane] = s_diff[lane / kSuperSide][lane % kSuperSide];
+    if (live) p.seg_tiles[(size_t)seg * kWave + lane] = s_diff[lane / kSuperSide][lane % kSuperSide];
 }
 
 // One workgroup per super-tile; lane k of each wave owns tile k.  The super-tile's segments are
@@ -328,8 +337,8 @@ __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinPara
 // value buffer holds (a launch on buffers sized for an earlier frame, which the host then
 // repeats) nothing is written.  kKeys: also the 64-bit keys.  kNarrow: positions below 2^30,
 // so a store's address is the buffer plus a 32-bit byte offset.
-template <bool kKeys, bool kNarrow>
-__global__ __launch_bounds__(kWave) void super_place_kernel(SuperBinParams p) {
+template <bool kKeys, bool kNarrow, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void super_place_kernel(SuperBinParams p) {
     __shared__ SegmentTable t;
     if ((int64_t)*p.num_dups > p.capacity) return;
     build_segment_table(p, t);
@@ -337,10 +346,10 @@ __global__ __launch_bounds__(kWave) void super_place_kernel(SuperBinParams p) {
     // contiguous block of segments, so the short runs that consecutive segments write into
     // one tile's list meet in one L2 and leave it as whole lines.
     const uint32_t per_xcd = gridDim.x / kXcds;   // the grid is a multiple of kXcds
-    const uint32_t seg = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const uint32_t seg = ((blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
     if (seg >= t.first[kMaxSuper]) return;
     const SegmentRange r = segment_range(p, t, seg);
-    const uint32_t lane = threadIdx.x;
+    const uint32_t lane = threadIdx.x % kWave;
     const uint32_t e = r.a + lane;
     const bool valid = e < r.b;
     const uint32_t key = p.keys[valid ? e : r.a];   // a lane past the segment meets no tile
@@ -387,19 +396,27 @@ void launch_super_list(const DuplicateParams &p, hipStream_t s) {
     super_list_kernel<<<(unsigned)((p.n_items + kBlock - 1) / kBlock), kBlock, 0, s>>>(p);
 }
 
+template <int kWaves>
+void launch_place(const SuperBinParams &p, unsigned segs, hipStream_t s) {
+    // every segment below the capacity has a wave; the grid is a multiple of kXcds
+    const unsigned groups = ((segs + kWaves - 1) / kWaves + kXcds - 1) / kXcds * kXcds;
+    if (p.keys_out)
+        super_place_kernel<true, false, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
+    else if (p.capacity <= ((int64_t)1 << 30))
+        super_place_kernel<false, true, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
+    else
+        super_place_kernel<false, false, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
+}
+
 void launch_super_binning(const SuperBinParams &p, hipStream_t s) {
     const unsigned segs = (unsigned)p.seg_capacity;
-    super_count_kernel<<<segs, kWave, 0, s>>>(p);
+    super_count_kernel<<<(segs + kCountWaves - 1) / kCountWaves, kCountWaves * kWave, 0, s>>>(p);
     super_column_kernel<<<(unsigned)(p.super_x * p.super_y), kColumnWaves * kWave, 0, s>>>(p);
     tile_ranges_kernel<<<1, kRangeThreads, 0, s>>>(p);
-    const bool narrow = p.capacity <= ((int64_t)1 << 30);
-    const unsigned segs8 = (segs + kXcds - 1) / kXcds * kXcds;   // every segment below it has a workgroup
-    if (p.keys_out)
-        super_place_kernel<true, false><<<segs8, kWave, 0, s>>>(p);
-    else if (narrow)
-        super_place_kernel<false, true><<<segs8, kWave, 0, s>>>(p);
+    if (segs >= kPlaceWideSegs)
+        launch_place<kPlaceWideWaves>(p, segs, s);
     else
-        super_place_kernel<false, false><<<segs8, kWave, 0, s>>>(p);
+        launch_place<kPlaceWaves>(p, segs, s);
 }
 
 }  // namespace gsr

@@ -346,7 +346,6 @@ __global__ __launch_bounds__(kBlock) void bucket_subbin_kernel(DepthBucketParams
         }
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
-            const uint32_t i = threadIdx.x + e * kBlock;
             cnt[e] = count_of(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's count, unused
             sub[e] = sub_bin(v[e], b, zlo, scale);
         }
