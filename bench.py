@@ -76,17 +76,18 @@ def stage_bytes(n, sh_degree, m, n_visible, supers, tiles, buckets):
         # one 8-bit pass over the super list (count reads the key; scatter reads and writes key and
         # value), the count and place kernels read it again, each tile entry written once (4 B),
         # the per-segment tile counts written, read and rewritten by the column scan, read by place
+        # (+ the tile totals read and the heaviest-first launch order written by the place kernel)
         segs = supers // 64 + 257
-        tile_sort = supers * (4 + 16) + supers * (4 + 8) + m * 4 + segs * 64 * 4 * 4 + tiles * 12
-        ranges = tiles * 12              # the heaviest-first launch order from the ranges
+        tile_sort = supers * (4 + 16) + supers * (4 + 8) + m * 4 + segs * 64 * 4 * 4 + tiles * 12 + tiles * 8
+        ranges = None
     else:
         kb = 2 if tiles <= 1 << 16 else 4   # tile-id key bytes
         passes = max(1, (max(tiles - 1, 1).bit_length() + 7) // 8)
         dup = n_visible * (4 + 4 + 8) + m * (kb + 4)
         tile_sort = passes * m * (kb + 2 * (kb + 4))   # count reads the key; scatter reads and writes both
         ranges = m * kb + tiles * 12
-    return dict(preprocess=pre, depth_sort=depth_sort, scan=scan, duplicate=dup, tile_sort=tile_sort,
-                ranges=ranges)
+    out = dict(preprocess=pre, depth_sort=depth_sort, scan=scan, duplicate=dup, tile_sort=tile_sort, ranges=ranges)
+    return {k: v for k, v in out.items() if v is not None}
 
 
 def _profile_summary(path):

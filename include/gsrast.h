@@ -229,11 +229,13 @@ typedef enum {
 /* Per-stage timing collected while GS_OPT_PROFILE is 1. */
 typedef enum {
     GS_STAGE_PREPROCESS = 0,
-    GS_STAGE_DEPTH_SORT = 1,   /* depth-first mode: radix passes over the per-Gaussian depth keys */
+    GS_STAGE_DEPTH_SORT = 1,   /* depth-first mode: the depth order (buckets or radix passes) */
     GS_STAGE_SCAN = 2,         /* prefix sum of tile counts */
-    GS_STAGE_DUPLICATE = 3,
-    GS_STAGE_TILE_SORT = 4,    /* radix passes over the pair list */
-    GS_STAGE_RANGES = 5,       /* tile ranges (+ key emission), heaviest-first tile launch order */
+    GS_STAGE_DUPLICATE = 3,    /* pair listing, or the super-tile listing */
+    GS_STAGE_TILE_SORT = 4,    /* radix passes over the pair list; or super-tile sort, expansion into
+                                  tiles, ranges and the heaviest-first tile launch order */
+    GS_STAGE_RANGES = 5,       /* radix binning: tile ranges (+ key emission), heaviest-first tile
+                                  launch order; not recorded under super-tile binning */
     GS_STAGE_COMPOSITE = 6,
     GS_STAGE_READBACK = 7,     /* not recorded: the pair count reaches the host with no stream operation */
     GS_STAGE_BACKWARD_COMPOSITE = 8,   /* gs_backward: per-tile reverse walk */

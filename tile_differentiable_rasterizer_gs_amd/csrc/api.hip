@@ -785,18 +785,12 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
         b.depth = pr->depth;
         b.keys_out = as<uint64_t>(ctx->keys_out);
     }
+    // the heaviest-first launch order comes from the place kernel's first workgroup
+    b.order = tiles <= kMaxOrderedTiles ? as<uint32_t>(ctx->tile_order) : nullptr;
     launch_super_binning(b, stream);
     GS_TRY(check_launch(ctx, "super-tile expansion"));
     GS_TRY(span_end(ctx, stream));
-
-    GS_TRY(span_begin(ctx, GS_STAGE_RANGES, stream));
-    TileOrderParams o{};
-    o.tiles = (int32_t)tiles;
-    o.ranges = b.ranges;
-    o.order = as<uint32_t>(ctx->tile_order);
-    ctx->launch_order = launch_tile_order(o, stream) ? o.order : nullptr;
-    GS_TRY(check_launch(ctx, "tile order"));
-    GS_TRY(span_end(ctx, stream));
+    ctx->launch_order = b.order;
     ctx->sorted_values = b.values;
     ctx->sorted_keys = b.keys_out;
     return GS_OK;

@@ -17,7 +17,8 @@
 //   super_column_kernel  per super-tile: each segment's offset within each tile, tile totals
 //   tile_ranges_kernel   exclusive scan of the tile totals: [start, end) per tile
 //   super_place_kernel   per tile of the super-tile, a ballot ranks the chunk's entries that
-//                        meet it, and they write at the tile's next position plus their rank
+//                        meet it, and they write at the tile's next position plus their rank;
+//                        its first workgroup builds the tiles' launch order (order_tiles)
 // The lists equal those of a stable sort of the pairs by tile, and each pair is written once,
 // 4 bytes (plus 8 when the 64-bit keys are asked for).
 #include "gs_internal.h"
@@ -337,16 +338,38 @@ __global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinPara
 // value buffer holds (a launch on buffers sized for an earlier frame, which the host then
 // repeats) nothing is written.  kKeys: also the 64-bit keys.  kNarrow: positions below 2^30,
 // so a store's address is the buffer plus a 32-bit byte offset.
+template <int kWaves>
+union PlaceShared {
+    SegmentTable t;
+    struct {
+        uint32_t count[kOrderBuckets];
+        uint32_t wave[kWaves];
+    } order;
+};
+
 template <bool kKeys, bool kNarrow, int kWaves>
 __global__ __launch_bounds__(kWaves * kWave) void super_place_kernel(SuperBinParams p) {
-    __shared__ SegmentTable t;
+    __shared__ PlaceShared<kWaves> sh;
+    SegmentTable &t = sh.t;
+    // With a launch order asked for, workgroup 0 builds it from the tile totals (complete since
+    // the column kernel) while the others place the pairs; it starts first and hides under them.
+    uint32_t block = blockIdx.x;
+    if (p.order) {
+        if (block == 0) {
+            const TileOrderParams o{p.tiles_x * p.tiles_y, nullptr, p.tile_total, p.order};
+            order_tiles<kWaves * kWave>(o, sh.order.count, sh.order.wave);
+            return;
+        }
+        --block;
+    }
     if ((int64_t)*p.num_dups > p.capacity) return;
     build_segment_table(p, t);
-    // Workgroups go round-robin to the eight XCDs, each with its own L2: XCD x takes the x-th
+    // Workgroups go round-robin to the eight XCDs, each with its own L2: the XCD of `block`
+    // (counted after the order's workgroup) is fixed by block % 8, and XCD x takes the x-th
     // contiguous block of segments, so the short runs that consecutive segments write into
     // one tile's list meet in one L2 and leave it as whole lines.
-    const uint32_t per_xcd = gridDim.x / kXcds;   // the grid is a multiple of kXcds
-    const uint32_t seg = ((blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
+    const uint32_t per_xcd = (gridDim.x - (p.order ? 1u : 0u)) / kXcds;   // a multiple of kXcds
+    const uint32_t seg = ((block % kXcds) * per_xcd + block / kXcds) * kWaves + threadIdx.x / kWave;
     if (seg >= t.first[kMaxSuper]) return;
     const SegmentRange r = segment_range(p, t, seg);
     const uint32_t lane = threadIdx.x % kWave;
@@ -398,8 +421,9 @@ void launch_super_list(const DuplicateParams &p, hipStream_t s) {
 
 template <int kWaves>
 void launch_place(const SuperBinParams &p, unsigned segs, hipStream_t s) {
-    // every segment below the capacity has a wave; the grid is a multiple of kXcds
-    const unsigned groups = ((segs + kWaves - 1) / kWaves + kXcds - 1) / kXcds * kXcds;
+    // every segment below the capacity has a wave; the placing workgroups are a multiple of
+    // kXcds, after the order's
+    const unsigned groups = ((segs + kWaves - 1) / kWaves + kXcds - 1) / kXcds * kXcds + (p.order ? 1u : 0u);
     if (p.keys_out)
         super_place_kernel<true, false, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
     else if (p.capacity <= ((int64_t)1 << 30))

@@ -246,6 +246,7 @@ struct SuperBinParams {
     uint32_t *values;              // out: Gaussian index per entry, by tile then depth
     const float *depth;            // key emission (optional): keys_out[e] = tile << 32 | bits(depth[g])
     uint64_t *keys_out;
+    uint32_t *order;               // optional: the heaviest-first tile launch order, from tile_total
 };
 // Segments the grids need for a super list of `entries` entries.
 int64_t super_segment_capacity(int64_t entries);
@@ -364,6 +365,66 @@ struct TileOrderParams {
     uint32_t *order;
 };
 bool launch_tile_order(const TileOrderParams &p, hipStream_t s);
+
+// The heaviest-first order by one workgroup of kThreads threads (a multiple of the wave, at most
+// 1024, dividing kOrderBuckets): a counting sort over the order buckets in s_count
+// [kOrderBuckets], with s_wave [kThreads / kWave] for the wave totals.  Order within a bucket
+// depends on the LDS atomics' timing; it changes only when a tile runs.
+__device__ __forceinline__ uint32_t order_weight(const TileOrderParams &p, int t) {
+    return p.weights ? p.weights[t] : p.ranges[2 * t + 1] - p.ranges[2 * t];
+}
+template <int kThreads>
+__device__ void order_tiles(const TileOrderParams &p, uint32_t *s_count, uint32_t *s_wave) {
+    constexpr int kPer = kOrderBuckets / kThreads;        // buckets per thread in the scan
+    constexpr int kKept = kThreads >= 1024 ? 8 : 4096 / kThreads;   // tiles whose bucket stays in registers
+    static_assert(kPer * kThreads == kOrderBuckets && kThreads % kWave == 0, "order workgroup");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int b = threadIdx.x; b < kOrderBuckets; b += kThreads) s_count[b] = 0;
+    __syncthreads();
+    uint32_t kept[kKept];
+#pragma unroll
+    for (int j = 0; j < kKept; ++j) {
+        const int t = threadIdx.x + j * kThreads;
+        kept[j] = t < p.tiles ? order_bucket(order_weight(p, t)) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kKept; ++j)
+        if (threadIdx.x + j * kThreads < p.tiles) atomicAdd(&s_count[kept[j]], 1u);
+    for (int t = threadIdx.x + kKept * kThreads; t < p.tiles; t += kThreads)
+        atomicAdd(&s_count[order_bucket(order_weight(p, t))], 1u);
+    __syncthreads();
+    // exclusive prefix over the buckets: kPer consecutive buckets per thread, a scan per wave,
+    // then the wave totals
+    uint32_t c[kPer], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        c[k] = s_count[threadIdx.x * kPer + k];
+        sum += c[k];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t up = (uint32_t)__shfl_up((int)incl, off);
+        if (lane >= off) incl += up;
+    }
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - sum;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        s_count[threadIdx.x * kPer + k] = base;
+        base += c[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kKept; ++j) {
+        const int t = threadIdx.x + j * kThreads;
+        if (t < p.tiles) p.order[atomicAdd(&s_count[kept[j]], 1u)] = (uint32_t)t;
+    }
+    for (int t = threadIdx.x + kKept * kThreads; t < p.tiles; t += kThreads)
+        p.order[atomicAdd(&s_count[order_bucket(order_weight(p, t))], 1u)] = (uint32_t)t;
+}
 // weights[t] = min(largest n_blend over tile t's pixels, tile t's list length)
 void launch_backward_tile_weight(const uint32_t *n_blend, const uint32_t *ranges, int32_t width, int32_t height,
                                  int32_t tiles_x, int32_t tiles_y, uint32_t *weights, hipStream_t s);

@@ -7,70 +7,19 @@
 // the finish.  The order is a counting sort by weight on a logarithmic scale, 2048
 // buckets of 1/64 octave (the leading bit of the weight and the six below it), so no
 // pass for the largest weight is needed; order within a bucket is arbitrary, which
-// only changes when a tile runs, never what it computes.
+// only changes when a tile runs, never what it computes.  The counting sort itself
+// (order_tiles) also runs as one workgroup of the super-tile place kernel.
 #include "gs_internal.h"
 
 namespace gsr {
 namespace {
 
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderPer = kOrderBuckets / kOrderThreads;      // buckets per thread in the scan
-constexpr int kOrderKept = 8;   // tiles per thread whose bucket stays in registers (8192 tiles)
-
-__device__ __forceinline__ uint32_t tile_weight(const TileOrderParams &p, int t) {
-    return p.weights ? p.weights[t] : p.ranges[2 * t + 1] - p.ranges[2 * t];
-}
 
 __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(TileOrderParams p) {
     __shared__ uint32_t s_count[kOrderBuckets];
     __shared__ uint32_t s_wave[kOrderThreads / kWave];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int b = threadIdx.x; b < kOrderBuckets; b += kOrderThreads) s_count[b] = 0;
-    __syncthreads();
-    // each thread keeps the buckets of its first kOrderKept tiles (and recomputes the rest)
-    uint32_t kept[kOrderKept];
-#pragma unroll
-    for (int j = 0; j < kOrderKept; ++j) {
-        const int t = threadIdx.x + j * kOrderThreads;
-        kept[j] = t < p.tiles ? order_bucket(tile_weight(p, t)) : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < kOrderKept; ++j)
-        if (threadIdx.x + j * kOrderThreads < p.tiles) atomicAdd(&s_count[kept[j]], 1u);
-    for (int t = threadIdx.x + kOrderKept * kOrderThreads; t < p.tiles; t += kOrderThreads)
-        atomicAdd(&s_count[order_bucket(tile_weight(p, t))], 1u);
-    __syncthreads();
-    // exclusive prefix over the buckets: kOrderPer consecutive buckets per thread, a scan per
-    // wave, then the wave totals
-    uint32_t c[kOrderPer], sum = 0;
-#pragma unroll
-    for (int k = 0; k < kOrderPer; ++k) {
-        c[k] = s_count[threadIdx.x * kOrderPer + k];
-        sum += c[k];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t up = (uint32_t)__shfl_up((int)incl, off);
-        if (lane >= off) incl += up;
-    }
-    if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
-    uint32_t base = incl - sum;
-    for (int w = 0; w < wave; ++w) base += s_wave[w];
-#pragma unroll
-    for (int k = 0; k < kOrderPer; ++k) {
-        s_count[threadIdx.x * kOrderPer + k] = base;
-        base += c[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kOrderKept; ++j) {
-        const int t = threadIdx.x + j * kOrderThreads;
-        if (t < p.tiles) p.order[atomicAdd(&s_count[kept[j]], 1u)] = (uint32_t)t;
-    }
-    for (int t = threadIdx.x + kOrderKept * kOrderThreads; t < p.tiles; t += kOrderThreads)
-        p.order[atomicAdd(&s_count[order_bucket(tile_weight(p, t))], 1u)] = (uint32_t)t;
+    order_tiles<kOrderThreads>(p, s_count, s_wave);
 }
 
 // Backward work of a tile: the entries up to the deepest one any of its pixels blended.
