@@ -739,7 +739,10 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
     GS_TRY(ensure(ctx, ctx->sval[1], ss * 4));
     GS_TRY(ensure(ctx, ctx->ssort_scratch, (size_t)sort_scratch_words(scap) * 4));
     GS_TRY(ensure(ctx, ctx->seg_tiles, (size_t)segs * kWave * 4));
-    GS_TRY(ensure(ctx, ctx->tile_total, (size_t)tiles * 4));
+    const int64_t row_parts = (int64_t)ctx->tiles_y * super_x;
+    const int64_t rows_at = (tiles + 1) & ~(int64_t)1;   // the row parts 8-byte aligned
+    // tile totals, row parts, their offsets (up to kRowStride words apart)
+    GS_TRY(ensure(ctx, ctx->tile_total, (size_t)(rows_at + row_parts + row_parts * kRowStride) * 4));
     ctx->sorted_values = nullptr;
     ctx->sorted_keys = nullptr;
     ctx->launch_order = nullptr;
@@ -777,6 +780,8 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
     b.seg_tiles = as<uint32_t>(ctx->seg_tiles);
     b.seg_capacity = segs;
     b.tile_total = as<uint32_t>(ctx->tile_total);
+    b.rows = b.tile_total + rows_at;
+    b.row_start = b.rows + row_parts;
     b.ranges = as<uint32_t>(ctx->ranges);
     b.num_dups = d_total + 1;
     b.capacity = cap;

@@ -14,11 +14,14 @@
 // super-tile form a 64-bit mask (bit 8 r + c: tile column c, row r of the super-tile), one
 // row span per tile row: the rectangle's columns, or the exact-footprint rule's span.
 //   super_count_kernel   pairs per (segment, tile), from span corners in an LDS difference grid
-//   super_column_kernel  per super-tile: each segment's offset within each tile, tile totals
-//   tile_ranges_kernel   exclusive scan of the tile totals: [start, end) per tile
-//   super_place_kernel   per tile of the super-tile, a ballot ranks the chunk's entries that
-//                        meet it, and they write at the tile's next position plus their rank;
-//                        its first workgroup builds the tiles' launch order (order_tiles)
+//   super_column_kernel  per super-tile: tile totals, the pairs of each of its tile rows (row
+//                        parts), and each segment's offset in each tile counted from the start
+//                        of the tile's row part (the tiles left of it, then earlier segments)
+//   row_offsets_kernel   exclusive scan of the row parts in tile order (one workgroup)
+//   super_place_kernel   per tile of the super-tile, a ballot ranks the segment's entries
+//                        that meet it, and they write at the row part's offset plus the
+//                        segment's offset plus their rank; the kernel's first workgroup
+//                        completes the tile ranges and builds the launch order (order_tiles)
 // The lists equal those of a stable sort of the pairs by tile, and each pair is written once,
 // 4 bytes (plus 8 when the 64-bit keys are asked for).
 #include "gs_internal.h"
@@ -26,7 +29,6 @@
 namespace gsr {
 namespace {
 
-constexpr int kRangeThreads = 1024;   // tile_ranges_kernel: one workgroup, each thread up to 64 tiles
 constexpr int kXcds = 8;              // XCDs of the chip (workgroups are dealt to them round-robin)
 constexpr int kColumnWaves = 16;      // super_column_kernel: waves per super-tile ...
 constexpr int kColumnBatch = 8;       // ... and segment counts each lane loads per round trip
@@ -228,6 +230,16 @@ __global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(Supe
         off += w < wave ? v : 0u;
         total += v;
     }
+    // the pairs of the tiles left of this one in its row of the super-tile (lanes 8 r .. 8 r + 7
+    // hold row r; tiles past the image's edge have none): offsets count from the row part's start
+    uint32_t incl = total;
+#pragma unroll
+    for (int d = 1; d < kSuperSide; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, d, kSuperSide);
+        if ((int)(lane % kSuperSide) >= d) incl += y;
+    }
+    const uint32_t left = incl - total;
+    off += left;
     for (uint32_t j = lo; j < hi; j += kColumnBatch) {
         uint32_t c[kColumnBatch];
 #pragma unroll
@@ -238,9 +250,43 @@ __global__ __launch_bounds__(kColumnWaves * kWave) void super_column_kernel(Supe
             off += c[q];
         }
     }
-    const int tx = (s % p.super_x) * kSuperSide + (int)lane % kSuperSide;
+    const int sx = s % p.super_x;
+    const int tx = sx * kSuperSide + (int)lane % kSuperSide;
     const int ty = (s / p.super_x) * kSuperSide + (int)lane / kSuperSide;
-    if (wave == 0 && tx < p.tiles_x && ty < p.tiles_y) p.tile_total[ty * p.tiles_x + tx] = total;
+    if (wave == 0) {
+        // the tile's total, its range from the row part's start ((0, 0) without pairs; the place
+        // kernel adds the row part's offset), and the row part (the last lane of each row)
+        if (tx < p.tiles_x && ty < p.tiles_y) {
+            p.tile_total[ty * p.tiles_x + tx] = total;
+            reinterpret_cast<uint2 *>(p.ranges)[ty * p.tiles_x + tx] = total ? make_uint2(left, incl) : make_uint2(0u, 0u);
+        }
+        if (lane % kSuperSide == kSuperSide - 1 && ty < p.tiles_y) p.rows[ty * p.super_x + sx] = incl;
+    }
+}
+
+// The row parts into the pairs before each of them in tile order (row by row, and left to
+// right within a row): one workgroup, an exclusive scan of at most 8 kMaxSuper values, two
+// consecutive ones per thread, written row_stride words apart.
+constexpr int kRowThreads = 1024;
+__global__ __launch_bounds__(kRowThreads) void row_offsets_kernel(SuperBinParams p) {
+    static_assert(kRowThreads * 2 >= kSuperSide * kMaxSuper, "two row parts per thread");
+    __shared__ uint32_t s_tot[kRowThreads / kWave];
+    const uint32_t lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const uint32_t parts = (uint32_t)(p.tiles_y * p.super_x), i0 = 2 * threadIdx.x;
+    const uint2 v = i0 + 1 < parts ? reinterpret_cast<const uint2 *>(p.rows)[threadIdx.x]
+                                   : make_uint2(i0 < parts ? p.rows[i0] : 0u, 0u);
+    uint32_t inc = v.x + v.y;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)inc, d);
+        if ((int)lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) s_tot[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - v.x - v.y;
+    for (uint32_t w = 0; w < wave; ++w) before += s_tot[w];
+    if (i0 < parts) p.row_start[i0 * (uint32_t)p.row_stride] = before;
+    if (i0 + 1 < parts) p.row_start[(i0 + 1) * (uint32_t)p.row_stride] = before + v.x;
 }
 
 // The super list in rank order: a thread per ranked Gaussian writes its entries, one per
@@ -295,41 +341,6 @@ __global__ __launch_bounds__(kBlock) void super_list_kernel(DuplicateParams p) {
     }
 }
 
-// [start, end) of every tile: an exclusive scan of the tile totals in tile order (one
-// workgroup, each thread a run of consecutive tiles, held in registers between the sum and the
-// writes); (0, 0) for a tile without pairs.
-__global__ __launch_bounds__(kRangeThreads) void tile_ranges_kernel(SuperBinParams p) {
-    constexpr int kMaxPer = kMaxSuperBinningTiles / kRangeThreads;
-    __shared__ uint32_t s_wave[kRangeThreads / kWave];
-    const int tiles = p.tiles_x * p.tiles_y;
-    const int per = (tiles + kRangeThreads - 1) / kRangeThreads;   // at most kMaxPer
-    const int lo = min(tiles, (int)threadIdx.x * per), hi = min(tiles, lo + per);
-    uint32_t c[kMaxPer];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-        c[q] = lo + q < hi ? p.tile_total[lo + q] : 0u;
-        sum += c[q];
-    }
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    uint32_t inc = sum;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)inc, d);
-        if (lane >= d) inc += y;
-    }
-    if (lane == kWave - 1) s_wave[wave] = inc;
-    __syncthreads();
-    uint32_t run = inc - sum;
-    for (int w = 0; w < wave; ++w) run += s_wave[w];
-#pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-        if (lo + q < hi)
-            reinterpret_cast<uint2 *>(p.ranges)[lo + q] = c[q] ? make_uint2(run, run + c[q]) : make_uint2(0u, 0u);
-        run += c[q];
-    }
-}
-
 // The segment's entries, one per lane, in list order.  For each tile k of the super-tile (a
 // uniform loop): the ballot of the lanes whose entry meets tile k gives each such lane its
 // rank among them, and they write their Gaussians at the tile's position for this segment
@@ -351,24 +362,33 @@ template <bool kKeys, bool kNarrow, int kWaves>
 __global__ __launch_bounds__(kWaves * kWave) void super_place_kernel(SuperBinParams p) {
     __shared__ PlaceShared<kWaves> sh;
     SegmentTable &t = sh.t;
-    // With a launch order asked for, workgroup 0 builds it from the tile totals (complete since
-    // the column kernel) while the others place the pairs; it starts first and hides under them.
-    uint32_t block = blockIdx.x;
-    if (p.order) {
-        if (block == 0) {
-            const TileOrderParams o{p.tiles_x * p.tiles_y, nullptr, p.tile_total, p.order};
-            order_tiles<kWaves * kWave>(o, sh.order.count, sh.order.wave);
-            return;
+    // Workgroup 0 completes the ranges (the row parts' offsets added to the column kernel's
+    // row-relative ones) and builds the launch order when asked for, from the tile totals, while
+    // the others place the pairs; it starts first and hides under them.
+    if (blockIdx.x == 0) {
+        const int tiles = p.tiles_x * p.tiles_y;
+        uint2 *ranges = reinterpret_cast<uint2 *>(p.ranges);
+        for (int i = threadIdx.x; i < tiles; i += kWaves * kWave) {
+            const uint2 r = ranges[i];
+            if (r.y != 0u) {   // a tile with pairs
+                const uint32_t add = p.row_start[((i / p.tiles_x) * p.super_x + (i % p.tiles_x) / kSuperSide) * p.row_stride];
+                ranges[i] = make_uint2(r.x + add, r.y + add);
+            }
         }
-        --block;
+        if (p.order) {
+            const TileOrderParams o{tiles, nullptr, p.tile_total, p.order};
+            order_tiles<kWaves * kWave>(o, sh.order.count, sh.order.wave);
+        }
+        return;
     }
+    const uint32_t block = blockIdx.x - 1;
     if ((int64_t)*p.num_dups > p.capacity) return;
     build_segment_table(p, t);
     // Workgroups go round-robin to the eight XCDs, each with its own L2: the XCD of `block`
-    // (counted after the order's workgroup) is fixed by block % 8, and XCD x takes the x-th
-    // contiguous block of segments, so the short runs that consecutive segments write into
-    // one tile's list meet in one L2 and leave it as whole lines.
-    const uint32_t per_xcd = (gridDim.x - (p.order ? 1u : 0u)) / kXcds;   // a multiple of kXcds
+    // (counted after workgroup 0) is fixed by block % 8, and XCD x takes the x-th contiguous
+    // block of segments, so the short runs that consecutive segments write into one tile's
+    // list meet in one L2 and leave it as whole lines.
+    const uint32_t per_xcd = (gridDim.x - 1) / kXcds;   // a multiple of kXcds
     const uint32_t seg = ((block % kXcds) * per_xcd + block / kXcds) * kWaves + threadIdx.x / kWave;
     if (seg >= t.first[kMaxSuper]) return;
     const SegmentRange r = segment_range(p, t, seg);
@@ -380,7 +400,11 @@ __global__ __launch_bounds__(kWaves * kWave) void super_place_kernel(SuperBinPar
     const uint32_t tx = (uint32_t)r.sx * kSuperSide + lane % kSuperSide;
     const uint32_t ty = (uint32_t)r.sy * kSuperSide + lane / kSuperSide;
     const bool have_tile = tx < (uint32_t)p.tiles_x && ty < (uint32_t)p.tiles_y;
-    const uint32_t at = have_tile ? p.ranges[2 * (ty * p.tiles_x + tx)] + p.seg_tiles[(size_t)seg * kWave + lane] : 0u;
+    // the tile's position for this segment: its row part's offset in tile order plus the
+    // segment's offset within the row part
+    const uint32_t at = have_tile ? p.row_start[(ty * (uint32_t)p.super_x + (uint32_t)r.sx) * (uint32_t)p.row_stride] +
+                                        p.seg_tiles[(size_t)seg * kWave + lane]
+                                  : 0u;
     const uint64_t mask = valid ? entry_mask(p, key, g, r.sx, r.sy) : 0ull;
     const uint32_t mlo = (uint32_t)mask, mhi = (uint32_t)(mask >> 32);
     const uint32_t dbits = kKeys ? __float_as_uint(p.depth[g]) : 0u;
@@ -422,8 +446,8 @@ void launch_super_list(const DuplicateParams &p, hipStream_t s) {
 template <int kWaves>
 void launch_place(const SuperBinParams &p, unsigned segs, hipStream_t s) {
     // every segment below the capacity has a wave; the placing workgroups are a multiple of
-    // kXcds, after the order's
-    const unsigned groups = ((segs + kWaves - 1) / kWaves + kXcds - 1) / kXcds * kXcds + (p.order ? 1u : 0u);
+    // kXcds, after workgroup 0
+    const unsigned groups = ((segs + kWaves - 1) / kWaves + kXcds - 1) / kXcds * kXcds + 1;
     if (p.keys_out)
         super_place_kernel<true, false, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
     else if (p.capacity <= ((int64_t)1 << 30))
@@ -432,11 +456,13 @@ void launch_place(const SuperBinParams &p, unsigned segs, hipStream_t s) {
         super_place_kernel<false, false, kWaves><<<groups, kWaves * kWave, 0, s>>>(p);
 }
 
-void launch_super_binning(const SuperBinParams &p, hipStream_t s) {
-    const unsigned segs = (unsigned)p.seg_capacity;
+void launch_super_binning(const SuperBinParams &params, hipStream_t s) {
+    const unsigned segs = (unsigned)params.seg_capacity;
+    SuperBinParams p = params;
+    p.row_stride = segs >= kPlaceWideSegs ? kRowStride : 1;
     super_count_kernel<<<(segs + kCountWaves - 1) / kCountWaves, kCountWaves * kWave, 0, s>>>(p);
     super_column_kernel<<<(unsigned)(p.super_x * p.super_y), kColumnWaves * kWave, 0, s>>>(p);
-    tile_ranges_kernel<<<1, kRangeThreads, 0, s>>>(p);
+    row_offsets_kernel<<<1, kRowThreads, 0, s>>>(p);
     if (segs >= kPlaceWideSegs)
         launch_place<kPlaceWideWaves>(p, segs, s);
     else

@@ -207,6 +207,11 @@ constexpr int kMaxSuper = 1 << kRadixBits;         // super-tiles one 8-bit pass
 constexpr int kMaxSuperBinningTiles = 1 << 16;     // tile counts fit the packed count below
 constexpr int64_t kAutoSuperMin = 1 << 16;         // GS_BINNING_AUTO: super-tile binning from this many Gaussians
 constexpr int kSegment = 64;                       // super-list entries per segment (one wave, one per lane)
+// Words between consecutive row-part offsets in the wide place shape: every place wave reads
+// the offsets of its super-tile's 8 tile rows, and spread over 8 cache lines those reads do
+// not pile onto a few L2 channels (packed, the 5 M-Gaussian frame's place kernel took 7 %
+// longer); below that shape they are packed (the 1 M frame's tile lists 2 us faster).
+constexpr int kRowStride = 16;
 constexpr int kPackShift = 17;                     // packed count: tile count | super count << 17
 constexpr int kPairShift = 36;                     // scan of packed counts: tiles | super-tiles << 36
 
@@ -240,6 +245,9 @@ struct SuperBinParams {
     uint32_t *seg_tiles;           // [segment capacity][64] pairs per (segment, tile), then offsets
     int64_t seg_capacity;          // segments the grids cover
     uint32_t *tile_total;          // [tiles] pairs per tile
+    uint32_t *rows;                // [tiles_y][super_x] pairs per (tile row, super-tile column): row parts
+    uint32_t *row_start;           // [tiles_y][super_x] x row_stride: pairs before each row part in tile order
+    int32_t row_stride;            // words between consecutive row_start entries (set by the launch)
     uint32_t *ranges;              // [tiles][2]
     const unsigned long long *num_dups;   // device: the frame's pair count
     int64_t capacity;              // entries `values` holds; with more pairs nothing is written
