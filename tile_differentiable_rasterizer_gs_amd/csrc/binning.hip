@@ -13,7 +13,7 @@
 // wave builds in LDS.  An entry's tiles inside its
 // super-tile form a 64-bit mask (bit 8 r + c: tile column c, row r of the super-tile), one
 // row span per tile row: the rectangle's columns, or the exact-footprint rule's span.
-//   super_count_kernel   pairs per (segment, tile), from span corners in an LDS difference grid
+//   super_count_kernel   pairs per (segment, tile): the wave's 64 entry masks transposed, popcounts
 //   super_column_kernel  per super-tile: tile totals, the pairs of each of its tile rows (row
 //                        parts), and each segment's offset in each tile counted from the start
 //                        of the tile's row part (the tiles left of it, then earlier segments)
@@ -154,50 +154,53 @@ __device__ inline uint64_t entry_mask(const SuperBinParams &p, uint32_t key, uin
 
 static_assert(kSegment == kWave, "one entry per lane");
 
-// Pairs per (segment, tile of its super-tile): each entry adds +1 / -1 at the corners of its
-// part (the rectangle, or each row span of the exact-footprint rule) in a 9 x 9 difference
-// grid, whose 2D prefix is then the count of each tile.  The square rule reads the keys only.
+// Lane e's 64-bit word is row e of a 64 x 64 bit matrix; returns column `lane`: bit e set when
+// row e has bit `lane`.  Six exchanges between lanes l and l ^ j (j = 32, 16, .., 1), each
+// swapping bit j of the row and column indices: the lane whose bit j is clear keeps the bits
+// at positions with bit j clear and takes its partner's such bits moved up by j; the other
+// keeps the positions with bit j set and takes its partner's such bits moved down by j.
+__device__ inline uint64_t transpose_bits(uint64_t row, uint32_t lane) {
+    uint32_t lo = (uint32_t)row, hi = (uint32_t)(row >> 32);
+    {   // j = 32: whole halves
+        const bool up = (lane & 32u) != 0u;
+        const uint32_t got = (uint32_t)__shfl_xor((int)(up ? lo : hi), 32);
+        if (up)
+            lo = got;
+        else
+            hi = got;
+    }
+    constexpr uint32_t kKeep[5] = {0x0000ffffu, 0x00ff00ffu, 0x0f0f0f0fu, 0x33333333u, 0x55555555u};
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const int j = 16 >> k;
+        const uint32_t m = kKeep[k];
+        const bool up = (lane & (uint32_t)j) != 0u;
+        // what the partner takes: the set lane's kept bits, the clear lane's upper bits moved down
+        const uint32_t slo = (up ? lo : lo >> j) & m, shi = (up ? hi : hi >> j) & m;
+        const uint32_t glo = (uint32_t)__shfl_xor((int)slo, j), ghi = (uint32_t)__shfl_xor((int)shi, j);
+        lo = up ? (glo | (lo & ~m)) : ((lo & m) | (glo << j));
+        hi = up ? (ghi | (hi & ~m)) : ((hi & m) | (ghi << j));
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Pairs per (segment, tile of its super-tile): each lane builds its entry's tile mask (the
+// rectangle's part in the super-tile, or each row span of the exact-footprint rule), the
+// wave transposes the 64 masks, and lane k's popcount is the number of entries meeting tile k.
+// The square rule reads the keys only.
 __global__ __launch_bounds__(kCountWaves * kWave) void super_count_kernel(SuperBinParams p) {
     __shared__ SegmentTable t;
-    __shared__ uint32_t s_all[kCountWaves][kSuperSide + 1][kSuperSide + 1];
     build_segment_table(p, t);
     const uint32_t lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const uint32_t seg = blockIdx.x * kCountWaves + wave;
-    const bool live = seg < t.first[kMaxSuper];   // the workgroup's barriers need every wave
-    uint32_t(&s_diff)[kSuperSide + 1][kSuperSide + 1] = s_all[wave];
-    const SegmentRange r = segment_range(p, t, live ? seg : 0u);
-    for (uint32_t i = lane; i < (kSuperSide + 1) * (kSuperSide + 1); i += kWave) (&s_diff[0][0])[i] = 0u;
+    if (seg >= t.first[kMaxSuper]) return;   // the whole wave; no barrier follows
+    const SegmentRange r = segment_range(p, t, seg);
     const uint32_t e = r.a + lane;
-    const uint32_t key = live ? p.keys[e < r.b ? e : r.a] : 0u;
-    __syncthreads();
-    auto corners = [&](uint32_t r0, uint32_t r1, uint32_t a, uint32_t b) {   // rows [r0, r1), columns [a, b)
-        atomicAdd(&s_diff[r0][a], 1u);
-        atomicAdd(&s_diff[r0][b], 0xffffffffu);
-        atomicAdd(&s_diff[r1][a], 0xffffffffu);
-        atomicAdd(&s_diff[r1][b], 1u);
-    };
-    if (live && e < r.b) {
-        const LocalRect lr = local_rect(key);
-        if (p.ellipse) {
-            const EllipseRec E = p.ellipse[p.gauss[e]];
-            const uint32_t cx = (uint32_t)r.sx * kSuperSide, cy = (uint32_t)r.sy * kSuperSide;
-            for (uint32_t row = lr.r0; row < lr.r1; ++row) {
-                uint32_t sa, sb;
-                local_span(E, lr, cx, cy, row, sa, sb);
-                if (sa < sb) corners(row, row + 1, sa, sb);
-            }
-        } else if (lr.a < lr.b && lr.r0 < lr.r1) {
-            corners(lr.r0, lr.r1, lr.a, lr.b);
-        }
-    }
-    __syncthreads();
-    if (lane <= kSuperSide)
-        for (int c = 1; c <= kSuperSide; ++c) s_diff[lane][c] += s_diff[lane][c - 1];
-    __syncthreads();
-    if (lane <= kSuperSide)
-        for (int row = 1; row <= kSuperSide; ++row) s_diff[row][lane] += s_diff[row - 1][lane];
-    __syncthreads();
-    if (live) p.seg_tiles[(size_t)seg * kWave + lane] = s_diff[lane / kSuperSide][lane % kSuperSide];
+    const bool valid = e < r.b;
+    const uint32_t key = p.keys[valid ? e : r.a];   // a lane past the segment meets no tile
+    const uint32_t g = p.ellipse ? p.gauss[valid ? e : r.a] : 0u;
+    const uint64_t mask = valid ? entry_mask(p, key, g, r.sx, r.sy) : 0ull;
+    p.seg_tiles[(size_t)seg * kWave + lane] = (uint32_t)__popcll(transpose_bits(mask, lane));
 }
 
 // One workgroup per super-tile; lane k of each wave owns tile k.  The super-tile's segments are
