@@ -418,11 +418,11 @@ __global__ __launch_bounds__(kWaves * kWave) void super_place_kernel(SuperBinPar
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int k = 0; k < kWave; ++k) {
-        const uint32_t meets = __builtin_amdgcn_ubfe(k < 32 ? mlo : mhi, (uint32_t)(k & 31), 1u);
-        const uint64_t bk = __ballot(meets != 0u);
-        if (bk == 0) continue;
-        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)at, k);
-        if (meets != 0u) {
+        if (__builtin_amdgcn_ubfe(k < 32 ? mlo : mhi, (uint32_t)(k & 31), 1u) != 0u) {
+            // the lanes here are the entries meeting tile k (one bit test serves as the branch
+            // and, through the active lanes, as the ballot)
+            const uint64_t bk = __ballot(1);
+            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)at, k);
             const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bk, 0u));
             if (kNarrow) {
                 *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(p.values) + ((rank << 2) + (base << 2))) = g;
