@@ -17,13 +17,13 @@
 //            (bits(depth) << 32 | index) into the bucket's range, a Gaussian without
 //            pairs straight into the output tail (their relative order is immaterial:
 //            they have no pairs, and their gathered count is 0)
-//   rank     one workgroup per bucket of at most kRankCap entries: an entry's place is the
-//            number of smaller entries, counted against the whole bucket in LDS (every lane
-//            reads the same word: a broadcast); it writes rank -> Gaussian and the
-//            gathered per-Gaussian count.  Larger buckets go to a list for
-//   sub-bin  per listed bucket (up to kBucketCap entries): a counting sort in LDS into
-//            kSubBins finer depth bins (the fractional part of the same bucket coordinate,
-//            monotone too), then each entry ranked within its sub-bin
+//   sort     one workgroup per bucket of at most kRankCap entries: a counting sort in LDS
+//            into one sub-bin per thread (the fractional part of the same bucket
+//            coordinate, monotone too), then each entry ranked among the few entries of its
+//            sub-bin; it writes rank -> Gaussian and the gathered per-Gaussian count.
+//            Larger buckets go to a list for
+//   larger   per listed bucket (up to kBucketCap entries): the same with a 1024-thread
+//            workgroup and 1024 sub-bins
 // Entries compare as 64-bit integers, i.e. by depth then index: the order the stable
 // radix sort of the depth bits gives.  A bucket of more than kBucketCap entries (depths
 // crowded into a sliver of the range) is written unsorted and raises a flag; the host
@@ -38,10 +38,10 @@ namespace {
 constexpr int kGroupThreads = 1024;  // count and scatter workgroups
 constexpr int kGroupBatch = 4;       // 16-byte key loads per thread in flight
 constexpr int kXcds = 8;             // workgroups go round-robin to the eight XCDs
-constexpr int kRankThreads = kBlock; // rank workgroups
-constexpr int kRankCap = 2 * kRankThreads;   // largest bucket the rank kernel sorts
-constexpr int kSubBins = kBlock;     // sub-bins of a larger bucket
-constexpr int kSubbinGroups = 4096;  // workgroups that share the list of larger buckets
+constexpr int kRankThreads = kBlock; // workgroups of the per-bucket kernel
+constexpr int kRankCap = 2 * kRankThreads;   // largest bucket the per-bucket kernel sorts
+constexpr int kBigThreads = 1024;    // workgroups of the larger-bucket kernel
+constexpr int kSubbinGroups = 512;   // workgroups that share the list of larger buckets
 
 struct Bounds {
     float zlo, scale;   // scale 0: every Gaussian with pairs in bucket 0
@@ -242,50 +242,70 @@ __device__ inline void emit(const DepthBucketParams &p, uint32_t at, uint64_t en
     p.gathered[at] = count;
 }
 
-// Rank sort of one bucket of `size` <= kE * kRankThreads entries: thread t holds entries t,
-// t + kRankThreads, ..; each counts the bucket's smaller entries, two per 16-byte broadcast read.
-template <int kE>
-__device__ inline void rank_bucket(const DepthBucketParams &p, uint64_t *s_ent, uint32_t start, uint32_t size) {
+// Sub-bin of an entry of bucket b: the fractional part of the bucket coordinate
+// t = (z - zmin) * scale (the same operations as bucket_of, so the same t) in kSub steps,
+// clamped.  Monotone in the depth, like the bucket.
+template <int kSub>
+__device__ inline uint32_t sub_bin(uint64_t entry, uint32_t b, float zlo, float scale) {
+#pragma clang fp contract(off)
+    const float t = (__uint_as_float((uint32_t)(entry >> 32)) - zlo) * scale;
+    const float f = (t - (float)b) * (float)kSub;
+    if (!(f > 0.0f)) return 0u;
+    return f < (float)kSub ? (uint32_t)f : (uint32_t)kSub - 1u;
+}
+
+// Sorts bucket b (`size` <= kE * kThreads entries from `start`) with the whole workgroup: a
+// counting sort into kThreads sub-bins in LDS, then each entry ranked among the entries of
+// its own sub-bin (about size / kThreads of them).  Barriers inside; the caller waits at a
+// barrier before it reuses the LDS.
+template <int kThreads, int kE>
+__device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint32_t start, uint32_t size,
+                                   float zlo, float scale, uint64_t *s_ent, uint32_t *s_cnt, uint32_t *s_base,
+                                   uint32_t *s_tmp) {
     uint64_t v[kE];
-    uint32_t rank[kE], cnt[kE];
+    uint32_t sub[kE], off[kE], cnt[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        const uint32_t i = threadIdx.x + e * kRankThreads;
-        v[e] = i < size ? p.entries[start + i] : ~0ull;
-        rank[e] = 0;
+        const uint32_t i = threadIdx.x + e * kThreads;
+        v[e] = i < size ? p.entries[start + i] : 0ull;
     }
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        const uint32_t i = threadIdx.x + e * kRankThreads;
-        cnt[e] = count_of(p, i < size ? v[e] : 0ull);   // a padding lane reads Gaussian 0's, unused
-        if (i < size) s_ent[i] = v[e];
+        cnt[e] = count_of(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's count, unused
+        sub[e] = sub_bin<kThreads>(v[e], b, zlo, scale);
     }
-    // pad to a multiple of 8 entries with ~0 (never smaller than an entry)
-    if (threadIdx.x < 8 && size + threadIdx.x < (uint32_t)kRankCap + 8) s_ent[size + threadIdx.x] = ~0ull;
+    s_cnt[threadIdx.x] = 0u;   // one sub-bin per thread
     __syncthreads();
-    const ulonglong2 *pairs = reinterpret_cast<const ulonglong2 *>(s_ent);
-    for (uint32_t q = 0; q < (size + 7) / 8; ++q) {   // 4 independent 16-byte broadcast reads per step
-        ulonglong2 w[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = pairs[4 * q + u];
+    for (int e = 0; e < kE; ++e)
+        if (threadIdx.x + e * kThreads < size) off[e] = atomicAdd(&s_cnt[sub[e]], 1u);
+    __syncthreads();
+    uint32_t total;
+    const uint32_t c = s_cnt[threadIdx.x];
+    s_base[threadIdx.x] = block_scan<kThreads>(c, s_tmp, &total);   // barriers inside
+    __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < kE; ++e) rank[e] += (uint32_t)(w[u].x < v[e]) + (uint32_t)(w[u].y < v[e]);
-    }
+    for (int e = 0; e < kE; ++e)
+        if (threadIdx.x + e * kThreads < size) s_ent[s_base[sub[e]] + off[e]] = v[e];
+    __syncthreads();
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        const uint32_t i = threadIdx.x + e * kRankThreads;
-        if (i < size) emit(p, start + rank[e], v[e], cnt[e]);
+        if (threadIdx.x + e * kThreads < size) {
+            const uint32_t lo = s_base[sub[e]], hi = lo + s_cnt[sub[e]];
+            uint32_t r = 0;
+            for (uint32_t q = lo; q < hi; ++q) r += (uint32_t)(s_ent[q] < v[e]);
+            emit(p, start + lo + r, v[e], cnt[e]);
+        }
     }
 }
 
 // One workgroup per bucket of Gaussians with pairs: buckets of at most kRankCap entries are
-// ranked here, larger ones listed for the sub-bin kernel, and one of more than kBucketCap
-// entries is written unsorted with the flag raised.  Workgroup 0 also empties the bound
-// slots for the next preprocess (no later kernel reads them).
+// sorted here, larger ones listed for the larger-bucket kernel, and one of more than
+// kBucketCap entries is written unsorted with the flag raised.  Workgroup 0 also empties the
+// bound slots for the next preprocess (no later kernel reads them).
 __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketParams p) {
-    __shared__ __align__(16) uint64_t s_ent[kRankCap + 8];
+    __shared__ uint64_t s_ent[kRankCap];
+    __shared__ uint32_t s_cnt[kRankThreads], s_base[kRankThreads], s_tmp[kRankThreads / kWave];
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < kDepthSlots; i += kRankThreads) {
             p.range[i] = 0xffffffffu;
@@ -307,71 +327,24 @@ __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketPa
         if (threadIdx.x == 0) p.big_list[atomicAdd(p.big_count, 1u)] = blockIdx.x;
         return;
     }
+    const float zlo = p.bounds[0], scale = p.bounds[1];
     if (size <= (uint32_t)kRankThreads)
-        rank_bucket<1>(p, s_ent, start, size);
+        subbin_sort<kRankThreads, 1>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
     else
-        rank_bucket<2>(p, s_ent, start, size);
+        subbin_sort<kRankThreads, 2>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
 }
 
-// Sub-bin of an entry of bucket b: the fractional part of the bucket coordinate
-// t = (z - zmin) * scale (the same operations as bucket_of, so the same t) in kSubBins
-// steps, clamped.  Monotone in the depth, like the bucket.
-__device__ inline uint32_t sub_bin(uint64_t entry, uint32_t b, float zlo, float scale) {
-#pragma clang fp contract(off)
-    const float t = (__uint_as_float((uint32_t)(entry >> 32)) - zlo) * scale;
-    const float f = (t - (float)b) * (float)kSubBins;
-    if (!(f > 0.0f)) return 0u;
-    return f < (float)kSubBins ? (uint32_t)f : (uint32_t)kSubBins - 1u;
-}
-
-// The listed buckets (kRankCap < size <= kBucketCap), shared round-robin by the workgroups:
-// a counting sort into kSubBins sub-bins in LDS, then each entry ranked among the entries of
-// its own sub-bin.
-__global__ __launch_bounds__(kBlock) void bucket_subbin_kernel(DepthBucketParams p) {
-    constexpr int kE = kBucketCap / kBlock;
+// The listed buckets (kRankCap < size <= kBucketCap), shared round-robin by the workgroups.
+__global__ __launch_bounds__(kBigThreads) void bucket_subbin_kernel(DepthBucketParams p) {
     __shared__ uint64_t s_ent[kBucketCap];
-    __shared__ uint32_t s_cnt[kSubBins], s_base[kSubBins], s_tmp[kBlock / kWave];
+    __shared__ uint32_t s_cnt[kBigThreads], s_base[kBigThreads], s_tmp[kBigThreads / kWave];
     const uint32_t count = *p.big_count;
     const float zlo = p.bounds[0], scale = p.bounds[1];
     for (uint32_t li = blockIdx.x; li < count; li += gridDim.x) {
         const uint32_t b = p.big_list[li];
         const uint32_t start = p.starts[b];
-        const uint32_t size = p.starts[b + 1] - start;
-        uint64_t v[kE];
-        uint32_t sub[kE], off[kE], cnt[kE];
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            const uint32_t i = threadIdx.x + e * kBlock;
-            v[e] = i < size ? p.entries[start + i] : 0ull;
-        }
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            cnt[e] = count_of(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's count, unused
-            sub[e] = sub_bin(v[e], b, zlo, scale);
-        }
-        for (int i = threadIdx.x; i < kSubBins; i += kBlock) s_cnt[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < kE; ++e)
-            if (threadIdx.x + e * kBlock < size) off[e] = atomicAdd(&s_cnt[sub[e]], 1u);
-        __syncthreads();
-        uint32_t total;
-        const uint32_t c = s_cnt[threadIdx.x];   // kSubBins == kBlock
-        s_base[threadIdx.x] = block_scan<kBlock>(c, s_tmp, &total);   // barriers inside
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < kE; ++e)
-            if (threadIdx.x + e * kBlock < size) s_ent[s_base[sub[e]] + off[e]] = v[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            if (threadIdx.x + e * kBlock < size) {
-                const uint32_t lo = s_base[sub[e]], hi = lo + s_cnt[sub[e]];
-                uint32_t r = 0;
-                for (uint32_t q = lo; q < hi; ++q) r += (uint32_t)(s_ent[q] < v[e]);
-                emit(p, start + lo + r, v[e], cnt[e]);
-            }
-        }
+        subbin_sort<kBigThreads, kBucketCap / kBigThreads>(p, b, start, p.starts[b + 1] - start, zlo, scale, s_ent,
+                                                           s_cnt, s_base, s_tmp);
         __syncthreads();   // the next bucket reuses the LDS
     }
 }
@@ -385,8 +358,8 @@ __global__ void fill_range_kernel(uint32_t *range) {
 
 }  // namespace
 
-static_assert(kBucketCap % kBlock == 0 && kSubBins == kBlock, "sub-bin kernel shapes");
-static_assert(kRankCap == 2 * kRankThreads && kRankCap % 8 == 0, "rank kernel shapes");
+static_assert(kBucketCap % kBigThreads == 0 && kBucketCap >= kRankCap, "larger-bucket kernel shapes");
+static_assert(kRankCap == 2 * kRankThreads, "per-bucket kernel shapes");
 
 int depth_bucket_bits(int64_t n) {
     int bits = kMinBucketBits;
@@ -435,7 +408,7 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
     bucket_scatter_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     bucket_rank_kernel<<<buckets, kRankThreads, 0, s>>>(p);
-    bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBlock, 0, s>>>(p);
+    bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBigThreads, 0, s>>>(p);
 }
 
 }  // namespace gsr
