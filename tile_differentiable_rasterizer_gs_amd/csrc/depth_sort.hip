@@ -39,7 +39,7 @@ constexpr int kGroupThreads = 1024;  // count and scatter workgroups
 constexpr int kGroupBatch = 4;       // 16-byte key loads per thread in flight
 constexpr int kXcds = 8;             // workgroups go round-robin to the eight XCDs
 constexpr int kRankThreads = kBlock; // workgroups of the per-bucket kernel
-constexpr int kRankCap = 4 * kRankThreads;   // largest bucket the per-bucket kernel sorts
+constexpr int kRankCap = 8 * kRankThreads;   // largest bucket the per-bucket kernel sorts
 constexpr int kBigThreads = 1024;    // workgroups of the larger-bucket kernel
 constexpr int kSubbinGroups = 512;   // workgroups that share the list of larger buckets
 
@@ -332,8 +332,10 @@ __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketPa
         subbin_sort<kRankThreads, 1>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
     else if (size <= 2u * kRankThreads)
         subbin_sort<kRankThreads, 2>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
-    else
+    else if (size <= 4u * kRankThreads)
         subbin_sort<kRankThreads, 4>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
+    else
+        subbin_sort<kRankThreads, 8>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
 }
 
 // The listed buckets (kRankCap < size <= kBucketCap), shared round-robin by the workgroups.
@@ -361,7 +363,7 @@ __global__ void fill_range_kernel(uint32_t *range) {
 }  // namespace
 
 static_assert(kBucketCap % kBigThreads == 0 && kBucketCap >= kRankCap, "larger-bucket kernel shapes");
-static_assert(kRankCap == 4 * kRankThreads, "per-bucket kernel shapes");
+static_assert(kRankCap == 8 * kRankThreads, "per-bucket kernel shapes");
 
 int depth_bucket_bits(int64_t n) {
     int bits = kMinBucketBits;
