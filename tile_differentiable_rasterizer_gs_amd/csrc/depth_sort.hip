@@ -41,7 +41,7 @@ constexpr int kXcds = 8;             // workgroups go round-robin to the eight X
 constexpr int kRankThreads = kBlock; // workgroups of the per-bucket kernel
 constexpr int kRankCap = 8 * kRankThreads;   // largest bucket the per-bucket kernel sorts
 constexpr int kBigThreads = 1024;    // workgroups of the larger-bucket kernel
-constexpr int kSubbinGroups = 512;   // workgroups that share the list of larger buckets
+constexpr int kSubbinGroups = 128;   // workgroups that share the list of larger buckets (usually none)
 
 struct Bounds {
     float zlo, scale;   // scale 0: every Gaussian with pairs in bucket 0
