@@ -30,9 +30,9 @@ def _run(arrays, deg, cam, order, binning=binding.GS_BINNING_AUTO, bg=(0.0, 0.0,
 
 
 def _buckets(n):
-    # the library's choice: 256 .. 8192 buckets, about 256 Gaussians each
+    # the library's choice: 256 .. 8192 buckets, about 512 Gaussians each
     b = 8
-    while b < 13 and (1 << b) * 256 < n:
+    while b < 13 and (1 << b) * 512 < n:
         b += 1
     return 1 << b
 
@@ -59,12 +59,13 @@ def _check(arrays, deg, cam, what, fallback=False, binning=binding.GS_BINNING_AU
     return bk
 
 
-# (width, height, Gaussians, SH degree, log-scale range): 256 to 512 buckets, ragged groups
+# (width, height, Gaussians, SH degree, log-scale range): 256 or 1024 buckets, ragged groups
 CASES = [
     (211, 139, 4000, 2, (-4.0, -1.8)),
     (320, 240, 25000, 0, (-4.5, -2.5)),
     (640, 360, 60001, 1, (-4.5, -3.0)),
     (96, 64, 3, 0, (-2.0, -1.0)),
+    (640, 360, 300007, 0, (-5.0, -3.5)),
 ]
 
 

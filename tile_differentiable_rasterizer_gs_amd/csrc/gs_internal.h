@@ -163,7 +163,7 @@ int64_t sort_totals_offset(int64_t n);
 // ---------------------------------------------------------------------------
 constexpr int kBucketCap = 4096;          // largest bucket one workgroup sorts in LDS
 constexpr int kMinBucketBits = 8, kMaxBucketBits = 13;
-constexpr int64_t kBucketTarget = 256;    // Gaussians per bucket the bucket count aims at
+constexpr int64_t kBucketTarget = 512;    // Gaussians per bucket the bucket count aims at
 constexpr int64_t kGroupKeys = 4096;      // Gaussians per counting group (at least)
 constexpr int64_t kMaxCountWords = 1 << 21;   // bound on the (bucket, group) count table
 
