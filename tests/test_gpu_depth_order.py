@@ -127,3 +127,24 @@ def test_bucket_order_sequence_on_one_context():
         g = gpu_run(arrays, 0, cam, rast=r)
         check_binning(g, oracle.bin_pairs(oracle.preprocess(arrays, 0, cam)))
     r.close()
+
+
+def test_larger_bucket_kernel_follows_the_last_frame():
+    # the larger-bucket kernel runs only while the last bucketed frame met a bucket of more than
+    # 2048 Gaussians; a frame that meets one without it is redone by the radix sort (reported as
+    # 0 buckets) and exact, and the frame after it runs the kernel again
+    r = binding.Rasterizer()
+    small = scenes.random_scene(350, 20000, 0, 301, 197, log_scale_range=(-4.0, -2.0))
+    crowded = plane_scene(351, 9000, (3.0, 4.0, 5.0))   # ~3000 Gaussians per occupied bucket
+    seq = [(small.arrays(), small.cameras[0], _buckets(20000)),   # first frame: the kernel runs
+           (small.arrays(), small.cameras[0], _buckets(20000)),   # left out: no larger bucket
+           (crowded[0], crowded[1], 0),                            # met without it: redone
+           (crowded[0], crowded[1], _buckets(9000)),               # run again
+           (small.arrays(), small.cameras[0], _buckets(20000)),
+           (crowded[0], crowded[1], 0)]
+    for i, (arrays, cam, want) in enumerate(seq):
+        g = gpu_run(arrays, 0, cam, rast=r)
+        assert g["depth_buckets"] == want, (i, g["depth_buckets"], want)
+        check_binning(g, oracle.bin_pairs(oracle.preprocess(arrays, 0, cam)))
+    r.close()
+    note("larger-bucket kernel launched after frames that met such buckets; other frames redone exactly")

@@ -141,6 +141,10 @@ struct gs_context {
     const uint64_t *sorted_keys = nullptr;
     int64_t pair_capacity = 0;                 // entries the pair buffers hold
     int64_t super_capacity = 0;                // entries the super-list buffers hold
+    // bucketed depth order: launch the larger-bucket kernel (set while the last bucketed frame
+    // met a bucket too large for the per-bucket kernel; a frame that meets one without it
+    // redoes its order with the radix sort)
+    bool run_larger = true;
 
     std::vector<TimedSpan> spans;
     size_t spans_used = 0;
@@ -682,6 +686,7 @@ static gs_status order_by_depth(gs_context *ctx, int64_t n, const uint32_t *gath
         b.gather_src = gather;
         b.order = as<uint32_t>(ctx->dval[1]);
         b.gathered = as<uint32_t>(ctx->dcount);
+        b.run_larger = ctx->run_larger ? 1 : 0;
         launch_depth_bucket_sort(b, stream);
         GS_TRY(check_launch(ctx, "depth buckets"));
         *order = b.order;
@@ -873,9 +878,14 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         } else {
             M = (int64_t)published;
         }
-        if (bucket_flag && __atomic_load_n(ctx->host_total + 2, __ATOMIC_ACQUIRE) != 0) {
-            // a bucket too large to sort in LDS: order this frame by the radix sort, recount the
-            // offsets in that order (the totals do not change) and list the pairs afresh
+        // the flag: low word, redo the order; high word, a larger bucket was met (the next
+        // frame launches the larger-bucket kernel only if this one met such a bucket)
+        const unsigned long long bflag = bucket_flag ? __atomic_load_n(ctx->host_total + 2, __ATOMIC_ACQUIRE) : 0ull;
+        if (bucket_flag) ctx->run_larger = (bflag >> 32) != 0;
+        if ((bflag & 0xffffffffull) != 0) {
+            // a bucket too large to sort in LDS (or one for the larger-bucket kernel, which this
+            // frame left out): order this frame by the radix sort, recount the offsets in that
+            // order (the totals do not change) and list the pairs afresh
             GS_HIP(ctx, hipStreamSynchronize(stream));
             GS_TRY(order_by_depth(ctx, n, gather, false, &order, nullptr, stream));
             GS_TRY(enqueue_scan(ctx, counts, n, super_bin, nullptr, nullptr, stream));

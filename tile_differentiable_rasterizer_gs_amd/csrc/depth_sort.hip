@@ -23,7 +23,10 @@
 //            sub-bin; it writes rank -> Gaussian and the gathered per-Gaussian count.
 //            Larger buckets go to a list for
 //   larger   per listed bucket (up to kBucketCap entries): the same with a 1024-thread
-//            workgroup and 1024 sub-bins
+//            workgroup and 1024 sub-bins.  This kernel is launched only while the frames
+//            before met such buckets (flag word 1); a frame that meets one without it is
+//            redone like a frame with a bucket too large (below), and the next frame
+//            launches it again
 // Entries compare as 64-bit integers, i.e. by depth then index: the order the stable
 // radix sort of the depth bits gives.  A bucket of more than kBucketCap entries (depths
 // crowded into a sliver of the range) is written unsorted and raises a flag; the host
@@ -232,6 +235,11 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
     });
 }
 
+// The frame's flag as two words (the host reads them as one 64-bit value): [0] the order must
+// be redone by the radix sort, [1] a bucket too large for the per-bucket kernel was met.  Every
+// writer stores 1, so concurrent plain stores agree.
+__device__ inline uint32_t *flag_words(const DepthBucketParams &p) { return reinterpret_cast<uint32_t *>(p.flag); }
+
 // Writes a sorted entry: rank -> Gaussian and the Gaussian's count (read beforehand with
 // count_of, so that a thread's reads are in flight together and overlap the sorting).
 __device__ inline uint32_t count_of(const DepthBucketParams &p, uint64_t entry) {
@@ -315,16 +323,21 @@ __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketPa
     const uint32_t start = p.starts[blockIdx.x];
     const uint32_t size = p.starts[blockIdx.x + 1] - start;
     if (size == 0) return;
-    if (size > (uint32_t)kBucketCap) {   // not sorted here: the host redoes the frame's order
+    if (size > (uint32_t)kRankCap) {
+        if (threadIdx.x == 0) flag_words(p)[1] = 1u;   // a larger bucket was met
+        if (size <= (uint32_t)kBucketCap && p.run_larger) {
+            if (threadIdx.x == 0) p.big_list[atomicAdd(p.big_count, 1u)] = blockIdx.x;
+            return;
+        }
+        // not sorted this frame (too large, or its kernel left out): the host redoes the
+        // frame's order.  The entries are still written, unsorted, so that every rank names a
+        // Gaussian with that Gaussian's own count for the kernels enqueued before the host
+        // reads the flag (with stale ranks their listing walks would leave the rectangles).
         for (uint32_t i = threadIdx.x; i < size; i += kRankThreads) {
             const uint64_t v = p.entries[start + i];
             emit(p, start + i, v, count_of(p, v));
         }
-        if (threadIdx.x == 0) *p.flag = 1ull;
-        return;
-    }
-    if (size > (uint32_t)kRankCap) {
-        if (threadIdx.x == 0) p.big_list[atomicAdd(p.big_count, 1u)] = blockIdx.x;
+        if (threadIdx.x == 0) flag_words(p)[0] = 1u;   // redo the frame's order
         return;
     }
     const float zlo = p.bounds[0], scale = p.bounds[1];
@@ -412,7 +425,8 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
     bucket_scatter_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     bucket_rank_kernel<<<buckets, kRankThreads, 0, s>>>(p);
-    bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBigThreads, 0, s>>>(p);
+    if (p.run_larger)
+        bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBigThreads, 0, s>>>(p);
 }
 
 }  // namespace gsr

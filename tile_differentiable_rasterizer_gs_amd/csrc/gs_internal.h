@@ -173,7 +173,12 @@ struct DepthBucketParams {
     int32_t bucket_bits;           // B = 1 << bucket_bits buckets; bucket B: no pairs
     int32_t groups;                // G contiguous ranges of Gaussians
     uint32_t *range;               // [2][kDepthSlots] bound slots (reset by the last kernel)
-    unsigned long long *flag;      // device: 1 when a bucket was too large to sort
+    unsigned long long *flag;      // device: low word 1 when the order must be redone (a bucket
+                                   // too large, or a larger bucket without run_larger), high
+                                   // word 1 when a bucket too large for the per-bucket kernel
+                                   // was met
+    int32_t run_larger;            // launch the larger-bucket kernel (else such a bucket sets the
+                                   // low word)
     uint32_t *big_count;           // device: buckets listed for the sub-bin kernel
     uint32_t *big_list;            // [B] their ids
     float *bounds;                 // [2] the frame's (zmin, B / (zmax - zmin)) for the sub-bins
