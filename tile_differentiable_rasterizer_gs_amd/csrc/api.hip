@@ -108,6 +108,9 @@ struct gs_context {
     bool packed_counts = false;                // the last gs_preprocess wrote pcount
     // bucketed depth order: the bound slots, the bucketed entries and the count tables
     DeviceBuffer drange, dentries, dbscratch;
+    // the rectangles in rank order, written by the bucketed depth order (square rule)
+    DeviceBuffer drect;
+    const uint2 *ranked_rect = nullptr;        // this frame's, or null (the listings gather by Gaussian)
     bool depth_range = false;                  // the last gs_preprocess reduced its depths into drange
     // gs_cache_covariance: Sigma [6][cov_n] of the Gaussians with these quat / log_scale planes
     DeviceBuffer cov;
@@ -279,7 +282,7 @@ int ceil_log2(int64_t v) {
 }
 
 // Every device buffer of the context (destroy frees them; gs_render_noalloc swaps them out).
-constexpr int kContextBuffers = 51;
+constexpr int kContextBuffers = 52;
 void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
     DeviceBuffer *all[kContextBuffers] = {
         &ctx->splat, &ctx->depth, &ctx->rect, &ctx->tile_count, &ctx->dkey[0], &ctx->dkey[1], &ctx->dval[0],
@@ -290,7 +293,7 @@ void context_buffers(gs_context *ctx, DeviceBuffer *out[kContextBuffers]) {
         &ctx->pair_grad, &ctx->scan_total, &ctx->fix_list, &ctx->fix_count, &ctx->s2_order, &ctx->s2_rec,
         &ctx->s2_trans, &ctx->s2_partial, &ctx->skey[0], &ctx->skey[1], &ctx->sval[0], &ctx->sval[1],
         &ctx->ssort_scratch, &ctx->seg_tiles, &ctx->tile_total, &ctx->pcount, &ctx->drange,
-        &ctx->dentries, &ctx->dbscratch, &ctx->cov};
+        &ctx->dentries, &ctx->dbscratch, &ctx->cov, &ctx->drect};
     for (int i = 0; i < kContextBuffers; ++i) out[i] = all[i];
 }
 
@@ -581,6 +584,7 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
     d.offsets = as<uint32_t>(ctx->offsets);
     d.order = order;
     d.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    d.rect_ranked = order ? ctx->ranked_rect : nullptr;
     d.depth = pr->depth;
     d.tiles_x = ctx->tiles_x;
     d.values = as<uint32_t>(ctx->pval[0]);
@@ -670,7 +674,8 @@ static gs_status enqueue_pairs(gs_context *ctx, const gs_projected *pr, const ui
 // (n > 1; otherwise the identity).  buckets: the bucketed order, whose overflow flag (device
 // memory) comes back in *flag; else the four-pass radix sort of the depth bits.
 static gs_status order_by_depth(gs_context *ctx, int64_t n, const uint32_t *gather, bool buckets,
-                                const uint32_t **order, const unsigned long long **flag, hipStream_t stream) {
+                                const uint32_t **order, const unsigned long long **flag, hipStream_t stream,
+                                const uint2 *rect = nullptr, bool packed = false) {
     const size_t nn = (size_t)(n > 0 ? n : 1);
     GS_TRY(ensure(ctx, ctx->dcount, nn * sizeof(uint32_t)));
     GS_TRY(ensure(ctx, ctx->dval[1], nn * sizeof(uint32_t)));
@@ -687,6 +692,13 @@ static gs_status order_by_depth(gs_context *ctx, int64_t n, const uint32_t *gath
         b.order = as<uint32_t>(ctx->dval[1]);
         b.gathered = as<uint32_t>(ctx->dcount);
         b.run_larger = ctx->run_larger ? 1 : 0;
+        if (rect) {   // square rule: the counts follow from the rectangles, kept in rank order too
+            GS_TRY(ensure(ctx, ctx->drect, nn * sizeof(uint2)));
+            b.rect = rect;
+            b.rect_out = as<uint2>(ctx->drect);
+            b.packed_counts = packed ? 1 : 0;
+            ctx->ranked_rect = b.rect_out;
+        }
         launch_depth_bucket_sort(b, stream);
         GS_TRY(check_launch(ctx, "depth buckets"));
         *order = b.order;
@@ -759,6 +771,7 @@ static gs_status enqueue_super_pairs(gs_context *ctx, const gs_projected *pr, co
     d.offsets = as<uint32_t>(ctx->offsets);
     d.order = order;
     d.rect = reinterpret_cast<const uint2 *>(pr->rect);
+    d.rect_ranked = order ? ctx->ranked_rect : nullptr;
     d.tiles_x = super_x;
     d.tile_keys = as<uint32_t>(ctx->skey[0]);
     d.values = as<uint32_t>(ctx->sval[0]);
@@ -832,6 +845,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
     int64_t M = 0, S = 0;
     int64_t depth_buckets = 0;   // buckets of the depth order that stood, 0: the radix sort
     bool speculated = false;
+    ctx->ranked_rect = nullptr;
     if (n > 0) {
         const uint32_t *counts = pr->tile_count;   // tile counts in rank order
         // by buckets of depth when the preprocess left the depth bounds (a bucket too large
@@ -840,7 +854,9 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         const uint32_t *gather = super_bin ? as<uint32_t>(ctx->pcount) : pr->tile_count;
         const unsigned long long *bucket_flag = nullptr;
         if (depth_first) {
-            GS_TRY(order_by_depth(ctx, n, gather, buckets, &order, &bucket_flag, stream));
+            // square rule: the bucketed order writes the rectangles in rank order for the listing
+            const uint2 *rect = ctx->tile_test_used == GS_TILE_ELLIPSE ? nullptr : reinterpret_cast<const uint2 *>(pr->rect);
+            GS_TRY(order_by_depth(ctx, n, gather, buckets, &order, &bucket_flag, stream, rect, super_bin));
             counts = n > 1 ? as<uint32_t>(ctx->dcount) : pr->tile_count;
             if (buckets) depth_buckets = (int64_t)1 << depth_bucket_bits(n);
         }
@@ -888,6 +904,7 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
             // order (the totals do not change) and list the pairs afresh
             GS_HIP(ctx, hipStreamSynchronize(stream));
             GS_TRY(order_by_depth(ctx, n, gather, false, &order, nullptr, stream));
+            ctx->ranked_rect = nullptr;   // the listing gathers the rectangles by Gaussian again
             GS_TRY(enqueue_scan(ctx, counts, n, super_bin, nullptr, nullptr, stream));
             speculated = false;
             depth_buckets = 0;
@@ -1034,10 +1051,10 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
     if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_render_noalloc is already running on this context");
     // what the Gaussians and the tiles need before any pair (per Gaussian: record 64, depth 4,
     // rect 8, count 4, packed count 4, two key/index pairs 16, bucket entry 8, gathered count 4,
-    // offsets 4; the bucket count tables; per tile: range 8, launch order 4), checked before
-    // anything is enqueued; the pairs are checked once counted
+    // rect in rank order 8, offsets 4; the bucket count tables; per tile: range 8, launch order
+    // 4), checked before anything is enqueued; the pairs are checked once counted
     const int64_t tiles = (int64_t)((cam->width + GS_TILE - 1) / GS_TILE) * ((cam->height + GS_TILE - 1) / GS_TILE);
-    const int64_t fixed = g->n * 116 + depth_bucket_scratch_words(g->n) * 4 + tiles * 12;
+    const int64_t fixed = g->n * 124 + depth_bucket_scratch_words(g->n) * 4 + tiles * 12;
     if (fixed > (int64_t)(kNoAllocBytes / 2))
         return fail(ctx, GS_ERR_CAPACITY,
                     "gs_render_noalloc: %lld Gaussians and %lld tiles need %lld bytes, more than half of the "

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void super_list_kernel(DuplicateParams p) {
         k0 = p.offsets[i];
         if (k0 < stop) {
             g = p.order ? p.order[i] : (uint32_t)i;
-            rc = p.rect[g];
+            rc = p.rect_ranked ? p.rect_ranked[i] : p.rect[g];
         }
     }
     const bool solo = stop - k0 > (int64_t)kSuperListSolo;

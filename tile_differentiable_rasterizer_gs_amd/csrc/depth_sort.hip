@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
         } else {
             p.order[pos] = (uint32_t)i;
             p.gathered[pos] = 0u;
+            if (p.rect_out) p.rect_out[pos] = make_uint2(0u, 0u);
         }
     });
 }
@@ -240,14 +241,37 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
 // writer stores 1, so concurrent plain stores agree.
 __device__ inline uint32_t *flag_words(const DepthBucketParams &p) { return reinterpret_cast<uint32_t *>(p.flag); }
 
-// Writes a sorted entry: rank -> Gaussian and the Gaussian's count (read beforehand with
-// count_of, so that a thread's reads are in flight together and overlap the sorting).
-__device__ inline uint32_t count_of(const DepthBucketParams &p, uint64_t entry) {
-    return p.gather_src[(uint32_t)entry];
+// What a sorted entry carries besides its Gaussian, read right after the entry so that a
+// thread's reads are in flight together and overlap the sorting: the Gaussian's count
+// (gather_src), or with kRect its rectangle, from which the count follows (square rule) and
+// which is written in rank order too (the pair listing then reads it coalesced instead of
+// gathering it by Gaussian).
+template <bool kRect>
+struct Fetched {
+    uint32_t cnt;
+};
+template <>
+struct Fetched<true> {
+    uint2 rc;
+};
+template <bool kRect>
+__device__ inline Fetched<kRect> fetch(const DepthBucketParams &p, uint64_t entry) {
+    if constexpr (kRect)
+        return Fetched<true>{p.rect[(uint32_t)entry]};
+    else
+        return Fetched<false>{p.gather_src[(uint32_t)entry]};
 }
-__device__ inline void emit(const DepthBucketParams &p, uint32_t at, uint64_t entry, uint32_t count) {
+// Writes a sorted entry: rank -> Gaussian, the Gaussian's count and (kRect) its rectangle.
+template <bool kRect>
+__device__ inline void emit(const DepthBucketParams &p, uint32_t at, uint64_t entry, const Fetched<kRect> &f) {
     p.order[at] = (uint32_t)entry;
-    p.gathered[at] = count;
+    if constexpr (kRect) {
+        const uint32_t area = ((f.rc.x >> 16) - (f.rc.x & 0xffffu)) * ((f.rc.y >> 16) - (f.rc.y & 0xffffu));
+        p.gathered[at] = p.packed_counts ? pack_counts(area, f.rc) : area;
+        p.rect_out[at] = f.rc;
+    } else {
+        p.gathered[at] = f.cnt;
+    }
 }
 
 // Sub-bin of an entry of bucket b: the fractional part of the bucket coordinate
@@ -266,12 +290,13 @@ __device__ inline uint32_t sub_bin(uint64_t entry, uint32_t b, float zlo, float 
 // counting sort into kThreads sub-bins in LDS, then each entry ranked among the entries of
 // its own sub-bin (about size / kThreads of them).  Barriers inside; the caller waits at a
 // barrier before it reuses the LDS.
-template <int kThreads, int kE>
+template <bool kRect, int kThreads, int kE>
 __device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint32_t start, uint32_t size,
                                    float zlo, float scale, uint64_t *s_ent, uint32_t *s_cnt, uint32_t *s_base,
                                    uint32_t *s_tmp) {
     uint64_t v[kE];
-    uint32_t sub[kE], off[kE], cnt[kE];
+    uint32_t sub[kE], off[kE];
+    Fetched<kRect> f[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
         const uint32_t i = threadIdx.x + e * kThreads;
@@ -279,7 +304,7 @@ __device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint3
     }
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        cnt[e] = count_of(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's count, unused
+        f[e] = fetch<kRect>(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's, unused
         sub[e] = sub_bin<kThreads>(v[e], b, zlo, scale);
     }
     s_cnt[threadIdx.x] = 0u;   // one sub-bin per thread
@@ -302,7 +327,7 @@ __device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint3
             const uint32_t lo = s_base[sub[e]], hi = lo + s_cnt[sub[e]];
             uint32_t r = 0;
             for (uint32_t q = lo; q < hi; ++q) r += (uint32_t)(s_ent[q] < v[e]);
-            emit(p, start + lo + r, v[e], cnt[e]);
+            emit<kRect>(p, start + lo + r, v[e], f[e]);
         }
     }
 }
@@ -311,6 +336,7 @@ __device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint3
 // sorted here, larger ones listed for the larger-bucket kernel, and one of more than
 // kBucketCap entries is written unsorted with the flag raised.  Workgroup 0 also empties the
 // bound slots for the next preprocess (no later kernel reads them).
+template <bool kRect>
 __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketParams p) {
     __shared__ uint64_t s_ent[kRankCap];
     __shared__ uint32_t s_cnt[kRankThreads], s_base[kRankThreads], s_tmp[kRankThreads / kWave];
@@ -335,23 +361,24 @@ __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketPa
         // reads the flag (with stale ranks their listing walks would leave the rectangles).
         for (uint32_t i = threadIdx.x; i < size; i += kRankThreads) {
             const uint64_t v = p.entries[start + i];
-            emit(p, start + i, v, count_of(p, v));
+            emit<kRect>(p, start + i, v, fetch<kRect>(p, v));
         }
         if (threadIdx.x == 0) flag_words(p)[0] = 1u;   // redo the frame's order
         return;
     }
     const float zlo = p.bounds[0], scale = p.bounds[1];
     if (size <= (uint32_t)kRankThreads)
-        subbin_sort<kRankThreads, 1>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
+        subbin_sort<kRect, kRankThreads, 1>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
     else if (size <= 2u * kRankThreads)
-        subbin_sort<kRankThreads, 2>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
+        subbin_sort<kRect, kRankThreads, 2>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
     else if (size <= 4u * kRankThreads)
-        subbin_sort<kRankThreads, 4>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
+        subbin_sort<kRect, kRankThreads, 4>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
     else
-        subbin_sort<kRankThreads, 8>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
+        subbin_sort<kRect, kRankThreads, 8>(p, blockIdx.x, start, size, zlo, scale, s_ent, s_cnt, s_base, s_tmp);
 }
 
 // The listed buckets (kRankCap < size <= kBucketCap), shared round-robin by the workgroups.
+template <bool kRect>
 __global__ __launch_bounds__(kBigThreads) void bucket_subbin_kernel(DepthBucketParams p) {
     __shared__ uint64_t s_ent[kBucketCap];
     __shared__ uint32_t s_cnt[kBigThreads], s_base[kBigThreads], s_tmp[kBigThreads / kWave];
@@ -360,7 +387,7 @@ __global__ __launch_bounds__(kBigThreads) void bucket_subbin_kernel(DepthBucketP
     for (uint32_t li = blockIdx.x; li < count; li += gridDim.x) {
         const uint32_t b = p.big_list[li];
         const uint32_t start = p.starts[b];
-        subbin_sort<kBigThreads, kBucketCap / kBigThreads>(p, b, start, p.starts[b + 1] - start, zlo, scale, s_ent,
+        subbin_sort<kRect, kBigThreads, kBucketCap / kBigThreads>(p, b, start, p.starts[b + 1] - start, zlo, scale, s_ent,
                                                            s_cnt, s_base, s_tmp);
         __syncthreads();   // the next bucket reuses the LDS
     }
@@ -424,9 +451,14 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
     bucket_scatter_kernel<<<grid, kGroupThreads, lds, s>>>(p);
-    bucket_rank_kernel<<<buckets, kRankThreads, 0, s>>>(p);
-    if (p.run_larger)
-        bucket_subbin_kernel<<<buckets < kSubbinGroups ? buckets : kSubbinGroups, kBigThreads, 0, s>>>(p);
+    const unsigned larger = buckets < kSubbinGroups ? buckets : kSubbinGroups;
+    if (p.rect) {
+        bucket_rank_kernel<true><<<buckets, kRankThreads, 0, s>>>(p);
+        if (p.run_larger) bucket_subbin_kernel<true><<<larger, kBigThreads, 0, s>>>(p);
+    } else {
+        bucket_rank_kernel<false><<<buckets, kRankThreads, 0, s>>>(p);
+        if (p.run_larger) bucket_subbin_kernel<false><<<larger, kBigThreads, 0, s>>>(p);
+    }
 }
 
 }  // namespace gsr

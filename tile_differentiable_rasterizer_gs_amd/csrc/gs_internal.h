@@ -189,6 +189,12 @@ struct DepthBucketParams {
     const uint32_t *gather_src;    // [n] per-Gaussian value to gather in rank order
     uint32_t *order;               // out [n]: rank -> Gaussian
     uint32_t *gathered;            // out [n]: gather_src[order[r]]
+    const uint2 *rect;             // null, or [n] the square rule's tile rectangles: then the count
+                                   // comes from the rectangle instead of gather_src (the tile count
+                                   // (x1 - x0)(y1 - y0), packed with the super-tile count when
+                                   // packed_counts), and rect_out[r] = rect[order[r]]
+    uint2 *rect_out;
+    int32_t packed_counts;
 };
 int depth_bucket_bits(int64_t n);
 int depth_bucket_groups(int64_t n);
@@ -278,6 +284,7 @@ struct DuplicateParams {
     const uint32_t *offsets;     // [n_items] exclusive prefix of tile counts (in rank order)
     const uint32_t *order;       // [n_items] rank -> Gaussian index, or null (rank = index)
     const uint2 *rect;
+    const uint2 *rect_ranked;    // null, or [n_items] each rank's rectangle (rect[order[i]], read in rank order)
     const float *depth;
     int32_t tiles_x;
     uint64_t *keys64;            // key64 mode: (tile << 32) | bits(depth)

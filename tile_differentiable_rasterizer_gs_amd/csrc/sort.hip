@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             const uint32_t g = p.order ? p.order[i] : (uint32_t)i;
             s_off[k] = p.offsets[i];
             s_g[k] = g;
-            s_rect[k] = p.rect[g];
+            s_rect[k] = p.rect_ranked ? p.rect_ranked[i] : p.rect[g];
             if (kDepth) s_depth[k] = __float_as_uint(p.depth[g]);
         }
         __syncthreads();
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_kernel(DuplicateParams p, co
             const int64_t r = lo + k;
             g = p.order ? p.order[r] : (uint32_t)r;
             off = p.offsets[r];
-            rc = p.rect[g];
+            rc = p.rect_ranked ? p.rect_ranked[r] : p.rect[g];
             db = kDepth ? __float_as_uint(p.depth[g]) : 0u;
         }
     };
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kBlock) void pair_list_kernel(DuplicateParams p) {
         k0 = p.offsets[i];
         if (k0 < stop) {
             g = p.order ? p.order[i] : (uint32_t)i;
-            rc = p.rect[g];
+            rc = p.rect_ranked ? p.rect_ranked[i] : p.rect[g];
         }
     }
     const bool solo = stop - k0 > (int64_t)kPairListSolo;
