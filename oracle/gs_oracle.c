@@ -16,6 +16,13 @@
  * Plain and slow on purpose: the image is a per-pixel loop over every
  * visible Gaussian in global (depth, index) order, keeping those whose tile
  * rectangle contains the pixel's 16x16 tile.
+ *
+ * Parity unpinned: a few conventions that the lesson does not fix are taken
+ * as stated and pinned only by self-consistency -- the sign convention of the
+ * degree-3 SH terms, the quaternion component order (w, x, y, z) and
+ * handedness, the camera axes (x right, y down, z forward), the pixel (i, j)
+ * sampled at (x = j, y = i), and the near-plane value.  Every formula built
+ * on them is pinned (tests/test_oracle_pins.py).
  */
 #include <math.h>
 #include <stdint.h>
