@@ -337,8 +337,8 @@ gs_status gs_render(gs_context *ctx, const gs_gaussians *gaussians, const gs_cam
  * (64 MiB) that each device the library runs on holds until the process ends, and the call
  * makes no allocation (no hipMalloc, hipFree or event creation; profiling is off for it).
  * The context must exist (created beforehand: it holds the host-visible pair-count word).
- * Limits: the Gaussians and tiles may take at most half the array (124 bytes per Gaussian,
- * up to 8 MiB of depth-bucket counts, 12 bytes per tile: about 265 k Gaussians at 1080p),
+ * Limits: the Gaussians and tiles may take at most half the array (132 bytes per Gaussian,
+ * up to 8 MiB of depth-bucket counts, 12 bytes per tile: about 250 k Gaussians at 1080p),
  * the frame as a whole with its pairs
  * (4 to 12 bytes each, counted on the device) the full array; beyond either the call returns
  * GS_ERR_CAPACITY (the pair case after waiting for the count, with nothing composited).

@@ -681,7 +681,7 @@ static gs_status order_by_depth(gs_context *ctx, int64_t n, const uint32_t *gath
     GS_TRY(ensure(ctx, ctx->dval[1], nn * sizeof(uint32_t)));
     GS_TRY(span_begin(ctx, GS_STAGE_DEPTH_SORT, stream));
     if (buckets) {
-        GS_TRY(ensure(ctx, ctx->dentries, nn * sizeof(uint64_t)));
+        GS_TRY(ensure(ctx, ctx->dentries, nn * (rect ? 16 : 8)));   // with the rectangles: 16-byte entries
         GS_TRY(ensure(ctx, ctx->dbscratch, (size_t)depth_bucket_scratch_words(n) * sizeof(uint32_t)));
         DepthBucketParams b{};
         depth_bucket_layout(as<uint32_t>(ctx->dbscratch), n, b);
@@ -1050,11 +1050,11 @@ gs_status gs_render_noalloc(gs_context *ctx, const gs_gaussians *g, const gs_cam
     if (gs_check_arguments(g, cam, why, sizeof why) != GS_OK) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "%s", why);
     if (ctx->arena) return fail(ctx, GS_ERR_INVALID_ARGUMENT, "gs_render_noalloc is already running on this context");
     // what the Gaussians and the tiles need before any pair (per Gaussian: record 64, depth 4,
-    // rect 8, count 4, packed count 4, two key/index pairs 16, bucket entry 8, gathered count 4,
+    // rect 8, count 4, packed count 4, two key/index pairs 16, bucket entry 16, gathered count 4,
     // rect in rank order 8, offsets 4; the bucket count tables; per tile: range 8, launch order
     // 4), checked before anything is enqueued; the pairs are checked once counted
     const int64_t tiles = (int64_t)((cam->width + GS_TILE - 1) / GS_TILE) * ((cam->height + GS_TILE - 1) / GS_TILE);
-    const int64_t fixed = g->n * 124 + depth_bucket_scratch_words(g->n) * 4 + tiles * 12;
+    const int64_t fixed = g->n * 132 + depth_bucket_scratch_words(g->n) * 4 + tiles * 12;
     if (fixed > (int64_t)(kNoAllocBytes / 2))
         return fail(ctx, GS_ERR_CAPACITY,
                     "gs_render_noalloc: %lld Gaussians and %lld tiles need %lld bytes, more than half of the "

@@ -163,6 +163,9 @@ __device__ inline void for_each_key(const uint32_t *keys, int64_t lo, int64_t hi
     for (int64_t i = max(lo, 4 * vhi) + threadIdx.x; i < hi; i += kGroupThreads) f(i, keys[i]);
 }
 
+// The entries as 16-byte records (index, depth bits, rectangle) when p.rect is given.
+__device__ inline uint4 *entries16(const DepthBucketParams &p) { return reinterpret_cast<uint4 *>(p.entries); }
+
 // counts[b * G + group] = Gaussians of the group in bucket b (b = 0 .. B).  Group 0 also
 // clears the overflow flag and the list of larger buckets.
 __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucketParams p) {
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(kBlock) void bucket_column_kernel(DepthBucketParams
 
 // Each group places its Gaussians: bucket starts (exclusive prefix of the totals; group 0
 // also stores them for the sort kernels) plus the group's prefix give the cursors.
+template <bool kRect>
 __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBucketParams p) {
     extern __shared__ uint32_t s_cur[];   // [B + 1]
     __shared__ uint32_t s_lo[kDepthSlots / kWave], s_hi[kDepthSlots / kWave];
@@ -227,7 +231,12 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
         const uint32_t b = bucket_of(key, bd);
         const uint32_t pos = atomicAdd(&s_cur[b], 1u);
         if ((int)b < nb - 1) {
-            p.entries[pos] = ((uint64_t)key << 32) | (uint32_t)i;
+            if constexpr (kRect) {   // the rectangle rides with the entry (read here in index order)
+                const uint2 rc = p.rect[i];
+                entries16(p)[pos] = make_uint4((uint32_t)i, key, rc.x, rc.y);
+            } else {
+                p.entries[pos] = ((uint64_t)key << 32) | (uint32_t)i;
+            }
         } else {
             p.order[pos] = (uint32_t)i;
             p.gathered[pos] = 0u;
@@ -241,11 +250,12 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
 // writer stores 1, so concurrent plain stores agree.
 __device__ inline uint32_t *flag_words(const DepthBucketParams &p) { return reinterpret_cast<uint32_t *>(p.flag); }
 
-// What a sorted entry carries besides its Gaussian, read right after the entry so that a
-// thread's reads are in flight together and overlap the sorting: the Gaussian's count
-// (gather_src), or with kRect its rectangle, from which the count follows (square rule) and
-// which is written in rank order too (the pair listing then reads it coalesced instead of
-// gathering it by Gaussian).
+// What a sorted entry carries besides its Gaussian: the Gaussian's count, gathered right
+// after the entry is read (so that a thread's reads are in flight together and overlap the
+// sorting), or with kRect its rectangle, which the scatter stored in the entry itself (16
+// bytes: index, depth bits, rectangle), from which the count follows (square rule) and which
+// is written in rank order too (the pair listing then reads it coalesced instead of gathering
+// it by Gaussian).
 template <bool kRect>
 struct Fetched {
     uint32_t cnt;
@@ -254,12 +264,20 @@ template <>
 struct Fetched<true> {
     uint2 rc;
 };
+// Entry i of a bucket starting at `start` (i < size; else a padding entry 0, Gaussian 0's).
 template <bool kRect>
-__device__ inline Fetched<kRect> fetch(const DepthBucketParams &p, uint64_t entry) {
-    if constexpr (kRect)
-        return Fetched<true>{p.rect[(uint32_t)entry]};
-    else
-        return Fetched<false>{p.gather_src[(uint32_t)entry]};
+__device__ inline uint64_t load_entry(const DepthBucketParams &p, uint32_t at, bool real, Fetched<kRect> &f) {
+    if constexpr (kRect) {
+        const uint4 q = real ? entries16(p)[at] : make_uint4(0u, 0u, 0u, 0u);
+        f.rc = make_uint2(q.z, q.w);
+        return ((uint64_t)q.y << 32) | q.x;
+    } else {
+        return real ? p.entries[at] : 0ull;
+    }
+}
+template <bool kRect>
+__device__ inline void fetch(const DepthBucketParams &p, uint64_t entry, Fetched<kRect> &f) {
+    if constexpr (!kRect) f.cnt = p.gather_src[(uint32_t)entry];
 }
 // Writes a sorted entry: rank -> Gaussian, the Gaussian's count and (kRect) its rectangle.
 template <bool kRect>
@@ -300,11 +318,11 @@ __device__ inline void subbin_sort(const DepthBucketParams &p, uint32_t b, uint3
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
         const uint32_t i = threadIdx.x + e * kThreads;
-        v[e] = i < size ? p.entries[start + i] : 0ull;
+        v[e] = load_entry<kRect>(p, start + i, i < size, f[e]);
     }
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-        f[e] = fetch<kRect>(p, v[e]);   // a padding lane's entry is 0: Gaussian 0's, unused
+        fetch<kRect>(p, v[e], f[e]);   // a padding lane's entry is 0: Gaussian 0's, unused
         sub[e] = sub_bin<kThreads>(v[e], b, zlo, scale);
     }
     s_cnt[threadIdx.x] = 0u;   // one sub-bin per thread
@@ -360,8 +378,10 @@ __global__ __launch_bounds__(kRankThreads) void bucket_rank_kernel(DepthBucketPa
         // Gaussian with that Gaussian's own count for the kernels enqueued before the host
         // reads the flag (with stale ranks their listing walks would leave the rectangles).
         for (uint32_t i = threadIdx.x; i < size; i += kRankThreads) {
-            const uint64_t v = p.entries[start + i];
-            emit<kRect>(p, start + i, v, fetch<kRect>(p, v));
+            Fetched<kRect> f;
+            const uint64_t v = load_entry<kRect>(p, start + i, true, f);
+            fetch<kRect>(p, v, f);
+            emit<kRect>(p, start + i, v, f);
         }
         if (threadIdx.x == 0) flag_words(p)[0] = 1u;   // redo the frame's order
         return;
@@ -450,7 +470,10 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     const size_t lds = (size_t)(buckets + 1) * sizeof(uint32_t);
     bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
-    bucket_scatter_kernel<<<grid, kGroupThreads, lds, s>>>(p);
+    if (p.rect)
+        bucket_scatter_kernel<true><<<grid, kGroupThreads, lds, s>>>(p);
+    else
+        bucket_scatter_kernel<false><<<grid, kGroupThreads, lds, s>>>(p);
     const unsigned larger = buckets < kSubbinGroups ? buckets : kSubbinGroups;
     if (p.rect) {
         bucket_rank_kernel<true><<<buckets, kRankThreads, 0, s>>>(p);

@@ -185,7 +185,8 @@ struct DepthBucketParams {
     uint32_t *counts;              // [(B + 1) * G]
     uint32_t *totals;              // [B + 1]
     uint32_t *starts;              // [B + 2]
-    uint64_t *entries;             // [n] bits(depth) << 32 | index, grouped by bucket
+    uint64_t *entries;             // [n] bits(depth) << 32 | index, grouped by bucket (with rect:
+                                   // [n] 16-byte records: index, depth bits, rectangle)
     const uint32_t *gather_src;    // [n] per-Gaussian value to gather in rank order
     uint32_t *order;               // out [n]: rank -> Gaussian
     uint32_t *gathered;            // out [n]: gather_src[order[r]]
