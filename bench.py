@@ -64,9 +64,10 @@ def stage_bytes(n, sh_degree, m, n_visible, supers, tiles, buckets):
     K = (sh_degree + 1) ** 2
     pre = n * ((3 + 4 + 3 + 1 + 3 * K) * 4 + 12 * 4 + 4 + 8 + 4 + 8)
     if buckets:
-        # count and scatter read the key (4 + 4), the scatter writes an 8-byte entry, the bucket
-        # sort reads it and writes rank -> Gaussian and the gathered count (8 + 8), gathering 4
-        depth_sort = n * (4 + 4 + 8 + 8 + 8 + 4)
+        # count and scatter read the key (4 + 4), the scatter reads the rectangle (8) and writes
+        # a 16-byte entry (index, depth bits, rectangle), the bucket sort reads it and writes
+        # rank -> Gaussian, the count and the rectangle in rank order (4 + 4 + 8)
+        depth_sort = n * (4 + 4 + 8 + 16 + 16 + 16)
     else:
         depth_sort = 4 * n * 16 + n * 8    # 4 passes x (read key+value, write key+value); the last gathers
     scan = n * (4 + 4 + 4)             # gathered count + order read, offset write
