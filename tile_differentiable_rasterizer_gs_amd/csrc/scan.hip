@@ -14,6 +14,12 @@
 namespace gsr {
 namespace {
 
+// Summand of one packed count (tile count | super count << kPackShift): the two fields apart,
+// tiles | super-tiles << kPairShift, so that one uint64 sum carries both totals.
+__device__ inline unsigned long long scan_summand(uint32_t v) {
+    return (unsigned long long)(v & ((1u << kPackShift) - 1u)) | ((unsigned long long)(v >> kPackShift) << kPairShift);
+}
+
 template <typename T>
 __device__ inline T wave_inclusive_scan(T x) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -53,13 +59,27 @@ template <typename TIn, bool kPair>
 __device__ inline void load_items(const TIn *in, const uint32_t *gather, int64_t n, int64_t base,
                                   unsigned long long v[kScanItems]) {
     const int64_t first = base + (int64_t)threadIdx.x * kScanItems;
+    if constexpr (sizeof(TIn) == 4) {
+        // a thread's eight values as two 16-byte loads (blocks start at multiples of 2048
+        // values, so they are aligned when the array is): per-value loads would each touch a
+        // wave's whole 2 KB span for 256 useful bytes
+        static_assert(kScanItems == 8, "two 16-byte loads per thread");
+        if (!gather && first + kScanItems <= n && (reinterpret_cast<uintptr_t>(in) & 15) == 0) {
+            const uint4 *q = reinterpret_cast<const uint4 *>(in + first);
+            const uint4 a = q[0], b = q[1];
+            const uint32_t w[kScanItems] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < kScanItems; ++k)
+                v[k] = kPair ? scan_summand(w[k]) : (unsigned long long)w[k];
+            return;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const int64_t i = first + k;
         v[k] = 0;
         if (i < n) v[k] = gather ? (unsigned long long)in[gather[i]] : (unsigned long long)in[i];
-        if (kPair)
-            v[k] = (v[k] & ((1ull << kPackShift) - 1)) | ((v[k] >> kPackShift) << kPairShift);
+        if (kPair) v[k] = scan_summand((uint32_t)v[k]);
     }
 }
 
@@ -109,11 +129,24 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
     unsigned long long block_total;
     unsigned long long run = block_exclusive_scan(s, &block_total) + offset;
     const int64_t first = base + (int64_t)threadIdx.x * kScanItems;
+    if (sizeof(TOut) == 4 && first + kScanItems <= n && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        // two 16-byte stores, for the reason the loads are two
+        uint32_t w[kScanItems];
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-        const int64_t i = first + k;
-        if (i < n) out[i] = kPair ? (TOut)(run >> kPairShift) : (TOut)run;
-        run += v[k];
+        for (int k = 0; k < kScanItems; ++k) {
+            w[k] = kPair ? (uint32_t)(run >> kPairShift) : (uint32_t)run;
+            run += v[k];
+        }
+        uint4 *q = reinterpret_cast<uint4 *>(out + first);
+        q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            const int64_t i = first + k;
+            if (i < n) out[i] = kPair ? (TOut)(run >> kPairShift) : (TOut)run;
+            run += v[k];
+        }
     }
     if (total && threadIdx.x == 0 && blockIdx.x == gridDim.x - 1) {
         const unsigned long long all = offset + block_total;
