@@ -12,7 +12,11 @@
 //            [0, B - 1].  binary32 subtraction and product round monotonically, so the
 //            bucket never decreases with the depth whatever the bounds (they only set the
 //            balance).  Gaussians without pairs form bucket B.
-//   column   per bucket: exclusive prefix of the group counts, and the bucket total
+//   column   per bucket: exclusive prefix of the group counts, and the bucket total.  From
+//            kGroupMajorGroups groups on the table is group-major, so that count writes and
+//            scatter reads a group's row whole, and a column workgroup takes 64 buckets, its
+//            waves a quarter of the groups each, 64 neighbouring counts per row; with fewer
+//            groups it is bucket-major, a workgroup per bucket (its fixed cost is lower)
 //   scatter  each group puts its Gaussians at running per-bucket cursors in LDS: an entry
 //            (bits(depth) << 32 | index) into the bucket's range, a Gaussian without
 //            pairs straight into the output tail (their relative order is immaterial:
@@ -44,6 +48,7 @@ constexpr int kXcds = 8;             // workgroups go round-robin to the eight X
 constexpr int kRankThreads = kBlock; // workgroups of the per-bucket kernel
 constexpr int kRankCap = 8 * kRankThreads;   // largest bucket the per-bucket kernel sorts
 constexpr int kBigThreads = 1024;    // workgroups of the larger-bucket kernel
+constexpr int kGroupMajorGroups = 64;   // groups from which the count table is group-major
 constexpr int kSubbinGroups = 128;   // workgroups that share the list of larger buckets (usually none)
 
 struct Bounds {
@@ -166,7 +171,12 @@ __device__ inline void for_each_key(const uint32_t *keys, int64_t lo, int64_t hi
 // The entries as 16-byte records (index, depth bits, rectangle) when p.rect is given.
 __device__ inline uint4 *entries16(const DepthBucketParams &p) { return reinterpret_cast<uint4 *>(p.entries); }
 
-// counts[b * G + group] = Gaussians of the group in bucket b (b = 0 .. B).  Group 0 also
+// Where the count of (group, bucket b) lives in the table.
+__device__ inline int64_t count_at(const DepthBucketParams &p, int nb, int grp, int b) {
+    return p.groups >= kGroupMajorGroups ? (int64_t)grp * nb + b : (int64_t)b * p.groups + grp;
+}
+
+// count_at(group, b) = Gaussians of the group in bucket b (b = 0 .. B).  Group 0 also
 // clears the overflow flag and the list of larger buckets.
 __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucketParams p) {
     extern __shared__ uint32_t s_hist[];   // [B + 1]
@@ -183,11 +193,54 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucket
     }
     for_each_key(p.keys, lo, hi, [&](int64_t, uint32_t key) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
     __syncthreads();
-    for (int b = threadIdx.x; b < nb; b += kGroupThreads) p.counts[(int64_t)b * p.groups + grp] = s_hist[b];
+    for (int b = threadIdx.x; b < nb; b += kGroupThreads) p.counts[count_at(p, nb, grp, b)] = s_hist[b];
 }
 
-// One workgroup per bucket b (0 .. B): counts[b][*] -> exclusive prefix over groups; totals[b].
+// Buckets [64 w, 64 w + 64) for workgroup w: each count becomes the exclusive prefix over the
+// groups before it (in its bucket), and totals[b] the bucket's sum.  Lane l of each wave takes
+// bucket 64 w + l; wave k takes the k-th quarter of the groups (at most 64, as G <= 256), whose
+// counts it loads together, then stores their prefix plus the sums of the quarters before.
+constexpr int kColumnBuckets = kWave;
 __global__ __launch_bounds__(kBlock) void bucket_column_kernel(DepthBucketParams p) {
+    constexpr int kQuarters = kBlock / kWave;
+    constexpr int kPer = kBlock / kQuarters;   // groups per quarter at most
+    __shared__ uint32_t s_sum[kQuarters][kColumnBuckets];
+    const int nb = (1 << p.bucket_bits) + 1;
+    const int lane = threadIdx.x & (kWave - 1), q = threadIdx.x / kWave;
+    const int b = blockIdx.x * kColumnBuckets + lane;
+    const int g0 = p.groups * q / kQuarters, g1 = p.groups * (q + 1) / kQuarters;
+    uint32_t *col = p.counts + b;
+    uint32_t c[kPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        c[k] = (b < nb && g0 + k < g1) ? col[(int64_t)(g0 + k) * nb] : 0u;
+        sum += c[k];
+    }
+    s_sum[q][lane] = sum;
+    __syncthreads();
+    uint32_t run = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kQuarters; ++k) {
+        const uint32_t v = s_sum[k][lane];
+        run += k < q ? v : 0u;
+        all += v;
+    }
+    if (b < nb) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (g0 + k < g1) col[(int64_t)(g0 + k) * nb] = run;
+            run += c[k];
+        }
+        if (q == 0) p.totals[b] = all;
+    }
+}
+
+static_assert(kColumnBuckets == kWave && kBlock % kWave == 0, "column kernel shapes");
+
+// Bucket-major table (fewer than kGroupMajorGroups groups): one workgroup per bucket b (0 .. B),
+// counts[b][*] -> exclusive prefix over groups; totals[b].
+__global__ __launch_bounds__(kBlock) void bucket_column_small_kernel(DepthBucketParams p) {
     __shared__ uint32_t s_tmp[kBlock / kWave];
     uint32_t *row = p.counts + (int64_t)blockIdx.x * p.groups;
     const uint32_t v = (int)threadIdx.x < p.groups ? row[threadIdx.x] : 0u;   // groups <= kBlock
@@ -217,7 +270,7 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
     uint32_t all;
     uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);
     for (int b = b0; b < b1; ++b) {
-        s_cur[b] = run + p.counts[(int64_t)b * p.groups + grp];
+        s_cur[b] = run + p.counts[count_at(p, nb, grp, b)];
         if (grp == 0) p.starts[b] = run;
         run += p.totals[b];
     }
@@ -469,7 +522,10 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     const unsigned grid = (unsigned)((p.groups + kXcds - 1) / kXcds * kXcds);
     const size_t lds = (size_t)(buckets + 1) * sizeof(uint32_t);
     bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
-    bucket_column_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
+    if (p.groups >= kGroupMajorGroups)
+        bucket_column_kernel<<<(buckets + 1 + kColumnBuckets - 1) / kColumnBuckets, kBlock, 0, s>>>(p);
+    else
+        bucket_column_small_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
     if (p.rect)
         bucket_scatter_kernel<true><<<grid, kGroupThreads, lds, s>>>(p);
     else

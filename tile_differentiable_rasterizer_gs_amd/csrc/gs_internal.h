@@ -182,7 +182,7 @@ struct DepthBucketParams {
     uint32_t *big_count;           // device: buckets listed for the sub-bin kernel
     uint32_t *big_list;            // [B] their ids
     float *bounds;                 // [2] the frame's (zmin, B / (zmax - zmin)) for the sub-bins
-    uint32_t *counts;              // [(B + 1) * G]
+    uint32_t *counts;              // [G][B + 1] from 64 groups on, else [B + 1][G]
     uint32_t *totals;              // [B + 1]
     uint32_t *starts;              // [B + 2]
     uint64_t *entries;             // [n] bits(depth) << 32 | index, grouped by bucket (with rect:
