@@ -855,7 +855,11 @@ static gs_status bin_and_sort(gs_context *ctx, const gs_projected *pr, int emit_
         const unsigned long long *bucket_flag = nullptr;
         if (depth_first) {
             // square rule: the bucketed order writes the rectangles in rank order for the listing
-            const uint2 *rect = ctx->tile_test_used == GS_TILE_ELLIPSE ? nullptr : reinterpret_cast<const uint2 *>(pr->rect);
+            // (read as 16-byte vectors: a caller's rectangle plane that is not 16-byte aligned
+            // takes the gathering path)
+            const uint2 *rect = ctx->tile_test_used == GS_TILE_ELLIPSE || (reinterpret_cast<uintptr_t>(pr->rect) & 15)
+                                    ? nullptr
+                                    : reinterpret_cast<const uint2 *>(pr->rect);
             GS_TRY(order_by_depth(ctx, n, gather, buckets, &order, &bucket_flag, stream, rect, super_bin));
             counts = n > 1 ? as<uint32_t>(ctx->dcount) : pr->tile_count;
             if (buckets) depth_buckets = (int64_t)1 << depth_bucket_bits(n);

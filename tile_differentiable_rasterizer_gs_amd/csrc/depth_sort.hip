@@ -141,31 +141,41 @@ __device__ inline bool group_range(const DepthBucketParams &p, int *grp, int64_t
     return true;
 }
 
-// Visits every Gaussian of [lo, hi) once: f(index, key), kGroupBatch 16-byte loads per thread
-// issued together.
-template <typename F>
-__device__ inline void for_each_key(const uint32_t *keys, int64_t lo, int64_t hi, F f) {
+// Visits every Gaussian of [lo, hi) once: f(index, key, rectangle), kGroupBatch 16-byte loads
+// of four keys per thread issued together, and with kRect their four rectangles as two more
+// 16-byte loads each (else the rectangle passed is empty).
+template <bool kRect = false, typename F>
+__device__ inline void for_each_key(const uint32_t *keys, const uint2 *rect, int64_t lo, int64_t hi, F f) {
     const int64_t vlo = lo / 4, vhi = hi / 4;   // lo is a multiple of 4
     const uint4 *kv = reinterpret_cast<const uint4 *>(keys);
+    const uint4 *rv = reinterpret_cast<const uint4 *>(rect);
     for (int64_t j0 = vlo + threadIdx.x; j0 < vhi; j0 += (int64_t)kGroupThreads * kGroupBatch) {
-        uint4 k[kGroupBatch];
+        uint4 k[kGroupBatch], r[kGroupBatch][2];
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
             const int64_t j = j0 + (int64_t)u * kGroupThreads;
-            k[u] = kv[j < vhi ? j : j0];
+            const int64_t jj = j < vhi ? j : j0;
+            k[u] = kv[jj];
+            if constexpr (kRect) {
+                r[u][0] = rv[2 * jj];
+                r[u][1] = rv[2 * jj + 1];
+            } else {
+                r[u][0] = r[u][1] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
             const int64_t j = j0 + (int64_t)u * kGroupThreads;
             if (j < vhi) {
-                f(4 * j, k[u].x);
-                f(4 * j + 1, k[u].y);
-                f(4 * j + 2, k[u].z);
-                f(4 * j + 3, k[u].w);
+                f(4 * j, k[u].x, make_uint2(r[u][0].x, r[u][0].y));
+                f(4 * j + 1, k[u].y, make_uint2(r[u][0].z, r[u][0].w));
+                f(4 * j + 2, k[u].z, make_uint2(r[u][1].x, r[u][1].y));
+                f(4 * j + 3, k[u].w, make_uint2(r[u][1].z, r[u][1].w));
             }
         }
     }
-    for (int64_t i = max(lo, 4 * vhi) + threadIdx.x; i < hi; i += kGroupThreads) f(i, keys[i]);
+    for (int64_t i = max(lo, 4 * vhi) + threadIdx.x; i < hi; i += kGroupThreads)
+        f(i, keys[i], kRect ? rect[i] : make_uint2(0u, 0u));
 }
 
 // The entries as 16-byte records (index, depth bits, rectangle) when p.rect is given.
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucket
         *p.flag = 0ull;
         *p.big_count = 0u;
     }
-    for_each_key(p.keys, lo, hi, [&](int64_t, uint32_t key) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
+    for_each_key(p.keys, nullptr, lo, hi, [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
     __syncthreads();
     for (int b = threadIdx.x; b < nb; b += kGroupThreads) p.counts[count_at(p, nb, grp, b)] = s_hist[b];
 }
@@ -280,12 +290,11 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
         p.bounds[1] = bd.scale;
     }
     __syncthreads();
-    for_each_key(p.keys, lo, hi, [&](int64_t i, uint32_t key) {
+    for_each_key<kRect>(p.keys, p.rect, lo, hi, [&](int64_t i, uint32_t key, uint2 rc) {
         const uint32_t b = bucket_of(key, bd);
         const uint32_t pos = atomicAdd(&s_cur[b], 1u);
         if ((int)b < nb - 1) {
             if constexpr (kRect) {   // the rectangle rides with the entry (read here in index order)
-                const uint2 rc = p.rect[i];
                 entries16(p)[pos] = make_uint4((uint32_t)i, key, rc.x, rc.y);
             } else {
                 p.entries[pos] = ((uint64_t)key << 32) | (uint32_t)i;

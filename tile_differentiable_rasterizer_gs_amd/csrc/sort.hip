@@ -141,20 +141,42 @@ __global__ __launch_bounds__(kBlock) void radix_digit_scan_kernel(uint32_t *coun
     __shared__ uint32_t s_tmp[kBlock / kWave];
     uint32_t *row = counts + (int64_t)blockIdx.x * groups;
     constexpr int kPer = kMaxSortGroups / kBlock;   // groups <= kMaxSortGroups
+    static_assert(kPer == 4, "one 16-byte access per thread");
+    // a thread's four counts as one 16-byte load and store when the row allows it (per-value
+    // accesses would each spread over the wave's 1 KB span)
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0 && (int)threadIdx.x * kPer + kPer <= groups;
     uint32_t v[kPer];
     uint32_t sum = 0;
+    if (vec) {
+        const uint4 q = reinterpret_cast<const uint4 *>(row)[threadIdx.x];
+        v[0] = q.x;
+        v[1] = q.y;
+        v[2] = q.z;
+        v[3] = q.w;
+    } else {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int g = threadIdx.x * kPer + k;
-        v[k] = g < groups ? row[g] : 0u;
-        sum += v[k];
+        for (int k = 0; k < kPer; ++k) {
+            const int g = threadIdx.x * kPer + k;
+            v[k] = g < groups ? row[g] : 0u;
+        }
     }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) sum += v[k];
     uint32_t run = block_exclusive_scan_u32(sum, s_tmp);
+    uint32_t out[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int g = threadIdx.x * kPer + k;
-        if (g < groups) row[g] = run;
+        out[k] = run;
         run += v[k];
+    }
+    if (vec) {
+        reinterpret_cast<uint4 *>(row)[threadIdx.x] = make_uint4(out[0], out[1], out[2], out[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int g = threadIdx.x * kPer + k;
+            if (g < groups) row[g] = out[k];
+        }
     }
     if (threadIdx.x == kBlock - 1) totals[blockIdx.x] = run;
 }
