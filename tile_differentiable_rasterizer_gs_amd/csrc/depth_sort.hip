@@ -208,12 +208,13 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucket
 
 // Buckets [64 w, 64 w + 64) for workgroup w: each count becomes the exclusive prefix over the
 // groups before it (in its bucket), and totals[b] the bucket's sum.  Lane l of each wave takes
-// bucket 64 w + l; wave k takes the k-th quarter of the groups (at most 64, as G <= 256), whose
-// counts it loads together, then stores their prefix plus the sums of the quarters before.
+// bucket 64 w + l; wave k takes the k-th sixteenth of the groups (at most 16, as G <= 256),
+// whose counts it loads together, then stores their prefix plus the sums of the parts before.
 constexpr int kColumnBuckets = kWave;
-__global__ __launch_bounds__(kBlock) void bucket_column_kernel(DepthBucketParams p) {
-    constexpr int kQuarters = kBlock / kWave;
-    constexpr int kPer = kBlock / kQuarters;   // groups per quarter at most
+constexpr int kColumnThreads = 1024;
+__global__ __launch_bounds__(kColumnThreads) void bucket_column_kernel(DepthBucketParams p) {
+    constexpr int kQuarters = kColumnThreads / kWave;   // parts of the groups, one per wave
+    constexpr int kPer = kBlock / kQuarters;             // groups per part at most (G <= kBlock)
     __shared__ uint32_t s_sum[kQuarters][kColumnBuckets];
     const int nb = (1 << p.bucket_bits) + 1;
     const int lane = threadIdx.x & (kWave - 1), q = threadIdx.x / kWave;
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void bucket_column_kernel(DepthBucketParams
     }
 }
 
-static_assert(kColumnBuckets == kWave && kBlock % kWave == 0, "column kernel shapes");
+static_assert(kColumnBuckets == kWave && kBlock % (kColumnThreads / kWave) == 0, "column kernel shapes");
 
 // Bucket-major table (fewer than kGroupMajorGroups groups): one workgroup per bucket b (0 .. B),
 // counts[b][*] -> exclusive prefix over groups; totals[b].
@@ -532,7 +533,7 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     const size_t lds = (size_t)(buckets + 1) * sizeof(uint32_t);
     bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     if (p.groups >= kGroupMajorGroups)
-        bucket_column_kernel<<<(buckets + 1 + kColumnBuckets - 1) / kColumnBuckets, kBlock, 0, s>>>(p);
+        bucket_column_kernel<<<(buckets + 1 + kColumnBuckets - 1) / kColumnBuckets, kColumnThreads, 0, s>>>(p);
     else
         bucket_column_small_kernel<<<buckets + 1, kBlock, 0, s>>>(p);
     if (p.rect)
