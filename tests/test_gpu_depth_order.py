@@ -59,13 +59,15 @@ def _check(arrays, deg, cam, what, fallback=False, binning=binding.GS_BINNING_AU
     return bk
 
 
-# (width, height, Gaussians, SH degree, log-scale range): 256 or 1024 buckets, ragged groups
+# (width, height, Gaussians, SH degree, log-scale range): 256 to 1024 buckets, ragged groups
 CASES = [
     (211, 139, 4000, 2, (-4.0, -1.8)),
     (320, 240, 25000, 0, (-4.5, -2.5)),
     (640, 360, 60001, 1, (-4.5, -3.0)),
     (96, 64, 3, 0, (-2.0, -1.0)),
     (640, 360, 300007, 0, (-5.0, -3.5)),
+    (512, 384, 262144, 0, (-5.0, -3.5)),   # exactly 64 counting groups: the group-major count table
+    (512, 384, 258047, 0, (-5.0, -3.5)),   # 63 groups: the bucket-major one
 ]
 
 
