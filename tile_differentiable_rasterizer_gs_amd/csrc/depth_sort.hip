@@ -49,6 +49,7 @@ constexpr int kRankThreads = kBlock; // workgroups of the per-bucket kernel
 constexpr int kRankCap = 8 * kRankThreads;   // largest bucket the per-bucket kernel sorts
 constexpr int kBigThreads = 1024;    // workgroups of the larger-bucket kernel
 constexpr int kGroupMajorGroups = 64;   // groups from which the count table is group-major
+constexpr int64_t kSingleGroupKeys = 16384;   // up to this many Gaussians: one group, one launch
 constexpr int kSubbinGroups = 128;   // workgroups that share the list of larger buckets (usually none)
 
 struct Bounds {
@@ -308,6 +309,55 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
     });
 }
 
+// At most kSingleGroupKeys Gaussians (one group): count, bucket starts and scatter in one
+// workgroup and one launch instead of three (the count table is not needed).
+template <bool kRect>
+__global__ __launch_bounds__(kGroupThreads) void bucket_single_kernel(DepthBucketParams p) {
+    extern __shared__ uint32_t s_cur[];   // [B + 1]: counts, then cursors
+    __shared__ uint32_t s_lo[kDepthSlots / kWave], s_hi[kDepthSlots / kWave];
+    __shared__ uint32_t s_tmp[kGroupThreads / kWave];
+    const int nb = (1 << p.bucket_bits) + 1;
+    for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_cur[i] = 0u;
+    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
+    if (threadIdx.x == 0) {
+        *p.flag = 0ull;
+        *p.big_count = 0u;
+        p.bounds[0] = bd.zlo;   // for the sub-bins
+        p.bounds[1] = bd.scale;
+    }
+    for_each_key(p.keys, nullptr, 0, p.n, [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_cur[bucket_of(key, bd)], 1u); });
+    __syncthreads();
+    // thread t: buckets [b0, b1); their counts become the bucket starts
+    const int per = (nb + kGroupThreads - 1) / kGroupThreads;
+    const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+    uint32_t sum = 0;
+    for (int b = b0; b < b1; ++b) sum += s_cur[b];
+    uint32_t all;
+    uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);   // barriers inside
+    for (int b = b0; b < b1; ++b) {
+        const uint32_t c = s_cur[b];
+        s_cur[b] = run;
+        p.starts[b] = run;
+        run += c;
+    }
+    if (threadIdx.x == 0) p.starts[nb] = all;
+    __syncthreads();
+    for_each_key<kRect>(p.keys, p.rect, 0, p.n, [&](int64_t i, uint32_t key, uint2 rc) {
+        const uint32_t b = bucket_of(key, bd);
+        const uint32_t pos = atomicAdd(&s_cur[b], 1u);
+        if ((int)b < nb - 1) {
+            if constexpr (kRect)
+                entries16(p)[pos] = make_uint4((uint32_t)i, key, rc.x, rc.y);
+            else
+                p.entries[pos] = ((uint64_t)key << 32) | (uint32_t)i;
+        } else {
+            p.order[pos] = (uint32_t)i;
+            p.gathered[pos] = 0u;
+            if (p.rect_out) p.rect_out[pos] = make_uint2(0u, 0u);
+        }
+    });
+}
+
 // The frame's flag as two words (the host reads them as one 64-bit value): [0] the order must
 // be redone by the radix sort, [1] a bucket too large for the per-bucket kernel was met.  Every
 // writer stores 1, so concurrent plain stores agree.
@@ -495,6 +545,7 @@ int depth_bucket_bits(int64_t n) {
 }
 
 int depth_bucket_groups(int64_t n) {
+    if (n <= kSingleGroupKeys) return 1;   // one workgroup does count, starts and scatter
     const int64_t buckets = ((int64_t)1 << depth_bucket_bits(n)) + 1;
     int64_t g = (n + kGroupKeys - 1) / kGroupKeys;
     const int64_t cap = kMaxCountWords / buckets;
@@ -531,6 +582,12 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
     const int buckets = 1 << p.bucket_bits;
     const unsigned grid = (unsigned)((p.groups + kXcds - 1) / kXcds * kXcds);
     const size_t lds = (size_t)(buckets + 1) * sizeof(uint32_t);
+    if (p.groups == 1) {
+        if (p.rect)
+            bucket_single_kernel<true><<<1, kGroupThreads, lds, s>>>(p);
+        else
+            bucket_single_kernel<false><<<1, kGroupThreads, lds, s>>>(p);
+    } else {
     bucket_count_kernel<<<grid, kGroupThreads, lds, s>>>(p);
     if (p.groups >= kGroupMajorGroups)
         bucket_column_kernel<<<(buckets + 1 + kColumnBuckets - 1) / kColumnBuckets, kColumnThreads, 0, s>>>(p);
@@ -540,6 +597,7 @@ void launch_depth_bucket_sort(const DepthBucketParams &p, hipStream_t s) {
         bucket_scatter_kernel<true><<<grid, kGroupThreads, lds, s>>>(p);
     else
         bucket_scatter_kernel<false><<<grid, kGroupThreads, lds, s>>>(p);
+    }
     const unsigned larger = buckets < kSubbinGroups ? buckets : kSubbinGroups;
     if (p.rect) {
         bucket_rank_kernel<true><<<buckets, kRankThreads, 0, s>>>(p);
