@@ -142,7 +142,8 @@ typedef struct {
  *               binning, else 0 (informational: the traffic of the binning stage)
  *   depth_buckets  number of depth buckets when GS_DEPTH_ORDER_BUCKETS ordered the
  *               Gaussians of this frame, 0 when the radix sort did (GS_DEPTH_ORDER_RADIX,
- *               a fallback from too large a bucket, GS_SORT_KEY64, or fewer than 2 Gaussians)
+ *               a fallback from too large a bucket or one whose kernel the frame left out,
+ *               GS_SORT_KEY64, or fewer than 2 Gaussians)
  */
 typedef struct {
     int64_t num_dups;
@@ -207,7 +208,10 @@ typedef enum {
        tiles (B = 256 .. 8192 with the scene), one distribution pass, then each bucket sorted
        by (depth bits, index) in LDS.  If a bucket holds more than 4096 Gaussians (depths
        crowded into a sliver of the range) the frame falls back to GS_DEPTH_ORDER_RADIX.
-       The default. */
+       Buckets of 2049 to 4096 Gaussians have a kernel of their own, which a context launches
+       only while its last bucketed frame met such a bucket; a frame that meets one without it
+       falls back the same way (and the next frame launches it).  Results are the same bits on
+       every path.  The default. */
     GS_DEPTH_ORDER_BUCKETS = 0,
     /* stable LSD radix sort of the 32 depth bits, four 8-bit passes */
     GS_DEPTH_ORDER_RADIX = 1
