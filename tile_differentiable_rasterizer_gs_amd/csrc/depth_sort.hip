@@ -144,14 +144,16 @@ __device__ inline bool group_range(const DepthBucketParams &p, int *grp, int64_t
 
 // Visits every Gaussian of [lo, hi) once: f(index, key, rectangle), kGroupBatch 16-byte loads
 // of four keys per thread issued together, and with kRect their four rectangles as two more
-// 16-byte loads each (else the rectangle passed is empty).
-template <bool kRect = false, typename F>
-__device__ inline void for_each_key(const uint32_t *keys, const uint2 *rect, int64_t lo, int64_t hi, F f) {
+// 16-byte loads each (else the rectangle passed is empty).  pre() runs once in every thread
+// after the first batch's loads are issued and before any f: the caller's set-up (bounds,
+// cursors, barriers) overlaps those loads.
+template <bool kRect = false, typename Pre, typename F>
+__device__ inline void for_each_key(const uint32_t *keys, const uint2 *rect, int64_t lo, int64_t hi, Pre pre, F f) {
     const int64_t vlo = lo / 4, vhi = hi / 4;   // lo is a multiple of 4
     const uint4 *kv = reinterpret_cast<const uint4 *>(keys);
     const uint4 *rv = reinterpret_cast<const uint4 *>(rect);
-    for (int64_t j0 = vlo + threadIdx.x; j0 < vhi; j0 += (int64_t)kGroupThreads * kGroupBatch) {
-        uint4 k[kGroupBatch], r[kGroupBatch][2];
+    uint4 k[kGroupBatch], r[kGroupBatch][2];
+    auto load = [&](int64_t j0) {
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
             const int64_t j = j0 + (int64_t)u * kGroupThreads;
@@ -164,6 +166,12 @@ __device__ inline void for_each_key(const uint32_t *keys, const uint2 *rect, int
                 r[u][0] = r[u][1] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
+    };
+    int64_t j0 = vlo + threadIdx.x;
+    if (j0 < vhi) load(j0);
+    pre();
+    for (bool first = true; j0 < vhi; j0 += (int64_t)kGroupThreads * kGroupBatch, first = false) {
+        if (!first) load(j0);
 #pragma unroll
         for (int u = 0; u < kGroupBatch; ++u) {
             const int64_t j = j0 + (int64_t)u * kGroupThreads;
@@ -196,13 +204,18 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_count_kernel(DepthBucket
     int64_t lo, hi;
     if (!group_range(p, &grp, &lo, &hi)) return;   // whole workgroup
     const int nb = (1 << p.bucket_bits) + 1;
-    for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_hist[i] = 0u;
-    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
-    if (grp == 0 && threadIdx.x == 0) {
-        *p.flag = 0ull;
-        *p.big_count = 0u;
-    }
-    for_each_key(p.keys, nullptr, lo, hi, [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
+    Bounds bd;
+    for_each_key(
+        p.keys, nullptr, lo, hi,
+        [&]() {
+            for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_hist[i] = 0u;
+            bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
+            if (grp == 0 && threadIdx.x == 0) {
+                *p.flag = 0ull;
+                *p.big_count = 0u;
+            }
+        },
+        [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_hist[bucket_of(key, bd)], 1u); });
     __syncthreads();
     for (int b = threadIdx.x; b < nb; b += kGroupThreads) p.counts[count_at(p, nb, grp, b)] = s_hist[b];
 }
@@ -273,26 +286,29 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_scatter_kernel(DepthBuck
     int64_t lo, hi;
     if (!group_range(p, &grp, &lo, &hi)) return;   // whole workgroup
     const int nb = (1 << p.bucket_bits) + 1;
-    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);
-    // thread t: buckets [b0, b1)
-    const int per = (nb + kGroupThreads - 1) / kGroupThreads;
-    const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
-    uint32_t sum = 0;
-    for (int b = b0; b < b1; ++b) sum += p.totals[b];
-    uint32_t all;
-    uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);
-    for (int b = b0; b < b1; ++b) {
-        s_cur[b] = run + p.counts[count_at(p, nb, grp, b)];
-        if (grp == 0) p.starts[b] = run;
-        run += p.totals[b];
-    }
-    if (grp == 0 && threadIdx.x == 0) {
-        p.starts[nb] = all;
-        p.bounds[0] = bd.zlo;   // for the sub-bins of larger buckets
-        p.bounds[1] = bd.scale;
-    }
-    __syncthreads();
-    for_each_key<kRect>(p.keys, p.rect, lo, hi, [&](int64_t i, uint32_t key, uint2 rc) {
+    Bounds bd;
+    auto setup = [&]() {
+        bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);
+        // thread t: buckets [b0, b1)
+        const int per = (nb + kGroupThreads - 1) / kGroupThreads;
+        const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+        uint32_t sum = 0;
+        for (int b = b0; b < b1; ++b) sum += p.totals[b];
+        uint32_t all;
+        uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);
+        for (int b = b0; b < b1; ++b) {
+            s_cur[b] = run + p.counts[count_at(p, nb, grp, b)];
+            if (grp == 0) p.starts[b] = run;
+            run += p.totals[b];
+        }
+        if (grp == 0 && threadIdx.x == 0) {
+            p.starts[nb] = all;
+            p.bounds[0] = bd.zlo;   // for the sub-bins of larger buckets
+            p.bounds[1] = bd.scale;
+        }
+        __syncthreads();
+    };
+    for_each_key<kRect>(p.keys, p.rect, lo, hi, setup, [&](int64_t i, uint32_t key, uint2 rc) {
         const uint32_t b = bucket_of(key, bd);
         const uint32_t pos = atomicAdd(&s_cur[b], 1u);
         if ((int)b < nb - 1) {
@@ -317,32 +333,40 @@ __global__ __launch_bounds__(kGroupThreads) void bucket_single_kernel(DepthBucke
     __shared__ uint32_t s_lo[kDepthSlots / kWave], s_hi[kDepthSlots / kWave];
     __shared__ uint32_t s_tmp[kGroupThreads / kWave];
     const int nb = (1 << p.bucket_bits) + 1;
-    for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_cur[i] = 0u;
-    const Bounds bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
-    if (threadIdx.x == 0) {
-        *p.flag = 0ull;
-        *p.big_count = 0u;
-        p.bounds[0] = bd.zlo;   // for the sub-bins
-        p.bounds[1] = bd.scale;
-    }
-    for_each_key(p.keys, nullptr, 0, p.n, [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_cur[bucket_of(key, bd)], 1u); });
+    Bounds bd;
+    for_each_key(
+        p.keys, nullptr, 0, p.n,
+        [&]() {
+            for (int i = threadIdx.x; i < nb; i += kGroupThreads) s_cur[i] = 0u;
+            bd = load_bounds(p.range, 1 << p.bucket_bits, s_lo, s_hi);   // barrier inside
+            if (threadIdx.x == 0) {
+                *p.flag = 0ull;
+                *p.big_count = 0u;
+                p.bounds[0] = bd.zlo;   // for the sub-bins
+                p.bounds[1] = bd.scale;
+            }
+        },
+        [&](int64_t, uint32_t key, uint2) { atomicAdd(&s_cur[bucket_of(key, bd)], 1u); });
     __syncthreads();
-    // thread t: buckets [b0, b1); their counts become the bucket starts
-    const int per = (nb + kGroupThreads - 1) / kGroupThreads;
-    const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
-    uint32_t sum = 0;
-    for (int b = b0; b < b1; ++b) sum += s_cur[b];
-    uint32_t all;
-    uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);   // barriers inside
-    for (int b = b0; b < b1; ++b) {
-        const uint32_t c = s_cur[b];
-        s_cur[b] = run;
-        p.starts[b] = run;
-        run += c;
-    }
-    if (threadIdx.x == 0) p.starts[nb] = all;
-    __syncthreads();
-    for_each_key<kRect>(p.keys, p.rect, 0, p.n, [&](int64_t i, uint32_t key, uint2 rc) {
+    // thread t: buckets [b0, b1); their counts become the bucket starts (while the second
+    // pass's first loads are in flight)
+    auto starts = [&]() {
+        const int per = (nb + kGroupThreads - 1) / kGroupThreads;
+        const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+        uint32_t sum = 0;
+        for (int b = b0; b < b1; ++b) sum += s_cur[b];
+        uint32_t all;
+        uint32_t run = block_scan<kGroupThreads>(sum, s_tmp, &all);   // barriers inside
+        for (int b = b0; b < b1; ++b) {
+            const uint32_t c = s_cur[b];
+            s_cur[b] = run;
+            p.starts[b] = run;
+            run += c;
+        }
+        if (threadIdx.x == 0) p.starts[nb] = all;
+        __syncthreads();
+    };
+    for_each_key<kRect>(p.keys, p.rect, 0, p.n, starts, [&](int64_t i, uint32_t key, uint2 rc) {
         const uint32_t b = bucket_of(key, bd);
         const uint32_t pos = atomicAdd(&s_cur[b], 1u);
         if ((int)b < nb - 1) {
