@@ -112,6 +112,10 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
                                                                 unsigned long long *total,
                                                                 unsigned long long *host_total,
                                                                 const unsigned long long *flag) {
+    // the block's own values first: their loads are in flight while the offset is summed
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    unsigned long long v[kScanItems];
+    load_items<TIn, kPair>(in, gather, n, base, v);
     unsigned long long offset = 0;
     if (prefix) {
         offset = prefix[blockIdx.x];
@@ -120,9 +124,6 @@ __global__ __launch_bounds__(kBlock) void scan_downsweep_kernel(const TIn *in, c
         for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kBlock) before += block_sums[j];
         block_exclusive_scan(before, &offset);
     }
-    const int64_t base = (int64_t)blockIdx.x * kScanTile;
-    unsigned long long v[kScanItems];
-    load_items<TIn, kPair>(in, gather, n, base, v);
     unsigned long long s = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) s += v[k];
